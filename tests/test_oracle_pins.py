@@ -1,0 +1,505 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+Each test checks the oracle against something other than itself: values
+worked by hand (tests/golden), closed forms, library routines that the
+definition reduces to in special cases (torch.optim in float64, torch's bf16
+cast), exact integer arithmetic, published hash test vectors, and the
+statistical statements of the FORGE paper's Appendices B and C.
+"""
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _hyper(opt, d):
+    return O.Hyper(opt=opt, **d)
+
+
+# ---------------------------------------------------------------------------
+# Element-wise optimizers
+# ---------------------------------------------------------------------------
+def _run_scalar(case):
+    h = case["hyper"]
+    W, m, v = case["W0"], 0.0, 0.0
+    out = {"W": [], "m": [], "v": []}
+    for t, G in enumerate(case["G"], 1):
+        if case["opt"] == "adamw":
+            W, m, v = O.adamw(W, G, m, v, t, h["lr"], h["beta1"], h["beta2"], h["eps"], h["weight_decay"])
+        elif case["opt"] == "lion":
+            W, m = O.lion(W, G, m, h["lr"], h["beta1"], h["beta2"], h["weight_decay"])
+        else:
+            W, m = O.sgdm(W, G, m, h["lr"], h["beta1"], h["weight_decay"])
+        out["W"].append(W)
+        out["m"].append(m)
+        out["v"].append(v)
+    return out
+
+
+def test_hand_worked_trajectories():
+    """Algorithm 1 Phase 2 (AdamW), Lion and SGD-m against values worked by hand."""
+    with open(os.path.join(GOLDEN, "hand_worked_steps.json")) as f:
+        cases = json.load(f)["cases"]
+    for case in cases:
+        got = _run_scalar(case)
+        for key in ("W", "m", "v"):
+            if key not in case:
+                continue
+            for t, (a, r) in enumerate(zip(got[key], case[key]), 1):
+                assert a == pytest.approx(r, rel=1e-12, abs=1e-18), (case["opt"], key, t, a, r)
+
+
+def test_adamw_first_step_closed_form():
+    """t = 1 from m = v = 0: m_hat = G and v_hat = G^2, so
+    W1 = (1 - lr wd) W0 - lr G/(|G| + eps)."""
+    rng = np.random.default_rng(0)
+    W0, G = rng.normal(0, 0.02, 1000), rng.normal(0, 1e-2, 1000)
+    lr, b1, b2, eps, wd = 1e-3, 0.9, 0.999, 1e-8, 0.01
+    W1, m1, v1 = O.adamw(W0, G, np.zeros(1000), np.zeros(1000), 1, lr, b1, b2, eps, wd)
+    np.testing.assert_allclose(W1, (1 - lr * wd) * W0 - lr * G / (np.abs(G) + eps), rtol=1e-13)
+    np.testing.assert_allclose(m1 / (1 - b1), G, rtol=1e-13)
+    np.testing.assert_allclose(v1 / (1 - b2), G * G, rtol=1e-12)
+
+
+def test_adamw_constant_gradient_bias_correction():
+    """A constant gradient gives m_hat = G and v_hat = G^2 at every step: the
+    bias correction uses the 1-based t directly."""
+    G = np.array([0.3, -2e-3, 5e-6])
+    b1, b2 = 0.9, 0.999
+    m = v = np.zeros(3)
+    W = np.full(3, 0.1)
+    for t in range(1, 30):
+        W, m, v = O.adamw(W, G, m, v, t, 1e-3, b1, b2, 1e-8, 0.0)
+        np.testing.assert_allclose(m / (1 - b1 ** t), G, rtol=1e-12)
+        np.testing.assert_allclose(v / (1 - b2 ** t), G * G, rtol=1e-11)
+
+
+def test_adamw_zero_gradient_is_pure_decay():
+    W0 = np.array([0.02, -0.5, 3.0])
+    W, m, v = W0, np.zeros(3), np.zeros(3)
+    for t in range(1, 6):
+        W, m, v = O.adamw(W, np.zeros(3), m, v, t, 1e-3, 0.9, 0.999, 1e-8, 0.01)
+        np.testing.assert_allclose(W, (1 - 1e-5) ** t * W0, rtol=1e-14)
+
+
+def test_adamw_matches_torch_adamw_float64():
+    """torch.optim.AdamW (decoupled decay, bias correction, eps outside the
+    root) is the same map; in float64 the two agree to rounding."""
+    rng = np.random.default_rng(1)
+    n = 4096
+    W = rng.normal(0, 0.02, n)
+    m, v = np.zeros(n), np.zeros(n)
+    p = torch.tensor(W.copy(), dtype=torch.float64, requires_grad=True)
+    opt = torch.optim.AdamW([p], lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01)
+    for t in range(1, 8):
+        G = rng.normal(0, 1e-2, n)
+        W, m, v = O.adamw(W, G, m, v, t, 1e-3, 0.9, 0.999, 1e-8, 0.01)
+        p.grad = torch.tensor(G, dtype=torch.float64)
+        opt.step()
+    st = opt.state[p]
+    np.testing.assert_allclose(W, p.detach().numpy(), rtol=1e-13, atol=1e-18)
+    np.testing.assert_allclose(m, st["exp_avg"].numpy(), rtol=1e-12, atol=1e-20)
+    np.testing.assert_allclose(v, st["exp_avg_sq"].numpy(), rtol=1e-12, atol=1e-24)
+
+
+def test_sgdm_matches_torch_sgd_float64():
+    rng = np.random.default_rng(2)
+    n = 2048
+    W = rng.normal(0, 0.02, n)
+    b = np.zeros(n)
+    p = torch.tensor(W.copy(), dtype=torch.float64, requires_grad=True)
+    opt = torch.optim.SGD([p], lr=1e-3, momentum=0.9, weight_decay=0.01)
+    for _ in range(5):
+        G = rng.normal(0, 1e-2, n)
+        W, b = O.sgdm(W, G, b, 1e-3, 0.9, 0.01)
+        p.grad = torch.tensor(G, dtype=torch.float64)
+        opt.step()
+    np.testing.assert_allclose(W, p.detach().numpy(), rtol=1e-14)
+    np.testing.assert_allclose(b, opt.state[p]["momentum_buffer"].numpy(), rtol=1e-12)
+
+
+def test_lion_sign_and_zero():
+    """Lion moves every coordinate by exactly lr (plus decay) in the direction
+    of -sign(c); where c == 0 only the decay acts.  (b1 = 0.5 keeps c exact.)"""
+    W0 = np.array([0.5, 0.5, 0.5, -0.25])
+    m0 = np.array([0.0, 1.0, -1.0, 0.0])
+    G = np.array([0.0, -1.0, 3.0, -3.0])       # c = 0, 0, 1, -1.5
+    W1, m1 = O.lion(W0, G, m0, 1e-4, 0.5, 0.99, 0.01)
+    dec = (1 - 1e-6) * W0
+    np.testing.assert_allclose(W1, dec - 1e-4 * np.array([0, 0, 1, -1]), rtol=1e-15)
+    np.testing.assert_allclose(m1, 0.99 * m0 + 0.01 * G, rtol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# Gradient (Eq. 3)
+# ---------------------------------------------------------------------------
+def _int_inputs(BT, N, K, rng, in_dtype):
+    """Integer-valued inputs exact in bf16: X in {-2..2}, dY in {-2..2} * 2^-10."""
+    Xi = rng.integers(-2, 3, (BT, K))
+    dYi = rng.integers(-2, 3, (BT, N))
+    Xt = torch.tensor(Xi, dtype=torch.float32)
+    dYt = torch.tensor(dYi, dtype=torch.float32) * 2.0 ** -10
+    if in_dtype == "bf16":
+        X = Xt.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        dY = dYt.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    else:
+        X, dY = Xt.numpy(), dYt.numpy()
+    return Xi, dYi, X, dY
+
+
+@pytest.mark.parametrize("in_dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("BT,N,K", [(1, 1, 1), (2, 3, 9), (3, 9, 3), (7, 5, 130), (64, 130, 7)])
+def test_weight_grad_brute_force(BT, N, K, in_dtype):
+    """G[p, q] = sum_t dY[t, p] X[t, q] against an exact integer triple loop.
+    Non-square shapes make a transposed operand fail."""
+    rng = np.random.default_rng(BT * 1000 + N * 10 + K)
+    Xi, dYi, X, dY = _int_inputs(BT, N, K, rng, in_dtype)
+    exact = np.zeros((N, K), dtype=object)
+    for p in range(N):
+        for q in range(K):
+            s = 0
+            for t in range(BT):
+                s += int(dYi[t, p]) * int(Xi[t, q])
+            exact[p, q] = Fraction(s, 1024)
+    ref = np.array([[float(x) for x in row] for row in exact])
+    for order in ("blas", "seq64", "seq32"):
+        G = O.weight_grad(X, dY, order=order)
+        assert G.shape == (N, K)
+        np.testing.assert_array_equal(G, ref)
+
+
+def test_weight_grad_sub_block_indexing():
+    """A sub-block (rows, cols) of G equals the same entries of the full G,
+    computed independently with math.fsum."""
+    rng = np.random.default_rng(5)
+    X = rng.normal(size=(33, 21)).astype(np.float32)
+    dY = rng.normal(size=(33, 17)).astype(np.float32)
+    rows, cols = np.array([16, 3, 0]), np.array([20, 1])
+    G = O.weight_grad(X, dY, rows, cols)
+    for a, p in enumerate(rows):
+        for b, q in enumerate(cols):
+            ref = math.fsum(float(dY[t, p]) * float(X[t, q]) for t in range(33))
+            assert G[a, b] == pytest.approx(ref, rel=1e-14, abs=1e-14)
+
+
+def test_grad_error_bound_covers_fp32_orders():
+    """The fp32 sequential accumulation lies within the stated bound of the
+    fp64 value (Corollary 1(b): only the reduction order differs)."""
+    rng = np.random.default_rng(6)
+    X = rng.normal(size=(512, 40)).astype(np.float32)
+    dY = (rng.normal(size=(512, 30)) * 1e-3).astype(np.float32)
+    G64 = O.weight_grad(X, dY)
+    G32 = O.weight_grad(X, dY, order="seq32")
+    E = O.grad_error_bound(X, dY)
+    assert np.all(np.abs(G32 - G64) <= E)
+    # ... and the bound is far tighter than dropping a single token would be
+    G_drop = O.weight_grad(X[1:], dY[1:])
+    assert np.mean(np.abs(G_drop - G64) > E) > 0.95
+
+
+# ---------------------------------------------------------------------------
+# Counter-based random bits
+# ---------------------------------------------------------------------------
+def test_fmix32_published_vectors():
+    """MurmurHash3_x86_32 of the empty input is fmix32(seed); its published test
+    vectors for seeds 0, 1 and 0xFFFFFFFF are 0, 0x514E28B7, 0x81F16F39."""
+    assert O.fmix32(0) == 0
+    assert O.fmix32(1) == 0x514E28B7
+    assert O.fmix32(0xFFFFFFFF) == 0x81F16F39
+    arr = O.fmix32(np.array([0, 1, 0xFFFFFFFF], dtype=np.uint32))
+    assert list(map(int, arr)) == [0, 0x514E28B7, 0x81F16F39]
+
+
+def test_sr_bits_uniform_and_independent():
+    n = 1 << 20
+    idx = np.arange(n, dtype=np.uint64)
+    r = O.sr_bits(O.sr_key(1337, 10, 0), idx).astype(np.int64)
+    assert r.min() >= 0 and r.max() < 65536
+    # mean of U{0..65535} is 32767.5, sd 18918.6 -> 5 sigma of the mean ~ 92
+    assert abs(r.mean() - 32767.5) < 5 * 18918.6 / math.sqrt(n)
+    for bit in range(16):
+        frac = ((r >> bit) & 1).mean()
+        assert abs(frac - 0.5) < 5 * 0.5 / math.sqrt(n)
+    hist = np.bincount(r >> 8, minlength=256)
+    chi2 = ((hist - n / 256) ** 2 / (n / 256)).sum()
+    assert chi2 < 400  # 255 dof: mean 255, sd 22.6
+    # different tensor / step / seed -> uncorrelated streams
+    for key in (O.sr_key(1337, 10, 1), O.sr_key(1337, 11, 0), O.sr_key(1338, 10, 0)):
+        r2 = O.sr_bits(key, idx).astype(np.int64)
+        c = np.corrcoef(r, r2)[0, 1]
+        assert abs(c) < 5 / math.sqrt(n)
+    # keys are all distinct across the three tensors
+    assert len({O.sr_key(7, 3, t) for t in range(3)}) == 3
+
+
+# ---------------------------------------------------------------------------
+# bf16 rounding (Appendix C)
+# ---------------------------------------------------------------------------
+def test_bf16_rne_matches_torch_cast():
+    rng = np.random.default_rng(3)
+    x = np.concatenate([
+        rng.normal(size=100000).astype(np.float32),
+        (rng.normal(size=1000) * 1e-40).astype(np.float32),           # subnormals
+        np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 0.0, -0.0, np.inf, -np.inf,
+                  3.3895314e38, 1e-45], dtype=np.float32),           # ties, specials, overflow
+    ])
+    ours = O.f32_to_bf16_rne(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ours, ref)
+    nan = O.f32_to_bf16_rne(np.array([np.nan], dtype=np.float32))
+    assert np.isnan(O.bf16_bits_to_f64(nan))[0]
+
+
+def test_bf16_dead_zone_and_sr_exact_values():
+    """Round-to-nearest discards an update below half an ULP (Appendix C,
+    dead-zone); SR leaves exactly representable values unchanged."""
+    w = np.float32(0.75)                  # bf16 ULP at 0.75 is 2^-8
+    x = np.full(1000, w - np.float32(1e-3), dtype=np.float32)
+    assert np.all(O.bf16_bits_to_f64(O.f32_to_bf16_rne(x)) == 0.75)
+    exact = O.bf16_bits_to_f64(np.arange(0, 65535, 7, dtype=np.uint16)).astype(np.float32)
+    exact = exact[np.isfinite(exact)]
+    r = O.sr_bits(O.sr_key(1, 1, 0), np.arange(exact.size))
+    out = O.bf16_bits_to_f64(O.f32_to_bf16_sr(exact, r))
+    np.testing.assert_array_equal(out, exact.astype(np.float64))
+
+
+def test_sr_unbiased_1e6_draws():
+    """Proposition 5: E[SR(x)] = x.  x = 1 + 2^-10 sits 1/8 ULP above 1.0, so
+    SR rounds up with probability 0.125; round-to-nearest is biased by
+    -2^-10 = -9.77e-4."""
+    n = 1_000_000
+    x = np.full(n, 1 + 2 ** -10, dtype=np.float32)
+    r = O.sr_bits(O.sr_key(1337, 1, 0), np.arange(n))
+    y = O.bf16_bits_to_f64(O.f32_to_bf16_sr(x, r))
+    assert set(np.unique(y)) <= {1.0, 1.0 + 2 ** -7}
+    up = np.mean(y > 1.0)
+    sd = math.sqrt(0.125 * 0.875 / n)                   # 3.3e-4
+    assert abs(up - 0.125) < 5 * sd
+    err = np.mean(y) - (1 + 2 ** -10)
+    assert abs(err) < 5 * sd * 2 ** -7                  # 1.3e-5
+    rne = O.bf16_bits_to_f64(O.f32_to_bf16_rne(x))
+    assert np.all(rne == 1.0)
+    assert np.mean(rne) - (1 + 2 ** -10) == pytest.approx(-2 ** -10)
+
+
+def test_sr_quarter_ulp_microbenchmark():
+    """Appendix C, Implementation: 100 steps of a true update of -1e-3 at a
+    quarter ULP.  Round-to-nearest reports a mean change of 0.000, stochastic
+    rounding -0.100 (the fp32-master value)."""
+    n, steps = 100_000, 100
+    idx = np.arange(n)
+    w_sr = np.full(n, 0.75, dtype=np.float32)
+    w_rn = w_sr.copy()
+    for t in range(1, steps + 1):
+        r = O.sr_bits(O.sr_key(1337, t, 0), idx)
+        w_sr = O.bf16_bits_to_f64(O.f32_to_bf16_sr(w_sr - np.float32(1e-3), r)).astype(np.float32)
+        w_rn = O.bf16_bits_to_f64(O.f32_to_bf16_rne(w_rn - np.float32(1e-3))).astype(np.float32)
+    assert np.mean(w_rn.astype(np.float64) - 0.75) == 0.0
+    assert abs(np.mean(w_sr.astype(np.float64) - 0.75) - (-0.100)) < 5e-4
+
+
+# ---------------------------------------------------------------------------
+# int8 moments (section 2.3, Appendix B)
+# ---------------------------------------------------------------------------
+def test_int8_round_trip_bound():
+    """|q(x) - x| <= s/2 for every element of a block (Appendix B)."""
+    rng = np.random.default_rng(7)
+    x = (rng.standard_t(3, size=(64, 512)) * 1e-3).astype(np.float32)
+    q, s = O.quantize_signed(x, 128)
+    back = O.dequantize(q, s, 128)
+    half = np.repeat(s, 128, axis=1) / 2
+    assert np.all(np.abs(back.astype(np.float64) - x) <= half * (1 + 1e-6))
+    assert q.min() >= -127 and q.max() <= 127
+    # the absmax element of every block takes code +-127 exactly
+    xb = x.reshape(64, 4, 128)
+    qb = q.reshape(64, 4, 128)
+    arg = np.abs(xb).argmax(axis=2)
+    top = np.take_along_axis(qb, arg[:, :, None], axis=2)[:, :, 0]
+    assert np.all(np.abs(top) == 127)
+    v = np.abs(x)
+    qu, su = O.quantize_unsigned(v, 128)
+    backu = O.dequantize(qu, su, 128)
+    halfu = np.repeat(su, 128, axis=1) / 2
+    pos = v > 0
+    # positive values below half a step are floored to code 1 (one step s):
+    # their error is at most s, every other value is within s/2
+    lim = np.where(v < halfu, 2 * halfu, halfu)
+    assert np.all(np.abs(backu.astype(np.float64) - v)[pos] <= lim[pos] * (1 + 1e-6))
+
+
+def test_int8_exact_grid_values():
+    """Values on the quantisation grid come back exactly."""
+    s = np.float32(0.5)
+    codes = np.arange(-127, 128, dtype=np.int64)
+    x = np.zeros((1, 256), dtype=np.float32)
+    x[0, :255] = codes.astype(np.float32) * s
+    q, sc = O.quantize_signed(x, 256)
+    assert sc[0, 0] == np.float32(127 * 0.5 / 127)
+    np.testing.assert_array_equal(q[0, :255], codes)
+
+
+def test_uint8_reserved_zero():
+    """Code 0 is reserved for an exact zero: v == 0 <=> code 0; tiny positive
+    values are floored to code 1; an all-zero block has scale 0."""
+    v = np.zeros((3, 128), dtype=np.float32)
+    v[0, :] = np.linspace(0, 1, 128, dtype=np.float32)
+    v[1, 5] = 1e-30
+    v[1, 6] = 1.0
+    q, s = O.quantize_unsigned(v, 128)
+    assert np.all((q == 0) == (v == 0))
+    assert q[1, 5] == 1 and q[1, 6] == 255
+    assert s[2, 0] == 0 and np.all(q[2] == 0)
+    assert q[0, 127] == 255
+
+
+def test_int8_state_drift_bound_prop4():
+    """Proposition 4: with identical gradients the int8-stored first moment
+    stays within s/(2(1-b1)) of the exact one, and its RMS deviation is about
+    s/sqrt(12(1-b1^2)); same for v with b2."""
+    rng = np.random.default_rng(8)
+    R, C, steps = 8, 512, 200
+    b1, b2 = 0.9, 0.999
+    m_ex, v_ex = np.zeros((R, C)), np.zeros((R, C))
+    m_st = O.Stored("s8", np.zeros((R, C), np.int8), np.zeros((R, C // 128), np.float32))
+    v_st = O.Stored("u8", np.zeros((R, C), np.uint8), np.zeros((R, C // 128), np.float32))
+    W_st = O.Stored("f32", np.zeros((R, C), np.float32))
+    smax_m = np.zeros((R, C // 128))
+    smax_v = np.zeros((R, C // 128))
+    worst_m = worst_v = 0.0
+    devs, scales = [], []
+    hyp = O.Hyper(opt="adamw", lr=1e-3, beta1=b1, beta2=b2, eps=1e-8, weight_decay=0.0)
+    for t in range(1, steps + 1):
+        G = rng.normal(0, 1e-2, (R, C))
+        res = O.apply_step(G, W_st, m_st, v_st, hyp, t, 1337)
+        m_st, v_st = res["m"], res["v"]
+        m_ex = b1 * m_ex + (1 - b1) * G
+        v_ex = b2 * v_ex + (1 - b2) * G * G
+        smax_m = np.maximum(smax_m, m_st.scale)
+        smax_v = np.maximum(smax_v, v_st.scale)
+        dm = np.abs(O.decode(m_st) - m_ex)
+        dv = np.abs(O.decode(v_st) - v_ex)
+        worst_m = max(worst_m, np.max(dm / np.repeat(smax_m / (2 * (1 - b1)), 128, axis=1)))
+        worst_v = max(worst_v, np.max(dv / np.repeat(smax_v / (2 * (1 - b2)), 128, axis=1)))
+        if t > 50:
+            devs.append(O.decode(m_st) - m_ex)
+            scales.append(np.repeat(m_st.scale, 128, axis=1))
+    assert worst_m <= 1.0 + 1e-5
+    assert worst_v <= 1.0 + 1e-5
+    rms = math.sqrt(np.mean(np.square(devs)))
+    pred = math.sqrt(np.mean(np.square(scales))) / math.sqrt(12 * (1 - b1 ** 2))
+    assert 0.5 * pred < rms < 2.0 * pred
+
+
+# ---------------------------------------------------------------------------
+# Proposition 1 / Corollary 1(a): per-tile schedule == materialise-then-step
+# ---------------------------------------------------------------------------
+def _small_layer(N, K, BT, in_dtype, w_fmt, m_fmt, v_fmt, seed, block=32):
+    rng = np.random.default_rng(seed)
+    Xf = rng.normal(0, 1, (BT, K)).astype(np.float32)
+    dYf = (rng.normal(0, 1e-3, (BT, N))).astype(np.float32)
+    if in_dtype == "bf16":
+        X, dY = O.f32_to_bf16_rne(Xf), O.f32_to_bf16_rne(dYf)
+    else:
+        X, dY = Xf, dYf
+    W32 = rng.normal(0, 0.02, (N, K)).astype(np.float32)
+    W = O.Stored("f32", W32) if w_fmt == "f32" else O.Stored("bf16", O.f32_to_bf16_rne(W32))
+
+    def mk(fmt, signed):
+        x = (rng.normal(0, 1e-4, (N, K)) if signed else np.abs(rng.normal(0, 1e-6, (N, K)))).astype(np.float32)
+        if fmt is None:
+            return None
+        if fmt == "f32":
+            return O.Stored("f32", x)
+        if fmt == "bf16":
+            return O.Stored("bf16", O.f32_to_bf16_rne(x))
+        q, s = (O.quantize_signed if signed else O.quantize_unsigned)(x, block)
+        return O.Stored(fmt, q, s, block)
+
+    return X, dY, W, mk(m_fmt, True), mk(v_fmt, False)
+
+
+def _same(a, b):
+    if a is None:
+        assert b is None
+        return
+    np.testing.assert_array_equal(a.data, b.data)
+    if a.scale is not None:
+        np.testing.assert_array_equal(a.scale, b.scale)
+
+
+@pytest.mark.parametrize("acc", ["seq32", "seq64"])
+@pytest.mark.parametrize("fmts,opt", [
+    (("f32", "f32", "f32", "f32"), "adamw"),
+    (("bf16", "bf16", "f32", "f32"), "adamw"),
+    (("bf16", "bf16", "bf16", "bf16"), "adamw"),
+    (("bf16", "bf16", "s8", "u8"), "adamw"),
+    (("bf16", "bf16", "f32", None), "lion"),
+    (("bf16", "f32", "bf16", None), "sgdm"),
+])
+def test_tiled_schedule_equals_materialise_then_step(fmts, opt, acc):
+    in_dtype, w_fmt, m_fmt, v_fmt = fmts
+    int8 = m_fmt == "s8"
+    N, K, BT = (70, 192, 37) if int8 else (70, 45, 37)
+    X, dY, W, m, v = _small_layer(N, K, BT, in_dtype, w_fmt, m_fmt, v_fmt, seed=11)
+    hyp = O.Hyper(opt=opt, lr=1e-3 if opt != "lion" else 1e-4, beta1=0.9,
+                  beta2=0.999 if opt != "lion" else 0.99, round="sr")
+    ref = O.wgrad_step(X, dY, W, m, v, hyp, 10, 1337, order=acc)
+    rng = np.random.default_rng(12)
+    tilings = [(32, 32 if int8 else 16, 8), (64, 64, 13), (17, 32 if int8 else 7, 5)]
+    for tr, tc, tk in tilings:
+        ntiles = -(-N // tr) * -(-K // tc)
+        order = rng.permutation(ntiles)
+        got = O.step_tiled(X, dY, W, m, v, hyp, 10, 1337, tr, tc, tk, order, acc=acc)
+        _same(ref["W"], got["W"])
+        _same(ref["m"], got["m"])
+        _same(ref["v"], got["v"])
+
+
+def test_tiled_schedule_detects_a_dropped_chunk():
+    """The invariance test has teeth: skipping one token chunk changes W."""
+    X, dY, W, m, v = _small_layer(40, 40, 64, "bf16", "f32", "f32", "f32", seed=3)
+    hyp = O.Hyper()
+    ref = O.wgrad_step(X, dY, W, m, v, hyp, 1, 1, order="seq32")
+    bad = O.step_tiled(X[:48], dY[:48], W, m, v, hyp, 1, 1, 16, 16, 16, acc="seq32")
+    assert not np.array_equal(ref["m"].data, bad["m"].data)
+
+
+# ---------------------------------------------------------------------------
+# End-to-end composition on the fp32 single-layer workload
+# ---------------------------------------------------------------------------
+def test_fp32_layer_three_steps_match_torch():
+    """fp32 everywhere, BT 64, 256 x 256, AdamW t = 1..3 with fresh inputs:
+    the oracle equals torch (matmul + torch.optim.AdamW in float64, state
+    rounded to fp32 after each step) to fp32 rounding."""
+    import synth
+    spec = synth.LayerSpec(in_dtype="f32", w_fmt="f32", m_fmt="f32", v_fmt="f32")
+    st = synth.state(0, 256, 256, spec, v_zero=True)
+    W = O.Stored("f32", synth.host(st["W"]))
+    m = O.Stored("f32", synth.host(st["m"]))
+    v = O.Stored("f32", synth.host(st["v"]))
+    p = torch.tensor(W.data.astype(np.float64), requires_grad=True)
+    opt = torch.optim.AdamW([p], lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01)
+    hyp = O.Hyper(opt="adamw")
+    for t in (1, 2, 3):
+        X, dY = synth.activations(0, 64, 256, 256, t, in_dtype="f32", dy_std=0.01)
+        X, dY = synth.host(X), synth.host(dY)
+        res = O.wgrad_step(X, dY, W, m, v, hyp, t, 1337)
+        W, m, v = res["W"], res["m"], res["v"]
+        p.grad = torch.from_numpy(dY.astype(np.float64)).T @ torch.from_numpy(X.astype(np.float64))
+        opt.step()
+        with torch.no_grad():   # fp32 storage between steps
+            p.copy_(p.to(torch.float32).to(torch.float64))
+            for k in ("exp_avg", "exp_avg_sq"):
+                opt.state[p][k].copy_(opt.state[p][k].to(torch.float32).to(torch.float64))
+        np.testing.assert_allclose(W.data, p.detach().numpy().astype(np.float32), rtol=2e-7, atol=1e-12)
+        np.testing.assert_allclose(m.data, opt.state[p]["exp_avg"].numpy().astype(np.float32), rtol=2e-7, atol=1e-20)
+        np.testing.assert_allclose(v.data, opt.state[p]["exp_avg_sq"].numpy().astype(np.float32), rtol=2e-7, atol=1e-30)
