@@ -1,0 +1,184 @@
+"""Python binding of libforge, the gfx950 fused weight-gradient + optimizer step.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/forge.h``.  PyTorch is used for
+device memory and streams; tensors are passed by their device pointers.
+
+The library must have been built (``python backward_weight_gradient_amd/build.py``
+or ``__graft_entry__.build()``); importing this package without it raises
+``ImportError`` -- there is no fallback implementation.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libforge.so")
+
+FORGE_OK = 0
+STATUS_NAMES = ["FORGE_OK", "FORGE_E_NULL", "FORGE_E_SHAPE", "FORGE_E_DTYPE", "FORGE_E_ALIGN",
+                "FORGE_E_STEP", "FORGE_E_HYPER", "FORGE_E_ALIAS", "FORGE_E_UNSUPPORTED", "FORGE_E_HIP"]
+(FORGE_E_NULL, FORGE_E_SHAPE, FORGE_E_DTYPE, FORGE_E_ALIGN, FORGE_E_STEP, FORGE_E_HYPER,
+ FORGE_E_ALIAS, FORGE_E_UNSUPPORTED, FORGE_E_HIP) = range(1, 10)
+
+FORGE_F32, FORGE_BF16, FORGE_S8, FORGE_U8 = 0, 1, 2, 3
+FORGE_ADAMW, FORGE_LION, FORGE_SGDM = 0, 1, 2
+FORGE_ROUND_RNE, FORGE_ROUND_SR = 0, 1
+OPTIMIZERS = {"adamw": FORGE_ADAMW, "lion": FORGE_LION, "sgdm": FORGE_SGDM}
+ROUNDING = {"rne": FORGE_ROUND_RNE, "sr": FORGE_ROUND_SR}
+
+
+class ForgeError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {forge_status_str(code)} (code {code})")
+
+
+class forge_mat(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64), ("ld", ctypes.c_int64)]
+
+
+class forge_state(ctypes.Structure):
+    _fields_ = [("q", forge_mat), ("scale", ctypes.c_void_p), ("block", ctypes.c_int32)]
+
+
+class forge_hyper(ctypes.Structure):
+    _fields_ = [("opt", ctypes.c_int32), ("round", ctypes.c_int32), ("lr", ctypes.c_double),
+                ("beta1", ctypes.c_double), ("beta2", ctypes.c_double), ("eps", ctypes.c_double),
+                ("weight_decay", ctypes.c_double)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libforge.so is not built ({LIB_PATH}); run "
+                          "`python backward_weight_gradient_amd/build.py` first")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    st = ctypes.c_int
+    lib.forge_wgrad_step.argtypes = [P(forge_mat), P(forge_mat), P(forge_mat), P(forge_state), P(forge_state),
+                                     P(forge_hyper), ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p]
+    lib.forge_wgrad_step.restype = st
+    lib.forge_wgrad_check.argtypes = [P(forge_mat), P(forge_mat), P(forge_mat), P(forge_state), P(forge_state),
+                                      P(forge_hyper), ctypes.c_int64]
+    lib.forge_wgrad_check.restype = st
+    lib.forge_wgrad_unfused.argtypes = [P(forge_mat), P(forge_mat), P(forge_mat), P(forge_state), P(forge_state),
+                                        P(forge_hyper), ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p,
+                                        ctypes.c_int32, ctypes.c_void_p]
+    lib.forge_wgrad_unfused.restype = st
+    lib.forge_debug_sr_bf16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64,
+                                        ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p]
+    lib.forge_debug_sr_bf16.restype = st
+    lib.forge_status_str.argtypes = [ctypes.c_int]
+    lib.forge_status_str.restype = ctypes.c_char_p
+    lib.forge_version.argtypes = []
+    lib.forge_version.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+# ---------------------------------------------------------------------------
+# Struct builders
+# ---------------------------------------------------------------------------
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: FORGE_F32, torch.bfloat16: FORGE_BF16, torch.int8: FORGE_S8, torch.uint8: FORGE_U8}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported tensor dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def mat_raw(ptr: int, dtype: int, rows: int, cols: int, ld: Optional[int] = None) -> forge_mat:
+    """A forge_mat from a raw device address (no tensor)."""
+    return forge_mat(ptr or None, dtype, rows, cols, cols if ld is None else ld)
+
+
+def mat(t) -> forge_mat:
+    """A forge_mat describing a 2-D tensor whose rows are contiguous."""
+    if t.dim() != 2:
+        raise ValueError("expected a 2-D tensor")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError("rows must be contiguous (stride(1) == 1)")
+    ld = t.stride(0) if t.shape[0] > 1 else max(1, t.shape[1])
+    return forge_mat(t.data_ptr() or None, _dtype_code(t), t.shape[0], t.shape[1], ld)
+
+
+def state(t, scale=None, block: int = 0) -> forge_state:
+    """A forge_state: values (f32 / bf16) or int8 codes plus fp32 block scales."""
+    return forge_state(mat(t), (scale.data_ptr() or None) if scale is not None else None,
+                       block if scale is not None else 0)
+
+
+def hyper(opt: str = "adamw", lr: float = 1e-3, beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
+          weight_decay: float = 0.01, round: str = "sr") -> forge_hyper:
+    return forge_hyper(OPTIMIZERS[opt], ROUNDING[round], lr, beta1, beta2, eps, weight_decay)
+
+
+def current_stream() -> int:
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ref(x):
+    return ctypes.byref(x) if x is not None else None
+
+
+def _stream(stream):
+    return current_stream() if stream is None else stream
+
+
+# ---------------------------------------------------------------------------
+# Entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+def forge_status_str(code: int) -> str:
+    return lib.forge_status_str(code).decode()
+
+
+def forge_version() -> str:
+    return lib.forge_version().decode()
+
+
+def forge_wgrad_check(X: forge_mat, dY: forge_mat, W: forge_mat, m: Optional[forge_state],
+                      v: Optional[forge_state], h: forge_hyper, step: int) -> int:
+    return lib.forge_wgrad_check(_ref(X), _ref(dY), _ref(W), _ref(m), _ref(v), _ref(h), step)
+
+
+def forge_wgrad_step(X, dY, W, m, v, h: forge_hyper, step: int, seed: int, stream=None, check: bool = True) -> int:
+    """Fused dW = dY^T X + optimizer step, in place on W / m / v.
+
+    X, dY, W: tensors or forge_mat; m, v: forge_state (or None for v).
+    """
+    X = mat(X) if not isinstance(X, forge_mat) else X
+    dY = mat(dY) if not isinstance(dY, forge_mat) else dY
+    W = mat(W) if not isinstance(W, forge_mat) else W
+    rc = lib.forge_wgrad_step(_ref(X), _ref(dY), _ref(W), _ref(m), _ref(v), _ref(h), step, seed, _stream(stream))
+    if check and rc != FORGE_OK:
+        raise ForgeError(rc, "forge_wgrad_step")
+    return rc
+
+
+def forge_wgrad_unfused(X, dY, W, m, v, h: forge_hyper, step: int, seed: int, dW, stream=None,
+                        check: bool = True) -> int:
+    """Unfused baseline: G -> dW (the tensor's dtype, f32 or bf16), then the step."""
+    X = mat(X) if not isinstance(X, forge_mat) else X
+    dY = mat(dY) if not isinstance(dY, forge_mat) else dY
+    W = mat(W) if not isinstance(W, forge_mat) else W
+    rc = lib.forge_wgrad_unfused(_ref(X), _ref(dY), _ref(W), _ref(m), _ref(v), _ref(h), step, seed,
+                                 dW.data_ptr(), _dtype_code(dW), _stream(stream))
+    if check and rc != FORGE_OK:
+        raise ForgeError(rc, "forge_wgrad_unfused")
+    return rc
+
+
+def forge_debug_sr_bf16(inp, out, seed: int, step: int, tensor_id: int, stream=None, check: bool = True) -> int:
+    """Stochastic rounding of a float32 tensor into a bf16 tensor (test hook)."""
+    rc = lib.forge_debug_sr_bf16(inp.data_ptr(), out.data_ptr(), inp.numel(), seed, step, tensor_id,
+                                 _stream(stream))
+    if check and rc != FORGE_OK:
+        raise ForgeError(rc, "forge_debug_sr_bf16")
+    return rc

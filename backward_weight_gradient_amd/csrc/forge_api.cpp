@@ -1,0 +1,303 @@
+// Host side of libforge: argument validation, per-call scalars, dispatch.
+// Implements include/forge.h.
+
+#include "../../include/forge.h"
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "forge_internal.h"
+
+namespace {
+
+using namespace forge;
+
+constexpr uint32_t kGolden = 0x9E3779B9u;
+
+// MurmurHash3 32-bit finaliser (Appleby, public domain).
+uint32_t fmix32_host(uint32_t h) {
+  h ^= h >> 16;
+  h *= 0x85EBCA6Bu;
+  h ^= h >> 13;
+  h *= 0xC2B2AE35u;
+  h ^= h >> 16;
+  return h;
+}
+
+// Stochastic-rounding key of one stored tensor: the 64-bit step and seed are
+// folded in as four 32-bit words, each through the finaliser.
+uint32_t sr_key(uint64_t seed, uint64_t step, uint32_t tensor_id) {
+  uint32_t k = fmix32_host((uint32_t)(step >> 32) + kGolden * (tensor_id + 1u));
+  k = fmix32_host((uint32_t)step ^ k);
+  k = fmix32_host((uint32_t)(seed >> 32) ^ k);
+  k = fmix32_host((uint32_t)seed ^ k);
+  return k;
+}
+
+int elem_size(int dtype) {
+  switch (dtype) {
+    case FORGE_F32: return 4;
+    case FORGE_BF16: return 2;
+    case FORGE_S8:
+    case FORGE_U8: return 1;
+    default: return 0;
+  }
+}
+
+struct Range {
+  uintptr_t lo = 0, hi = 0;  // [lo, hi)
+  bool empty() const { return hi <= lo; }
+};
+
+Range mat_range(const forge_mat& m) {
+  Range r;
+  if (m.rows <= 0 || m.cols <= 0 || m.data == nullptr) return r;
+  const uint64_t n = (uint64_t)(m.rows - 1) * (uint64_t)m.ld + (uint64_t)m.cols;
+  r.lo = (uintptr_t)m.data;
+  r.hi = r.lo + (uintptr_t)(n * (uint64_t)elem_size(m.dtype));
+  return r;
+}
+
+Range raw_range(const void* p, uint64_t bytes) {
+  Range r;
+  if (p == nullptr || bytes == 0) return r;
+  r.lo = (uintptr_t)p;
+  r.hi = r.lo + (uintptr_t)bytes;
+  return r;
+}
+
+bool overlap(const Range& a, const Range& b) {
+  if (a.empty() || b.empty()) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned(const void* p, int bytes) { return ((uintptr_t)p % (uintptr_t)bytes) == 0; }
+
+bool finite(double x) { return std::isfinite(x); }
+
+// Shape / dtype / pointer checks of one matrix.
+forge_status check_mat(const forge_mat& m, int64_t rows, int64_t cols) {
+  if (m.rows != rows || m.cols != cols) return FORGE_E_SHAPE;
+  if (m.rows < 0 || m.cols < 0) return FORGE_E_SHAPE;
+  if (m.ld < m.cols || (m.cols > 0 && m.ld < 1)) return FORGE_E_SHAPE;
+  const int es = elem_size(m.dtype);
+  if (es == 0) return FORGE_E_DTYPE;
+  if (m.rows > 0 && m.cols > 0) {
+    if (m.data == nullptr) return FORGE_E_NULL;
+    if (!aligned(m.data, es)) return FORGE_E_ALIGN;
+  }
+  return FORGE_OK;
+}
+
+struct Plan {
+  int64_t BT = 0, N = 0, K = 0;
+  int in_fmt = -1, w_fmt = -1, m_fmt = -1, v_fmt = FMT_NONE;
+  int block = 0;
+  bool empty = false;  // N == 0 or K == 0: nothing to do
+};
+
+forge_status check_state(const forge_state& s, int64_t N, int64_t K, bool first, Plan& pl) {
+  forge_status st = check_mat(s.q, N, K);
+  if (st != FORGE_OK) return st;
+  const int dt = s.q.dtype;
+  const bool int8 = first ? dt == FORGE_S8 : dt == FORGE_U8;
+  if (!(dt == FORGE_F32 || dt == FORGE_BF16 || int8)) return FORGE_E_DTYPE;
+  if (int8) {
+    if (!(s.block == 32 || s.block == 64 || s.block == 128)) return FORGE_E_SHAPE;
+    if (K % s.block != 0) return FORGE_E_SHAPE;
+    if (N > 0 && K > 0) {
+      if (s.scale == nullptr) return FORGE_E_NULL;
+      if (!aligned(s.scale, 4)) return FORGE_E_ALIGN;
+    }
+    if (pl.block != 0 && pl.block != s.block) return FORGE_E_UNSUPPORTED;
+    pl.block = s.block;
+  } else if (s.scale != nullptr) {
+    return FORGE_E_DTYPE;  // a scale array only makes sense for int8 codes
+  }
+  return FORGE_OK;
+}
+
+forge_status validate(const forge_mat* X, const forge_mat* dY, const forge_mat* W, const forge_state* m,
+                      const forge_state* v, const forge_hyper* h, int64_t step, Plan& pl) {
+  if (!X || !dY || !W || !h) return FORGE_E_NULL;
+  // optimizer and which states it keeps
+  if (h->opt != FORGE_ADAMW && h->opt != FORGE_LION && h->opt != FORGE_SGDM) return FORGE_E_HYPER;
+  if (h->round != FORGE_ROUND_RNE && h->round != FORGE_ROUND_SR) return FORGE_E_HYPER;
+  if (!m) return FORGE_E_NULL;
+  if (h->opt == FORGE_ADAMW && !v) return FORGE_E_NULL;
+  if (h->opt != FORGE_ADAMW && v) return FORGE_E_UNSUPPORTED;
+  if (step < 1) return FORGE_E_STEP;
+  // hyper-parameters
+  if (!finite(h->lr) || !finite(h->beta1) || !finite(h->beta2) || !finite(h->eps) || !finite(h->weight_decay))
+    return FORGE_E_HYPER;
+  if (h->lr < 0 || h->weight_decay < 0) return FORGE_E_HYPER;
+  if (h->beta1 < 0 || h->beta1 >= 1) return FORGE_E_HYPER;
+  if (h->opt != FORGE_SGDM && (h->beta2 < 0 || h->beta2 >= 1)) return FORGE_E_HYPER;
+  if (h->opt == FORGE_ADAMW && !(h->eps > 0)) return FORGE_E_HYPER;
+  // shapes
+  pl.BT = X->rows;
+  pl.K = X->cols;
+  pl.N = dY->cols;
+  if (pl.BT < 0 || pl.N < 0 || pl.K < 0) return FORGE_E_SHAPE;
+  if (dY->rows != pl.BT) return FORGE_E_SHAPE;
+  forge_status st;
+  if ((st = check_mat(*X, pl.BT, pl.K)) != FORGE_OK) return st;
+  if ((st = check_mat(*dY, pl.BT, pl.N)) != FORGE_OK) return st;
+  if ((st = check_mat(*W, pl.N, pl.K)) != FORGE_OK) return st;
+  if (X->dtype != dY->dtype) return FORGE_E_DTYPE;
+  if (X->dtype != FORGE_F32 && X->dtype != FORGE_BF16) return FORGE_E_DTYPE;
+  if (W->dtype != FORGE_F32 && W->dtype != FORGE_BF16) return FORGE_E_DTYPE;
+  if ((st = check_state(*m, pl.N, pl.K, true, pl)) != FORGE_OK) return st;
+  if (v && (st = check_state(*v, pl.N, pl.K, false, pl)) != FORGE_OK) return st;
+  // size limits: 32-bit flat SR index and 32-bit tile / token counters
+  if ((uint64_t)pl.N * (uint64_t)pl.K >= (1ull << 32)) return FORGE_E_SHAPE;
+  if (pl.BT >= (1ll << 31) || pl.N >= (1ll << 31) || pl.K >= (1ll << 31)) return FORGE_E_SHAPE;
+  const int64_t tiles = ((pl.N + 127) / 128) * ((pl.K + 127) / 128);
+  if (tiles >= (1ll << 31)) return FORGE_E_SHAPE;
+  // aliasing: outputs must not overlap inputs or each other
+  Range outs[5] = {mat_range(*W), mat_range(m->q), v ? mat_range(v->q) : Range(),
+                   raw_range(m->scale, m->scale ? (uint64_t)pl.N * (uint64_t)(pl.K / (m->block ? m->block : 1)) * 4 : 0),
+                   (v && v->scale) ? raw_range(v->scale, (uint64_t)pl.N * (uint64_t)(pl.K / (v->block ? v->block : 1)) * 4)
+                                   : Range()};
+  const Range ins[2] = {mat_range(*X), mat_range(*dY)};
+  for (int i = 0; i < 5; ++i) {
+    for (int j = 0; j < 2; ++j)
+      if (overlap(outs[i], ins[j])) return FORGE_E_ALIAS;
+    for (int j = i + 1; j < 5; ++j)
+      if (overlap(outs[i], outs[j])) return FORGE_E_ALIAS;
+  }
+  pl.in_fmt = X->dtype;
+  pl.w_fmt = W->dtype;
+  pl.m_fmt = m->q.dtype;
+  pl.v_fmt = v ? v->q.dtype : FMT_NONE;
+  if (!combo_supported(pl.in_fmt, pl.w_fmt, h->opt, pl.m_fmt, pl.v_fmt)) return FORGE_E_UNSUPPORTED;
+  pl.empty = (pl.N == 0 || pl.K == 0);
+  return FORGE_OK;
+}
+
+bool vec_ok(const void* p, int64_t ld, int elems, int es) {
+  return p == nullptr || (aligned(p, elems * es) && (ld % elems) == 0);
+}
+
+KArgs make_args(const forge_mat* X, const forge_mat* dY, forge_mat* W, forge_state* m, forge_state* v,
+                const forge_hyper* h, int64_t step, uint64_t seed, const Plan& pl) {
+  KArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.X = X->data; a.ldx = X->ld;
+  a.dY = dY->data; a.lddy = dY->ld;
+  a.W = W->data; a.ldw = W->ld;
+  a.m = m->q.data; a.ldm = m->q.ld; a.ms = m->scale;
+  if (v) { a.v = v->q.data; a.ldv = v->q.ld; a.vs = v->scale; }
+  a.BT = (int32_t)pl.BT; a.N = (int32_t)pl.N; a.K = (int32_t)pl.K;
+  a.tiles_n = (int32_t)((pl.N + 127) / 128);
+  a.tiles_k = (int32_t)((pl.K + 127) / 128);
+  a.block = pl.block ? pl.block : 128;
+  // 16-byte vector loads of 8 bf16 / 4 fp32 activations
+  const int ies = elem_size(pl.in_fmt), ivec = 16 / ies;
+  a.vec_in = (vec_ok(X->data, X->ld, ivec, ies) && vec_ok(dY->data, dY->ld, ivec, ies)) ? 1 : 0;
+  // 8-element state accesses
+  bool vs = vec_ok(W->data, W->ld, 8, elem_size(pl.w_fmt)) && vec_ok(m->q.data, m->q.ld, 8, elem_size(pl.m_fmt));
+  if (v) vs = vs && vec_ok(v->q.data, v->q.ld, 8, elem_size(pl.v_fmt));
+  // fp32 rows are read as two 16-byte halves
+  if (pl.w_fmt == FORGE_F32) vs = vs && aligned(W->data, 16);
+  a.vec_state = vs ? 1 : 0;
+  // scalars, in double, rounded once
+  const double lr = h->lr, b1 = h->beta1, b2 = h->beta2, wd = h->weight_decay;
+  EpiConst& c = a.c;
+  c.lr = (float)lr;
+  c.b1 = (float)b1;
+  c.b2 = (float)b2;
+  c.omb1 = (float)(1.0 - b1);
+  c.omb2 = (float)(1.0 - b2);
+  c.eps = (float)h->eps;
+  c.decay = (float)(1.0 - lr * wd);
+  c.wd = (float)wd;
+  const double t = (double)step;
+  c.bc1 = (float)(1.0 / (1.0 - std::pow(b1, t)));
+  c.bc2s = (h->opt == FORGE_ADAMW) ? (float)(1.0 / std::sqrt(1.0 - std::pow(b2, t))) : 1.0f;
+  if (h->opt != FORGE_ADAMW) c.bc1 = 1.0f;
+  c.keyW = sr_key(seed, (uint64_t)step, 0);
+  c.keyM = sr_key(seed, (uint64_t)step, 1);
+  c.keyV = sr_key(seed, (uint64_t)step, 2);
+  c.sr = h->round == FORGE_ROUND_SR ? 1 : 0;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+forge_status forge_wgrad_check(const forge_mat* X, const forge_mat* dY, const forge_mat* W, const forge_state* m,
+                               const forge_state* v, const forge_hyper* h, int64_t step) {
+  Plan pl;
+  return validate(X, dY, W, m, v, h, step, pl);
+}
+
+forge_status forge_wgrad_step(const forge_mat* X, const forge_mat* dY, forge_mat* W, forge_state* m, forge_state* v,
+                              const forge_hyper* h, int64_t step, uint64_t seed, void* stream) {
+  Plan pl;
+  forge_status st = validate(X, dY, W, m, v, h, step, pl);
+  if (st != FORGE_OK || pl.empty) return st;
+  const KArgs a = make_args(X, dY, W, m, v, h, step, seed, pl);
+  hipError_t e = launch_fused(a, pl.in_fmt, pl.w_fmt, h->opt, pl.m_fmt, pl.v_fmt, (hipStream_t)stream);
+  return e == hipSuccess ? FORGE_OK : FORGE_E_HIP;
+}
+
+forge_status forge_wgrad_unfused(const forge_mat* X, const forge_mat* dY, forge_mat* W, forge_state* m,
+                                 forge_state* v, const forge_hyper* h, int64_t step, uint64_t seed, void* dW,
+                                 int32_t dW_dtype, void* stream) {
+  Plan pl;
+  forge_status st = validate(X, dY, W, m, v, h, step, pl);
+  if (st != FORGE_OK) return st;
+  if (dW_dtype != FORGE_F32 && dW_dtype != FORGE_BF16) return FORGE_E_DTYPE;
+  if (pl.empty) return FORGE_OK;
+  if (dW == nullptr) return FORGE_E_NULL;
+  if (!aligned(dW, 16)) return FORGE_E_ALIGN;
+  const Range ws = raw_range(dW, (uint64_t)pl.N * (uint64_t)pl.K * (uint64_t)elem_size(dW_dtype));
+  const Range others[7] = {
+      mat_range(*X), mat_range(*dY), mat_range(*W), mat_range(m->q), v ? mat_range(v->q) : Range(),
+      raw_range(m->scale, m->scale ? (uint64_t)pl.N * (uint64_t)(pl.K / pl.block) * 4 : 0),
+      (v && v->scale) ? raw_range(v->scale, (uint64_t)pl.N * (uint64_t)(pl.K / pl.block) * 4) : Range()};
+  for (const Range& r : others)
+    if (overlap(ws, r)) return FORGE_E_ALIAS;
+  KArgs a = make_args(X, dY, W, m, v, h, step, seed, pl);
+  a.dW = dW;
+  a.dw_fmt = dW_dtype == FORGE_F32 ? FMT_F32 : FMT_BF16;
+  hipError_t e = launch_gemm(a, pl.in_fmt, (hipStream_t)stream);
+  if (e == hipSuccess) e = launch_step(a, pl.w_fmt, h->opt, pl.m_fmt, pl.v_fmt, (hipStream_t)stream);
+  return e == hipSuccess ? FORGE_OK : FORGE_E_HIP;
+}
+
+forge_status forge_debug_sr_bf16(const float* in, uint16_t* out, int64_t n, uint64_t seed, int64_t step,
+                                 uint32_t tensor_id, void* stream) {
+  if (n < 0 || (uint64_t)n >= (1ull << 32)) return FORGE_E_SHAPE;
+  if (step < 1) return FORGE_E_STEP;
+  if (n == 0) return FORGE_OK;
+  if (!in || !out) return FORGE_E_NULL;
+  if (!aligned(in, 4) || !aligned(out, 2)) return FORGE_E_ALIGN;
+  if (overlap(raw_range(in, (uint64_t)n * 4), raw_range(out, (uint64_t)n * 2))) return FORGE_E_ALIAS;
+  const uint32_t key = sr_key(seed, (uint64_t)step, tensor_id);
+  hipError_t e = launch_debug_sr(in, out, (uint32_t)n, key, (hipStream_t)stream);
+  return e == hipSuccess ? FORGE_OK : FORGE_E_HIP;
+}
+
+const char* forge_status_str(forge_status s) {
+  switch (s) {
+    case FORGE_OK: return "FORGE_OK";
+    case FORGE_E_NULL: return "FORGE_E_NULL: a required pointer is NULL";
+    case FORGE_E_SHAPE: return "FORGE_E_SHAPE: shapes disagree or exceed a limit";
+    case FORGE_E_DTYPE: return "FORGE_E_DTYPE: dtype not allowed here";
+    case FORGE_E_ALIGN: return "FORGE_E_ALIGN: misaligned pointer";
+    case FORGE_E_STEP: return "FORGE_E_STEP: step must be >= 1";
+    case FORGE_E_HYPER: return "FORGE_E_HYPER: invalid optimizer or hyper-parameter";
+    case FORGE_E_ALIAS: return "FORGE_E_ALIAS: an output overlaps another buffer";
+    case FORGE_E_UNSUPPORTED: return "FORGE_E_UNSUPPORTED: combination not implemented";
+    case FORGE_E_HIP: return "FORGE_E_HIP: HIP launch error";
+  }
+  return "unknown forge_status";
+}
+
+const char* forge_version(void) { return "forge-mi355x 0.1.0 (gfx950)"; }
+
+}  // extern "C"

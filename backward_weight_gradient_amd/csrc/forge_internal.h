@@ -1,0 +1,60 @@
+// Internal interface between the host API (forge_api.cpp) and the gfx950
+// kernels (forge_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <cstdint>
+#include <hip/hip_runtime.h>
+
+namespace forge {
+
+enum Fmt : int { FMT_NONE = -1, FMT_F32 = 0, FMT_BF16 = 1, FMT_S8 = 2, FMT_U8 = 3 };
+enum Opt : int { OPT_ADAMW = 0, OPT_LION = 1, OPT_SGDM = 2 };
+
+// Scalars of the element-wise step, computed once per call on the host in
+// double precision and rounded once to fp32.
+struct EpiConst {
+  float lr;        // eta
+  float b1, b2;    // beta1 (SGD-m: momentum), beta2
+  float omb1;      // 1 - beta1
+  float omb2;      // 1 - beta2
+  float eps;
+  float decay;     // 1 - eta * lambda   (decoupled decay: AdamW, Lion)
+  float wd;        // lambda             (L2 decay: SGD-m)
+  float bc1;       // 1 / (1 - beta1^t)
+  float bc2s;      // 1 / sqrt(1 - beta2^t)
+  uint32_t keyW, keyM, keyV;  // stochastic-rounding keys of the three tensors
+  int32_t sr;      // 1: stochastic rounding of bf16 stores, 0: round to nearest even
+};
+
+// Everything a launch needs.  Pointers are device pointers; leading
+// dimensions are in elements.
+struct KArgs {
+  const void* X;  int64_t ldx;    // [BT, K]
+  const void* dY; int64_t lddy;   // [BT, N]
+  void* W;  int64_t ldw;          // [N, K]
+  void* m;  int64_t ldm; float* ms;   // state 1 (+ int8 scales [N, K/block])
+  void* v;  int64_t ldv; float* vs;   // state 2 (+ int8 scales)
+  void* dW;                       // unfused workspace [N, K], ld = K
+  int32_t dw_fmt;                 // FMT_F32 / FMT_BF16 for dW
+  int32_t BT, N, K;
+  int32_t tiles_n, tiles_k;       // ceil(N/128), ceil(K/128)
+  int32_t block;                  // int8 block length (32, 64, 128)
+  int32_t vec_in;                 // X / dY rows allow 16-byte vector loads
+  int32_t vec_state;              // W / m / v rows allow 8-element vector access
+  EpiConst c;
+};
+
+bool combo_supported(int in_fmt, int w_fmt, int opt, int m_fmt, int v_fmt);
+
+// Fused weight-gradient + step: one workgroup per 128 x 128 tile of W.
+hipError_t launch_fused(const KArgs& a, int in_fmt, int w_fmt, int opt, int m_fmt, int v_fmt,
+                        hipStream_t stream);
+// Unfused baseline, phase 1: G tiles -> a.dW (a.dw_fmt).
+hipError_t launch_gemm(const KArgs& a, int in_fmt, hipStream_t stream);
+// Unfused baseline, phase 2: the same step, reading G from a.dW.
+hipError_t launch_step(const KArgs& a, int w_fmt, int opt, int m_fmt, int v_fmt, hipStream_t stream);
+// Stochastic rounding of n floats with one key, element i using flat index i.
+hipError_t launch_debug_sr(const float* in, uint16_t* out, uint32_t n, uint32_t key,
+                           hipStream_t stream);
+
+}  // namespace forge

@@ -1,0 +1,183 @@
+/*
+ * forge.h -- C ABI of libforge: the weight gradient of a linear layer fused
+ * with an element-wise optimizer step, for AMD MI355X (gfx950).
+ *
+ * What it computes (FORGE paper, arXiv 2606.22932 -- "the paper" below):
+ *   for a linear layer Y = X W^T (section 2.1, Eq. 2) with
+ *     X  [BT, K]  saved input activations (K = D_in),
+ *     dY [BT, N]  upstream gradient dL/dY  (N = D_out),
+ *     W  [N, K]   weight, nn.Linear layout,
+ *   the weight gradient G = dY^T X, G[p,q] = sum_t dY[t,p] X[t,q]
+ *   (section 2.1, Eq. 3; Appendix A, "Setup"), reduced over the token axis
+ *   BT in fp32, one 128 x 128 tile of G at a time (section 2.2, Eq. 5), and
+ *   an element-wise optimizer step (Appendix A, Definition 1) applied to each
+ *   tile in registers as soon as it is complete (Algorithm 1, Phase 2).
+ *   Only W and the optimizer state are written back (Algorithm 1, Phase 3);
+ *   G itself never reaches device memory.
+ *
+ * Conventions shared by every entry point
+ *   - All matrix data pointers are DEVICE pointers owned by the caller.  The
+ *     library never allocates, frees or retains them (forge_wgrad_unfused
+ *     writes into a caller-provided workspace).
+ *   - Matrices are row-major; `ld` is the leading dimension in elements
+ *     (ld >= cols).  Flat indices used by stochastic rounding are the logical
+ *     row-major index p*K + q, independent of ld.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream) and return after the kernels are enqueued.  W, m, v and the
+ *     int8 scales are updated in place.
+ *   - Argument validation is synchronous and host-only.  On any error code
+ *     other than FORGE_E_HIP nothing has been enqueued and nothing modified.
+ *   - No exception crosses the ABI.  The library keeps no mutable global
+ *     state; calls on distinct streams may run concurrently on disjoint
+ *     buffers.
+ *   - Precondition the library cannot check (paper, Appendix A, Remark 1):
+ *     the caller has already computed the input gradient dX = dY W from the
+ *     pre-update W; a weight with more than one gradient consumer in a step
+ *     (tied embeddings, expert-parallel experts) must not be stepped here.
+ *   - Precondition of the fused schedule: one gradient per step (no
+ *     accumulation across micro-batches) and no global gradient-norm clip.
+ */
+#ifndef FORGE_H
+#define FORGE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FORGE_OK = 0,
+  FORGE_E_NULL = 1,        /* a required pointer (struct or data) is NULL           */
+  FORGE_E_SHAPE = 2,       /* shapes disagree, ld < cols, or a size limit is exceeded */
+  FORGE_E_DTYPE = 3,       /* a dtype is not allowed in that position               */
+  FORGE_E_ALIGN = 4,       /* a data pointer is not aligned to its element size     */
+  FORGE_E_STEP = 5,        /* step < 1                                              */
+  FORGE_E_HYPER = 6,       /* a hyper-parameter is non-finite or out of range       */
+  FORGE_E_ALIAS = 7,       /* an output buffer overlaps an input or another output  */
+  FORGE_E_UNSUPPORTED = 8, /* a valid combination this build does not implement     */
+  FORGE_E_HIP = 9          /* the HIP runtime reported an error at launch           */
+} forge_status;
+
+typedef enum { FORGE_F32 = 0, FORGE_BF16 = 1, FORGE_S8 = 2, FORGE_U8 = 3 } forge_dtype;
+
+/* Optimizers (paper, Appendix N, "fully fused" families). */
+typedef enum {
+  FORGE_ADAMW = 0, /* Algorithm 1 Phase 2: bias correction, decoupled decay; needs m and v */
+  FORGE_LION = 1,  /* sign of the interpolated momentum (Chen et al. 2023); needs m only   */
+  FORGE_SGDM = 2   /* SGD with momentum, PyTorch semantics (coupled L2 decay, dampening 0,
+                      no Nesterov), momentum = beta1; needs m (the momentum buffer) only   */
+} forge_optim;
+
+/* Rounding of every bf16 store (paper, Appendix C). */
+typedef enum {
+  FORGE_ROUND_RNE = 0, /* round to nearest, ties to even                                 */
+  FORGE_ROUND_SR = 1   /* stochastic rounding from a counter-based hash of
+                          (seed, step, tensor, flat index)                               */
+} forge_round;
+
+typedef struct {
+  void* data;     /* device pointer                                   */
+  int32_t dtype;  /* forge_dtype                                      */
+  int64_t rows;
+  int64_t cols;
+  int64_t ld;     /* leading dimension in elements, >= cols           */
+} forge_mat;
+
+/* One optimizer state tensor.  F32 / BF16: values in q.  S8 (first moment)
+ * / U8 (second moment): codes in q plus one fp32 scale per `block`
+ * consecutive elements of a row, `scale` being a dense row-major
+ * [rows, cols / block] fp32 device array.  Stored value = code * scale.
+ * S8 codes are symmetric in -127..127 (scale = absmax / 127); U8 codes
+ * reserve 0 for an exact zero and use 1..255 for positive values
+ * (scale = absmax / 255), which keeps the second moment away from zero
+ * (paper, section 2.3 and Appendix B). */
+typedef struct {
+  forge_mat q;
+  float* scale;   /* S8 / U8 only, else NULL               */
+  int32_t block;  /* S8 / U8 only: 32, 64 or 128, else 0   */
+} forge_state;
+
+typedef struct {
+  int32_t opt;    /* forge_optim */
+  int32_t round;  /* forge_round */
+  double lr;           /* eta                                         */
+  double beta1;        /* AdamW / Lion beta1; SGD-m momentum          */
+  double beta2;        /* AdamW / Lion beta2; ignored by SGD-m        */
+  double eps;          /* AdamW only                                  */
+  double weight_decay; /* lambda: decoupled (AdamW, Lion), L2 (SGD-m) */
+} forge_hyper;
+
+/*
+ * forge_wgrad_step -- the fused hot path.
+ *
+ * X  : [BT, K], dtype BF16 or F32.      dY : [BT, N], same dtype as X.
+ * W  : [N, K], BF16 or F32, updated in place.
+ * m  : [N, K] state, F32 / BF16 / S8.    v : [N, K] state, F32 / BF16 / U8,
+ *      AdamW only (must be NULL for Lion and SGD-m).
+ * h  : optimizer and hyper-parameters.  step: the 1-based global step t,
+ *      used by the AdamW bias correction 1/(1 - beta^t) and by the SR key.
+ * seed: 64-bit stochastic-rounding seed.
+ *
+ * Supported combinations: X/dY in {BF16, F32} x W in {BF16, F32} x
+ *   AdamW (m, v) in {(F32, F32), (BF16, BF16), (S8, U8)} or
+ *   Lion / SGD-m m in {F32, BF16, S8}.
+ * Int8 states need K % block == 0.  N * K must be < 2^32 (flat SR index).
+ * BT may be 0 (G = 0: the step still applies decay / momentum).
+ * N == 0 or K == 0 is a no-op.
+ *
+ * Errors: FORGE_E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_STEP, E_HYPER,
+ * E_ALIAS, E_UNSUPPORTED (nothing enqueued) or E_HIP (launch failed).
+ */
+forge_status forge_wgrad_step(const forge_mat* X, const forge_mat* dY, forge_mat* W,
+                              forge_state* m, forge_state* v, const forge_hyper* h,
+                              int64_t step, uint64_t seed, void* stream);
+
+/*
+ * forge_wgrad_check -- the validation of forge_wgrad_step alone: same
+ * arguments, same return codes, no device call at all (usable on a host
+ * without a GPU).
+ */
+forge_status forge_wgrad_check(const forge_mat* X, const forge_mat* dY, const forge_mat* W,
+                               const forge_state* m, const forge_state* v, const forge_hyper* h,
+                               int64_t step);
+
+/*
+ * forge_wgrad_unfused -- the two-phase baseline the fused path replaces
+ * (paper, section 2.1: the gradient is stored in device memory, then the
+ * optimizer reads it back).  Kernel 1 computes G with the same tiles and
+ * accumulation order as forge_wgrad_step and writes it to `dW` ([N, K],
+ * leading dimension K) as F32 or BF16 (round to nearest even); kernel 2
+ * applies the same optimizer step reading G back.  With dW_dtype == F32 the
+ * results are bit-identical to forge_wgrad_step (paper, Corollary 1(a)).
+ * dW: caller-owned device workspace of N*K elements of dW_dtype, must not
+ * overlap any other argument.  Other arguments and errors as
+ * forge_wgrad_step.
+ */
+forge_status forge_wgrad_unfused(const forge_mat* X, const forge_mat* dY, forge_mat* W,
+                                 forge_state* m, forge_state* v, const forge_hyper* h,
+                                 int64_t step, uint64_t seed, void* dW, int32_t dW_dtype,
+                                 void* stream);
+
+/*
+ * forge_debug_sr_bf16 -- test hook: rounds n fp32 values to bf16 with the
+ * same device stochastic-rounding function and key derivation the step
+ * kernels use for tensor `tensor_id` (0 = W, 1 = m, 2 = v), element i taking
+ * flat index i.  in: n floats, out: n uint16 bf16 patterns, both device
+ * pointers.  Errors: E_NULL, E_SHAPE (n < 0 or n >= 2^32), E_ALIAS,
+ * E_STEP, E_HIP.
+ */
+forge_status forge_debug_sr_bf16(const float* in, uint16_t* out, int64_t n, uint64_t seed,
+                                 int64_t step, uint32_t tensor_id, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* forge_status_str(forge_status s);
+
+/* Library version string (static). */
+const char* forge_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FORGE_H */

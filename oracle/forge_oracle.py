@@ -410,9 +410,15 @@ def encode(x64: np.ndarray, fmt: str, *, round: str = "sr", key: int = 0,
 # --------------------------------------------------------------------------
 def apply_step(G: np.ndarray, W: Stored, m: Optional[Stored], v: Optional[Stored],
                hyper: Hyper, step: int, seed: int, rows=None, c0: int = 0,
-               c1: Optional[int] = None) -> dict:
+               c1: Optional[int] = None, flat: Optional[np.ndarray] = None) -> dict:
     """Apply the optimizer to the sub-block rows x [c0, c1) given its fp64
     gradient G, and store the results.
+
+    ``flat`` optionally gives the flat index p*K + q of every element of the
+    sub-block in the logical [N, K] weight (used only to draw the SR bits);
+    by default it is computed from ``rows``, the column range and the stored
+    width, i.e. the arrays passed in are the whole layer.  Pass it when the
+    arrays hold a gathered subset of the layer's rows.
 
     Returns a dict with the stored sub-blocks ``W``, ``m``, ``v`` (``None``
     where the optimizer keeps no such state) and ``pre``: the fp64 values
@@ -438,7 +444,8 @@ def apply_step(G: np.ndarray, W: Stored, m: Optional[Stored], v: Optional[Stored
         v1 = None
     else:
         raise ValueError(f"unknown optimizer {h.opt!r}")
-    flat = rows.astype(np.uint64)[:, None] * np.uint64(K) + cols.astype(np.uint64)[None, :]
+    if flat is None:
+        flat = rows.astype(np.uint64)[:, None] * np.uint64(K) + cols.astype(np.uint64)[None, :]
 
     def store(x, st, tid):
         if st is None:
@@ -452,14 +459,14 @@ def apply_step(G: np.ndarray, W: Stored, m: Optional[Stored], v: Optional[Stored
 
 def wgrad_step(X, dY, W: Stored, m: Optional[Stored], v: Optional[Stored], hyper: Hyper,
                step: int, seed: int, rows=None, c0: int = 0, c1: Optional[int] = None,
-               order: str = "blas") -> dict:
+               order: str = "blas", flat: Optional[np.ndarray] = None) -> dict:
     """Materialise-then-step on the sub-block rows x [c0, c1): G from Eq. 3,
-    then :func:`apply_step`.  With the defaults this is the whole layer.
-    The result dict also carries ``G`` (fp64)."""
+    then :func:`apply_step` (``flat`` as there).  With the defaults this is
+    the whole layer.  The result dict also carries ``G`` (fp64)."""
     K = W.data.shape[1]
     c1 = K if c1 is None else c1
     G = weight_grad(X, dY, rows, np.arange(c0, c1), order)
-    out = apply_step(G, W, m, v, hyper, step, seed, rows, c0, c1)
+    out = apply_step(G, W, m, v, hyper, step, seed, rows, c0, c1, flat)
     out["G"] = G
     return out
 

@@ -1,0 +1,281 @@
+"""Shared helpers of the GPU parity tests.
+
+A ``Layer`` holds one linear layer's tensors on the GPU, drawn from the seeded
+generators in ``synth``; ``snapshot`` copies what the oracle needs to the host
+*before* the in-place GPU step; ``check_against_oracle`` runs the oracle on
+the same inputs and compares every output element by element:
+
+* fp32 outputs: ``|got - ref| <= 1e-5 S``, or ``got`` inside the hull of
+  the optimizer evaluated over ``G +- E`` (E the forward error bound of an
+  fp32 reduction in any order -- the only discrepancy Corollary 1(b) of the
+  FORGE paper allows), widened by ``1e-5 S``; S is the larger of |ref| and
+  the magnitude of the terms the output is summed from (the step evaluated
+  on absolute values), so that an output which cancels -- a weight that the
+  update drives through zero -- is judged against its operands' scale;
+* bf16 outputs: within one bf16 ULP (+ 1e-5 S) of that hull, and bit-identical to the
+  oracle's stored pattern for at least 99.9% of the elements (the SR bits
+  come from the same counter-based hash on both sides);
+* int8 codes: within one code of the oracle's, at least 99% identical;
+  scales within 1e-5 relative or inside the hull of the block absmax.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+import torch
+
+import backward_weight_gradient_amd as F
+import oracle as O
+import synth
+
+FMT_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "s8": torch.int8, "u8": torch.uint8}
+
+
+@dataclass
+class Layer:
+    N: int
+    K: int
+    BT: int
+    spec: synth.LayerSpec
+    X: torch.Tensor
+    dY: torch.Tensor
+    W: torch.Tensor
+    m: Optional[torch.Tensor]
+    v: Optional[torch.Tensor]
+    ms: Optional[torch.Tensor] = None
+    vs: Optional[torch.Tensor] = None
+
+    def forge_m(self):
+        return F.state(self.m, self.ms, self.spec.block) if self.ms is not None else F.state(self.m)
+
+    def forge_v(self):
+        if self.v is None:
+            return None
+        return F.state(self.v, self.vs, self.spec.block) if self.vs is not None else F.state(self.v)
+
+    def clone(self) -> "Layer":
+        c = lambda t: None if t is None else t.clone()
+        return Layer(self.N, self.K, self.BT, self.spec, self.X, self.dY, c(self.W), c(self.m), c(self.v),
+                     c(self.ms), c(self.vs))
+
+
+def make_layer(cfg: int, N: int, K: int, BT: int, step: int, spec: synth.LayerSpec, *, device="cuda",
+               gen_device="cpu", x_std=1.0, dy_std=1e-3, outlier_p=0.0, v_zero=False, w_std=0.02,
+               v_init="random", extra=0) -> Layer:
+    """Seeded layer on `device`.  Small layers are drawn on the CPU and moved;
+    large ones directly on the GPU (gen_device="cuda").  With int8 v and
+    v_init="quantized", v starts as the oracle's quantisation of
+    |N(0, 1e-6)| (the same codes and scales go to both sides)."""
+    X, dY = synth.activations(cfg, BT, N, K, step, in_dtype=spec.in_dtype, x_std=x_std, dy_std=dy_std,
+                              outlier_p=outlier_p, device=gen_device, extra=extra)
+    st = synth.state(cfg, N, K, spec, w_std=w_std, v_zero=v_zero, device=gen_device, extra=extra)
+    if spec.v_fmt == "u8" and v_init == "quantized" and not v_zero:
+        v32 = synth.normal((N, K), 1e-6, "cpu", cfg, 0, synth.T_V, extra).abs().numpy()
+        q, s = O.quantize_unsigned(v32, spec.block)
+        st["v"], st["v_scale"] = torch.from_numpy(q), torch.from_numpy(s)
+    mv = lambda t: None if t is None else t.to(device)
+    return Layer(N, K, BT, spec, mv(X), mv(dY), mv(st["W"]), mv(st["m"]), mv(st["v"]), mv(st["m_scale"]),
+                 mv(st["v_scale"]))
+
+
+def run_fused(L: Layer, h, step: int, seed: int):
+    F.forge_wgrad_step(L.X, L.dY, L.W, L.forge_m(), L.forge_v(), h, step, seed)
+
+
+def run_unfused(L: Layer, h, step: int, seed: int, dw_dtype=torch.float32):
+    dW = torch.empty((L.N, L.K), device=L.W.device, dtype=dw_dtype)
+    F.forge_wgrad_unfused(L.X, L.dY, L.W, L.forge_m(), L.forge_v(), h, step, seed, dW)
+    return dW
+
+
+def oracle_hyper(h) -> O.Hyper:
+    inv_opt = {v: k for k, v in F.OPTIMIZERS.items()}
+    inv_round = {v: k for k, v in F.ROUNDING.items()}
+    return O.Hyper(opt=inv_opt[h.opt], lr=h.lr, beta1=h.beta1, beta2=h.beta2, eps=h.eps,
+                   weight_decay=h.weight_decay, round=inv_round[h.round])
+
+
+# ---------------------------------------------------------------------------
+# Host snapshots
+# ---------------------------------------------------------------------------
+@dataclass
+class Snap:
+    """Host copies of the rows `rows` (global indices) of a layer, and of the
+    columns of dY those rows need, taken before a step."""
+    rows: np.ndarray
+    X: np.ndarray
+    dY: np.ndarray
+    W: O.Stored
+    m: Optional[O.Stored]
+    v: Optional[O.Stored]
+
+
+def _stored(t, fmt, scale, block, rows):
+    if t is None:
+        return None
+    idx = torch.as_tensor(rows, device=t.device, dtype=torch.long)
+    data = synth.host(t.index_select(0, idx))
+    sc = None if scale is None else scale.index_select(0, idx).cpu().numpy()
+    return O.Stored(fmt, data, sc, block)
+
+
+def snapshot(L: Layer, rows=None) -> Snap:
+    rows = np.arange(L.N) if rows is None else np.asarray(rows)
+    idx = torch.as_tensor(rows, device=L.dY.device, dtype=torch.long)
+    s = L.spec
+    return Snap(rows=rows, X=synth.host(L.X), dY=synth.host(L.dY.index_select(1, idx)),
+                W=_stored(L.W, s.w_fmt, None, s.block, rows),
+                m=_stored(L.m, s.m_fmt, L.ms, s.block, rows),
+                v=_stored(L.v, s.v_fmt, L.vs, s.block, rows))
+
+
+# ---------------------------------------------------------------------------
+# Comparison
+# ---------------------------------------------------------------------------
+def _bf16_ulp(x: np.ndarray) -> np.ndarray:
+    ax = np.abs(x)
+    ax = np.where(ax < 2.0 ** -126, 2.0 ** -126, ax)
+    return 2.0 ** (np.floor(np.log2(ax)) - 7)
+
+
+@dataclass
+class Report:
+    checked: int = 0
+    clause2: dict = field(default_factory=dict)     # fp32 elements passing only via the hull
+    exact_frac: dict = field(default_factory=dict)  # bf16 / int8 bit-exact fractions
+    failures: list = field(default_factory=list)
+
+    def ok(self):
+        return not self.failures
+
+
+def _hull(snap: Snap, hyp: O.Hyper, step: int, seed: int, c0: int, c1: int, K: int):
+    rows_local = np.arange(len(snap.rows))
+    cols = np.arange(c0, c1)
+    G = O.weight_grad(snap.X, snap.dY, rows_local, cols)
+    E = O.grad_error_bound(snap.X, snap.dY, rows_local, cols)
+    flat = snap.rows.astype(np.uint64)[:, None] * np.uint64(K) + cols.astype(np.uint64)[None, :]
+    ref = O.apply_step(G, snap.W, snap.m, snap.v, hyp, step, seed, rows_local, c0, c1, flat)
+    lo = {k: v.copy() for k, v in ref["pre"].items() if v is not None}
+    hi = {k: v.copy() for k, v in ref["pre"].items() if v is not None}
+    probes = [G - E, G - 0.5 * E, G + 0.5 * E, G + E, np.where(np.abs(G) <= E, 0.0, G)]
+    for Gp in probes:
+        r = O.apply_step(Gp, snap.W, snap.m, snap.v, hyp, step, seed, rows_local, c0, c1, flat)
+        for k in lo:
+            lo[k] = np.minimum(lo[k], r["pre"][k])
+            hi[k] = np.maximum(hi[k], r["pre"][k])
+    # Scale of the terms each output is summed from: the same step evaluated
+    # on absolute values with the update added instead of subtracted (the
+    # usual device of running a computation on |inputs| to bound its
+    # rounding error).  fp32 evaluation error is a few ulps of this scale.
+    absW, absm, absv = (_abs_stored(x) for x in (snap.W, snap.m, snap.v))
+    ahyp = O.Hyper(opt=hyp.opt, lr=-hyp.lr, beta1=hyp.beta1, beta2=hyp.beta2, eps=hyp.eps,
+                   weight_decay=hyp.weight_decay, round=hyp.round)
+    ra = O.apply_step(np.abs(G) + E, absW, absm, absv, ahyp, step, seed, rows_local, c0, c1, flat)
+    scale = {k: np.abs(ra["pre"][k]) for k in lo}
+    return ref, lo, hi, scale
+
+
+def _abs_stored(st):
+    if st is None:
+        return None
+    if st.fmt == "f32":
+        return O.Stored("f32", np.abs(st.data))
+    if st.fmt == "bf16":
+        return O.Stored("bf16", st.data & np.uint16(0x7FFF))
+    if st.fmt == "s8":
+        return O.Stored("s8", np.abs(st.data.astype(np.int16)).astype(np.int8), st.scale, st.block)
+    return st
+
+
+def check_against_oracle(snap: Snap, L: Layer, h, step: int, seed: int, col_ranges=None,
+                         rep: Optional[Report] = None, exact_min=0.999, code_exact_min=0.99) -> Report:
+    """Compare the layer's current (post-step) tensors on rows snap.rows and
+    the given column ranges with the oracle run on the snapshot."""
+    rep = rep or Report()
+    hyp = oracle_hyper(h)
+    K = L.K
+    col_ranges = col_ranges or [(0, K)]
+    idx = torch.as_tensor(snap.rows, device=L.W.device, dtype=torch.long)
+    s = L.spec
+    for c0, c1 in col_ranges:
+        if c1 <= c0:
+            continue
+        ref, lo, hi, tscale = _hull(snap, hyp, step, seed, c0, c1, K)
+        got = {"W": (L.W, s.w_fmt, None), "m": (L.m, s.m_fmt, L.ms), "v": (L.v, s.v_fmt, L.vs)}
+        for name, (t, fmt, scale) in got.items():
+            if t is None or fmt is None:
+                continue
+            g = synth.host(t.index_select(0, idx)[:, c0:c1])
+            r_st = ref[name]
+            r_pre = ref["pre"][name]
+            where = f"{name}[{fmt}] cols {c0}:{c1}"
+            rep.checked += g.size
+            if fmt == "f32":
+                g64 = g.astype(np.float64)
+                tol = 1e-5 * np.maximum(np.abs(r_pre), tscale[name])
+                c1ok = np.abs(g64 - r_pre) <= tol
+                c2ok = (g64 >= lo[name] - tol) & (g64 <= hi[name] + tol)
+                bad = ~(c1ok | c2ok)
+                rep.clause2[where] = int(np.sum(~c1ok & c2ok))
+                if bad.any():
+                    i = np.argwhere(bad)[0]
+                    rep.failures.append(f"{where}: {int(bad.sum())} fp32 elements off, e.g. {tuple(i)} "
+                                        f"got {g64[tuple(i)]!r} ref {r_pre[tuple(i)]!r} "
+                                        f"hull [{lo[name][tuple(i)]!r}, {hi[name][tuple(i)]!r}]")
+            elif fmt == "bf16":
+                gv = O.bf16_bits_to_f64(g)
+                ulp = np.maximum(_bf16_ulp(lo[name]), _bf16_ulp(hi[name])) + 1e-5 * tscale[name]
+                bad = (gv < lo[name] - ulp) | (gv > hi[name] + ulp)
+                exact = float(np.mean(g == r_st.data)) if g.size else 1.0
+                rep.exact_frac[where] = exact
+                if bad.any():
+                    i = np.argwhere(bad)[0]
+                    rep.failures.append(f"{where}: {int(bad.sum())} bf16 elements beyond 1 ulp, e.g. {tuple(i)} "
+                                        f"got {gv[tuple(i)]!r} hull [{lo[name][tuple(i)]!r}, {hi[name][tuple(i)]!r}]")
+                if exact < exact_min:
+                    rep.failures.append(f"{where}: bf16 bit-exact fraction {exact:.6f} < {exact_min}")
+            else:  # int8 codes + scales
+                gi = g.astype(np.int64)
+                ri = r_st.data.astype(np.int64)
+                d = np.abs(gi - ri)
+                exact = float(np.mean(d == 0)) if d.size else 1.0
+                rep.exact_frac[where] = exact
+                if (d > 1).any():
+                    i = np.argwhere(d > 1)[0]
+                    rep.failures.append(f"{where}: {int((d > 1).sum())} codes off by > 1, e.g. {tuple(i)} "
+                                        f"got {gi[tuple(i)]} ref {ri[tuple(i)]}")
+                if exact < code_exact_min:
+                    rep.failures.append(f"{where}: code exact fraction {exact:.6f} < {code_exact_min}")
+                b = s.block
+                gs = scale.index_select(0, idx)[:, c0 // b:c1 // b].cpu().numpy().astype(np.float64)
+                rs = r_st.scale.astype(np.float64)
+                qmax = 127.0 if fmt == "s8" else 255.0
+                alo = np.where((lo[name] <= 0) & (hi[name] >= 0), 0.0, np.minimum(np.abs(lo[name]), np.abs(hi[name])))
+                ahi = np.maximum(np.abs(lo[name]), np.abs(hi[name]))
+                R = alo.shape[0]
+                slo = alo.reshape(R, -1, b).max(axis=2) / qmax
+                shi = ahi.reshape(R, -1, b).max(axis=2) / qmax
+                tol = 1e-5 * rs
+                sbad = ~((np.abs(gs - rs) <= tol) | ((gs >= slo - tol) & (gs <= shi + tol)))
+                if sbad.any():
+                    i = np.argwhere(sbad)[0]
+                    rep.failures.append(f"{where}: {int(sbad.sum())} scales off, e.g. {tuple(i)} "
+                                        f"got {gs[tuple(i)]!r} ref {rs[tuple(i)]!r}")
+    return rep
+
+
+def assert_ok(rep: Report, label: str = ""):
+    if not rep.ok():
+        raise AssertionError(f"{label}: " + "\n".join(rep.failures[:10]))
+
+
+def sample_rows(N: int, n: int, seed: int) -> np.ndarray:
+    """First, last and tile-boundary rows plus random ones, sorted."""
+    rng = np.random.default_rng(seed)
+    base = {0, N - 1, min(N - 1, 127), min(N - 1, 128)}
+    extra = rng.choice(N, size=min(N, n), replace=False)
+    return np.array(sorted(base | set(int(x) for x in extra)))

@@ -1,0 +1,193 @@
+"""Host-only checks of the C ABI: the library loads, exports every declared
+entry point, and validates arguments (no device call is made; the pointers
+below are fake and never dereferenced)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import backward_weight_gradient_amd as F
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "forge.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(forge_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("forge_wgrad_step", "forge_wgrad_check", "forge_wgrad_unfused", "forge_debug_sr_bf16",
+              "forge_status_str", "forge_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(F.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in forge.h but not exported"
+
+
+def test_version_and_status_strings():
+    assert "gfx950" in F.forge_version()
+    for code in range(10):
+        assert F.forge_status_str(code).startswith(F.STATUS_NAMES[code])
+
+
+# fake, well-aligned, non-overlapping device addresses
+BASE = 0x7F0000000000
+GAP = 1 << 36
+
+
+def addr(i):
+    return BASE + i * GAP
+
+
+def layer(N=256, K=256, BT=64, in_dt=F.FORGE_BF16, w_dt=F.FORGE_BF16, m_dt=F.FORGE_F32, v_dt=F.FORGE_F32,
+          block=128):
+    X = F.mat_raw(addr(0), in_dt, BT, K)
+    dY = F.mat_raw(addr(1), in_dt, BT, N)
+    W = F.mat_raw(addr(2), w_dt, N, K)
+    ms = addr(5) if m_dt == F.FORGE_S8 else None
+    vs = addr(6) if v_dt == F.FORGE_U8 else None
+    m = F.forge_state(F.mat_raw(addr(3), m_dt, N, K), ms, block if ms else 0)
+    v = F.forge_state(F.mat_raw(addr(4), v_dt, N, K), vs, block if vs else 0) if v_dt is not None else None
+    return X, dY, W, m, v
+
+
+def check(X, dY, W, m, v, h=None, step=10):
+    return F.forge_wgrad_check(X, dY, W, m, v, h or F.hyper(), step)
+
+
+def test_valid_configurations_pass():
+    assert check(*layer()) == F.FORGE_OK
+    assert check(*layer(in_dt=F.FORGE_F32, w_dt=F.FORGE_F32)) == F.FORGE_OK
+    assert check(*layer(m_dt=F.FORGE_BF16, v_dt=F.FORGE_BF16)) == F.FORGE_OK
+    assert check(*layer(m_dt=F.FORGE_S8, v_dt=F.FORGE_U8)) == F.FORGE_OK
+    X, dY, W, m, _ = layer(v_dt=None)
+    assert check(X, dY, W, m, None, F.hyper("lion", lr=1e-4, beta2=0.99)) == F.FORGE_OK
+    assert check(X, dY, W, m, None, F.hyper("sgdm")) == F.FORGE_OK
+    # ragged and degenerate shapes
+    assert check(*layer(N=129, K=131, BT=65)) == F.FORGE_OK
+    assert check(*layer(BT=0)) == F.FORGE_OK
+    assert check(*layer(N=0)) == F.FORGE_OK
+
+
+def test_null_pointers():
+    X, dY, W, m, v = layer()
+    assert F.forge_wgrad_check(None, dY, W, m, v, F.hyper(), 1) == F.FORGE_E_NULL
+    assert F.forge_wgrad_check(X, dY, W, m, v, None, 1) == F.FORGE_E_NULL
+    assert check(X, dY, W, None, v) == F.FORGE_E_NULL
+    assert check(X, dY, W, m, None) == F.FORGE_E_NULL           # AdamW needs v
+    W0 = F.mat_raw(0, F.FORGE_BF16, 256, 256)
+    assert check(X, dY, W0, m, v) == F.FORGE_E_NULL
+    X, dY, W, m, v = layer(m_dt=F.FORGE_S8, v_dt=F.FORGE_U8)
+    m.scale = None
+    assert check(X, dY, W, m, v) == F.FORGE_E_NULL
+
+
+def test_step_zero_rejected():
+    assert check(*layer(), step=0) == F.FORGE_E_STEP
+    assert check(*layer(), step=-3) == F.FORGE_E_STEP
+
+
+def test_shape_mismatches():
+    X, dY, W, m, v = layer()
+    assert check(F.mat_raw(addr(0), F.FORGE_BF16, 64, 255), dY, W, m, v) == F.FORGE_E_SHAPE
+    assert check(X, F.mat_raw(addr(1), F.FORGE_BF16, 63, 256), W, m, v) == F.FORGE_E_SHAPE
+    assert check(X, dY, F.mat_raw(addr(2), F.FORGE_BF16, 256, 128), m, v) == F.FORGE_E_SHAPE
+    bad_m = F.forge_state(F.mat_raw(addr(3), F.FORGE_F32, 255, 256), None, 0)
+    assert check(X, dY, W, bad_m, v) == F.FORGE_E_SHAPE
+    assert check(X, dY, F.mat_raw(addr(2), F.FORGE_BF16, 256, 256, ld=200), m, v) == F.FORGE_E_SHAPE
+
+
+def test_int8_block_rules():
+    # K must be a multiple of the block
+    assert check(*layer(K=200, m_dt=F.FORGE_S8, v_dt=F.FORGE_U8)) == F.FORGE_E_SHAPE
+    # block must divide the 128-wide tile
+    assert check(*layer(m_dt=F.FORGE_S8, v_dt=F.FORGE_U8, block=96)) == F.FORGE_E_SHAPE
+    assert check(*layer(K=192, m_dt=F.FORGE_S8, v_dt=F.FORGE_U8, block=64)) == F.FORGE_OK
+    # signed codes are for m, unsigned for v
+    assert check(*layer(m_dt=F.FORGE_U8, v_dt=F.FORGE_U8)) == F.FORGE_E_DTYPE
+    assert check(*layer(m_dt=F.FORGE_S8, v_dt=F.FORGE_S8)) == F.FORGE_E_DTYPE
+
+
+def test_dtype_rules():
+    X, dY, W, m, v = layer()
+    assert check(F.mat_raw(addr(0), F.FORGE_F32, 64, 256), dY, W, m, v) == F.FORGE_E_DTYPE   # X != dY
+    assert check(*layer(in_dt=F.FORGE_S8)) == F.FORGE_E_DTYPE
+    assert check(*layer(w_dt=F.FORGE_U8)) == F.FORGE_E_DTYPE
+    assert check(X, dY, W, m, v) == F.FORGE_OK
+    assert check(*layer(in_dt=7)) == F.FORGE_E_DTYPE
+    # mixed state layouts that are not built
+    assert check(*layer(m_dt=F.FORGE_F32, v_dt=F.FORGE_BF16)) == F.FORGE_E_UNSUPPORTED
+
+
+def test_optimizer_state_rules():
+    X, dY, W, m, v = layer()
+    assert check(X, dY, W, m, v, F.hyper("lion", lr=1e-4, beta2=0.99)) == F.FORGE_E_UNSUPPORTED  # v given
+    assert check(X, dY, W, m, v, F.hyper("sgdm")) == F.FORGE_E_UNSUPPORTED
+
+
+def test_hyper_parameter_rules():
+    base = layer()
+    bad = [F.hyper(lr=float("nan")), F.hyper(lr=-1.0), F.hyper(beta1=1.0), F.hyper(beta2=1.5),
+           F.hyper(eps=0.0), F.hyper(weight_decay=float("inf")), F.hyper(weight_decay=-0.1)]
+    for h in bad:
+        assert check(*base, h=h) == F.FORGE_E_HYPER
+    h = F.hyper()
+    h.opt = 9
+    assert check(*base, h=h) == F.FORGE_E_HYPER
+    h = F.hyper()
+    h.round = 5
+    assert check(*base, h=h) == F.FORGE_E_HYPER
+
+
+def test_alignment():
+    X, dY, W, m, v = layer()
+    assert check(X, dY, F.mat_raw(addr(2) + 1, F.FORGE_BF16, 256, 256), m, v) == F.FORGE_E_ALIGN
+    bad_m = F.forge_state(F.mat_raw(addr(3) + 2, F.FORGE_F32, 256, 256), None, 0)
+    assert check(X, dY, W, bad_m, v) == F.FORGE_E_ALIGN
+
+
+def test_aliasing_rejected():
+    X, dY, W, m, v = layer()
+    assert check(X, dY, F.mat_raw(addr(0), F.FORGE_BF16, 256, 256), m, v) == F.FORGE_E_ALIAS   # W == X
+    assert check(X, dY, F.mat_raw(addr(1) + 512, F.FORGE_BF16, 256, 256), m, v) == F.FORGE_E_ALIAS
+    m2 = F.forge_state(F.mat_raw(addr(2) + 4096, F.FORGE_F32, 256, 256), None, 0)             # m inside W
+    assert check(X, dY, W, m2, v) == F.FORGE_E_ALIAS
+    v2 = F.forge_state(F.mat_raw(addr(3), F.FORGE_F32, 256, 256), None, 0)                    # v == m
+    assert check(X, dY, W, m, v2) == F.FORGE_E_ALIAS
+
+
+def test_flat_index_limit():
+    # N * K >= 2^32 cannot be addressed by the 32-bit SR index
+    assert check(*layer(N=65536, K=65536)) == F.FORGE_E_SHAPE
+    assert check(*layer(N=65536, K=65535)) == F.FORGE_OK
+
+
+def test_debug_sr_argument_errors():
+    assert F.lib.forge_debug_sr_bf16(None, None, -1, 1, 1, 0, None) == F.FORGE_E_SHAPE
+    assert F.lib.forge_debug_sr_bf16(None, None, 10, 1, 1, 0, None) == F.FORGE_E_NULL
+    assert F.lib.forge_debug_sr_bf16(addr(0), addr(1), 10, 1, 0, 0, None) == F.FORGE_E_STEP
+    assert F.lib.forge_debug_sr_bf16(addr(0), addr(0) + 8, 10, 1, 1, 0, None) == F.FORGE_E_ALIAS
+    assert F.lib.forge_debug_sr_bf16(None, None, 0, 1, 1, 0, None) == F.FORGE_OK
+
+
+def test_unfused_argument_errors():
+    X, dY, W, m, v = layer()
+    h = F.hyper()
+    rc = F.lib.forge_wgrad_unfused(ctypes.byref(X), ctypes.byref(dY), ctypes.byref(W), ctypes.byref(m),
+                                   ctypes.byref(v), ctypes.byref(h), 1, 1, addr(7), F.FORGE_S8, None)
+    assert rc == F.FORGE_E_DTYPE
+    rc = F.lib.forge_wgrad_unfused(ctypes.byref(X), ctypes.byref(dY), ctypes.byref(W), ctypes.byref(m),
+                                   ctypes.byref(v), ctypes.byref(h), 1, 1, None, F.FORGE_F32, None)
+    assert rc == F.FORGE_E_NULL
+    rc = F.lib.forge_wgrad_unfused(ctypes.byref(X), ctypes.byref(dY), ctypes.byref(W), ctypes.byref(m),
+                                   ctypes.byref(v), ctypes.byref(h), 1, 1, addr(2) + 64, F.FORGE_F32, None)
+    assert rc == F.FORGE_E_ALIAS
