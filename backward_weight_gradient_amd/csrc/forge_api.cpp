@@ -196,6 +196,12 @@ KArgs make_args(const forge_mat* X, const forge_mat* dY, forge_mat* W, forge_sta
   // 16-byte vector loads of 8 bf16 / 4 fp32 activations
   const int ies = elem_size(pl.in_fmt), ivec = 16 / ies;
   a.vec_in = (vec_ok(X->data, X->ld, ivec, ies) && vec_ok(dY->data, dY->ld, ivec, ies)) ? 1 : 0;
+  // direct-to-LDS mainloop: 16-byte aligned bf16 rows, feature counts that
+  // are multiples of 8 (a chunk is all inside or all outside), and byte
+  // offsets that fit the 32-bit buffer addressing
+  a.dma_ok = (pl.in_fmt == FORGE_BF16 && a.vec_in && pl.N % 8 == 0 && pl.K % 8 == 0 &&
+              (uint64_t)pl.BT * (uint64_t)dY->ld * 2 < (1ull << 31) &&
+              (uint64_t)pl.BT * (uint64_t)X->ld * 2 < (1ull << 31)) ? 1 : 0;
   // 8-element state accesses
   bool vs = vec_ok(W->data, W->ld, 8, elem_size(pl.w_fmt)) && vec_ok(m->q.data, m->q.ld, 8, elem_size(pl.m_fmt));
   if (v) vs = vs && vec_ok(v->q.data, v->q.ld, 8, elem_size(pl.v_fmt));

@@ -41,6 +41,7 @@ struct KArgs {
   int32_t block;                  // int8 block length (32, 64, 128)
   int32_t vec_in;                 // X / dY rows allow 16-byte vector loads
   int32_t vec_state;              // W / m / v rows allow 8-element vector access
+  int32_t dma_ok;                 // bf16 X / dY qualify for the direct-to-LDS mainloop
   EpiConst c;
 };
 

@@ -22,13 +22,15 @@
 // thread owns 8 consecutive elements of a row; W / m / v are then read and
 // written with 16-byte accesses, and an int8 block (<= 128 elements of one
 // row) is owned by <= 16 adjacent lanes, which reduce its absmax with lane
-// shuffles.  The element-wise step is written once (step_chunk) and is used
+// shuffles.  The element-wise step is written once (Step::apply_store) and is used
 // by the fused kernel and by the unfused baseline's step kernel alike, so
 // the two are bit-identical when the baseline keeps G in fp32 (paper,
 // Corollary 1(a)).
 //
-// All arithmetic is IEEE fp32 with explicit fmaf; the library is compiled
-// with -ffp-contract=off so no other contraction happens.
+// All arithmetic is IEEE fp32 with explicit fmaf (the library is compiled
+// with -ffp-contract=off so no other contraction happens); the AdamW square
+// root and reciprocal are the hardware instructions, the int8 scale
+// divisions are correctly rounded.
 
 #include "forge_internal.h"
 
@@ -178,6 +180,206 @@ struct MainBF16 {
 };
 
 // ------------------------------------------------------------------------
+// Mainloop, bf16 inputs, asynchronous: buffer loads straight into LDS
+// (buffer_load_dwordx4 ... lds), S stages in flight, no register staging.
+// A load instruction writes its 64 lanes' 16 bytes lane-linearly at a
+// wave-uniform LDS address, so each lane fetches the global chunk that the
+// swizzled layout expects at its slot.  Out-of-range offsets read as zero,
+// which pads the token tail and a feature tail that is a multiple of 8.
+// Requires 16-byte aligned rows (ld % 8 == 0), N % 8 == K % 8 == 0 and
+// operands smaller than 4 GiB; other shapes use MainBF16.
+// ------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // raw buffer (stride 0): out-of-range offsets return zero
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (((N >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+struct MainBF16Dma {
+  static constexpr int TK = 32;                        // tokens per chunk
+  static constexpr int S = 4;                          // LDS stages (3 chunks in flight)
+  static constexpr int OPB = TK * TILE * 2;            // 8 KiB per operand per stage
+  static constexpr int STAGE = 2 * OPB;
+  static constexpr int LOADS = 4;                      // buffer loads per thread per chunk
+
+  __amdgpu_buffer_rsrc_t rA, rB;
+  uint32_t oobA, oobB;         // an offset past the end: reads zero
+  uint32_t baseA[2], baseB[2]; // byte offset of this lane's feature chunk in token row 0
+  int trow[2];                 // token row within the chunk
+  bool fokA[2], fokB[2];       // feature chunk inside the matrix
+
+  __device__ __forceinline__ void init(const KArgs& a, int row0, int col0) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    oobA = (uint32_t)((uint64_t)a.BT * a.lddy * 2);
+    oobB = (uint32_t)((uint64_t)a.BT * a.ldx * 2);
+    rA = make_rsrc(a.dY, oobA);
+    rB = make_rsrc(a.X, oobB);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int t = 4 * (2 * wave + r) + (lane >> 4);
+      const int c = (lane & 15) ^ ((t & 3) << 2);        // logical 8-feature chunk at this slot
+      trow[r] = t;
+      fokA[r] = row0 + c * 8 < a.N;
+      fokB[r] = col0 + c * 8 < a.K;
+      baseA[r] = (uint32_t)(row0 + c * 8) * 2;
+      baseB[r] = (uint32_t)(col0 + c * 8) * 2;
+    }
+  }
+
+  __device__ __forceinline__ void issue(const KArgs& a, int kc, char* stage) const {
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int tok = kc * TK + trow[r];
+      const bool tok_ok = tok < a.BT;
+      const uint32_t oa = (tok_ok && fokA[r]) ? (uint32_t)tok * (uint32_t)(a.lddy * 2) + baseA[r] : oobA;
+      const uint32_t ob = (tok_ok && fokB[r]) ? (uint32_t)tok * (uint32_t)(a.ldx * 2) + baseB[r] : oobB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void*)(stage + (2 * wave + r) * 1024), 16, oa, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void*)(stage + OPB + (2 * wave + r) * 1024), 16, ob, 0,
+                                               0, 0);
+    }
+  }
+
+  // Wait until this wave's loads of the chunk issued `ahead` chunks ago
+  // have landed (later chunks may still be in flight).
+  __device__ __forceinline__ static void wait_chunk(int ahead) {
+    if (ahead >= 2) wait_vmcnt<2 * LOADS>();
+    else if (ahead == 1) wait_vmcnt<LOADS>();
+    else wait_vmcnt<0>();
+  }
+};
+
+// Transposing LDS read issued as inline assembly: the compiler cannot tell
+// which stage an in-flight LDS DMA writes, and would otherwise wait for all
+// of them (vmcnt(0)) before every LDS read.  Completion is awaited
+// explicitly with lds_wait below.
+__device__ __forceinline__ u32x2 tr_read(uint32_t lds_addr) {
+  u32x2 v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(lds_addr));
+  return v;
+}
+
+// 32-bit LDS address of (token row t, feature f) in a region at `region`.
+__device__ __forceinline__ uint32_t tr_addr(uint32_t region, int t, int f) {
+  return region + (uint32_t)MainBF16::off(t, f);
+}
+
+// The two transposing reads of an MFMA operand fragment (see MainBF16::frag).
+__device__ __forceinline__ void frag_issue(uint32_t region, int t0, int f0, int lane, u32x2& lo, u32x2& hi) {
+  const int t = t0 + 8 * (lane >> 5) + ((lane & 15) >> 2);
+  const int f = f0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  lo = tr_read(tr_addr(region, t, f));
+  hi = tr_read(tr_addr(region, t + 4, f));
+}
+
+__device__ __forceinline__ bf16x8 frag_join(u32x2 lo, u32x2 hi) {
+  return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
+// Wait for LDS reads until at most N are outstanding; the fragments are
+// threaded through the statement so that their uses stay after it.
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x2 (&f)[8]) {
+  static_assert(N == 0 || N == 8, "lgkmcnt");
+  if constexpr (N == 0)
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5]),
+                 "+v"(f[6]), "+v"(f[7]));
+  else
+    asm volatile("s_waitcnt lgkmcnt(8)" : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5]),
+                 "+v"(f[6]), "+v"(f[7]));
+}
+
+// Workgroup barrier without a memory fence: LDS-DMA completion is awaited
+// per wave with wait_vmcnt before it (a fenced barrier would wait for every
+// load in flight).  The empty asm statements keep the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void bar() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Phase 1 with the asynchronous mainloop; same output as tile_gradient.
+__device__ __forceinline__ void tile_gradient_dma(const KArgs& a, char* lds, int row0, int col0) {
+  using M = MainBF16Dma;
+  static_assert(M::S * M::STAGE <= LDS_BYTES, "LDS budget");
+  static_assert(M::TK == 32, "two 16-token k-steps per chunk");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)lds;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[bi][bj][e] = 0.f;
+  const int nk = (a.BT + M::TK - 1) / M::TK;
+  M ml;
+  ml.init(a, row0, col0);
+#pragma unroll
+  for (int k = 0; k < M::S - 1; ++k)
+    if (k < nk) ml.issue(a, k, lds + k * M::STAGE);
+  for (int kc = 0; kc < nk; ++kc) {
+    // loads issued after chunk kc: chunks kc+1 .. min(kc+S-2, nk-1)
+    M::wait_chunk(min(M::S - 2, nk - 1 - kc));
+    bar();   // chunk kc visible to all waves; all waves done with chunk kc-1
+    if (kc + M::S - 1 < nk) ml.issue(a, kc + M::S - 1, lds + ((kc + M::S - 1) % M::S) * M::STAGE);
+    const uint32_t cur = lds0 + (uint32_t)((kc % M::S) * M::STAGE);
+    // fragments of both k-steps: [0..3] = k-step 0 (A0, A1, B0, B1 as lo/hi pairs), [4..7] unused layout below
+    u32x2 f0[8], f1[8];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      frag_issue(cur, 0, wr * 64 + b * 32, lane, f0[2 * b], f0[2 * b + 1]);
+      frag_issue(cur + M::OPB, 0, wc * 64 + b * 32, lane, f0[4 + 2 * b], f0[4 + 2 * b + 1]);
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      frag_issue(cur, 16, wr * 64 + b * 32, lane, f1[2 * b], f1[2 * b + 1]);
+      frag_issue(cur + M::OPB, 16, wc * 64 + b * 32, lane, f1[4 + 2 * b], f1[4 + 2 * b + 1]);
+    }
+    lds_wait<8>(f0);
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < 2; ++bj)
+        acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_join(f0[2 * bi], f0[2 * bi + 1]),
+                                                              frag_join(f0[4 + 2 * bj], f0[4 + 2 * bj + 1]),
+                                                              acc[bi][bj], 0, 0, 0);
+    lds_wait<0>(f1);
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < 2; ++bj)
+        acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_join(f1[2 * bi], f1[2 * bi + 1]),
+                                                              frag_join(f1[4 + 2 * bj], f1[4 + 2 * bj + 1]),
+                                                              acc[bi][bj], 0, 0, 0);
+  }
+  wait_vmcnt<0>();
+  bar();   // every wave is done reading the stages before G overwrites them
+  float* sG = reinterpret_cast<float*>(lds);
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = wr * 64 + bi * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        const int c = wc * 64 + bj * 32 + (lane & 31);
+        sG[r * GP + c] = acc[bi][bj][e];
+      }
+  __syncthreads();
+}
+
+// ------------------------------------------------------------------------
 // Mainloop, fp32 inputs
 // ------------------------------------------------------------------------
 struct MainF32 {
@@ -293,102 +495,130 @@ __device__ __forceinline__ void tile_gradient(const KArgs& a, char* lds, int row
 // Element-wise step on 8 consecutive elements of one row (Algorithm 1
 // Phase 2 and 3; Appendix N families)
 // ------------------------------------------------------------------------
-template <int FMT> struct Io;
+// Raw (undecoded) storage of 8 consecutive elements, so that the loads of
+// later chunks can be in flight while earlier chunks are computed.
+template <int FMT> struct Raw8;
+template <> struct Raw8<FMT_F32> { f32x4 lo, hi; };
+template <> struct Raw8<FMT_BF16> { u32x4 w; };
+template <> struct Raw8<FMT_S8> { u32x2 w; float s; };
+template <> struct Raw8<FMT_U8> { u32x2 w; float s; };
+template <> struct Raw8<FMT_NONE> {};
 
-template <> struct Io<FMT_F32> {
-  __device__ __forceinline__ static void load(const void* base, int64_t off, int nv, bool vec, float (&x)[8]) {
+// State tensors are streamed once per step: their accesses are marked
+// non-temporal so that they do not evict the activation panels the
+// neighbouring tiles re-read from L2.
+template <typename T> __device__ __forceinline__ T ld_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
+}
+template <typename T> __device__ __forceinline__ void st_nt(void* p, T v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<T*>(p));
+}
+
+// Load 8 elements at element offset `off`; `nv` (<= 8) of them are valid;
+// `vec`: the row allows one aligned vector access.  Invalid ones read as 0.
+template <int FMT>
+__device__ __forceinline__ void ld8(Raw8<FMT>& r, const void* base, int64_t off, int nv, bool vec) {
+  if constexpr (FMT == FMT_F32) {
     const float* p = static_cast<const float*>(base) + off;
     if (vec && nv == 8) {
-      const f32x4 a = *reinterpret_cast<const f32x4*>(p);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) { x[i] = a[i]; x[i + 4] = b[i]; }
+      r.lo = ld_nt<f32x4>(p);
+      r.hi = ld_nt<f32x4>(p + 4);
     } else {
+      float x[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) x[i] = i < nv ? p[i] : 0.f;
+      r.lo = f32x4{x[0], x[1], x[2], x[3]};
+      r.hi = f32x4{x[4], x[5], x[6], x[7]};
+    }
+  } else if constexpr (FMT == FMT_BF16) {
+    const uint16_t* p = static_cast<const uint16_t*>(base) + off;
+    if (vec && nv == 8) {
+      r.w = ld_nt<u32x4>(p);
+    } else {
+      uint32_t e[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) e[i] = i < nv ? (uint32_t)p[i] : 0u;
+      r.w = u32x4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+    }
+  } else if constexpr (FMT == FMT_S8 || FMT == FMT_U8) {
+    const uint8_t* p = static_cast<const uint8_t*>(base) + off;
+    if (vec && nv == 8) {
+      r.w = ld_nt<u32x2>(p);
+    } else {
+      uint32_t e[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) e[i] = i < nv ? (uint32_t)p[i] : 0u;
+      r.w = u32x2{e[0] | (e[1] << 8) | (e[2] << 16) | (e[3] << 24), e[4] | (e[5] << 8) | (e[6] << 16) | (e[7] << 24)};
     }
   }
-  __device__ __forceinline__ static void store(void* base, int64_t off, int nv, bool vec, const float (&x)[8],
-                                               int, uint32_t, uint32_t) {
+}
+
+template <int FMT>
+__device__ __forceinline__ void zero8(Raw8<FMT>& r) {
+  if constexpr (FMT == FMT_F32) { r.lo = f32x4{0.f, 0.f, 0.f, 0.f}; r.hi = r.lo; }
+  else if constexpr (FMT == FMT_BF16) { r.w = u32x4{0u, 0u, 0u, 0u}; }
+  else if constexpr (FMT == FMT_S8 || FMT == FMT_U8) { r.w = u32x2{0u, 0u}; r.s = 0.f; }
+}
+
+// Decode to fp32; int8 codes are dequantised as code * scale (one fp32 multiply).
+template <int FMT>
+__device__ __forceinline__ void dec8(const Raw8<FMT>& r, float (&x)[8]) {
+  if constexpr (FMT == FMT_F32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { x[i] = r.lo[i]; x[i + 4] = r.hi[i]; }
+  } else if constexpr (FMT == FMT_BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(r.w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(r.w[i] & 0xFFFF0000u);
+    }
+  } else if constexpr (FMT == FMT_S8) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = (float)(int8_t)((r.w[i >> 2] >> (8 * (i & 3))) & 0xFFu) * r.s;
+  } else if constexpr (FMT == FMT_U8) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = (float)((r.w[i >> 2] >> (8 * (i & 3))) & 0xFFu) * r.s;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = 0.f;
+  }
+}
+
+// Store 8 fp32 values as FMT (int8 formats go through quantize8 instead).
+// bf16: stochastic rounding keyed on (key, idx0 + i) when sr != 0, else RNE.
+template <int FMT>
+__device__ __forceinline__ void st8(void* base, int64_t off, int nv, bool vec, const float (&x)[8], int sr,
+                                    uint32_t key, uint32_t idx0) {
+  if constexpr (FMT == FMT_F32) {
     float* p = static_cast<float*>(base) + off;
     if (vec && nv == 8) {
-      *reinterpret_cast<f32x4*>(p) = f32x4{x[0], x[1], x[2], x[3]};
-      *reinterpret_cast<f32x4*>(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
+      st_nt<f32x4>(p, f32x4{x[0], x[1], x[2], x[3]});
+      st_nt<f32x4>(p + 4, f32x4{x[4], x[5], x[6], x[7]});
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         if (i < nv) p[i] = x[i];
     }
-  }
-};
-
-template <> struct Io<FMT_BF16> {
-  __device__ __forceinline__ static void load(const void* base, int64_t off, int nv, bool vec, float (&x)[8]) {
-    const uint16_t* p = static_cast<const uint16_t*>(base) + off;
-    if (vec && nv == 8) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(p);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[2 * i] = __uint_as_float(a[i] << 16);
-        x[2 * i + 1] = __uint_as_float(a[i] & 0xFFFF0000u);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = i < nv ? bf16_val(p[i]) : 0.f;
-    }
-  }
-  // sr != 0: stochastic rounding keyed on (key, idx0 + i); else RNE.
-  __device__ __forceinline__ static void store(void* base, int64_t off, int nv, bool vec, const float (&x)[8],
-                                               int sr, uint32_t key, uint32_t idx0) {
+  } else if constexpr (FMT == FMT_BF16) {
     uint32_t b[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) b[i] = sr ? bf16_sr_bits(x[i], key, idx0 + i) : bf16_rne_bits(x[i]);
     uint16_t* p = static_cast<uint16_t*>(base) + off;
     if (vec && nv == 8) {
-      *reinterpret_cast<u32x4*>(p) =
-          u32x4{b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16)};
+      st_nt<u32x4>(p, u32x4{b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16)});
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         if (i < nv) p[i] = (uint16_t)b[i];
     }
   }
-};
-
-// int8 codes: load = dequantise (code * scale in fp32).
-template <> struct Io<FMT_S8> {
-  __device__ __forceinline__ static void load_codes(const void* base, int64_t off, int nv, bool vec,
-                                                    float scale, float (&x)[8]) {
-    const int8_t* p = static_cast<const int8_t*>(base) + off;
-    if (vec && nv == 8) {
-      const u32x2 a = *reinterpret_cast<const u32x2*>(p);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = (float)(int8_t)((a[i >> 2] >> (8 * (i & 3))) & 0xFF) * scale;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = i < nv ? (float)p[i] * scale : 0.f;
-    }
-  }
-};
-template <> struct Io<FMT_U8> {
-  __device__ __forceinline__ static void load_codes(const void* base, int64_t off, int nv, bool vec,
-                                                    float scale, float (&x)[8]) {
-    const uint8_t* p = static_cast<const uint8_t*>(base) + off;
-    if (vec && nv == 8) {
-      const u32x2 a = *reinterpret_cast<const u32x2*>(p);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = (float)((a[i >> 2] >> (8 * (i & 3))) & 0xFF) * scale;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = i < nv ? (float)p[i] * scale : 0.f;
-    }
-  }
-};
+}
 
 // Block-absmax quantisation of 8 values per lane; a block is `lpb` adjacent
 // lanes (lpb = block / 8, a power of two <= 16).  Every lane of the wave
 // must call this (lane shuffles).  SIGNED: codes -127..127, scale a/127.
-// Unsigned: code 0 only for an exact zero, else 1..255, scale a/255.
+// Unsigned: code 0 only for an exact zero, else 1..255, scale a/255.  The
+// scale and the reciprocal are correctly rounded fp32 divisions.
 template <bool SIGNED>
 __device__ __forceinline__ void quantize8(const float (&x)[8], int lpb, bool valid, void* codes_base,
                                           int64_t off, bool vec, float* scale_ptr, bool write_scale) {
@@ -416,165 +646,163 @@ __device__ __forceinline__ void quantize8(const float (&x)[8], int lpb, bool val
   if (write_scale) *scale_ptr = s;
   uint8_t* p = static_cast<uint8_t*>(codes_base) + off;
   if (vec) {
-    *reinterpret_cast<u32x2*>(p) = u32x2{q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24),
-                                         q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24)};
+    st_nt<u32x2>(p, u32x2{q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24),
+                          q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24)});
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i) p[i] = (uint8_t)q[i];
   }
 }
 
-// Loaded state of one 8-element chunk.
-struct Chunk {
-  float w[8], m[8], v[8];
-};
-
 template <int OPT, int WF, int MF, int VF>
 struct Step {
   static constexpr bool HAS_V = (OPT == OPT_ADAMW);
+  static constexpr int VFMT = HAS_V ? VF : FMT_NONE;
 
-  __device__ __forceinline__ static void load(const KArgs& a, int p, int q, int nv, Chunk& c) {
-    const bool vec = a.vec_state != 0;
+  // Everything one chunk reads, still undecoded.
+  struct Pending {
+    Raw8<WF> w;
+    Raw8<MF> m;
+    Raw8<VFMT> v;
+  };
+
+  __device__ __forceinline__ static void load(const KArgs& a, int p, int q, int nv, Pending& r) {
     if (p >= a.N || nv <= 0) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) c.w[i] = c.m[i] = c.v[i] = 0.f;
+      zero8(r.w); zero8(r.m); zero8(r.v);
       return;
     }
-    if constexpr (!HAS_V) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) c.v[i] = 0.f;
-    }
-    Io<WF>::load(a.W, (int64_t)p * a.ldw + q, nv, vec, c.w);
-    if constexpr (MF == FMT_S8) {
-      const float s = a.ms[(int64_t)p * (a.K / a.block) + q / a.block];
-      Io<FMT_S8>::load_codes(a.m, (int64_t)p * a.ldm + q, nv, vec, s, c.m);
-    } else {
-      Io<MF>::load(a.m, (int64_t)p * a.ldm + q, nv, vec, c.m);
-    }
+    const bool vec = a.vec_state != 0;
+    ld8<WF>(r.w, a.W, (int64_t)p * a.ldw + q, nv, vec);
+    ld8<MF>(r.m, a.m, (int64_t)p * a.ldm + q, nv, vec);
+    if constexpr (MF == FMT_S8) r.m.s = a.ms[(int64_t)p * (a.K / a.block) + q / a.block];
     if constexpr (HAS_V) {
-      if constexpr (VF == FMT_U8) {
-        const float s = a.vs[(int64_t)p * (a.K / a.block) + q / a.block];
-        Io<FMT_U8>::load_codes(a.v, (int64_t)p * a.ldv + q, nv, vec, s, c.v);
-      } else {
-        Io<VF>::load(a.v, (int64_t)p * a.ldv + q, nv, vec, c.v);
-      }
+      ld8<VF>(r.v, a.v, (int64_t)p * a.ldv + q, nv, vec);
+      if constexpr (VF == FMT_U8) r.v.s = a.vs[(int64_t)p * (a.K / a.block) + q / a.block];
     }
   }
 
   // The optimizer on one element, fp32 (Algorithm 1 Phase 2 for AdamW).
+  // sqrt and the reciprocal are the hardware instructions (<= 1 ulp).
   __device__ __forceinline__ static void phi(const EpiConst& k, float g, float& w, float& m, float& v) {
     if constexpr (OPT == OPT_ADAMW) {
-      m = fmaf(k.b1, m, k.omb1 * g);                  // m' = b1 m + (1-b1) G
-      v = fmaf(k.b2, v, k.omb2 * (g * g));            // v' = b2 v + (1-b2) G^2
-      const float den = fmaf(sqrtf(v), k.bc2s, k.eps);  // sqrt(v'/(1-b2^t)) + eps
-      const float upd = (m * k.bc1) / den;            // m_hat / den
-      w = fmaf(k.decay, w, -k.lr * upd);              // (1 - lr wd) W - lr upd
+      m = fmaf(k.b1, m, k.omb1 * g);                                 // m' = b1 m + (1-b1) G
+      v = fmaf(k.b2, v, k.omb2 * (g * g));                           // v' = b2 v + (1-b2) G^2
+      const float den = fmaf(__builtin_amdgcn_sqrtf(v), k.bc2s, k.eps);  // sqrt(v'/(1-b2^t)) + eps
+      const float upd = (m * k.bc1) * __builtin_amdgcn_rcpf(den);    // m_hat / den
+      w = fmaf(k.decay, w, -k.lr * upd);                             // (1 - lr wd) W - lr upd
     } else if constexpr (OPT == OPT_LION) {
-      const float c = fmaf(k.b1, m, k.omb1 * g);      // interpolation
+      const float c = fmaf(k.b1, m, k.omb1 * g);                     // interpolation
       const float s = c > 0.f ? 1.f : (c < 0.f ? -1.f : 0.f);
       w = fmaf(k.decay, w, -k.lr * s);
       m = fmaf(k.b2, m, k.omb2 * g);
-    } else {                                          // SGD with momentum
-      const float gg = fmaf(k.wd, w, g);              // coupled L2
-      m = fmaf(k.b1, m, gg);                          // b' = mu b + g
-      w = fmaf(-k.lr, m, w);                          // W - lr b'
+    } else {                                                         // SGD with momentum
+      const float gg = fmaf(k.wd, w, g);                             // coupled L2
+      m = fmaf(k.b1, m, gg);                                         // b' = mu b + g
+      w = fmaf(-k.lr, m, w);                                         // W - lr b'
     }
   }
 
-  // Apply phi to the chunk and store.  Must be called by every lane of the
-  // wave when a state is int8 (lane shuffles).
+  // Decode, apply phi and store one chunk.  Must be called by every lane of
+  // the wave when a state is int8 (lane shuffles).
   __device__ __forceinline__ static void apply_store(const KArgs& a, int p, int q, int nv, const float (&g)[8],
-                                                     Chunk& c) {
-    const bool valid = p < a.N && nv > 0;
+                                                     const Pending& r) {
+    float w[8], m[8], v[8];
+    dec8<WF>(r.w, w);
+    dec8<MF>(r.m, m);
+    dec8<VFMT>(r.v, v);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) phi(a.c, g[i], c.w[i], c.m[i], c.v[i]);
+    for (int i = 0; i < 8; ++i) phi(a.c, g[i], w[i], m[i], v[i]);
+    const bool valid = p < a.N && nv > 0;
     const bool vec = a.vec_state != 0;
     const uint32_t idx0 = (uint32_t)p * (uint32_t)a.K + (uint32_t)q;
-    if (valid) Io<WF>::store(a.W, (int64_t)p * a.ldw + q, nv, vec, c.w, a.c.sr, a.c.keyW, idx0);
+    if (valid) st8<WF>(a.W, (int64_t)p * a.ldw + q, nv, vec, w, a.c.sr, a.c.keyW, idx0);
     if constexpr (MF == FMT_S8) {
       const int lpb = a.block >> 3;
       const bool first = ((threadIdx.x & (lpb - 1)) == 0);
-      quantize8<true>(c.m, lpb, valid, a.m, (int64_t)p * a.ldm + q, vec,
+      quantize8<true>(m, lpb, valid, a.m, (int64_t)p * a.ldm + q, vec,
                       a.ms + (int64_t)p * (a.K / a.block) + q / a.block, first);
     } else {
-      if (valid) Io<MF>::store(a.m, (int64_t)p * a.ldm + q, nv, vec, c.m, a.c.sr, a.c.keyM, idx0);
+      if (valid) st8<MF>(a.m, (int64_t)p * a.ldm + q, nv, vec, m, a.c.sr, a.c.keyM, idx0);
     }
     if constexpr (HAS_V) {
       if constexpr (VF == FMT_U8) {
         const int lpb = a.block >> 3;
         const bool first = ((threadIdx.x & (lpb - 1)) == 0);
-        quantize8<false>(c.v, lpb, valid, a.v, (int64_t)p * a.ldv + q, vec,
+        quantize8<false>(v, lpb, valid, a.v, (int64_t)p * a.ldv + q, vec,
                          a.vs + (int64_t)p * (a.K / a.block) + q / a.block, first);
       } else {
-        if (valid) Io<VF>::store(a.v, (int64_t)p * a.ldv + q, nv, vec, c.v, a.c.sr, a.c.keyV, idx0);
+        if (valid) st8<VF>(a.v, (int64_t)p * a.ldv + q, nv, vec, v, a.c.sr, a.c.keyV, idx0);
       }
     }
   }
 };
 
-// Epilogue over one 128 x 128 tile: thread t owns, in pass s, the 8
-// elements of row (s*16 + t/16) starting at column 8*(t%16).  G comes from
-// the LDS staging buffer (fused) or from dW (unfused step kernel).
-template <class S, bool FROM_LDS>
+// Epilogue over one 128 x 128 tile: thread t owns, in pass s = 0..7, the 8
+// elements of row (s*16 + t/16) starting at column 8*(t%16).  The state of
+// DEPTH chunks is in flight at any time: chunk s+DEPTH is requested as soon
+// as chunk s has been decoded.  G comes from the LDS staging buffer (fused,
+// GF == FMT_NONE) or from the dW workspace in format GF (unfused).
+template <class S, int GF>
 __device__ __forceinline__ void tile_epilogue(const KArgs& a, const float* sG, int row0, int col0) {
+  constexpr int DEPTH = 4;
+  constexpr int PASSES = TILE * TILE / (8 * NT);  // 8
   const int tid = threadIdx.x;
   const int cl = (tid & 15) * 8;
   const int q = col0 + cl;
   const int nv = min(8, a.K - q);
-#pragma unroll 1
-  for (int half = 0; half < 2; ++half) {
-    Chunk c[4];
-    float g[4][8];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int rl = (half * 4 + s) * 16 + (tid >> 4);
-      S::load(a, row0 + rl, q, nv, c[s]);
-      if constexpr (FROM_LDS) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) g[s][i] = sG[rl * GP + cl + i];
-      } else {
-        const int p = row0 + rl;
-        const bool ok = p < a.N && nv > 0;
-        const int64_t off = (int64_t)p * a.K + q;
-        const bool vec = (a.K & 7) == 0;
-        if (!ok) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) g[s][i] = 0.f;
-        } else if (a.dw_fmt == FMT_F32) {
-          Io<FMT_F32>::load(a.dW, off, nv, vec, g[s]);
-        } else {
-          Io<FMT_BF16>::load(a.dW, off, nv, vec, g[s]);
-        }
-      }
+  const bool gvec = (a.K & 7) == 0;
+  typename S::Pending pend[DEPTH];
+  Raw8<GF == FMT_NONE ? FMT_F32 : GF> graw[DEPTH];
+  auto issue = [&](int s, int slot) {
+    const int p = row0 + s * 16 + (tid >> 4);
+    S::load(a, p, q, nv, pend[slot]);
+    if constexpr (GF != FMT_NONE) {
+      if (p < a.N && nv > 0) ld8<GF>(graw[slot], a.dW, (int64_t)p * a.K + q, nv, gvec);
+      else zero8(graw[slot]);
     }
+  };
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int rl = (half * 4 + s) * 16 + (tid >> 4);
-      S::apply_store(a, row0 + rl, q, nv, g[s], c[s]);
+  for (int s = 0; s < DEPTH; ++s) issue(s, s);
+#pragma unroll
+  for (int s = 0; s < PASSES; ++s) {
+    const int slot = s % DEPTH;
+    const int rl = s * 16 + (tid >> 4);
+    float g[8];
+    if constexpr (GF == FMT_NONE) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) g[i] = sG[rl * GP + cl + i];
+    } else {
+      dec8<GF>(graw[slot], g);
     }
+    const typename S::Pending cur = pend[slot];
+    if (s + DEPTH < PASSES) issue(s + DEPTH, slot);
+    S::apply_store(a, row0 + rl, q, nv, g, cur);
   }
 }
 
 // ------------------------------------------------------------------------
 // Kernels
 // ------------------------------------------------------------------------
-template <int IN, int OPT, int WF, int MF, int VF>
+// IN: input format; DMA: asynchronous direct-to-LDS mainloop (bf16 only).
+template <int IN, bool DMA, int OPT, int WF, int MF, int VF>
 __global__ void __launch_bounds__(NT, 2) k_fused(const KArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   int ti, tj;
   tile_coords(blockIdx.x, a.tiles_n, a.tiles_k, ti, tj);
   const int row0 = ti * TILE, col0 = tj * TILE;
-  tile_gradient<IN>(a, lds, row0, col0);
-  tile_epilogue<Step<OPT, WF, MF, VF>, true>(a, reinterpret_cast<const float*>(lds), row0, col0);
+  if constexpr (DMA) tile_gradient_dma(a, lds, row0, col0);
+  else tile_gradient<IN>(a, lds, row0, col0);
+  tile_epilogue<Step<OPT, WF, MF, VF>, FMT_NONE>(a, reinterpret_cast<const float*>(lds), row0, col0);
 }
 
-template <int IN>
+template <int IN, bool DMA>
 __global__ void __launch_bounds__(NT, 2) k_gemm(const KArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   int ti, tj;
   tile_coords(blockIdx.x, a.tiles_n, a.tiles_k, ti, tj);
   const int row0 = ti * TILE, col0 = tj * TILE;
-  tile_gradient<IN>(a, lds, row0, col0);
+  if constexpr (DMA) tile_gradient_dma(a, lds, row0, col0);
+  else tile_gradient<IN>(a, lds, row0, col0);
   const float* sG = reinterpret_cast<const float*>(lds);
   const int tid = threadIdx.x;
   const int cl = (tid & 15) * 8;
@@ -590,16 +818,16 @@ __global__ void __launch_bounds__(NT, 2) k_gemm(const KArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) g[i] = sG[rl * GP + cl + i];
     const int64_t off = (int64_t)p * a.K + q;
-    if (a.dw_fmt == FMT_F32) Io<FMT_F32>::store(a.dW, off, nv, vec, g, 0, 0, 0);
-    else Io<FMT_BF16>::store(a.dW, off, nv, vec, g, 0, 0, 0);
+    if (a.dw_fmt == FMT_F32) st8<FMT_F32>(a.dW, off, nv, vec, g, 0, 0, 0);
+    else st8<FMT_BF16>(a.dW, off, nv, vec, g, 0, 0, 0);
   }
 }
 
-template <int OPT, int WF, int MF, int VF>
+template <int GF, int OPT, int WF, int MF, int VF>
 __global__ void __launch_bounds__(NT, 2) k_step(const KArgs a) {
   int ti, tj;
   tile_coords(blockIdx.x, a.tiles_n, a.tiles_k, ti, tj);
-  tile_epilogue<Step<OPT, WF, MF, VF>, false>(a, nullptr, ti * TILE, tj * TILE);
+  tile_epilogue<Step<OPT, WF, MF, VF>, GF>(a, nullptr, ti * TILE, tj * TILE);
 }
 
 __global__ void k_debug_sr(const float* __restrict__ in, uint16_t* __restrict__ out, uint32_t n, uint32_t key) {
@@ -633,12 +861,12 @@ bool combo_supported(int in_fmt, int w_fmt, int opt, int m_fmt, int v_fmt) {
 
 static inline dim3 tile_grid(const KArgs& a) { return dim3((unsigned)(a.tiles_n * a.tiles_k)); }
 
-template <int IN, int WF>
+template <int IN, bool DMA, int WF>
 static hipError_t fused_w(const KArgs& a, int opt, int m_fmt, int v_fmt, hipStream_t st) {
-#define X(O, M, V)                                                                 \
-  if (opt == O && m_fmt == M && v_fmt == V) {                                      \
-    hipLaunchKernelGGL((k_fused<IN, O, WF, M, V>), tile_grid(a), dim3(NT), 0, st, a); \
-    return hipGetLastError();                                                      \
+#define X(O, M, V)                                                                      \
+  if (opt == O && m_fmt == M && v_fmt == V) {                                           \
+    hipLaunchKernelGGL((k_fused<IN, DMA, O, WF, M, V>), tile_grid(a), dim3(NT), 0, st, a); \
+    return hipGetLastError();                                                           \
   }
   FORGE_STATE_LIST(X)
 #undef X
@@ -646,29 +874,33 @@ static hipError_t fused_w(const KArgs& a, int opt, int m_fmt, int v_fmt, hipStre
 }
 
 hipError_t launch_fused(const KArgs& a, int in_fmt, int w_fmt, int opt, int m_fmt, int v_fmt, hipStream_t st) {
-  if (in_fmt == FMT_BF16) {
-    if (w_fmt == FMT_BF16) return fused_w<FMT_BF16, FMT_BF16>(a, opt, m_fmt, v_fmt, st);
-    if (w_fmt == FMT_F32) return fused_w<FMT_BF16, FMT_F32>(a, opt, m_fmt, v_fmt, st);
+  if (in_fmt == FMT_BF16 && a.dma_ok) {
+    if (w_fmt == FMT_BF16) return fused_w<FMT_BF16, true, FMT_BF16>(a, opt, m_fmt, v_fmt, st);
+    if (w_fmt == FMT_F32) return fused_w<FMT_BF16, true, FMT_F32>(a, opt, m_fmt, v_fmt, st);
+  } else if (in_fmt == FMT_BF16) {
+    if (w_fmt == FMT_BF16) return fused_w<FMT_BF16, false, FMT_BF16>(a, opt, m_fmt, v_fmt, st);
+    if (w_fmt == FMT_F32) return fused_w<FMT_BF16, false, FMT_F32>(a, opt, m_fmt, v_fmt, st);
   } else if (in_fmt == FMT_F32) {
-    if (w_fmt == FMT_BF16) return fused_w<FMT_F32, FMT_BF16>(a, opt, m_fmt, v_fmt, st);
-    if (w_fmt == FMT_F32) return fused_w<FMT_F32, FMT_F32>(a, opt, m_fmt, v_fmt, st);
+    if (w_fmt == FMT_BF16) return fused_w<FMT_F32, false, FMT_BF16>(a, opt, m_fmt, v_fmt, st);
+    if (w_fmt == FMT_F32) return fused_w<FMT_F32, false, FMT_F32>(a, opt, m_fmt, v_fmt, st);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm(const KArgs& a, int in_fmt, hipStream_t st) {
-  if (in_fmt == FMT_BF16) hipLaunchKernelGGL((k_gemm<FMT_BF16>), tile_grid(a), dim3(NT), 0, st, a);
-  else if (in_fmt == FMT_F32) hipLaunchKernelGGL((k_gemm<FMT_F32>), tile_grid(a), dim3(NT), 0, st, a);
+  if (in_fmt == FMT_BF16 && a.dma_ok) hipLaunchKernelGGL((k_gemm<FMT_BF16, true>), tile_grid(a), dim3(NT), 0, st, a);
+  else if (in_fmt == FMT_BF16) hipLaunchKernelGGL((k_gemm<FMT_BF16, false>), tile_grid(a), dim3(NT), 0, st, a);
+  else if (in_fmt == FMT_F32) hipLaunchKernelGGL((k_gemm<FMT_F32, false>), tile_grid(a), dim3(NT), 0, st, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
-template <int WF>
+template <int GF, int WF>
 static hipError_t step_w(const KArgs& a, int opt, int m_fmt, int v_fmt, hipStream_t st) {
-#define X(O, M, V)                                                              \
-  if (opt == O && m_fmt == M && v_fmt == V) {                                   \
-    hipLaunchKernelGGL((k_step<O, WF, M, V>), tile_grid(a), dim3(NT), 0, st, a); \
-    return hipGetLastError();                                                   \
+#define X(O, M, V)                                                                  \
+  if (opt == O && m_fmt == M && v_fmt == V) {                                       \
+    hipLaunchKernelGGL((k_step<GF, O, WF, M, V>), tile_grid(a), dim3(NT), 0, st, a); \
+    return hipGetLastError();                                                       \
   }
   FORGE_STATE_LIST(X)
 #undef X
@@ -676,8 +908,13 @@ static hipError_t step_w(const KArgs& a, int opt, int m_fmt, int v_fmt, hipStrea
 }
 
 hipError_t launch_step(const KArgs& a, int w_fmt, int opt, int m_fmt, int v_fmt, hipStream_t st) {
-  if (w_fmt == FMT_BF16) return step_w<FMT_BF16>(a, opt, m_fmt, v_fmt, st);
-  if (w_fmt == FMT_F32) return step_w<FMT_F32>(a, opt, m_fmt, v_fmt, st);
+  if (a.dw_fmt == FMT_F32) {
+    if (w_fmt == FMT_BF16) return step_w<FMT_F32, FMT_BF16>(a, opt, m_fmt, v_fmt, st);
+    if (w_fmt == FMT_F32) return step_w<FMT_F32, FMT_F32>(a, opt, m_fmt, v_fmt, st);
+  } else if (a.dw_fmt == FMT_BF16) {
+    if (w_fmt == FMT_BF16) return step_w<FMT_BF16, FMT_BF16>(a, opt, m_fmt, v_fmt, st);
+    if (w_fmt == FMT_F32) return step_w<FMT_BF16, FMT_F32>(a, opt, m_fmt, v_fmt, st);
+  }
   return hipErrorInvalidValue;
 }
 

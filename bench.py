@@ -1,0 +1,278 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused weight-gradient + AdamW step on one MI355X.
+
+One step = one fused forge_wgrad_step launch for each linear layer of a
+Llama-3.1-8B decoder layer (q, k, v, o, gate, up, down) at BT = 512 tokens
+(batch 1 x sequence 512): bf16 X / dY / W, fp32 m / v, AdamW with bias
+correction (step t = 10), stochastic-rounding bf16 weight store.  Inputs are
+seeded synthetic tensors with the real layer shapes (X ~ N(0, 1),
+dY ~ N(0, 1e-3^2), W ~ N(0, 0.02^2), m = 0, v = |N(0, 1e-6^2)|), resident in
+HBM before timing starts.
+
+Prints one JSON line: params/s over the whole step, the fused kernel's
+achieved HBM bandwidth against the 8 TB/s peak (algorithmic bytes: state read
+and written once plus X and dY read once, per launch, divided by the launch
+time measured with HIP events on the launch stream), the CPU oracle's
+throughput on a bounded sample, and the unfused baseline (G written to HBM,
+then the step) for comparison.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+BT = 512
+STEP_T = 10
+SEED = 1337
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_wgrad_llama8b_bt512_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "backward_weight_gradient_amd", "csrc", "forge_kernels.hip")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    p.add_argument("--no-unfused", action="store_true", help="skip the unfused comparison")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle work in seconds")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="instead of the step, time a plain 1 GiB device copy (read 1 GiB, write 1 GiB): the "
+                        "reference kernel for scaling HBM counter readings")
+    return p.parse_args()
+
+
+def copy_calibration(steps):
+    """A plain device-to-device copy of known size, for calibrating the
+    FETCH_SIZE / WRITE_SIZE counters against a kernel whose traffic is known."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms_per_copy": round(ms, 4),
+                      "copy_gbs": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+
+
+def layer_bytes(N, K, bt):
+    """Algorithmic HBM bytes of one fused launch: W bf16 (2+2), m and v fp32
+    (4+4 each) read and written once, X and dY (bf16) read once."""
+    P = N * K
+    return 20 * P + 2 * bt * (N + K)
+
+
+def kernel_sha():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic():
+    """HBM bytes per step measured with rocprofv3 counters, if they were taken
+    on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_sha():
+        return None
+    return t.get("hbm_bytes_per_step")
+
+
+def cpu_baseline(layers, seconds):
+    """The oracle on whole layers (k_proj first, then the others in turn)
+    until about `seconds` of CPU time are spent; params/s over them."""
+    import numpy as np
+    import oracle as O
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    order = ["k_proj", "v_proj", "q_proj", "o_proj", "gate_proj", "up_proj", "down_proj"]
+    done, params, t_total = [], 0, 0.0
+    spec = synth.LayerSpec(in_dtype="bf16", w_fmt="bf16", m_fmt="f32", v_fmt="f32")
+    hyp = O.Hyper(opt="adamw", round="sr")
+    for name in order:
+        N, K = layers[name]
+        X, dY = synth.activations(1, BT, N, K, STEP_T, extra=order.index(name))
+        st = synth.state(1, N, K, spec, extra=order.index(name))
+        Xh, dYh = synth.host(X), synth.host(dY)
+        W = O.Stored("bf16", synth.host(st["W"]))
+        m = O.Stored("f32", synth.host(st["m"]))
+        v = O.Stored("f32", synth.host(st["v"]))
+        t0 = time.perf_counter()
+        O.wgrad_step(Xh, dYh, W, m, v, hyp, STEP_T, SEED)
+        t_total += time.perf_counter() - t0
+        params += N * K
+        done.append(name)
+        if t_total >= seconds:
+            break
+    return {"value": params / t_total, "unit": "params/s", "cores": cores, "kind": "oracle",
+            "sample": f"whole layers {','.join(done)} at BT={BT} ({params} params, {t_total:.1f} s); "
+                      f"fp64 BLAS matmul on {cores} threads, element-wise step single-threaded NumPy"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1"}), flush=True)
+        sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.steps)
+        return
+
+    import torch
+    import backward_weight_gradient_amd as F
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    layers = synth.LLAMA8B_LAYERS
+    spec = synth.LayerSpec(in_dtype="bf16", w_fmt="bf16", m_fmt="f32", v_fmt="f32")
+    h = F.hyper("adamw", lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, round="sr")
+
+    L = {}
+    for i, (name, (N, K)) in enumerate(layers.items()):
+        X, dY = synth.activations(1, BT, N, K, STEP_T, device="cuda", extra=i)
+        st = synth.state(1, N, K, spec, device="cuda", extra=i)
+        L[name] = dict(N=N, K=K, X=X, dY=dY, W=st["W"], m=st["m"], v=st["v"],
+                       mst=F.state(st["m"]), vst=F.state(st["v"]), Xm=F.mat(X), dYm=F.mat(dY), Wm=F.mat(st["W"]))
+    torch.cuda.synchronize()
+    P_total = sum(N * K for N, K in layers.values())
+    bytes_total = sum(layer_bytes(N, K, BT) for N, K in layers.values())
+    flops_total = sum(2 * BT * N * K for N, K in layers.values())
+    names = list(layers)
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+
+    def launch(name):
+        d = L[name]
+        F.forge_wgrad_step(d["Xm"], d["dYm"], d["Wm"], d["mst"], d["vst"], h, STEP_T, SEED, stream=sptr)
+
+    for _ in range(args.warmup):
+        for n in names:
+            launch(n)
+    torch.cuda.synchronize()
+
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in names]
+          for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for s in range(args.steps):
+        for j, n in enumerate(names):
+            ev[s][j][0].record(stream)
+            launch(n)
+            ev[s][j][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    per_layer = {n: sorted(ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(args.steps))
+                 for j, n in enumerate(names)}
+    med = {n: v[len(v) // 2] for n, v in per_layer.items()}
+    kernel_ms = sum(sum(v) for v in per_layer.values()) / args.steps   # mean kernel time per step
+    achieved_gbs = bytes_total / (kernel_ms * 1e-3) / 1e9
+
+    traffic_step = load_traffic()
+    roofline = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+                "traffic": None if traffic_step is None else round(traffic_step / len(names))}
+
+    extras = {
+        "kernel": "forge::k_fused<bf16 in, AdamW, bf16 W, fp32 m, fp32 v>",
+        "launches_per_step": len(names),
+        "algorithmic_bytes_per_step": bytes_total,
+        "algorithmic_bytes_per_launch_mean": bytes_total / len(names),
+        "kernel_ms_per_step_mean": round(kernel_ms, 4),
+        "mfma_util": round(flops_total / (kernel_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "per_layer_us_median": {n: round(1e3 * v, 2) for n, v in med.items()},
+        "per_layer_gbs_median": {n: round(layer_bytes(*layers[n], BT) / (med[n] * 1e-3) / 1e9, 1) for n in names},
+    }
+
+    if not args.no_unfused:
+        # unfused baseline: G (fp32) to HBM, then the step; same layers, same protocol
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
+        base_alloc = torch.cuda.memory_allocated()
+        for n in names:
+            launch(n)
+        torch.cuda.synchronize()
+        peak_fused = torch.cuda.max_memory_allocated() - base_alloc
+        dws = {}
+        torch.cuda.reset_peak_memory_stats()
+        for n in names:
+            dws[n] = torch.empty((L[n]["N"], L[n]["K"]), device=dev, dtype=torch.float32)
+        for _ in range(max(1, args.warmup)):
+            for n in names:
+                d = L[n]
+                F.forge_wgrad_unfused(d["Xm"], d["dYm"], d["Wm"], d["mst"], d["vst"], h, STEP_T, SEED, dws[n],
+                                      stream=sptr)
+        torch.cuda.synchronize()
+        peak_unfused = torch.cuda.max_memory_allocated() - base_alloc
+        u0 = torch.cuda.Event(enable_timing=True)
+        u1 = torch.cuda.Event(enable_timing=True)
+        u0.record(stream)
+        for _ in range(args.steps):
+            for n in names:
+                d = L[n]
+                F.forge_wgrad_unfused(d["Xm"], d["dYm"], d["Wm"], d["mst"], d["vst"], h, STEP_T, SEED, dws[n],
+                                      stream=sptr)
+        u1.record(stream)
+        torch.cuda.synchronize()
+        extras["unfused_fp32_dw_ms_per_step"] = round(u0.elapsed_time(u1) / args.steps, 4)
+        extras["fused_speedup_vs_unfused"] = round(extras["unfused_fp32_dw_ms_per_step"] / ms_per_step, 3)
+        extras["peak_extra_bytes_fused"] = int(peak_fused)
+        extras["peak_extra_bytes_unfused_fp32_dw"] = int(peak_unfused)
+        del dws
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(layers, args.cpu_seconds)
+
+    out = {
+        "metric": "fused wgrad+AdamW params/s & HBM GB/s (% roofline), Llama-8B shapes, BT=512",
+        "value": P_total / (ms_per_step * 1e-3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "Llama-3.1-8B decoder-layer linears q,k,v,o,gate,up,down; BT=512 (BS 1 x SEQ 512); "
+                               "bf16 X/dY/W, fp32 m/v, AdamW t=10, SR bf16 W store",
+                   "global_batch": 1, "seq_len": BT, "params_per_step": P_total, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extras": extras,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
