@@ -202,11 +202,9 @@ KArgs make_args(const forge_mat* X, const forge_mat* dY, forge_mat* W, forge_sta
   a.dma_ok = (pl.in_fmt == FORGE_BF16 && a.vec_in && pl.N % 8 == 0 && pl.K % 8 == 0 &&
               (uint64_t)pl.BT * (uint64_t)dY->ld * 2 < (1ull << 31) &&
               (uint64_t)pl.BT * (uint64_t)X->ld * 2 < (1ull << 31)) ? 1 : 0;
-  // 8-element state accesses
-  bool vs = vec_ok(W->data, W->ld, 8, elem_size(pl.w_fmt)) && vec_ok(m->q.data, m->q.ld, 8, elem_size(pl.m_fmt));
-  if (v) vs = vs && vec_ok(v->q.data, v->q.ld, 8, elem_size(pl.v_fmt));
-  // fp32 rows are read as two 16-byte halves
-  if (pl.w_fmt == FORGE_F32) vs = vs && aligned(W->data, 16);
+  // 4-element state accesses (16 B fp32, 8 B bf16, 4 B int8)
+  bool vs = vec_ok(W->data, W->ld, 4, elem_size(pl.w_fmt)) && vec_ok(m->q.data, m->q.ld, 4, elem_size(pl.m_fmt));
+  if (v) vs = vs && vec_ok(v->q.data, v->q.ld, 4, elem_size(pl.v_fmt));
   a.vec_state = vs ? 1 : 0;
   // scalars, in double, rounded once
   const double lr = h->lr, b1 = h->beta1, b2 = h->beta2, wd = h->weight_decay;

@@ -19,10 +19,10 @@
 // v_mfma_f32_32x32x2_f32 straight from a row-major LDS copy.
 //
 // Epilogue: the fp32 accumulators are staged through LDS so that each
-// thread owns 8 consecutive elements of a row; W / m / v are then read and
-// written with 16-byte accesses, and an int8 block (<= 128 elements of one
-// row) is owned by <= 16 adjacent lanes, which reduce its absmax with lane
-// shuffles.  The element-wise step is written once (Step::apply_store) and is used
+// thread owns two 4-element segments of a row; the 16 lanes of a row read
+// and write W / m / v in contiguous 64-element runs, and an int8 block (<=
+// 128 elements of one row) is owned by <= 16 adjacent lanes, which reduce
+// its absmax with lane shuffles.  The element-wise step is written once (Step::apply_store) and is used
 // by the fused kernel and by the unfused baseline's step kernel alike, so
 // the two are bit-identical when the baseline keeps G in fp32 (paper,
 // Corollary 1(a)).
@@ -64,41 +64,55 @@ __device__ __forceinline__ uint32_t fmix32(uint32_t h) {
   return h;
 }
 
-__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;  // quiet NaN
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+// fp32 -> bf16 bit patterns, branch-free.  Round to nearest even adds
+// 0x7FFF plus the kept half's lowest bit and truncates.  Stochastic rounding
+// adds 16 random bits instead and truncates: the carry into the kept half
+// happens with probability (x - x_lo)/ULP.  Inf and NaN keep their pattern
+// (NaN made quiet) in both modes.
+__device__ __forceinline__ uint32_t bf16_bits_add(float x, uint32_t add) {
+  const uint32_t u = __float_as_uint(x);
+  const bool finite = (u & 0x7F800000u) != 0x7F800000u;
+  const bool nan = (u & 0x7FFFFFFFu) > 0x7F800000u;
+  return finite ? (u + add) >> 16 : ((u >> 16) | (nan ? 0x40u : 0u));
 }
 
-// Stochastic rounding: add 16 random bits below the bf16 cut and truncate;
-// the carry into the kept half happens with probability (x - x_lo)/ULP.
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
+  return bf16_bits_add(x, 0x7FFFu + ((__float_as_uint(x) >> 16) & 1u));
+}
+
+// The SR bits are the top half of fmix32(key ^ (idx * 0x9E3779B9)); callers
+// that round consecutive indices pass idx * 0x9E3779B9 (mod 2^32) directly
+// and step it by adding the constant.
+__device__ __forceinline__ uint32_t bf16_sr_bits_m(float x, uint32_t key, uint32_t idx_mul) {
+  return bf16_bits_add(x, fmix32(key ^ idx_mul) >> 16);
+}
 __device__ __forceinline__ uint32_t bf16_sr_bits(float x, uint32_t key, uint32_t idx) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7F800000u) == 0x7F800000u) return bf16_rne_bits(x);  // Inf / NaN
-  uint32_t r = fmix32(key ^ (idx * GOLDEN)) >> 16;
-  return (u + r) >> 16;
+  return bf16_sr_bits_m(x, key, idx * GOLDEN);
+}
+
+// sr != 0 (wave-uniform): stochastic rounding, else round to nearest even.
+__device__ __forceinline__ uint32_t bf16_store_bits(float x, int sr, uint32_t key, uint32_t idx_mul) {
+  const uint32_t rne_add = 0x7FFFu + ((__float_as_uint(x) >> 16) & 1u);
+  const uint32_t sr_add = fmix32(key ^ idx_mul) >> 16;
+  return bf16_bits_add(x, sr ? sr_add : rne_add);
 }
 
 __device__ __forceinline__ float bf16_val(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
 // ------------------------------------------------------------------------
-// Tile order: workgroup b runs on XCD b % 8; give each XCD a contiguous
-// range of logical tiles, and walk that range in groups of GROUP tile rows so
-// that neighbouring workgroups share the activation panels in that XCD's L2.
+// Tile order: row-major over the tile grid.  The tiles in flight across the
+// whole chip then cover whole rows of W / m / v, which is what the HBM
+// streams best (measured on MI355X: ~6.0 TB/s for the state stream of a
+// 14336 x 4096 layer in row-major tile order, 5.5 TB/s when every XCD is
+// given its own contiguous block of tiles, 4.7 TB/s in column-major
+// order).  Workgroups are dispatched round-robin to the 8 XCDs, so each
+// XCD still sees every 8th tile of a few consecutive tile rows: its L2
+// holds the dY panels of those rows and a quarter of the X panels.
 // ------------------------------------------------------------------------
 __device__ __forceinline__ void tile_coords(int bid, int tiles_n, int tiles_k, int& ti, int& tj) {
-  const int T = tiles_n * tiles_k;
-  const int x = bid & 7, pos = bid >> 3;
-  const int q = T >> 3, r = T & 7;
-  const int logical = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + pos;
-  constexpr int GROUP = 8;
-  const int gsize = GROUP * tiles_k;
-  const int g = logical / gsize;
-  const int first = g * GROUP;
-  const int rows = min(tiles_n - first, GROUP);
-  const int in = logical - g * gsize;
-  ti = first + in % rows;
-  tj = in / rows;
+  (void)tiles_n;
+  ti = bid / tiles_k;
+  tj = bid - ti * tiles_k;
 }
 
 // ------------------------------------------------------------------------
@@ -308,6 +322,8 @@ __device__ __forceinline__ void bar() {
 }
 
 // Phase 1 with the asynchronous mainloop; same output as tile_gradient.
+// The vmcnt waits count this wave's loads in issue order, so no other
+// global load may be in flight while the mainloop runs.
 __device__ __forceinline__ void tile_gradient_dma(const KArgs& a, char* lds, int row0, int col0) {
   using M = MainBF16Dma;
   static_assert(M::S * M::STAGE <= LDS_BYTES, "LDS budget");
@@ -492,17 +508,23 @@ __device__ __forceinline__ void tile_gradient(const KArgs& a, char* lds, int row
 }
 
 // ------------------------------------------------------------------------
-// Element-wise step on 8 consecutive elements of one row (Algorithm 1
-// Phase 2 and 3; Appendix N families)
+// Element-wise step (Algorithm 1 Phase 2 and 3; Appendix N families)
+//
+// Epilogue thread mapping: in pass s (0..7) thread t owns row
+// s*16 + t/16 of the tile and two 4-element segments of it, at columns
+// 4*(t%16) and 64 + 4*(t%16).  The 16 lanes of a row therefore access one
+// contiguous 64-element run per instruction (whole 128-byte lines for
+// every format but int8), and a row's 128 columns stay within 16 lanes for
+// the int8 block reduction.
 // ------------------------------------------------------------------------
-// Raw (undecoded) storage of 8 consecutive elements, so that the loads of
-// later chunks can be in flight while earlier chunks are computed.
-template <int FMT> struct Raw8;
-template <> struct Raw8<FMT_F32> { f32x4 lo, hi; };
-template <> struct Raw8<FMT_BF16> { u32x4 w; };
-template <> struct Raw8<FMT_S8> { u32x2 w; float s; };
-template <> struct Raw8<FMT_U8> { u32x2 w; float s; };
-template <> struct Raw8<FMT_NONE> {};
+// Raw (undecoded) storage of 4 consecutive elements, so that the loads of
+// later passes can be in flight while earlier ones are computed.
+template <int FMT> struct Raw4;
+template <> struct Raw4<FMT_F32> { f32x4 v; };
+template <> struct Raw4<FMT_BF16> { u32x2 v; };
+template <> struct Raw4<FMT_S8> { uint32_t v; float s; };
+template <> struct Raw4<FMT_U8> { uint32_t v; float s; };
+template <> struct Raw4<FMT_NONE> {};
 
 // State tensors are streamed once per step: their accesses are marked
 // non-temporal so that they do not evict the activation panels the
@@ -514,170 +536,201 @@ template <typename T> __device__ __forceinline__ void st_nt(void* p, T v) {
   __builtin_nontemporal_store(v, reinterpret_cast<T*>(p));
 }
 
-// Load 8 elements at element offset `off`; `nv` (<= 8) of them are valid;
-// `vec`: the row allows one aligned vector access.  Invalid ones read as 0.
-template <int FMT>
-__device__ __forceinline__ void ld8(Raw8<FMT>& r, const void* base, int64_t off, int nv, bool vec) {
+// Element offsets of one thread's segment in the current pass.
+//  FAST: rows allow aligned 4-element vector accesses and K % 4 == 0, so a
+//        segment is either entirely inside the matrix or entirely outside;
+//        only `ok` is consulted.
+//  otherwise: `nv` (0..4) elements are inside; accesses are element-wise
+//        unless `vec` and nv == 4.
+struct Seg {
+  bool ok;      // row < N and at least one column inside
+  int nv;       // valid elements (<= 4)
+  int q;        // first column
+};
+
+template <int FMT, bool FAST>
+__device__ __forceinline__ void ld4(Raw4<FMT>& r, const void* row, const Seg& g, bool vec) {
   if constexpr (FMT == FMT_F32) {
-    const float* p = static_cast<const float*>(base) + off;
-    if (vec && nv == 8) {
-      r.lo = ld_nt<f32x4>(p);
-      r.hi = ld_nt<f32x4>(p + 4);
+    const float* p = static_cast<const float*>(row) + g.q;
+    if (FAST || (vec && g.nv == 4)) {
+      r.v = ld_nt<f32x4>(p);
     } else {
-      float x[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = i < nv ? p[i] : 0.f;
-      r.lo = f32x4{x[0], x[1], x[2], x[3]};
-      r.hi = f32x4{x[4], x[5], x[6], x[7]};
+      for (int i = 0; i < 4; ++i) r.v[i] = i < g.nv ? p[i] : 0.f;
     }
   } else if constexpr (FMT == FMT_BF16) {
-    const uint16_t* p = static_cast<const uint16_t*>(base) + off;
-    if (vec && nv == 8) {
-      r.w = ld_nt<u32x4>(p);
+    const uint16_t* p = static_cast<const uint16_t*>(row) + g.q;
+    if (FAST || (vec && g.nv == 4)) {
+      r.v = ld_nt<u32x2>(p);
     } else {
-      uint32_t e[8];
+      uint32_t e[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) e[i] = i < nv ? (uint32_t)p[i] : 0u;
-      r.w = u32x4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+      for (int i = 0; i < 4; ++i) e[i] = i < g.nv ? (uint32_t)p[i] : 0u;
+      r.v = u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
     }
   } else if constexpr (FMT == FMT_S8 || FMT == FMT_U8) {
-    const uint8_t* p = static_cast<const uint8_t*>(base) + off;
-    if (vec && nv == 8) {
-      r.w = ld_nt<u32x2>(p);
+    const uint8_t* p = static_cast<const uint8_t*>(row) + g.q;
+    if (FAST || (vec && g.nv == 4)) {
+      r.v = ld_nt<uint32_t>(p);
     } else {
-      uint32_t e[8];
+      uint32_t e[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) e[i] = i < nv ? (uint32_t)p[i] : 0u;
-      r.w = u32x2{e[0] | (e[1] << 8) | (e[2] << 16) | (e[3] << 24), e[4] | (e[5] << 8) | (e[6] << 16) | (e[7] << 24)};
+      for (int i = 0; i < 4; ++i) e[i] = i < g.nv ? (uint32_t)p[i] : 0u;
+      r.v = e[0] | (e[1] << 8) | (e[2] << 16) | (e[3] << 24);
     }
   }
 }
 
 template <int FMT>
-__device__ __forceinline__ void zero8(Raw8<FMT>& r) {
-  if constexpr (FMT == FMT_F32) { r.lo = f32x4{0.f, 0.f, 0.f, 0.f}; r.hi = r.lo; }
-  else if constexpr (FMT == FMT_BF16) { r.w = u32x4{0u, 0u, 0u, 0u}; }
-  else if constexpr (FMT == FMT_S8 || FMT == FMT_U8) { r.w = u32x2{0u, 0u}; r.s = 0.f; }
+__device__ __forceinline__ void zero4(Raw4<FMT>& r) {
+  if constexpr (FMT == FMT_F32) r.v = f32x4{0.f, 0.f, 0.f, 0.f};
+  else if constexpr (FMT == FMT_BF16) r.v = u32x2{0u, 0u};
+  else if constexpr (FMT == FMT_S8 || FMT == FMT_U8) { r.v = 0u; r.s = 0.f; }
 }
 
 // Decode to fp32; int8 codes are dequantised as code * scale (one fp32 multiply).
 template <int FMT>
-__device__ __forceinline__ void dec8(const Raw8<FMT>& r, float (&x)[8]) {
+__device__ __forceinline__ void dec4(const Raw4<FMT>& r, float* x) {
   if constexpr (FMT == FMT_F32) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { x[i] = r.lo[i]; x[i + 4] = r.hi[i]; }
+    for (int i = 0; i < 4; ++i) x[i] = r.v[i];
   } else if constexpr (FMT == FMT_BF16) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[2 * i] = __uint_as_float(r.w[i] << 16);
-      x[2 * i + 1] = __uint_as_float(r.w[i] & 0xFFFF0000u);
+    for (int i = 0; i < 2; ++i) {
+      x[2 * i] = __uint_as_float(r.v[i] << 16);
+      x[2 * i + 1] = __uint_as_float(r.v[i] & 0xFFFF0000u);
     }
   } else if constexpr (FMT == FMT_S8) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = (float)(int8_t)((r.w[i >> 2] >> (8 * (i & 3))) & 0xFFu) * r.s;
+    for (int i = 0; i < 4; ++i) x[i] = (float)(int8_t)((r.v >> (8 * i)) & 0xFFu) * r.s;
   } else if constexpr (FMT == FMT_U8) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = (float)((r.w[i >> 2] >> (8 * (i & 3))) & 0xFFu) * r.s;
+    for (int i = 0; i < 4; ++i) x[i] = (float)((r.v >> (8 * i)) & 0xFFu) * r.s;
   } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = 0.f;
+    for (int i = 0; i < 4; ++i) x[i] = 0.f;
   }
 }
 
-// Store 8 fp32 values as FMT (int8 formats go through quantize8 instead).
-// bf16: stochastic rounding keyed on (key, idx0 + i) when sr != 0, else RNE.
-template <int FMT>
-__device__ __forceinline__ void st8(void* base, int64_t off, int nv, bool vec, const float (&x)[8], int sr,
-                                    uint32_t key, uint32_t idx0) {
+// Store 4 fp32 values as FMT (int8 formats go through quantize_chunk instead).
+// bf16: stochastic rounding when sr != 0 (idx_mul = flat index of the first
+// element times 0x9E3779B9), else round to nearest even.
+template <int FMT, bool FAST>
+__device__ __forceinline__ void st4(void* row, const Seg& g, bool vec, const float* x, int sr, uint32_t key,
+                                    uint32_t idx_mul) {
   if constexpr (FMT == FMT_F32) {
-    float* p = static_cast<float*>(base) + off;
-    if (vec && nv == 8) {
+    float* p = static_cast<float*>(row) + g.q;
+    if (FAST || (vec && g.nv == 4)) {
       st_nt<f32x4>(p, f32x4{x[0], x[1], x[2], x[3]});
-      st_nt<f32x4>(p + 4, f32x4{x[4], x[5], x[6], x[7]});
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (i < nv) p[i] = x[i];
+      for (int i = 0; i < 4; ++i)
+        if (i < g.nv) p[i] = x[i];
     }
   } else if constexpr (FMT == FMT_BF16) {
-    uint32_t b[8];
+    uint32_t b[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) b[i] = sr ? bf16_sr_bits(x[i], key, idx0 + i) : bf16_rne_bits(x[i]);
-    uint16_t* p = static_cast<uint16_t*>(base) + off;
-    if (vec && nv == 8) {
-      st_nt<u32x4>(p, u32x4{b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16)});
+    for (int i = 0; i < 4; ++i) b[i] = bf16_store_bits(x[i], sr, key, idx_mul + (uint32_t)i * GOLDEN);
+    uint16_t* p = static_cast<uint16_t*>(row) + g.q;
+    if (FAST || (vec && g.nv == 4)) {
+      st_nt<u32x2>(p, u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)});
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (i < nv) p[i] = (uint16_t)b[i];
+      for (int i = 0; i < 4; ++i)
+        if (i < g.nv) p[i] = (uint16_t)b[i];
     }
   }
 }
 
-// Block-absmax quantisation of 8 values per lane; a block is `lpb` adjacent
-// lanes (lpb = block / 8, a power of two <= 16).  Every lane of the wave
-// must call this (lane shuffles).  SIGNED: codes -127..127, scale a/127.
-// Unsigned: code 0 only for an exact zero, else 1..255, scale a/255.  The
-// scale and the reciprocal are correctly rounded fp32 divisions.
+// Block-absmax quantisation of a chunk (two 4-element segments 64 columns
+// apart).  block == 128: one block spans both segments of the 16 lanes of
+// a row; block 32 / 64: each segment lies in its own block, shared by
+// block/4 adjacent lanes.  Every lane of the wave must call this (lane
+// shuffles).  SIGNED: codes -127..127, scale a/127.  Unsigned: code 0 only
+// for an exact zero, else 1..255, scale a/255.  The scale and the
+// reciprocal are correctly rounded fp32 divisions.  Int8 states need
+// K % block == 0, so a segment is either entirely inside or outside.
 template <bool SIGNED>
-__device__ __forceinline__ void quantize8(const float (&x)[8], int lpb, bool valid, void* codes_base,
-                                          int64_t off, bool vec, float* scale_ptr, bool write_scale) {
-  float a = 0.f;
+__device__ __forceinline__ void quantize_chunk(const float (&x)[8], int block, const Seg (&sg)[2], void* row_codes,
+                                               bool vec, float* row_scales) {
+  float a[2];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) a = fmaxf(a, SIGNED ? fabsf(x[i]) : x[i]);
-  if (!valid) a = 0.f;
-  for (int o = 1; o < lpb; o <<= 1) a = fmaxf(a, __shfl_xor(a, o));
-  const float qmax = SIGNED ? 127.f : 255.f;
-  const float s = a > 0.f ? a / qmax : 0.f;
-  const float inv = a > 0.f ? qmax / a : 0.f;
-  uint32_t q[8];
+  for (int g = 0; g < 2; ++g) {
+    float m = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float r = rintf(x[i] * inv);
-    if (SIGNED) {
-      r = fminf(fmaxf(r, -127.f), 127.f);
-      q[i] = (uint32_t)(int32_t)r & 0xFFu;
-    } else {
-      r = fminf(fmaxf(r, 1.f), 255.f);
-      q[i] = x[i] == 0.f ? 0u : (uint32_t)r;
-    }
+    for (int i = 0; i < 4; ++i) m = fmaxf(m, SIGNED ? fabsf(x[4 * g + i]) : x[4 * g + i]);
+    a[g] = sg[g].ok ? m : 0.f;
   }
-  if (!valid) return;
-  if (write_scale) *scale_ptr = s;
-  uint8_t* p = static_cast<uint8_t*>(codes_base) + off;
-  if (vec) {
-    st_nt<u32x2>(p, u32x2{q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24),
-                          q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24)});
-  } else {
+  const int lpb = block == 128 ? 16 : block >> 2;
+  if (block == 128) a[0] = a[1] = fmaxf(a[0], a[1]);
+  for (int o = 1; o < lpb; o <<= 1) {
+    a[0] = fmaxf(a[0], __shfl_xor(a[0], o));
+    a[1] = fmaxf(a[1], __shfl_xor(a[1], o));
+  }
+  const float qmax = SIGNED ? 127.f : 255.f;
+  const bool writer = (threadIdx.x & (lpb - 1)) == 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) p[i] = (uint8_t)q[i];
+  for (int g = 0; g < 2; ++g) {
+    const float sc = a[g] > 0.f ? a[g] / qmax : 0.f;
+    const float inv = a[g] > 0.f ? qmax / a[g] : 0.f;
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float xv = x[4 * g + i];
+      float r = rintf(xv * inv);
+      uint32_t c;
+      if (SIGNED) {
+        r = fminf(fmaxf(r, -127.f), 127.f);
+        c = (uint32_t)(int32_t)r & 0xFFu;
+      } else {
+        r = fminf(fmaxf(r, 1.f), 255.f);
+        c = xv == 0.f ? 0u : (uint32_t)r;
+      }
+      word |= c << (8 * i);
+    }
+    if (!sg[g].ok) continue;
+    if (writer && (block != 128 || g == 0)) row_scales[sg[g].q / block] = sc;
+    uint8_t* p = static_cast<uint8_t*>(row_codes) + sg[g].q;
+    if (vec) {
+      st_nt<uint32_t>(p, word);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = (uint8_t)((word >> (8 * i)) & 0xFFu);
+    }
   }
 }
 
-template <int OPT, int WF, int MF, int VF>
+template <int OPT, int WF, int MF, int VF, bool FAST>
 struct Step {
   static constexpr bool HAS_V = (OPT == OPT_ADAMW);
   static constexpr int VFMT = HAS_V ? VF : FMT_NONE;
 
   // Everything one chunk reads, still undecoded.
   struct Pending {
-    Raw8<WF> w;
-    Raw8<MF> m;
-    Raw8<VFMT> v;
+    Raw4<WF> w[2];
+    Raw4<MF> m[2];
+    Raw4<VFMT> v[2];
   };
 
-  __device__ __forceinline__ static void load(const KArgs& a, int p, int q, int nv, Pending& r) {
-    if (p >= a.N || nv <= 0) {
-      zero8(r.w); zero8(r.m); zero8(r.v);
-      return;
-    }
+  __device__ __forceinline__ static void load(const KArgs& a, int p, const Seg (&sg)[2], Pending& r) {
     const bool vec = a.vec_state != 0;
-    ld8<WF>(r.w, a.W, (int64_t)p * a.ldw + q, nv, vec);
-    ld8<MF>(r.m, a.m, (int64_t)p * a.ldm + q, nv, vec);
-    if constexpr (MF == FMT_S8) r.m.s = a.ms[(int64_t)p * (a.K / a.block) + q / a.block];
-    if constexpr (HAS_V) {
-      ld8<VF>(r.v, a.v, (int64_t)p * a.ldv + q, nv, vec);
-      if constexpr (VF == FMT_U8) r.v.s = a.vs[(int64_t)p * (a.K / a.block) + q / a.block];
+    const char* rw = static_cast<const char*>(a.W) + (int64_t)p * a.ldw * (WF == FMT_F32 ? 4 : 2);
+    const char* rm = static_cast<const char*>(a.m) + (int64_t)p * a.ldm * (MF == FMT_F32 ? 4 : MF == FMT_BF16 ? 2 : 1);
+    const char* rv = static_cast<const char*>(a.v) + (int64_t)p * a.ldv * (VF == FMT_F32 ? 4 : VF == FMT_BF16 ? 2 : 1);
+    const int64_t srow = (int64_t)p * (a.K / a.block);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      if (!sg[g].ok) {
+        zero4(r.w[g]); zero4(r.m[g]); zero4(r.v[g]);
+        continue;
+      }
+      ld4<WF, FAST>(r.w[g], rw, sg[g], vec);
+      ld4<MF, FAST>(r.m[g], rm, sg[g], vec);
+      if constexpr (MF == FMT_S8) r.m[g].s = a.ms[srow + sg[g].q / a.block];
+      if constexpr (HAS_V) {
+        ld4<VF, FAST>(r.v[g], rv, sg[g], vec);
+        if constexpr (VF == FMT_U8) r.v[g].s = a.vs[srow + sg[g].q / a.block];
+      }
     }
   }
 
@@ -685,114 +738,151 @@ struct Step {
   // sqrt and the reciprocal are the hardware instructions (<= 1 ulp).
   __device__ __forceinline__ static void phi(const EpiConst& k, float g, float& w, float& m, float& v) {
     if constexpr (OPT == OPT_ADAMW) {
-      m = fmaf(k.b1, m, k.omb1 * g);                                 // m' = b1 m + (1-b1) G
-      v = fmaf(k.b2, v, k.omb2 * (g * g));                           // v' = b2 v + (1-b2) G^2
+      m = fmaf(k.b1, m, k.omb1 * g);                                     // m' = b1 m + (1-b1) G
+      v = fmaf(k.b2, v, k.omb2 * (g * g));                               // v' = b2 v + (1-b2) G^2
       const float den = fmaf(__builtin_amdgcn_sqrtf(v), k.bc2s, k.eps);  // sqrt(v'/(1-b2^t)) + eps
-      const float upd = (m * k.bc1) * __builtin_amdgcn_rcpf(den);    // m_hat / den
-      w = fmaf(k.decay, w, -k.lr * upd);                             // (1 - lr wd) W - lr upd
+      const float upd = (m * k.bc1) * __builtin_amdgcn_rcpf(den);        // m_hat / den
+      w = fmaf(k.decay, w, -k.lr * upd);                                 // (1 - lr wd) W - lr upd
     } else if constexpr (OPT == OPT_LION) {
-      const float c = fmaf(k.b1, m, k.omb1 * g);                     // interpolation
+      const float c = fmaf(k.b1, m, k.omb1 * g);                         // interpolation
       const float s = c > 0.f ? 1.f : (c < 0.f ? -1.f : 0.f);
       w = fmaf(k.decay, w, -k.lr * s);
       m = fmaf(k.b2, m, k.omb2 * g);
-    } else {                                                         // SGD with momentum
-      const float gg = fmaf(k.wd, w, g);                             // coupled L2
-      m = fmaf(k.b1, m, gg);                                         // b' = mu b + g
-      w = fmaf(-k.lr, m, w);                                         // W - lr b'
+    } else {                                                             // SGD with momentum
+      const float gg = fmaf(k.wd, w, g);                                 // coupled L2
+      m = fmaf(k.b1, m, gg);                                             // b' = mu b + g
+      w = fmaf(-k.lr, m, w);                                             // W - lr b'
     }
   }
 
-  // Decode, apply phi and store one chunk.  Must be called by every lane of
-  // the wave when a state is int8 (lane shuffles).
-  __device__ __forceinline__ static void apply_store(const KArgs& a, int p, int q, int nv, const float (&g)[8],
+  // Decode, apply phi and store one chunk of row p.  Must be called by every
+  // lane of the wave when a state is int8 (lane shuffles).
+  __device__ __forceinline__ static void apply_store(const KArgs& a, int p, const Seg (&sg)[2], const float (&g)[8],
                                                      const Pending& r) {
     float w[8], m[8], v[8];
-    dec8<WF>(r.w, w);
-    dec8<MF>(r.m, m);
-    dec8<VFMT>(r.v, v);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      dec4<WF>(r.w[s], w + 4 * s);
+      dec4<MF>(r.m[s], m + 4 * s);
+      dec4<VFMT>(r.v[s], v + 4 * s);
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) phi(a.c, g[i], w[i], m[i], v[i]);
-    const bool valid = p < a.N && nv > 0;
     const bool vec = a.vec_state != 0;
-    const uint32_t idx0 = (uint32_t)p * (uint32_t)a.K + (uint32_t)q;
-    if (valid) st8<WF>(a.W, (int64_t)p * a.ldw + q, nv, vec, w, a.c.sr, a.c.keyW, idx0);
-    if constexpr (MF == FMT_S8) {
-      const int lpb = a.block >> 3;
-      const bool first = ((threadIdx.x & (lpb - 1)) == 0);
-      quantize8<true>(m, lpb, valid, a.m, (int64_t)p * a.ldm + q, vec,
-                      a.ms + (int64_t)p * (a.K / a.block) + q / a.block, first);
-    } else {
-      if (valid) st8<MF>(a.m, (int64_t)p * a.ldm + q, nv, vec, m, a.c.sr, a.c.keyM, idx0);
+    char* rw = static_cast<char*>(a.W) + (int64_t)p * a.ldw * (WF == FMT_F32 ? 4 : 2);
+    char* rm = static_cast<char*>(a.m) + (int64_t)p * a.ldm * (MF == FMT_F32 ? 4 : MF == FMT_BF16 ? 2 : 1);
+    char* rv = static_cast<char*>(a.v) + (int64_t)p * a.ldv * (VF == FMT_F32 ? 4 : VF == FMT_BF16 ? 2 : 1);
+    const uint32_t rowbase = (uint32_t)p * (uint32_t)a.K;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if (!sg[s].ok) continue;
+      const uint32_t idx_mul = (rowbase + (uint32_t)sg[s].q) * GOLDEN;
+      st4<WF, FAST>(rw, sg[s], vec, w + 4 * s, a.c.sr, a.c.keyW, idx_mul);
+      if constexpr (MF != FMT_S8) st4<MF, FAST>(rm, sg[s], vec, m + 4 * s, a.c.sr, a.c.keyM, idx_mul);
+      if constexpr (HAS_V && VF != FMT_U8) st4<VF, FAST>(rv, sg[s], vec, v + 4 * s, a.c.sr, a.c.keyV, idx_mul);
     }
-    if constexpr (HAS_V) {
-      if constexpr (VF == FMT_U8) {
-        const int lpb = a.block >> 3;
-        const bool first = ((threadIdx.x & (lpb - 1)) == 0);
-        quantize8<false>(v, lpb, valid, a.v, (int64_t)p * a.ldv + q, vec,
-                         a.vs + (int64_t)p * (a.K / a.block) + q / a.block, first);
-      } else {
-        if (valid) st8<VF>(a.v, (int64_t)p * a.ldv + q, nv, vec, v, a.c.sr, a.c.keyV, idx0);
+    const int64_t srow = (int64_t)p * (a.K / a.block);
+    if constexpr (MF == FMT_S8) quantize_chunk<true>(m, a.block, sg, rm, vec, a.ms + srow);
+    if constexpr (HAS_V && VF == FMT_U8) quantize_chunk<false>(v, a.block, sg, rv, vec, a.vs + srow);
+  }
+};
+
+// Epilogue over one 128 x 128 tile.  Thread mapping: in pass s (0..7)
+// thread t owns row s*16 + t/16 of the tile and two 4-element segments of
+// it, at columns 4*(t%16) and 64 + 4*(t%16); the 16 lanes of a row access
+// one contiguous 64-element run per instruction (whole 128-byte lines for
+// every format but int8), and a row's 128 columns stay within 16 lanes for
+// the int8 block reduction.  The state of DEPTH passes is in flight at any
+// time: pass s+DEPTH is requested as soon as pass s has been taken out of
+// its slot.  start() issues the first DEPTH passes; finish() runs the
+// rolling loop.  G comes from the LDS staging buffer (GF == FMT_NONE) or
+// from the dW workspace in format GF (unfused baseline).
+template <class S, int GF, bool FAST>
+struct Epilogue {
+  static constexpr int DEPTH = 4;
+  static constexpr int PASSES = TILE * TILE / (8 * NT);  // 8
+  typename S::Pending pend[DEPTH];
+  Raw4<GF> graw[DEPTH][2];
+  int cl;
+  Seg col[2];   // column part of the segments (row validity added per pass)
+
+  __device__ __forceinline__ void segs(const KArgs& a, int p, Seg (&sg)[2]) const {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      sg[g] = col[g];
+      sg[g].ok = col[g].ok && p < a.N;
+    }
+  }
+
+  __device__ __forceinline__ void issue(const KArgs& a, int row0, int s, int slot) {
+    const int p = row0 + s * 16 + (threadIdx.x >> 4);
+    Seg sg[2];
+    segs(a, p, sg);
+    S::load(a, p, sg, pend[slot]);
+    if constexpr (GF != FMT_NONE) {
+      const bool gvec = (a.K & 3) == 0;
+      const char* rg = static_cast<const char*>(a.dW) + (int64_t)p * a.K * (GF == FMT_F32 ? 4 : 2);
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        if (sg[g].ok) ld4<GF, FAST>(graw[slot][g], rg, sg[g], gvec);
+        else zero4(graw[slot][g]);
       }
+    }
+  }
+
+  __device__ __forceinline__ void start(const KArgs& a, int row0, int col0) {
+    cl = 4 * (threadIdx.x & 15);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      col[g].q = col0 + 64 * g + cl;
+      col[g].nv = max(0, min(4, a.K - col[g].q));
+      col[g].ok = col[g].nv > 0;
+    }
+#pragma unroll
+    for (int s = 0; s < DEPTH; ++s) issue(a, row0, s, s);
+  }
+
+  __device__ __forceinline__ void finish(const KArgs& a, const float* sG, int row0) {
+#pragma unroll
+    for (int s = 0; s < PASSES; ++s) {
+      const int slot = s % DEPTH;
+      const int rl = s * 16 + (threadIdx.x >> 4);
+      float g[8];
+      if constexpr (GF == FMT_NONE) {
+        const f32x4 g0 = *reinterpret_cast<const f32x4*>(sG + rl * GP + cl);
+        const f32x4 g1 = *reinterpret_cast<const f32x4*>(sG + rl * GP + 64 + cl);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { g[i] = g0[i]; g[4 + i] = g1[i]; }
+      } else {
+        dec4<GF>(graw[slot][0], g);
+        dec4<GF>(graw[slot][1], g + 4);
+      }
+      const typename S::Pending cur = pend[slot];
+      if (s + DEPTH < PASSES) issue(a, row0, s + DEPTH, slot);
+      Seg sg[2];
+      segs(a, row0 + rl, sg);
+      S::apply_store(a, row0 + rl, sg, g, cur);
     }
   }
 };
 
-// Epilogue over one 128 x 128 tile: thread t owns, in pass s = 0..7, the 8
-// elements of row (s*16 + t/16) starting at column 8*(t%16).  The state of
-// DEPTH chunks is in flight at any time: chunk s+DEPTH is requested as soon
-// as chunk s has been decoded.  G comes from the LDS staging buffer (fused,
-// GF == FMT_NONE) or from the dW workspace in format GF (unfused).
-template <class S, int GF>
-__device__ __forceinline__ void tile_epilogue(const KArgs& a, const float* sG, int row0, int col0) {
-  constexpr int DEPTH = 4;
-  constexpr int PASSES = TILE * TILE / (8 * NT);  // 8
-  const int tid = threadIdx.x;
-  const int cl = (tid & 15) * 8;
-  const int q = col0 + cl;
-  const int nv = min(8, a.K - q);
-  const bool gvec = (a.K & 7) == 0;
-  typename S::Pending pend[DEPTH];
-  Raw8<GF == FMT_NONE ? FMT_F32 : GF> graw[DEPTH];
-  auto issue = [&](int s, int slot) {
-    const int p = row0 + s * 16 + (tid >> 4);
-    S::load(a, p, q, nv, pend[slot]);
-    if constexpr (GF != FMT_NONE) {
-      if (p < a.N && nv > 0) ld8<GF>(graw[slot], a.dW, (int64_t)p * a.K + q, nv, gvec);
-      else zero8(graw[slot]);
-    }
-  };
-#pragma unroll
-  for (int s = 0; s < DEPTH; ++s) issue(s, s);
-#pragma unroll
-  for (int s = 0; s < PASSES; ++s) {
-    const int slot = s % DEPTH;
-    const int rl = s * 16 + (tid >> 4);
-    float g[8];
-    if constexpr (GF == FMT_NONE) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) g[i] = sG[rl * GP + cl + i];
-    } else {
-      dec8<GF>(graw[slot], g);
-    }
-    const typename S::Pending cur = pend[slot];
-    if (s + DEPTH < PASSES) issue(s + DEPTH, slot);
-    S::apply_store(a, row0 + rl, q, nv, g, cur);
-  }
-}
-
 // ------------------------------------------------------------------------
 // Kernels
 // ------------------------------------------------------------------------
-// IN: input format; DMA: asynchronous direct-to-LDS mainloop (bf16 only).
-template <int IN, bool DMA, int OPT, int WF, int MF, int VF>
+// IN: input format.  FAST (bf16 inputs only): the asynchronous
+// direct-to-LDS mainloop and the vector-only epilogue; the host selects it
+// when X, dY and the state rows are aligned and N, K are multiples of 8.
+template <int IN, bool FAST, int OPT, int WF, int MF, int VF>
 __global__ void __launch_bounds__(NT, 2) k_fused(const KArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   int ti, tj;
   tile_coords(blockIdx.x, a.tiles_n, a.tiles_k, ti, tj);
   const int row0 = ti * TILE, col0 = tj * TILE;
-  if constexpr (DMA) tile_gradient_dma(a, lds, row0, col0);
+  if constexpr (FAST) tile_gradient_dma(a, lds, row0, col0);
   else tile_gradient<IN>(a, lds, row0, col0);
-  tile_epilogue<Step<OPT, WF, MF, VF>, FMT_NONE>(a, reinterpret_cast<const float*>(lds), row0, col0);
+  Epilogue<Step<OPT, WF, MF, VF, FAST>, FMT_NONE, FAST> epi;
+  epi.start(a, row0, col0);
+  epi.finish(a, reinterpret_cast<const float*>(lds), row0);
 }
 
 template <int IN, bool DMA>
@@ -804,30 +894,37 @@ __global__ void __launch_bounds__(NT, 2) k_gemm(const KArgs a) {
   if constexpr (DMA) tile_gradient_dma(a, lds, row0, col0);
   else tile_gradient<IN>(a, lds, row0, col0);
   const float* sG = reinterpret_cast<const float*>(lds);
-  const int tid = threadIdx.x;
-  const int cl = (tid & 15) * 8;
-  const int q = col0 + cl;
-  const int nv = min(8, a.K - q);
-  const bool vec = (a.K & 7) == 0;
+  const int cl = 4 * (threadIdx.x & 15);
+  const bool vec = (a.K & 3) == 0;
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
-    const int rl = s * 16 + (tid >> 4);
+    const int rl = s * 16 + (threadIdx.x >> 4);
     const int p = row0 + rl;
-    if (p >= a.N || nv <= 0) continue;
-    float g[8];
+    if (p >= a.N) continue;
+    char* rowp = static_cast<char*>(a.dW) + (int64_t)p * a.K * (a.dw_fmt == FMT_F32 ? 4 : 2);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) g[i] = sG[rl * GP + cl + i];
-    const int64_t off = (int64_t)p * a.K + q;
-    if (a.dw_fmt == FMT_F32) st8<FMT_F32>(a.dW, off, nv, vec, g, 0, 0, 0);
-    else st8<FMT_BF16>(a.dW, off, nv, vec, g, 0, 0, 0);
+    for (int g = 0; g < 2; ++g) {
+      Seg sg;
+      sg.q = col0 + 64 * g + cl;
+      sg.nv = max(0, min(4, a.K - sg.q));
+      sg.ok = sg.nv > 0;
+      if (!sg.ok) continue;
+      float x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = sG[rl * GP + 64 * g + cl + i];
+      if (a.dw_fmt == FMT_F32) st4<FMT_F32, false>(rowp, sg, vec, x, 0, 0, 0);
+      else st4<FMT_BF16, false>(rowp, sg, vec, x, 0, 0, 0);
+    }
   }
 }
 
-template <int GF, int OPT, int WF, int MF, int VF>
+template <int GF, bool FAST, int OPT, int WF, int MF, int VF>
 __global__ void __launch_bounds__(NT, 2) k_step(const KArgs a) {
   int ti, tj;
   tile_coords(blockIdx.x, a.tiles_n, a.tiles_k, ti, tj);
-  tile_epilogue<Step<OPT, WF, MF, VF>, GF>(a, nullptr, ti * TILE, tj * TILE);
+  Epilogue<Step<OPT, WF, MF, VF, FAST>, GF, FAST> epi;
+  epi.start(a, ti * TILE, tj * TILE);
+  epi.finish(a, nullptr, ti * TILE);
 }
 
 __global__ void k_debug_sr(const float* __restrict__ in, uint16_t* __restrict__ out, uint32_t n, uint32_t key) {
@@ -874,7 +971,8 @@ static hipError_t fused_w(const KArgs& a, int opt, int m_fmt, int v_fmt, hipStre
 }
 
 hipError_t launch_fused(const KArgs& a, int in_fmt, int w_fmt, int opt, int m_fmt, int v_fmt, hipStream_t st) {
-  if (in_fmt == FMT_BF16 && a.dma_ok) {
+  const bool fast = a.dma_ok && a.vec_state && (a.K % 4) == 0;
+  if (in_fmt == FMT_BF16 && fast) {
     if (w_fmt == FMT_BF16) return fused_w<FMT_BF16, true, FMT_BF16>(a, opt, m_fmt, v_fmt, st);
     if (w_fmt == FMT_F32) return fused_w<FMT_BF16, true, FMT_F32>(a, opt, m_fmt, v_fmt, st);
   } else if (in_fmt == FMT_BF16) {
@@ -895,26 +993,34 @@ hipError_t launch_gemm(const KArgs& a, int in_fmt, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int GF, int WF>
+template <int GF, bool FAST, int WF>
 static hipError_t step_w(const KArgs& a, int opt, int m_fmt, int v_fmt, hipStream_t st) {
-#define X(O, M, V)                                                                  \
-  if (opt == O && m_fmt == M && v_fmt == V) {                                       \
-    hipLaunchKernelGGL((k_step<GF, O, WF, M, V>), tile_grid(a), dim3(NT), 0, st, a); \
-    return hipGetLastError();                                                       \
+#define X(O, M, V)                                                                        \
+  if (opt == O && m_fmt == M && v_fmt == V) {                                             \
+    hipLaunchKernelGGL((k_step<GF, FAST, O, WF, M, V>), tile_grid(a), dim3(NT), 0, st, a); \
+    return hipGetLastError();                                                             \
   }
   FORGE_STATE_LIST(X)
 #undef X
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_step(const KArgs& a, int w_fmt, int opt, int m_fmt, int v_fmt, hipStream_t st) {
-  if (a.dw_fmt == FMT_F32) {
-    if (w_fmt == FMT_BF16) return step_w<FMT_F32, FMT_BF16>(a, opt, m_fmt, v_fmt, st);
-    if (w_fmt == FMT_F32) return step_w<FMT_F32, FMT_F32>(a, opt, m_fmt, v_fmt, st);
-  } else if (a.dw_fmt == FMT_BF16) {
-    if (w_fmt == FMT_BF16) return step_w<FMT_BF16, FMT_BF16>(a, opt, m_fmt, v_fmt, st);
-    if (w_fmt == FMT_F32) return step_w<FMT_BF16, FMT_F32>(a, opt, m_fmt, v_fmt, st);
+template <int GF>
+static hipError_t step_g(const KArgs& a, int w_fmt, int opt, int m_fmt, int v_fmt, hipStream_t st) {
+  const bool fast = a.vec_state && (a.K % 4) == 0;
+  if (fast) {
+    if (w_fmt == FMT_BF16) return step_w<GF, true, FMT_BF16>(a, opt, m_fmt, v_fmt, st);
+    if (w_fmt == FMT_F32) return step_w<GF, true, FMT_F32>(a, opt, m_fmt, v_fmt, st);
+  } else {
+    if (w_fmt == FMT_BF16) return step_w<GF, false, FMT_BF16>(a, opt, m_fmt, v_fmt, st);
+    if (w_fmt == FMT_F32) return step_w<GF, false, FMT_F32>(a, opt, m_fmt, v_fmt, st);
   }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_step(const KArgs& a, int w_fmt, int opt, int m_fmt, int v_fmt, hipStream_t st) {
+  if (a.dw_fmt == FMT_F32) return step_g<FMT_F32>(a, w_fmt, opt, m_fmt, v_fmt, st);
+  if (a.dw_fmt == FMT_BF16) return step_g<FMT_BF16>(a, w_fmt, opt, m_fmt, v_fmt, st);
   return hipErrorInvalidValue;
 }
 
