@@ -229,9 +229,12 @@ struct MainBF16Dma {
   uint32_t baseA[2], baseB[2]; // byte offset of this lane's feature chunk in token row 0
   int trow[2];                 // token row within the chunk
   bool fokA[2], fokB[2];       // feature chunk inside the matrix
+  int gwave;                   // wave index within the mainloop group
 
-  __device__ __forceinline__ void init(const KArgs& a, int row0, int col0) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // gtid: thread index within the 256 threads that run the mainloop
+  __device__ __forceinline__ void init(const KArgs& a, int row0, int col0, int gtid) {
+    const int lane = gtid & 63, wave = gtid >> 6;
+    gwave = wave;
     oobA = (uint32_t)((uint64_t)a.BT * a.lddy * 2);
     oobB = (uint32_t)((uint64_t)a.BT * a.ldx * 2);
     rA = make_rsrc(a.dY, oobA);
@@ -249,7 +252,7 @@ struct MainBF16Dma {
   }
 
   __device__ __forceinline__ void issue(const KArgs& a, int kc, char* stage) const {
-    const int wave = threadIdx.x >> 6;
+    const int wave = gwave;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int tok = kc * TK + trow[r];
@@ -321,17 +324,18 @@ __device__ __forceinline__ void bar() {
   asm volatile("" ::: "memory");
 }
 
-// Phase 1 with the asynchronous mainloop; same output as tile_gradient.
-// The vmcnt waits count this wave's loads in issue order, so no other
-// global load may be in flight while the mainloop runs.
-__device__ __forceinline__ void tile_gradient_dma(const KArgs& a, char* lds, int row0, int col0) {
+// Phase 1 with the asynchronous mainloop, run by the 256 threads gtid =
+// 0..255 of a group of 4 waves that share the LDS ring at `ring`.  Executes
+// exactly max(nk, 0) workgroup barriers (one per token chunk), where
+// nk = ceil(BT / 32).  The vmcnt waits count this wave's loads in issue
+// order, so no other global load of these waves may be in flight.
+__device__ __forceinline__ void dma_accumulate(const KArgs& a, char* ring, int row0, int col0, int gtid,
+                                               f32x16 (&acc)[2][2]) {
   using M = MainBF16Dma;
-  static_assert(M::S * M::STAGE <= LDS_BYTES, "LDS budget");
   static_assert(M::TK == 32, "two 16-token k-steps per chunk");
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = gtid & 63, wave = gtid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)lds;
-  f32x16 acc[2][2];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)ring;
 #pragma unroll
   for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
@@ -340,17 +344,17 @@ __device__ __forceinline__ void tile_gradient_dma(const KArgs& a, char* lds, int
       for (int e = 0; e < 16; ++e) acc[bi][bj][e] = 0.f;
   const int nk = (a.BT + M::TK - 1) / M::TK;
   M ml;
-  ml.init(a, row0, col0);
+  ml.init(a, row0, col0, gtid);
 #pragma unroll
   for (int k = 0; k < M::S - 1; ++k)
-    if (k < nk) ml.issue(a, k, lds + k * M::STAGE);
+    if (k < nk) ml.issue(a, k, ring + k * M::STAGE);
   for (int kc = 0; kc < nk; ++kc) {
     // loads issued after chunk kc: chunks kc+1 .. min(kc+S-2, nk-1)
     M::wait_chunk(min(M::S - 2, nk - 1 - kc));
     bar();   // chunk kc visible to all waves; all waves done with chunk kc-1
-    if (kc + M::S - 1 < nk) ml.issue(a, kc + M::S - 1, lds + ((kc + M::S - 1) % M::S) * M::STAGE);
+    if (kc + M::S - 1 < nk) ml.issue(a, kc + M::S - 1, ring + ((kc + M::S - 1) % M::S) * M::STAGE);
     const uint32_t cur = lds0 + (uint32_t)((kc % M::S) * M::STAGE);
-    // fragments of both k-steps: [0..3] = k-step 0 (A0, A1, B0, B1 as lo/hi pairs), [4..7] unused layout below
+    // operand fragments of the chunk's two k-steps: [A0 lo, A0 hi, A1 lo, A1 hi, B0 lo, B0 hi, B1 lo, B1 hi]
     u32x2 f0[8], f1[8];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
@@ -380,8 +384,13 @@ __device__ __forceinline__ void tile_gradient_dma(const KArgs& a, char* lds, int
                                                               acc[bi][bj], 0, 0, 0);
   }
   wait_vmcnt<0>();
-  bar();   // every wave is done reading the stages before G overwrites them
-  float* sG = reinterpret_cast<float*>(lds);
+}
+
+// Accumulator layout of v_mfma_f32_32x32x*: lane l, register 4j+i of block
+// (bi, bj) holds row 8j + 4(l/32) + i, column l%32 of that 32 x 32 block.
+__device__ __forceinline__ void store_acc(float* sG, const f32x16 (&acc)[2][2], int gtid) {
+  const int lane = gtid & 63, wave = gtid >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
 #pragma unroll
   for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
@@ -392,6 +401,15 @@ __device__ __forceinline__ void tile_gradient_dma(const KArgs& a, char* lds, int
         const int c = wc * 64 + bj * 32 + (lane & 31);
         sG[r * GP + c] = acc[bi][bj][e];
       }
+}
+
+// Phase 1 for a 256-thread workgroup; same output as tile_gradient.
+__device__ __forceinline__ void tile_gradient_dma(const KArgs& a, char* lds, int row0, int col0) {
+  static_assert(MainBF16Dma::S * MainBF16Dma::STAGE <= LDS_BYTES, "LDS budget");
+  f32x16 acc[2][2];
+  dma_accumulate(a, lds, row0, col0, threadIdx.x, acc);
+  bar();   // every wave is done reading the stages before G overwrites them
+  store_acc(reinterpret_cast<float*>(lds), acc, threadIdx.x);
   __syncthreads();
 }
 
@@ -787,37 +805,37 @@ struct Step {
   }
 };
 
-// Epilogue over one 128 x 128 tile.  Thread mapping: in pass s (0..7)
-// thread t owns row s*16 + t/16 of the tile and two 4-element segments of
-// it, at columns 4*(t%16) and 64 + 4*(t%16); the 16 lanes of a row access
-// one contiguous 64-element run per instruction (whole 128-byte lines for
-// every format but int8), and a row's 128 columns stay within 16 lanes for
-// the int8 block reduction.  The state of DEPTH passes is in flight at any
-// time: pass s+DEPTH is requested as soon as pass s has been taken out of
-// its slot.  start() issues the first DEPTH passes; finish() runs the
-// rolling loop.  G comes from the LDS staging buffer (GF == FMT_NONE) or
-// from the dW workspace in format GF (unfused baseline).
-template <class S, int GF, bool FAST>
+// Epilogue over one 128 x 128 tile.  Thread mapping: in pass s thread t
+// (0..NTE-1 of the epilogue group) owns row s*(NTE/16) + t/16 of the tile
+// and two 4-element segments of it, at columns 4*(t%16) and 64 + 4*(t%16);
+// the 16 lanes of a row access one contiguous 64-element run per
+// instruction (whole 128-byte lines for every format but int8), and a
+// row's 128 columns stay within 16 lanes for the int8 block reduction.
+// issue() requests the state of one pass into a slot; consume() decodes a
+// slot, applies the step and stores.  G comes from the LDS staging buffer
+// (GF == FMT_NONE) or from the dW workspace in format GF (unfused baseline).
+template <class S, int GF, bool FAST, int DEPTH, int NTE = NT>
 struct Epilogue {
-  static constexpr int DEPTH = 4;
-  static constexpr int PASSES = TILE * TILE / (8 * NT);  // 8
+  static constexpr int PASSES = TILE * TILE / (8 * NTE);  // 8 with 256 threads, 4 with 512
+  static constexpr int RPP = NTE / 16;                    // rows per pass
   typename S::Pending pend[DEPTH];
   Raw4<GF> graw[DEPTH][2];
-  int cl;
-  Seg col[2];   // column part of the segments (row validity added per pass)
+  int tid;
 
-  __device__ __forceinline__ void segs(const KArgs& a, int p, Seg (&sg)[2]) const {
+  __device__ __forceinline__ void segs(const KArgs& a, int p, int col0, Seg (&sg)[2]) const {
+    const int cl = 4 * (tid & 15);
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      sg[g] = col[g];
-      sg[g].ok = col[g].ok && p < a.N;
+      sg[g].q = col0 + 64 * g + cl;
+      sg[g].nv = max(0, min(4, a.K - sg[g].q));
+      sg[g].ok = sg[g].nv > 0 && p < a.N;
     }
   }
 
-  __device__ __forceinline__ void issue(const KArgs& a, int row0, int s, int slot) {
-    const int p = row0 + s * 16 + (threadIdx.x >> 4);
+  __device__ __forceinline__ void issue(const KArgs& a, int row0, int col0, int s, int slot) {
+    const int p = row0 + s * RPP + (tid >> 4);
     Seg sg[2];
-    segs(a, p, sg);
+    segs(a, p, col0, sg);
     S::load(a, p, sg, pend[slot]);
     if constexpr (GF != FMT_NONE) {
       const bool gvec = (a.K & 3) == 0;
@@ -830,38 +848,40 @@ struct Epilogue {
     }
   }
 
-  __device__ __forceinline__ void start(const KArgs& a, int row0, int col0) {
-    cl = 4 * (threadIdx.x & 15);
+  // G of pass s (from sG or from the slot's dW words)
+  __device__ __forceinline__ void grad(const float* sG, int s, int slot, float (&g)[8]) const {
+    if constexpr (GF == FMT_NONE) {
+      const int rl = s * RPP + (tid >> 4), cl = 4 * (tid & 15);
+      const f32x4 g0 = *reinterpret_cast<const f32x4*>(sG + rl * GP + cl);
+      const f32x4 g1 = *reinterpret_cast<const f32x4*>(sG + rl * GP + 64 + cl);
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      col[g].q = col0 + 64 * g + cl;
-      col[g].nv = max(0, min(4, a.K - col[g].q));
-      col[g].ok = col[g].nv > 0;
+      for (int i = 0; i < 4; ++i) { g[i] = g0[i]; g[4 + i] = g1[i]; }
+    } else {
+      dec4<GF>(graw[slot][0], g);
+      dec4<GF>(graw[slot][1], g + 4);
     }
-#pragma unroll
-    for (int s = 0; s < DEPTH; ++s) issue(a, row0, s, s);
   }
 
-  __device__ __forceinline__ void finish(const KArgs& a, const float* sG, int row0) {
+  __device__ __forceinline__ void consume(const KArgs& a, int row0, int col0, int s, const float (&g)[8],
+                                          const typename S::Pending& cur) const {
+    const int p = row0 + s * RPP + (tid >> 4);
+    Seg sg[2];
+    segs(a, p, col0, sg);
+    S::apply_store(a, p, sg, g, cur);
+  }
+
+  // One tile with a rolling window of DEPTH passes in flight.
+  __device__ __forceinline__ void run_tile(const KArgs& a, const float* sG, int row0, int col0) {
+#pragma unroll
+    for (int s = 0; s < DEPTH && s < PASSES; ++s) issue(a, row0, col0, s, s);
 #pragma unroll
     for (int s = 0; s < PASSES; ++s) {
       const int slot = s % DEPTH;
-      const int rl = s * 16 + (threadIdx.x >> 4);
       float g[8];
-      if constexpr (GF == FMT_NONE) {
-        const f32x4 g0 = *reinterpret_cast<const f32x4*>(sG + rl * GP + cl);
-        const f32x4 g1 = *reinterpret_cast<const f32x4*>(sG + rl * GP + 64 + cl);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { g[i] = g0[i]; g[4 + i] = g1[i]; }
-      } else {
-        dec4<GF>(graw[slot][0], g);
-        dec4<GF>(graw[slot][1], g + 4);
-      }
+      grad(sG, s, slot, g);
       const typename S::Pending cur = pend[slot];
-      if (s + DEPTH < PASSES) issue(a, row0, s + DEPTH, slot);
-      Seg sg[2];
-      segs(a, row0 + rl, sg);
-      S::apply_store(a, row0 + rl, sg, g, cur);
+      if (s + DEPTH < PASSES) issue(a, row0, col0, s + DEPTH, slot);
+      consume(a, row0, col0, s, g, cur);
     }
   }
 };
@@ -880,9 +900,95 @@ __global__ void __launch_bounds__(NT, 2) k_fused(const KArgs a) {
   const int row0 = ti * TILE, col0 = tj * TILE;
   if constexpr (FAST) tile_gradient_dma(a, lds, row0, col0);
   else tile_gradient<IN>(a, lds, row0, col0);
-  Epilogue<Step<OPT, WF, MF, VF, FAST>, FMT_NONE, FAST> epi;
-  epi.start(a, row0, col0);
-  epi.finish(a, reinterpret_cast<const float*>(lds), row0);
+  Epilogue<Step<OPT, WF, MF, VF, FAST>, FMT_NONE, FAST, 4> epi;
+  epi.tid = threadIdx.x;
+  epi.run_tile(a, reinterpret_cast<const float*>(lds), row0, col0);
+}
+
+// Persistent, wave-specialised variant for aligned bf16 layers with at
+// least 8 token chunks (BT >= 256).  One 768-thread workgroup per CU walks
+// the tiles blockIdx.x, blockIdx.x + gridDim.x, ... (row-major).  Waves 0-3
+// accumulate the next tile's G through the LDS-DMA ring while waves 4-11
+// stream the current tile's state: 4 passes of 32 rows, all in flight, each
+// slot refilled with the same pass of the next tile as soon as it is
+// consumed.  The two groups meet at the same workgroup barriers: iteration
+// `it` has nb = nk barriers (one per token chunk) while a tile is being
+// accumulated, 8 in the final drain iteration, plus one hand-off barrier
+// after which the staged G of tile `it` is visible.  Epilogue pass p of an
+// iteration runs after (p * nb) / 4 of its barriers, so the last pass is
+// done reading the staged G before the accumulating waves overwrite it
+// after their last chunk barrier.  All barriers are fence-free (bar()): the
+// accumulating waves wait for their own LDS-DMA loads (vmcnt) and LDS
+// stores (lgkmcnt) before them, and the streaming waves' global loads stay
+// in flight across them.
+constexpr int NT_WS_MMA = NT;                                     // 4 waves
+constexpr int NT_WS_EPI = 512;                                    // 8 waves
+constexpr int NT_WS = NT_WS_MMA + NT_WS_EPI;
+constexpr int LDS_RING_WS = MainBF16Dma::S * MainBF16Dma::STAGE;  // 64 KiB
+constexpr int LDS_WS = LDS_RING_WS + LDS_G;                       // 130 KiB
+
+template <int OPT, int WF, int MF, int VF>
+__global__ void __launch_bounds__(NT_WS, 3) k_fused_ws(const KArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS_WS];
+  char* ring = lds;
+  float* sG = reinterpret_cast<float*>(lds + LDS_RING_WS);
+  const int T = a.tiles_n * a.tiles_k;
+  const int n_my = (T - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int nk = (a.BT + MainBF16Dma::TK - 1) / MainBF16Dma::TK;
+  if (n_my <= 0 || nk <= 0) return;   // the host launches min(tiles, CUs) workgroups and BT >= 256
+  auto tile_of = [&](int it, int& row0, int& col0) {
+    const int t = (int)blockIdx.x + it * (int)gridDim.x;
+    const int ti = t / a.tiles_k;
+    row0 = ti * TILE;
+    col0 = (t - ti * a.tiles_k) * TILE;
+  };
+  if (threadIdx.x < NT_WS_MMA) {
+    const int gtid = threadIdx.x;
+    for (int it = 0; it <= n_my; ++it) {
+      if (it < n_my) {
+        int row0, col0;
+        tile_of(it, row0, col0);
+        f32x16 acc[2][2];
+        dma_accumulate(a, ring, row0, col0, gtid, acc);   // nk barriers
+        store_acc(sG, acc, gtid);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      } else {
+        for (int s = 0; s < 8; ++s) bar();
+      }
+      bar();                                              // hand-off
+    }
+  } else {
+    using E = Epilogue<Step<OPT, WF, MF, VF, true>, FMT_NONE, true, 4, NT_WS_EPI>;
+    static_assert(E::PASSES == 4, "one tile in flight");
+    E epi;
+    epi.tid = threadIdx.x - NT_WS_MMA;
+    for (int it = 0; it <= n_my; ++it) {
+      const int nb = it < n_my ? nk : 8;
+      if (it == 0) {
+        int row0, col0;
+        tile_of(0, row0, col0);
+#pragma unroll
+        for (int s = 0; s < E::PASSES; ++s) epi.issue(a, row0, col0, s, s);
+        for (int b = 0; b < nb; ++b) bar();
+      } else {
+        int row0, col0, nrow0 = 0, ncol0 = 0;
+        tile_of(it - 1, row0, col0);
+        const bool next = it < n_my;
+        if (next) tile_of(it, nrow0, ncol0);
+#pragma unroll
+        for (int s = 0; s < E::PASSES; ++s) {
+          float g[8];
+          epi.grad(sG, s, s, g);
+          const auto cur = epi.pend[s];
+          if (next) epi.issue(a, nrow0, ncol0, s, s);
+          epi.consume(a, row0, col0, s, g, cur);
+          const int b0 = (s * nb) / E::PASSES, b1 = ((s + 1) * nb) / E::PASSES;
+          for (int b = b0; b < b1; ++b) bar();
+        }
+      }
+      bar();                                              // hand-off
+    }
+  }
 }
 
 template <int IN, bool DMA>
@@ -922,9 +1028,9 @@ template <int GF, bool FAST, int OPT, int WF, int MF, int VF>
 __global__ void __launch_bounds__(NT, 2) k_step(const KArgs a) {
   int ti, tj;
   tile_coords(blockIdx.x, a.tiles_n, a.tiles_k, ti, tj);
-  Epilogue<Step<OPT, WF, MF, VF, FAST>, GF, FAST> epi;
-  epi.start(a, ti * TILE, tj * TILE);
-  epi.finish(a, nullptr, ti * TILE);
+  Epilogue<Step<OPT, WF, MF, VF, FAST>, GF, FAST, 4> epi;
+  epi.tid = threadIdx.x;
+  epi.run_tile(a, nullptr, ti * TILE, tj * TILE);
 }
 
 __global__ void k_debug_sr(const float* __restrict__ in, uint16_t* __restrict__ out, uint32_t n, uint32_t key) {
@@ -970,8 +1076,24 @@ static hipError_t fused_w(const KArgs& a, int opt, int m_fmt, int v_fmt, hipStre
   return hipErrorInvalidValue;
 }
 
+template <int WF>
+static hipError_t fused_ws(const KArgs& a, int opt, int m_fmt, int v_fmt, hipStream_t st) {
+#define X(O, M, V)                                                                        \
+  if (opt == O && m_fmt == M && v_fmt == V) {                                             \
+    hipLaunchKernelGGL((k_fused_ws<O, WF, M, V>), dim3((unsigned)a.ws_grid), dim3(NT_WS), 0, st, a); \
+    return hipGetLastError();                                                             \
+  }
+  FORGE_STATE_LIST(X)
+#undef X
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_fused(const KArgs& a, int in_fmt, int w_fmt, int opt, int m_fmt, int v_fmt, hipStream_t st) {
   const bool fast = a.dma_ok && a.vec_state && (a.K % 4) == 0;
+  // the persistent kernel holds a whole tile's state per streaming thread in
+  // registers: bf16 weights only (fp32 weights would spill)
+  if (in_fmt == FMT_BF16 && fast && a.ws_grid > 0 && a.BT >= 256 && w_fmt == FMT_BF16)
+    return fused_ws<FMT_BF16>(a, opt, m_fmt, v_fmt, st);
   if (in_fmt == FMT_BF16 && fast) {
     if (w_fmt == FMT_BF16) return fused_w<FMT_BF16, true, FMT_BF16>(a, opt, m_fmt, v_fmt, st);
     if (w_fmt == FMT_F32) return fused_w<FMT_BF16, true, FMT_F32>(a, opt, m_fmt, v_fmt, st);
