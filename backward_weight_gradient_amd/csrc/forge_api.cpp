@@ -202,17 +202,6 @@ KArgs make_args(const forge_mat* X, const forge_mat* dY, forge_mat* W, forge_sta
   a.dma_ok = (pl.in_fmt == FORGE_BF16 && a.vec_in && pl.N % 8 == 0 && pl.K % 8 == 0 &&
               (uint64_t)pl.BT * (uint64_t)dY->ld * 2 < (1ull << 31) &&
               (uint64_t)pl.BT * (uint64_t)X->ld * 2 < (1ull << 31)) ? 1 : 0;
-  // persistent wave-specialised kernel: one workgroup per compute unit
-  // (at most one per tile); used when the token axis has >= 8 chunks
-  a.ws_grid = 0;
-  if (pl.BT >= 256) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0) {
-      const int64_t tiles = (int64_t)a.tiles_n * a.tiles_k;
-      a.ws_grid = (int32_t)(tiles < cus ? tiles : cus);
-    }
-  }
   // 4-element state accesses (16 B fp32, 8 B bf16, 4 B int8)
   bool vs = vec_ok(W->data, W->ld, 4, elem_size(pl.w_fmt)) && vec_ok(m->q.data, m->q.ld, 4, elem_size(pl.m_fmt));
   if (v) vs = vs && vec_ok(v->q.data, v->q.ld, 4, elem_size(pl.v_fmt));

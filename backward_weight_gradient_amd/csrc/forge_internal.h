@@ -42,7 +42,6 @@ struct KArgs {
   int32_t vec_in;                 // X / dY rows allow 16-byte vector loads
   int32_t vec_state;              // W / m / v rows allow 8-element vector access
   int32_t dma_ok;                 // bf16 X / dY qualify for the direct-to-LDS mainloop
-  int32_t ws_grid;                // > 0: persistent wave-specialised launch with this many workgroups
   EpiConst c;
 };
 

@@ -324,13 +324,19 @@ __device__ __forceinline__ void bar() {
   asm volatile("" ::: "memory");
 }
 
+// Synchronisation of the waves that share an LDS ring: the workgroup barrier.
+struct WorkgroupSync {
+  __device__ __forceinline__ void arrive_wait() { bar(); }
+};
+
 // Phase 1 with the asynchronous mainloop, run by the 256 threads gtid =
-// 0..255 of a group of 4 waves that share the LDS ring at `ring`.  Executes
-// exactly max(nk, 0) workgroup barriers (one per token chunk), where
+// 0..255 of a group of 4 waves that share the LDS ring at `ring`.  Calls
+// sync.arrive_wait() exactly max(nk, 0) times (once per token chunk), where
 // nk = ceil(BT / 32).  The vmcnt waits count this wave's loads in issue
 // order, so no other global load of these waves may be in flight.
+template <class Sync>
 __device__ __forceinline__ void dma_accumulate(const KArgs& a, char* ring, int row0, int col0, int gtid,
-                                               f32x16 (&acc)[2][2]) {
+                                               f32x16 (&acc)[2][2], Sync& sync) {
   using M = MainBF16Dma;
   static_assert(M::TK == 32, "two 16-token k-steps per chunk");
   const int lane = gtid & 63, wave = gtid >> 6;
@@ -351,7 +357,7 @@ __device__ __forceinline__ void dma_accumulate(const KArgs& a, char* ring, int r
   for (int kc = 0; kc < nk; ++kc) {
     // loads issued after chunk kc: chunks kc+1 .. min(kc+S-2, nk-1)
     M::wait_chunk(min(M::S - 2, nk - 1 - kc));
-    bar();   // chunk kc visible to all waves; all waves done with chunk kc-1
+    sync.arrive_wait();   // chunk kc visible to all 4 waves; all of them done with chunk kc-1
     if (kc + M::S - 1 < nk) ml.issue(a, kc + M::S - 1, ring + ((kc + M::S - 1) % M::S) * M::STAGE);
     const uint32_t cur = lds0 + (uint32_t)((kc % M::S) * M::STAGE);
     // operand fragments of the chunk's two k-steps: [A0 lo, A0 hi, A1 lo, A1 hi, B0 lo, B0 hi, B1 lo, B1 hi]
@@ -407,7 +413,8 @@ __device__ __forceinline__ void store_acc(float* sG, const f32x16 (&acc)[2][2], 
 __device__ __forceinline__ void tile_gradient_dma(const KArgs& a, char* lds, int row0, int col0) {
   static_assert(MainBF16Dma::S * MainBF16Dma::STAGE <= LDS_BYTES, "LDS budget");
   f32x16 acc[2][2];
-  dma_accumulate(a, lds, row0, col0, threadIdx.x, acc);
+  WorkgroupSync sync;
+  dma_accumulate(a, lds, row0, col0, threadIdx.x, acc, sync);
   bar();   // every wave is done reading the stages before G overwrites them
   store_acc(reinterpret_cast<float*>(lds), acc, threadIdx.x);
   __syncthreads();
@@ -905,92 +912,6 @@ __global__ void __launch_bounds__(NT, 2) k_fused(const KArgs a) {
   epi.run_tile(a, reinterpret_cast<const float*>(lds), row0, col0);
 }
 
-// Persistent, wave-specialised variant for aligned bf16 layers with at
-// least 8 token chunks (BT >= 256).  One 768-thread workgroup per CU walks
-// the tiles blockIdx.x, blockIdx.x + gridDim.x, ... (row-major).  Waves 0-3
-// accumulate the next tile's G through the LDS-DMA ring while waves 4-11
-// stream the current tile's state: 4 passes of 32 rows, all in flight, each
-// slot refilled with the same pass of the next tile as soon as it is
-// consumed.  The two groups meet at the same workgroup barriers: iteration
-// `it` has nb = nk barriers (one per token chunk) while a tile is being
-// accumulated, 8 in the final drain iteration, plus one hand-off barrier
-// after which the staged G of tile `it` is visible.  Epilogue pass p of an
-// iteration runs after (p * nb) / 4 of its barriers, so the last pass is
-// done reading the staged G before the accumulating waves overwrite it
-// after their last chunk barrier.  All barriers are fence-free (bar()): the
-// accumulating waves wait for their own LDS-DMA loads (vmcnt) and LDS
-// stores (lgkmcnt) before them, and the streaming waves' global loads stay
-// in flight across them.
-constexpr int NT_WS_MMA = NT;                                     // 4 waves
-constexpr int NT_WS_EPI = 512;                                    // 8 waves
-constexpr int NT_WS = NT_WS_MMA + NT_WS_EPI;
-constexpr int LDS_RING_WS = MainBF16Dma::S * MainBF16Dma::STAGE;  // 64 KiB
-constexpr int LDS_WS = LDS_RING_WS + LDS_G;                       // 130 KiB
-
-template <int OPT, int WF, int MF, int VF>
-__global__ void __launch_bounds__(NT_WS, 3) k_fused_ws(const KArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[LDS_WS];
-  char* ring = lds;
-  float* sG = reinterpret_cast<float*>(lds + LDS_RING_WS);
-  const int T = a.tiles_n * a.tiles_k;
-  const int n_my = (T - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
-  const int nk = (a.BT + MainBF16Dma::TK - 1) / MainBF16Dma::TK;
-  if (n_my <= 0 || nk <= 0) return;   // the host launches min(tiles, CUs) workgroups and BT >= 256
-  auto tile_of = [&](int it, int& row0, int& col0) {
-    const int t = (int)blockIdx.x + it * (int)gridDim.x;
-    const int ti = t / a.tiles_k;
-    row0 = ti * TILE;
-    col0 = (t - ti * a.tiles_k) * TILE;
-  };
-  if (threadIdx.x < NT_WS_MMA) {
-    const int gtid = threadIdx.x;
-    for (int it = 0; it <= n_my; ++it) {
-      if (it < n_my) {
-        int row0, col0;
-        tile_of(it, row0, col0);
-        f32x16 acc[2][2];
-        dma_accumulate(a, ring, row0, col0, gtid, acc);   // nk barriers
-        store_acc(sG, acc, gtid);
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      } else {
-        for (int s = 0; s < 8; ++s) bar();
-      }
-      bar();                                              // hand-off
-    }
-  } else {
-    using E = Epilogue<Step<OPT, WF, MF, VF, true>, FMT_NONE, true, 4, NT_WS_EPI>;
-    static_assert(E::PASSES == 4, "one tile in flight");
-    E epi;
-    epi.tid = threadIdx.x - NT_WS_MMA;
-    for (int it = 0; it <= n_my; ++it) {
-      const int nb = it < n_my ? nk : 8;
-      if (it == 0) {
-        int row0, col0;
-        tile_of(0, row0, col0);
-#pragma unroll
-        for (int s = 0; s < E::PASSES; ++s) epi.issue(a, row0, col0, s, s);
-        for (int b = 0; b < nb; ++b) bar();
-      } else {
-        int row0, col0, nrow0 = 0, ncol0 = 0;
-        tile_of(it - 1, row0, col0);
-        const bool next = it < n_my;
-        if (next) tile_of(it, nrow0, ncol0);
-#pragma unroll
-        for (int s = 0; s < E::PASSES; ++s) {
-          float g[8];
-          epi.grad(sG, s, s, g);
-          const auto cur = epi.pend[s];
-          if (next) epi.issue(a, nrow0, ncol0, s, s);
-          epi.consume(a, row0, col0, s, g, cur);
-          const int b0 = (s * nb) / E::PASSES, b1 = ((s + 1) * nb) / E::PASSES;
-          for (int b = b0; b < b1; ++b) bar();
-        }
-      }
-      bar();                                              // hand-off
-    }
-  }
-}
-
 template <int IN, bool DMA>
 __global__ void __launch_bounds__(NT, 2) k_gemm(const KArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
@@ -1076,24 +997,8 @@ static hipError_t fused_w(const KArgs& a, int opt, int m_fmt, int v_fmt, hipStre
   return hipErrorInvalidValue;
 }
 
-template <int WF>
-static hipError_t fused_ws(const KArgs& a, int opt, int m_fmt, int v_fmt, hipStream_t st) {
-#define X(O, M, V)                                                                        \
-  if (opt == O && m_fmt == M && v_fmt == V) {                                             \
-    hipLaunchKernelGGL((k_fused_ws<O, WF, M, V>), dim3((unsigned)a.ws_grid), dim3(NT_WS), 0, st, a); \
-    return hipGetLastError();                                                             \
-  }
-  FORGE_STATE_LIST(X)
-#undef X
-  return hipErrorInvalidValue;
-}
-
 hipError_t launch_fused(const KArgs& a, int in_fmt, int w_fmt, int opt, int m_fmt, int v_fmt, hipStream_t st) {
   const bool fast = a.dma_ok && a.vec_state && (a.K % 4) == 0;
-  // the persistent kernel holds a whole tile's state per streaming thread in
-  // registers: bf16 weights only (fp32 weights would spill)
-  if (in_fmt == FMT_BF16 && fast && a.ws_grid > 0 && a.BT >= 256 && w_fmt == FMT_BF16)
-    return fused_ws<FMT_BF16>(a, opt, m_fmt, v_fmt, st);
   if (in_fmt == FMT_BF16 && fast) {
     if (w_fmt == FMT_BF16) return fused_w<FMT_BF16, true, FMT_BF16>(a, opt, m_fmt, v_fmt, st);
     if (w_fmt == FMT_F32) return fused_w<FMT_BF16, true, FMT_F32>(a, opt, m_fmt, v_fmt, st);

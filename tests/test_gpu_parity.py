@@ -285,15 +285,15 @@ def test_compute_bound_sweep_full_size(BT, name, N, K, opt):
 
 
 # ---------------------------------------------------------------------------
-# Persistent wave-specialised kernel: several tiles per workgroup, ragged N
-# and BT (it is used for aligned bf16 layers with BT >= 256)
+# Aligned (direct-to-LDS, vector epilogue) path on many tiles with ragged N
+# and BT, every optimizer and state layout; bit-equal to the unfused baseline
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("spec,opt", [(SPEC_CFG1, "adamw"), (SPEC_CFG2, "adamw"), (SPEC_CFG3, "adamw"),
                                       (synth.LayerSpec("bf16", "bf16", "f32", None), "lion"),
                                       (synth.LayerSpec("bf16", "f32", "bf16", None), "sgdm")])
 @pytest.mark.parametrize("N,K,BT", [(2000, 4096, 300), (4104, 1024, 520), (600, 17152, 256)])
-def test_persistent_kernel_multi_tile(spec, opt, N, K, BT):
-    _say(f"case: persistent {spec} {opt} {N}x{K} BT{BT}")
+def test_aligned_multi_tile(spec, opt, N, K, BT):
+    _say(f"case: aligned multi-tile {spec} {opt} {N}x{K} BT{BT}")
     L = make_layer(5, N, K, BT, 7, spec, gen_device="cuda", outlier_p=0.01 if spec.m_fmt == "s8" else 0.0)
     h = F.hyper(opt, lr=1e-4 if opt == "lion" else 1e-3, beta2=0.99 if opt == "lion" else 0.999)
     rows = np.array(sorted({0, 1, 127, 128, 255, 256, N // 2, N - 9, N - 1} |
@@ -305,8 +305,7 @@ def test_persistent_kernel_multi_tile(spec, opt, N, K, BT):
     torch.cuda.synchronize()
     nb = K // 128
     cols = [(0, 128), (128, 256), ((nb // 2) * 128, (nb // 2) * 128 + 128), (K - 128, K)]
-    assert_ok(check_against_oracle(snap, L, h, 7, SEED, col_ranges=cols), f"persistent {N}x{K}x{BT}")
-    # the persistent kernel's G and step equal the unfused baseline's bit for bit
+    assert_ok(check_against_oracle(snap, L, h, 7, SEED, col_ranges=cols), f"aligned {N}x{K}x{BT}")
     for a, b in ((L.W, U.W), (L.m, U.m), (L.v, U.v), (L.ms, U.ms), (L.vs, U.vs)):
         if a is not None:
             assert torch.equal(a.view(torch.uint8) if a.dtype != torch.uint8 else a,
