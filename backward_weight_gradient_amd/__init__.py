@@ -15,6 +15,13 @@ import ctypes
 import os
 from typing import Optional
 
+# torch is imported before libforge is loaded so that the library's
+# libamdhip64.so.7 dependency resolves to the HIP runtime torch has already
+# loaded: one runtime per process, which owns the device pointers and stream
+# handles passed in.  Loaded first, libforge would bring up a second runtime
+# from the system ROCm install, and that one need not see the device.
+import torch  # noqa: F401
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libforge.so")
 
@@ -34,7 +41,8 @@ ROUNDING = {"rne": FORGE_ROUND_RNE, "sr": FORGE_ROUND_SR}
 class ForgeError(RuntimeError):
     def __init__(self, code: int, where: str):
         self.code = code
-        super().__init__(f"{where}: {forge_status_str(code)} (code {code})")
+        detail = f" [{forge_last_error()}]" if code == FORGE_E_HIP else ""
+        super().__init__(f"{where}: {forge_status_str(code)} (code {code}){detail}")
 
 
 class forge_mat(ctypes.Structure):
@@ -76,6 +84,8 @@ def _load() -> ctypes.CDLL:
     lib.forge_status_str.restype = ctypes.c_char_p
     lib.forge_version.argtypes = []
     lib.forge_version.restype = ctypes.c_char_p
+    lib.forge_last_error.argtypes = []
+    lib.forge_last_error.restype = ctypes.c_char_p
     return lib
 
 
@@ -141,6 +151,11 @@ def forge_status_str(code: int) -> str:
 
 def forge_version() -> str:
     return lib.forge_version().decode()
+
+
+def forge_last_error() -> str:
+    """HIP's description of the error behind the last FORGE_E_HIP on this thread."""
+    return lib.forge_last_error().decode()
 
 
 def forge_wgrad_check(X: forge_mat, dY: forge_mat, W: forge_mat, m: Optional[forge_state],

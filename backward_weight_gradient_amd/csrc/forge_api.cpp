@@ -232,6 +232,16 @@ KArgs make_args(const forge_mat* X, const forge_mat* dY, forge_mat* W, forge_sta
 
 extern "C" {
 
+namespace {
+thread_local hipError_t g_last_hip = hipSuccess;
+
+forge_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return FORGE_OK;
+  g_last_hip = e;
+  return FORGE_E_HIP;
+}
+}  // namespace
+
 forge_status forge_wgrad_check(const forge_mat* X, const forge_mat* dY, const forge_mat* W, const forge_state* m,
                                const forge_state* v, const forge_hyper* h, int64_t step) {
   Plan pl;
@@ -244,8 +254,7 @@ forge_status forge_wgrad_step(const forge_mat* X, const forge_mat* dY, forge_mat
   forge_status st = validate(X, dY, W, m, v, h, step, pl);
   if (st != FORGE_OK || pl.empty) return st;
   const KArgs a = make_args(X, dY, W, m, v, h, step, seed, pl);
-  hipError_t e = launch_fused(a, pl.in_fmt, pl.w_fmt, h->opt, pl.m_fmt, pl.v_fmt, (hipStream_t)stream);
-  return e == hipSuccess ? FORGE_OK : FORGE_E_HIP;
+  return hip_status(launch_fused(a, pl.in_fmt, pl.w_fmt, h->opt, pl.m_fmt, pl.v_fmt, (hipStream_t)stream));
 }
 
 forge_status forge_wgrad_unfused(const forge_mat* X, const forge_mat* dY, forge_mat* W, forge_state* m,
@@ -270,7 +279,7 @@ forge_status forge_wgrad_unfused(const forge_mat* X, const forge_mat* dY, forge_
   a.dw_fmt = dW_dtype == FORGE_F32 ? FMT_F32 : FMT_BF16;
   hipError_t e = launch_gemm(a, pl.in_fmt, (hipStream_t)stream);
   if (e == hipSuccess) e = launch_step(a, pl.w_fmt, h->opt, pl.m_fmt, pl.v_fmt, (hipStream_t)stream);
-  return e == hipSuccess ? FORGE_OK : FORGE_E_HIP;
+  return hip_status(e);
 }
 
 forge_status forge_debug_sr_bf16(const float* in, uint16_t* out, int64_t n, uint64_t seed, int64_t step,
@@ -282,9 +291,10 @@ forge_status forge_debug_sr_bf16(const float* in, uint16_t* out, int64_t n, uint
   if (!aligned(in, 4) || !aligned(out, 2)) return FORGE_E_ALIGN;
   if (overlap(raw_range(in, (uint64_t)n * 4), raw_range(out, (uint64_t)n * 2))) return FORGE_E_ALIAS;
   const uint32_t key = sr_key(seed, (uint64_t)step, tensor_id);
-  hipError_t e = launch_debug_sr(in, out, (uint32_t)n, key, (hipStream_t)stream);
-  return e == hipSuccess ? FORGE_OK : FORGE_E_HIP;
+  return hip_status(launch_debug_sr(in, out, (uint32_t)n, key, (hipStream_t)stream));
 }
+
+const char* forge_last_error(void) { return hipGetErrorString(g_last_hip); }
 
 const char* forge_status_str(forge_status s) {
   switch (s) {

@@ -50,6 +50,7 @@ constexpr int LDS_G = TILE * GP * 4;             // 67,584 bytes
 constexpr int LDS_MAIN = 2 * 2 * 64 * TILE * 2;  // 2 stages x (dY, X) x 64 tok x 128 x bf16 = 65,536
 constexpr int LDS_BYTES = LDS_G > LDS_MAIN ? LDS_G : LDS_MAIN;
 constexpr uint32_t GOLDEN = 0x9E3779B9u;
+constexpr int WIDE_MIN_BT = 2048;                // token count from which the 256 x 256 kernel is used
 
 // ------------------------------------------------------------------------
 // Rounding helpers (paper, Appendix C)
@@ -418,6 +419,202 @@ __device__ __forceinline__ void tile_gradient_dma(const KArgs& a, char* lds, int
   bar();   // every wave is done reading the stages before G overwrites them
   store_acc(reinterpret_cast<float*>(lds), acc, threadIdx.x);
   __syncthreads();
+}
+
+// ------------------------------------------------------------------------
+// Wide mainloop for long token axes: a 256 x 256 macro tile per workgroup,
+// 4 waves in a 2 x 2 arrangement of 128 x 128 sub-tiles (16 accumulator
+// blocks per wave, 256 accumulator registers).  Per token the workgroup
+// fetches 1 KiB of dY and X for 128 Ki MFMA flops, half the bytes per flop
+// of the 128 x 128 tile, which matters once BT is long enough that the
+// activation panels no longer stay in L2.  Same asynchronous LDS-DMA ring
+// (4 stages of 32 tokens, 512-byte rows XOR-swizzled in 64-byte units) and
+// transposing reads as MainBF16Dma.
+// ------------------------------------------------------------------------
+struct MainWide {
+  static constexpr int TK = 32;
+  static constexpr int S = 4;
+  static constexpr int W = 256;                         // macro tile edge
+  static constexpr int ROWB = W * 2;                    // bytes per token row
+  static constexpr int OPB = TK * ROWB;                 // 16 KiB per operand per stage
+  static constexpr int STAGE = 2 * OPB;                 // 32 KiB
+  static constexpr int ROUNDS = OPB / (NT * 16);        // 4 load rounds per operand per chunk
+  static constexpr int LOADS = 2 * ROUNDS;              // buffer loads per thread per chunk
+
+  __amdgpu_buffer_rsrc_t rA, rB;
+  uint32_t oobA, oobB;
+  uint32_t baseA[ROUNDS], baseB[ROUNDS];
+  int trow[ROUNDS];
+  bool fokA[ROUNDS], fokB[ROUNDS];
+  int wave;
+
+  __device__ __forceinline__ static int off(int t, int f) { return t * ROWB + ((f * 2) ^ ((t & 3) << 6)); }
+
+  __device__ __forceinline__ void init(const KArgs& a, int row0, int col0) {
+    const int lane = threadIdx.x & 63;
+    wave = threadIdx.x >> 6;
+    oobA = (uint32_t)((uint64_t)a.BT * a.lddy * 2);
+    oobB = (uint32_t)((uint64_t)a.BT * a.ldx * 2);
+    rA = make_rsrc(a.dY, oobA);
+    rB = make_rsrc(a.X, oobB);
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r) {
+      // instruction (wave, r) fills bytes [(4r + wave) KiB, +1 KiB) of the operand region: 2 token rows
+      const int t = 2 * (4 * r + wave) + (lane >> 5);
+      const int c = (lane & 31) ^ ((t & 3) << 2);        // logical 8-feature chunk at this slot
+      trow[r] = t;
+      fokA[r] = row0 + c * 8 < a.N;
+      fokB[r] = col0 + c * 8 < a.K;
+      baseA[r] = (uint32_t)(row0 + c * 8) * 2;
+      baseB[r] = (uint32_t)(col0 + c * 8) * 2;
+    }
+  }
+
+  // Load J of this wave's share of chunk kc (round J / 2, operand J % 2).
+  // Tokens past BT (including whole chunks past the end) read as zeros.
+  template <int J>
+  __device__ __forceinline__ void issue_one(const KArgs& a, int kc, char* stage) const {
+    constexpr int r = J >> 1;
+    const int tok = kc * TK + trow[r];
+    const bool tok_ok = tok < a.BT;
+    if constexpr ((J & 1) == 0) {
+      const uint32_t oa = (tok_ok && fokA[r]) ? (uint32_t)tok * (uint32_t)(a.lddy * 2) + baseA[r] : oobA;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void*)(stage + (4 * r + wave) * 1024), 16, oa, 0, 0, 0);
+    } else {
+      const uint32_t ob = (tok_ok && fokB[r]) ? (uint32_t)tok * (uint32_t)(a.ldx * 2) + baseB[r] : oobB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void*)(stage + OPB + (4 * r + wave) * 1024), 16, ob, 0, 0,
+                                               0);
+    }
+  }
+
+  __device__ __forceinline__ void issue(const KArgs& a, int kc, char* stage) const {
+    issue_one<0>(a, kc, stage);
+    issue_one<1>(a, kc, stage);
+    issue_one<2>(a, kc, stage);
+    issue_one<3>(a, kc, stage);
+    issue_one<4>(a, kc, stage);
+    issue_one<5>(a, kc, stage);
+    issue_one<6>(a, kc, stage);
+    issue_one<7>(a, kc, stage);
+  }
+};
+
+// Transposing LDS read at a VGPR address plus an immediate byte offset.
+template <int IMM>
+__device__ __forceinline__ u32x2 tr_read_at(uint32_t lds_addr) {
+  static_assert(IMM >= 0 && IMM < 65536, "ds offset field");
+  u32x2 v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(lds_addr), "i"(IMM));
+  return v;
+}
+
+// Wait for every outstanding LDS read; ties the sixteen fragment registers of
+// one k-step to the wait so no use moves above it.
+__device__ __forceinline__ void lds_wait_all(u32x2 (&f)[16]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5]), "+v"(f[6]), "+v"(f[7]),
+                 "+v"(f[8]), "+v"(f[9]), "+v"(f[10]), "+v"(f[11]), "+v"(f[12]), "+v"(f[13]), "+v"(f[14]),
+                 "+v"(f[15]));
+}
+
+// One MFMA of a 16-token k-step on the wave's 128 x 128 sub-tile (block
+// I / 4, I % 4), followed, when READ, by read I of the next k-step's
+// fragments and, when DMA and I is even, by load I / 2 of the wave's share of
+// chunk kdma.  Fragment register r of a k-step: operand r / 8 (dY, X),
+// 32-wide block (r / 2) % 4, token half r % 2; adr[r / 2] is its LDS address
+// at token 0 of the stage and the immediate adds the k-step's first token T0
+// and the half.  The scheduling barrier keeps this order, so LDS latency and
+// the address unit's queue drain behind the matrix pipe instead of stalling
+// the wave's in-order issue.
+template <bool READ, bool DMA, int T0, int I>
+__device__ __forceinline__ void wide_one(f32x16 (&acc)[4][4], const u32x2 (&cur)[16], u32x2 (&nxt)[16],
+                                         const uint32_t (&adr)[8], const MainWide& ml, const KArgs& a, int kdma,
+                                         char* dstage) {
+  constexpr int bi = I >> 2, bj = I & 3;
+  acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_join(cur[2 * bi], cur[2 * bi + 1]),
+                                                        frag_join(cur[8 + 2 * bj], cur[8 + 2 * bj + 1]),
+                                                        acc[bi][bj], 0, 0, 0);
+  if constexpr (READ) nxt[I] = tr_read_at<(T0 + 4 * (I & 1)) * MainWide::ROWB>(adr[I >> 1]);
+  if constexpr (DMA && (I & 1) == 0) ml.template issue_one<I / 2>(a, kdma, dstage);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <bool READ, bool DMA, int T0, int... I>
+__device__ __forceinline__ void wide_kstep_seq(f32x16 (&acc)[4][4], const u32x2 (&cur)[16], u32x2 (&nxt)[16],
+                                               const uint32_t (&adr)[8], const MainWide& ml, const KArgs& a,
+                                               int kdma, char* dstage, std::integer_sequence<int, I...>) {
+  (wide_one<READ, DMA, T0, I>(acc, cur, nxt, adr, ml, a, kdma, dstage), ...);
+}
+
+template <bool READ, bool DMA, int T0>
+__device__ __forceinline__ void wide_kstep(f32x16 (&acc)[4][4], const u32x2 (&cur)[16], u32x2 (&nxt)[16],
+                                           const uint32_t (&adr)[8], const MainWide& ml, const KArgs& a, int kdma,
+                                           char* dstage) {
+  wide_kstep_seq<READ, DMA, T0>(acc, cur, nxt, adr, ml, a, kdma, dstage, std::make_integer_sequence<int, 16>{});
+}
+
+// Accumulate the wave's 128 x 128 sub-tile of the macro tile at (row0, col0).
+// Software pipeline: the fragments of each k-step are read from LDS while
+// the previous k-step's 16 MFMAs run.  The one barrier per chunk sits between
+// the chunk's two k-steps: by then every wave has finished reading the chunk,
+// so its stage is refilled with the chunk S ahead, and the next chunk has
+// landed, so its first k-step can be read during the second k-step here.
+__device__ __forceinline__ void wide_accumulate(const KArgs& a, char* ring, int row0, int col0,
+                                                f32x16 (&acc)[4][4]) {
+  using M = MainWide;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)ring;
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[bi][bj][e] = 0.f;
+  const int nk = (a.BT + M::TK - 1) / M::TK;
+  if (nk == 0) return;
+  M ml;
+  ml.init(a, row0, col0);
+  // lane part of the fragment addresses (token row and swizzled feature byte within a stage)
+  uint32_t off[8];
+  {
+    const int tl = 8 * (lane >> 5) + ((lane & 15) >> 2);
+    const int fl = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      off[b] = (uint32_t)M::off(tl, wr * 128 + b * 32 + fl);
+      off[4 + b] = (uint32_t)(M::OPB + M::off(tl, wc * 128 + b * 32 + fl));
+    }
+  }
+  // Every chunk slot gets its loads, real or (past the last chunk) zero
+  // fills of a stage that is never read again, so the waits are constant.
+  static_assert(M::S == 4, "the waits below assume 4 stages");
+#pragma unroll
+  for (int k = 0; k < M::S; ++k) ml.issue(a, k, ring + k * M::STAGE);
+  wait_vmcnt<3 * M::LOADS>();   // chunk 0
+  bar();
+  u32x2 f0[16], f1[16];
+  uint32_t adr[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) adr[r] = lds0 + off[r];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) f0[r] = tr_read(adr[r >> 1] + (uint32_t)(4 * (r & 1) * M::ROWB));
+  lds_wait_all(f0);
+  for (int kc = 0; kc < nk; ++kc) {
+    wide_kstep<true, false, 16>(acc, f0, f1, adr, ml, a, 0, ring);   // k-step 0 of chunk kc; read k-step 1
+    lds_wait_all(f1);
+    wait_vmcnt<2 * M::LOADS>();   // chunk kc + 1 (chunks kc + 2, kc + 3 may stay in flight)
+    bar();                        // all waves done with stage kc % S; chunk kc + 1 visible
+    // After the last chunk the reads below fetch a stale stage (inside the
+    // ring) and their values are never used.
+    const uint32_t st = lds0 + (uint32_t)(((kc + 1) % M::S) * M::STAGE);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) adr[r] = st + off[r];
+    // k-step 1 of chunk kc; read k-step 0 of chunk kc + 1; refill stage kc % S with chunk kc + S
+    wide_kstep<true, true, 0>(acc, f1, f0, adr, ml, a, kc + M::S, ring + (kc % M::S) * M::STAGE);
+    lds_wait_all(f0);
+  }
+  wait_vmcnt<0>();
 }
 
 // ------------------------------------------------------------------------
@@ -912,6 +1109,48 @@ __global__ void __launch_bounds__(NT, 2) k_fused(const KArgs a) {
   epi.run_tile(a, reinterpret_cast<const float*>(lds), row0, col0);
 }
 
+// Wide variant for aligned bf16 layers with a long token axis: one 256 x 256
+// macro tile per workgroup (one workgroup per CU: the ring takes 128 KiB of
+// LDS, the 256 accumulator registers of a wave the rest of the register
+// file).  After the mainloop the four 128 x 128 sub-tiles are staged through
+// LDS one at a time and run through the same epilogue as k_fused.
+constexpr int LDS_WIDE = MainWide::S * MainWide::STAGE;   // 128 KiB
+static_assert(LDS_WIDE >= LDS_G, "the staged G tile aliases the ring");
+
+template <int OPT, int WF, int MF, int VF>
+__global__ void __launch_bounds__(NT, 1) k_fused_wide(const KArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS_WIDE];
+  const int tw = (a.K + MainWide::W - 1) / MainWide::W;
+  const int mi = (int)blockIdx.x / tw;
+  const int row0 = mi * MainWide::W, col0 = ((int)blockIdx.x - mi * tw) * MainWide::W;
+  f32x16 acc[4][4];
+  wide_accumulate(a, lds, row0, col0, acc);
+  const int wave = threadIdx.x >> 6;
+  float* sG = reinterpret_cast<float*>(lds);
+  Epilogue<Step<OPT, WF, MF, VF, true>, FMT_NONE, true, 4> epi;
+  epi.tid = threadIdx.x;
+#pragma unroll
+  for (int sub = 0; sub < 4; ++sub) {
+    const int srow0 = row0 + (sub >> 1) * TILE, scol0 = col0 + (sub & 1) * TILE;
+    bar();                                   // the ring / the previous sub-tile is no longer read
+    if (wave == sub) {
+      const int lane = threadIdx.x & 63;
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int r = bi * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+            const int c = bj * 32 + (lane & 31);
+            sG[r * GP + c] = acc[bi][bj][e];
+          }
+    }
+    __syncthreads();
+    if (srow0 < a.N && scol0 < a.K) epi.run_tile(a, sG, srow0, scol0);
+  }
+}
+
 template <int IN, bool DMA>
 __global__ void __launch_bounds__(NT, 2) k_gemm(const KArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
@@ -997,8 +1236,25 @@ static hipError_t fused_w(const KArgs& a, int opt, int m_fmt, int v_fmt, hipStre
   return hipErrorInvalidValue;
 }
 
+template <int WF>
+static hipError_t fused_wide(const KArgs& a, int opt, int m_fmt, int v_fmt, hipStream_t st) {
+  const dim3 g((unsigned)(((a.N + 255) / 256) * ((a.K + 255) / 256)));
+#define X(O, M, V)                                                                  \
+  if (opt == O && m_fmt == M && v_fmt == V) {                                       \
+    hipLaunchKernelGGL((k_fused_wide<O, WF, M, V>), g, dim3(NT), 0, st, a);          \
+    return hipGetLastError();                                                       \
+  }
+  FORGE_STATE_LIST(X)
+#undef X
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_fused(const KArgs& a, int in_fmt, int w_fmt, int opt, int m_fmt, int v_fmt, hipStream_t st) {
   const bool fast = a.dma_ok && a.vec_state && (a.K % 4) == 0;
+  if (in_fmt == FMT_BF16 && fast && a.BT >= WIDE_MIN_BT) {
+    if (w_fmt == FMT_BF16) return fused_wide<FMT_BF16>(a, opt, m_fmt, v_fmt, st);
+    if (w_fmt == FMT_F32) return fused_wide<FMT_F32>(a, opt, m_fmt, v_fmt, st);
+  }
   if (in_fmt == FMT_BF16 && fast) {
     if (w_fmt == FMT_BF16) return fused_w<FMT_BF16, true, FMT_BF16>(a, opt, m_fmt, v_fmt, st);
     if (w_fmt == FMT_F32) return fused_w<FMT_BF16, true, FMT_F32>(a, opt, m_fmt, v_fmt, st);

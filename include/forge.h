@@ -176,6 +176,11 @@ const char* forge_status_str(forge_status s);
 /* Library version string (static). */
 const char* forge_version(void);
 
+/* HIP's description of the error behind the last FORGE_E_HIP returned on the
+ * calling thread ("no error" if there was none).  The string is static and
+ * stays valid until the process ends. */
+const char* forge_last_error(void);
+
 #ifdef __cplusplus
 }
 #endif

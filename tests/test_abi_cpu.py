@@ -23,7 +23,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("forge_wgrad_step", "forge_wgrad_check", "forge_wgrad_unfused", "forge_debug_sr_bf16",
-              "forge_status_str", "forge_version"):
+              "forge_status_str", "forge_version", "forge_last_error"):
         assert n in names
 
 
@@ -191,3 +191,23 @@ def test_unfused_argument_errors():
     rc = F.lib.forge_wgrad_unfused(ctypes.byref(X), ctypes.byref(dY), ctypes.byref(W), ctypes.byref(m),
                                    ctypes.byref(v), ctypes.byref(h), 1, 1, addr(2) + 64, F.FORGE_F32, None)
     assert rc == F.FORGE_E_ALIAS
+
+
+def test_last_error_is_a_static_string_before_any_launch():
+    # No device call has been made on this thread: the HIP error behind the
+    # last FORGE_E_HIP is hipSuccess's description.
+    s = F.forge_last_error()
+    assert isinstance(s, str) and len(s) > 0
+
+
+def test_one_hip_runtime_per_process():
+    # A fresh interpreter that imports only the binding must end up with a
+    # single libamdhip64 mapped (the one torch loads), whatever the order.
+    import subprocess
+    import sys
+    code = ("import os, backward_weight_gradient_amd\n"
+            "maps = open(f'/proc/{os.getpid()}/maps').read()\n"
+            "print(len(set(l.split()[-1] for l in maps.splitlines() if 'libamdhip64' in l)))\n")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip().splitlines()[-1] == "1"

@@ -291,7 +291,10 @@ def test_compute_bound_sweep_full_size(BT, name, N, K, opt):
 @pytest.mark.parametrize("spec,opt", [(SPEC_CFG1, "adamw"), (SPEC_CFG2, "adamw"), (SPEC_CFG3, "adamw"),
                                       (synth.LayerSpec("bf16", "bf16", "f32", None), "lion"),
                                       (synth.LayerSpec("bf16", "f32", "bf16", None), "sgdm")])
-@pytest.mark.parametrize("N,K,BT", [(2000, 4096, 300), (4104, 1024, 520), (600, 17152, 256)])
+# The last two shapes take the 256 x 256 macro-tile kernel used for long token
+# axes (ragged against 256 in both W dimensions and in the token chunks).
+@pytest.mark.parametrize("N,K,BT", [(2000, 4096, 300), (4104, 1024, 520), (600, 17152, 256),
+                                    (1000, 1408, 2050), (2048, 1664, 2080)])
 def test_aligned_multi_tile(spec, opt, N, K, BT):
     _say(f"case: aligned multi-tile {spec} {opt} {N}x{K} BT{BT}")
     L = make_layer(5, N, K, BT, 7, spec, gen_device="cuda", outlier_p=0.01 if spec.m_fmt == "s8" else 0.0)
