@@ -60,6 +60,14 @@ class forge_hyper(ctypes.Structure):
                 ("weight_decay", ctypes.c_double)]
 
 
+FORGE_GROUP_MAX = 8
+
+
+class forge_layer(ctypes.Structure):
+    _fields_ = [("X", ctypes.POINTER(forge_mat)), ("dY", ctypes.POINTER(forge_mat)), ("W", ctypes.POINTER(forge_mat)),
+                ("m", ctypes.POINTER(forge_state)), ("v", ctypes.POINTER(forge_state)), ("seed", ctypes.c_uint64)]
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libforge.so is not built ({LIB_PATH}); run "
@@ -80,6 +88,9 @@ def _load() -> ctypes.CDLL:
     lib.forge_debug_sr_bf16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64,
                                         ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p]
     lib.forge_debug_sr_bf16.restype = st
+    lib.forge_wgrad_step_group.argtypes = [P(forge_layer), ctypes.c_int32, P(forge_hyper), ctypes.c_int64,
+                                           ctypes.c_void_p]
+    lib.forge_wgrad_step_group.restype = st
     lib.forge_status_str.argtypes = [ctypes.c_int]
     lib.forge_status_str.restype = ctypes.c_char_p
     lib.forge_version.argtypes = []
@@ -174,6 +185,31 @@ def forge_wgrad_step(X, dY, W, m, v, h: forge_hyper, step: int, seed: int, strea
     rc = lib.forge_wgrad_step(_ref(X), _ref(dY), _ref(W), _ref(m), _ref(v), _ref(h), step, seed, _stream(stream))
     if check and rc != FORGE_OK:
         raise ForgeError(rc, "forge_wgrad_step")
+    return rc
+
+
+def forge_wgrad_step_group(layers, h: forge_hyper, step: int, stream=None, check: bool = True) -> int:
+    """forge_wgrad_step on several independent layers in as few launches as possible.
+
+    layers: sequence of (X, dY, W, m, v, seed) with X, dY, W tensors or forge_mat,
+    m, v forge_state (v None unless AdamW).
+    """
+    keep = []
+    arr = (forge_layer * max(1, len(layers)))()
+    for i, (X, dY, W, m, v, seed) in enumerate(layers):
+        X = mat(X) if not isinstance(X, forge_mat) else X
+        dY = mat(dY) if not isinstance(dY, forge_mat) else dY
+        W = mat(W) if not isinstance(W, forge_mat) else W
+        keep.append((X, dY, W, m, v))
+        arr[i].X = ctypes.pointer(X)
+        arr[i].dY = ctypes.pointer(dY)
+        arr[i].W = ctypes.pointer(W)
+        arr[i].m = ctypes.pointer(m) if m is not None else None
+        arr[i].v = ctypes.pointer(v) if v is not None else None
+        arr[i].seed = seed
+    rc = lib.forge_wgrad_step_group(arr, len(layers), _ref(h), step, _stream(stream))
+    if check and rc != FORGE_OK:
+        raise ForgeError(rc, "forge_wgrad_step_group")
     return rc
 
 

@@ -9,6 +9,8 @@
 
 #include "forge_internal.h"
 
+static_assert(FORGE_GROUP_MAX == forge::GROUP_MAX, "group size of the ABI and the kernels");
+
 namespace {
 
 using namespace forge;
@@ -118,6 +120,19 @@ forge_status check_state(const forge_state& s, int64_t N, int64_t K, bool first,
   return FORGE_OK;
 }
 
+// Memory written by a call (W, m, v and their scale arrays) and read-only inputs (X, dY).
+void layer_ranges(const forge_mat* X, const forge_mat* dY, const forge_mat* W, const forge_state* m,
+                  const forge_state* v, const Plan& pl, Range (&outs)[5], Range (&ins)[2]) {
+  outs[0] = mat_range(*W);
+  outs[1] = mat_range(m->q);
+  outs[2] = v ? mat_range(v->q) : Range();
+  outs[3] = raw_range(m->scale, m->scale ? (uint64_t)pl.N * (uint64_t)(pl.K / (m->block ? m->block : 1)) * 4 : 0);
+  outs[4] = (v && v->scale) ? raw_range(v->scale, (uint64_t)pl.N * (uint64_t)(pl.K / (v->block ? v->block : 1)) * 4)
+                            : Range();
+  ins[0] = mat_range(*X);
+  ins[1] = mat_range(*dY);
+}
+
 forge_status validate(const forge_mat* X, const forge_mat* dY, const forge_mat* W, const forge_state* m,
                       const forge_state* v, const forge_hyper* h, int64_t step, Plan& pl) {
   if (!X || !dY || !W || !h) return FORGE_E_NULL;
@@ -156,11 +171,8 @@ forge_status validate(const forge_mat* X, const forge_mat* dY, const forge_mat* 
   const int64_t tiles = ((pl.N + 127) / 128) * ((pl.K + 127) / 128);
   if (tiles >= (1ll << 31)) return FORGE_E_SHAPE;
   // aliasing: outputs must not overlap inputs or each other
-  Range outs[5] = {mat_range(*W), mat_range(m->q), v ? mat_range(v->q) : Range(),
-                   raw_range(m->scale, m->scale ? (uint64_t)pl.N * (uint64_t)(pl.K / (m->block ? m->block : 1)) * 4 : 0),
-                   (v && v->scale) ? raw_range(v->scale, (uint64_t)pl.N * (uint64_t)(pl.K / (v->block ? v->block : 1)) * 4)
-                                   : Range()};
-  const Range ins[2] = {mat_range(*X), mat_range(*dY)};
+  Range outs[5], ins[2];
+  layer_ranges(X, dY, W, m, v, pl, outs, ins);
   for (int i = 0; i < 5; ++i) {
     for (int j = 0; j < 2; ++j)
       if (overlap(outs[i], ins[j])) return FORGE_E_ALIAS;
@@ -255,6 +267,68 @@ forge_status forge_wgrad_step(const forge_mat* X, const forge_mat* dY, forge_mat
   if (st != FORGE_OK || pl.empty) return st;
   const KArgs a = make_args(X, dY, W, m, v, h, step, seed, pl);
   return hip_status(launch_fused(a, pl.in_fmt, pl.w_fmt, h->opt, pl.m_fmt, pl.v_fmt, (hipStream_t)stream));
+}
+
+forge_status forge_wgrad_step_group(const forge_layer* layers, int32_t n, const forge_hyper* h, int64_t step,
+                                    void* stream) {
+  if (n < 1 || n > FORGE_GROUP_MAX) return FORGE_E_SHAPE;
+  if (!layers || !h) return FORGE_E_NULL;
+  Plan pl[FORGE_GROUP_MAX];
+  for (int i = 0; i < n; ++i) {
+    const forge_layer& L = layers[i];
+    const forge_status st = validate(L.X, L.dY, L.W, L.m, L.v, h, step, pl[i]);
+    if (st != FORGE_OK) return st;
+  }
+  // one kernel instantiation serves the group: identical formats
+  int ref = -1;
+  for (int i = 0; i < n; ++i) {
+    if (pl[i].empty) continue;
+    if (ref < 0) { ref = i; continue; }
+    const Plan& a = pl[ref];
+    const Plan& b = pl[i];
+    if (a.in_fmt != b.in_fmt || a.w_fmt != b.w_fmt || a.m_fmt != b.m_fmt || a.v_fmt != b.v_fmt ||
+        a.block != b.block)
+      return FORGE_E_UNSUPPORTED;
+  }
+  if (ref < 0) return FORGE_OK;
+  // layers are independent: nothing one layer writes may overlap any buffer of another
+  Range outs[FORGE_GROUP_MAX][5], ins[FORGE_GROUP_MAX][2];
+  for (int i = 0; i < n; ++i) {
+    const forge_layer& L = layers[i];
+    layer_ranges(L.X, L.dY, L.W, L.m, L.v, pl[i], outs[i], ins[i]);
+  }
+  for (int i = 0; i < n; ++i)
+    for (int j = 0; j < n; ++j) {
+      if (i == j) continue;
+      for (int p = 0; p < 5; ++p) {
+        for (int q = 0; q < 5; ++q)
+          if (overlap(outs[i][p], outs[j][q])) return FORGE_E_ALIAS;
+        for (int q = 0; q < 2; ++q)
+          if (overlap(outs[i][p], ins[j][q])) return FORGE_E_ALIAS;
+      }
+    }
+  // eligible layers share one launch; the others get their own
+  GroupArgs g;
+  std::memset(&g, 0, sizeof(g));
+  int64_t tiles = 0;
+  for (int i = 0; i < n; ++i) {
+    if (pl[i].empty) continue;
+    const forge_layer& L = layers[i];
+    const KArgs a = make_args(L.X, L.dY, L.W, L.m, L.v, h, step, L.seed, pl[i]);
+    if (group_eligible(a, pl[i].in_fmt)) {
+      g.layer[g.n] = a;
+      g.first_tile[g.n] = (int32_t)tiles;
+      tiles += (int64_t)a.tiles_n * a.tiles_k;
+      ++g.n;
+    } else {
+      const forge_status st =
+          hip_status(launch_fused(a, pl[i].in_fmt, pl[i].w_fmt, h->opt, pl[i].m_fmt, pl[i].v_fmt, (hipStream_t)stream));
+      if (st != FORGE_OK) return st;
+    }
+  }
+  if (g.n == 0) return FORGE_OK;
+  g.first_tile[g.n] = (int32_t)tiles;
+  return hip_status(launch_fused_group(g, pl[ref].w_fmt, h->opt, pl[ref].m_fmt, pl[ref].v_fmt, (hipStream_t)stream));
 }
 
 forge_status forge_wgrad_unfused(const forge_mat* X, const forge_mat* dY, forge_mat* W, forge_state* m,

@@ -45,11 +45,25 @@ struct KArgs {
   EpiConst c;
 };
 
+// Up to GROUP_MAX independent layers launched together (same formats and
+// optimizer).  first_tile[i] is the first workgroup of layer i;
+// first_tile[n] is the grid size.
+constexpr int GROUP_MAX = 8;
+struct GroupArgs {
+  KArgs layer[GROUP_MAX];
+  int32_t first_tile[GROUP_MAX + 1];
+  int32_t n;
+};
+
 bool combo_supported(int in_fmt, int w_fmt, int opt, int m_fmt, int v_fmt);
+// Whether a layer can run in the grouped kernel (aligned bf16, short token axis).
+bool group_eligible(const KArgs& a, int in_fmt);
 
 // Fused weight-gradient + step: one workgroup per 128 x 128 tile of W.
 hipError_t launch_fused(const KArgs& a, int in_fmt, int w_fmt, int opt, int m_fmt, int v_fmt,
                         hipStream_t stream);
+// Fused step of g.n group-eligible layers in one launch (bf16 inputs).
+hipError_t launch_fused_group(const GroupArgs& g, int w_fmt, int opt, int m_fmt, int v_fmt, hipStream_t stream);
 // Unfused baseline, phase 1: G tiles -> a.dW (a.dw_fmt).
 hipError_t launch_gemm(const KArgs& a, int in_fmt, hipStream_t stream);
 // Unfused baseline, phase 2: the same step, reading G from a.dW.

@@ -1109,6 +1109,28 @@ __global__ void __launch_bounds__(NT, 2) k_fused(const KArgs a) {
   epi.run_tile(a, reinterpret_cast<const float*>(lds), row0, col0);
 }
 
+// Several independent layers in one launch: the workgroups cover the
+// concatenation of the layers' tile spaces (layer order, row-major tiles
+// within a layer).  Each workgroup finds its layer from the prefix tile
+// counts (uniform scalar work) and then runs exactly the k_fused code on it,
+// so every element is computed as a separate call would compute it.
+template <int OPT, int WF, int MF, int VF>
+__global__ void __launch_bounds__(NT, 2) k_fused_group(const GroupArgs g) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  const int bid = (int)blockIdx.x;
+  int li = 0;
+#pragma unroll
+  for (int i = 1; i < GROUP_MAX; ++i) li += (i < g.n && bid >= g.first_tile[i]) ? 1 : 0;
+  const KArgs& a = g.layer[li];
+  int ti, tj;
+  tile_coords(bid - g.first_tile[li], a.tiles_n, a.tiles_k, ti, tj);
+  const int row0 = ti * TILE, col0 = tj * TILE;
+  tile_gradient_dma(a, lds, row0, col0);
+  Epilogue<Step<OPT, WF, MF, VF, true>, FMT_NONE, true, 4> epi;
+  epi.tid = threadIdx.x;
+  epi.run_tile(a, reinterpret_cast<const float*>(lds), row0, col0);
+}
+
 // Wide variant for aligned bf16 layers with a long token axis: one 256 x 256
 // macro tile per workgroup (one workgroup per CU: the ring takes 128 KiB of
 // LDS, the 256 accumulator registers of a wave the rest of the register
@@ -1265,6 +1287,30 @@ hipError_t launch_fused(const KArgs& a, int in_fmt, int w_fmt, int opt, int m_fm
     if (w_fmt == FMT_BF16) return fused_w<FMT_F32, false, FMT_BF16>(a, opt, m_fmt, v_fmt, st);
     if (w_fmt == FMT_F32) return fused_w<FMT_F32, false, FMT_F32>(a, opt, m_fmt, v_fmt, st);
   }
+  return hipErrorInvalidValue;
+}
+
+bool group_eligible(const KArgs& a, int in_fmt) {
+  return in_fmt == FMT_BF16 && a.dma_ok && a.vec_state && (a.K % 4) == 0 && a.BT < WIDE_MIN_BT;
+}
+
+template <int WF>
+static hipError_t fused_group_w(const GroupArgs& g, int opt, int m_fmt, int v_fmt, hipStream_t st) {
+  const dim3 grid((unsigned)g.first_tile[g.n]);
+#define X(O, M, V)                                                                   \
+  if (opt == O && m_fmt == M && v_fmt == V) {                                        \
+    hipLaunchKernelGGL((k_fused_group<O, WF, M, V>), grid, dim3(NT), 0, st, g);       \
+    return hipGetLastError();                                                        \
+  }
+  FORGE_STATE_LIST(X)
+#undef X
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fused_group(const GroupArgs& g, int w_fmt, int opt, int m_fmt, int v_fmt, hipStream_t st) {
+  if (g.n < 1 || g.n > GROUP_MAX) return hipErrorInvalidValue;
+  if (w_fmt == FMT_BF16) return fused_group_w<FMT_BF16>(g, opt, m_fmt, v_fmt, st);
+  if (w_fmt == FMT_F32) return fused_group_w<FMT_F32>(g, opt, m_fmt, v_fmt, st);
   return hipErrorInvalidValue;
 }
 

@@ -1,13 +1,21 @@
 #!/usr/bin/env python3
 """Benchmark of the fused weight-gradient + AdamW step on one MI355X.
 
-One step = one fused forge_wgrad_step launch for each linear layer of a
-Llama-3.1-8B decoder layer (q, k, v, o, gate, up, down) at BT = 512 tokens
+One step = the fused weight-gradient + AdamW update of every linear layer of
+a Llama-3.1-8B decoder layer (q, k, v, o, gate, up, down) at BT = 512 tokens
 (batch 1 x sequence 512): bf16 X / dY / W, fp32 m / v, AdamW with bias
 correction (step t = 10), stochastic-rounding bf16 weight store.  Inputs are
 seeded synthetic tensors with the real layer shapes (X ~ N(0, 1),
 dY ~ N(0, 1e-3^2), W ~ N(0, 0.02^2), m = 0, v = |N(0, 1e-6^2)|), resident in
 HBM before timing starts.
+
+Launch grouping (--grouping).  A layer's update only has to follow the input
+gradient dX computed from its pre-update W (FORGE, Remark 1), so its weight
+step may wait until the end of its sub-block's backward.  Default "subblock":
+one forge_wgrad_step_group launch for the MLP ([gate, up, down]) and one for
+attention ([q, k, v, o]).  "ready": four launches as the layer gradients
+become available in backward order ([down], [gate, up], [o], [q, k, v]).
+"layer": seven forge_wgrad_step launches.  The work is the same in all three.
 
 Prints one JSON line: params/s over the whole step, the fused kernel's
 achieved HBM bandwidth against the 8 TB/s peak (algorithmic bytes: state read
@@ -44,6 +52,10 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     p.add_argument("--no-unfused", action="store_true", help="skip the unfused comparison")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle work in seconds")
+    p.add_argument("--grouping", choices=["subblock", "ready", "layer"], default="subblock",
+                   help="subblock: one launch per sub-block, [gate, up, down] and [q, k, v, o]; ready: as the "
+                        "gradients become available, [down] [gate, up] [o] [q, k, v]; layer: one "
+                        "forge_wgrad_step launch per layer")
     p.add_argument("--copy-calibration", action="store_true",
                    help="instead of the step, time a plain 1 GiB device copy (read 1 GiB, write 1 GiB): the "
                         "reference kernel for scaling HBM counter readings")
@@ -159,13 +171,28 @@ def main():
     P_total = sum(N * K for N, K in layers.values())
     bytes_total = sum(layer_bytes(N, K, BT) for N, K in layers.values())
     flops_total = sum(2 * BT * N * K for N, K in layers.values())
-    names = list(layers)
+    if args.grouping == "layer":
+        groups = [(n,) for n in layers]
+    elif args.grouping == "ready":
+        groups = [("down_proj",), ("gate_proj", "up_proj"), ("o_proj",), ("q_proj", "k_proj", "v_proj")]
+    else:
+        groups = [("gate_proj", "up_proj", "down_proj"), ("q_proj", "k_proj", "v_proj", "o_proj")]
+    names = [",".join(g) for g in groups]
+    group_of = dict(zip(names, groups))
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
 
     def launch(name):
-        d = L[name]
-        F.forge_wgrad_step(d["Xm"], d["dYm"], d["Wm"], d["mst"], d["vst"], h, STEP_T, SEED, stream=sptr)
+        g = group_of[name]
+        if args.grouping == "layer":
+            d = L[g[0]]
+            F.forge_wgrad_step(d["Xm"], d["dYm"], d["Wm"], d["mst"], d["vst"], h, STEP_T, SEED, stream=sptr)
+        else:
+            F.forge_wgrad_step_group([(L[n]["Xm"], L[n]["dYm"], L[n]["Wm"], L[n]["mst"], L[n]["vst"], SEED)
+                                      for n in g], h, STEP_T, stream=sptr)
+
+    def group_bytes(name):
+        return sum(layer_bytes(*layers[n], BT) for n in group_of[name])
 
     for _ in range(args.warmup):
         for n in names:
@@ -199,14 +226,17 @@ def main():
                 "traffic": None if traffic_step is None else round(traffic_step / len(names))}
 
     extras = {
-        "kernel": "forge::k_fused<bf16 in, AdamW, bf16 W, fp32 m, fp32 v>",
+        "kernel": ("forge::k_fused<bf16 in, AdamW, bf16 W, fp32 m, fp32 v>" if args.grouping == "layer" else
+                   "forge::k_fused_group<AdamW, bf16 W, fp32 m, fp32 v>"),
+        "grouping": args.grouping,
+        "launches": names,
         "launches_per_step": len(names),
         "algorithmic_bytes_per_step": bytes_total,
         "algorithmic_bytes_per_launch_mean": bytes_total / len(names),
         "kernel_ms_per_step_mean": round(kernel_ms, 4),
         "mfma_util": round(flops_total / (kernel_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-        "per_layer_us_median": {n: round(1e3 * v, 2) for n, v in med.items()},
-        "per_layer_gbs_median": {n: round(layer_bytes(*layers[n], BT) / (med[n] * 1e-3) / 1e9, 1) for n in names},
+        "per_launch_us_median": {n: round(1e3 * v, 2) for n, v in med.items()},
+        "per_launch_gbs_median": {n: round(group_bytes(n) / (med[n] * 1e-3) / 1e9, 1) for n in names},
     }
 
     if not args.no_unfused:
@@ -221,10 +251,10 @@ def main():
         peak_fused = torch.cuda.max_memory_allocated() - base_alloc
         dws = {}
         torch.cuda.reset_peak_memory_stats()
-        for n in names:
+        for n in layers:
             dws[n] = torch.empty((L[n]["N"], L[n]["K"]), device=dev, dtype=torch.float32)
         for _ in range(max(1, args.warmup)):
-            for n in names:
+            for n in layers:
                 d = L[n]
                 F.forge_wgrad_unfused(d["Xm"], d["dYm"], d["Wm"], d["mst"], d["vst"], h, STEP_T, SEED, dws[n],
                                       stream=sptr)
@@ -234,7 +264,7 @@ def main():
         u1 = torch.cuda.Event(enable_timing=True)
         u0.record(stream)
         for _ in range(args.steps):
-            for n in names:
+            for n in layers:
                 d = L[n]
                 F.forge_wgrad_unfused(d["Xm"], d["dYm"], d["Wm"], d["mst"], d["vst"], h, STEP_T, SEED, dws[n],
                                       stream=sptr)

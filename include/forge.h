@@ -134,6 +134,42 @@ forge_status forge_wgrad_step(const forge_mat* X, const forge_mat* dY, forge_mat
                               int64_t step, uint64_t seed, void* stream);
 
 /*
+ * forge_wgrad_step_group -- forge_wgrad_step on n independent layers that
+ * share one optimizer, step and hyper-parameters, with as few launches as
+ * possible.  Layers whose gradients become available together in a backward
+ * pass (q/k/v after attention, gate/up after the MLP activation) are the
+ * intended use: their tiles are scheduled as one grid (the tile scheduling
+ * of FORGE, Section 3 and Algorithm 1: one workgroup per 128 x 128 tile,
+ * here over the union of the layers' tile spaces).
+ *
+ * layers[i] holds the arguments forge_wgrad_step takes for layer i, and its
+ * own SR seed.  The result equals n separate forge_wgrad_step calls, bit for
+ * bit.  Layers may share inputs (q/k/v read the same X) but nothing a layer
+ * writes (W, m, v, scales) may overlap any buffer of another layer.  All
+ * non-empty layers must have the same X / W / m / v dtypes and int8 block;
+ * shapes and BT may differ.  Aligned bf16 layers with BT < 2048 run in one
+ * launch; any other layer gets its own launch, on the same stream.
+ *
+ * Errors: FORGE_E_SHAPE (n < 1 or n > FORGE_GROUP_MAX), E_NULL, every error
+ * of forge_wgrad_step for each layer, E_UNSUPPORTED (formats differ between
+ * layers), E_ALIAS (between layers) -- all before anything is enqueued -- or
+ * E_HIP.
+ */
+#define FORGE_GROUP_MAX 8
+
+typedef struct {
+  const forge_mat* X;
+  const forge_mat* dY;
+  forge_mat* W;
+  forge_state* m;
+  forge_state* v;  /* NULL unless AdamW */
+  uint64_t seed;
+} forge_layer;
+
+forge_status forge_wgrad_step_group(const forge_layer* layers, int32_t n, const forge_hyper* h,
+                                    int64_t step, void* stream);
+
+/*
  * forge_wgrad_check -- the validation of forge_wgrad_step alone: same
  * arguments, same return codes, no device call at all (usable on a host
  * without a GPU).

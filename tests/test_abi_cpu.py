@@ -211,3 +211,65 @@ def test_one_hip_runtime_per_process():
     out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
     assert out.returncode == 0, out.stderr
     assert out.stdout.strip().splitlines()[-1] == "1"
+
+
+# ---------------------------------------------------------------------------
+# forge_wgrad_step_group: every error is decided before anything is enqueued,
+# so these cases make no device call.
+# ---------------------------------------------------------------------------
+def glayer(slot, seed=0, **kw):
+    """layer() at its own set of fake addresses (slot 0 == layer())."""
+    X, dY, W, m, v = layer(**kw)
+    shift = slot * 8 * GAP
+    X.data += shift
+    dY.data += shift
+    W.data += shift
+    m.q.data += shift
+    if m.scale:
+        m.scale += shift
+    if v is not None:
+        v.q.data += shift
+        if v.scale:
+            v.scale += shift
+    return (X, dY, W, m, v, seed)
+
+
+def group(layers, h=None, step=10):
+    return F.forge_wgrad_step_group(layers, h or F.hyper(), step, stream=0, check=False)
+
+
+def test_group_count_limits():
+    assert group([]) == F.FORGE_E_SHAPE
+    assert group([glayer(i) for i in range(F.FORGE_GROUP_MAX + 1)]) == F.FORGE_E_SHAPE
+
+
+def test_group_reports_a_layers_own_error():
+    bad = glayer(1, N=256, K=255)                       # W must be [N, K]: shape mismatch below
+    X, dY, W, m, v, s = bad
+    W.cols = 100
+    assert group([glayer(0), (X, dY, W, m, v, s)]) == F.FORGE_E_SHAPE
+    assert group([glayer(0), glayer(1)], step=0) == F.FORGE_E_STEP
+
+
+def test_group_formats_must_agree():
+    assert group([glayer(0), glayer(1, m_dt=F.FORGE_BF16, v_dt=F.FORGE_BF16)]) == F.FORGE_E_UNSUPPORTED
+    assert group([glayer(0), glayer(1, w_dt=F.FORGE_F32)]) == F.FORGE_E_UNSUPPORTED
+    assert group([glayer(0, m_dt=F.FORGE_S8, v_dt=F.FORGE_U8, block=128),
+                  glayer(1, m_dt=F.FORGE_S8, v_dt=F.FORGE_U8, block=64)]) == F.FORGE_E_UNSUPPORTED
+
+
+def test_group_layers_must_not_write_each_others_buffers():
+    a = glayer(0)
+    b = glayer(1)
+    # layer 1's W on top of layer 0's X
+    b[2].data = a[0].data
+    assert group([a, b]) == F.FORGE_E_ALIAS
+    # layer 1's m on top of layer 0's W
+    b = glayer(1)
+    b[3].q.data = a[2].data
+    assert group([a, b]) == F.FORGE_E_ALIAS
+
+
+def test_group_of_empty_layers_is_a_no_op():
+    # N == 0 everywhere: valid and nothing to launch
+    assert group([glayer(0, N=0), glayer(1, N=0)]) == F.FORGE_OK
