@@ -56,6 +56,8 @@ def parse():
                    help="subblock: one launch per sub-block, [gate, up, down] and [q, k, v, o]; ready: as the "
                         "gradients become available, [down] [gate, up] [o] [q, k, v]; layer: one "
                         "forge_wgrad_step launch per layer")
+    p.add_argument("--no-mfma-sweep", action="store_true",
+                   help="skip the compute-bound sweep (down_proj, lm_head at BT 2048 / 8192)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="instead of the step, time a plain 1 GiB device copy (read 1 GiB, write 1 GiB): the "
                         "reference kernel for scaling HBM counter readings")
@@ -93,17 +95,51 @@ def kernel_sha():
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def load_traffic():
+def load_traffic(grouping):
     """HBM bytes per step measured with rocprofv3 counters, if they were taken
-    on the current kernel source; else None."""
+    on the current kernel source with the same launch grouping; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha256") != kernel_sha():
+    if t.get("kernel_source_sha256") != kernel_sha() or t.get("grouping") != grouping:
         return None
     return t.get("hbm_bytes_per_step")
+
+
+def mfma_sweep(F, synth, h, reps=3):
+    """Compute-bound configurations: down_proj [4096, 14336] and lm_head
+    [128256, 4096] at BT = 2048 and 8192, same formats and optimizer as the
+    step (one launch each; HIP events on the launch stream).  Reported as
+    achieved bf16 MFMA TFLOP/s (2 BT N K flops) against the 2.5 PFLOP/s peak."""
+    import torch
+    spec = synth.LayerSpec(in_dtype="bf16", w_fmt="bf16", m_fmt="f32", v_fmt="f32")
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name, (N, K) in (("down_proj", (4096, 14336)), ("lm_head", (128256, 4096))):
+        for bt in (2048, 8192):
+            X, dY = synth.activations(4, bt, N, K, STEP_T, device="cuda")
+            st = synth.state(4, N, K, spec, device="cuda")
+            args = (F.mat(X), F.mat(dY), F.mat(st["W"]), F.state(st["m"]), F.state(st["v"]))
+            F.forge_wgrad_step(*args, h, STEP_T, SEED, stream=stream.cuda_stream)
+            torch.cuda.synchronize()
+            times = []
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                F.forge_wgrad_step(*args, h, STEP_T, SEED, stream=stream.cuda_stream)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1))
+            ms = sorted(times)[len(times) // 2]
+            tflops = 2.0 * bt * N * K / (ms * 1e-3) / 1e12
+            out[f"{name}_bt{bt}"] = {"us": round(1e3 * ms, 1), "tflops": round(tflops, 1),
+                                     "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                                     "hbm_gbs_alg": round(layer_bytes(N, K, bt) / (ms * 1e-3) / 1e9, 1)}
+            del X, dY, st, args
+            torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(layers, seconds):
@@ -220,7 +256,7 @@ def main():
     kernel_ms = sum(sum(v) for v in per_layer.values()) / args.steps   # mean kernel time per step
     achieved_gbs = bytes_total / (kernel_ms * 1e-3) / 1e9
 
-    traffic_step = load_traffic()
+    traffic_step = load_traffic(args.grouping)
     roofline = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
                 "traffic": None if traffic_step is None else round(traffic_step / len(names))}
@@ -276,6 +312,9 @@ def main():
         extras["peak_extra_bytes_unfused_fp32_dw"] = int(peak_unfused)
         del dws
         torch.cuda.empty_cache()
+
+    if not args.no_mfma_sweep:
+        extras["compute_bound_sweep"] = mfma_sweep(F, synth, h)
 
     cpu = None
     if not args.no_cpu_baseline:
