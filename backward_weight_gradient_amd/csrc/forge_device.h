@@ -1,4 +1,10 @@
-// gfx950 kernels: fused weight gradient + element-wise optimizer step.
+#pragma once
+
+// gfx950 device code: fused weight gradient + element-wise optimizer step.
+//
+// Every kernel here is a template; the family sources (forge_k_*.hip)
+// instantiate the launchers at the end of this file for their optimizer /
+// state combinations, so the families compile in parallel.
 //
 // FORGE paper (arXiv 2606.22932), section 2.2 and Algorithm 1: for every
 // 128 x 128 tile (i, j) of W the tile gradient
@@ -50,7 +56,6 @@ constexpr int LDS_G = TILE * GP * 4;             // 67,584 bytes
 constexpr int LDS_MAIN = 2 * 2 * 64 * TILE * 2;  // 2 stages x (dY, X) x 64 tok x 128 x bf16 = 65,536
 constexpr int LDS_BYTES = LDS_G > LDS_MAIN ? LDS_G : LDS_MAIN;
 constexpr uint32_t GOLDEN = 0x9E3779B9u;
-constexpr int WIDE_MIN_BT = 2048;                // token count from which the 256 x 256 kernel is used
 
 // ------------------------------------------------------------------------
 // Rounding helpers (paper, Appendix C)
@@ -1151,8 +1156,7 @@ __global__ void __launch_bounds__(NT, 1) k_fused_wide(const KArgs a) {
   float* sG = reinterpret_cast<float*>(lds);
   Epilogue<Step<OPT, WF, MF, VF, true>, FMT_NONE, true, 4> epi;
   epi.tid = threadIdx.x;
-#pragma unroll
-  for (int sub = 0; sub < 4; ++sub) {
+  for (int sub = 0; sub < 4; ++sub) {   // sub-tile (sub / 2, sub % 2), owned by wave sub
     const int srow0 = row0 + (sub >> 1) * TILE, scol0 = col0 + (sub & 1) * TILE;
     bar();                                   // the ring / the previous sub-tile is no longer read
     if (wave == sub) {
@@ -1215,149 +1219,69 @@ __global__ void __launch_bounds__(NT, 2) k_step(const KArgs a) {
   epi.run_tile(a, nullptr, ti * TILE, tj * TILE);
 }
 
-__global__ void k_debug_sr(const float* __restrict__ in, uint16_t* __restrict__ out, uint32_t n, uint32_t key) {
-  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) out[i] = (uint16_t)bf16_sr_bits(in[i], key, i);
-}
-
 // ------------------------------------------------------------------------
-// Dispatch
+// Launchers of one (optimizer, m format, v format) combination.
 // ------------------------------------------------------------------------
-// Supported (opt, m, v) state layouts.
-#define FORGE_STATE_LIST(X)                       \
-  X(OPT_ADAMW, FMT_F32, FMT_F32)                  \
-  X(OPT_ADAMW, FMT_BF16, FMT_BF16)                \
-  X(OPT_ADAMW, FMT_S8, FMT_U8)                    \
-  X(OPT_LION, FMT_F32, FMT_NONE)                  \
-  X(OPT_LION, FMT_BF16, FMT_NONE)                 \
-  X(OPT_LION, FMT_S8, FMT_NONE)                   \
-  X(OPT_SGDM, FMT_F32, FMT_NONE)                  \
-  X(OPT_SGDM, FMT_BF16, FMT_NONE)                 \
-  X(OPT_SGDM, FMT_S8, FMT_NONE)
-
-bool combo_supported(int in_fmt, int w_fmt, int opt, int m_fmt, int v_fmt) {
-  if (in_fmt != FMT_F32 && in_fmt != FMT_BF16) return false;
-  if (w_fmt != FMT_F32 && w_fmt != FMT_BF16) return false;
-#define X(O, M, V) if (opt == O && m_fmt == M && v_fmt == V) return true;
-  FORGE_STATE_LIST(X)
-#undef X
-  return false;
-}
-
 static inline dim3 tile_grid(const KArgs& a) { return dim3((unsigned)(a.tiles_n * a.tiles_k)); }
 
-template <int IN, bool DMA, int WF>
-static hipError_t fused_w(const KArgs& a, int opt, int m_fmt, int v_fmt, hipStream_t st) {
-#define X(O, M, V)                                                                      \
-  if (opt == O && m_fmt == M && v_fmt == V) {                                           \
-    hipLaunchKernelGGL((k_fused<IN, DMA, O, WF, M, V>), tile_grid(a), dim3(NT), 0, st, a); \
-    return hipGetLastError();                                                           \
-  }
-  FORGE_STATE_LIST(X)
-#undef X
-  return hipErrorInvalidValue;
-}
-
-template <int WF>
-static hipError_t fused_wide(const KArgs& a, int opt, int m_fmt, int v_fmt, hipStream_t st) {
-  const dim3 g((unsigned)(((a.N + 255) / 256) * ((a.K + 255) / 256)));
-#define X(O, M, V)                                                                  \
-  if (opt == O && m_fmt == M && v_fmt == V) {                                       \
-    hipLaunchKernelGGL((k_fused_wide<O, WF, M, V>), g, dim3(NT), 0, st, a);          \
-    return hipGetLastError();                                                       \
-  }
-  FORGE_STATE_LIST(X)
-#undef X
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_fused(const KArgs& a, int in_fmt, int w_fmt, int opt, int m_fmt, int v_fmt, hipStream_t st) {
+template <int O, int M, int V>
+hipError_t combo_fused(const KArgs& a, int in_fmt, int w_fmt, hipStream_t st) {
   const bool fast = a.dma_ok && a.vec_state && (a.K % 4) == 0;
+  const dim3 b(NT);
+  if (w_fmt != FMT_BF16 && w_fmt != FMT_F32) return hipErrorInvalidValue;
+  const bool wbf = w_fmt == FMT_BF16;
   if (in_fmt == FMT_BF16 && fast && a.BT >= WIDE_MIN_BT) {
-    if (w_fmt == FMT_BF16) return fused_wide<FMT_BF16>(a, opt, m_fmt, v_fmt, st);
-    if (w_fmt == FMT_F32) return fused_wide<FMT_F32>(a, opt, m_fmt, v_fmt, st);
-  }
-  if (in_fmt == FMT_BF16 && fast) {
-    if (w_fmt == FMT_BF16) return fused_w<FMT_BF16, true, FMT_BF16>(a, opt, m_fmt, v_fmt, st);
-    if (w_fmt == FMT_F32) return fused_w<FMT_BF16, true, FMT_F32>(a, opt, m_fmt, v_fmt, st);
+    const dim3 g((unsigned)(((a.N + 255) / 256) * ((a.K + 255) / 256)));
+    if (wbf) hipLaunchKernelGGL((k_fused_wide<O, FMT_BF16, M, V>), g, b, 0, st, a);
+    else hipLaunchKernelGGL((k_fused_wide<O, FMT_F32, M, V>), g, b, 0, st, a);
+  } else if (in_fmt == FMT_BF16 && fast) {
+    if (wbf) hipLaunchKernelGGL((k_fused<FMT_BF16, true, O, FMT_BF16, M, V>), tile_grid(a), b, 0, st, a);
+    else hipLaunchKernelGGL((k_fused<FMT_BF16, true, O, FMT_F32, M, V>), tile_grid(a), b, 0, st, a);
   } else if (in_fmt == FMT_BF16) {
-    if (w_fmt == FMT_BF16) return fused_w<FMT_BF16, false, FMT_BF16>(a, opt, m_fmt, v_fmt, st);
-    if (w_fmt == FMT_F32) return fused_w<FMT_BF16, false, FMT_F32>(a, opt, m_fmt, v_fmt, st);
+    if (wbf) hipLaunchKernelGGL((k_fused<FMT_BF16, false, O, FMT_BF16, M, V>), tile_grid(a), b, 0, st, a);
+    else hipLaunchKernelGGL((k_fused<FMT_BF16, false, O, FMT_F32, M, V>), tile_grid(a), b, 0, st, a);
   } else if (in_fmt == FMT_F32) {
-    if (w_fmt == FMT_BF16) return fused_w<FMT_F32, false, FMT_BF16>(a, opt, m_fmt, v_fmt, st);
-    if (w_fmt == FMT_F32) return fused_w<FMT_F32, false, FMT_F32>(a, opt, m_fmt, v_fmt, st);
+    if (wbf) hipLaunchKernelGGL((k_fused<FMT_F32, false, O, FMT_BF16, M, V>), tile_grid(a), b, 0, st, a);
+    else hipLaunchKernelGGL((k_fused<FMT_F32, false, O, FMT_F32, M, V>), tile_grid(a), b, 0, st, a);
+  } else {
+    return hipErrorInvalidValue;
   }
-  return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
-bool group_eligible(const KArgs& a, int in_fmt) {
-  return in_fmt == FMT_BF16 && a.dma_ok && a.vec_state && (a.K % 4) == 0 && a.BT < WIDE_MIN_BT;
-}
-
-template <int WF>
-static hipError_t fused_group_w(const GroupArgs& g, int opt, int m_fmt, int v_fmt, hipStream_t st) {
-  const dim3 grid((unsigned)g.first_tile[g.n]);
-#define X(O, M, V)                                                                   \
-  if (opt == O && m_fmt == M && v_fmt == V) {                                        \
-    hipLaunchKernelGGL((k_fused_group<O, WF, M, V>), grid, dim3(NT), 0, st, g);       \
-    return hipGetLastError();                                                        \
-  }
-  FORGE_STATE_LIST(X)
-#undef X
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_fused_group(const GroupArgs& g, int w_fmt, int opt, int m_fmt, int v_fmt, hipStream_t st) {
+template <int O, int M, int V>
+hipError_t combo_group(const GroupArgs& g, int w_fmt, hipStream_t st) {
   if (g.n < 1 || g.n > GROUP_MAX) return hipErrorInvalidValue;
-  if (w_fmt == FMT_BF16) return fused_group_w<FMT_BF16>(g, opt, m_fmt, v_fmt, st);
-  if (w_fmt == FMT_F32) return fused_group_w<FMT_F32>(g, opt, m_fmt, v_fmt, st);
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_gemm(const KArgs& a, int in_fmt, hipStream_t st) {
-  if (in_fmt == FMT_BF16 && a.dma_ok) hipLaunchKernelGGL((k_gemm<FMT_BF16, true>), tile_grid(a), dim3(NT), 0, st, a);
-  else if (in_fmt == FMT_BF16) hipLaunchKernelGGL((k_gemm<FMT_BF16, false>), tile_grid(a), dim3(NT), 0, st, a);
-  else if (in_fmt == FMT_F32) hipLaunchKernelGGL((k_gemm<FMT_F32, false>), tile_grid(a), dim3(NT), 0, st, a);
+  const dim3 grid((unsigned)g.first_tile[g.n]);
+  if (w_fmt == FMT_BF16) hipLaunchKernelGGL((k_fused_group<O, FMT_BF16, M, V>), grid, dim3(NT), 0, st, g);
+  else if (w_fmt == FMT_F32) hipLaunchKernelGGL((k_fused_group<O, FMT_F32, M, V>), grid, dim3(NT), 0, st, g);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
-template <int GF, bool FAST, int WF>
-static hipError_t step_w(const KArgs& a, int opt, int m_fmt, int v_fmt, hipStream_t st) {
-#define X(O, M, V)                                                                        \
-  if (opt == O && m_fmt == M && v_fmt == V) {                                             \
-    hipLaunchKernelGGL((k_step<GF, FAST, O, WF, M, V>), tile_grid(a), dim3(NT), 0, st, a); \
-    return hipGetLastError();                                                             \
-  }
-  FORGE_STATE_LIST(X)
-#undef X
-  return hipErrorInvalidValue;
-}
-
-template <int GF>
-static hipError_t step_g(const KArgs& a, int w_fmt, int opt, int m_fmt, int v_fmt, hipStream_t st) {
+template <int O, int M, int V>
+hipError_t combo_step(const KArgs& a, int w_fmt, hipStream_t st) {
   const bool fast = a.vec_state && (a.K % 4) == 0;
-  if (fast) {
-    if (w_fmt == FMT_BF16) return step_w<GF, true, FMT_BF16>(a, opt, m_fmt, v_fmt, st);
-    if (w_fmt == FMT_F32) return step_w<GF, true, FMT_F32>(a, opt, m_fmt, v_fmt, st);
+  if (w_fmt != FMT_BF16 && w_fmt != FMT_F32) return hipErrorInvalidValue;
+  const bool wbf = w_fmt == FMT_BF16;
+#define FORGE_STEP_LAUNCH(GF, FA)                                                                         \
+  if (wbf) hipLaunchKernelGGL((k_step<GF, FA, O, FMT_BF16, M, V>), tile_grid(a), dim3(NT), 0, st, a);     \
+  else hipLaunchKernelGGL((k_step<GF, FA, O, FMT_F32, M, V>), tile_grid(a), dim3(NT), 0, st, a);
+  if (a.dw_fmt == FMT_F32) {
+    if (fast) { FORGE_STEP_LAUNCH(FMT_F32, true) } else { FORGE_STEP_LAUNCH(FMT_F32, false) }
+  } else if (a.dw_fmt == FMT_BF16) {
+    if (fast) { FORGE_STEP_LAUNCH(FMT_BF16, true) } else { FORGE_STEP_LAUNCH(FMT_BF16, false) }
   } else {
-    if (w_fmt == FMT_BF16) return step_w<GF, false, FMT_BF16>(a, opt, m_fmt, v_fmt, st);
-    if (w_fmt == FMT_F32) return step_w<GF, false, FMT_F32>(a, opt, m_fmt, v_fmt, st);
+    return hipErrorInvalidValue;
   }
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_step(const KArgs& a, int w_fmt, int opt, int m_fmt, int v_fmt, hipStream_t st) {
-  if (a.dw_fmt == FMT_F32) return step_g<FMT_F32>(a, w_fmt, opt, m_fmt, v_fmt, st);
-  if (a.dw_fmt == FMT_BF16) return step_g<FMT_BF16>(a, w_fmt, opt, m_fmt, v_fmt, st);
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_debug_sr(const float* in, uint16_t* out, uint32_t n, uint32_t key, hipStream_t st) {
-  if (n == 0) return hipSuccess;
-  const unsigned blocks = (unsigned)((n + 255u) / 256u);
-  hipLaunchKernelGGL(k_debug_sr, dim3(blocks), dim3(256), 0, st, in, out, n, key);
+#undef FORGE_STEP_LAUNCH
   return hipGetLastError();
 }
+
+// Explicit instantiation of the three launchers of one combination.
+#define FORGE_INSTANTIATE(O, M, V)                                                  \
+  template hipError_t combo_fused<O, M, V>(const KArgs&, int, int, hipStream_t);   \
+  template hipError_t combo_group<O, M, V>(const GroupArgs&, int, hipStream_t);    \
+  template hipError_t combo_step<O, M, V>(const KArgs&, int, hipStream_t);
 
 }  // namespace forge

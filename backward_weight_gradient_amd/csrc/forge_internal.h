@@ -1,5 +1,6 @@
 // Internal interface between the host API (forge_api.cpp) and the gfx950
-// kernels (forge_kernels.hip).  Not part of the public ABI.
+// kernels (forge_device.h, forge_k_*.hip, forge_dispatch.cpp).  Not part of
+// the public ABI.
 #pragma once
 
 #include <cstdint>
@@ -55,19 +56,59 @@ struct GroupArgs {
   int32_t n;
 };
 
-bool combo_supported(int in_fmt, int w_fmt, int opt, int m_fmt, int v_fmt);
-// Whether a layer can run in the grouped kernel (aligned bf16, short token axis).
-bool group_eligible(const KArgs& a, int in_fmt);
+constexpr int WIDE_MIN_BT = 2048;  // token count from which the 256 x 256 kernel is used
 
+// Supported (optimizer, m format, v format) combinations, by family; each
+// family's kernels are instantiated in its own source file.
+#define FORGE_ADAMW_LIST(X)        \
+  X(OPT_ADAMW, FMT_F32, FMT_F32)   \
+  X(OPT_ADAMW, FMT_BF16, FMT_BF16) \
+  X(OPT_ADAMW, FMT_S8, FMT_U8)
+#define FORGE_LION_LIST(X)         \
+  X(OPT_LION, FMT_F32, FMT_NONE)   \
+  X(OPT_LION, FMT_BF16, FMT_NONE)  \
+  X(OPT_LION, FMT_S8, FMT_NONE)
+#define FORGE_SGDM_LIST(X)         \
+  X(OPT_SGDM, FMT_F32, FMT_NONE)   \
+  X(OPT_SGDM, FMT_BF16, FMT_NONE)  \
+  X(OPT_SGDM, FMT_S8, FMT_NONE)
+#define FORGE_STATE_LIST(X) FORGE_ADAMW_LIST(X) FORGE_LION_LIST(X) FORGE_SGDM_LIST(X)
+
+inline bool combo_supported(int in_fmt, int w_fmt, int opt, int m_fmt, int v_fmt) {
+  if (in_fmt != FMT_F32 && in_fmt != FMT_BF16) return false;
+  if (w_fmt != FMT_F32 && w_fmt != FMT_BF16) return false;
+#define X(O, M, V) \
+  if (opt == O && m_fmt == M && v_fmt == V) return true;
+  FORGE_STATE_LIST(X)
+#undef X
+  return false;
+}
+
+// Whether a layer can run in the grouped kernel (aligned bf16, short token axis).
+inline bool group_eligible(const KArgs& a, int in_fmt) {
+  return in_fmt == FMT_BF16 && a.dma_ok && a.vec_state && (a.K % 4) == 0 && a.BT < WIDE_MIN_BT;
+}
+
+// Launchers of one combination (defined in forge_device.h, instantiated by
+// the family sources).  combo_step reads G from a.dW in format a.dw_fmt.
+template <int O, int M, int V>
+hipError_t combo_fused(const KArgs& a, int in_fmt, int w_fmt, hipStream_t st);
+template <int O, int M, int V>
+hipError_t combo_group(const GroupArgs& g, int w_fmt, hipStream_t st);
+template <int O, int M, int V>
+hipError_t combo_step(const KArgs& a, int w_fmt, hipStream_t st);
+
+// Runtime dispatch over the combinations (forge_dispatch.cpp).
 // Fused weight-gradient + step: one workgroup per 128 x 128 tile of W.
 hipError_t launch_fused(const KArgs& a, int in_fmt, int w_fmt, int opt, int m_fmt, int v_fmt,
                         hipStream_t stream);
 // Fused step of g.n group-eligible layers in one launch (bf16 inputs).
 hipError_t launch_fused_group(const GroupArgs& g, int w_fmt, int opt, int m_fmt, int v_fmt, hipStream_t stream);
-// Unfused baseline, phase 1: G tiles -> a.dW (a.dw_fmt).
+// Unfused baseline, phase 1 (forge_k_common.hip): G tiles -> a.dW (a.dw_fmt).
 hipError_t launch_gemm(const KArgs& a, int in_fmt, hipStream_t stream);
 // Unfused baseline, phase 2: the same step, reading G from a.dW.
 hipError_t launch_step(const KArgs& a, int w_fmt, int opt, int m_fmt, int v_fmt, hipStream_t stream);
+// forge_k_common.hip:
 // Stochastic rounding of n floats with one key, element i using flat index i.
 hipError_t launch_debug_sr(const float* in, uint16_t* out, uint32_t n, uint32_t key,
                            hipStream_t stream);

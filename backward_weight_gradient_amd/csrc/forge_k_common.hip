@@ -1,0 +1,28 @@
+// Kernels shared by every optimizer: the unfused baseline's GEMM (G to HBM)
+// and the stochastic-rounding test hook.
+#include "forge_device.h"
+
+namespace forge {
+
+// The device stochastic rounding on its own: element i uses flat index i.
+__global__ void k_debug_sr(const float* __restrict__ in, uint16_t* __restrict__ out, uint32_t n, uint32_t key) {
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = (uint16_t)bf16_sr_bits(in[i], key, i);
+}
+
+hipError_t launch_gemm(const KArgs& a, int in_fmt, hipStream_t st) {
+  if (in_fmt == FMT_BF16 && a.dma_ok) hipLaunchKernelGGL((k_gemm<FMT_BF16, true>), tile_grid(a), dim3(NT), 0, st, a);
+  else if (in_fmt == FMT_BF16) hipLaunchKernelGGL((k_gemm<FMT_BF16, false>), tile_grid(a), dim3(NT), 0, st, a);
+  else if (in_fmt == FMT_F32) hipLaunchKernelGGL((k_gemm<FMT_F32, false>), tile_grid(a), dim3(NT), 0, st, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_sr(const float* in, uint16_t* out, uint32_t n, uint32_t key, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((n + 255u) / 256u);
+  hipLaunchKernelGGL(k_debug_sr, dim3(blocks), dim3(256), 0, st, in, out, n, key);
+  return hipGetLastError();
+}
+
+}  // namespace forge

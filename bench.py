@@ -41,7 +41,7 @@ BT = 512
 STEP_T = 10
 SEED = 1337
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_wgrad_llama8b_bt512_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "backward_weight_gradient_amd", "csrc", "forge_kernels.hip")
+KERNEL_DIR = os.path.join(ROOT, "backward_weight_gradient_amd", "csrc")
 
 
 def parse():
@@ -91,8 +91,13 @@ def layer_bytes(N, K, bt):
 
 
 def kernel_sha():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """sha256 over the device sources (the kernels and their launchers)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(KERNEL_DIR)):
+        if name.endswith((".h", ".hip")):
+            with open(os.path.join(KERNEL_DIR, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
 
 
 def load_traffic(grouping):
