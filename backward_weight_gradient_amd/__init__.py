@@ -32,9 +32,13 @@ STATUS_NAMES = ["FORGE_OK", "FORGE_E_NULL", "FORGE_E_SHAPE", "FORGE_E_DTYPE", "F
  FORGE_E_ALIAS, FORGE_E_UNSUPPORTED, FORGE_E_HIP) = range(1, 10)
 
 FORGE_F32, FORGE_BF16, FORGE_S8, FORGE_U8 = 0, 1, 2, 3
-FORGE_ADAMW, FORGE_LION, FORGE_SGDM = 0, 1, 2
+FORGE_ADAMW, FORGE_LION, FORGE_SGDM, FORGE_NADAM, FORGE_RADAM, FORGE_RMSPROP, FORGE_ADAGRAD, FORGE_SGD = range(8)
 FORGE_ROUND_RNE, FORGE_ROUND_SR = 0, 1
-OPTIMIZERS = {"adamw": FORGE_ADAMW, "lion": FORGE_LION, "sgdm": FORGE_SGDM}
+OPTIMIZERS = {"adamw": FORGE_ADAMW, "lion": FORGE_LION, "sgdm": FORGE_SGDM, "nadam": FORGE_NADAM,
+              "radam": FORGE_RADAM, "rmsprop": FORGE_RMSPROP, "adagrad": FORGE_ADAGRAD, "sgd": FORGE_SGD}
+# which states each optimizer keeps (m: first moment / momentum, v: second moment)
+KEEPS_M = {"adamw", "lion", "sgdm", "nadam", "radam"}
+KEEPS_V = {"adamw", "nadam", "radam", "rmsprop", "adagrad"}
 ROUNDING = {"rne": FORGE_ROUND_RNE, "sr": FORGE_ROUND_SR}
 
 
@@ -135,8 +139,14 @@ def state(t, scale=None, block: int = 0) -> forge_state:
                        block if scale is not None else 0)
 
 
-def hyper(opt: str = "adamw", lr: float = 1e-3, beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
-          weight_decay: float = 0.01, round: str = "sr") -> forge_hyper:
+def hyper(opt: str = "adamw", lr: float = 1e-3, beta1: float = 0.9, beta2: Optional[float] = None,
+          eps: Optional[float] = None, weight_decay: float = 0.01, round: str = "sr") -> forge_hyper:
+    """Hyper-parameters; beta2 defaults to 0.99 for RMSprop (its smoothing constant) and 0.999
+    otherwise, eps to 1e-10 for AdaGrad and 1e-8 otherwise."""
+    if beta2 is None:
+        beta2 = 0.99 if opt == "rmsprop" else 0.999
+    if eps is None:
+        eps = 1e-10 if opt == "adagrad" else 1e-8
     return forge_hyper(OPTIMIZERS[opt], ROUNDING[round], lr, beta1, beta2, eps, weight_decay)
 
 

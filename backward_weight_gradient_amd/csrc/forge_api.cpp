@@ -124,9 +124,10 @@ forge_status check_state(const forge_state& s, int64_t N, int64_t K, bool first,
 void layer_ranges(const forge_mat* X, const forge_mat* dY, const forge_mat* W, const forge_state* m,
                   const forge_state* v, const Plan& pl, Range (&outs)[5], Range (&ins)[2]) {
   outs[0] = mat_range(*W);
-  outs[1] = mat_range(m->q);
+  outs[1] = m ? mat_range(m->q) : Range();
   outs[2] = v ? mat_range(v->q) : Range();
-  outs[3] = raw_range(m->scale, m->scale ? (uint64_t)pl.N * (uint64_t)(pl.K / (m->block ? m->block : 1)) * 4 : 0);
+  outs[3] = (m && m->scale) ? raw_range(m->scale, (uint64_t)pl.N * (uint64_t)(pl.K / (m->block ? m->block : 1)) * 4)
+                            : Range();
   outs[4] = (v && v->scale) ? raw_range(v->scale, (uint64_t)pl.N * (uint64_t)(pl.K / (v->block ? v->block : 1)) * 4)
                             : Range();
   ins[0] = mat_range(*X);
@@ -137,19 +138,24 @@ forge_status validate(const forge_mat* X, const forge_mat* dY, const forge_mat* 
                       const forge_state* v, const forge_hyper* h, int64_t step, Plan& pl) {
   if (!X || !dY || !W || !h) return FORGE_E_NULL;
   // optimizer and which states it keeps
-  if (h->opt != FORGE_ADAMW && h->opt != FORGE_LION && h->opt != FORGE_SGDM) return FORGE_E_HYPER;
+  const int o = h->opt;
+  if (o < FORGE_ADAMW || o > FORGE_SGD) return FORGE_E_HYPER;
   if (h->round != FORGE_ROUND_RNE && h->round != FORGE_ROUND_SR) return FORGE_E_HYPER;
-  if (!m) return FORGE_E_NULL;
-  if (h->opt == FORGE_ADAMW && !v) return FORGE_E_NULL;
-  if (h->opt != FORGE_ADAMW && v) return FORGE_E_UNSUPPORTED;
+  if (opt_has_m(o) && !m) return FORGE_E_NULL;
+  if (opt_has_v(o) && !v) return FORGE_E_NULL;
+  if ((!opt_has_m(o) && m) || (!opt_has_v(o) && v)) return FORGE_E_UNSUPPORTED;
   if (step < 1) return FORGE_E_STEP;
-  // hyper-parameters
+  // hyper-parameters: all finite; the ones the optimizer uses in range
   if (!finite(h->lr) || !finite(h->beta1) || !finite(h->beta2) || !finite(h->eps) || !finite(h->weight_decay))
     return FORGE_E_HYPER;
   if (h->lr < 0 || h->weight_decay < 0) return FORGE_E_HYPER;
-  if (h->beta1 < 0 || h->beta1 >= 1) return FORGE_E_HYPER;
-  if (h->opt != FORGE_SGDM && (h->beta2 < 0 || h->beta2 >= 1)) return FORGE_E_HYPER;
-  if (h->opt == FORGE_ADAMW && !(h->eps > 0)) return FORGE_E_HYPER;
+  const bool adam_like = o == FORGE_ADAMW || o == FORGE_NADAM || o == FORGE_RADAM;
+  const bool uses_b1 = adam_like || o == FORGE_LION || o == FORGE_SGDM;
+  const bool uses_b2 = adam_like || o == FORGE_LION || o == FORGE_RMSPROP;
+  const bool uses_eps = adam_like || o == FORGE_RMSPROP || o == FORGE_ADAGRAD;
+  if (uses_b1 && (h->beta1 < 0 || h->beta1 >= 1)) return FORGE_E_HYPER;
+  if (uses_b2 && (h->beta2 < 0 || h->beta2 >= 1)) return FORGE_E_HYPER;
+  if (uses_eps && !(h->eps > 0)) return FORGE_E_HYPER;
   // shapes
   pl.BT = X->rows;
   pl.K = X->cols;
@@ -163,7 +169,7 @@ forge_status validate(const forge_mat* X, const forge_mat* dY, const forge_mat* 
   if (X->dtype != dY->dtype) return FORGE_E_DTYPE;
   if (X->dtype != FORGE_F32 && X->dtype != FORGE_BF16) return FORGE_E_DTYPE;
   if (W->dtype != FORGE_F32 && W->dtype != FORGE_BF16) return FORGE_E_DTYPE;
-  if ((st = check_state(*m, pl.N, pl.K, true, pl)) != FORGE_OK) return st;
+  if (m && (st = check_state(*m, pl.N, pl.K, true, pl)) != FORGE_OK) return st;
   if (v && (st = check_state(*v, pl.N, pl.K, false, pl)) != FORGE_OK) return st;
   // size limits: 32-bit flat SR index and 32-bit tile / token counters
   if ((uint64_t)pl.N * (uint64_t)pl.K >= (1ull << 32)) return FORGE_E_SHAPE;
@@ -181,7 +187,7 @@ forge_status validate(const forge_mat* X, const forge_mat* dY, const forge_mat* 
   }
   pl.in_fmt = X->dtype;
   pl.w_fmt = W->dtype;
-  pl.m_fmt = m->q.dtype;
+  pl.m_fmt = m ? m->q.dtype : FMT_NONE;
   pl.v_fmt = v ? v->q.dtype : FMT_NONE;
   if (!combo_supported(pl.in_fmt, pl.w_fmt, h->opt, pl.m_fmt, pl.v_fmt)) return FORGE_E_UNSUPPORTED;
   pl.empty = (pl.N == 0 || pl.K == 0);
@@ -199,7 +205,7 @@ KArgs make_args(const forge_mat* X, const forge_mat* dY, forge_mat* W, forge_sta
   a.X = X->data; a.ldx = X->ld;
   a.dY = dY->data; a.lddy = dY->ld;
   a.W = W->data; a.ldw = W->ld;
-  a.m = m->q.data; a.ldm = m->q.ld; a.ms = m->scale;
+  if (m) { a.m = m->q.data; a.ldm = m->q.ld; a.ms = m->scale; }
   if (v) { a.v = v->q.data; a.ldv = v->q.ld; a.vs = v->scale; }
   a.BT = (int32_t)pl.BT; a.N = (int32_t)pl.N; a.K = (int32_t)pl.K;
   a.tiles_n = (int32_t)((pl.N + 127) / 128);
@@ -215,7 +221,8 @@ KArgs make_args(const forge_mat* X, const forge_mat* dY, forge_mat* W, forge_sta
               (uint64_t)pl.BT * (uint64_t)dY->ld * 2 < (1ull << 31) &&
               (uint64_t)pl.BT * (uint64_t)X->ld * 2 < (1ull << 31)) ? 1 : 0;
   // 4-element state accesses (16 B fp32, 8 B bf16, 4 B int8)
-  bool vs = vec_ok(W->data, W->ld, 4, elem_size(pl.w_fmt)) && vec_ok(m->q.data, m->q.ld, 4, elem_size(pl.m_fmt));
+  bool vs = vec_ok(W->data, W->ld, 4, elem_size(pl.w_fmt));
+  if (m) vs = vs && vec_ok(m->q.data, m->q.ld, 4, elem_size(pl.m_fmt));
   if (v) vs = vs && vec_ok(v->q.data, v->q.ld, 4, elem_size(pl.v_fmt));
   a.vec_state = vs ? 1 : 0;
   // scalars, in double, rounded once
@@ -230,9 +237,34 @@ KArgs make_args(const forge_mat* X, const forge_mat* dY, forge_mat* W, forge_sta
   c.decay = (float)(1.0 - lr * wd);
   c.wd = (float)wd;
   const double t = (double)step;
-  c.bc1 = (float)(1.0 / (1.0 - std::pow(b1, t)));
-  c.bc2s = (h->opt == FORGE_ADAMW) ? (float)(1.0 / std::sqrt(1.0 - std::pow(b2, t))) : 1.0f;
-  if (h->opt != FORGE_ADAMW) c.bc1 = 1.0f;
+  const int o = h->opt;
+  const bool adam_like = o == FORGE_ADAMW || o == FORGE_NADAM || o == FORGE_RADAM;
+  c.bc1 = adam_like ? (float)(1.0 / (1.0 - std::pow(b1, t))) : 1.0f;
+  c.bc2s = (o == FORGE_ADAMW || o == FORGE_NADAM) ? (float)(1.0 / std::sqrt(1.0 - std::pow(b2, t))) : 1.0f;
+  if (o == FORGE_NADAM) {
+    // momentum schedule mu_i = b1 (1 - 0.5 * 0.96^(psi i)), psi = 0.004, and
+    // its running product over i = 1..t (+1), in double in increasing i;
+    // once the product is below 2^-60, 1 - product is 1 in double and the
+    // remaining factors cannot change it
+    const double psi = 0.004;
+    auto mu = [&](double i) { return b1 * (1.0 - 0.5 * std::pow(0.96, i * psi)); };
+    double prod = 1.0;
+    for (int64_t i = 1; i <= step && prod >= 0x1p-60; ++i) prod *= mu((double)i);
+    if (prod < 0x1p-60) prod = 0.0;
+    const double mu_t = mu(t), mu_next = mu(t + 1.0);
+    c.na1 = (float)(mu_next / (1.0 - prod * mu_next));
+    c.na2 = (float)((1.0 - mu_t) / (1.0 - prod));
+  }
+  if (o == FORGE_RADAM) {
+    const double b2t = std::pow(b2, t);
+    const double rho_inf = 2.0 / (1.0 - b2) - 1.0;
+    const double rho_t = rho_inf - 2.0 * t * b2t / (1.0 - b2t);
+    c.rect = rho_t > 5.0 ? 1 : 0;
+    if (c.rect) {
+      const double r = std::sqrt((rho_t - 4.0) * (rho_t - 2.0) * rho_inf / ((rho_inf - 4.0) * (rho_inf - 2.0) * rho_t));
+      c.rc = (float)(r * std::sqrt(1.0 - b2t) / (1.0 - std::pow(b1, t)));
+    }
+  }
   c.keyW = sr_key(seed, (uint64_t)step, 0);
   c.keyM = sr_key(seed, (uint64_t)step, 1);
   c.keyV = sr_key(seed, (uint64_t)step, 2);
@@ -342,11 +374,11 @@ forge_status forge_wgrad_unfused(const forge_mat* X, const forge_mat* dY, forge_
   if (dW == nullptr) return FORGE_E_NULL;
   if (!aligned(dW, 16)) return FORGE_E_ALIGN;
   const Range ws = raw_range(dW, (uint64_t)pl.N * (uint64_t)pl.K * (uint64_t)elem_size(dW_dtype));
-  const Range others[7] = {
-      mat_range(*X), mat_range(*dY), mat_range(*W), mat_range(m->q), v ? mat_range(v->q) : Range(),
-      raw_range(m->scale, m->scale ? (uint64_t)pl.N * (uint64_t)(pl.K / pl.block) * 4 : 0),
-      (v && v->scale) ? raw_range(v->scale, (uint64_t)pl.N * (uint64_t)(pl.K / pl.block) * 4) : Range()};
-  for (const Range& r : others)
+  Range outs[5], ins[2];
+  layer_ranges(X, dY, W, m, v, pl, outs, ins);
+  for (const Range& r : outs)
+    if (overlap(ws, r)) return FORGE_E_ALIAS;
+  for (const Range& r : ins)
     if (overlap(ws, r)) return FORGE_E_ALIAS;
   KArgs a = make_args(X, dY, W, m, v, h, step, seed, pl);
   a.dW = dW;

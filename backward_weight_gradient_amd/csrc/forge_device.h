@@ -929,21 +929,21 @@ __device__ __forceinline__ void quantize_chunk(const float (&x)[8], int block, c
 
 template <int OPT, int WF, int MF, int VF, bool FAST>
 struct Step {
-  static constexpr bool HAS_V = (OPT == OPT_ADAMW);
+  static constexpr bool HAS_M = opt_has_m(OPT);
+  static constexpr bool HAS_V = opt_has_v(OPT);
+  static constexpr int MFMT = HAS_M ? MF : FMT_NONE;
   static constexpr int VFMT = HAS_V ? VF : FMT_NONE;
 
   // Everything one chunk reads, still undecoded.
   struct Pending {
     Raw4<WF> w[2];
-    Raw4<MF> m[2];
+    Raw4<MFMT> m[2];
     Raw4<VFMT> v[2];
   };
 
   __device__ __forceinline__ static void load(const KArgs& a, int p, const Seg (&sg)[2], Pending& r) {
     const bool vec = a.vec_state != 0;
     const char* rw = static_cast<const char*>(a.W) + (int64_t)p * a.ldw * (WF == FMT_F32 ? 4 : 2);
-    const char* rm = static_cast<const char*>(a.m) + (int64_t)p * a.ldm * (MF == FMT_F32 ? 4 : MF == FMT_BF16 ? 2 : 1);
-    const char* rv = static_cast<const char*>(a.v) + (int64_t)p * a.ldv * (VF == FMT_F32 ? 4 : VF == FMT_BF16 ? 2 : 1);
     const int64_t srow = (int64_t)p * (a.K / a.block);
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
@@ -952,16 +952,21 @@ struct Step {
         continue;
       }
       ld4<WF, FAST>(r.w[g], rw, sg[g], vec);
-      ld4<MF, FAST>(r.m[g], rm, sg[g], vec);
-      if constexpr (MF == FMT_S8) r.m[g].s = a.ms[srow + sg[g].q / a.block];
+      if constexpr (HAS_M) {
+        const char* rm = static_cast<const char*>(a.m) + (int64_t)p * a.ldm * (MF == FMT_F32 ? 4 : MF == FMT_BF16 ? 2 : 1);
+        ld4<MF, FAST>(r.m[g], rm, sg[g], vec);
+        if constexpr (MF == FMT_S8) r.m[g].s = a.ms[srow + sg[g].q / a.block];
+      }
       if constexpr (HAS_V) {
+        const char* rv = static_cast<const char*>(a.v) + (int64_t)p * a.ldv * (VF == FMT_F32 ? 4 : VF == FMT_BF16 ? 2 : 1);
         ld4<VF, FAST>(r.v[g], rv, sg[g], vec);
         if constexpr (VF == FMT_U8) r.v[g].s = a.vs[srow + sg[g].q / a.block];
       }
     }
   }
 
-  // The optimizer on one element, fp32 (Algorithm 1 Phase 2 for AdamW).
+  // The optimizer on one element, fp32 (Algorithm 1 Phase 2 for AdamW; the
+  // other families of the paper's Appendix N list replace this body only).
   // sqrt and the reciprocal are the hardware instructions (<= 1 ulp).
   __device__ __forceinline__ static void phi(const EpiConst& k, float g, float& w, float& m, float& v) {
     if constexpr (OPT == OPT_ADAMW) {
@@ -970,11 +975,35 @@ struct Step {
       const float den = fmaf(__builtin_amdgcn_sqrtf(v), k.bc2s, k.eps);  // sqrt(v'/(1-b2^t)) + eps
       const float upd = (m * k.bc1) * __builtin_amdgcn_rcpf(den);        // m_hat / den
       w = fmaf(k.decay, w, -k.lr * upd);                                 // (1 - lr wd) W - lr upd
+    } else if constexpr (OPT == OPT_NADAM) {
+      m = fmaf(k.b1, m, k.omb1 * g);
+      v = fmaf(k.b2, v, k.omb2 * (g * g));
+      const float den = fmaf(__builtin_amdgcn_sqrtf(v), k.bc2s, k.eps);  // sqrt(v'/(1-b2^t)) + eps
+      const float num = fmaf(k.na1, m, k.na2 * g);                       // Nesterov-corrected m_hat
+      w = fmaf(k.decay, w, -k.lr * (num * __builtin_amdgcn_rcpf(den)));
+    } else if constexpr (OPT == OPT_RADAM) {
+      m = fmaf(k.b1, m, k.omb1 * g);
+      v = fmaf(k.b2, v, k.omb2 * (g * g));
+      const float den = __builtin_amdgcn_sqrtf(v) + k.eps;               // sqrt(v') + eps
+      const float upd = k.rect ? (m * k.rc) * __builtin_amdgcn_rcpf(den) : m * k.bc1;
+      w = fmaf(k.decay, w, -k.lr * upd);
     } else if constexpr (OPT == OPT_LION) {
       const float c = fmaf(k.b1, m, k.omb1 * g);                         // interpolation
       const float s = c > 0.f ? 1.f : (c < 0.f ? -1.f : 0.f);
       w = fmaf(k.decay, w, -k.lr * s);
       m = fmaf(k.b2, m, k.omb2 * g);
+    } else if constexpr (OPT == OPT_RMSPROP) {
+      const float gg = fmaf(k.wd, w, g);                                 // coupled L2
+      v = fmaf(k.b2, v, k.omb2 * (gg * gg));                             // a v + (1-a) g^2
+      const float den = __builtin_amdgcn_sqrtf(v) + k.eps;
+      w = fmaf(-k.lr, gg * __builtin_amdgcn_rcpf(den), w);
+    } else if constexpr (OPT == OPT_ADAGRAD) {
+      const float gg = fmaf(k.wd, w, g);                                 // coupled L2
+      v = fmaf(gg, gg, v);                                               // v + g^2
+      const float den = __builtin_amdgcn_sqrtf(v) + k.eps;
+      w = fmaf(-k.lr, gg * __builtin_amdgcn_rcpf(den), w);
+    } else if constexpr (OPT == OPT_SGD) {
+      w = fmaf(-k.lr, fmaf(k.wd, w, g), w);                              // W - lr (G + wd W)
     } else {                                                             // SGD with momentum
       const float gg = fmaf(k.wd, w, g);                                 // coupled L2
       m = fmaf(k.b1, m, gg);                                             // b' = mu b + g
@@ -990,26 +1019,28 @@ struct Step {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       dec4<WF>(r.w[s], w + 4 * s);
-      dec4<MF>(r.m[s], m + 4 * s);
+      dec4<MFMT>(r.m[s], m + 4 * s);
       dec4<VFMT>(r.v[s], v + 4 * s);
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) phi(a.c, g[i], w[i], m[i], v[i]);
     const bool vec = a.vec_state != 0;
     char* rw = static_cast<char*>(a.W) + (int64_t)p * a.ldw * (WF == FMT_F32 ? 4 : 2);
-    char* rm = static_cast<char*>(a.m) + (int64_t)p * a.ldm * (MF == FMT_F32 ? 4 : MF == FMT_BF16 ? 2 : 1);
-    char* rv = static_cast<char*>(a.v) + (int64_t)p * a.ldv * (VF == FMT_F32 ? 4 : VF == FMT_BF16 ? 2 : 1);
+    char* rm = nullptr;
+    char* rv = nullptr;
+    if constexpr (HAS_M) rm = static_cast<char*>(a.m) + (int64_t)p * a.ldm * (MF == FMT_F32 ? 4 : MF == FMT_BF16 ? 2 : 1);
+    if constexpr (HAS_V) rv = static_cast<char*>(a.v) + (int64_t)p * a.ldv * (VF == FMT_F32 ? 4 : VF == FMT_BF16 ? 2 : 1);
     const uint32_t rowbase = (uint32_t)p * (uint32_t)a.K;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       if (!sg[s].ok) continue;
       const uint32_t idx_mul = (rowbase + (uint32_t)sg[s].q) * GOLDEN;
       st4<WF, FAST>(rw, sg[s], vec, w + 4 * s, a.c.sr, a.c.keyW, idx_mul);
-      if constexpr (MF != FMT_S8) st4<MF, FAST>(rm, sg[s], vec, m + 4 * s, a.c.sr, a.c.keyM, idx_mul);
+      if constexpr (HAS_M && MF != FMT_S8) st4<MF, FAST>(rm, sg[s], vec, m + 4 * s, a.c.sr, a.c.keyM, idx_mul);
       if constexpr (HAS_V && VF != FMT_U8) st4<VF, FAST>(rv, sg[s], vec, v + 4 * s, a.c.sr, a.c.keyV, idx_mul);
     }
     const int64_t srow = (int64_t)p * (a.K / a.block);
-    if constexpr (MF == FMT_S8) quantize_chunk<true>(m, a.block, sg, rm, vec, a.ms + srow);
+    if constexpr (HAS_M && MF == FMT_S8) quantize_chunk<true>(m, a.block, sg, rm, vec, a.ms + srow);
     if constexpr (HAS_V && VF == FMT_U8) quantize_chunk<false>(v, a.block, sg, rv, vec, a.vs + srow);
   }
 };

@@ -9,7 +9,19 @@
 namespace forge {
 
 enum Fmt : int { FMT_NONE = -1, FMT_F32 = 0, FMT_BF16 = 1, FMT_S8 = 2, FMT_U8 = 3 };
-enum Opt : int { OPT_ADAMW = 0, OPT_LION = 1, OPT_SGDM = 2 };
+enum Opt : int {
+  OPT_ADAMW = 0, OPT_LION = 1, OPT_SGDM = 2, OPT_NADAM = 3, OPT_RADAM = 4, OPT_RMSPROP = 5, OPT_ADAGRAD = 6,
+  OPT_SGD = 7
+};
+
+// Which states an optimizer keeps: m (first moment / momentum) and v
+// (second moment / squared-gradient sum).
+constexpr bool opt_has_m(int o) {
+  return o == OPT_ADAMW || o == OPT_LION || o == OPT_SGDM || o == OPT_NADAM || o == OPT_RADAM;
+}
+constexpr bool opt_has_v(int o) {
+  return o == OPT_ADAMW || o == OPT_NADAM || o == OPT_RADAM || o == OPT_RMSPROP || o == OPT_ADAGRAD;
+}
 
 // Scalars of the element-wise step, computed once per call on the host in
 // double precision and rounded once to fp32.
@@ -23,6 +35,10 @@ struct EpiConst {
   float wd;        // lambda             (L2 decay: SGD-m)
   float bc1;       // 1 / (1 - beta1^t)
   float bc2s;      // 1 / sqrt(1 - beta2^t)
+  float na1;       // NAdam: mu_{t+1} / (1 - prod_{i<=t+1} mu_i)   (weight of m')
+  float na2;       // NAdam: (1 - mu_t) / (1 - prod_{i<=t} mu_i)   (weight of G)
+  float rc;        // RAdam, rectified: r_t sqrt(1 - beta2^t) / (1 - beta1^t)
+  int32_t rect;    // RAdam: 1 once rho_t > 5 (adaptive step), else 0 (momentum step)
   uint32_t keyW, keyM, keyV;  // stochastic-rounding keys of the three tensors
   int32_t sr;      // 1: stochastic rounding of bf16 stores, 0: round to nearest even
 };
@@ -72,7 +88,19 @@ constexpr int WIDE_MIN_BT = 2048;  // token count from which the 256 x 256 kerne
   X(OPT_SGDM, FMT_F32, FMT_NONE)   \
   X(OPT_SGDM, FMT_BF16, FMT_NONE)  \
   X(OPT_SGDM, FMT_S8, FMT_NONE)
-#define FORGE_STATE_LIST(X) FORGE_ADAMW_LIST(X) FORGE_LION_LIST(X) FORGE_SGDM_LIST(X)
+#define FORGE_ADAM_VARIANT_LIST(X)  \
+  X(OPT_NADAM, FMT_F32, FMT_F32)    \
+  X(OPT_NADAM, FMT_BF16, FMT_BF16)  \
+  X(OPT_RADAM, FMT_F32, FMT_F32)    \
+  X(OPT_RADAM, FMT_BF16, FMT_BF16)
+#define FORGE_SECOND_MOMENT_LIST(X)    \
+  X(OPT_RMSPROP, FMT_NONE, FMT_F32)    \
+  X(OPT_RMSPROP, FMT_NONE, FMT_BF16)   \
+  X(OPT_ADAGRAD, FMT_NONE, FMT_F32)    \
+  X(OPT_ADAGRAD, FMT_NONE, FMT_BF16)   \
+  X(OPT_SGD, FMT_NONE, FMT_NONE)
+#define FORGE_STATE_LIST(X) \
+  FORGE_ADAMW_LIST(X) FORGE_LION_LIST(X) FORGE_SGDM_LIST(X) FORGE_ADAM_VARIANT_LIST(X) FORGE_SECOND_MOMENT_LIST(X)
 
 inline bool combo_supported(int in_fmt, int w_fmt, int opt, int m_fmt, int v_fmt) {
   if (in_fmt != FMT_F32 && in_fmt != FMT_BF16) return false;

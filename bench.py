@@ -56,6 +56,8 @@ def parse():
                    help="subblock: one launch per sub-block, [gate, up, down] and [q, k, v, o]; ready: as the "
                         "gradients become available, [down] [gate, up] [o] [q, k, v]; layer: one "
                         "forge_wgrad_step launch per layer")
+    p.add_argument("--no-family-sweep", action="store_true",
+                   help="skip the per-optimizer timing (gate_proj, BT 512, all eight families)")
     p.add_argument("--no-mfma-sweep", action="store_true",
                    help="skip the compute-bound sweep (down_proj, lm_head at BT 2048 / 8192)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -144,6 +146,46 @@ def mfma_sweep(F, synth, h, reps=3):
                                      "hbm_gbs_alg": round(layer_bytes(N, K, bt) / (ms * 1e-3) / 1e9, 1)}
             del X, dY, st, args
             torch.cuda.empty_cache()
+    return out
+
+
+def family_sweep(F, synth, reps=5):
+    """Each of the eight optimizer families on gate_proj [14336, 4096] at
+    BT = 512 (bf16 X / dY / W with SR, fp32 states where the family keeps
+    them; median of `reps` launches).  Algorithmic bytes: W read + written
+    (4 B), each fp32 state read + written (8 B), X and dY read once."""
+    import torch
+    N, K = 14336, 4096
+    stream = torch.cuda.current_stream()
+    X, dY = synth.activations(1, BT, N, K, STEP_T, device="cuda", extra=40)
+    out = {}
+    for opt in ("adamw", "nadam", "radam", "lion", "sgdm", "rmsprop", "adagrad", "sgd"):
+        spec = synth.LayerSpec(in_dtype="bf16", w_fmt="bf16", m_fmt="f32" if opt in F.KEEPS_M else None,
+                               v_fmt="f32" if opt in F.KEEPS_V else None)
+        st = synth.state(1, N, K, spec, device="cuda", extra=40)
+        m = F.state(st["m"]) if st["m"] is not None else None
+        v = F.state(st["v"]) if st["v"] is not None else None
+        args = (F.mat(X), F.mat(dY), F.mat(st["W"]), m, v)
+        h = F.hyper(opt, lr=1e-4 if opt == "lion" else 1e-3, beta2=0.99 if opt == "lion" else None)
+        F.forge_wgrad_step(*args, h, STEP_T, SEED, stream=stream.cuda_stream)
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            F.forge_wgrad_step(*args, h, STEP_T, SEED, stream=stream.cuda_stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        ms = sorted(times)[len(times) // 2]
+        bpp = 4 + 8 * (opt in F.KEEPS_M) + 8 * (opt in F.KEEPS_V)
+        nbytes = bpp * N * K + 2 * BT * (N + K) * 2
+        out[opt] = {"us": round(1e3 * ms, 1), "state_bytes_per_param": bpp,
+                    "hbm_gbs_alg": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                    "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del st, args, m, v
+    del X, dY
+    torch.cuda.empty_cache()
     return out
 
 
@@ -318,6 +360,8 @@ def main():
         del dws
         torch.cuda.empty_cache()
 
+    if not args.no_family_sweep:
+        extras["optimizer_families_gate_proj_bt512"] = family_sweep(F, synth)
     if not args.no_mfma_sweep:
         extras["compute_bound_sweep"] = mfma_sweep(F, synth, h)
 

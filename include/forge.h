@@ -61,12 +61,27 @@ typedef enum {
 
 typedef enum { FORGE_F32 = 0, FORGE_BF16 = 1, FORGE_S8 = 2, FORGE_U8 = 3 } forge_dtype;
 
-/* Optimizers (paper, Appendix N, "fully fused" families). */
+/* Optimizers: the eight element-wise families the paper fuses in full
+ * (Appendix N, "Fully fused").  Where the pages name a family without its
+ * formula, the library follows the textbook rule as PyTorch implements it
+ * (the pages verify every family against a PyTorch reference, Appendix N,
+ * "Numerical verification"); "decoupled" decay is W <- (1 - lr wd) W before
+ * the update, "coupled" (L2) decay adds wd W to the gradient. */
 typedef enum {
-  FORGE_ADAMW = 0, /* Algorithm 1 Phase 2: bias correction, decoupled decay; needs m and v */
-  FORGE_LION = 1,  /* sign of the interpolated momentum (Chen et al. 2023); needs m only   */
-  FORGE_SGDM = 2   /* SGD with momentum, PyTorch semantics (coupled L2 decay, dampening 0,
-                      no Nesterov), momentum = beta1; needs m (the momentum buffer) only   */
+  FORGE_ADAMW = 0,   /* Algorithm 1 Phase 2: bias correction, decoupled decay; m and v      */
+  FORGE_LION = 1,    /* sign of the interpolated momentum (Chen et al. 2023); m only        */
+  FORGE_SGDM = 2,    /* SGD with momentum: coupled decay, dampening 0, no Nesterov,
+                        momentum = beta1; m (the momentum buffer) only                      */
+  FORGE_NADAM = 3,   /* AdamW with the Nesterov-corrected first moment (Dozat 2016; momentum
+                        schedule mu_t = beta1 (1 - 0.5 * 0.96^(0.004 t))), decoupled decay;
+                        m and v                                                             */
+  FORGE_RADAM = 4,   /* AdamW with the rectified variance term (Liu et al. 2019: the adaptive
+                        step only once rho_t > 5), decoupled decay; m and v                 */
+  FORGE_RMSPROP = 5, /* second moment only: v <- a v + (1 - a) g^2 with a = beta2, coupled
+                        decay, no momentum, not centred; v only (m NULL)                    */
+  FORGE_ADAGRAD = 6, /* cumulative squared gradient v <- v + g^2 (no decay of v, learning-
+                        rate decay 0), coupled decay; v only (m NULL)                       */
+  FORGE_SGD = 7      /* vanilla gradient descent with coupled decay; no state (m, v NULL)   */
 } forge_optim;
 
 /* Rounding of every bf16 store (paper, Appendix C). */
@@ -101,11 +116,12 @@ typedef struct {
 typedef struct {
   int32_t opt;    /* forge_optim */
   int32_t round;  /* forge_round */
-  double lr;           /* eta                                         */
-  double beta1;        /* AdamW / Lion beta1; SGD-m momentum          */
-  double beta2;        /* AdamW / Lion beta2; ignored by SGD-m        */
-  double eps;          /* AdamW only                                  */
-  double weight_decay; /* lambda: decoupled (AdamW, Lion), L2 (SGD-m) */
+  double lr;           /* eta                                                        */
+  double beta1;        /* AdamW / NAdam / RAdam / Lion beta1; SGD-m momentum         */
+  double beta2;        /* AdamW / NAdam / RAdam / Lion beta2; RMSprop smoothing a     */
+  double eps;          /* AdamW, NAdam, RAdam, RMSprop, AdaGrad                       */
+  double weight_decay; /* lambda: decoupled (AdamW, NAdam, RAdam, Lion), coupled L2
+                          (SGD-m, RMSprop, AdaGrad, SGD)                             */
 } forge_hyper;
 
 /*
@@ -113,15 +129,21 @@ typedef struct {
  *
  * X  : [BT, K], dtype BF16 or F32.      dY : [BT, N], same dtype as X.
  * W  : [N, K], BF16 or F32, updated in place.
- * m  : [N, K] state, F32 / BF16 / S8.    v : [N, K] state, F32 / BF16 / U8,
- *      AdamW only (must be NULL for Lion and SGD-m).
+ * m  : [N, K] first state, F32 / BF16 / S8: AdamW, NAdam, RAdam, Lion, SGD-m
+ *      (NULL for RMSprop, AdaGrad, SGD).
+ * v  : [N, K] second state, F32 / BF16 / U8: AdamW, NAdam, RAdam, RMSprop,
+ *      AdaGrad (NULL for Lion, SGD-m, SGD).
  * h  : optimizer and hyper-parameters.  step: the 1-based global step t,
  *      used by the AdamW bias correction 1/(1 - beta^t) and by the SR key.
  * seed: 64-bit stochastic-rounding seed.
  *
  * Supported combinations: X/dY in {BF16, F32} x W in {BF16, F32} x
- *   AdamW (m, v) in {(F32, F32), (BF16, BF16), (S8, U8)} or
- *   Lion / SGD-m m in {F32, BF16, S8}.
+ *   AdamW (m, v) in {(F32, F32), (BF16, BF16), (S8, U8)},
+ *   NAdam / RAdam (m, v) in {(F32, F32), (BF16, BF16)},
+ *   Lion / SGD-m m in {F32, BF16, S8},
+ *   RMSprop / AdaGrad v in {F32, BF16}, or SGD (no state).
+ *   A missing required state is E_NULL, a state the optimizer does not keep
+ *   is E_UNSUPPORTED.
  * Int8 states need K % block == 0.  N * K must be < 2^32 (flat SR index).
  * BT may be 0 (G = 0: the step still applies decay / momentum).
  * N == 0 or K == 0 is a no-op.

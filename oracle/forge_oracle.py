@@ -34,6 +34,18 @@ design notes):
   check is against "a reference PyTorch implementation", Appendix N):
   coupled L2 decay ``g = G + wd*W``, ``b <- mu*b + g`` (dampening 0, no
   Nesterov), ``W <- W - lr*b``; ``mu`` is passed as ``beta1``.
+* NAdam, RAdam, RMSprop, AdaGrad and plain SGD: the pages name each family
+  in one line (Appendix N, "fully fused") and verify it against a PyTorch
+  reference, so each follows its textbook rule as PyTorch states it.  NAdam
+  ("AdamW with Nesterov momentum correction on m_hat", Dozat 2016) uses the
+  momentum schedule ``mu_i = b1 (1 - 0.5 * 0.96^(0.004 i))`` and its running
+  product; RAdam ("AdamW with rectified-variance term", Liu et al. 2019)
+  takes the adaptive step only once ``rho_t > 5``; both take AdamW's
+  decoupled decay (the pages call them AdamW variants).  RMSprop ("second
+  moment only") keeps ``v <- a v + (1-a) g^2`` with ``a = beta2``, no
+  momentum, not centred; AdaGrad ("cumulative squared gradient") keeps
+  ``v <- v + g^2`` with no learning-rate decay; RMSprop, AdaGrad and SGD take
+  coupled L2 decay like SGD with momentum.
 * The step index t is 1-based and is used directly in the bias correction.
 * The SR random bits come from a counter-based hash of (seed, step, tensor,
   flat index).  The pages ask only for "a six-operation splitmix-style
@@ -72,7 +84,8 @@ __all__ = [
     "bf16_bits_to_f64", "f32_to_bf16_rne", "f32_to_bf16_sr",
     "fmix32", "sr_key", "sr_bits",
     "weight_grad", "weight_grad_abs", "grad_error_bound",
-    "adamw", "lion", "sgdm",
+    "adamw", "lion", "sgdm", "nadam", "radam", "rmsprop", "adagrad", "sgd",
+    "nadam_mu", "radam_rect",
     "quantize_signed", "quantize_unsigned", "dequantize",
     "decode", "encode", "wgrad_step", "apply_step", "step_tiled",
     "TENSOR_W", "TENSOR_M", "TENSOR_V",
@@ -109,10 +122,10 @@ class Stored:
 @dataclass
 class Hyper:
     """Optimizer hyper-parameters (Algorithm 1 inputs: eta, beta1, beta2, eps, lambda)."""
-    opt: str = "adamw"          # "adamw" | "lion" | "sgdm"
+    opt: str = "adamw"          # "adamw" | "lion" | "sgdm" | "nadam" | "radam" | "rmsprop" | "adagrad" | "sgd"
     lr: float = 1e-3
     beta1: float = 0.9          # SGD-m: momentum mu
-    beta2: float = 0.999
+    beta2: float = 0.999        # RMSprop: smoothing constant a
     eps: float = 1e-8
     weight_decay: float = 0.01
     round: str = "sr"           # bf16 stores: "sr" | "rne"
@@ -314,6 +327,84 @@ def sgdm(W, G, b, lr, mu, weight_decay):
     return W1, b1
 
 
+NADAM_PSI = 0.004   # momentum decay of the NAdam schedule
+
+
+def nadam_mu(i, beta1):
+    """NAdam momentum schedule mu_i = b1 (1 - 0.5 * 0.96^(psi i)) (Dozat 2016,
+    as PyTorch states it), i 1-based."""
+    return beta1 * (1.0 - 0.5 * 0.96 ** (i * NADAM_PSI))
+
+
+def nadam(W, G, m, v, t, lr, beta1, beta2, eps, weight_decay):
+    """NAdam (Appendix N: AdamW with Nesterov momentum correction on m_hat),
+    decoupled decay, fp64:
+    m' = b1 m + (1-b1) G;  v' = b2 v + (1-b2) G^2;
+    m_hat = mu_{t+1} m' / (1 - prod_{i<=t+1} mu_i) + (1 - mu_t) G / (1 - prod_{i<=t} mu_i);
+    W' = (1 - lr wd) W - lr m_hat / (sqrt(v'/(1-b2^t)) + eps)."""
+    prod = 1.0
+    for i in range(1, t + 1):
+        prod *= nadam_mu(i, beta1)
+    mu_t, mu_next = nadam_mu(t, beta1), nadam_mu(t + 1, beta1)
+    m1 = beta1 * m + (1.0 - beta1) * G
+    v1 = beta2 * v + (1.0 - beta2) * G * G
+    m_hat = mu_next * m1 / (1.0 - prod * mu_next) + (1.0 - mu_t) * G / (1.0 - prod)
+    W1 = (1.0 - lr * weight_decay) * W - lr * m_hat / (np.sqrt(v1 / (1.0 - beta2 ** t)) + eps)
+    return W1, m1, v1
+
+
+def radam_rect(t, beta2):
+    """RAdam's rectification at step t (Liu et al. 2019): (rho_t > 5, r_t)."""
+    rho_inf = 2.0 / (1.0 - beta2) - 1.0
+    rho_t = rho_inf - 2.0 * t * beta2 ** t / (1.0 - beta2 ** t)
+    if rho_t <= 5.0:
+        return False, 0.0
+    return True, np.sqrt((rho_t - 4.0) * (rho_t - 2.0) * rho_inf / ((rho_inf - 4.0) * (rho_inf - 2.0) * rho_t))
+
+
+def radam(W, G, m, v, t, lr, beta1, beta2, eps, weight_decay):
+    """RAdam (Appendix N: AdamW with rectified-variance term), decoupled
+    decay, fp64: m', v' as AdamW, m_hat = m'/(1-b1^t); once rho_t > 5
+    W' = (1 - lr wd) W - lr m_hat r_t sqrt(1-b2^t) / (sqrt(v') + eps), before
+    that W' = (1 - lr wd) W - lr m_hat."""
+    m1 = beta1 * m + (1.0 - beta1) * G
+    v1 = beta2 * v + (1.0 - beta2) * G * G
+    m_hat = m1 / (1.0 - beta1 ** t)
+    on, r = radam_rect(t, beta2)
+    if on:
+        upd = m_hat * r * np.sqrt(1.0 - beta2 ** t) / (np.sqrt(v1) + eps)
+    else:
+        upd = m_hat
+    W1 = (1.0 - lr * weight_decay) * W - lr * upd
+    return W1, m1, v1
+
+
+def rmsprop(W, G, v, lr, alpha, eps, weight_decay):
+    """RMSprop (Appendix N: second moment only, no first moment), coupled
+    decay, no momentum, not centred, fp64:
+    g = G + wd W;  v' = a v + (1-a) g^2;  W' = W - lr g / (sqrt(v') + eps)."""
+    g = G + weight_decay * W
+    v1 = alpha * v + (1.0 - alpha) * g * g
+    W1 = W - lr * g / (np.sqrt(v1) + eps)
+    return W1, v1
+
+
+def adagrad(W, G, v, lr, eps, weight_decay):
+    """AdaGrad (Appendix N: cumulative squared gradient, no decay), coupled
+    decay, no learning-rate decay, fp64:
+    g = G + wd W;  v' = v + g^2;  W' = W - lr g / (sqrt(v') + eps)."""
+    g = G + weight_decay * W
+    v1 = v + g * g
+    W1 = W - lr * g / (np.sqrt(v1) + eps)
+    return W1, v1
+
+
+def sgd(W, G, lr, weight_decay):
+    """SGD (Appendix N: vanilla gradient descent, no moment buffers), coupled
+    decay, fp64: W' = W - lr (G + wd W)."""
+    return W - lr * (G + weight_decay * W)
+
+
 # --------------------------------------------------------------------------
 # int8 block quantisation (section 2.3, Appendix B)
 # --------------------------------------------------------------------------
@@ -442,6 +533,19 @@ def apply_step(G: np.ndarray, W: Stored, m: Optional[Stored], v: Optional[Stored
     elif h.opt == "sgdm":
         W1, m1 = sgdm(W0, G, m0, h.lr, h.beta1, h.weight_decay)
         v1 = None
+    elif h.opt == "nadam":
+        W1, m1, v1 = nadam(W0, G, m0, v0, step, h.lr, h.beta1, h.beta2, h.eps, h.weight_decay)
+    elif h.opt == "radam":
+        W1, m1, v1 = radam(W0, G, m0, v0, step, h.lr, h.beta1, h.beta2, h.eps, h.weight_decay)
+    elif h.opt == "rmsprop":
+        W1, v1 = rmsprop(W0, G, v0, h.lr, h.beta2, h.eps, h.weight_decay)
+        m1 = None
+    elif h.opt == "adagrad":
+        W1, v1 = adagrad(W0, G, v0, h.lr, h.eps, h.weight_decay)
+        m1 = None
+    elif h.opt == "sgd":
+        W1 = sgd(W0, G, h.lr, h.weight_decay)
+        m1 = v1 = None
     else:
         raise ValueError(f"unknown optimizer {h.opt!r}")
     if flat is None:

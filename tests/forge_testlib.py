@@ -49,6 +49,8 @@ class Layer:
     vs: Optional[torch.Tensor] = None
 
     def forge_m(self):
+        if self.m is None:
+            return None
         return F.state(self.m, self.ms, self.spec.block) if self.ms is not None else F.state(self.m)
 
     def forge_v(self):

@@ -273,3 +273,52 @@ def test_group_layers_must_not_write_each_others_buffers():
 def test_group_of_empty_layers_is_a_no_op():
     # N == 0 everywhere: valid and nothing to launch
     assert group([glayer(0, N=0), glayer(1, N=0)]) == F.FORGE_OK
+
+
+# ---------------------------------------------------------------------------
+# State and hyper-parameter rules of the eight optimizer families
+# ---------------------------------------------------------------------------
+def test_family_state_rules():
+    X, dY, W, m, v = layer()
+    for opt in ("nadam", "radam"):
+        assert check(X, dY, W, m, v, F.hyper(opt)) == F.FORGE_OK
+        assert check(X, dY, W, m, None, F.hyper(opt)) == F.FORGE_E_NULL
+    for opt in ("rmsprop", "adagrad"):
+        assert check(X, dY, W, None, v, F.hyper(opt)) == F.FORGE_OK
+        assert check(X, dY, W, m, v, F.hyper(opt)) == F.FORGE_E_UNSUPPORTED    # no first moment kept
+        assert check(X, dY, W, None, None, F.hyper(opt)) == F.FORGE_E_NULL
+    assert check(X, dY, W, None, None, F.hyper("sgd")) == F.FORGE_OK
+    assert check(X, dY, W, m, None, F.hyper("sgd")) == F.FORGE_E_UNSUPPORTED
+    assert check(X, dY, W, None, v, F.hyper("sgd")) == F.FORGE_E_UNSUPPORTED
+    # AdamW, Lion, SGD-m still need m
+    for opt in ("adamw", "lion", "sgdm"):
+        assert check(X, dY, W, None, v if opt == "adamw" else None, F.hyper(opt)) == F.FORGE_E_NULL
+
+
+def test_family_formats():
+    # NAdam / RAdam: fp32 or bf16 moments, no int8
+    X, dY, W, m, v = layer(m_dt=F.FORGE_BF16, v_dt=F.FORGE_BF16)
+    assert check(X, dY, W, m, v, F.hyper("radam")) == F.FORGE_OK
+    X, dY, W, m, v = layer(m_dt=F.FORGE_S8, v_dt=F.FORGE_U8)
+    assert check(X, dY, W, m, v, F.hyper("nadam")) == F.FORGE_E_UNSUPPORTED
+    # RMSprop / AdaGrad: v fp32 or bf16
+    X, dY, W, m, v = layer(v_dt=F.FORGE_BF16)
+    assert check(X, dY, W, None, v, F.hyper("adagrad")) == F.FORGE_OK
+    X, dY, W, m, v = layer(m_dt=F.FORGE_S8, v_dt=F.FORGE_U8)
+    assert check(X, dY, W, None, v, F.hyper("rmsprop")) == F.FORGE_E_UNSUPPORTED
+
+
+def test_family_hyper_ranges():
+    X, dY, W, m, v = layer()
+    assert check(X, dY, W, None, v, F.hyper("rmsprop", beta2=1.0)) == F.FORGE_E_HYPER   # smoothing constant
+    assert check(X, dY, W, None, v, F.hyper("rmsprop", eps=0.0)) == F.FORGE_E_HYPER
+    assert check(X, dY, W, None, v, F.hyper("adagrad", eps=0.0)) == F.FORGE_E_HYPER
+    assert check(X, dY, W, m, v, F.hyper("nadam", beta1=1.0)) == F.FORGE_E_HYPER
+    assert check(X, dY, W, m, v, F.hyper("radam", eps=-1.0)) == F.FORGE_E_HYPER
+    # parameters an optimizer does not use are not range-checked (only finiteness)
+    assert check(X, dY, W, None, v, F.hyper("adagrad", beta1=1.5, beta2=2.0)) == F.FORGE_OK
+    assert check(X, dY, W, None, None, F.hyper("sgd", beta1=3.0, eps=0.0)) == F.FORGE_OK
+    assert check(X, dY, W, None, None, F.hyper("sgd", beta1=float("nan"))) == F.FORGE_E_HYPER
+    h = F.hyper("sgd")
+    h.opt = 8
+    assert check(X, dY, W, None, None, h) == F.FORGE_E_HYPER

@@ -503,3 +503,103 @@ def test_fp32_layer_three_steps_match_torch():
         np.testing.assert_allclose(W.data, p.detach().numpy().astype(np.float32), rtol=2e-7, atol=1e-12)
         np.testing.assert_allclose(m.data, opt.state[p]["exp_avg"].numpy().astype(np.float32), rtol=2e-7, atol=1e-20)
         np.testing.assert_allclose(v.data, opt.state[p]["exp_avg_sq"].numpy().astype(np.float32), rtol=2e-7, atol=1e-30)
+
+
+# ---------------------------------------------------------------------------
+# The other element-wise families (Appendix N, "fully fused"): each against
+# torch.optim in float64 over enough steps to cover RAdam's switch to the
+# rectified step (t = 6 with beta2 = 0.999), and against closed forms.
+# ---------------------------------------------------------------------------
+def _torch_run(make_opt, oracle_step, n=2048, steps=9, seed=11, state_keys=()):
+    rng = np.random.default_rng(seed)
+    W = rng.normal(0, 0.02, n)
+    st = [np.zeros(n) for _ in state_keys]
+    p = torch.tensor(W.copy(), dtype=torch.float64, requires_grad=True)
+    opt = make_opt([p])
+    for t in range(1, steps + 1):
+        G = rng.normal(0, 1e-2, n)
+        W, *st = oracle_step(W, G, st, t)
+        p.grad = torch.tensor(G, dtype=torch.float64)
+        opt.step()
+        np.testing.assert_allclose(W, p.detach().numpy(), rtol=1e-12, atol=1e-18, err_msg=f"W at t={t}")
+        for k, s in zip(state_keys, st):
+            # torch forms the moments with lerp; rounding differs from b m + (1-b) g
+            np.testing.assert_allclose(s, opt.state[p][k].numpy(), rtol=1e-10, atol=1e-22, err_msg=f"{k} at t={t}")
+
+
+def test_nadam_matches_torch_nadam_decoupled_float64():
+    # torch keeps NAdam's running product of mu_i as a tensor of the default
+    # dtype; float64 throughout makes it the same product as the oracle's
+    old = torch.get_default_dtype()
+    torch.set_default_dtype(torch.float64)
+    try:
+        _nadam_run()
+    finally:
+        torch.set_default_dtype(old)
+
+
+def _nadam_run():
+    _torch_run(lambda ps: torch.optim.NAdam(ps, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01,
+                                            momentum_decay=4e-3, decoupled_weight_decay=True),
+               lambda W, G, st, t: O.nadam(W, G, st[0], st[1], t, 1e-3, 0.9, 0.999, 1e-8, 0.01),
+               state_keys=("exp_avg", "exp_avg_sq"))
+
+
+def test_radam_matches_torch_radam_decoupled_float64():
+    _torch_run(lambda ps: torch.optim.RAdam(ps, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01,
+                                            decoupled_weight_decay=True),
+               lambda W, G, st, t: O.radam(W, G, st[0], st[1], t, 1e-3, 0.9, 0.999, 1e-8, 0.01),
+               state_keys=("exp_avg", "exp_avg_sq"))
+
+
+def test_rmsprop_matches_torch_rmsprop_float64():
+    _torch_run(lambda ps: torch.optim.RMSprop(ps, lr=1e-3, alpha=0.99, eps=1e-8, weight_decay=0.01),
+               lambda W, G, st, t: O.rmsprop(W, G, st[0], 1e-3, 0.99, 1e-8, 0.01),
+               state_keys=("square_avg",))
+
+
+def test_adagrad_matches_torch_adagrad_float64():
+    _torch_run(lambda ps: torch.optim.Adagrad(ps, lr=1e-3, lr_decay=0, weight_decay=0.01, eps=1e-10,
+                                              initial_accumulator_value=0.0),
+               lambda W, G, st, t: O.adagrad(W, G, st[0], 1e-3, 1e-10, 0.01),
+               state_keys=("sum",))
+
+
+def test_sgd_matches_torch_sgd_float64():
+    _torch_run(lambda ps: torch.optim.SGD(ps, lr=1e-3, weight_decay=0.01),
+               lambda W, G, st, t: (O.sgd(W, G, 1e-3, 0.01),))
+
+
+def test_first_steps_closed_forms():
+    """t = 1 from zero state, eps = 0: each rule reduces to a sign step of a
+    known length (nonzero G), independent of the gradient's magnitude."""
+    W = np.array([0.3, -0.2, 0.05, -0.7])
+    G = np.array([2e-3, -5e-1, 7.0, -1e-6])
+    lr, wd = 1e-3, 0.01
+    # RMSprop: v' = (1-a) g^2 -> W - lr sign(g) / sqrt(1-a), with g = G + wd W
+    g = G + wd * W
+    W1, v1 = O.rmsprop(W, G, np.zeros(4), lr, 0.99, 0.0, wd)
+    np.testing.assert_allclose(W1, W - lr * np.sign(g) / math.sqrt(0.01), rtol=1e-13)
+    np.testing.assert_allclose(v1, 0.01 * g * g, rtol=1e-15)
+    # AdaGrad: v' = g^2 -> W - lr sign(g)
+    W1, v1 = O.adagrad(W, G, np.zeros(4), lr, 0.0, wd)
+    np.testing.assert_allclose(W1, W - lr * np.sign(g), rtol=1e-15)
+    # RAdam before rectification: W' = (1 - lr wd) W - lr m_hat, m_hat = G at t = 1
+    W1, m1, v1 = O.radam(W, G, np.zeros(4), np.zeros(4), 1, lr, 0.9, 0.999, 1e-8, wd)
+    np.testing.assert_allclose(W1, (1 - lr * wd) * W - lr * G, rtol=1e-15)
+    # NAdam: m_hat = G (1 + mu2 (1 - b1) / (1 - mu1 mu2)), v_hat = G^2
+    mu1 = 0.9 * (1 - 0.5 * 0.96 ** 0.004)
+    mu2 = 0.9 * (1 - 0.5 * 0.96 ** 0.008)
+    W1, m1, v1 = O.nadam(W, G, np.zeros(4), np.zeros(4), 1, lr, 0.9, 0.999, 0.0, wd)
+    np.testing.assert_allclose(W1, (1 - lr * wd) * W - lr * np.sign(G) * (1 + mu2 * 0.1 / (1 - mu1 * mu2)),
+                               rtol=1e-13)
+    # SGD is SGD with momentum at mu = 0 from a zero buffer
+    np.testing.assert_allclose(O.sgd(W, G, lr, wd), O.sgdm(W, G, np.zeros(4), lr, 0.0, wd)[0], rtol=0)
+
+
+def test_radam_rectification_limits():
+    """rho_t <= 5 for t <= 5 (beta2 = 0.999): plain momentum steps; the
+    rectification r_t -> 1 as t -> infinity (rho_t -> rho_inf)."""
+    assert [O.radam_rect(t, 0.999)[0] for t in range(1, 8)] == [False] * 5 + [True] * 2
+    on, r = O.radam_rect(10 ** 7, 0.999)
+    assert on and abs(r - 1.0) < 1e-6
