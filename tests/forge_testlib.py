@@ -13,8 +13,12 @@ the same inputs and compares every output element by element:
   on absolute values), so that an output which cancels -- a weight that the
   update drives through zero -- is judged against its operands' scale;
 * bf16 outputs: within one bf16 ULP (+ 1e-5 S) of that hull, and bit-identical to the
-  oracle's stored pattern for at least 99.9% of the elements (the SR bits
-  come from the same counter-based hash on both sides);
+  oracle's stored pattern for at least a fraction 1 - (1e-3 + 2 sqrt(BT) 2^-16)
+  of the elements (the SR bits come from the same counter-based hash on both
+  sides, so a stored pattern differs only where the fp32 gradient's rounding
+  -- relative size about sqrt(BT) 2^-24 for a BT-term fp32 sum -- moves the
+  value across the rounding decision, which happens with probability of that
+  size in units of a bf16 ULP, 2^-8: about sqrt(BT) 2^-16);
 * int8 codes: within one code of the oracle's, at least 99% identical;
   scales within 1e-5 relative or inside the hull of the block absmax.
 """
@@ -194,10 +198,12 @@ def _abs_stored(st):
 
 
 def check_against_oracle(snap: Snap, L: Layer, h, step: int, seed: int, col_ranges=None,
-                         rep: Optional[Report] = None, exact_min=0.999, code_exact_min=0.99) -> Report:
+                         rep: Optional[Report] = None, exact_min=None, code_exact_min=0.99) -> Report:
     """Compare the layer's current (post-step) tensors on rows snap.rows and
     the given column ranges with the oracle run on the snapshot."""
     rep = rep or Report()
+    if exact_min is None:
+        exact_min = 1.0 - (1e-3 + 2.0 * np.sqrt(max(1, snap.X.shape[0])) * 2.0 ** -16)
     hyp = oracle_hyper(h)
     K = L.K
     col_ranges = col_ranges or [(0, K)]

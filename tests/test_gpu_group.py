@@ -94,7 +94,7 @@ def test_group_eight_mixed_layers(spec):
     _say(f"case: group of eight mixed layers {spec}")
     cases = [(256, 256, 64), (136, 520, 100), (1024, 128, 512), (8, 8, 1),
              (264, 1001, 77),     # K % 8 != 0: rows not 16-byte aligned, runs as its own launch
-             (256, 512, 2100),    # long token axis: the wide kernel, its own launch
+             (256, 512, 4100),    # long token axis: the wide kernel, its own launch
              (0, 256, 64),        # empty: nothing to do
              (128, 128, 0)]       # BT = 0: the step with G = 0
     layers = [make_layer(7, N, K, BT, 2, spec, extra=i) for i, (N, K, BT) in enumerate(cases)]

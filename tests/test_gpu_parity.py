@@ -294,7 +294,7 @@ def test_compute_bound_sweep_full_size(BT, name, N, K, opt):
 # The last two shapes take the 256 x 256 macro-tile kernel used for long token
 # axes (ragged against 256 in both W dimensions and in the token chunks).
 @pytest.mark.parametrize("N,K,BT", [(2000, 4096, 300), (4104, 1024, 520), (600, 17152, 256),
-                                    (1000, 1408, 2050), (2048, 1664, 2080)])
+                                    (1000, 1408, 4100), (2048, 1664, 4128)])
 def test_aligned_multi_tile(spec, opt, N, K, BT):
     _say(f"case: aligned multi-tile {spec} {opt} {N}x{K} BT{BT}")
     L = make_layer(5, N, K, BT, 7, spec, gen_device="cuda", outlier_p=0.01 if spec.m_fmt == "s8" else 0.0)
