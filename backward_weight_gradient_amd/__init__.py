@@ -95,6 +95,12 @@ def _load() -> ctypes.CDLL:
     lib.forge_wgrad_step_group.argtypes = [P(forge_layer), ctypes.c_int32, P(forge_hyper), ctypes.c_int64,
                                            ctypes.c_void_p]
     lib.forge_wgrad_step_group.restype = st
+    lib.forge_wgrad_accumulate.argtypes = [P(forge_mat), P(forge_mat), P(forge_mat), ctypes.c_int32, ctypes.c_void_p]
+    lib.forge_wgrad_accumulate.restype = st
+    lib.forge_wgrad_step_accumulated.argtypes = [P(forge_mat), P(forge_mat), P(forge_mat), P(forge_mat),
+                                                 P(forge_state), P(forge_state), P(forge_hyper), ctypes.c_int64,
+                                                 ctypes.c_uint64, ctypes.c_void_p]
+    lib.forge_wgrad_step_accumulated.restype = st
     lib.forge_status_str.argtypes = [ctypes.c_int]
     lib.forge_status_str.restype = ctypes.c_char_p
     lib.forge_version.argtypes = []
@@ -220,6 +226,31 @@ def forge_wgrad_step_group(layers, h: forge_hyper, step: int, stream=None, check
     rc = lib.forge_wgrad_step_group(arr, len(layers), _ref(h), step, _stream(stream))
     if check and rc != FORGE_OK:
         raise ForgeError(rc, "forge_wgrad_step_group")
+    return rc
+
+
+def forge_wgrad_accumulate(X, dY, acc, first: bool, stream=None, check: bool = True) -> int:
+    """One micro-step of exact gradient accumulation: acc = dY^T X (first) or acc += dY^T X (fp32)."""
+    X = mat(X) if not isinstance(X, forge_mat) else X
+    dY = mat(dY) if not isinstance(dY, forge_mat) else dY
+    acc = mat(acc) if not isinstance(acc, forge_mat) else acc
+    rc = lib.forge_wgrad_accumulate(_ref(X), _ref(dY), _ref(acc), 1 if first else 0, _stream(stream))
+    if check and rc != FORGE_OK:
+        raise ForgeError(rc, "forge_wgrad_accumulate")
+    return rc
+
+
+def forge_wgrad_step_accumulated(X, dY, acc, W, m, v, h: forge_hyper, step: int, seed: int, stream=None,
+                                 check: bool = True) -> int:
+    """Final micro-step: the fused step on G = acc + dY^T X (acc is consumed)."""
+    X = mat(X) if not isinstance(X, forge_mat) else X
+    dY = mat(dY) if not isinstance(dY, forge_mat) else dY
+    acc = mat(acc) if not isinstance(acc, forge_mat) else acc
+    W = mat(W) if not isinstance(W, forge_mat) else W
+    rc = lib.forge_wgrad_step_accumulated(_ref(X), _ref(dY), _ref(acc), _ref(W), _ref(m), _ref(v), _ref(h), step,
+                                          seed, _stream(stream))
+    if check and rc != FORGE_OK:
+        raise ForgeError(rc, "forge_wgrad_step_accumulated")
     return rc
 
 

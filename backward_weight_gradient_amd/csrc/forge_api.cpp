@@ -194,23 +194,46 @@ forge_status validate(const forge_mat* X, const forge_mat* dY, const forge_mat* 
   return FORGE_OK;
 }
 
+// X and dY of a call that has no weight (gradient accumulation).
+forge_status validate_inputs(const forge_mat* X, const forge_mat* dY, Plan& pl) {
+  if (!X || !dY) return FORGE_E_NULL;
+  pl.BT = X->rows;
+  pl.K = X->cols;
+  pl.N = dY->cols;
+  if (pl.BT < 0 || pl.N < 0 || pl.K < 0) return FORGE_E_SHAPE;
+  if (dY->rows != pl.BT) return FORGE_E_SHAPE;
+  forge_status st;
+  if ((st = check_mat(*X, pl.BT, pl.K)) != FORGE_OK) return st;
+  if ((st = check_mat(*dY, pl.BT, pl.N)) != FORGE_OK) return st;
+  if (X->dtype != dY->dtype) return FORGE_E_DTYPE;
+  if (X->dtype != FORGE_F32 && X->dtype != FORGE_BF16) return FORGE_E_DTYPE;
+  if ((uint64_t)pl.N * (uint64_t)pl.K >= (1ull << 32)) return FORGE_E_SHAPE;
+  if (pl.BT >= (1ll << 31) || pl.N >= (1ll << 31) || pl.K >= (1ll << 31)) return FORGE_E_SHAPE;
+  pl.in_fmt = X->dtype;
+  pl.empty = (pl.N == 0 || pl.K == 0);
+  return FORGE_OK;
+}
+
+// The fp32 gradient accumulator of forge_wgrad_accumulate / _step_accumulated.
+forge_status check_acc(const forge_mat* acc, int64_t N, int64_t K) {
+  if (!acc) return FORGE_E_NULL;
+  const forge_status st = check_mat(*acc, N, K);
+  if (st != FORGE_OK) return st;
+  if (acc->dtype != FORGE_F32) return FORGE_E_DTYPE;
+  return FORGE_OK;
+}
+
 bool vec_ok(const void* p, int64_t ld, int elems, int es) {
   return p == nullptr || (aligned(p, elems * es) && (ld % elems) == 0);
 }
 
-KArgs make_args(const forge_mat* X, const forge_mat* dY, forge_mat* W, forge_state* m, forge_state* v,
-                const forge_hyper* h, int64_t step, uint64_t seed, const Plan& pl) {
-  KArgs a;
-  std::memset(&a, 0, sizeof(a));
+// The activation half of a launch: X, dY, sizes, tile counts, loader choice.
+void input_args(const forge_mat* X, const forge_mat* dY, const Plan& pl, KArgs& a) {
   a.X = X->data; a.ldx = X->ld;
   a.dY = dY->data; a.lddy = dY->ld;
-  a.W = W->data; a.ldw = W->ld;
-  if (m) { a.m = m->q.data; a.ldm = m->q.ld; a.ms = m->scale; }
-  if (v) { a.v = v->q.data; a.ldv = v->q.ld; a.vs = v->scale; }
   a.BT = (int32_t)pl.BT; a.N = (int32_t)pl.N; a.K = (int32_t)pl.K;
   a.tiles_n = (int32_t)((pl.N + 127) / 128);
   a.tiles_k = (int32_t)((pl.K + 127) / 128);
-  a.block = pl.block ? pl.block : 128;
   // 16-byte vector loads of 8 bf16 / 4 fp32 activations
   const int ies = elem_size(pl.in_fmt), ivec = 16 / ies;
   a.vec_in = (vec_ok(X->data, X->ld, ivec, ies) && vec_ok(dY->data, dY->ld, ivec, ies)) ? 1 : 0;
@@ -220,6 +243,26 @@ KArgs make_args(const forge_mat* X, const forge_mat* dY, forge_mat* W, forge_sta
   a.dma_ok = (pl.in_fmt == FORGE_BF16 && a.vec_in && pl.N % 8 == 0 && pl.K % 8 == 0 &&
               (uint64_t)pl.BT * (uint64_t)dY->ld * 2 < (1ull << 31) &&
               (uint64_t)pl.BT * (uint64_t)X->ld * 2 < (1ull << 31)) ? 1 : 0;
+  a.lddw = pl.K;
+}
+
+// An fp32 G buffer (accumulator) as the launch's dW.
+void acc_args(forge_mat* acc, KArgs& a) {
+  a.dW = acc->data;
+  a.lddw = acc->ld;
+  a.dw_fmt = FMT_F32;
+  a.vec_dw = vec_ok(acc->data, acc->ld, 4, 4) ? 1 : 0;
+}
+
+KArgs make_args(const forge_mat* X, const forge_mat* dY, forge_mat* W, forge_state* m, forge_state* v,
+                const forge_hyper* h, int64_t step, uint64_t seed, const Plan& pl) {
+  KArgs a;
+  std::memset(&a, 0, sizeof(a));
+  input_args(X, dY, pl, a);
+  a.W = W->data; a.ldw = W->ld;
+  if (m) { a.m = m->q.data; a.ldm = m->q.ld; a.ms = m->scale; }
+  if (v) { a.v = v->q.data; a.ldv = v->q.ld; a.vs = v->scale; }
+  a.block = pl.block ? pl.block : 128;
   // 4-element state accesses (16 B fp32, 8 B bf16, 4 B int8)
   bool vs = vec_ok(W->data, W->ld, 4, elem_size(pl.w_fmt));
   if (m) vs = vs && vec_ok(m->q.data, m->q.ld, 4, elem_size(pl.m_fmt));
@@ -383,6 +426,52 @@ forge_status forge_wgrad_unfused(const forge_mat* X, const forge_mat* dY, forge_
   KArgs a = make_args(X, dY, W, m, v, h, step, seed, pl);
   a.dW = dW;
   a.dw_fmt = dW_dtype == FORGE_F32 ? FMT_F32 : FMT_BF16;
+  a.vec_dw = (pl.K % 4) == 0 ? 1 : 0;   // the workspace is 16-byte aligned with ld = K
+  hipError_t e = launch_gemm(a, pl.in_fmt, (hipStream_t)stream);
+  if (e == hipSuccess) e = launch_step(a, pl.w_fmt, h->opt, pl.m_fmt, pl.v_fmt, (hipStream_t)stream);
+  return hip_status(e);
+}
+
+forge_status forge_wgrad_accumulate(const forge_mat* X, const forge_mat* dY, forge_mat* acc, int32_t first,
+                                    void* stream) {
+  Plan pl;
+  forge_status st = validate_inputs(X, dY, pl);
+  if (st != FORGE_OK) return st;
+  if ((st = check_acc(acc, pl.N, pl.K)) != FORGE_OK) return st;
+  const Range ra = mat_range(*acc);
+  if (overlap(ra, mat_range(*X)) || overlap(ra, mat_range(*dY))) return FORGE_E_ALIAS;
+  if (pl.empty) return FORGE_OK;
+  KArgs a;
+  std::memset(&a, 0, sizeof(a));
+  input_args(X, dY, pl, a);
+  acc_args(acc, a);
+  a.dw_add = first ? 0 : 1;
+  return hip_status(launch_gemm(a, pl.in_fmt, (hipStream_t)stream));
+}
+
+forge_status forge_wgrad_step_accumulated(const forge_mat* X, const forge_mat* dY, forge_mat* acc, forge_mat* W,
+                                          forge_state* m, forge_state* v, const forge_hyper* h, int64_t step,
+                                          uint64_t seed, void* stream) {
+  Plan pl;
+  forge_status st = validate(X, dY, W, m, v, h, step, pl);
+  if (st != FORGE_OK) return st;
+  if ((st = check_acc(acc, pl.N, pl.K)) != FORGE_OK) return st;
+  Range outs[5], ins[2];
+  layer_ranges(X, dY, W, m, v, pl, outs, ins);
+  const Range ra = mat_range(*acc);
+  for (const Range& r : outs)
+    if (overlap(ra, r)) return FORGE_E_ALIAS;
+  for (const Range& r : ins)
+    if (overlap(ra, r)) return FORGE_E_ALIAS;
+  if (pl.empty) return FORGE_OK;
+  KArgs a = make_args(X, dY, W, m, v, h, step, seed, pl);
+  acc_args(acc, a);
+  // aligned bf16: one fused kernel adds the accumulator to the tile in the
+  // epilogue; otherwise this micro-batch is added into the accumulator and
+  // the step reads it back (the same fp32 addition, so the same result)
+  if (pl.in_fmt == FORGE_BF16 && a.dma_ok && a.vec_state && a.vec_dw && pl.K % 4 == 0)
+    return hip_status(launch_fused_acc(a, pl.w_fmt, h->opt, pl.m_fmt, pl.v_fmt, (hipStream_t)stream));
+  a.dw_add = 1;
   hipError_t e = launch_gemm(a, pl.in_fmt, (hipStream_t)stream);
   if (e == hipSuccess) e = launch_step(a, pl.w_fmt, h->opt, pl.m_fmt, pl.v_fmt, (hipStream_t)stream);
   return hip_status(e);

@@ -1054,12 +1054,16 @@ struct Step {
 // issue() requests the state of one pass into a slot; consume() decodes a
 // slot, applies the step and stores.  G comes from the LDS staging buffer
 // (GF == FMT_NONE) or from the dW workspace in format GF (unfused baseline).
-template <class S, int GF, bool FAST, int DEPTH, int NTE = NT>
+// With ACC, G is the staged tile plus the fp32 accumulator a.dW (one fp32
+// addition per element, the same one k_gemm's accumulation performs).
+template <class S, int GF, bool FAST, int DEPTH, int NTE = NT, bool ACC = false>
 struct Epilogue {
+  static_assert(!ACC || GF == FMT_NONE, "the accumulator adds to the staged tile");
   static constexpr int PASSES = TILE * TILE / (8 * NTE);  // 8 with 256 threads, 4 with 512
   static constexpr int RPP = NTE / 16;                    // rows per pass
+  static constexpr int GR = ACC ? FMT_F32 : GF;           // format of the G words loaded per pass
   typename S::Pending pend[DEPTH];
-  Raw4<GF> graw[DEPTH][2];
+  Raw4<GR> graw[DEPTH][2];
   int tid;
 
   __device__ __forceinline__ void segs(const KArgs& a, int p, int col0, Seg (&sg)[2]) const {
@@ -1077,12 +1081,12 @@ struct Epilogue {
     Seg sg[2];
     segs(a, p, col0, sg);
     S::load(a, p, sg, pend[slot]);
-    if constexpr (GF != FMT_NONE) {
-      const bool gvec = (a.K & 3) == 0;
-      const char* rg = static_cast<const char*>(a.dW) + (int64_t)p * a.K * (GF == FMT_F32 ? 4 : 2);
+    if constexpr (GR != FMT_NONE) {
+      const bool gvec = a.vec_dw != 0;
+      const char* rg = static_cast<const char*>(a.dW) + (int64_t)p * a.lddw * (GR == FMT_F32 ? 4 : 2);
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        if (sg[g].ok) ld4<GF, FAST>(graw[slot][g], rg, sg[g], gvec);
+        if (sg[g].ok) ld4<GR, FAST>(graw[slot][g], rg, sg[g], gvec);
         else zero4(graw[slot][g]);
       }
     }
@@ -1096,6 +1100,13 @@ struct Epilogue {
       const f32x4 g1 = *reinterpret_cast<const f32x4*>(sG + rl * GP + 64 + cl);
 #pragma unroll
       for (int i = 0; i < 4; ++i) { g[i] = g0[i]; g[4 + i] = g1[i]; }
+      if constexpr (ACC) {
+        float acc[8];
+        dec4<FMT_F32>(graw[slot][0], acc);
+        dec4<FMT_F32>(graw[slot][1], acc + 4);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) g[i] = acc[i] + g[i];
+      }
     } else {
       dec4<GF>(graw[slot][0], g);
       dec4<GF>(graw[slot][1], g + 4);
@@ -1132,7 +1143,7 @@ struct Epilogue {
 // IN: input format.  FAST (bf16 inputs only): the asynchronous
 // direct-to-LDS mainloop and the vector-only epilogue; the host selects it
 // when X, dY and the state rows are aligned and N, K are multiples of 8.
-template <int IN, bool FAST, int OPT, int WF, int MF, int VF>
+template <int IN, bool FAST, int OPT, int WF, int MF, int VF, bool ACC = false>
 __global__ void __launch_bounds__(NT, 2) k_fused(const KArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   int ti, tj;
@@ -1140,7 +1151,7 @@ __global__ void __launch_bounds__(NT, 2) k_fused(const KArgs a) {
   const int row0 = ti * TILE, col0 = tj * TILE;
   if constexpr (FAST) tile_gradient_dma(a, lds, row0, col0);
   else tile_gradient<IN>(a, lds, row0, col0);
-  Epilogue<Step<OPT, WF, MF, VF, FAST>, FMT_NONE, FAST, 4> epi;
+  Epilogue<Step<OPT, WF, MF, VF, FAST>, FMT_NONE, FAST, 4, NT, ACC> epi;
   epi.tid = threadIdx.x;
   epi.run_tile(a, reinterpret_cast<const float*>(lds), row0, col0);
 }
@@ -1218,13 +1229,13 @@ __global__ void __launch_bounds__(NT, 2) k_gemm(const KArgs a) {
   else tile_gradient<IN>(a, lds, row0, col0);
   const float* sG = reinterpret_cast<const float*>(lds);
   const int cl = 4 * (threadIdx.x & 15);
-  const bool vec = (a.K & 3) == 0;
+  const bool vec = a.vec_dw != 0;
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     const int rl = s * 16 + (threadIdx.x >> 4);
     const int p = row0 + rl;
     if (p >= a.N) continue;
-    char* rowp = static_cast<char*>(a.dW) + (int64_t)p * a.K * (a.dw_fmt == FMT_F32 ? 4 : 2);
+    char* rowp = static_cast<char*>(a.dW) + (int64_t)p * a.lddw * (a.dw_fmt == FMT_F32 ? 4 : 2);
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       Seg sg;
@@ -1235,6 +1246,14 @@ __global__ void __launch_bounds__(NT, 2) k_gemm(const KArgs a) {
       float x[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) x[i] = sG[rl * GP + 64 * g + cl + i];
+      if (a.dw_add) {                       // gradient accumulation: old + G, one fp32 addition
+        Raw4<FMT_F32> r;
+        ld4<FMT_F32, false>(r, rowp, sg, vec);
+        float old[4];
+        dec4<FMT_F32>(r, old);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = old[i] + x[i];
+      }
       if (a.dw_fmt == FMT_F32) st4<FMT_F32, false>(rowp, sg, vec, x, 0, 0, 0);
       else st4<FMT_BF16, false>(rowp, sg, vec, x, 0, 0, 0);
     }
@@ -1292,7 +1311,7 @@ hipError_t combo_group(const GroupArgs& g, int w_fmt, hipStream_t st) {
 
 template <int O, int M, int V>
 hipError_t combo_step(const KArgs& a, int w_fmt, hipStream_t st) {
-  const bool fast = a.vec_state && (a.K % 4) == 0;
+  const bool fast = a.vec_state && a.vec_dw && (a.K % 4) == 0;
   if (w_fmt != FMT_BF16 && w_fmt != FMT_F32) return hipErrorInvalidValue;
   const bool wbf = w_fmt == FMT_BF16;
 #define FORGE_STEP_LAUNCH(GF, FA)                                                                         \
@@ -1309,10 +1328,19 @@ hipError_t combo_step(const KArgs& a, int w_fmt, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Explicit instantiation of the three launchers of one combination.
+template <int O, int M, int V>
+hipError_t combo_fused_acc(const KArgs& a, int w_fmt, hipStream_t st) {
+  if (w_fmt == FMT_BF16) hipLaunchKernelGGL((k_fused<FMT_BF16, true, O, FMT_BF16, M, V, true>), tile_grid(a), dim3(NT), 0, st, a);
+  else if (w_fmt == FMT_F32) hipLaunchKernelGGL((k_fused<FMT_BF16, true, O, FMT_F32, M, V, true>), tile_grid(a), dim3(NT), 0, st, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// Explicit instantiation of the launchers of one combination.
 #define FORGE_INSTANTIATE(O, M, V)                                                  \
   template hipError_t combo_fused<O, M, V>(const KArgs&, int, int, hipStream_t);   \
   template hipError_t combo_group<O, M, V>(const GroupArgs&, int, hipStream_t);    \
-  template hipError_t combo_step<O, M, V>(const KArgs&, int, hipStream_t);
+  template hipError_t combo_step<O, M, V>(const KArgs&, int, hipStream_t);         \
+  template hipError_t combo_fused_acc<O, M, V>(const KArgs&, int, hipStream_t);
 
 }  // namespace forge

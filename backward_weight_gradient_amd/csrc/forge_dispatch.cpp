@@ -21,6 +21,14 @@ hipError_t launch_fused_group(const GroupArgs& g, int w_fmt, int opt, int m_fmt,
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_fused_acc(const KArgs& a, int w_fmt, int opt, int m_fmt, int v_fmt, hipStream_t st) {
+#define X(O, M, V) \
+  if (opt == O && m_fmt == M && v_fmt == V) return combo_fused_acc<O, M, V>(a, w_fmt, st);
+  FORGE_STATE_LIST(X)
+#undef X
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_step(const KArgs& a, int w_fmt, int opt, int m_fmt, int v_fmt, hipStream_t st) {
 #define X(O, M, V) \
   if (opt == O && m_fmt == M && v_fmt == V) return combo_step<O, M, V>(a, w_fmt, st);

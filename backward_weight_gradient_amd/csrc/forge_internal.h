@@ -51,8 +51,10 @@ struct KArgs {
   void* W;  int64_t ldw;          // [N, K]
   void* m;  int64_t ldm; float* ms;   // state 1 (+ int8 scales [N, K/block])
   void* v;  int64_t ldv; float* vs;   // state 2 (+ int8 scales)
-  void* dW;                       // unfused workspace [N, K], ld = K
+  void* dW; int64_t lddw;         // G buffer [N, K]: unfused workspace (ld = K) or fp32 accumulator
   int32_t dw_fmt;                 // FMT_F32 / FMT_BF16 for dW
+  int32_t vec_dw;                 // dW rows allow 16-byte vector access
+  int32_t dw_add;                 // k_gemm: dW += G instead of dW = G (fp32 accumulation)
   int32_t BT, N, K;
   int32_t tiles_n, tiles_k;       // ceil(N/128), ceil(K/128)
   int32_t block;                  // int8 block length (32, 64, 128)
@@ -125,6 +127,9 @@ template <int O, int M, int V>
 hipError_t combo_group(const GroupArgs& g, int w_fmt, hipStream_t st);
 template <int O, int M, int V>
 hipError_t combo_step(const KArgs& a, int w_fmt, hipStream_t st);
+// Fused step with G = a.dW (fp32 accumulator) + this call's G (aligned bf16 inputs only).
+template <int O, int M, int V>
+hipError_t combo_fused_acc(const KArgs& a, int w_fmt, hipStream_t st);
 
 // Runtime dispatch over the combinations (forge_dispatch.cpp).
 // Fused weight-gradient + step: one workgroup per 128 x 128 tile of W.
@@ -132,7 +137,10 @@ hipError_t launch_fused(const KArgs& a, int in_fmt, int w_fmt, int opt, int m_fm
                         hipStream_t stream);
 // Fused step of g.n group-eligible layers in one launch (bf16 inputs).
 hipError_t launch_fused_group(const GroupArgs& g, int w_fmt, int opt, int m_fmt, int v_fmt, hipStream_t stream);
-// Unfused baseline, phase 1 (forge_k_common.hip): G tiles -> a.dW (a.dw_fmt).
+// Fused step from an fp32 accumulator plus this call's gradient.
+hipError_t launch_fused_acc(const KArgs& a, int w_fmt, int opt, int m_fmt, int v_fmt, hipStream_t stream);
+// Unfused baseline, phase 1, and gradient accumulation (forge_k_common.hip):
+// G tiles -> a.dW (a.dw_fmt), or a.dW += G when a.dw_add.
 hipError_t launch_gemm(const KArgs& a, int in_fmt, hipStream_t stream);
 // Unfused baseline, phase 2: the same step, reading G from a.dW.
 hipError_t launch_step(const KArgs& a, int w_fmt, int opt, int m_fmt, int v_fmt, hipStream_t stream);

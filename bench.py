@@ -58,6 +58,8 @@ def parse():
                         "forge_wgrad_step launch per layer")
     p.add_argument("--no-family-sweep", action="store_true",
                    help="skip the per-optimizer timing (gate_proj, BT 512, all eight families)")
+    p.add_argument("--no-accumulation", action="store_true",
+                   help="skip the gradient-accumulation timing (gate_proj, 4 micro-batches of 128 tokens)")
     p.add_argument("--no-mfma-sweep", action="store_true",
                    help="skip the compute-bound sweep (down_proj, lm_head at BT 2048 / 8192)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -185,6 +187,60 @@ def family_sweep(F, synth, reps=5):
                     "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         del st, args, m, v
     del X, dY
+    torch.cuda.empty_cache()
+    return out
+
+
+def accumulation_sweep(F, synth, h, micro=4, reps=5):
+    """Exact gradient accumulation (Appendix L) on gate_proj [14336, 4096]:
+    `micro` micro-batches of BT / micro tokens, AdamW as in the step.  Each
+    micro-step but the last adds into an fp32 accumulator (first one
+    overwrites); the last runs the fused step on accumulator + its gradient.
+    Algorithmic bytes: accumulator written (first) or read and written (4 / 8
+    B per parameter), final step 20 + 4 B per parameter, activations once."""
+    import torch
+    N, K = 14336, 4096
+    bt = BT // micro
+    stream = torch.cuda.current_stream()
+    spec = synth.LayerSpec(in_dtype="bf16", w_fmt="bf16", m_fmt="f32", v_fmt="f32")
+    st = synth.state(1, N, K, spec, device="cuda", extra=50)
+    mb = [synth.activations(1, bt, N, K, STEP_T, device="cuda", extra=50 + i) for i in range(micro)]
+    acc = torch.empty((N, K), device="cuda", dtype=torch.float32)
+    W, m, v = F.mat(st["W"]), F.state(st["m"]), F.state(st["v"])
+    sp = stream.cuda_stream
+    mats = [(F.mat(X), F.mat(dY)) for X, dY in mb]
+    accm = F.mat(acc)
+
+    def run(ev=None):
+        for i, (Xm, dYm) in enumerate(mats):
+            if ev is not None:
+                ev[i][0].record(stream)
+            if i < micro - 1:
+                F.forge_wgrad_accumulate(Xm, dYm, accm, first=(i == 0), stream=sp)
+            else:
+                F.forge_wgrad_step_accumulated(Xm, dYm, accm, W, m, v, h, STEP_T, SEED, stream=sp)
+            if ev is not None:
+                ev[i][1].record(stream)
+
+    run()
+    torch.cuda.synchronize()
+    per = [[] for _ in range(micro)]
+    for _ in range(reps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(micro)]
+        run(ev)
+        torch.cuda.synchronize()
+        for i in range(micro):
+            per[i].append(ev[i][0].elapsed_time(ev[i][1]))
+    med = [sorted(t)[len(t) // 2] for t in per]
+    act = 2 * bt * (N + K) * 2
+    nbytes = [(4 if i == 0 else 8) * N * K + act for i in range(micro - 1)] + [24 * N * K + act]
+    out = {"micro_batches": micro, "tokens_per_micro_batch": bt,
+           "accumulate_first_us": round(1e3 * med[0], 1),
+           "accumulate_add_us": round(1e3 * sum(med[1:-1]) / max(1, micro - 2), 1),
+           "final_fused_step_us": round(1e3 * med[-1], 1),
+           "total_us": round(1e3 * sum(med), 1)}
+    out["hbm_gbs_alg"] = round(sum(nbytes) / (sum(med) * 1e-3) / 1e9, 1)
+    del st, mb, acc, mats
     torch.cuda.empty_cache()
     return out
 
@@ -362,6 +418,8 @@ def main():
 
     if not args.no_family_sweep:
         extras["optimizer_families_gate_proj_bt512"] = family_sweep(F, synth)
+    if not args.no_accumulation:
+        extras["grad_accumulation_gate_proj"] = accumulation_sweep(F, synth, h)
     if not args.no_mfma_sweep:
         extras["compute_bound_sweep"] = mfma_sweep(F, synth, h)
 

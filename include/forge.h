@@ -34,8 +34,10 @@
  *     the caller has already computed the input gradient dX = dY W from the
  *     pre-update W; a weight with more than one gradient consumer in a step
  *     (tied embeddings, expert-parallel experts) must not be stepped here.
- *   - Precondition of the fused schedule: one gradient per step (no
- *     accumulation across micro-batches) and no global gradient-norm clip.
+ *   - Precondition of the fused schedule: no global gradient-norm clip, and
+ *     forge_wgrad_step sees the whole gradient of the step; to accumulate
+ *     micro-batches use forge_wgrad_accumulate and
+ *     forge_wgrad_step_accumulated (paper, Appendix L).
  */
 #ifndef FORGE_H
 #define FORGE_H
@@ -190,6 +192,36 @@ typedef struct {
 
 forge_status forge_wgrad_step_group(const forge_layer* layers, int32_t n, const forge_hyper* h,
                                     int64_t step, void* stream);
+
+/*
+ * Exact gradient accumulation (paper, Appendix L): for an effective batch of
+ * several micro-batches, each micro-step adds its weight gradient into an
+ * fp32 accumulator in device memory, and the fused step fires once, at the
+ * final micro-step, on the summed gradient.
+ *
+ * forge_wgrad_accumulate -- one micro-step: acc = dY^T X (first != 0) or
+ * acc += dY^T X (first == 0), in fp32, with the tiled reduction of the
+ * fused kernels (one fp32 addition of each tile's gradient into acc).
+ * acc: [N, K] F32, caller-owned device buffer, any ld >= K, not overlapping X
+ * or dY.  X, dY as for forge_wgrad_step (BT may be 0: acc = 0 or unchanged).
+ * Errors: FORGE_E_NULL, E_SHAPE, E_DTYPE (acc not F32; X, dY as for
+ * forge_wgrad_step), E_ALIGN, E_ALIAS (nothing enqueued) or E_HIP.
+ */
+forge_status forge_wgrad_accumulate(const forge_mat* X, const forge_mat* dY, forge_mat* acc, int32_t first,
+                                    void* stream);
+
+/*
+ * forge_wgrad_step_accumulated -- the final micro-step: G = acc + dY^T X
+ * (this micro-batch's gradient), then exactly the step of forge_wgrad_step
+ * on G (same arguments, formats, rules and errors).  acc must not overlap
+ * any other argument.  acc is consumed: its contents are unspecified after
+ * the call (aligned bf16 inputs read it inside the fused kernel; other
+ * layouts first add this micro-batch into it and then step from it, with
+ * the same fp32 addition, so the result is the same either way).
+ */
+forge_status forge_wgrad_step_accumulated(const forge_mat* X, const forge_mat* dY, forge_mat* acc, forge_mat* W,
+                                          forge_state* m, forge_state* v, const forge_hyper* h, int64_t step,
+                                          uint64_t seed, void* stream);
 
 /*
  * forge_wgrad_check -- the validation of forge_wgrad_step alone: same

@@ -276,7 +276,7 @@ def weight_grad_abs(X, dY, rows=None, cols=None) -> np.ndarray:
     return np.abs(_as_f64(dY[:, rows])).T @ np.abs(_as_f64(X[:, cols]))
 
 
-def grad_error_bound(X, dY, rows=None, cols=None) -> np.ndarray:
+def grad_error_bound(X, dY, rows=None, cols=None, extra_terms: int = 0) -> np.ndarray:
     """Largest deviation of an fp32-accumulated G from the exact one.
 
     Corollary 1(b): against any other implementation the only discrepancy is
@@ -285,9 +285,11 @@ def grad_error_bound(X, dY, rows=None, cols=None) -> np.ndarray:
     ``|G_hat - G| <= gamma_n * sum_t |dY X|`` with ``gamma_n = n u/(1 - n u)``,
     u = 2^-24 and n the number of terms (+1 for a rounded fp32 product).  The
     bound is doubled so that accumulators which truncate instead of rounding
-    are covered too.
+    are covered too.  ``extra_terms`` counts further fp32 additions of
+    partial sums (gradient accumulation over micro-batches, Appendix L: one
+    per micro-batch), each of which adds at most u * sum_t |dY X|.
     """
-    n = X.shape[0] + 1
+    n = X.shape[0] + 1 + extra_terms
     u = 2.0 ** -24
     gamma = n * u / (1.0 - n * u)
     return 2.0 * gamma * weight_grad_abs(X, dY, rows, cols)

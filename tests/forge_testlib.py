@@ -117,6 +117,7 @@ class Snap:
     W: O.Stored
     m: Optional[O.Stored]
     v: Optional[O.Stored]
+    extra_terms: int = 0      # fp32 additions of partial gradients (micro-batch accumulation)
 
 
 def _stored(t, fmt, scale, block, rows):
@@ -162,7 +163,7 @@ def _hull(snap: Snap, hyp: O.Hyper, step: int, seed: int, c0: int, c1: int, K: i
     rows_local = np.arange(len(snap.rows))
     cols = np.arange(c0, c1)
     G = O.weight_grad(snap.X, snap.dY, rows_local, cols)
-    E = O.grad_error_bound(snap.X, snap.dY, rows_local, cols)
+    E = O.grad_error_bound(snap.X, snap.dY, rows_local, cols, snap.extra_terms)
     flat = snap.rows.astype(np.uint64)[:, None] * np.uint64(K) + cols.astype(np.uint64)[None, :]
     ref = O.apply_step(G, snap.W, snap.m, snap.v, hyp, step, seed, rows_local, c0, c1, flat)
     lo = {k: v.copy() for k, v in ref["pre"].items() if v is not None}

@@ -322,3 +322,42 @@ def test_family_hyper_ranges():
     h = F.hyper("sgd")
     h.opt = 8
     assert check(X, dY, W, None, None, h) == F.FORGE_E_HYPER
+
+
+# ---------------------------------------------------------------------------
+# Gradient accumulation entry points (validation only; no device call)
+# ---------------------------------------------------------------------------
+def _acc(N=256, K=256, dtype=F.FORGE_F32, slot=7):
+    return F.mat_raw(addr(slot), dtype, N, K)
+
+
+def test_accumulate_validation():
+    X, dY, W, m, v = layer()
+    acc = lambda *a, **k: F.forge_wgrad_accumulate(*a, stream=0, check=False, **k)
+    assert acc(X, dY, _acc(dtype=F.FORGE_BF16), True) == F.FORGE_E_DTYPE
+    assert acc(X, dY, _acc(N=255), True) == F.FORGE_E_SHAPE
+    bad = _acc()
+    bad.data = X.data                                   # on top of X
+    assert acc(X, dY, bad, False) == F.FORGE_E_ALIAS
+    assert F.lib.forge_wgrad_accumulate(F._ref(X), F._ref(dY), None, 1, None) == F.FORGE_E_NULL
+    Xe, dYe, *_ = layer(N=0)
+    assert acc(Xe, dYe, _acc(N=0), True) == F.FORGE_OK  # nothing to do, nothing launched
+
+
+def test_step_accumulated_validation():
+    X, dY, W, m, v = layer()
+    step = lambda a, *r, **k: F.forge_wgrad_step_accumulated(X, dY, a, W, m, v, F.hyper(), 10, 1, stream=0,
+                                                              check=False)
+    bad = _acc()
+    bad.data = W.data                                   # on top of W
+    assert step(bad) == F.FORGE_E_ALIAS
+    bad = _acc()
+    bad.data = m.q.data
+    assert step(bad) == F.FORGE_E_ALIAS
+    assert step(_acc(dtype=F.FORGE_BF16)) == F.FORGE_E_DTYPE
+    assert step(_acc(K=128)) == F.FORGE_E_SHAPE
+    # the step's own rules still apply
+    assert F.forge_wgrad_step_accumulated(X, dY, _acc(), W, m, None, F.hyper(), 10, 1, stream=0,
+                                          check=False) == F.FORGE_E_NULL
+    assert F.forge_wgrad_step_accumulated(X, dY, _acc(), W, m, v, F.hyper(), 0, 1, stream=0,
+                                          check=False) == F.FORGE_E_STEP
