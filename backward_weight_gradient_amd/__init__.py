@@ -101,6 +101,12 @@ def _load() -> ctypes.CDLL:
                                                  P(forge_state), P(forge_state), P(forge_hyper), ctypes.c_int64,
                                                  ctypes.c_uint64, ctypes.c_void_p]
     lib.forge_wgrad_step_accumulated.restype = st
+    lib.forge_dgrad.argtypes = [P(forge_mat), P(forge_mat), P(forge_mat), ctypes.c_void_p]
+    lib.forge_dgrad.restype = st
+    lib.forge_backward_step.argtypes = [P(forge_mat), P(forge_mat), P(forge_mat), P(forge_state), P(forge_state),
+                                        P(forge_hyper), ctypes.c_int64, ctypes.c_uint64, P(forge_mat),
+                                        ctypes.c_void_p]
+    lib.forge_backward_step.restype = st
     lib.forge_status_str.argtypes = [ctypes.c_int]
     lib.forge_status_str.restype = ctypes.c_char_p
     lib.forge_version.argtypes = []
@@ -251,6 +257,31 @@ def forge_wgrad_step_accumulated(X, dY, acc, W, m, v, h: forge_hyper, step: int,
                                           seed, _stream(stream))
     if check and rc != FORGE_OK:
         raise ForgeError(rc, "forge_wgrad_step_accumulated")
+    return rc
+
+
+def forge_dgrad(dY, W, dX, stream=None, check: bool = True) -> int:
+    """dX = dY W (the input gradient), fp32 accumulation; dX bf16 (RNE) or f32."""
+    dY = mat(dY) if not isinstance(dY, forge_mat) else dY
+    W = mat(W) if not isinstance(W, forge_mat) else W
+    dX = mat(dX) if not isinstance(dX, forge_mat) else dX
+    rc = lib.forge_dgrad(_ref(dY), _ref(W), _ref(dX), _stream(stream))
+    if check and rc != FORGE_OK:
+        raise ForgeError(rc, "forge_dgrad")
+    return rc
+
+
+def forge_backward_step(X, dY, W, m, v, h: forge_hyper, step: int, seed: int, dX, stream=None,
+                        check: bool = True) -> int:
+    """dX = dY W from the current W, then the fused weight-gradient step, in that order."""
+    X = mat(X) if not isinstance(X, forge_mat) else X
+    dY = mat(dY) if not isinstance(dY, forge_mat) else dY
+    W = mat(W) if not isinstance(W, forge_mat) else W
+    dX = mat(dX) if not isinstance(dX, forge_mat) else dX
+    rc = lib.forge_backward_step(_ref(X), _ref(dY), _ref(W), _ref(m), _ref(v), _ref(h), step, seed, _ref(dX),
+                                 _stream(stream))
+    if check and rc != FORGE_OK:
+        raise ForgeError(rc, "forge_backward_step")
     return rc
 
 

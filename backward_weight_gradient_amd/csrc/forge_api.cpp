@@ -227,6 +227,36 @@ bool vec_ok(const void* p, int64_t ld, int elems, int es) {
   return p == nullptr || (aligned(p, elems * es) && (ld % elems) == 0);
 }
 
+// dX = dY W: shapes, dtypes, limits, aliasing; fills the launch arguments.
+forge_status check_dgrad(const forge_mat* dY, const forge_mat* W, const forge_mat* dX, DgArgs& g, bool& fast) {
+  if (!dY || !W || !dX) return FORGE_E_NULL;
+  const int64_t BT = dY->rows, N = dY->cols, K = W->cols;
+  if (BT < 0 || N < 0 || K < 0) return FORGE_E_SHAPE;
+  forge_status st;
+  if ((st = check_mat(*dY, BT, N)) != FORGE_OK) return st;
+  if ((st = check_mat(*W, N, K)) != FORGE_OK) return st;
+  if ((st = check_mat(*dX, BT, K)) != FORGE_OK) return st;
+  for (const forge_mat* t : {dY, W, dX})
+    if (t->dtype != FORGE_F32 && t->dtype != FORGE_BF16) return FORGE_E_DTYPE;
+  if (BT >= (1ll << 31) || N >= (1ll << 31) || K >= (1ll << 31)) return FORGE_E_SHAPE;
+  if (((BT + 127) / 128) * ((K + 127) / 128) >= (1ll << 31)) return FORGE_E_SHAPE;
+  const Range out = mat_range(*dX);
+  if (overlap(out, mat_range(*dY)) || overlap(out, mat_range(*W))) return FORGE_E_ALIAS;
+  std::memset(&g, 0, sizeof(g));
+  g.dY = dY->data; g.lddy = dY->ld;
+  g.W = W->data; g.ldw = W->ld;
+  g.dX = dX->data; g.ldx = dX->ld;
+  g.BT = (int32_t)BT; g.N = (int32_t)N; g.K = (int32_t)K;
+  g.tiles_m = (int32_t)((BT + 127) / 128);
+  g.tiles_k = (int32_t)((K + 127) / 128);
+  g.in_fmt = dY->dtype; g.w_fmt = W->dtype; g.dx_fmt = dX->dtype;
+  g.vec_out = vec_ok(dX->data, dX->ld, 4, elem_size(dX->dtype)) ? 1 : 0;
+  fast = dY->dtype == FORGE_BF16 && W->dtype == FORGE_BF16 && N % 8 == 0 && K % 8 == 0 &&
+         vec_ok(dY->data, dY->ld, 8, 2) && vec_ok(W->data, W->ld, 8, 2) &&
+         (uint64_t)BT * (uint64_t)dY->ld * 2 < (1ull << 31) && (uint64_t)N * (uint64_t)W->ld * 2 < (1ull << 31);
+  return FORGE_OK;
+}
+
 // The activation half of a launch: X, dY, sizes, tile counts, loader choice.
 void input_args(const forge_mat* X, const forge_mat* dY, const Plan& pl, KArgs& a) {
   a.X = X->data; a.ldx = X->ld;
@@ -475,6 +505,37 @@ forge_status forge_wgrad_step_accumulated(const forge_mat* X, const forge_mat* d
   hipError_t e = launch_gemm(a, pl.in_fmt, (hipStream_t)stream);
   if (e == hipSuccess) e = launch_step(a, pl.w_fmt, h->opt, pl.m_fmt, pl.v_fmt, (hipStream_t)stream);
   return hip_status(e);
+}
+
+forge_status forge_dgrad(const forge_mat* dY, const forge_mat* W, forge_mat* dX, void* stream) {
+  DgArgs g;
+  bool fast = false;
+  const forge_status st = check_dgrad(dY, W, dX, g, fast);
+  if (st != FORGE_OK) return st;
+  return hip_status(launch_dgrad(g, fast, (hipStream_t)stream));
+}
+
+forge_status forge_backward_step(const forge_mat* X, const forge_mat* dY, forge_mat* W, forge_state* m, forge_state* v,
+                                 const forge_hyper* h, int64_t step, uint64_t seed, forge_mat* dX, void* stream) {
+  Plan pl;
+  forge_status st = validate(X, dY, W, m, v, h, step, pl);
+  if (st != FORGE_OK) return st;
+  DgArgs g;
+  bool fast = false;
+  if ((st = check_dgrad(dY, W, dX, g, fast)) != FORGE_OK) return st;
+  Range outs[5], ins[2];
+  layer_ranges(X, dY, W, m, v, pl, outs, ins);
+  const Range rx = mat_range(*dX);
+  for (const Range& r : outs)
+    if (overlap(rx, r)) return FORGE_E_ALIAS;
+  for (const Range& r : ins)
+    if (overlap(rx, r)) return FORGE_E_ALIAS;
+  // stream order is the contract: dX reads W before the fused step rewrites it
+  hipError_t e = launch_dgrad(g, fast, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e);
+  if (pl.empty) return FORGE_OK;
+  const KArgs a = make_args(X, dY, W, m, v, h, step, seed, pl);
+  return hip_status(launch_fused(a, pl.in_fmt, pl.w_fmt, h->opt, pl.m_fmt, pl.v_fmt, (hipStream_t)stream));
 }
 
 forge_status forge_debug_sr_bf16(const float* in, uint16_t* out, int64_t n, uint64_t seed, int64_t step,

@@ -104,6 +104,19 @@ constexpr int WIDE_MIN_BT = 3072;  // token count from which the 256 x 256 kerne
 #define FORGE_STATE_LIST(X) \
   FORGE_ADAMW_LIST(X) FORGE_LION_LIST(X) FORGE_SGDM_LIST(X) FORGE_ADAM_VARIANT_LIST(X) FORGE_SECOND_MOMENT_LIST(X)
 
+// The input-gradient GEMM dX = dY W (dY [BT, N], W [N, K], dX [BT, K]).
+struct DgArgs {
+  const void* dY; int64_t lddy;
+  const void* W; int64_t ldw;
+  void* dX; int64_t ldx;
+  int32_t BT, N, K;
+  int32_t tiles_m, tiles_k;       // ceil(BT/128), ceil(K/128) (MFMA kernel)
+  int32_t in_fmt, w_fmt, dx_fmt;  // dtypes of dY, W, dX
+  int32_t vec_out;                // dX rows allow 4-element vector stores
+};
+// forge_k_dgrad.hip: fast = bf16 dY and W with 16-byte aligned rows, N and K multiples of 8.
+hipError_t launch_dgrad(const DgArgs& g, bool fast, hipStream_t stream);
+
 inline bool combo_supported(int in_fmt, int w_fmt, int opt, int m_fmt, int v_fmt) {
   if (in_fmt != FMT_F32 && in_fmt != FMT_BF16) return false;
   if (w_fmt != FMT_F32 && w_fmt != FMT_BF16) return false;

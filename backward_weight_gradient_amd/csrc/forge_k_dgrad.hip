@@ -1,0 +1,307 @@
+// The input gradient of a linear layer, dX = dY W (FORGE paper, Appendix A,
+// Remark 1: it must be formed from the weight before the fused step
+// overwrites it).  dY [BT, N], W [N, K], dX [BT, K], reduction over N in
+// fp32.
+//
+// k_dgrad_bf16<TM> (bf16 dY and W, 16-byte aligned rows, N and K multiples
+// of 8): one TM x 128 tile of dX per 256-thread workgroup (4 waves, 2 x 2
+// arrangement of TM/2 x 64; TM = 64 when 128-token tiles would leave CUs
+// idle, as for q/gate/up at BT = 512), v_mfma_f32_32x32x16_bf16 over chunks
+// of 32 of the reduction index, both operands brought into a 4-stage LDS
+// ring by
+// buffer_load ... lds.  W's chunk (32 rows of W, 128 columns) has the
+// reduction index as its row, like the weight-gradient operands, and is
+// read with the transposing LDS read; dY's chunk (128 tokens, 32 reduction
+// elements) has the reduction index along the row and is read 16 bytes per
+// lane, its 64-byte rows XOR-swizzled in 16-byte units so that 16 lanes
+// reading 16 consecutive rows cover all 64 banks.
+//
+// k_dgrad_generic (any dtype combination, any alignment): 64 x 64 tiles, fp32
+// FMA from an LDS-staged fp32 copy of both operands.
+
+#include "forge_device.h"
+
+namespace forge {
+
+namespace {
+
+constexpr int DG_TN = 32;                            // reduction elements per chunk
+constexpr int DG_OPB = 8192;                         // bytes of W's chunk per stage (32 x 128 bf16)
+
+// TM-token tiles with an S-stage ring (S - 1 chunks in flight).
+template <int TM, int S>
+struct DgShape {
+  static constexpr int APB = TM * DG_TN * 2;         // bytes of dY's chunk per stage
+  static constexpr int STAGE = APB + DG_OPB;
+  static constexpr int ABLK = TM / 64;               // dY loads per wave per chunk (1 KiB each)
+  static constexpr int LOADS = ABLK + 2;             // buffer loads per wave per chunk
+  static constexpr int GP_ = TILE + 4;               // fp32 pitch of the staged output tile
+  static constexpr int LDS = (S * STAGE > TM * GP_ * 4) ? S * STAGE : TM * GP_ * 4;
+};
+
+// Wait until at most `ahead` chunks' loads (LOADS each) are still in flight.
+template <int LOADS, int K>
+__device__ __forceinline__ void dg_wait_ahead(int ahead) {
+  if constexpr (K == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (ahead >= K) wait_vmcnt<K * LOADS>();
+    else dg_wait_ahead<LOADS, K - 1>(ahead);
+  }
+}
+
+// Byte offset of (token row m, 16-byte segment s) in dY's chunk region.
+__device__ __forceinline__ uint32_t dg_a_off(int m, int s) { return (uint32_t)(m * 64 + ((s ^ ((m >> 2) & 3)) << 4)); }
+
+template <int TM, int S>
+struct DgradLoader {
+  using SH = DgShape<TM, S>;
+  __amdgpu_buffer_rsrc_t rA, rB;
+  uint32_t oobA, oobB;
+  uint32_t aTok[SH::ABLK], aSeg[SH::ABLK];   // dY: byte offset of this lane's token row, 16-byte segment
+  bool aOk[SH::ABLK];
+  uint32_t bCol[2];            // W: byte offset of this lane's 8-column chunk
+  int bRow[2];                 // W: row within the chunk
+  bool bOk[2];
+  int wave;
+
+  __device__ __forceinline__ void init(const DgArgs& g, int tok0, int col0) {
+    const int lane = threadIdx.x & 63;
+    wave = threadIdx.x >> 6;
+    oobA = (uint32_t)((uint64_t)g.BT * g.lddy * 2);
+    oobB = (uint32_t)((uint64_t)g.N * g.ldw * 2);
+    rA = make_rsrc(g.dY, oobA);
+    rB = make_rsrc(g.W, oobB);
+#pragma unroll
+    for (int r = 0; r < SH::ABLK; ++r) {
+      // dY: 1 KiB block = 16 token rows x 4 segments; lane -> (row, physical segment)
+      const int blk = SH::ABLK * wave + r;
+      const int m = blk * 16 + (lane >> 2);
+      const int s = (lane & 3) ^ ((m >> 2) & 3);       // logical segment stored at this slot
+      aOk[r] = tok0 + m < g.BT;
+      aTok[r] = (uint32_t)((uint64_t)(tok0 + m) * g.lddy * 2);
+      aSeg[r] = (uint32_t)(s * 16);
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      // W: 1 KiB block = 4 rows x 16 chunks of 8 columns, rows XOR-swizzled as
+      // the weight-gradient operands (MainBF16::off)
+      const int blk = 2 * wave + r;
+      const int t = blk * 4 + (lane >> 4);
+      const int c = (lane & 15) ^ ((t & 3) << 2);
+      bRow[r] = t;
+      bOk[r] = col0 + c * 8 < g.K;
+      bCol[r] = (uint32_t)(col0 + c * 8) * 2;
+    }
+  }
+
+  __device__ __forceinline__ void issue(const DgArgs& g, int kc, char* stage) const {
+    const int n0 = kc * DG_TN;
+#pragma unroll
+    for (int r = 0; r < SH::ABLK; ++r) {
+      const uint32_t oa = (aOk[r] && n0 + (int)(aSeg[r] >> 1) < g.N) ? aTok[r] + (uint32_t)n0 * 2 + aSeg[r] : oobA;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void*)(stage + (SH::ABLK * wave + r) * 1024), 16, oa, 0, 0,
+                                               0);
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int n = n0 + bRow[r];
+      const uint32_t ob = (bOk[r] && n < g.N) ? (uint32_t)n * (uint32_t)(g.ldw * 2) + bCol[r] : oobB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void*)(stage + SH::APB + (2 * wave + r) * 1024), 16, ob, 0,
+                                               0, 0);
+    }
+  }
+};
+
+__device__ __forceinline__ u32x4 ds_read_16(uint32_t addr) {
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+  return v;
+}
+
+__device__ __forceinline__ void dg_wait(u32x4 (&a)[2], u32x2 (&b)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(a[0]), "+v"(a[1]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]));
+}
+__device__ __forceinline__ void dg_wait(u32x4 (&a)[1], u32x2 (&b)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]));
+}
+
+
+}  // namespace
+
+template <int TM, int S>
+__global__ void __launch_bounds__(NT, 2) k_dgrad_bf16(const DgArgs g) {
+  using SH = DgShape<TM, S>;
+  constexpr int BI = TM / 64;                        // 32-row MFMA blocks per wave
+  __shared__ __attribute__((aligned(16))) char lds[SH::LDS];
+  // W panels are shared by the token tiles of one column: those run together
+  const int tiles_m = (g.BT + TM - 1) / TM;
+  const int tj = (int)blockIdx.x / tiles_m, ti = (int)blockIdx.x - tj * tiles_m;
+  const int tok0 = ti * TM, col0 = tj * TILE;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)lds;
+  f32x16 acc[BI][2];
+#pragma unroll
+  for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[bi][bj][e] = 0.f;
+  const int nk = (g.N + DG_TN - 1) / DG_TN;
+  DgradLoader<TM, S> ld;
+  ld.init(g, tok0, col0);
+#pragma unroll
+  for (int k = 0; k < S - 1; ++k)
+    if (k < nk) ld.issue(g, k, lds + k * SH::STAGE);
+  for (int kc = 0; kc < nk; ++kc) {
+    dg_wait_ahead<SH::LOADS, S - 2>(min(S - 2, nk - 1 - kc));   // chunk kc landed
+    bar();
+    if (kc + S - 1 < nk) ld.issue(g, kc + S - 1, lds + ((kc + S - 1) % S) * SH::STAGE);
+    const uint32_t cur = lds0 + (uint32_t)((kc % S) * SH::STAGE);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      u32x4 af[BI];
+      u32x2 bf[4];
+#pragma unroll
+      for (int bi = 0; bi < BI; ++bi) {
+        const int m = wr * (TM / 2) + bi * 32 + (lane & 31);
+        af[bi] = ds_read_16(cur + dg_a_off(m, 2 * ks + (lane >> 5)));
+      }
+#pragma unroll
+      for (int bj = 0; bj < 2; ++bj)
+        frag_issue(cur + SH::APB, 16 * ks, wc * 64 + bj * 32, lane, bf[2 * bj], bf[2 * bj + 1]);
+      dg_wait(af, bf);
+#pragma unroll
+      for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj)
+          acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[bi]),
+                                                                frag_join(bf[2 * bj], bf[2 * bj + 1]),
+                                                                acc[bi][bj], 0, 0, 0);
+    }
+  }
+  wait_vmcnt<0>();
+  bar();
+  // stage the fp32 tile: lane l, register 4j+i of a 32 x 32 block holds row 8j + 4(l/32) + i, column l % 32
+  float* sG = reinterpret_cast<float*>(lds);
+#pragma unroll
+  for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = wr * (TM / 2) + bi * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        const int c = wc * 64 + bj * 32 + (lane & 31);
+        sG[r * SH::GP_ + c] = acc[bi][bj][e];
+      }
+  __syncthreads();
+  // write out: pass s, thread t -> row s*16 + t/16, two 4-column segments 64 apart
+  const int cl = 4 * (threadIdx.x & 15);
+  const bool vec = g.vec_out != 0;
+#pragma unroll
+  for (int s = 0; s < TM / 16; ++s) {
+    const int rl = s * 16 + (threadIdx.x >> 4);
+    const int p = tok0 + rl;
+    if (p >= g.BT) continue;
+    char* rowp = static_cast<char*>(g.dX) + (int64_t)p * g.ldx * (g.dx_fmt == FMT_F32 ? 4 : 2);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      Seg sg;
+      sg.q = col0 + 64 * h + cl;
+      sg.nv = max(0, min(4, g.K - sg.q));
+      sg.ok = sg.nv > 0;
+      if (!sg.ok) continue;
+      float x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = sG[rl * SH::GP_ + 64 * h + cl + i];
+      if (g.dx_fmt == FMT_F32) st4<FMT_F32, false>(rowp, sg, vec, x, 0, 0, 0);
+      else st4<FMT_BF16, false>(rowp, sg, vec, x, 0, 0, 0);
+    }
+  }
+}
+
+namespace {
+constexpr int DGG_T = 64;    // output tile edge of the generic kernel
+constexpr int DGG_R = 16;    // reduction elements per step
+
+__device__ __forceinline__ float ld_elem(const void* base, int fmt, int64_t i) {
+  if (fmt == FMT_F32) return static_cast<const float*>(base)[i];
+  return __uint_as_float((uint32_t)static_cast<const uint16_t*>(base)[i] << 16);
+}
+}  // namespace
+
+__global__ void __launch_bounds__(NT) k_dgrad_generic(const DgArgs g) {
+  __shared__ float sa[DGG_R][DGG_T + 1];   // dY^T chunk: [reduction][token]
+  __shared__ float sb[DGG_R][DGG_T + 1];   // W chunk: [reduction][column]
+  const int tiles_k = (g.K + DGG_T - 1) / DGG_T;
+  const int ti = (int)blockIdx.x / tiles_k, tj = (int)blockIdx.x - ti * tiles_k;
+  const int tok0 = ti * DGG_T, col0 = tj * DGG_T;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;   // 16 x 16 threads, 4 x 4 outputs each
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+  for (int n0 = 0; n0 < g.N; n0 += DGG_R) {
+    for (int e = threadIdx.x; e < DGG_R * DGG_T; e += NT) {
+      const int r = e / DGG_T, c = e - r * DGG_T;
+      const int n = n0 + r;
+      const int tok = tok0 + c, col = col0 + c;
+      sa[r][c] = (n < g.N && tok < g.BT) ? ld_elem(g.dY, g.in_fmt, (int64_t)tok * g.lddy + n) : 0.f;
+      sb[r][c] = (n < g.N && col < g.K) ? ld_elem(g.W, g.w_fmt, (int64_t)n * g.ldw + col) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < DGG_R; ++r) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = sa[r][ty * 4 + i];
+        b[i] = sb[r][tx * 4 + i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tok = tok0 + ty * 4 + i;
+    if (tok >= g.BT) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = col0 + tx * 4 + j;
+      if (col >= g.K) continue;
+      const int64_t o = (int64_t)tok * g.ldx + col;
+      if (g.dx_fmt == FMT_F32) static_cast<float*>(g.dX)[o] = acc[i][j];
+      else static_cast<uint16_t*>(g.dX)[o] = (uint16_t)bf16_rne_bits(acc[i][j]);
+    }
+  }
+}
+
+hipError_t launch_dgrad(const DgArgs& g, bool fast, hipStream_t st) {
+  if (g.BT == 0 || g.K == 0) return hipSuccess;
+  if (fast) {
+    // 128-token tiles, two workgroups per CU; when those would not give every
+    // CU a workgroup (short token axis, few columns), 64-token tiles, up to
+    // three workgroups per CU (measured: a deeper ring does not help them --
+    // with 4 MFMAs per wave and chunk the per-chunk overhead dominates)
+    const int64_t t128 = (int64_t)((g.BT + 127) / 128) * g.tiles_k;
+    if (t128 >= 256) {
+      hipLaunchKernelGGL((k_dgrad_bf16<128, 4>), dim3((unsigned)t128), dim3(NT), 0, st, g);
+    } else {
+      const unsigned t64 = (unsigned)(((g.BT + 63) / 64) * g.tiles_k);
+      hipLaunchKernelGGL((k_dgrad_bf16<64, 4>), dim3(t64), dim3(NT), 0, st, g);
+    }
+  } else {
+    const unsigned tiles = (unsigned)(((g.BT + DGG_T - 1) / DGG_T) * ((g.K + DGG_T - 1) / DGG_T));
+    hipLaunchKernelGGL(k_dgrad_generic, dim3(tiles), dim3(NT), 0, st, g);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace forge

@@ -60,6 +60,8 @@ def parse():
                    help="skip the per-optimizer timing (gate_proj, BT 512, all eight families)")
     p.add_argument("--no-accumulation", action="store_true",
                    help="skip the gradient-accumulation timing (gate_proj, 4 micro-batches of 128 tokens)")
+    p.add_argument("--no-dgrad", action="store_true",
+                   help="skip the input-gradient GEMM timing (dX = dY W for the seven layers at BT 512)")
     p.add_argument("--no-mfma-sweep", action="store_true",
                    help="skip the compute-bound sweep (down_proj, lm_head at BT 2048 / 8192)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -245,6 +247,34 @@ def accumulation_sweep(F, synth, h, micro=4, reps=5):
     return out
 
 
+def dgrad_sweep(F, L, layers, reps=5):
+    """dX = dY W (bf16, fp32 accumulation, bf16 dX) for each layer of the step
+    at BT = 512, from the step's own dY and W (median of `reps` launches)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name, (N, K) in layers.items():
+        d = L[name]
+        dX = torch.empty((BT, K), device="cuda", dtype=torch.bfloat16)
+        dXm = F.mat(dX)
+        F.forge_dgrad(d["dYm"], d["Wm"], dXm, stream=stream.cuda_stream)
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            F.forge_dgrad(d["dYm"], d["Wm"], dXm, stream=stream.cuda_stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        ms = sorted(times)[len(times) // 2]
+        tflops = 2.0 * BT * N * K / (ms * 1e-3) / 1e12
+        out[name] = {"us": round(1e3 * ms, 1), "tflops": round(tflops, 1),
+                     "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4)}
+        del dX
+    return out
+
+
 def cpu_baseline(layers, seconds):
     """The oracle on whole layers (k_proj first, then the others in turn)
     until about `seconds` of CPU time are spent; params/s over them."""
@@ -418,6 +448,8 @@ def main():
 
     if not args.no_family_sweep:
         extras["optimizer_families_gate_proj_bt512"] = family_sweep(F, synth)
+    if not args.no_dgrad:
+        extras["dgrad_bt512"] = dgrad_sweep(F, L, layers)
     if not args.no_accumulation:
         extras["grad_accumulation_gate_proj"] = accumulation_sweep(F, synth, h)
     if not args.no_mfma_sweep:

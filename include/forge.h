@@ -224,6 +224,31 @@ forge_status forge_wgrad_step_accumulated(const forge_mat* X, const forge_mat* d
                                           uint64_t seed, void* stream);
 
 /*
+ * forge_dgrad -- the input gradient dX = dY W of the layer (the GEMM that
+ * must read W before the fused step overwrites it: paper, Appendix A,
+ * Remark 1), fp32 accumulation over N.
+ * dY : [BT, N] BF16 or F32.   W : [N, K] BF16 or F32.
+ * dX : [BT, K] BF16 (round to nearest even) or F32, written; must not
+ *      overlap dY or W.
+ * bf16 dY and W with 16-byte aligned rows and N, K multiples of 8 take the
+ * MFMA kernel; any other combination a plain fp32 kernel.
+ * Errors: FORGE_E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_ALIAS (nothing
+ * enqueued) or E_HIP.
+ */
+forge_status forge_dgrad(const forge_mat* dY, const forge_mat* W, forge_mat* dX, void* stream);
+
+/*
+ * forge_backward_step -- a linear layer's whole weight-side backward in the
+ * order Remark 1 requires: dX = dY W from the current W (forge_dgrad), then
+ * forge_wgrad_step, enqueued in that order on `stream`.  Arguments as for
+ * the two calls; dX must not overlap any other buffer.  Errors: those of
+ * both calls, all checked before anything is enqueued, or E_HIP.
+ */
+forge_status forge_backward_step(const forge_mat* X, const forge_mat* dY, forge_mat* W, forge_state* m,
+                                 forge_state* v, const forge_hyper* h, int64_t step, uint64_t seed,
+                                 forge_mat* dX, void* stream);
+
+/*
  * forge_wgrad_check -- the validation of forge_wgrad_step alone: same
  * arguments, same return codes, no device call at all (usable on a host
  * without a GPU).

@@ -83,7 +83,7 @@ __all__ = [
     "Stored", "Hyper",
     "bf16_bits_to_f64", "f32_to_bf16_rne", "f32_to_bf16_sr",
     "fmix32", "sr_key", "sr_bits",
-    "weight_grad", "weight_grad_abs", "grad_error_bound",
+    "weight_grad", "weight_grad_abs", "grad_error_bound", "input_grad", "input_grad_error_bound",
     "adamw", "lion", "sgdm", "nadam", "radam", "rmsprop", "adagrad", "sgd",
     "nadam_mu", "radam_rect",
     "quantize_signed", "quantize_unsigned", "dequantize",
@@ -293,6 +293,25 @@ def grad_error_bound(X, dY, rows=None, cols=None, extra_terms: int = 0) -> np.nd
     u = 2.0 ** -24
     gamma = n * u / (1.0 - n * u)
     return 2.0 * gamma * weight_grad_abs(X, dY, rows, cols)
+
+
+def input_grad(dY: np.ndarray, W: np.ndarray, rows=None) -> np.ndarray:
+    """The input gradient dX[t, q] = sum_p dY[t, p] W[p, q] (the GEMM that
+    Remark 1 orders before the in-place update) for tokens t in ``rows``;
+    dY [BT, N], W [N, K], float32 or uint16 bf16 bits.  fp64 library matmul:
+    every product is exact in fp64."""
+    rows = np.arange(dY.shape[0]) if rows is None else np.asarray(rows)
+    return _as_f64(dY[rows]) @ _as_f64(W)
+
+
+def input_grad_error_bound(dY: np.ndarray, W: np.ndarray, rows=None) -> np.ndarray:
+    """Largest deviation of an fp32-accumulated dX from the exact one in any
+    summation order: 2 gamma_{N+1} sum_p |dY W| (as grad_error_bound)."""
+    rows = np.arange(dY.shape[0]) if rows is None else np.asarray(rows)
+    n = dY.shape[1] + 1
+    u = 2.0 ** -24
+    gamma = n * u / (1.0 - n * u)
+    return 2.0 * gamma * (np.abs(_as_f64(dY[rows])) @ np.abs(_as_f64(W)))
 
 
 # --------------------------------------------------------------------------

@@ -361,3 +361,29 @@ def test_step_accumulated_validation():
                                           check=False) == F.FORGE_E_NULL
     assert F.forge_wgrad_step_accumulated(X, dY, _acc(), W, m, v, F.hyper(), 0, 1, stream=0,
                                           check=False) == F.FORGE_E_STEP
+
+
+# ---------------------------------------------------------------------------
+# dX = dY W and the ordered backward step (validation only)
+# ---------------------------------------------------------------------------
+def test_dgrad_validation():
+    X, dY, W, m, v = layer()                     # dY [64, 256], W [256, 256]
+    dX = F.mat_raw(addr(7), F.FORGE_BF16, 64, 256)
+    dg = lambda a, b, c: F.forge_dgrad(a, b, c, stream=0, check=False)
+    bad = F.mat_raw(W.data, F.FORGE_BF16, 64, 256)                     # on top of W
+    assert dg(dY, W, bad) == F.FORGE_E_ALIAS
+    assert dg(dY, W, F.mat_raw(addr(7), F.FORGE_S8, 64, 256)) == F.FORGE_E_DTYPE
+    assert dg(dY, W, F.mat_raw(addr(7), F.FORGE_BF16, 63, 256)) == F.FORGE_E_SHAPE
+    assert dg(dY, F.mat_raw(addr(2), F.FORGE_BF16, 255, 256), dX) == F.FORGE_E_SHAPE
+    assert F.lib.forge_dgrad(F._ref(dY), F._ref(W), None, None) == F.FORGE_E_NULL
+    # an empty output needs no launch
+    assert dg(F.mat_raw(addr(1), F.FORGE_BF16, 0, 256), W, F.mat_raw(addr(7), F.FORGE_BF16, 0, 256)) == F.FORGE_OK
+
+
+def test_backward_step_validation():
+    X, dY, W, m, v = layer()
+    bs = lambda dX, **k: F.forge_backward_step(X, dY, W, m, v, F.hyper(), k.get("step", 10), 1, dX, stream=0,
+                                               check=False)
+    assert bs(F.mat_raw(m.q.data, F.FORGE_BF16, 64, 256)) == F.FORGE_E_ALIAS   # on top of m
+    assert bs(F.mat_raw(X.data, F.FORGE_BF16, 64, 256)) == F.FORGE_E_ALIAS     # on top of X
+    assert bs(F.mat_raw(addr(7), F.FORGE_BF16, 64, 256), step=0) == F.FORGE_E_STEP

@@ -603,3 +603,39 @@ def test_radam_rectification_limits():
     assert [O.radam_rect(t, 0.999)[0] for t in range(1, 8)] == [False] * 5 + [True] * 2
     on, r = O.radam_rect(10 ** 7, 0.999)
     assert on and abs(r - 1.0) < 1e-6
+
+
+# ---------------------------------------------------------------------------
+# Input gradient dX = dY W (Remark 1's upstream GEMM)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("in_dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("BT,N,K", [(1, 1, 1), (2, 3, 9), (3, 9, 4), (7, 5, 130)])
+def test_input_grad_brute_force(BT, N, K, in_dtype):
+    """dX[t, q] = sum_p dY[t, p] W[p, q] against an exact integer triple loop;
+    non-square shapes make a transposed operand fail."""
+    rng = np.random.default_rng(BT * 77 + N * 7 + K)
+    dYi = rng.integers(-64, 64, size=(BT, N))
+    Wi = rng.integers(-64, 64, size=(N, K))
+    dYt = torch.tensor(dYi, dtype=torch.float32) * 2.0 ** -6
+    Wt = torch.tensor(Wi, dtype=torch.float32) * 2.0 ** -4
+    if in_dtype == "bf16":
+        dY = dYt.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        W = Wt.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    else:
+        dY, W = dYt.numpy(), Wt.numpy()
+    exact = np.array([[float(Fraction(sum(int(dYi[t, p]) * int(Wi[p, q]) for p in range(N)), 1024))
+                       for q in range(K)] for t in range(BT)])
+    np.testing.assert_array_equal(O.input_grad(dY, W), exact)
+    rows = np.array([BT - 1, 0])
+    np.testing.assert_array_equal(O.input_grad(dY, W, rows), exact[rows])
+
+
+def test_input_grad_error_bound_covers_fp32_order():
+    rng = np.random.default_rng(8)
+    dY = (rng.normal(size=(40, 700)) * 1e-3).astype(np.float32)
+    W = (rng.normal(size=(700, 30)) * 0.02).astype(np.float32)
+    ref = O.input_grad(dY, W)
+    acc = np.zeros((40, 30), dtype=np.float32)
+    for p in range(700):                       # one fp32 order: p ascending
+        acc = acc + np.multiply.outer(dY[:, p], W[p])
+    assert np.all(np.abs(acc.astype(np.float64) - ref) <= O.input_grad_error_bound(dY, W))
