@@ -31,7 +31,7 @@ STATUS_NAMES = ["FORGE_OK", "FORGE_E_NULL", "FORGE_E_SHAPE", "FORGE_E_DTYPE", "F
 (FORGE_E_NULL, FORGE_E_SHAPE, FORGE_E_DTYPE, FORGE_E_ALIGN, FORGE_E_STEP, FORGE_E_HYPER,
  FORGE_E_ALIAS, FORGE_E_UNSUPPORTED, FORGE_E_HIP) = range(1, 10)
 
-FORGE_F32, FORGE_BF16, FORGE_S8, FORGE_U8 = 0, 1, 2, 3
+FORGE_F32, FORGE_BF16, FORGE_S8, FORGE_U8, FORGE_E4M3 = 0, 1, 2, 3, 4
 FORGE_ADAMW, FORGE_LION, FORGE_SGDM, FORGE_NADAM, FORGE_RADAM, FORGE_RMSPROP, FORGE_ADAGRAD, FORGE_SGD = range(8)
 FORGE_ROUND_RNE, FORGE_ROUND_SR = 0, 1
 OPTIMIZERS = {"adamw": FORGE_ADAMW, "lion": FORGE_LION, "sgdm": FORGE_SGDM, "nadam": FORGE_NADAM,
@@ -107,6 +107,8 @@ def _load() -> ctypes.CDLL:
                                         P(forge_hyper), ctypes.c_int64, ctypes.c_uint64, P(forge_mat),
                                         ctypes.c_void_p]
     lib.forge_backward_step.restype = st
+    lib.forge_debug_e4m3.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.forge_debug_e4m3.restype = st
     lib.forge_status_str.argtypes = [ctypes.c_int]
     lib.forge_status_str.restype = ctypes.c_char_p
     lib.forge_version.argtypes = []
@@ -124,7 +126,8 @@ lib = _load()
 # ---------------------------------------------------------------------------
 def _dtype_code(t) -> int:
     import torch
-    codes = {torch.float32: FORGE_F32, torch.bfloat16: FORGE_BF16, torch.int8: FORGE_S8, torch.uint8: FORGE_U8}
+    codes = {torch.float32: FORGE_F32, torch.bfloat16: FORGE_BF16, torch.int8: FORGE_S8, torch.uint8: FORGE_U8,
+             torch.float8_e4m3fn: FORGE_E4M3}
     if t.dtype not in codes:
         raise TypeError(f"unsupported tensor dtype {t.dtype}")
     return codes[t.dtype]
@@ -295,6 +298,14 @@ def forge_wgrad_unfused(X, dY, W, m, v, h: forge_hyper, step: int, seed: int, dW
                                  dW.data_ptr(), _dtype_code(dW), _stream(stream))
     if check and rc != FORGE_OK:
         raise ForgeError(rc, "forge_wgrad_unfused")
+    return rc
+
+
+def forge_debug_e4m3(inp, out, stream=None, check: bool = True) -> int:
+    """E4M3 rounding of a float32 tensor into a uint8 code tensor (test hook)."""
+    rc = lib.forge_debug_e4m3(inp.data_ptr(), out.data_ptr(), inp.numel(), _stream(stream))
+    if check and rc != FORGE_OK:
+        raise ForgeError(rc, "forge_debug_e4m3")
     return rc
 
 

@@ -42,7 +42,8 @@ int elem_size(int dtype) {
     case FORGE_F32: return 4;
     case FORGE_BF16: return 2;
     case FORGE_S8:
-    case FORGE_U8: return 1;
+    case FORGE_U8:
+    case FORGE_E4M3: return 1;
     default: return 0;
   }
 }
@@ -103,7 +104,8 @@ forge_status check_state(const forge_state& s, int64_t N, int64_t K, bool first,
   forge_status st = check_mat(s.q, N, K);
   if (st != FORGE_OK) return st;
   const int dt = s.q.dtype;
-  const bool int8 = first ? dt == FORGE_S8 : dt == FORGE_U8;
+  // 8-bit codes with block scales: S8 (first moment) / U8 (second) / E4M3 (either)
+  const bool int8 = (first ? dt == FORGE_S8 : dt == FORGE_U8) || dt == FORGE_E4M3;
   if (!(dt == FORGE_F32 || dt == FORGE_BF16 || int8)) return FORGE_E_DTYPE;
   if (int8) {
     if (!(s.block == 32 || s.block == 64 || s.block == 128)) return FORGE_E_SHAPE;
@@ -548,6 +550,15 @@ forge_status forge_debug_sr_bf16(const float* in, uint16_t* out, int64_t n, uint
   if (overlap(raw_range(in, (uint64_t)n * 4), raw_range(out, (uint64_t)n * 2))) return FORGE_E_ALIAS;
   const uint32_t key = sr_key(seed, (uint64_t)step, tensor_id);
   return hip_status(launch_debug_sr(in, out, (uint32_t)n, key, (hipStream_t)stream));
+}
+
+forge_status forge_debug_e4m3(const float* in, uint8_t* out, int64_t n, void* stream) {
+  if (n < 0 || (uint64_t)n >= (1ull << 32)) return FORGE_E_SHAPE;
+  if (n == 0) return FORGE_OK;
+  if (!in || !out) return FORGE_E_NULL;
+  if (!aligned(in, 4)) return FORGE_E_ALIGN;
+  if (overlap(raw_range(in, (uint64_t)n * 4), raw_range(out, (uint64_t)n))) return FORGE_E_ALIAS;
+  return hip_status(launch_debug_e4m3(in, out, (uint32_t)n, (hipStream_t)stream));
 }
 
 const char* forge_last_error(void) { return hipGetErrorString(g_last_hip); }

@@ -746,11 +746,46 @@ __device__ __forceinline__ void tile_gradient(const KArgs& a, char* lds, int row
 // ------------------------------------------------------------------------
 // Raw (undecoded) storage of 4 consecutive elements, so that the loads of
 // later passes can be in flight while earlier ones are computed.
+// OCP FP8 E4M3 ("fn": 1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
+// largest finite 448, no infinities, S.1111.111 is NaN).  Both directions in
+// plain integer / fp32 arithmetic so that they are exact and identical to
+// the format's definition on every device.
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  if (e == 15u && m == 7u) return __uint_as_float(0x7FC00000u);
+  const float mag = e == 0u ? (float)m * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// Round to nearest, ties to even, onto the E4M3 grid, saturating at +-448.
+__device__ __forceinline__ uint32_t e4m3_rne(float y) {
+  const uint32_t b = __float_as_uint(y);
+  const uint32_t sign = (b >> 24) & 0x80u;
+  const float ay = fabsf(y);
+  uint32_t mag;
+  if (!(ay < 448.f)) {
+    mag = 0x7Eu;                                          // saturate (also NaN inputs)
+  } else if (ay < 0x1p-6f) {
+    mag = (uint32_t)rintf(ay * 512.f);                    // subnormal grid 2^-9; 8 becomes 2^-6
+  } else {
+    const uint32_t ab = __float_as_uint(ay);
+    uint32_t ee = ((ab >> 23) & 0xFFu) - 120u;            // biased E4M3 exponent, 1..15
+    uint32_t q = (ab >> 20) & 7u;
+    const uint32_t rem = ab & 0xFFFFFu;
+    if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ++q;
+    if (q == 8u) { q = 0u; ++ee; }
+    mag = (ee << 3) | q;
+    if (mag > 0x7Eu) mag = 0x7Eu;
+  }
+  return sign | mag;
+}
+
 template <int FMT> struct Raw4;
 template <> struct Raw4<FMT_F32> { f32x4 v; };
 template <> struct Raw4<FMT_BF16> { u32x2 v; };
 template <> struct Raw4<FMT_S8> { uint32_t v; float s; };
 template <> struct Raw4<FMT_U8> { uint32_t v; float s; };
+template <> struct Raw4<FMT_E4M3> { uint32_t v; float s; };
 template <> struct Raw4<FMT_NONE> {};
 
 // State tensors are streamed once per step: their accesses are marked
@@ -795,7 +830,7 @@ __device__ __forceinline__ void ld4(Raw4<FMT>& r, const void* row, const Seg& g,
       for (int i = 0; i < 4; ++i) e[i] = i < g.nv ? (uint32_t)p[i] : 0u;
       r.v = u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
     }
-  } else if constexpr (FMT == FMT_S8 || FMT == FMT_U8) {
+  } else if constexpr (fmt_blocked(FMT)) {
     const uint8_t* p = static_cast<const uint8_t*>(row) + g.q;
     if (FAST || (vec && g.nv == 4)) {
       r.v = ld_nt<uint32_t>(p);
@@ -812,7 +847,7 @@ template <int FMT>
 __device__ __forceinline__ void zero4(Raw4<FMT>& r) {
   if constexpr (FMT == FMT_F32) r.v = f32x4{0.f, 0.f, 0.f, 0.f};
   else if constexpr (FMT == FMT_BF16) r.v = u32x2{0u, 0u};
-  else if constexpr (FMT == FMT_S8 || FMT == FMT_U8) { r.v = 0u; r.s = 0.f; }
+  else if constexpr (fmt_blocked(FMT)) { r.v = 0u; r.s = 0.f; }
 }
 
 // Decode to fp32; int8 codes are dequantised as code * scale (one fp32 multiply).
@@ -833,6 +868,9 @@ __device__ __forceinline__ void dec4(const Raw4<FMT>& r, float* x) {
   } else if constexpr (FMT == FMT_U8) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = (float)((r.v >> (8 * i)) & 0xFFu) * r.s;
+  } else if constexpr (FMT == FMT_E4M3) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = e4m3_value((r.v >> (8 * i)) & 0xFFu) * r.s;
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = 0.f;
@@ -877,6 +915,52 @@ __device__ __forceinline__ void st4(void* row, const Seg& g, bool vec, const flo
 // for an exact zero, else 1..255, scale a/255.  The scale and the
 // reciprocal are correctly rounded fp32 divisions.  Int8 states need
 // K % block == 0, so a segment is either entirely inside or outside.
+// E4M3 block quantisation of one chunk (the int8 scheme with E4M3 codes):
+// scale s = absmax / 448, code = e4m3_rne(x * (448 / absmax)); for the
+// second moment (POSITIVE) a positive value never becomes code 0 (it takes
+// the smallest subnormal), which keeps v away from zero as the U8 format does.
+template <bool POSITIVE>
+__device__ __forceinline__ void quantize_chunk_e4m3(const float (&x)[8], int block, const Seg (&sg)[2],
+                                                    void* row_codes, bool vec, float* row_scales) {
+  float a[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(x[4 * g + i]));
+    a[g] = sg[g].ok ? m : 0.f;
+  }
+  const int lpb = block == 128 ? 16 : block >> 2;
+  if (block == 128) a[0] = a[1] = fmaxf(a[0], a[1]);
+  for (int o = 1; o < lpb; o <<= 1) {
+    a[0] = fmaxf(a[0], __shfl_xor(a[0], o));
+    a[1] = fmaxf(a[1], __shfl_xor(a[1], o));
+  }
+  const bool writer = (threadIdx.x & (lpb - 1)) == 0;
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const float sc = a[g] > 0.f ? a[g] / 448.f : 0.f;
+    const float inv = a[g] > 0.f ? 448.f / a[g] : 0.f;
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float xv = x[4 * g + i];
+      uint32_t c = e4m3_rne(xv * inv);
+      if (POSITIVE && xv > 0.f && c == 0u) c = 1u;
+      word |= c << (8 * i);
+    }
+    if (!sg[g].ok) continue;
+    if (writer && (block != 128 || g == 0)) row_scales[sg[g].q / block] = sc;
+    uint8_t* p = static_cast<uint8_t*>(row_codes) + sg[g].q;
+    if (vec) {
+      st_nt<uint32_t>(p, word);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = (uint8_t)((word >> (8 * i)) & 0xFFu);
+    }
+  }
+}
+
 template <bool SIGNED>
 __device__ __forceinline__ void quantize_chunk(const float (&x)[8], int block, const Seg (&sg)[2], void* row_codes,
                                                bool vec, float* row_scales) {
@@ -955,12 +1039,12 @@ struct Step {
       if constexpr (HAS_M) {
         const char* rm = static_cast<const char*>(a.m) + (int64_t)p * a.ldm * (MF == FMT_F32 ? 4 : MF == FMT_BF16 ? 2 : 1);
         ld4<MF, FAST>(r.m[g], rm, sg[g], vec);
-        if constexpr (MF == FMT_S8) r.m[g].s = a.ms[srow + sg[g].q / a.block];
+        if constexpr (fmt_blocked(MF)) r.m[g].s = a.ms[srow + sg[g].q / a.block];
       }
       if constexpr (HAS_V) {
         const char* rv = static_cast<const char*>(a.v) + (int64_t)p * a.ldv * (VF == FMT_F32 ? 4 : VF == FMT_BF16 ? 2 : 1);
         ld4<VF, FAST>(r.v[g], rv, sg[g], vec);
-        if constexpr (VF == FMT_U8) r.v[g].s = a.vs[srow + sg[g].q / a.block];
+        if constexpr (fmt_blocked(VF)) r.v[g].s = a.vs[srow + sg[g].q / a.block];
       }
     }
   }
@@ -1036,12 +1120,14 @@ struct Step {
       if (!sg[s].ok) continue;
       const uint32_t idx_mul = (rowbase + (uint32_t)sg[s].q) * GOLDEN;
       st4<WF, FAST>(rw, sg[s], vec, w + 4 * s, a.c.sr, a.c.keyW, idx_mul);
-      if constexpr (HAS_M && MF != FMT_S8) st4<MF, FAST>(rm, sg[s], vec, m + 4 * s, a.c.sr, a.c.keyM, idx_mul);
-      if constexpr (HAS_V && VF != FMT_U8) st4<VF, FAST>(rv, sg[s], vec, v + 4 * s, a.c.sr, a.c.keyV, idx_mul);
+      if constexpr (HAS_M && !fmt_blocked(MF)) st4<MF, FAST>(rm, sg[s], vec, m + 4 * s, a.c.sr, a.c.keyM, idx_mul);
+      if constexpr (HAS_V && !fmt_blocked(VF)) st4<VF, FAST>(rv, sg[s], vec, v + 4 * s, a.c.sr, a.c.keyV, idx_mul);
     }
     const int64_t srow = (int64_t)p * (a.K / a.block);
     if constexpr (HAS_M && MF == FMT_S8) quantize_chunk<true>(m, a.block, sg, rm, vec, a.ms + srow);
     if constexpr (HAS_V && VF == FMT_U8) quantize_chunk<false>(v, a.block, sg, rv, vec, a.vs + srow);
+    if constexpr (HAS_M && MF == FMT_E4M3) quantize_chunk_e4m3<false>(m, a.block, sg, rm, vec, a.ms + srow);
+    if constexpr (HAS_V && VF == FMT_E4M3) quantize_chunk_e4m3<true>(v, a.block, sg, rv, vec, a.vs + srow);
   }
 };
 

@@ -8,7 +8,10 @@
 
 namespace forge {
 
-enum Fmt : int { FMT_NONE = -1, FMT_F32 = 0, FMT_BF16 = 1, FMT_S8 = 2, FMT_U8 = 3 };
+enum Fmt : int { FMT_NONE = -1, FMT_F32 = 0, FMT_BF16 = 1, FMT_S8 = 2, FMT_U8 = 3, FMT_E4M3 = 4 };
+
+// Formats stored as 8-bit codes with one fp32 scale per block of a row.
+constexpr bool fmt_blocked(int f) { return f == FMT_S8 || f == FMT_U8 || f == FMT_E4M3; }
 enum Opt : int {
   OPT_ADAMW = 0, OPT_LION = 1, OPT_SGDM = 2, OPT_NADAM = 3, OPT_RADAM = 4, OPT_RMSPROP = 5, OPT_ADAGRAD = 6,
   OPT_SGD = 7
@@ -81,15 +84,18 @@ constexpr int WIDE_MIN_BT = 3072;  // token count from which the 256 x 256 kerne
 #define FORGE_ADAMW_LIST(X)        \
   X(OPT_ADAMW, FMT_F32, FMT_F32)   \
   X(OPT_ADAMW, FMT_BF16, FMT_BF16) \
-  X(OPT_ADAMW, FMT_S8, FMT_U8)
+  X(OPT_ADAMW, FMT_S8, FMT_U8)     \
+  X(OPT_ADAMW, FMT_E4M3, FMT_E4M3)
 #define FORGE_LION_LIST(X)         \
   X(OPT_LION, FMT_F32, FMT_NONE)   \
   X(OPT_LION, FMT_BF16, FMT_NONE)  \
-  X(OPT_LION, FMT_S8, FMT_NONE)
+  X(OPT_LION, FMT_S8, FMT_NONE)    \
+  X(OPT_LION, FMT_E4M3, FMT_NONE)
 #define FORGE_SGDM_LIST(X)         \
   X(OPT_SGDM, FMT_F32, FMT_NONE)   \
   X(OPT_SGDM, FMT_BF16, FMT_NONE)  \
-  X(OPT_SGDM, FMT_S8, FMT_NONE)
+  X(OPT_SGDM, FMT_S8, FMT_NONE)    \
+  X(OPT_SGDM, FMT_E4M3, FMT_NONE)
 #define FORGE_ADAM_VARIANT_LIST(X)  \
   X(OPT_NADAM, FMT_F32, FMT_F32)    \
   X(OPT_NADAM, FMT_BF16, FMT_BF16)  \
@@ -161,5 +167,7 @@ hipError_t launch_step(const KArgs& a, int w_fmt, int opt, int m_fmt, int v_fmt,
 // Stochastic rounding of n floats with one key, element i using flat index i.
 hipError_t launch_debug_sr(const float* in, uint16_t* out, uint32_t n, uint32_t key,
                            hipStream_t stream);
+// E4M3 rounding (nearest even, saturating) of n floats.
+hipError_t launch_debug_e4m3(const float* in, uint8_t* out, uint32_t n, hipStream_t stream);
 
 }  // namespace forge

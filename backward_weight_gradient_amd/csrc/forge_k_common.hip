@@ -10,6 +10,18 @@ __global__ void k_debug_sr(const float* __restrict__ in, uint16_t* __restrict__ 
   if (i < n) out[i] = (uint16_t)bf16_sr_bits(in[i], key, i);
 }
 
+// The device E4M3 rounding on its own: out[i] = e4m3_rne(in[i]).
+__global__ void k_debug_e4m3(const float* __restrict__ in, uint8_t* __restrict__ out, uint32_t n) {
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = (uint8_t)e4m3_rne(in[i]);
+}
+
+hipError_t launch_debug_e4m3(const float* in, uint8_t* out, uint32_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_debug_e4m3, dim3((unsigned)((n + 255u) / 256u)), dim3(256), 0, st, in, out, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(const KArgs& a, int in_fmt, hipStream_t st) {
   if (in_fmt == FMT_BF16 && a.dma_ok) hipLaunchKernelGGL((k_gemm<FMT_BF16, true>), tile_grid(a), dim3(NT), 0, st, a);
   else if (in_fmt == FMT_BF16) hipLaunchKernelGGL((k_gemm<FMT_BF16, false>), tile_grid(a), dim3(NT), 0, st, a);

@@ -156,19 +156,29 @@ def mfma_sweep(F, synth, h, reps=3):
 def family_sweep(F, synth, reps=5):
     """Each of the eight optimizer families on gate_proj [14336, 4096] at
     BT = 512 (bf16 X / dY / W with SR, fp32 states where the family keeps
-    them; median of `reps` launches).  Algorithmic bytes: W read + written
-    (4 B), each fp32 state read + written (8 B), X and dY read once."""
+    them), and AdamW with int8 and with E4M3 block-scaled moments; median of
+    `reps` launches.  Algorithmic bytes: W read + written (4 B), each fp32
+    state read + written (8 B) or each 8-bit state with its block scales
+    (2 + 8/128 B), X and dY read once."""
     import torch
     N, K = 14336, 4096
     stream = torch.cuda.current_stream()
     X, dY = synth.activations(1, BT, N, K, STEP_T, device="cuda", extra=40)
     out = {}
-    for opt in ("adamw", "nadam", "radam", "lion", "sgdm", "rmsprop", "adagrad", "sgd"):
-        spec = synth.LayerSpec(in_dtype="bf16", w_fmt="bf16", m_fmt="f32" if opt in F.KEEPS_M else None,
-                               v_fmt="f32" if opt in F.KEEPS_V else None)
+    cases = [(o, "f32") for o in ("adamw", "nadam", "radam", "lion", "sgdm", "rmsprop", "adagrad", "sgd")]
+    cases += [("adamw", "int8"), ("adamw", "e4m3")]
+    for opt, state in cases:
+        if state == "f32":
+            spec = synth.LayerSpec(in_dtype="bf16", w_fmt="bf16", m_fmt="f32" if opt in F.KEEPS_M else None,
+                                   v_fmt="f32" if opt in F.KEEPS_V else None)
+        elif state == "int8":
+            spec = synth.LayerSpec(in_dtype="bf16", w_fmt="bf16", m_fmt="s8", v_fmt="u8", block=128)
+        else:
+            spec = synth.LayerSpec(in_dtype="bf16", w_fmt="bf16", m_fmt="e4m3", v_fmt="e4m3", block=128)
         st = synth.state(1, N, K, spec, device="cuda", extra=40)
-        m = F.state(st["m"]) if st["m"] is not None else None
-        v = F.state(st["v"]) if st["v"] is not None else None
+        blocked = state != "f32"
+        m = (F.state(st["m"], st["m_scale"], 128) if blocked else F.state(st["m"])) if st["m"] is not None else None
+        v = (F.state(st["v"], st["v_scale"], 128) if blocked else F.state(st["v"])) if st["v"] is not None else None
         args = (F.mat(X), F.mat(dY), F.mat(st["W"]), m, v)
         h = F.hyper(opt, lr=1e-4 if opt == "lion" else 1e-3, beta2=0.99 if opt == "lion" else None)
         F.forge_wgrad_step(*args, h, STEP_T, SEED, stream=stream.cuda_stream)
@@ -182,11 +192,15 @@ def family_sweep(F, synth, reps=5):
             torch.cuda.synchronize()
             times.append(e0.elapsed_time(e1))
         ms = sorted(times)[len(times) // 2]
-        bpp = 4 + 8 * (opt in F.KEEPS_M) + 8 * (opt in F.KEEPS_V)
+        if blocked:    # 1-byte codes + one fp32 scale per 128 elements, read and written
+            bpp = 4 + 2 * (2 + 8 / 128)
+        else:
+            bpp = 4 + 8 * (opt in F.KEEPS_M) + 8 * (opt in F.KEEPS_V)
         nbytes = bpp * N * K + 2 * BT * (N + K) * 2
-        out[opt] = {"us": round(1e3 * ms, 1), "state_bytes_per_param": bpp,
-                    "hbm_gbs_alg": round(nbytes / (ms * 1e-3) / 1e9, 1),
-                    "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        name = opt if state == "f32" else f"{opt}_{state}"
+        out[name] = {"us": round(1e3 * ms, 1), "state_bytes_per_param": bpp,
+                     "hbm_gbs_alg": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         del st, args, m, v
     del X, dY
     torch.cuda.empty_cache()

@@ -61,7 +61,7 @@ typedef enum {
   FORGE_E_HIP = 9          /* the HIP runtime reported an error at launch           */
 } forge_status;
 
-typedef enum { FORGE_F32 = 0, FORGE_BF16 = 1, FORGE_S8 = 2, FORGE_U8 = 3 } forge_dtype;
+typedef enum { FORGE_F32 = 0, FORGE_BF16 = 1, FORGE_S8 = 2, FORGE_U8 = 3, FORGE_E4M3 = 4 } forge_dtype;
 
 /* Optimizers: the eight element-wise families the paper fuses in full
  * (Appendix N, "Fully fused").  Where the pages name a family without its
@@ -108,11 +108,17 @@ typedef struct {
  * S8 codes are symmetric in -127..127 (scale = absmax / 127); U8 codes
  * reserve 0 for an exact zero and use 1..255 for positive values
  * (scale = absmax / 255), which keeps the second moment away from zero
- * (paper, section 2.3 and Appendix B). */
+ * (paper, section 2.3 and Appendix B).
+ * E4M3 (either moment; the paper's FP8 moment quantization, section 3.6):
+ * OCP FP8 E4M3 codes (largest finite 448, no infinities) with the same
+ * block scales: scale = absmax / 448, code = the E4M3 value nearest (ties
+ * to even, saturating at 448) to x * (448 / absmax); a positive second
+ * moment never takes code 0 (it takes the smallest subnormal, 2^-9).
+ * Stored value = E4M3 value of the code * scale. */
 typedef struct {
   forge_mat q;
-  float* scale;   /* S8 / U8 only, else NULL               */
-  int32_t block;  /* S8 / U8 only: 32, 64 or 128, else 0   */
+  float* scale;   /* S8 / U8 / E4M3 only, else NULL               */
+  int32_t block;  /* S8 / U8 / E4M3 only: 32, 64 or 128, else 0   */
 } forge_state;
 
 typedef struct {
@@ -131,22 +137,22 @@ typedef struct {
  *
  * X  : [BT, K], dtype BF16 or F32.      dY : [BT, N], same dtype as X.
  * W  : [N, K], BF16 or F32, updated in place.
- * m  : [N, K] first state, F32 / BF16 / S8: AdamW, NAdam, RAdam, Lion, SGD-m
- *      (NULL for RMSprop, AdaGrad, SGD).
- * v  : [N, K] second state, F32 / BF16 / U8: AdamW, NAdam, RAdam, RMSprop,
- *      AdaGrad (NULL for Lion, SGD-m, SGD).
+ * m  : [N, K] first state, F32 / BF16 / S8 / E4M3: AdamW, NAdam, RAdam, Lion,
+ *      SGD-m (NULL for RMSprop, AdaGrad, SGD).
+ * v  : [N, K] second state, F32 / BF16 / U8 / E4M3: AdamW, NAdam, RAdam,
+ *      RMSprop, AdaGrad (NULL for Lion, SGD-m, SGD).
  * h  : optimizer and hyper-parameters.  step: the 1-based global step t,
  *      used by the AdamW bias correction 1/(1 - beta^t) and by the SR key.
  * seed: 64-bit stochastic-rounding seed.
  *
  * Supported combinations: X/dY in {BF16, F32} x W in {BF16, F32} x
- *   AdamW (m, v) in {(F32, F32), (BF16, BF16), (S8, U8)},
+ *   AdamW (m, v) in {(F32, F32), (BF16, BF16), (S8, U8), (E4M3, E4M3)},
  *   NAdam / RAdam (m, v) in {(F32, F32), (BF16, BF16)},
- *   Lion / SGD-m m in {F32, BF16, S8},
+ *   Lion / SGD-m m in {F32, BF16, S8, E4M3},
  *   RMSprop / AdaGrad v in {F32, BF16}, or SGD (no state).
  *   A missing required state is E_NULL, a state the optimizer does not keep
  *   is E_UNSUPPORTED.
- * Int8 states need K % block == 0.  N * K must be < 2^32 (flat SR index).
+ * Int8 and E4M3 states need K % block == 0.  N * K must be < 2^32 (flat SR index).
  * BT may be 0 (G = 0: the step still applies decay / momentum).
  * N == 0 or K == 0 is a no-op.
  *
@@ -284,6 +290,14 @@ forge_status forge_wgrad_unfused(const forge_mat* X, const forge_mat* dY, forge_
  */
 forge_status forge_debug_sr_bf16(const float* in, uint16_t* out, int64_t n, uint64_t seed,
                                  int64_t step, uint32_t tensor_id, void* stream);
+
+/*
+ * forge_debug_e4m3 -- test hook: the device's E4M3 rounding (nearest, ties
+ * to even, saturating at 448; the element code of the E4M3 state format) of
+ * n floats, out[i] = code of in[i].  Device pointers.  Errors: E_NULL,
+ * E_SHAPE (n < 0 or n >= 2^32), E_ALIGN, E_ALIAS, E_HIP.
+ */
+forge_status forge_debug_e4m3(const float* in, uint8_t* out, int64_t n, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* forge_status_str(forge_status s);

@@ -87,6 +87,7 @@ __all__ = [
     "adamw", "lion", "sgdm", "nadam", "radam", "rmsprop", "adagrad", "sgd",
     "nadam_mu", "radam_rect",
     "quantize_signed", "quantize_unsigned", "dequantize",
+    "E4M3_MAX", "e4m3_to_f64", "f32_to_e4m3_rne", "quantize_e4m3",
     "decode", "encode", "wgrad_step", "apply_step", "step_tiled",
     "TENSOR_W", "TENSOR_M", "TENSOR_V",
 ]
@@ -465,6 +466,56 @@ def quantize_unsigned(x32: np.ndarray, block: int):
     return q.reshape(x32.shape), s
 
 
+# OCP FP8 E4M3 ("fn"): sign, 4 exponent bits (bias 7), 3 mantissa bits; the
+# largest finite value is 448 = 1.75 * 2^8, there are no infinities and
+# S.1111.111 is NaN; exponent 0 holds the subnormals m * 2^-9.
+E4M3_MAX = 448.0
+
+
+def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
+    """Values of E4M3 codes (uint8), exactly, in fp64."""
+    c = np.asarray(codes).astype(np.int64)
+    e, m = (c >> 3) & 15, c & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2((e - 7).astype(np.float64)))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(c & 0x80, -mag, mag)
+
+
+_E4M3_GRID = e4m3_to_f64(np.arange(0x7F))          # the 127 finite magnitudes, codes 0 .. 0x7E, ascending
+
+
+def f32_to_e4m3_rne(y32: np.ndarray) -> np.ndarray:
+    """The E4M3 code nearest to each fp32 value (ties to the even code, i.e.
+    the even significand), saturating at +-448; the sign bit follows the
+    input's (so -0.0 gives 0x80)."""
+    y = np.asarray(y32, dtype=np.float32).astype(np.float64)
+    ay = np.abs(y)
+    hi = np.clip(np.searchsorted(_E4M3_GRID, ay, side="left"), 0, len(_E4M3_GRID) - 1)
+    lo = np.clip(hi - 1, 0, len(_E4M3_GRID) - 1)
+    dlo, dhi = ay - _E4M3_GRID[lo], _E4M3_GRID[hi] - ay
+    pick = np.where(dhi < dlo, hi, np.where(dlo < dhi, lo, np.where(hi % 2 == 0, hi, lo)))
+    pick = np.where(ay >= E4M3_MAX, 0x7E, pick)
+    return (pick | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+
+
+def quantize_e4m3(x32: np.ndarray, block: int, positive: bool):
+    """E4M3 block quantisation (the int8 scheme with E4M3 codes; the paper's
+    FP8 moment quantization, section 3.6, gives no format, this is the
+    reading): a = max|x| over the block, s = fp32(a/448), code =
+    f32_to_e4m3_rne(fp32(x * fp32(448/a))); with ``positive`` (the second
+    moment) a positive x never takes code 0 but the smallest subnormal.
+    a = 0 gives s = 0 and all codes +-0.  Returns (uint8 codes, float32 scales)."""
+    xb = _blocks(np.asarray(x32, dtype=np.float32), block)
+    a = np.max(np.abs(xb), axis=2)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        s = np.where(a > 0, a / np.float32(E4M3_MAX), np.float32(0)).astype(np.float32)
+        inv = np.where(a > 0, np.float32(E4M3_MAX) / a, np.float32(0)).astype(np.float32)
+    q = f32_to_e4m3_rne((xb * inv[:, :, None]).astype(np.float32))
+    if positive:
+        q = np.where((xb > 0) & (q == 0), np.uint8(1), q).astype(np.uint8)
+    return q.reshape(x32.shape), s
+
+
 def dequantize(codes: np.ndarray, scales: np.ndarray, block: int) -> np.ndarray:
     """Stored value = fp32(code * scale)."""
     r, c = codes.shape
@@ -484,22 +535,27 @@ def decode(st: Stored, rows=None, c0: int = 0, c1: Optional[int] = None) -> np.n
         return d.astype(np.float64)
     if st.fmt == "bf16":
         return bf16_bits_to_f64(d)
-    if st.fmt in ("s8", "u8"):
+    if st.fmt in ("s8", "u8", "e4m3"):
         if c0 % st.block or (c1 - c0) % st.block:
-            raise ValueError("int8 sub-blocks must be block aligned")
+            raise ValueError("block-scaled sub-blocks must be block aligned")
         s = st.scale[rows][:, c0 // st.block:c1 // st.block]
+        if st.fmt == "e4m3":
+            r, c = d.shape
+            vals = e4m3_to_f64(d).astype(np.float32).reshape(r, c // st.block, st.block)
+            return (vals * s.astype(np.float32)[:, :, None]).astype(np.float32).reshape(r, c).astype(np.float64)
         return dequantize(d, s, st.block).astype(np.float64)
     raise ValueError(f"unknown format {st.fmt!r}")
 
 
 def encode(x64: np.ndarray, fmt: str, *, round: str = "sr", key: int = 0,
-           flat_index: Optional[np.ndarray] = None, block: int = 128) -> Stored:
+           flat_index: Optional[np.ndarray] = None, block: int = 128, positive: bool = False) -> Stored:
     """Round fp64 results once into the storage format (Algorithm 1 Phase 3).
 
     fp32: round to nearest even.  bf16: the value is first rounded to fp32,
     then to bf16 by round-to-nearest-even or by stochastic rounding with the
-    counter-based bits of ``key`` and ``flat_index``.  s8 / u8: the fp32 value
-    is block-quantised.
+    counter-based bits of ``key`` and ``flat_index``.  s8 / u8 / e4m3: the
+    fp32 value is block-quantised (e4m3 with ``positive`` for the second
+    moment).
     """
     x32 = np.asarray(x64, dtype=np.float64).astype(np.float32)
     if fmt == "f32":
@@ -514,6 +570,9 @@ def encode(x64: np.ndarray, fmt: str, *, round: str = "sr", key: int = 0,
     if fmt == "u8":
         q, s = quantize_unsigned(x32, block)
         return Stored("u8", q, s, block)
+    if fmt == "e4m3":
+        q, s = quantize_e4m3(x32, block, positive)
+        return Stored("e4m3", q, s, block)
     raise ValueError(f"unknown format {fmt!r}")
 
 
@@ -576,7 +635,7 @@ def apply_step(G: np.ndarray, W: Stored, m: Optional[Stored], v: Optional[Stored
         if st is None:
             return None
         return encode(x, st.fmt, round=h.round, key=sr_key(seed, step, tid),
-                      flat_index=flat, block=st.block)
+                      flat_index=flat, block=st.block, positive=(tid == TENSOR_V))
 
     return {"W": store(W1, W, TENSOR_W), "m": store(m1, m, TENSOR_M),
             "v": store(v1, v, TENSOR_V), "pre": {"W": W1, "m": m1, "v": v1}}

@@ -69,8 +69,8 @@ class LayerSpec:
     """Formats of one layer's tensors."""
     in_dtype: str = "bf16"   # X, dY: "bf16" | "f32"
     w_fmt: str = "bf16"      # "bf16" | "f32"
-    m_fmt: Optional[str] = "f32"   # "f32" | "bf16" | "s8" | None
-    v_fmt: Optional[str] = "f32"   # "f32" | "bf16" | "u8" | None
+    m_fmt: Optional[str] = "f32"   # "f32" | "bf16" | "s8" | "e4m3" | None
+    v_fmt: Optional[str] = "f32"   # "f32" | "bf16" | "u8" | "e4m3" | None
     block: int = 128
 
 
@@ -108,6 +108,9 @@ def state(cfg, N, K, spec: LayerSpec, *, w_std=0.02, v_std=1e-6, v_zero=False,
     elif spec.m_fmt == "s8":
         out["m"] = torch.zeros((N, K), device=device, dtype=torch.int8)
         out["m_scale"] = torch.zeros((N, nb), device=device, dtype=torch.float32)
+    elif spec.m_fmt == "e4m3":
+        out["m"] = torch.zeros((N, K), device=device, dtype=torch.uint8).view(torch.float8_e4m3fn)
+        out["m_scale"] = torch.zeros((N, nb), device=device, dtype=torch.float32)
     if spec.v_fmt in ("f32", "bf16"):
         if v_zero:
             v = torch.zeros((N, K), device=device, dtype=torch.float32)
@@ -121,6 +124,14 @@ def state(cfg, N, K, spec: LayerSpec, *, w_std=0.02, v_std=1e-6, v_zero=False,
         else:
             out["v"] = uniform_int((N, K), 1, 256, device, cfg, step, T_V, extra)
             out["v_scale"] = torch.full((N, nb), 3.5 * v_std / 255.0, device=device, dtype=torch.float32)
+    elif spec.v_fmt == "e4m3":
+        if v_zero:
+            out["v"] = torch.zeros((N, K), device=device, dtype=torch.uint8).view(torch.float8_e4m3fn)
+            out["v_scale"] = torch.zeros((N, nb), device=device, dtype=torch.float32)
+        else:
+            # positive E4M3 codes 1 .. 0x7E (subnormals and normals up to 448)
+            out["v"] = uniform_int((N, K), 1, 0x7F, device, cfg, step, T_V, extra).view(torch.float8_e4m3fn)
+            out["v_scale"] = torch.full((N, nb), 3.5 * v_std / 448.0, device=device, dtype=torch.float32)
     return out
 
 
@@ -133,4 +144,6 @@ def host(t: torch.Tensor) -> np.ndarray:
     """Host NumPy copy: bf16 as uint16 bits, everything else as-is."""
     if t.dtype == torch.bfloat16:
         return bf16_bits(t)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.detach().cpu().contiguous().view(torch.uint8).numpy()
     return t.detach().cpu().contiguous().numpy()

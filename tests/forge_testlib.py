@@ -19,7 +19,7 @@ the same inputs and compares every output element by element:
   -- relative size about sqrt(BT) 2^-24 for a BT-term fp32 sum -- moves the
   value across the rounding decision, which happens with probability of that
   size in units of a bf16 ULP, 2^-8: about sqrt(BT) 2^-16);
-* int8 codes: within one code of the oracle's, at least 99% identical;
+* int8 and E4M3 codes: within one code (one step of the grid) of the oracle's, at least 99% identical;
   scales within 1e-5 relative or inside the hull of the block absmax.
 """
 
@@ -35,7 +35,13 @@ import backward_weight_gradient_amd as F
 import oracle as O
 import synth
 
-FMT_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "s8": torch.int8, "u8": torch.uint8}
+FMT_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "s8": torch.int8, "u8": torch.uint8,
+             "e4m3": torch.float8_e4m3fn}
+
+
+def _codes(t):
+    """FP8 tensors as their uint8 codes (row gathers are done on those)."""
+    return t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t
 
 
 @dataclass
@@ -124,7 +130,7 @@ def _stored(t, fmt, scale, block, rows):
     if t is None:
         return None
     idx = torch.as_tensor(rows, device=t.device, dtype=torch.long)
-    data = synth.host(t.index_select(0, idx))
+    data = synth.host(_codes(t).index_select(0, idx))
     sc = None if scale is None else scale.index_select(0, idx).cpu().numpy()
     return O.Stored(fmt, data, sc, block)
 
@@ -195,6 +201,8 @@ def _abs_stored(st):
         return O.Stored("bf16", st.data & np.uint16(0x7FFF))
     if st.fmt == "s8":
         return O.Stored("s8", np.abs(st.data.astype(np.int16)).astype(np.int8), st.scale, st.block)
+    if st.fmt == "e4m3":
+        return O.Stored("e4m3", st.data & np.uint8(0x7F), st.scale, st.block)
     return st
 
 
@@ -218,7 +226,7 @@ def check_against_oracle(snap: Snap, L: Layer, h, step: int, seed: int, col_rang
         for name, (t, fmt, scale) in got.items():
             if t is None or fmt is None:
                 continue
-            g = synth.host(t.index_select(0, idx)[:, c0:c1])
+            g = synth.host(_codes(t).index_select(0, idx)[:, c0:c1])
             r_st = ref[name]
             r_pre = ref["pre"][name]
             where = f"{name}[{fmt}] cols {c0}:{c1}"
@@ -247,9 +255,12 @@ def check_against_oracle(snap: Snap, L: Layer, h, step: int, seed: int, col_rang
                                         f"got {gv[tuple(i)]!r} hull [{lo[name][tuple(i)]!r}, {hi[name][tuple(i)]!r}]")
                 if exact < exact_min:
                     rep.failures.append(f"{where}: bf16 bit-exact fraction {exact:.6f} < {exact_min}")
-            else:  # int8 codes + scales
+            else:  # 8-bit codes + scales (int8, or E4M3 compared as sign-magnitude steps)
                 gi = g.astype(np.int64)
                 ri = r_st.data.astype(np.int64)
+                if fmt == "e4m3":
+                    gi = np.where(gi & 0x80, -(gi & 0x7F), gi)
+                    ri = np.where(ri & 0x80, -(ri & 0x7F), ri)
                 d = np.abs(gi - ri)
                 exact = float(np.mean(d == 0)) if d.size else 1.0
                 rep.exact_frac[where] = exact
@@ -262,7 +273,7 @@ def check_against_oracle(snap: Snap, L: Layer, h, step: int, seed: int, col_rang
                 b = s.block
                 gs = scale.index_select(0, idx)[:, c0 // b:c1 // b].cpu().numpy().astype(np.float64)
                 rs = r_st.scale.astype(np.float64)
-                qmax = 127.0 if fmt == "s8" else 255.0
+                qmax = {"s8": 127.0, "u8": 255.0, "e4m3": O.E4M3_MAX}[fmt]
                 alo = np.where((lo[name] <= 0) & (hi[name] >= 0), 0.0, np.minimum(np.abs(lo[name]), np.abs(hi[name])))
                 ahi = np.maximum(np.abs(lo[name]), np.abs(hi[name]))
                 R = alo.shape[0]

@@ -387,3 +387,24 @@ def test_backward_step_validation():
     assert bs(F.mat_raw(m.q.data, F.FORGE_BF16, 64, 256)) == F.FORGE_E_ALIAS   # on top of m
     assert bs(F.mat_raw(X.data, F.FORGE_BF16, 64, 256)) == F.FORGE_E_ALIAS     # on top of X
     assert bs(F.mat_raw(addr(7), F.FORGE_BF16, 64, 256), step=0) == F.FORGE_E_STEP
+
+
+# ---------------------------------------------------------------------------
+# E4M3 states (validation only)
+# ---------------------------------------------------------------------------
+def test_e4m3_state_rules():
+    E = F.FORGE_E4M3
+    X, dY, W, m, v = layer(m_dt=E, v_dt=E)
+    m.scale, m.block = addr(5), 128
+    v.scale, v.block = addr(6), 128
+    assert check(X, dY, W, m, v) == F.FORGE_OK
+    assert check(X, dY, W, m, None, F.hyper("lion")) == F.FORGE_OK
+    assert check(X, dY, W, m, None, F.hyper("sgdm")) == F.FORGE_OK
+    assert check(X, dY, W, m, v, F.hyper("nadam")) == F.FORGE_E_UNSUPPORTED       # fp32 / bf16 only
+    X2, dY2, W2, m2, v2 = layer(m_dt=F.FORGE_S8, v_dt=E)
+    v2.scale, v2.block = addr(6), 128
+    assert check(X2, dY2, W2, m2, v2) == F.FORGE_E_UNSUPPORTED                     # S8 with E4M3
+    m.scale = None
+    assert check(X, dY, W, m, v) == F.FORGE_E_NULL                                 # scales required
+    m.scale, m.block = addr(5), 48
+    assert check(X, dY, W, m, v) == F.FORGE_E_SHAPE                                # block 32 / 64 / 128

@@ -639,3 +639,54 @@ def test_input_grad_error_bound_covers_fp32_order():
     for p in range(700):                       # one fp32 order: p ascending
         acc = acc + np.multiply.outer(dY[:, p], W[p])
     assert np.all(np.abs(acc.astype(np.float64) - ref) <= O.input_grad_error_bound(dY, W))
+
+
+# ---------------------------------------------------------------------------
+# FP8 E4M3 moment storage
+# ---------------------------------------------------------------------------
+def test_e4m3_decode_matches_torch_for_every_code():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.e4m3_to_f64(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert O.e4m3_to_f64(np.array([0x7E]))[0] == 448.0 and O.e4m3_to_f64(np.array([0x01]))[0] == 2.0 ** -9
+
+
+def test_e4m3_round_to_nearest_even_matches_torch_in_range():
+    """torch's cast to float8_e4m3fn rounds to nearest even; inside the
+    finite range the two must agree everywhere, including at every midpoint
+    between neighbouring codes (ties) and in the subnormal range."""
+    grid = O.e4m3_to_f64(np.arange(0x7F))
+    mids = (grid[:-1] + grid[1:]) / 2
+    rng = np.random.default_rng(9)
+    x = np.concatenate([grid, mids, np.nextafter(mids, 0), np.nextafter(mids, 1e9),
+                        rng.uniform(0, 448, 20000), rng.uniform(0, 2 ** -6, 5000)]).astype(np.float32)
+    x = x[x < 448]
+    x = np.concatenate([x, -x])
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(O.f32_to_e4m3_rne(x), ref)
+    assert O.f32_to_e4m3_rne(np.array([448.0, 1e6, -600.0], dtype=np.float32)).tolist() == [0x7E, 0x7E, 0xFE]
+
+
+def test_e4m3_block_quantisation():
+    """Scale absmax/448; the block maximum maps to 448 exactly; every element
+    is within half a grid step of its value; a positive second moment never
+    becomes zero; an all-zero block stores scale 0."""
+    rng = np.random.default_rng(10)
+    x = (rng.normal(size=(6, 256)) * 10.0 ** rng.uniform(-8, 2, size=(6, 1))).astype(np.float32)
+    x[5] = 0
+    q, s = O.quantize_e4m3(x, 64, positive=False)
+    a = np.abs(x).reshape(6, 4, 64).max(axis=2)
+    np.testing.assert_array_equal(s, (a / np.float32(448)).astype(np.float32))
+    back = O.e4m3_to_f64(q).reshape(6, 4, 64) * s[:, :, None].astype(np.float64)
+    xb = x.reshape(6, 4, 64).astype(np.float64)
+    scaled = np.abs(xb) / np.where(s[:, :, None] > 0, s[:, :, None], 1)       # position on the E4M3 grid
+    step = np.where(scaled >= 2 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(scaled, 2 ** -6))) - 3), 2.0 ** -9)
+    assert np.all(np.abs(back - xb) <= (0.5 * step + 1e-6 * scaled) * s[:, :, None] + 1e-45)
+    assert np.all(s[5] == 0) and np.all((q[5] & 0x7F) == 0)
+    v = np.abs(x)
+    v[0, :3] = [1e-30, 0.0, 1e-12]
+    qv, sv = O.quantize_e4m3(v, 128, positive=True)
+    assert np.all(qv[v > 0] != 0) and np.all(qv[v == 0] == 0)
