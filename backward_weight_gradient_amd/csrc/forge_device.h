@@ -97,10 +97,13 @@ __device__ __forceinline__ uint32_t bf16_sr_bits(float x, uint32_t key, uint32_t
 }
 
 // sr != 0 (wave-uniform): stochastic rounding, else round to nearest even.
+// The empty asm keeps the increment in a register ahead of the finite test,
+// so the compiler selects instead of branching around the hash per element.
 __device__ __forceinline__ uint32_t bf16_store_bits(float x, int sr, uint32_t key, uint32_t idx_mul) {
   const uint32_t rne_add = 0x7FFFu + ((__float_as_uint(x) >> 16) & 1u);
-  const uint32_t sr_add = fmix32(key ^ idx_mul) >> 16;
-  return bf16_bits_add(x, sr ? sr_add : rne_add);
+  uint32_t add = sr ? fmix32(key ^ idx_mul) >> 16 : rne_add;
+  asm volatile("" : "+v"(add));
+  return bf16_bits_add(x, add);
 }
 
 __device__ __forceinline__ float bf16_val(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
@@ -747,37 +750,41 @@ __device__ __forceinline__ void tile_gradient(const KArgs& a, char* lds, int row
 // Raw (undecoded) storage of 4 consecutive elements, so that the loads of
 // later passes can be in flight while earlier ones are computed.
 // OCP FP8 E4M3 ("fn": 1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
-// largest finite 448, no infinities, S.1111.111 is NaN).  Both directions in
-// plain integer / fp32 arithmetic so that they are exact and identical to
-// the format's definition on every device.
-__device__ __forceinline__ float e4m3_value(uint32_t c) {
-  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  if (e == 15u && m == 7u) return __uint_as_float(0x7FC00000u);
-  const float mag = e == 0u ? (float)m * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
-  return (c & 0x80u) ? -mag : mag;
+// largest finite 448, no infinities, S.1111.111 is NaN), converted with
+// gfx950's FP8 instructions, which take and produce this format.  Encoding
+// rounds to nearest, ties to even (the mode register's default); inputs are
+// first clamped to +-448, so values beyond the largest finite saturate
+// instead of becoming NaN.  The sign of a zero result follows the input.
+// Both directions are exact functions of their inputs.
+__device__ __forceinline__ uint32_t e4m3_pack4(float y0, float y1, float y2, float y3) {
+  const auto sat = [](float y) { return fminf(fmaxf(y, -448.f), 448.f); };
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(y0), sat(y1), 0, false);   // bytes 0, 1
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(y2), sat(y3), w, true);        // bytes 2, 3
+  return (uint32_t)w;
 }
 
-// Round to nearest, ties to even, onto the E4M3 grid, saturating at +-448.
-__device__ __forceinline__ uint32_t e4m3_rne(float y) {
-  const uint32_t b = __float_as_uint(y);
-  const uint32_t sign = (b >> 24) & 0x80u;
-  const float ay = fabsf(y);
-  uint32_t mag;
-  if (!(ay < 448.f)) {
-    mag = 0x7Eu;                                          // saturate (also NaN inputs)
-  } else if (ay < 0x1p-6f) {
-    mag = (uint32_t)rintf(ay * 512.f);                    // subnormal grid 2^-9; 8 becomes 2^-6
-  } else {
-    const uint32_t ab = __float_as_uint(ay);
-    uint32_t ee = ((ab >> 23) & 0xFFu) - 120u;            // biased E4M3 exponent, 1..15
-    uint32_t q = (ab >> 20) & 7u;
-    const uint32_t rem = ab & 0xFFFFFu;
-    if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ++q;
-    if (q == 8u) { q = 0u; ++ee; }
-    mag = (ee << 3) | q;
-    if (mag > 0x7Eu) mag = 0x7Eu;
-  }
-  return sign | mag;
+__device__ __forceinline__ void e4m3_unpack4(uint32_t w, float* x) {
+  const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);        // bytes 0, 1
+  const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);         // bytes 2, 3
+  x[0] = lo[0]; x[1] = lo[1]; x[2] = hi[0]; x[3] = hi[1];
+}
+
+// Unsigned max across the lanes of one 16-lane DPP row.  CTRL selects the
+// partner: 0xB1 quad_perm [1,0,3,2] (lane ^ 1), 0x4E quad_perm [2,3,0,1]
+// (lane ^ 2), 0x141 row_half_mirror (lane i <-> 7 - i: the other quad of
+// its 8 lanes), 0x140 row_mirror (lane i <-> 15 - i: the other half of the
+// row).  Every partner lies in the same row, so all lanes must be active.
+// Applied to the bit patterns of non-negative floats, unsigned max is the
+// float max, exact and independent of the reduction order.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_umax(uint32_t x) {
+  return max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ uint32_t lanes8_max(uint32_t x) {   // over aligned groups of 8 lanes
+  return dpp_umax<0x141>(dpp_umax<0x4E>(dpp_umax<0xB1>(x)));
+}
+__device__ __forceinline__ uint32_t lanes16_max(uint32_t x) {  // over each 16-lane row
+  return dpp_umax<0x140>(lanes8_max(x));
 }
 
 template <int FMT> struct Raw4;
@@ -869,8 +876,9 @@ __device__ __forceinline__ void dec4(const Raw4<FMT>& r, float* x) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = (float)((r.v >> (8 * i)) & 0xFFu) * r.s;
   } else if constexpr (FMT == FMT_E4M3) {
+    e4m3_unpack4(r.v, x);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = e4m3_value((r.v >> (8 * i)) & 0xFFu) * r.s;
+    for (int i = 0; i < 4; ++i) x[i] *= r.s;
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = 0.f;
@@ -908,99 +916,86 @@ __device__ __forceinline__ void st4(void* row, const Seg& g, bool vec, const flo
 }
 
 // Block-absmax quantisation of a chunk (two 4-element segments 64 columns
-// apart).  block == 128: one block spans both segments of the 16 lanes of
-// a row; block 32 / 64: each segment lies in its own block, shared by
-// block/4 adjacent lanes.  Every lane of the wave must call this (lane
-// shuffles).  SIGNED: codes -127..127, scale a/127.  Unsigned: code 0 only
-// for an exact zero, else 1..255, scale a/255.  The scale and the
-// reciprocal are correctly rounded fp32 divisions.  Int8 states need
+// apart) to 8-bit codes with one fp32 scale per block.  block == 128: one
+// block spans both segments of the 16 lanes of a row; block 64 / 32: each
+// segment lies in its own block, shared by 16 / 8 adjacent lanes.  Every
+// lane of the wave must call this (DPP reductions).  8-bit states need
 // K % block == 0, so a segment is either entirely inside or outside.
-// E4M3 block quantisation of one chunk (the int8 scheme with E4M3 codes):
-// scale s = absmax / 448, code = e4m3_rne(x * (448 / absmax)); for the
-// second moment (POSITIVE) a positive value never becomes code 0 (it takes
-// the smallest subnormal), which keeps v away from zero as the U8 format does.
-template <bool POSITIVE>
-__device__ __forceinline__ void quantize_chunk_e4m3(const float (&x)[8], int block, const Seg (&sg)[2],
-                                                    void* row_codes, bool vec, float* row_scales) {
-  float a[2];
-#pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    float m = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(x[4 * g + i]));
-    a[g] = sg[g].ok ? m : 0.f;
-  }
-  const int lpb = block == 128 ? 16 : block >> 2;
-  if (block == 128) a[0] = a[1] = fmaxf(a[0], a[1]);
-  for (int o = 1; o < lpb; o <<= 1) {
-    a[0] = fmaxf(a[0], __shfl_xor(a[0], o));
-    a[1] = fmaxf(a[1], __shfl_xor(a[1], o));
-  }
-  const bool writer = (threadIdx.x & (lpb - 1)) == 0;
-#pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    const float sc = a[g] > 0.f ? a[g] / 448.f : 0.f;
-    const float inv = a[g] > 0.f ? 448.f / a[g] : 0.f;
-    uint32_t word = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float xv = x[4 * g + i];
-      uint32_t c = e4m3_rne(xv * inv);
-      if (POSITIVE && xv > 0.f && c == 0u) c = 1u;
-      word |= c << (8 * i);
-    }
-    if (!sg[g].ok) continue;
-    if (writer && (block != 128 || g == 0)) row_scales[sg[g].q / block] = sc;
-    uint8_t* p = static_cast<uint8_t*>(row_codes) + sg[g].q;
-    if (vec) {
-      st_nt<uint32_t>(p, word);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = (uint8_t)((word >> (8 * i)) & 0xFFu);
-    }
-  }
-}
-
-template <bool SIGNED>
+//  FMT_S8   (first moment): codes -127..127, scale a/127.
+//  FMT_U8   (second moment): code 0 only for an exact zero, else 1..255,
+//           scale a/255.
+//  FMT_E4M3 (either): scale a/448, code = the E4M3 value nearest to
+//           x * (448/a); with POSITIVE (the second moment) a positive value
+//           never becomes code 0 but the smallest subnormal 2^-9, which is
+//           what rounding max(y, 2^-9) gives for every positive y.
+// a is the block absmax; the scale and the reciprocal are correctly rounded
+// fp32 divisions.
+template <int FMT, bool POSITIVE>
 __device__ __forceinline__ void quantize_chunk(const float (&x)[8], int block, const Seg (&sg)[2], void* row_codes,
                                                bool vec, float* row_scales) {
-  float a[2];
+  constexpr float QMAX = FMT == FMT_S8 ? 127.f : FMT == FMT_U8 ? 255.f : 448.f;
+  // absmax as the unsigned max of |x| bit patterns (the second moment is
+  // never negative, so for U8 this is max x)
+  uint32_t ab[2];
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
-    float m = 0.f;
+    uint32_t m = 0u;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) m = fmaxf(m, SIGNED ? fabsf(x[4 * g + i]) : x[4 * g + i]);
-    a[g] = sg[g].ok ? m : 0.f;
+    for (int i = 0; i < 4; ++i) m = max(m, __float_as_uint(x[4 * g + i]) & 0x7FFFFFFFu);
+    ab[g] = sg[g].ok ? m : 0u;
   }
-  const int lpb = block == 128 ? 16 : block >> 2;
-  if (block == 128) a[0] = a[1] = fmaxf(a[0], a[1]);
-  for (int o = 1; o < lpb; o <<= 1) {
-    a[0] = fmaxf(a[0], __shfl_xor(a[0], o));
-    a[1] = fmaxf(a[1], __shfl_xor(a[1], o));
+  if (block == 128) {
+    ab[0] = ab[1] = lanes16_max(max(ab[0], ab[1]));
+  } else if (block == 64) {
+    ab[0] = lanes16_max(ab[0]);
+    ab[1] = lanes16_max(ab[1]);
+  } else {
+    ab[0] = lanes8_max(ab[0]);
+    ab[1] = lanes8_max(ab[1]);
   }
-  const float qmax = SIGNED ? 127.f : 255.f;
+  const float a[2] = {__uint_as_float(ab[0]), __uint_as_float(ab[1])};
+  float sc[2], inv[2];
+  sc[0] = a[0] > 0.f ? a[0] / QMAX : 0.f;
+  inv[0] = a[0] > 0.f ? QMAX / a[0] : 0.f;
+  if (block == 128) {
+    sc[1] = sc[0];
+    inv[1] = inv[0];
+  } else {
+    sc[1] = a[1] > 0.f ? a[1] / QMAX : 0.f;
+    inv[1] = a[1] > 0.f ? QMAX / a[1] : 0.f;
+  }
+  const int lpb = block == 32 ? 8 : 16;
   const bool writer = (threadIdx.x & (lpb - 1)) == 0;
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
-    const float sc = a[g] > 0.f ? a[g] / qmax : 0.f;
-    const float inv = a[g] > 0.f ? qmax / a[g] : 0.f;
     uint32_t word = 0;
+    if constexpr (FMT == FMT_E4M3) {
+      float y[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float xv = x[4 * g + i];
-      float r = rintf(xv * inv);
-      uint32_t c;
-      if (SIGNED) {
-        r = fminf(fmaxf(r, -127.f), 127.f);
-        c = (uint32_t)(int32_t)r & 0xFFu;
-      } else {
-        r = fminf(fmaxf(r, 1.f), 255.f);
-        c = xv == 0.f ? 0u : (uint32_t)r;
+      for (int i = 0; i < 4; ++i) {
+        const float xv = x[4 * g + i];
+        y[i] = xv * inv[g];
+        if (POSITIVE) y[i] = xv > 0.f ? fmaxf(y[i], 0x1p-9f) : y[i];
       }
-      word |= c << (8 * i);
+      word = e4m3_pack4(y[0], y[1], y[2], y[3]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float xv = x[4 * g + i];
+        float r = rintf(xv * inv[g]);
+        uint32_t c;
+        if (FMT == FMT_S8) {
+          r = fminf(fmaxf(r, -127.f), 127.f);
+          c = (uint32_t)(int32_t)r & 0xFFu;
+        } else {
+          r = fminf(fmaxf(r, 1.f), 255.f);
+          c = xv == 0.f ? 0u : (uint32_t)r;
+        }
+        word |= c << (8 * i);
+      }
     }
     if (!sg[g].ok) continue;
-    if (writer && (block != 128 || g == 0)) row_scales[sg[g].q / block] = sc;
+    if (writer && (block != 128 || g == 0)) row_scales[sg[g].q / block] = sc[g];
     uint8_t* p = static_cast<uint8_t*>(row_codes) + sg[g].q;
     if (vec) {
       st_nt<uint32_t>(p, word);
@@ -1124,10 +1119,8 @@ struct Step {
       if constexpr (HAS_V && !fmt_blocked(VF)) st4<VF, FAST>(rv, sg[s], vec, v + 4 * s, a.c.sr, a.c.keyV, idx_mul);
     }
     const int64_t srow = (int64_t)p * (a.K / a.block);
-    if constexpr (HAS_M && MF == FMT_S8) quantize_chunk<true>(m, a.block, sg, rm, vec, a.ms + srow);
-    if constexpr (HAS_V && VF == FMT_U8) quantize_chunk<false>(v, a.block, sg, rv, vec, a.vs + srow);
-    if constexpr (HAS_M && MF == FMT_E4M3) quantize_chunk_e4m3<false>(m, a.block, sg, rm, vec, a.ms + srow);
-    if constexpr (HAS_V && VF == FMT_E4M3) quantize_chunk_e4m3<true>(v, a.block, sg, rv, vec, a.vs + srow);
+    if constexpr (HAS_M && fmt_blocked(MF)) quantize_chunk<MF, false>(m, a.block, sg, rm, vec, a.ms + srow);
+    if constexpr (HAS_V && fmt_blocked(VF)) quantize_chunk<VF, true>(v, a.block, sg, rv, vec, a.vs + srow);
   }
 };
 
@@ -1207,10 +1200,20 @@ struct Epilogue {
     S::apply_store(a, p, sg, g, cur);
   }
 
-  // One tile with a rolling window of DEPTH passes in flight.
-  __device__ __forceinline__ void run_tile(const KArgs& a, const float* sG, int row0, int col0) {
+  // One tile with a rolling window of DEPTH passes in flight: prefetch()
+  // requests the first DEPTH passes (state only, no G needed), and
+  // run_prefetched() the rest of the tile.
+  __device__ __forceinline__ void prefetch(const KArgs& a, int row0, int col0) {
 #pragma unroll
     for (int s = 0; s < DEPTH && s < PASSES; ++s) issue(a, row0, col0, s, s);
+  }
+
+  __device__ __forceinline__ void run_tile(const KArgs& a, const float* sG, int row0, int col0) {
+    prefetch(a, row0, col0);
+    run_prefetched(a, sG, row0, col0);
+  }
+
+  __device__ __forceinline__ void run_prefetched(const KArgs& a, const float* sG, int row0, int col0) {
 #pragma unroll
     for (int s = 0; s < PASSES; ++s) {
       const int slot = s % DEPTH;
@@ -1235,11 +1238,21 @@ __global__ void __launch_bounds__(NT, 2) k_fused(const KArgs a) {
   int ti, tj;
   tile_coords(blockIdx.x, a.tiles_n, a.tiles_k, ti, tj);
   const int row0 = ti * TILE, col0 = tj * TILE;
-  if constexpr (FAST) tile_gradient_dma(a, lds, row0, col0);
-  else tile_gradient<IN>(a, lds, row0, col0);
+  // FAST: the state of the first passes is requested before the mainloop,
+  // so the HBM stream of this tile starts while its gradient is computed.
+  // These loads are older than every mainloop load, so the mainloop's
+  // in-order vmcnt waits still count exactly its own chunks.  (The
+  // register-staged mainloop has no registers to spare for it.)
   Epilogue<Step<OPT, WF, MF, VF, FAST>, FMT_NONE, FAST, 4, NT, ACC> epi;
   epi.tid = threadIdx.x;
-  epi.run_tile(a, reinterpret_cast<const float*>(lds), row0, col0);
+  if constexpr (FAST) {
+    epi.prefetch(a, row0, col0);
+    tile_gradient_dma(a, lds, row0, col0);
+  } else {
+    tile_gradient<IN>(a, lds, row0, col0);
+    epi.prefetch(a, row0, col0);
+  }
+  epi.run_prefetched(a, reinterpret_cast<const float*>(lds), row0, col0);
 }
 
 // Several independent layers in one launch: the workgroups cover the
@@ -1258,10 +1271,11 @@ __global__ void __launch_bounds__(NT, 2) k_fused_group(const GroupArgs g) {
   int ti, tj;
   tile_coords(bid - g.first_tile[li], a.tiles_n, a.tiles_k, ti, tj);
   const int row0 = ti * TILE, col0 = tj * TILE;
-  tile_gradient_dma(a, lds, row0, col0);
   Epilogue<Step<OPT, WF, MF, VF, true>, FMT_NONE, true, 4> epi;
   epi.tid = threadIdx.x;
-  epi.run_tile(a, reinterpret_cast<const float*>(lds), row0, col0);
+  epi.prefetch(a, row0, col0);                      // as in k_fused
+  tile_gradient_dma(a, lds, row0, col0);
+  epi.run_prefetched(a, reinterpret_cast<const float*>(lds), row0, col0);
 }
 
 // Wide variant for aligned bf16 layers with a long token axis: one 256 x 256
