@@ -11,11 +11,15 @@ HBM before timing starts.
 
 Launch grouping (--grouping).  A layer's update only has to follow the input
 gradient dX computed from its pre-update W (FORGE, Remark 1), so its weight
-step may wait until the end of its sub-block's backward.  Default "subblock":
-one forge_wgrad_step_group launch for the MLP ([gate, up, down]) and one for
-attention ([q, k, v, o]).  "ready": four launches as the layer gradients
-become available in backward order ([down], [gate, up], [o], [q, k, v]).
-"layer": seven forge_wgrad_step launches.  The work is the same in all three.
+step may wait until the end of the decoder layer's backward.  Default
+"block": one forge_wgrad_step_group launch for all seven layers after the
+decoder layer's backward (the activation gradients of the seven stay alive
+until then, ~44 MB at BT = 512).  "subblock": one launch for the MLP
+([gate, up, down]) and one for attention ([q, k, v, o]).  "ready": four
+launches as the layer gradients become available in backward order ([down],
+[gate, up], [o], [q, k, v]).  "layer": seven forge_wgrad_step launches.  The
+work is the same in all four; fewer launches pay the start of a launch (all
+workgroups computing G, no state streaming yet) and its drain fewer times.
 
 Prints one JSON line: params/s over the whole step, the fused kernel's
 achieved HBM bandwidth against the 8 TB/s peak (algorithmic bytes: state read
@@ -52,10 +56,10 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     p.add_argument("--no-unfused", action="store_true", help="skip the unfused comparison")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle work in seconds")
-    p.add_argument("--grouping", choices=["subblock", "ready", "layer"], default="subblock",
-                   help="subblock: one launch per sub-block, [gate, up, down] and [q, k, v, o]; ready: as the "
-                        "gradients become available, [down] [gate, up] [o] [q, k, v]; layer: one "
-                        "forge_wgrad_step launch per layer")
+    p.add_argument("--grouping", choices=["block", "subblock", "ready", "layer"], default="block",
+                   help="block: one launch for the decoder layer's seven; subblock: one launch per sub-block, "
+                        "[gate, up, down] and [q, k, v, o]; ready: as the gradients become available, [down] "
+                        "[gate, up] [o] [q, k, v]; layer: one forge_wgrad_step launch per layer")
     p.add_argument("--no-family-sweep", action="store_true",
                    help="skip the per-optimizer timing (gate_proj, BT 512, all eight families)")
     p.add_argument("--no-accumulation", action="store_true",
@@ -358,6 +362,8 @@ def main():
         groups = [(n,) for n in layers]
     elif args.grouping == "ready":
         groups = [("down_proj",), ("gate_proj", "up_proj"), ("o_proj",), ("q_proj", "k_proj", "v_proj")]
+    elif args.grouping == "block":
+        groups = [("gate_proj", "up_proj", "down_proj", "q_proj", "k_proj", "v_proj", "o_proj")]
     else:
         groups = [("gate_proj", "up_proj", "down_proj"), ("q_proj", "k_proj", "v_proj", "o_proj")]
     names = [",".join(g) for g in groups]

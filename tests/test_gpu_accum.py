@@ -44,6 +44,9 @@ def _spec(opt, state="f32", in_dtype="bf16", w="bf16"):
     if state == "int8":
         return synth.LayerSpec(in_dtype=in_dtype, w_fmt=w, m_fmt="s8" if opt in F.KEEPS_M else None,
                                v_fmt="u8" if opt in F.KEEPS_V else None, block=128)
+    if state == "e4m3":
+        return synth.LayerSpec(in_dtype=in_dtype, w_fmt=w, m_fmt="e4m3" if opt in F.KEEPS_M else None,
+                               v_fmt="e4m3" if opt in F.KEEPS_V else None, block=128)
     return synth.LayerSpec(in_dtype=in_dtype, w_fmt=w, m_fmt=state if opt in F.KEEPS_M else None,
                            v_fmt=state if opt in F.KEEPS_V else None)
 
@@ -87,8 +90,9 @@ def test_accumulator_strided_and_first_with_no_tokens():
     assert torch.isnan(big[:, K:]).all()
 
 
-CASES = [("adamw", "f32"), ("adamw", "bf16"), ("adamw", "int8"), ("lion", "f32"), ("sgdm", "bf16"),
-         ("nadam", "f32"), ("radam", "bf16"), ("rmsprop", "f32"), ("adagrad", "bf16"), ("sgd", None)]
+CASES = [("adamw", "f32"), ("adamw", "bf16"), ("adamw", "int8"), ("adamw", "e4m3"), ("lion", "f32"),
+         ("lion", "e4m3"), ("sgdm", "bf16"), ("sgdm", "e4m3"), ("nadam", "f32"), ("radam", "bf16"),
+         ("rmsprop", "f32"), ("adagrad", "bf16"), ("sgd", None)]
 
 
 @pytest.mark.parametrize("opt,state", CASES)
@@ -96,8 +100,8 @@ CASES = [("adamw", "f32"), ("adamw", "bf16"), ("adamw", "int8"), ("lion", "f32")
                                                (130, 136, (65, 33, 100), "bf16"),    # unaligned: accumulate, then step
                                                (128, 256, (50, 70), "f32")])         # fp32 inputs: accumulate, then step
 def test_step_accumulated_matches_oracle(opt, state, N, K, bts, in_dtype):
-    if state == "int8" and K % 128:
-        pytest.skip("int8 state needs K % 128 == 0")
+    if state in ("int8", "e4m3") and K % 128:
+        pytest.skip("8-bit block-scaled state needs K % 128 == 0")
     _say(f"case: accumulated step {opt} {state} {N}x{K} {bts} {in_dtype}")
     spec = _spec(opt, state or "f32", in_dtype)
     L = make_layer(22, N, K, 1, 8, spec, outlier_p=0.0)
@@ -117,7 +121,8 @@ def test_step_accumulated_matches_oracle(opt, state, N, K, bts, in_dtype):
     assert_ok(check_against_oracle(snap, L, h, 8, SEED), f"accumulated {opt} {state}")
 
 
-@pytest.mark.parametrize("opt,state", [("adamw", "f32"), ("adamw", "int8"), ("nadam", "bf16"), ("sgd", None)])
+@pytest.mark.parametrize("opt,state", [("adamw", "f32"), ("adamw", "int8"), ("adamw", "e4m3"), ("nadam", "bf16"),
+                                       ("sgd", None)])
 def test_fused_final_step_equals_accumulate_then_step(opt, state):
     """Fused kernel reading the accumulator == adding the last micro-batch
     into the accumulator first and stepping with no further tokens."""

@@ -122,12 +122,13 @@ def test_dgrad_full_size_llama_bt512(name):
 
 @pytest.mark.parametrize("opt,spec", [("adamw", synth.LayerSpec("bf16", "bf16", "f32", "f32")),
                                       ("rmsprop", synth.LayerSpec("bf16", "f32", None, "bf16")),
-                                      ("adamw", synth.LayerSpec("bf16", "bf16", "s8", "u8", block=128))])
+                                      ("adamw", synth.LayerSpec("bf16", "bf16", "s8", "u8", block=128)),
+                                      ("lion", synth.LayerSpec("bf16", "bf16", "e4m3", None, block=64))])
 @pytest.mark.parametrize("N,K,BT", [(512, 1024, 300), (130, 136, 65)])
 def test_backward_step_orders_dgrad_before_the_update(opt, spec, N, K, BT):
     """dX comes from the weight before the step; the step is forge_wgrad_step's, bit for bit."""
-    if spec.m_fmt == "s8" and K % 128:
-        pytest.skip("int8 state needs K % 128 == 0")
+    if spec.m_fmt in ("s8", "e4m3") and K % spec.block:
+        pytest.skip("8-bit block-scaled state needs K % block == 0")
     _say(f"case: backward step {opt} {N}x{K} BT{BT}")
     L = make_layer(31, N, K, BT, 6, spec)
     R = L.clone()
