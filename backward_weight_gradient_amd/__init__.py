@@ -109,6 +109,10 @@ def _load() -> ctypes.CDLL:
     lib.forge_backward_step.restype = st
     lib.forge_debug_e4m3.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
     lib.forge_debug_e4m3.restype = st
+    lib.forge_debug_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.forge_debug_copy.restype = st
+    lib.forge_debug_mfma_peak.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    lib.forge_debug_mfma_peak.restype = st
     lib.forge_status_str.argtypes = [ctypes.c_int]
     lib.forge_status_str.restype = ctypes.c_char_p
     lib.forge_version.argtypes = []
@@ -306,6 +310,27 @@ def forge_debug_e4m3(inp, out, stream=None, check: bool = True) -> int:
     rc = lib.forge_debug_e4m3(inp.data_ptr(), out.data_ptr(), inp.numel(), _stream(stream))
     if check and rc != FORGE_OK:
         raise ForgeError(rc, "forge_debug_e4m3")
+    return rc
+
+
+def forge_debug_copy(src, dst, stream=None, check: bool = True) -> int:
+    """dst = src through the streaming-ceiling copy kernel (measurement hook)."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("forge_debug_copy: src and dst sizes differ")
+    rc = lib.forge_debug_copy(src.data_ptr(), dst.data_ptr(), nbytes, _stream(stream))
+    if check and rc != FORGE_OK:
+        raise ForgeError(rc, "forge_debug_copy")
+    return rc
+
+
+def forge_debug_mfma_peak(out, blocks: int, iters: int, stream=None, check: bool = True) -> int:
+    """The matrix-core ceiling loop; `out` holds at least 256 * blocks floats (measurement hook)."""
+    if out.numel() < 256 * blocks or out.dtype != torch.float32:
+        raise ValueError("forge_debug_mfma_peak: out must be float32 with 256 * blocks elements")
+    rc = lib.forge_debug_mfma_peak(out.data_ptr(), blocks, iters, _stream(stream))
+    if check and rc != FORGE_OK:
+        raise ForgeError(rc, "forge_debug_mfma_peak")
     return rc
 
 

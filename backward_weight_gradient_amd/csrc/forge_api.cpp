@@ -561,6 +561,22 @@ forge_status forge_debug_e4m3(const float* in, uint8_t* out, int64_t n, void* st
   return hip_status(launch_debug_e4m3(in, out, (uint32_t)n, (hipStream_t)stream));
 }
 
+forge_status forge_debug_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+  if (bytes < 0 || bytes % 16 != 0) return FORGE_E_SHAPE;
+  if (bytes == 0) return FORGE_OK;
+  if (!src || !dst) return FORGE_E_NULL;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return FORGE_E_ALIGN;
+  if (overlap(raw_range(src, (uint64_t)bytes), raw_range(dst, (uint64_t)bytes))) return FORGE_E_ALIAS;
+  return hip_status(launch_debug_copy(src, dst, (uint64_t)bytes, (hipStream_t)stream));
+}
+
+forge_status forge_debug_mfma_peak(float* out, int32_t blocks, int32_t iters, void* stream) {
+  if (blocks < 1 || blocks > (1 << 20) || iters < 1 || iters > (1 << 20)) return FORGE_E_SHAPE;
+  if (!out) return FORGE_E_NULL;
+  if (!aligned(out, 4)) return FORGE_E_ALIGN;
+  return hip_status(launch_debug_mfma(out, blocks, iters, (hipStream_t)stream));
+}
+
 const char* forge_last_error(void) { return hipGetErrorString(g_last_hip); }
 
 const char* forge_status_str(forge_status s) {

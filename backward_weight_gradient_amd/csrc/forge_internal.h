@@ -169,5 +169,7 @@ hipError_t launch_debug_sr(const float* in, uint16_t* out, uint32_t n, uint32_t 
                            hipStream_t stream);
 // E4M3 rounding (nearest even, saturating) of n floats.
 hipError_t launch_debug_e4m3(const float* in, uint8_t* out, uint32_t n, hipStream_t stream);
+hipError_t launch_debug_copy(const void* src, void* dst, uint64_t bytes, hipStream_t stream);
+hipError_t launch_debug_mfma(float* out, int blocks, int iters, hipStream_t stream);
 
 }  // namespace forge

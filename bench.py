@@ -55,6 +55,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     p.add_argument("--no-unfused", action="store_true", help="skip the unfused comparison")
+    p.add_argument("--no-ceilings", action="store_true", help="skip the measured HBM and MFMA ceilings")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle work in seconds")
     p.add_argument("--grouping", choices=["block", "subblock", "ready", "layer"], default="block",
                    help="block: one launch for the decoder layer's seven; subblock: one launch per sub-block, "
@@ -293,6 +294,55 @@ def dgrad_sweep(F, L, layers, reps=5):
     return out
 
 
+def measured_ceilings(F, reps=5):
+    """The box's own ceilings through the library's measurement hooks: HBM read + write in the
+    fused epilogue's access width (a 1 GiB copy, 2 GiB moved; forge_debug_copy) and the matrix
+    cores in a register-only v_mfma_f32_32x32x16_bf16 loop (forge_debug_mfma_peak).  Medians of
+    `reps` launches timed with HIP events."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n // 4, device="cuda", dtype=torch.int32).random_()
+    dst = torch.empty_like(src)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return sorted(ts)[len(ts) // 2]
+
+    t_copy = timed(lambda: F.forge_debug_copy(src, dst))
+    del src, dst
+    blocks, iters = 2048, 4000
+    out = torch.empty(256 * blocks, device="cuda")
+    t_mfma = timed(lambda: F.forge_debug_mfma_peak(out, blocks, iters))
+    del out
+    torch.cuda.empty_cache()
+    gbs = 2 * n / t_copy / 1e9
+    tflops = blocks * 4 * iters * 131072 / t_mfma / 1e12
+    return {"hbm_copy_gbs": round(gbs, 1), "hbm_copy_frac_of_spec": round(gbs / HBM_PEAK_GBS, 4),
+            "mfma_bf16_tflops": round(tflops, 1), "mfma_frac_of_spec": round(tflops / BF16_PEAK_TFLOPS, 4),
+            "copy": "1 GiB device copy, 16-byte non-temporal loads and stores, a contiguous chunk per workgroup "
+                    "(2 GiB moved)",
+            "mfma": f"{blocks} workgroups x 4 waves x {iters} rounds of 4 independent 32x32x16 bf16 MFMAs"}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(layers, seconds):
     """The oracle on whole layers (k_proj first, then the others in turn)
     until about `seconds` of CPU time are spent; params/s over them."""
@@ -425,6 +475,8 @@ def main():
         "kernel_ms_per_step_mean": round(kernel_ms, 4),
         "mfma_util": round(flops_total / (kernel_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
         "per_launch_us_median": {n: round(1e3 * v, 2) for n, v in med.items()},
+        "per_launch_us_iqr": {n: [round(1e3 * v[len(v) // 4], 2), round(1e3 * v[(3 * len(v)) // 4], 2)]
+                              for n, v in per_layer.items()},
         "per_launch_gbs_median": {n: round(group_bytes(n) / (med[n] * 1e-3) / 1e9, 1) for n in names},
     }
 
@@ -476,7 +528,15 @@ def main():
         extras["compute_bound_sweep"] = mfma_sweep(F, synth, h)
 
     cpu = None
+    if not args.no_ceilings:
+        c = measured_ceilings(F)
+        extras["measured_ceilings"] = c
+        extras["roofline_frac_of_measured_hbm"] = round(achieved_gbs / c["hbm_copy_gbs"], 4)
+        for v in extras.get("compute_bound_sweep", {}).values():
+            v["mfma_frac_of_measured"] = round(v["tflops"] / c["mfma_bf16_tflops"], 4)
+
     if not args.no_cpu_baseline:
+        extras["cpu_model"] = cpu_model()
         cpu = cpu_baseline(layers, args.cpu_seconds)
 
     out = {

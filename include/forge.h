@@ -299,6 +299,26 @@ forge_status forge_debug_sr_bf16(const float* in, uint16_t* out, int64_t n, uint
  */
 forge_status forge_debug_e4m3(const float* in, uint8_t* out, int64_t n, void* stream);
 
+/*
+ * forge_debug_copy -- measurement hook for the HBM roofline (the pages
+ * measure their device's streaming bandwidth to quote fractions of it):
+ * copies `bytes` from src to dst in 16-byte non-temporal loads and stores
+ * (the fused epilogue's access width), one contiguous chunk per workgroup.  Device pointers,
+ * 16-byte aligned, non-overlapping; bytes a multiple of 16.  Errors: E_NULL,
+ * E_SHAPE (bytes < 0 or not a multiple of 16), E_ALIGN, E_ALIAS, E_HIP.
+ */
+forge_status forge_debug_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
+/*
+ * forge_debug_mfma_peak -- measurement hook for the matrix-core roofline:
+ * `blocks` workgroups of 4 waves; every wave runs `iters` rounds of four
+ * independent v_mfma_f32_32x32x16_bf16 (32,768 flops each) on register
+ * operands of ones, i.e. blocks * 4 * iters * 131,072 flops.  out: device
+ * array of 256 * blocks floats, each set to 64 * iters (exact).  Errors:
+ * E_NULL, E_SHAPE (blocks or iters outside 1 .. 2^20), E_ALIGN, E_HIP.
+ */
+forge_status forge_debug_mfma_peak(float* out, int32_t blocks, int32_t iters, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* forge_status_str(forge_status s);
 

@@ -179,6 +179,23 @@ def test_debug_sr_argument_errors():
     assert F.lib.forge_debug_sr_bf16(None, None, 0, 1, 1, 0, None) == F.FORGE_OK
 
 
+def test_measurement_hook_argument_errors():
+    """Validation of the ceiling hooks happens on the host, before any launch."""
+    c = F.lib.forge_debug_copy
+    assert c(addr(0), addr(1 << 20), -16, None) == F.FORGE_E_SHAPE
+    assert c(addr(0), addr(1 << 20), 24, None) == F.FORGE_E_SHAPE       # not a multiple of 16
+    assert c(None, addr(1 << 20), 32, None) == F.FORGE_E_NULL
+    assert c(addr(0) + 8, addr(1 << 20), 32, None) == F.FORGE_E_ALIGN
+    assert c(addr(0), addr(0) + 16, 64, None) == F.FORGE_E_ALIAS
+    assert c(None, None, 0, None) == F.FORGE_OK                        # nothing to do
+    m = F.lib.forge_debug_mfma_peak
+    assert m(addr(0), 0, 10, None) == F.FORGE_E_SHAPE
+    assert m(addr(0), 4, 0, None) == F.FORGE_E_SHAPE
+    assert m(addr(0), (1 << 20) + 1, 10, None) == F.FORGE_E_SHAPE
+    assert m(None, 4, 10, None) == F.FORGE_E_NULL
+    assert m(addr(0) + 2, 4, 10, None) == F.FORGE_E_ALIGN
+
+
 def test_unfused_argument_errors():
     X, dY, W, m, v = layer()
     h = F.hyper()
