@@ -75,11 +75,14 @@ __device__ __forceinline__ uint32_t fmix32(uint32_t h) {
 // adds 16 random bits instead and truncates: the carry into the kept half
 // happens with probability (x - x_lo)/ULP.  Inf and NaN keep their pattern
 // (NaN made quiet) in both modes.
+// Written as masks and selects of constants: non-finite values add nothing
+// (infinity keeps its pattern, NaN gets the quiet bit), so no per-element
+// branch is needed.
 __device__ __forceinline__ uint32_t bf16_bits_add(float x, uint32_t add) {
   const uint32_t u = __float_as_uint(x);
-  const bool finite = (u & 0x7F800000u) != 0x7F800000u;
-  const bool nan = (u & 0x7FFFFFFFu) > 0x7F800000u;
-  return finite ? (u + add) >> 16 : ((u >> 16) | (nan ? 0x40u : 0u));
+  const uint32_t nonfinite = (u & 0x7F800000u) == 0x7F800000u ? 0xFFFFFFFFu : 0u;
+  const uint32_t quiet = (u & 0x7FFFFFFFu) > 0x7F800000u ? 0x40u : 0u;
+  return ((u + (add & ~nonfinite)) >> 16) | quiet;
 }
 
 __device__ __forceinline__ uint32_t bf16_rne_bits(float x) {

@@ -224,6 +224,21 @@ def test_debug_sr_matches_oracle_and_is_unbiased():
         np.testing.assert_array_equal(synth.host(out[: xr.numel()]), ref)
 
 
+def test_debug_sr_special_values():
+    """Infinities keep their pattern, NaNs come out quiet (signalling ones too), values at the edge of
+    the bf16 range may round up to infinity, zeros keep their sign, denormals round stochastically."""
+    bits = np.array([0x7F800000, 0xFF800000, 0x7FC00000, 0x7F800001, 0xFF800123, 0x7FFFFFFF, 0xFFFFFFFF,
+                     0x7F7FFFFF, 0xFF7FFFFF, 0x7F7F8000, 0x00000000, 0x80000000, 0x00000001, 0x807FFFFF,
+                     0x3F800001, 0xBF80FFFF], dtype=np.uint32)
+    x = np.tile(bits, 4096).view(np.float32)
+    out = torch.empty(x.size, dtype=torch.bfloat16, device="cuda")
+    for tid in (0, 2):
+        F.forge_debug_sr_bf16(torch.from_numpy(x).cuda(), out, 7, 3, tid)
+        torch.cuda.synchronize()
+        ref = O.f32_to_bf16_sr(x, O.sr_bits(O.sr_key(7, 3, tid), np.arange(x.size)))
+        np.testing.assert_array_equal(synth.host(out), ref)
+
+
 # ---------------------------------------------------------------------------
 # Full sizes (sampled rows and column blocks)
 # ---------------------------------------------------------------------------
