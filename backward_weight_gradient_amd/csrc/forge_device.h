@@ -998,7 +998,7 @@ __device__ __forceinline__ void quantize_chunk(const float (&x)[8], int block, c
       }
     }
     if (!sg[g].ok) continue;
-    if (writer && (block != 128 || g == 0)) row_scales[sg[g].q / block] = sc[g];
+    if (writer && (block != 128 || g == 0)) row_scales[sg[g].q >> __builtin_ctz((unsigned)block)] = sc[g];
     uint8_t* p = static_cast<uint8_t*>(row_codes) + sg[g].q;
     if (vec) {
       st_nt<uint32_t>(p, word);
@@ -1026,7 +1026,9 @@ struct Step {
   __device__ __forceinline__ static void load(const KArgs& a, int p, const Seg (&sg)[2], Pending& r) {
     const bool vec = a.vec_state != 0;
     const char* rw = static_cast<const char*>(a.W) + (int64_t)p * a.ldw * (WF == FMT_F32 ? 4 : 2);
-    const int64_t srow = (int64_t)p * (a.K / a.block);
+    // block is 32, 64 or 128: the scale index is a shift (a runtime division costs ~18 VALU)
+    const int bsh = __builtin_ctz((unsigned)a.block);
+    const int64_t srow = (int64_t)p * (a.K >> bsh);
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       if (!sg[g].ok) {
@@ -1037,12 +1039,12 @@ struct Step {
       if constexpr (HAS_M) {
         const char* rm = static_cast<const char*>(a.m) + (int64_t)p * a.ldm * (MF == FMT_F32 ? 4 : MF == FMT_BF16 ? 2 : 1);
         ld4<MF, FAST>(r.m[g], rm, sg[g], vec);
-        if constexpr (fmt_blocked(MF)) r.m[g].s = a.ms[srow + sg[g].q / a.block];
+        if constexpr (fmt_blocked(MF)) r.m[g].s = a.ms[srow + (sg[g].q >> bsh)];
       }
       if constexpr (HAS_V) {
         const char* rv = static_cast<const char*>(a.v) + (int64_t)p * a.ldv * (VF == FMT_F32 ? 4 : VF == FMT_BF16 ? 2 : 1);
         ld4<VF, FAST>(r.v[g], rv, sg[g], vec);
-        if constexpr (fmt_blocked(VF)) r.v[g].s = a.vs[srow + sg[g].q / a.block];
+        if constexpr (fmt_blocked(VF)) r.v[g].s = a.vs[srow + (sg[g].q >> bsh)];
       }
     }
   }
@@ -1121,7 +1123,7 @@ struct Step {
       if constexpr (HAS_M && !fmt_blocked(MF)) st4<MF, FAST>(rm, sg[s], vec, m + 4 * s, a.c.sr, a.c.keyM, idx_mul);
       if constexpr (HAS_V && !fmt_blocked(VF)) st4<VF, FAST>(rv, sg[s], vec, v + 4 * s, a.c.sr, a.c.keyV, idx_mul);
     }
-    const int64_t srow = (int64_t)p * (a.K / a.block);
+    const int64_t srow = (int64_t)p * (a.K >> __builtin_ctz((unsigned)a.block));
     if constexpr (HAS_M && fmt_blocked(MF)) quantize_chunk<MF, false>(m, a.block, sg, rm, vec, a.ms + srow);
     if constexpr (HAS_V && fmt_blocked(VF)) quantize_chunk<VF, true>(v, a.block, sg, rv, vec, a.vs + srow);
   }
