@@ -65,9 +65,10 @@ struct DgradLoader {
   bool bOk[2];
   int wave;
 
-  __device__ __forceinline__ void init(const DgArgs& g, int tok0, int col0) {
-    const int lane = threadIdx.x & 63;
-    wave = threadIdx.x >> 6;
+  // gtid: thread index within the 256 threads of one reduction group
+  __device__ __forceinline__ void init(const DgArgs& g, int tok0, int col0, int gtid) {
+    const int lane = gtid & 63;
+    wave = gtid >> 6;
     oobA = (uint32_t)((uint64_t)g.BT * g.lddy * 2);
     oobB = (uint32_t)((uint64_t)g.N * g.ldw * 2);
     rA = make_rsrc(g.dY, oobA);
@@ -130,18 +131,29 @@ __device__ __forceinline__ void dg_wait(u32x4 (&a)[1], u32x2 (&b)[4]) {
 
 }  // namespace
 
-template <int TM, int S>
-__global__ void __launch_bounds__(NT, 2) k_dgrad_bf16(const DgArgs g) {
+// KG reduction groups of 4 waves per workgroup (at most 4: 1024 threads): group k takes the chunks
+// k, k + KG, k + 2 KG, ... through a ring of its own (chunks past the end
+// read zero, so every group runs the same iterations and barriers), and the
+// groups' partial tiles are added through LDS in a fixed order.  KG = 2
+// serves the short-token, long-reduction layers, whose few tiles would
+// otherwise leave one 4-wave workgroup per CU with every per-chunk latency
+// exposed.
+template <int TM, int S, int KG>
+__global__ void __launch_bounds__(NT * KG, KG == 1 ? 2 : 1) k_dgrad_bf16(const DgArgs g) {
+  static_assert(KG >= 1 && KG <= 4, "at most 1024 threads per workgroup");
   using SH = DgShape<TM, S>;
   constexpr int BI = TM / 64;                        // 32-row MFMA blocks per wave
-  __shared__ __attribute__((aligned(16))) char lds[SH::LDS];
+  constexpr int RINGS = KG * S * SH::STAGE;
+  __shared__ __attribute__((aligned(16))) char lds[RINGS > SH::LDS ? RINGS : SH::LDS];
   // W panels are shared by the token tiles of one column: those run together
   const int tiles_m = (g.BT + TM - 1) / TM;
   const int tj = (int)blockIdx.x / tiles_m, ti = (int)blockIdx.x - tj * tiles_m;
   const int tok0 = ti * TM, col0 = tj * TILE;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int kg = (int)threadIdx.x / NT, gtid = (int)threadIdx.x - kg * NT;
+  const int lane = gtid & 63, wave = gtid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)lds;
+  char* ring = lds + kg * S * SH::STAGE;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)ring;
   f32x16 acc[BI][2];
 #pragma unroll
   for (int bi = 0; bi < BI; ++bi)
@@ -150,16 +162,17 @@ __global__ void __launch_bounds__(NT, 2) k_dgrad_bf16(const DgArgs g) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[bi][bj][e] = 0.f;
   const int nk = (g.N + DG_TN - 1) / DG_TN;
+  const int nj = (nk + KG - 1) / KG;                 // iterations of every group
   DgradLoader<TM, S> ld;
-  ld.init(g, tok0, col0);
+  ld.init(g, tok0, col0, gtid);
 #pragma unroll
   for (int k = 0; k < S - 1; ++k)
-    if (k < nk) ld.issue(g, k, lds + k * SH::STAGE);
-  for (int kc = 0; kc < nk; ++kc) {
-    dg_wait_ahead<SH::LOADS, S - 2>(min(S - 2, nk - 1 - kc));   // chunk kc landed
+    if (k < nj) ld.issue(g, kg + KG * k, ring + k * SH::STAGE);
+  for (int j = 0; j < nj; ++j) {
+    dg_wait_ahead<SH::LOADS, S - 2>(min(S - 2, nj - 1 - j));   // chunk j of this group landed
     bar();
-    if (kc + S - 1 < nk) ld.issue(g, kc + S - 1, lds + ((kc + S - 1) % S) * SH::STAGE);
-    const uint32_t cur = lds0 + (uint32_t)((kc % S) * SH::STAGE);
+    if (j + S - 1 < nj) ld.issue(g, kg + KG * (j + S - 1), ring + ((j + S - 1) % S) * SH::STAGE);
+    const uint32_t cur = lds0 + (uint32_t)((j % S) * SH::STAGE);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       u32x4 af[BI];
@@ -184,25 +197,51 @@ __global__ void __launch_bounds__(NT, 2) k_dgrad_bf16(const DgArgs g) {
   }
   wait_vmcnt<0>();
   bar();
-  // stage the fp32 tile: lane l, register 4j+i of a 32 x 32 block holds row 8j + 4(l/32) + i, column l % 32
+  // lane l, register 4j+i of a 32 x 32 block holds row 8j + 4(l/32) + i, column l % 32
   float* sG = reinterpret_cast<float*>(lds);
+  auto g_at = [&](int bi, int bj, int e) -> float& {
+    const int r = wr * (TM / 2) + bi * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+    const int c = wc * 64 + bj * 32 + (lane & 31);
+    return sG[r * SH::GP_ + c];
+  };
+  // group 0's partial + group 1's + ... in that order, through LDS
+  for (int k = 1; k < KG; ++k) {
+    if (kg == k) {
 #pragma unroll
-  for (int bi = 0; bi < BI; ++bi)
+      for (int bi = 0; bi < BI; ++bi)
 #pragma unroll
-    for (int bj = 0; bj < 2; ++bj)
+        for (int bj = 0; bj < 2; ++bj)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int r = wr * (TM / 2) + bi * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        const int c = wc * 64 + bj * 32 + (lane & 31);
-        sG[r * SH::GP_ + c] = acc[bi][bj][e];
-      }
+          for (int e = 0; e < 16; ++e) g_at(bi, bj, e) = acc[bi][bj][e];
+    }
+    __syncthreads();
+    if (kg == 0) {
+#pragma unroll
+      for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[bi][bj][e] = acc[bi][bj][e] + g_at(bi, bj, e);
+    }
+    __syncthreads();
+  }
+  // stage the fp32 tile
+  if (kg == 0) {
+#pragma unroll
+    for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) g_at(bi, bj, e) = acc[bi][bj][e];
+  }
   __syncthreads();
+  if (kg != 0) return;
   // write out: pass s, thread t -> row s*16 + t/16, two 4-column segments 64 apart
-  const int cl = 4 * (threadIdx.x & 15);
+  const int cl = 4 * (gtid & 15);
   const bool vec = g.vec_out != 0;
 #pragma unroll
   for (int s = 0; s < TM / 16; ++s) {
-    const int rl = s * 16 + (threadIdx.x >> 4);
+    const int rl = s * 16 + (gtid >> 4);
     const int p = tok0 + rl;
     if (p >= g.BT) continue;
     char* rowp = static_cast<char*>(g.dX) + (int64_t)p * g.ldx * (g.dx_fmt == FMT_F32 ? 4 : 2);
@@ -291,11 +330,13 @@ hipError_t launch_dgrad(const DgArgs& g, bool fast, hipStream_t st) {
     // three workgroups per CU (measured: a deeper ring does not help them --
     // with 4 MFMAs per wave and chunk the per-chunk overhead dominates)
     const int64_t t128 = (int64_t)((g.BT + 127) / 128) * g.tiles_k;
+    const int64_t t64 = (int64_t)((g.BT + 63) / 64) * g.tiles_k;
     if (t128 >= 256) {
-      hipLaunchKernelGGL((k_dgrad_bf16<128, 4>), dim3((unsigned)t128), dim3(NT), 0, st, g);
+      hipLaunchKernelGGL((k_dgrad_bf16<128, 4, 1>), dim3((unsigned)t128), dim3(NT), 0, st, g);
+    } else if (t64 < 512 && g.N >= 8 * DG_TN) {
+      hipLaunchKernelGGL((k_dgrad_bf16<64, 4, 2>), dim3((unsigned)t64), dim3(2 * NT), 0, st, g);
     } else {
-      const unsigned t64 = (unsigned)(((g.BT + 63) / 64) * g.tiles_k);
-      hipLaunchKernelGGL((k_dgrad_bf16<64, 4>), dim3(t64), dim3(NT), 0, st, g);
+      hipLaunchKernelGGL((k_dgrad_bf16<64, 4, 1>), dim3((unsigned)t64), dim3(NT), 0, st, g);
     }
   } else {
     const unsigned tiles = (unsigned)(((g.BT + DGG_T - 1) / DGG_T) * ((g.K + DGG_T - 1) / DGG_T));
