@@ -24,7 +24,7 @@
  *     row-major index p*K + q, independent of ld.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *     stream) and return after the kernels are enqueued.  W, m, v and the
- *     int8 scales are updated in place.
+ *     block scales (int8 / E4M3 states) are updated in place.
  *   - Argument validation is synchronous and host-only.  On any error code
  *     other than FORGE_E_HIP nothing has been enqueued and nothing modified.
  *   - No exception crosses the ABI.  The library keeps no mutable global
@@ -176,7 +176,7 @@ forge_status forge_wgrad_step(const forge_mat* X, const forge_mat* dY, forge_mat
  * own SR seed.  The result equals n separate forge_wgrad_step calls, bit for
  * bit.  Layers may share inputs (q/k/v read the same X) but nothing a layer
  * writes (W, m, v, scales) may overlap any buffer of another layer.  All
- * non-empty layers must have the same X / W / m / v dtypes and int8 block;
+ * non-empty layers must have the same X / W / m / v dtypes and block size;
  * shapes and BT may differ.  Aligned bf16 layers with BT < 3072 run in one
  * launch; any other layer gets its own launch, on the same stream.
  *
@@ -294,7 +294,8 @@ forge_status forge_debug_sr_bf16(const float* in, uint16_t* out, int64_t n, uint
 /*
  * forge_debug_e4m3 -- test hook: the device's E4M3 rounding (nearest, ties
  * to even, saturating at 448; the element code of the E4M3 state format) of
- * n floats, out[i] = code of in[i].  Device pointers.  Errors: E_NULL,
+ * n floats, out[i] = code of in[i], through the same four-value packing the
+ * fused step uses.  Device pointers.  Errors: E_NULL,
  * E_SHAPE (n < 0 or n >= 2^32), E_ALIGN, E_ALIAS, E_HIP.
  */
 forge_status forge_debug_e4m3(const float* in, uint8_t* out, int64_t n, void* stream);
