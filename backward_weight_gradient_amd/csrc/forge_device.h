@@ -433,23 +433,23 @@ __device__ __forceinline__ void tile_gradient_dma(const KArgs& a, char* lds, int
 }
 
 // ------------------------------------------------------------------------
-// Wide mainloop for long token axes: a 256 x 256 macro tile per workgroup,
-// 4 waves in a 2 x 2 arrangement of 128 x 128 sub-tiles (16 accumulator
-// blocks per wave, 256 accumulator registers).  Per token the workgroup
-// fetches 1 KiB of dY and X for 128 Ki MFMA flops, half the bytes per flop
-// of the 128 x 128 tile, which matters once BT is long enough that the
-// activation panels no longer stay in L2.  Same asynchronous LDS-DMA ring
-// (4 stages of 32 tokens, 512-byte rows XOR-swizzled in 64-byte units) and
-// transposing reads as MainBF16Dma.
+// Wide mainloop for long token axes: a 256 x 256 macro tile per workgroup.
+// Per token the workgroup fetches 1 KiB of dY and X for 128 Ki MFMA flops,
+// half the bytes per flop of the 128 x 128 tile, which matters once BT is
+// long enough that the activation panels no longer stay in L2.  Same
+// asynchronous LDS-DMA ring (4 stages of 32 tokens, 512-byte rows
+// XOR-swizzled in 64-byte units) and transposing reads as MainBF16Dma; NW
+// waves share the ring, each issuing its share of a chunk's 32 1-KiB loads.
 // ------------------------------------------------------------------------
-struct MainWide {
+template <int NW>                                       // waves sharing the ring
+struct MainWideT {
   static constexpr int TK = 32;
   static constexpr int S = 4;
   static constexpr int W = 256;                         // macro tile edge
   static constexpr int ROWB = W * 2;                    // bytes per token row
   static constexpr int OPB = TK * ROWB;                 // 16 KiB per operand per stage
   static constexpr int STAGE = 2 * OPB;                 // 32 KiB
-  static constexpr int ROUNDS = OPB / (NT * 16);        // 4 load rounds per operand per chunk
+  static constexpr int ROUNDS = OPB / (NW * 64 * 16);   // load rounds per operand per chunk (4 waves: 4)
   static constexpr int LOADS = 2 * ROUNDS;              // buffer loads per thread per chunk
 
   __amdgpu_buffer_rsrc_t rA, rB;
@@ -470,8 +470,8 @@ struct MainWide {
     rB = make_rsrc(a.X, oobB);
 #pragma unroll
     for (int r = 0; r < ROUNDS; ++r) {
-      // instruction (wave, r) fills bytes [(4r + wave) KiB, +1 KiB) of the operand region: 2 token rows
-      const int t = 2 * (4 * r + wave) + (lane >> 5);
+      // instruction (wave, r) fills bytes [(NW r + wave) KiB, +1 KiB) of the operand region: 2 token rows
+      const int t = 2 * (NW * r + wave) + (lane >> 5);
       const int c = (lane & 31) ^ ((t & 3) << 2);        // logical 8-feature chunk at this slot
       trow[r] = t;
       fokA[r] = row0 + c * 8 < a.N;
@@ -490,23 +490,20 @@ struct MainWide {
     const bool tok_ok = tok < a.BT;
     if constexpr ((J & 1) == 0) {
       const uint32_t oa = (tok_ok && fokA[r]) ? (uint32_t)tok * (uint32_t)(a.lddy * 2) + baseA[r] : oobA;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void*)(stage + (4 * r + wave) * 1024), 16, oa, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void*)(stage + (NW * r + wave) * 1024), 16, oa, 0, 0, 0);
     } else {
       const uint32_t ob = (tok_ok && fokB[r]) ? (uint32_t)tok * (uint32_t)(a.ldx * 2) + baseB[r] : oobB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void*)(stage + OPB + (4 * r + wave) * 1024), 16, ob, 0, 0,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void*)(stage + OPB + (NW * r + wave) * 1024), 16, ob, 0, 0,
                                                0);
     }
   }
 
   __device__ __forceinline__ void issue(const KArgs& a, int kc, char* stage) const {
-    issue_one<0>(a, kc, stage);
-    issue_one<1>(a, kc, stage);
-    issue_one<2>(a, kc, stage);
-    issue_one<3>(a, kc, stage);
-    issue_one<4>(a, kc, stage);
-    issue_one<5>(a, kc, stage);
-    issue_one<6>(a, kc, stage);
-    issue_one<7>(a, kc, stage);
+    issue_seq(a, kc, stage, std::make_integer_sequence<int, LOADS>{});
+  }
+  template <int... J>
+  __device__ __forceinline__ void issue_seq(const KArgs& a, int kc, char* stage, std::integer_sequence<int, J...>) const {
+    (issue_one<J>(a, kc, stage), ...);
   }
 };
 
@@ -519,111 +516,122 @@ __device__ __forceinline__ u32x2 tr_read_at(uint32_t lds_addr) {
   return v;
 }
 
-// Wait for every outstanding LDS read; ties the sixteen fragment registers of
-// one k-step to the wait so no use moves above it.
-__device__ __forceinline__ void lds_wait_all(u32x2 (&f)[16]) {
-  asm volatile("s_waitcnt lgkmcnt(0)"
-               : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5]), "+v"(f[6]), "+v"(f[7]),
-                 "+v"(f[8]), "+v"(f[9]), "+v"(f[10]), "+v"(f[11]), "+v"(f[12]), "+v"(f[13]), "+v"(f[14]),
-                 "+v"(f[15]));
-}
+// ------------------------------------------------------------------------
+// The wide mainloop's waves: 8 in a 2 x 4 arrangement of 128 x 64 parts (8
+// accumulator blocks, 128 registers per wave), so two waves share each SIMD
+// and one's LDS-read, load-issue and barrier stalls overlap the other's
+// MFMAs (measured 9% faster at BT = 8192 than 4 waves holding 128 x 128
+// each, one per SIMD).  Per 16-token k-step a wave runs 8 MFMAs and reads
+// 12 fragments of the next k-step (4 dY blocks, 2 X blocks, two halves
+// each), the reads and its 4 loads per chunk interleaved with the MFMAs and
+// pinned by a scheduling barrier, so LDS latency and the address unit's
+// queue drain behind the matrix pipe instead of stalling the wave's in-order
+// issue.  The k-steps run in token order, so every element of G sees the
+// MFMA sequence of the other mainloops.
+// ------------------------------------------------------------------------
+using MainWide = MainWideT<8>;
 
-// One MFMA of a 16-token k-step on the wave's 128 x 128 sub-tile (block
-// I / 4, I % 4), followed, when READ, by read I of the next k-step's
-// fragments and, when DMA and I is even, by load I / 2 of the wave's share of
-// chunk kdma.  Fragment register r of a k-step: operand r / 8 (dY, X),
-// 32-wide block (r / 2) % 4, token half r % 2; adr[r / 2] is its LDS address
-// at token 0 of the stage and the immediate adds the k-step's first token T0
-// and the half.  The scheduling barrier keeps this order, so LDS latency and
-// the address unit's queue drain behind the matrix pipe instead of stalling
-// the wave's in-order issue.
+// Fragment registers of a k-step: 0..7 dY blocks (r / 2, half r % 2),
+// 8..11 X blocks ((r - 8) / 2, half r % 2); adr[0..3] dY blocks, adr[4..5]
+// X blocks at token 0 of the stage.  MFMA slot I reads fragment I and, when
+// I is even, fragment 8 + I / 2; when DMA and I is even it issues load I / 2.
 template <bool READ, bool DMA, int T0, int I>
-__device__ __forceinline__ void wide_one(f32x16 (&acc)[4][4], const u32x2 (&cur)[16], u32x2 (&nxt)[16],
-                                         const uint32_t (&adr)[8], const MainWide& ml, const KArgs& a, int kdma,
-                                         char* dstage) {
-  constexpr int bi = I >> 2, bj = I & 3;
+__device__ __forceinline__ void wide_one(f32x16 (&acc)[4][2], const u32x2 (&cur)[12], u32x2 (&nxt)[12],
+                                       const uint32_t (&adr)[6], const MainWide& ml, const KArgs& a, int kdma,
+                                       char* dstage) {
+  constexpr int bi = I >> 1, bj = I & 1;
   acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_join(cur[2 * bi], cur[2 * bi + 1]),
                                                         frag_join(cur[8 + 2 * bj], cur[8 + 2 * bj + 1]),
                                                         acc[bi][bj], 0, 0, 0);
-  if constexpr (READ) nxt[I] = tr_read_at<(T0 + 4 * (I & 1)) * MainWide::ROWB>(adr[I >> 1]);
+  if constexpr (READ) {
+    nxt[I] = tr_read_at<(T0 + 4 * (I & 1)) * MainWide::ROWB>(adr[I >> 1]);
+    if constexpr ((I & 1) == 0) {
+      constexpr int R = 8 + I / 2;
+      nxt[R] = tr_read_at<(T0 + 4 * (R & 1)) * MainWide::ROWB>(adr[4 + ((R - 8) >> 1)]);
+    }
+  }
   if constexpr (DMA && (I & 1) == 0) ml.template issue_one<I / 2>(a, kdma, dstage);
   __builtin_amdgcn_sched_barrier(0);
 }
 
 template <bool READ, bool DMA, int T0, int... I>
-__device__ __forceinline__ void wide_kstep_seq(f32x16 (&acc)[4][4], const u32x2 (&cur)[16], u32x2 (&nxt)[16],
-                                               const uint32_t (&adr)[8], const MainWide& ml, const KArgs& a,
-                                               int kdma, char* dstage, std::integer_sequence<int, I...>) {
+__device__ __forceinline__ void wide_kstep_seq(f32x16 (&acc)[4][2], const u32x2 (&cur)[12], u32x2 (&nxt)[12],
+                                             const uint32_t (&adr)[6], const MainWide& ml, const KArgs& a, int kdma,
+                                             char* dstage, std::integer_sequence<int, I...>) {
   (wide_one<READ, DMA, T0, I>(acc, cur, nxt, adr, ml, a, kdma, dstage), ...);
 }
 
 template <bool READ, bool DMA, int T0>
-__device__ __forceinline__ void wide_kstep(f32x16 (&acc)[4][4], const u32x2 (&cur)[16], u32x2 (&nxt)[16],
-                                           const uint32_t (&adr)[8], const MainWide& ml, const KArgs& a, int kdma,
-                                           char* dstage) {
-  wide_kstep_seq<READ, DMA, T0>(acc, cur, nxt, adr, ml, a, kdma, dstage, std::make_integer_sequence<int, 16>{});
+__device__ __forceinline__ void wide_kstep(f32x16 (&acc)[4][2], const u32x2 (&cur)[12], u32x2 (&nxt)[12],
+                                         const uint32_t (&adr)[6], const MainWide& ml, const KArgs& a, int kdma,
+                                         char* dstage) {
+  static_assert(MainWide::LOADS == 4, "one load per even MFMA slot");
+  wide_kstep_seq<READ, DMA, T0>(acc, cur, nxt, adr, ml, a, kdma, dstage, std::make_integer_sequence<int, 8>{});
 }
 
-// Accumulate the wave's 128 x 128 sub-tile of the macro tile at (row0, col0).
-// Software pipeline: the fragments of each k-step are read from LDS while
-// the previous k-step's 16 MFMAs run.  The one barrier per chunk sits between
-// the chunk's two k-steps: by then every wave has finished reading the chunk,
-// so its stage is refilled with the chunk S ahead, and the next chunk has
+__device__ __forceinline__ void lds_wait12(u32x2 (&f)[12]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5]), "+v"(f[6]), "+v"(f[7]),
+                 "+v"(f[8]), "+v"(f[9]), "+v"(f[10]), "+v"(f[11]));
+}
+
+// Accumulate the wave's 128 x 64 part of the macro tile at (row0, col0).
+// Software pipeline: the fragments of each k-step are read while the
+// previous k-step's MFMAs run.  The one barrier per chunk sits between the
+// chunk's two k-steps: by then every wave has finished reading the chunk, so
+// its stage is refilled with the chunk S ahead, and the next chunk has
 // landed, so its first k-step can be read during the second k-step here.
+// Loads past the last chunk zero-fill a stage never read again, so every
+// vmcnt wait is a constant.
 __device__ __forceinline__ void wide_accumulate(const KArgs& a, char* ring, int row0, int col0,
-                                                f32x16 (&acc)[4][4]) {
+                                                 f32x16 (&acc)[4][2]) {
   using M = MainWide;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wr = wave >> 1, wc = wave & 1;
+  const int wr = wave >> 2, wc = wave & 3;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)ring;
 #pragma unroll
   for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-    for (int bj = 0; bj < 4; ++bj)
+    for (int bj = 0; bj < 2; ++bj)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[bi][bj][e] = 0.f;
   const int nk = (a.BT + M::TK - 1) / M::TK;
   if (nk == 0) return;
   M ml;
   ml.init(a, row0, col0);
-  // lane part of the fragment addresses (token row and swizzled feature byte within a stage)
-  uint32_t off[8];
+  uint32_t off[6];
   {
     const int tl = 8 * (lane >> 5) + ((lane & 15) >> 2);
     const int fl = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      off[b] = (uint32_t)M::off(tl, wr * 128 + b * 32 + fl);
-      off[4 + b] = (uint32_t)(M::OPB + M::off(tl, wc * 128 + b * 32 + fl));
-    }
+    for (int b = 0; b < 4; ++b) off[b] = (uint32_t)M::off(tl, wr * 128 + b * 32 + fl);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) off[4 + b] = (uint32_t)(M::OPB + M::off(tl, wc * 64 + b * 32 + fl));
   }
-  // Every chunk slot gets its loads, real or (past the last chunk) zero
-  // fills of a stage that is never read again, so the waits are constant.
   static_assert(M::S == 4, "the waits below assume 4 stages");
 #pragma unroll
   for (int k = 0; k < M::S; ++k) ml.issue(a, k, ring + k * M::STAGE);
   wait_vmcnt<3 * M::LOADS>();   // chunk 0
   bar();
-  u32x2 f0[16], f1[16];
-  uint32_t adr[8];
+  u32x2 f0[12], f1[12];
+  uint32_t adr[6];
 #pragma unroll
-  for (int r = 0; r < 8; ++r) adr[r] = lds0 + off[r];
+  for (int r = 0; r < 6; ++r) adr[r] = lds0 + off[r];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) f0[r] = tr_read(adr[r >> 1] + (uint32_t)(4 * (r & 1) * M::ROWB));
-  lds_wait_all(f0);
+  for (int r = 0; r < 12; ++r)
+    f0[r] = tr_read(adr[r < 8 ? (r >> 1) : 4 + ((r - 8) >> 1)] + (uint32_t)(4 * (r & 1) * M::ROWB));
+  lds_wait12(f0);
   for (int kc = 0; kc < nk; ++kc) {
     wide_kstep<true, false, 16>(acc, f0, f1, adr, ml, a, 0, ring);   // k-step 0 of chunk kc; read k-step 1
-    lds_wait_all(f1);
-    wait_vmcnt<2 * M::LOADS>();   // chunk kc + 1 (chunks kc + 2, kc + 3 may stay in flight)
+    lds_wait12(f1);
+    wait_vmcnt<2 * M::LOADS>();   // chunk kc + 1
     bar();                        // all waves done with stage kc % S; chunk kc + 1 visible
-    // After the last chunk the reads below fetch a stale stage (inside the
-    // ring) and their values are never used.
     const uint32_t st = lds0 + (uint32_t)(((kc + 1) % M::S) * M::STAGE);
 #pragma unroll
-    for (int r = 0; r < 8; ++r) adr[r] = st + off[r];
+    for (int r = 0; r < 6; ++r) adr[r] = st + off[r];
     // k-step 1 of chunk kc; read k-step 0 of chunk kc + 1; refill stage kc % S with chunk kc + S
     wide_kstep<true, true, 0>(acc, f1, f0, adr, ml, a, kc + M::S, ring + (kc % M::S) * M::STAGE);
-    lds_wait_all(f0);
+    lds_wait12(f0);
   }
   wait_vmcnt<0>();
 }
@@ -1283,39 +1291,40 @@ __global__ void __launch_bounds__(NT, 2) k_fused_group(const GroupArgs g) {
   epi.run_prefetched(a, reinterpret_cast<const float*>(lds), row0, col0);
 }
 
-// Wide variant for aligned bf16 layers with a long token axis: one 256 x 256
-// macro tile per workgroup (one workgroup per CU: the ring takes 128 KiB of
-// LDS, the 256 accumulator registers of a wave the rest of the register
-// file).  After the mainloop the four 128 x 128 sub-tiles are staged through
-// LDS one at a time and run through the same epilogue as k_fused.
 constexpr int LDS_WIDE = MainWide::S * MainWide::STAGE;   // 128 KiB
 static_assert(LDS_WIDE >= LDS_G, "the staged G tile aliases the ring");
 
+// Wide variant for aligned bf16 layers with a long token axis: one 256 x 256
+// macro tile per workgroup of 8 waves (one workgroup per CU: the ring takes
+// 128 KiB of LDS).  After the mainloop the four 128 x 128 sub-tiles are
+// staged through LDS one at a time, each by its two owner waves (wr = sub / 2,
+// wc / 2 = sub % 2), and all 512 threads run the epilogue on it with 2 of its
+// 4 passes in flight.
 template <int OPT, int WF, int MF, int VF>
-__global__ void __launch_bounds__(NT, 1) k_fused_wide(const KArgs a) {
+__global__ void __launch_bounds__(2 * NT, 1) k_fused_wide(const KArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[LDS_WIDE];
   const int tw = (a.K + MainWide::W - 1) / MainWide::W;
   const int mi = (int)blockIdx.x / tw;
   const int row0 = mi * MainWide::W, col0 = ((int)blockIdx.x - mi * tw) * MainWide::W;
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
   wide_accumulate(a, lds, row0, col0, acc);
-  const int wave = threadIdx.x >> 6;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wr = wave >> 2, wc = wave & 3;
   float* sG = reinterpret_cast<float*>(lds);
-  Epilogue<Step<OPT, WF, MF, VF, true>, FMT_NONE, true, 4> epi;
+  Epilogue<Step<OPT, WF, MF, VF, true>, FMT_NONE, true, 2, 2 * NT> epi;   // 2 of the 4 passes in flight
   epi.tid = threadIdx.x;
-  for (int sub = 0; sub < 4; ++sub) {   // sub-tile (sub / 2, sub % 2), owned by wave sub
+  for (int sub = 0; sub < 4; ++sub) {
     const int srow0 = row0 + (sub >> 1) * TILE, scol0 = col0 + (sub & 1) * TILE;
     bar();                                   // the ring / the previous sub-tile is no longer read
-    if (wave == sub) {
-      const int lane = threadIdx.x & 63;
+    if (wr == (sub >> 1) && (wc >> 1) == (sub & 1)) {
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-        for (int bj = 0; bj < 4; ++bj)
+        for (int bj = 0; bj < 2; ++bj)
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int r = bi * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-            const int c = bj * 32 + (lane & 31);
+            const int c = (wc & 1) * 64 + bj * 32 + (lane & 31);
             sG[r * GP + c] = acc[bi][bj][e];
           }
     }
@@ -1387,8 +1396,8 @@ hipError_t combo_fused(const KArgs& a, int in_fmt, int w_fmt, hipStream_t st) {
   const bool wbf = w_fmt == FMT_BF16;
   if (in_fmt == FMT_BF16 && fast && a.BT >= WIDE_MIN_BT) {
     const dim3 g((unsigned)(((a.N + 255) / 256) * ((a.K + 255) / 256)));
-    if (wbf) hipLaunchKernelGGL((k_fused_wide<O, FMT_BF16, M, V>), g, b, 0, st, a);
-    else hipLaunchKernelGGL((k_fused_wide<O, FMT_F32, M, V>), g, b, 0, st, a);
+    if (wbf) hipLaunchKernelGGL((k_fused_wide<O, FMT_BF16, M, V>), g, dim3(2 * NT), 0, st, a);
+    else hipLaunchKernelGGL((k_fused_wide<O, FMT_F32, M, V>), g, dim3(2 * NT), 0, st, a);
   } else if (in_fmt == FMT_BF16 && fast) {
     if (wbf) hipLaunchKernelGGL((k_fused<FMT_BF16, true, O, FMT_BF16, M, V>), tile_grid(a), b, 0, st, a);
     else hipLaunchKernelGGL((k_fused<FMT_BF16, true, O, FMT_F32, M, V>), tile_grid(a), b, 0, st, a);

@@ -177,7 +177,7 @@ forge_status forge_wgrad_step(const forge_mat* X, const forge_mat* dY, forge_mat
  * bit.  Layers may share inputs (q/k/v read the same X) but nothing a layer
  * writes (W, m, v, scales) may overlap any buffer of another layer.  All
  * non-empty layers must have the same X / W / m / v dtypes and block size;
- * shapes and BT may differ.  Aligned bf16 layers with BT < 3072 run in one
+ * shapes and BT may differ.  Aligned bf16 layers with BT < 2048 run in one
  * launch; any other layer gets its own launch, on the same stream.
  *
  * Errors: FORGE_E_SHAPE (n < 1 or n > FORGE_GROUP_MAX), E_NULL, every error
