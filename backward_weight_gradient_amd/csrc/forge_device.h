@@ -20,22 +20,24 @@
 // tokens of one feature per lane, are read back with the gfx950 transposing
 // LDS read (ds_read_b64_tr_b16).  Rows are XOR-swizzled in 64-byte units so
 // that the four token rows one transposing read touches fall in distinct
-// banks.  v_mfma_f32_32x32x16_bf16, 4 waves in a 2 x 2 arrangement of 64 x
-// 64 sub-tiles, double-buffered LDS stages.  fp32 inputs use
-// v_mfma_f32_32x32x2_f32 straight from a row-major LDS copy.
+// banks.  v_mfma_f32_32x32x16_bf16: 128 x 128 tiles with 4 waves in a 2 x 2
+// arrangement of 64 x 64 (a 4-stage LDS-DMA ring for aligned shapes,
+// double-buffered register staging otherwise); for long token axes 256 x 256
+// tiles with 8 waves of 128 x 64.  fp32 inputs use v_mfma_f32_32x32x2_f32
+// straight from a row-major LDS copy.
 //
 // Epilogue: the fp32 accumulators are staged through LDS so that each
 // thread owns two 4-element segments of a row; the 16 lanes of a row read
-// and write W / m / v in contiguous 64-element runs, and an int8 block (<=
-// 128 elements of one row) is owned by <= 16 adjacent lanes, which reduce
-// its absmax with lane shuffles.  The element-wise step is written once (Step::apply_store) and is used
-// by the fused kernel and by the unfused baseline's step kernel alike, so
-// the two are bit-identical when the baseline keeps G in fp32 (paper,
-// Corollary 1(a)).
+// and write W / m / v in contiguous 64-element runs, and an 8-bit state
+// block (<= 128 elements of one row) is owned by <= 16 adjacent lanes,
+// which reduce its absmax with DPP row operations.  The element-wise step
+// is written once (Step::apply_store) and is used by the fused kernels and
+// by the unfused baseline's step kernel alike, so the two are bit-identical
+// when the baseline keeps G in fp32 (paper, Corollary 1(a)).
 //
 // All arithmetic is IEEE fp32 with explicit fmaf (the library is compiled
 // with -ffp-contract=off so no other contraction happens); the AdamW square
-// root and reciprocal are the hardware instructions, the int8 scale
+// root and reciprocal are the hardware instructions, the block-scale
 // divisions are correctly rounded.
 
 #include "forge_internal.h"
@@ -449,7 +451,7 @@ struct MainWideT {
   static constexpr int ROWB = W * 2;                    // bytes per token row
   static constexpr int OPB = TK * ROWB;                 // 16 KiB per operand per stage
   static constexpr int STAGE = 2 * OPB;                 // 32 KiB
-  static constexpr int ROUNDS = OPB / (NW * 64 * 16);   // load rounds per operand per chunk (4 waves: 4)
+  static constexpr int ROUNDS = OPB / (NW * 64 * 16);   // load rounds per operand per chunk (8 waves: 2)
   static constexpr int LOADS = 2 * ROUNDS;              // buffer loads per thread per chunk
 
   __amdgpu_buffer_rsrc_t rA, rB;
