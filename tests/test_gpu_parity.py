@@ -328,3 +328,31 @@ def test_aligned_multi_tile(spec, opt, N, K, BT):
         if a is not None:
             assert torch.equal(a.view(torch.uint8) if a.dtype != torch.uint8 else a,
                                b.view(torch.uint8) if b.dtype != torch.uint8 else b)
+
+
+# ---------------------------------------------------------------------------
+# The 256 x 256 kernel (BT >= 2048) at small and ragged shapes: sub-tiles
+# outside the matrix, a single partial macro tile, BT at the switch and one
+# below it (the 128 x 128 kernel), every element against the oracle and bit
+# for bit against the unfused baseline
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("N,K,BT", [(136, 72, 2100), (8, 8, 2049), (264, 520, 2048), (264, 512, 2047),
+                                    (520, 256, 2080)])
+@pytest.mark.parametrize("state", ["f32", "e4m3"])
+def test_wide_kernel_edge_shapes(N, K, BT, state):
+    if state == "e4m3" and K % 128:
+        pytest.skip("8-bit block-scaled state needs K % 128 == 0")
+    _say(f"case: wide-kernel edge {N}x{K} BT{BT} state {state}")
+    spec = synth.LayerSpec("bf16", "bf16", state, state, block=128)
+    L = make_layer(8, N, K, BT, 4, spec, gen_device="cuda")
+    h = F.hyper("adamw")
+    snap = snapshot(L)
+    U = L.clone()
+    run_fused(L, h, 4, SEED)
+    run_unfused(U, h, 4, SEED, torch.float32)
+    torch.cuda.synchronize()
+    assert_ok(check_against_oracle(snap, L, h, 4, SEED), f"wide edge {N}x{K}x{BT}")
+    for a, b in ((L.W, U.W), (L.m, U.m), (L.v, U.v), (L.ms, U.ms), (L.vs, U.vs)):
+        if a is not None:
+            assert torch.equal(a.view(torch.uint8) if a.dtype != torch.uint8 else a,
+                               b.view(torch.uint8) if b.dtype != torch.uint8 else b)
