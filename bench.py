@@ -161,9 +161,10 @@ def mfma_sweep(F, synth, h, reps=3):
 def family_sweep(F, synth, reps=5):
     """Each of the eight optimizer families on gate_proj [14336, 4096] at
     BT = 512 (bf16 X / dY / W with SR, fp32 states where the family keeps
-    them), and AdamW with int8 and with E4M3 block-scaled moments; median of
-    `reps` launches.  Algorithmic bytes: W read + written (4 B), each fp32
-    state read + written (8 B) or each 8-bit state with its block scales
+    them), and AdamW with bf16 moments (stochastic rounding on W, m and v), with
+    int8 and with E4M3 block-scaled moments; median of `reps` launches.
+    Algorithmic bytes: W read + written (4 B), each fp32 state read + written
+    (8 B), each bf16 state (4 B) or each 8-bit state with its block scales
     (2 + 8/128 B), X and dY read once."""
     import torch
     N, K = 14336, 4096
@@ -171,17 +172,17 @@ def family_sweep(F, synth, reps=5):
     X, dY = synth.activations(1, BT, N, K, STEP_T, device="cuda", extra=40)
     out = {}
     cases = [(o, "f32") for o in ("adamw", "nadam", "radam", "lion", "sgdm", "rmsprop", "adagrad", "sgd")]
-    cases += [("adamw", "int8"), ("adamw", "e4m3")]
+    cases += [("adamw", "bf16"), ("adamw", "int8"), ("adamw", "e4m3")]
     for opt, state in cases:
-        if state == "f32":
-            spec = synth.LayerSpec(in_dtype="bf16", w_fmt="bf16", m_fmt="f32" if opt in F.KEEPS_M else None,
-                                   v_fmt="f32" if opt in F.KEEPS_V else None)
+        if state in ("f32", "bf16"):
+            spec = synth.LayerSpec(in_dtype="bf16", w_fmt="bf16", m_fmt=state if opt in F.KEEPS_M else None,
+                                   v_fmt=state if opt in F.KEEPS_V else None)
         elif state == "int8":
             spec = synth.LayerSpec(in_dtype="bf16", w_fmt="bf16", m_fmt="s8", v_fmt="u8", block=128)
         else:
             spec = synth.LayerSpec(in_dtype="bf16", w_fmt="bf16", m_fmt="e4m3", v_fmt="e4m3", block=128)
         st = synth.state(1, N, K, spec, device="cuda", extra=40)
-        blocked = state != "f32"
+        blocked = state in ("int8", "e4m3")
         m = (F.state(st["m"], st["m_scale"], 128) if blocked else F.state(st["m"])) if st["m"] is not None else None
         v = (F.state(st["v"], st["v_scale"], 128) if blocked else F.state(st["v"])) if st["v"] is not None else None
         args = (F.mat(X), F.mat(dY), F.mat(st["W"]), m, v)
@@ -199,8 +200,9 @@ def family_sweep(F, synth, reps=5):
         ms = sorted(times)[len(times) // 2]
         if blocked:    # 1-byte codes + one fp32 scale per 128 elements, read and written
             bpp = 4 + 2 * (2 + 8 / 128)
-        else:
-            bpp = 4 + 8 * (opt in F.KEEPS_M) + 8 * (opt in F.KEEPS_V)
+        else:          # each fp32 state read and written: 8 B; each bf16 state: 4 B
+            per = 8 if state == "f32" else 4
+            bpp = 4 + per * (opt in F.KEEPS_M) + per * (opt in F.KEEPS_V)
         nbytes = bpp * N * K + 2 * BT * (N + K) * 2
         name = opt if state == "f32" else f"{opt}_{state}"
         out[name] = {"us": round(1e3 * ms, 1), "state_bytes_per_param": bpp,
