@@ -1019,10 +1019,31 @@ __device__ __forceinline__ void quantize_chunk(const float (&x)[8], int block, c
   }
 }
 
+// Per-thread addressing of the rows a thread steps in one tile: pointers to
+// its row of pass 0 and the uniform distance of one pass (RPP rows), so
+// pass s addresses its row with s * stride folded on the scalar unit and one
+// 64-bit add, instead of a 64-bit multiply per stream and pass; likewise the
+// flat SR index (p K + q) times the golden constant advances by a uniform
+// step per pass.  The arithmetic on the values is unchanged.
+struct TileRows {
+  char* w;                 // W, m, v, and the G source (dW / accumulator), at row p0
+  char* m;
+  char* v;
+  const char* g;
+  float* ms;               // block scales of row p0
+  float* vs;
+  int64_t dw, dm, dv, dg;  // bytes from one pass's row to the next
+  int64_t ds;              // scale elements from one pass's row to the next
+  uint32_t idx;            // p0 K GOLDEN (mod 2^32)
+  uint32_t didx;           // RPP K GOLDEN
+  uint32_t qg[2];          // q GOLDEN of the thread's two segments
+};
+
 template <int OPT, int WF, int MF, int VF, bool FAST>
 struct Step {
   static constexpr bool HAS_M = opt_has_m(OPT);
   static constexpr bool HAS_V = opt_has_v(OPT);
+  static constexpr int WFMT = WF;
   static constexpr int MFMT = HAS_M ? MF : FMT_NONE;
   static constexpr int VFMT = HAS_V ? VF : FMT_NONE;
 
@@ -1033,12 +1054,12 @@ struct Step {
     Raw4<VFMT> v[2];
   };
 
-  __device__ __forceinline__ static void load(const KArgs& a, int p, const Seg (&sg)[2], Pending& r) {
+  __device__ __forceinline__ static void load(const KArgs& a, const TileRows& tr, int s, const Seg (&sg)[2],
+                                              Pending& r) {
     const bool vec = a.vec_state != 0;
-    const char* rw = static_cast<const char*>(a.W) + (int64_t)p * a.ldw * (WF == FMT_F32 ? 4 : 2);
+    const char* rw = tr.w + s * tr.dw;
     // block is 32, 64 or 128: the scale index is a shift (a runtime division costs ~18 VALU)
     const int bsh = __builtin_ctz((unsigned)a.block);
-    const int64_t srow = (int64_t)p * (a.K >> bsh);
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       if (!sg[g].ok) {
@@ -1047,14 +1068,14 @@ struct Step {
       }
       ld4<WF, FAST>(r.w[g], rw, sg[g], vec);
       if constexpr (HAS_M) {
-        const char* rm = static_cast<const char*>(a.m) + (int64_t)p * a.ldm * (MF == FMT_F32 ? 4 : MF == FMT_BF16 ? 2 : 1);
+        const char* rm = tr.m + s * tr.dm;
         ld4<MF, FAST>(r.m[g], rm, sg[g], vec);
-        if constexpr (fmt_blocked(MF)) r.m[g].s = a.ms[srow + (sg[g].q >> bsh)];
+        if constexpr (fmt_blocked(MF)) r.m[g].s = (tr.ms + s * tr.ds)[sg[g].q >> bsh];
       }
       if constexpr (HAS_V) {
-        const char* rv = static_cast<const char*>(a.v) + (int64_t)p * a.ldv * (VF == FMT_F32 ? 4 : VF == FMT_BF16 ? 2 : 1);
+        const char* rv = tr.v + s * tr.dv;
         ld4<VF, FAST>(r.v[g], rv, sg[g], vec);
-        if constexpr (fmt_blocked(VF)) r.v[g].s = a.vs[srow + (sg[g].q >> bsh)];
+        if constexpr (fmt_blocked(VF)) r.v[g].s = (tr.vs + s * tr.ds)[sg[g].q >> bsh];
       }
     }
   }
@@ -1107,8 +1128,8 @@ struct Step {
 
   // Decode, apply phi and store one chunk of row p.  Must be called by every
   // lane of the wave when a state is int8 (lane shuffles).
-  __device__ __forceinline__ static void apply_store(const KArgs& a, int p, const Seg (&sg)[2], const float (&g)[8],
-                                                     const Pending& r) {
+  __device__ __forceinline__ static void apply_store(const KArgs& a, const TileRows& tr, int ps, const Seg (&sg)[2],
+                                                     const float (&g)[8], const Pending& r) {
     float w[8], m[8], v[8];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -1119,23 +1140,22 @@ struct Step {
 #pragma unroll
     for (int i = 0; i < 8; ++i) phi(a.c, g[i], w[i], m[i], v[i]);
     const bool vec = a.vec_state != 0;
-    char* rw = static_cast<char*>(a.W) + (int64_t)p * a.ldw * (WF == FMT_F32 ? 4 : 2);
+    char* rw = tr.w + ps * tr.dw;
     char* rm = nullptr;
     char* rv = nullptr;
-    if constexpr (HAS_M) rm = static_cast<char*>(a.m) + (int64_t)p * a.ldm * (MF == FMT_F32 ? 4 : MF == FMT_BF16 ? 2 : 1);
-    if constexpr (HAS_V) rv = static_cast<char*>(a.v) + (int64_t)p * a.ldv * (VF == FMT_F32 ? 4 : VF == FMT_BF16 ? 2 : 1);
-    const uint32_t rowbase = (uint32_t)p * (uint32_t)a.K;
+    if constexpr (HAS_M) rm = tr.m + ps * tr.dm;
+    if constexpr (HAS_V) rv = tr.v + ps * tr.dv;
+    const uint32_t rowbase = tr.idx + (uint32_t)ps * tr.didx;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       if (!sg[s].ok) continue;
-      const uint32_t idx_mul = (rowbase + (uint32_t)sg[s].q) * GOLDEN;
+      const uint32_t idx_mul = rowbase + tr.qg[s];
       st4<WF, FAST>(rw, sg[s], vec, w + 4 * s, a.c.sr, a.c.keyW, idx_mul);
       if constexpr (HAS_M && !fmt_blocked(MF)) st4<MF, FAST>(rm, sg[s], vec, m + 4 * s, a.c.sr, a.c.keyM, idx_mul);
       if constexpr (HAS_V && !fmt_blocked(VF)) st4<VF, FAST>(rv, sg[s], vec, v + 4 * s, a.c.sr, a.c.keyV, idx_mul);
     }
-    const int64_t srow = (int64_t)p * (a.K >> __builtin_ctz((unsigned)a.block));
-    if constexpr (HAS_M && fmt_blocked(MF)) quantize_chunk<MF, false>(m, a.block, sg, rm, vec, a.ms + srow);
-    if constexpr (HAS_V && fmt_blocked(VF)) quantize_chunk<VF, true>(v, a.block, sg, rv, vec, a.vs + srow);
+    if constexpr (HAS_M && fmt_blocked(MF)) quantize_chunk<MF, false>(m, a.block, sg, rm, vec, tr.ms + ps * tr.ds);
+    if constexpr (HAS_V && fmt_blocked(VF)) quantize_chunk<VF, true>(v, a.block, sg, rv, vec, tr.vs + ps * tr.ds);
   }
 };
 
@@ -1158,7 +1178,40 @@ struct Epilogue {
   static constexpr int GR = ACC ? FMT_F32 : GF;           // format of the G words loaded per pass
   typename S::Pending pend[DEPTH];
   Raw4<GR> graw[DEPTH][2];
+  TileRows tr;
   int tid;
+
+  static constexpr int esz(int fmt) { return fmt == FMT_F32 ? 4 : fmt == FMT_BF16 ? 2 : 1; }
+
+  // This thread's row bases and per-pass strides for the tile at (row0, col0).
+  __device__ __forceinline__ void rows(const KArgs& a, int row0, int col0) {
+    const int64_t p0 = row0 + (tid >> 4);
+    tr.w = static_cast<char*>(a.W) + p0 * a.ldw * esz(S::WFMT);
+    tr.dw = (int64_t)RPP * a.ldw * esz(S::WFMT);
+    if constexpr (S::HAS_M) {
+      tr.m = static_cast<char*>(a.m) + p0 * a.ldm * esz(S::MFMT);
+      tr.dm = (int64_t)RPP * a.ldm * esz(S::MFMT);
+    }
+    if constexpr (S::HAS_V) {
+      tr.v = static_cast<char*>(a.v) + p0 * a.ldv * esz(S::VFMT);
+      tr.dv = (int64_t)RPP * a.ldv * esz(S::VFMT);
+    }
+    if constexpr (GR != FMT_NONE) {
+      tr.g = static_cast<const char*>(a.dW) + p0 * a.lddw * esz(GR);
+      tr.dg = (int64_t)RPP * a.lddw * esz(GR);
+    }
+    if constexpr (fmt_blocked(S::MFMT) || fmt_blocked(S::VFMT)) {
+      const int64_t spr = a.K >> __builtin_ctz((unsigned)a.block);   // scales per row
+      if constexpr (fmt_blocked(S::MFMT)) tr.ms = a.ms + p0 * spr;
+      if constexpr (fmt_blocked(S::VFMT)) tr.vs = a.vs + p0 * spr;
+      tr.ds = (int64_t)RPP * spr;
+    }
+    tr.idx = ((uint32_t)p0 * (uint32_t)a.K) * GOLDEN;
+    tr.didx = ((uint32_t)RPP * (uint32_t)a.K) * GOLDEN;
+    const int cl = 4 * (tid & 15);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) tr.qg[g] = (uint32_t)(col0 + 64 * g + cl) * GOLDEN;
+  }
 
   __device__ __forceinline__ void segs(const KArgs& a, int p, int col0, Seg (&sg)[2]) const {
     const int cl = 4 * (tid & 15);
@@ -1174,10 +1227,10 @@ struct Epilogue {
     const int p = row0 + s * RPP + (tid >> 4);
     Seg sg[2];
     segs(a, p, col0, sg);
-    S::load(a, p, sg, pend[slot]);
+    S::load(a, tr, s, sg, pend[slot]);
     if constexpr (GR != FMT_NONE) {
       const bool gvec = a.vec_dw != 0;
-      const char* rg = static_cast<const char*>(a.dW) + (int64_t)p * a.lddw * (GR == FMT_F32 ? 4 : 2);
+      const char* rg = tr.g + s * tr.dg;
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         if (sg[g].ok) ld4<GR, FAST>(graw[slot][g], rg, sg[g], gvec);
@@ -1212,13 +1265,14 @@ struct Epilogue {
     const int p = row0 + s * RPP + (tid >> 4);
     Seg sg[2];
     segs(a, p, col0, sg);
-    S::apply_store(a, p, sg, g, cur);
+    S::apply_store(a, tr, s, sg, g, cur);
   }
 
   // One tile with a rolling window of DEPTH passes in flight: prefetch()
   // requests the first DEPTH passes (state only, no G needed), and
   // run_prefetched() the rest of the tile.
   __device__ __forceinline__ void prefetch(const KArgs& a, int row0, int col0) {
+    rows(a, row0, col0);
 #pragma unroll
     for (int s = 0; s < DEPTH && s < PASSES; ++s) issue(a, row0, col0, s, s);
   }
