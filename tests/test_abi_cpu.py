@@ -27,6 +27,22 @@ def test_header_declares_the_entry_points():
         assert n in names
 
 
+def test_header_is_plain_c(tmp_path):
+    """forge.h is a C ABI: it compiles as pedantic C99 (and as C++)."""
+    import shutil
+    import subprocess
+    src = tmp_path / "use_forge.c"
+    src.write_text('#include "forge.h"\nint main(void) { return (int)sizeof(forge_mat) + (int)sizeof(forge_layer)'
+                   ' + (int)sizeof(forge_hyper) + (int)sizeof(forge_state); }\n')
+    inc = os.path.dirname(HEADER)
+    for cc, std in (("gcc", ["-std=c99", "-pedantic", "-x", "c"]), ("g++", ["-std=c++17", "-x", "c++"])):
+        if shutil.which(cc) is None:
+            pytest.skip(f"{cc} not installed")
+        r = subprocess.run([cc, *std, "-Wall", "-Wextra", "-Werror", "-fsyntax-only", f"-I{inc}", str(src)],
+                           capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
+
+
 def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(F.LIB_PATH)
     for name in declared_functions():
