@@ -6,7 +6,9 @@ layers element by element.  Groups cover the q/k/v pattern (three layers
 reading one X), eight layers of mixed shapes and token counts (ragged tiles,
 BT = 0, an empty layer, a layer that needs its own launch because its rows
 are not 16-byte aligned, one long enough for the wide kernel), and every
-state format and optimizer.
+state format and optimizer.  At full size, the seven linear layers of a
+Llama-3.1-8B decoder layer at BT = 512 go through one call, the launch the
+throughput figure times.
 """
 
 import sys
@@ -17,7 +19,7 @@ import torch
 
 import backward_weight_gradient_amd as F
 import synth
-from forge_testlib import assert_ok, check_against_oracle, make_layer, snapshot
+from forge_testlib import assert_ok, check_against_oracle, make_layer, sample_rows, snapshot
 
 pytestmark = pytest.mark.gpu
 SEED = 1337
@@ -126,3 +128,34 @@ def test_group_repeated_steps_bit_equal():
     torch.cuda.synchronize()
     for L, R in zip(a, b):
         _assert_same_state(L, R, "three steps")
+
+
+# The seven layers of a Llama-3.1-8B decoder layer at BT = 512 in one call, in
+# the order the throughput figure launches them: bf16 X, dY and W, fp32 m and
+# v, AdamW with SR on W at t = 10.  Every element of every layer is compared
+# with separate single-layer calls (bit for bit), and sampled rows and column
+# blocks of each layer with the oracle.
+DECODER_LAYER = ("gate_proj", "up_proj", "down_proj", "q_proj", "k_proj", "v_proj", "o_proj")
+
+
+def test_llama_decoder_layer_group_full_size():
+    _say("case: group, Llama-3.1-8B decoder layer, BT 512, full size")
+    step, BT = 10, 512
+    h = F.hyper("adamw", lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, round="sr")
+    layers, snaps, cols = [], [], []
+    for i, name in enumerate(DECODER_LAYER):
+        N, K = synth.LLAMA8B_LAYERS[name]
+        L = make_layer(1, N, K, BT, step, SPEC_CFG1, gen_device="cuda", extra=i)
+        rows = sample_rows(N, 24, seed=N + K + i)
+        nb = K // 128
+        rng = np.random.default_rng(K + i)
+        blocks = sorted({0, nb - 1} | set(int(b) for b in rng.choice(nb, size=2, replace=False)))
+        layers.append(L)
+        snaps.append(snapshot(L, rows))
+        cols.append([(b * 128, b * 128 + 128) for b in blocks])
+    torch.cuda.synchronize()
+    _group_vs_separate(layers, h, step, [SEED] * len(layers))   # `layers` now hold the grouped result
+    for name, L, snap, c in zip(DECODER_LAYER, layers, snaps, cols):
+        assert_ok(check_against_oracle(snap, L, h, step, SEED, col_ranges=c), name)
+    del layers
+    torch.cuda.empty_cache()
