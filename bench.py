@@ -126,34 +126,47 @@ def load_traffic(grouping):
 
 def mfma_sweep(F, synth, h, reps=3):
     """Compute-bound configurations: down_proj [4096, 14336] and lm_head
-    [128256, 4096] at BT = 2048 and 8192, same formats and optimizer as the
-    step (one launch each; HIP events on the launch stream).  Reported as
-    achieved bf16 MFMA TFLOP/s (2 BT N K flops) against the 2.5 PFLOP/s peak."""
+    [128256, 4096] at BT = 2048 and 8192 with bf16 X, dY, W and fp32 moments,
+    under AdamW (the step's hyperparameters), Lion (lr 1e-4, beta1 0.9,
+    beta2 0.99) and SGD-momentum 0.9 (one launch each; HIP events on the
+    launch stream).  Reported as achieved bf16 MFMA TFLOP/s (2 BT N K flops)
+    against the 2.5 PFLOP/s peak.  AdamW keys are `<layer>_bt<BT>`, the other
+    optimizers' `<layer>_bt<BT>_<optimizer>`."""
     import torch
-    spec = synth.LayerSpec(in_dtype="bf16", w_fmt="bf16", m_fmt="f32", v_fmt="f32")
     stream = torch.cuda.current_stream()
+    optimizers = (("adamw", h, 20),
+                  ("lion", F.hyper("lion", lr=1e-4, beta1=0.9, beta2=0.99, weight_decay=0.01), 12),
+                  ("sgdm", F.hyper("sgdm", lr=1e-3, beta1=0.9, weight_decay=0.01), 12))
     out = {}
     for name, (N, K) in (("down_proj", (4096, 14336)), ("lm_head", (128256, 4096))):
         for bt in (2048, 8192):
             X, dY = synth.activations(4, bt, N, K, STEP_T, device="cuda")
-            st = synth.state(4, N, K, spec, device="cuda")
-            args = (F.mat(X), F.mat(dY), F.mat(st["W"]), F.state(st["m"]), F.state(st["v"]))
-            F.forge_wgrad_step(*args, h, STEP_T, SEED, stream=stream.cuda_stream)
-            torch.cuda.synchronize()
-            times = []
-            for _ in range(reps):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                F.forge_wgrad_step(*args, h, STEP_T, SEED, stream=stream.cuda_stream)
-                e1.record(stream)
+            for opt, hy, state_bytes in optimizers:
+                spec = synth.LayerSpec(in_dtype="bf16", w_fmt="bf16", m_fmt="f32",
+                                       v_fmt="f32" if opt == "adamw" else None)
+                st = synth.state(4, N, K, spec, device="cuda")
+                args = (F.mat(X), F.mat(dY), F.mat(st["W"]), F.state(st["m"]),
+                        None if st["v"] is None else F.state(st["v"]))
+                F.forge_wgrad_step(*args, hy, STEP_T, SEED, stream=stream.cuda_stream)
                 torch.cuda.synchronize()
-                times.append(e0.elapsed_time(e1))
-            ms = sorted(times)[len(times) // 2]
-            tflops = 2.0 * bt * N * K / (ms * 1e-3) / 1e12
-            out[f"{name}_bt{bt}"] = {"us": round(1e3 * ms, 1), "tflops": round(tflops, 1),
-                                     "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
-                                     "hbm_gbs_alg": round(layer_bytes(N, K, bt) / (ms * 1e-3) / 1e9, 1)}
-            del X, dY, st, args
+                times = []
+                for _ in range(reps):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    F.forge_wgrad_step(*args, hy, STEP_T, SEED, stream=stream.cuda_stream)
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    times.append(e0.elapsed_time(e1))
+                ms = sorted(times)[len(times) // 2]
+                tflops = 2.0 * bt * N * K / (ms * 1e-3) / 1e12
+                alg = state_bytes * N * K + 2 * bt * (N + K)
+                key = f"{name}_bt{bt}" if opt == "adamw" else f"{name}_bt{bt}_{opt}"
+                out[key] = {"us": round(1e3 * ms, 1), "tflops": round(tflops, 1),
+                            "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                            "hbm_gbs_alg": round(alg / (ms * 1e-3) / 1e9, 1)}
+                del st, args
+                torch.cuda.empty_cache()
+            del X, dY
             torch.cuda.empty_cache()
     return out
 
