@@ -57,6 +57,7 @@ constexpr int GP = TILE + 4;                     // fp32 row pitch of the staged
 constexpr int LDS_G = TILE * GP * 4;             // 67,584 bytes
 constexpr int LDS_MAIN = 2 * 2 * 64 * TILE * 2;  // 2 stages x (dY, X) x 64 tok x 128 x bf16 = 65,536
 constexpr int LDS_BYTES = LDS_G > LDS_MAIN ? LDS_G : LDS_MAIN;
+constexpr int LDS_HALF = 3 * 2 * 32 * TILE * 2;  // 3-stage DMA ring = 49,152 bytes, >= 64 rows of G (33,792)
 constexpr uint32_t GOLDEN = 0x9E3779B9u;
 
 // ------------------------------------------------------------------------
@@ -231,9 +232,10 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (((N >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-struct MainBF16Dma {
+template <int STAGES>
+struct MainBF16DmaT {
   static constexpr int TK = 32;                        // tokens per chunk
-  static constexpr int S = 4;                          // LDS stages (3 chunks in flight)
+  static constexpr int S = STAGES;                     // LDS stages (S - 1 chunks in flight)
   static constexpr int OPB = TK * TILE * 2;            // 8 KiB per operand per stage
   static constexpr int STAGE = 2 * OPB;
   static constexpr int LOADS = 4;                      // buffer loads per thread per chunk
@@ -287,6 +289,9 @@ struct MainBF16Dma {
     else wait_vmcnt<0>();
   }
 };
+
+using MainBF16Dma = MainBF16DmaT<4>;    // 64 KiB ring: two workgroups per CU
+using MainBF16Dma3 = MainBF16DmaT<3>;   // 48 KiB ring: three workgroups per CU
 
 // Transposing LDS read issued as inline assembly: the compiler cannot tell
 // which stage an in-flight LDS DMA writes, and would otherwise wait for all
@@ -348,10 +353,9 @@ struct WorkgroupSync {
 // sync.arrive_wait() exactly max(nk, 0) times (once per token chunk), where
 // nk = ceil(BT / 32).  The vmcnt waits count this wave's loads in issue
 // order, so no other global load of these waves may be in flight.
-template <class Sync>
+template <class M, class Sync>
 __device__ __forceinline__ void dma_accumulate(const KArgs& a, char* ring, int row0, int col0, int gtid,
                                                f32x16 (&acc)[2][2], Sync& sync) {
-  using M = MainBF16Dma;
   static_assert(M::TK == 32, "two 16-token k-steps per chunk");
   const int lane = gtid & 63, wave = gtid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
@@ -423,12 +427,28 @@ __device__ __forceinline__ void store_acc(float* sG, const f32x16 (&acc)[2][2], 
       }
 }
 
+// Rows 64h .. 64h + 63 of the tile, held by the waves with wr = h, into rows
+// 0..63 of sG (called by those two waves only).
+__device__ __forceinline__ void store_acc_half(float* sG, const f32x16 (&acc)[2][2], int gtid) {
+  const int lane = gtid & 63, wc = (gtid >> 6) & 1;
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = bi * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        const int c = wc * 64 + bj * 32 + (lane & 31);
+        sG[r * GP + c] = acc[bi][bj][e];
+      }
+}
+
 // Phase 1 for a 256-thread workgroup; same output as tile_gradient.
 __device__ __forceinline__ void tile_gradient_dma(const KArgs& a, char* lds, int row0, int col0) {
   static_assert(MainBF16Dma::S * MainBF16Dma::STAGE <= LDS_BYTES, "LDS budget");
   f32x16 acc[2][2];
   WorkgroupSync sync;
-  dma_accumulate(a, lds, row0, col0, threadIdx.x, acc, sync);
+  dma_accumulate<MainBF16Dma>(a, lds, row0, col0, threadIdx.x, acc, sync);
   bar();   // every wave is done reading the stages before G overwrites them
   store_acc(reinterpret_cast<float*>(lds), acc, threadIdx.x);
   __syncthreads();
@@ -1240,9 +1260,10 @@ struct Epilogue {
   }
 
   // G of pass s (from sG or from the slot's dW words)
-  __device__ __forceinline__ void grad(const float* sG, int s, int slot, float (&g)[8]) const {
+  // r_off: the tile row that sG's row 0 holds
+  __device__ __forceinline__ void grad(const float* sG, int s, int slot, float (&g)[8], int r_off = 0) const {
     if constexpr (GF == FMT_NONE) {
-      const int rl = s * RPP + (tid >> 4), cl = 4 * (tid & 15);
+      const int rl = s * RPP + (tid >> 4) - r_off, cl = 4 * (tid & 15);
       const f32x4 g0 = *reinterpret_cast<const f32x4*>(sG + rl * GP + cl);
       const f32x4 g1 = *reinterpret_cast<const f32x4*>(sG + rl * GP + 64 + cl);
 #pragma unroll
@@ -1282,6 +1303,35 @@ struct Epilogue {
     run_prefetched(a, sG, row0, col0);
   }
 
+  // The rest of the tile with G staged through LDS in two 64-row halves (sG
+  // holds 64 rows): the waves that own a half (wr = h) write it, and all four
+  // consume it in passes 4h .. 4h + 3.  Called right after the mainloop with
+  // a barrier between: the stages are free.
+  __device__ __forceinline__ void run_halves(const KArgs& a, float* sG, const f32x16 (&acc)[2][2], int row0,
+                                             int col0) {
+    static_assert(NTE == NT && PASSES == 8, "four passes per 64-row half");
+    const int wr = tid >> 7;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (wr == h) store_acc_half(sG, acc, tid);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      bar();   // the half is in LDS
+#pragma unroll
+      for (int s = 4 * h; s < 4 * h + 4; ++s) {
+        const int slot = s % DEPTH;
+        float g[8];
+        grad(sG, s, slot, g, 64 * h);
+        const typename S::Pending cur = pend[slot];
+        if (s + DEPTH < PASSES) issue(a, row0, col0, s + DEPTH, slot);
+        consume(a, row0, col0, s, g, cur);
+      }
+      if (h == 0) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        bar();   // every wave has read the first half
+      }
+    }
+  }
+
   __device__ __forceinline__ void run_prefetched(const KArgs& a, const float* sG, int row0, int col0) {
 #pragma unroll
     for (int s = 0; s < PASSES; ++s) {
@@ -1301,9 +1351,27 @@ struct Epilogue {
 // IN: input format.  FAST (bf16 inputs only): the asynchronous
 // direct-to-LDS mainloop and the vector-only epilogue; the host selects it
 // when X, dY and the state rows are aligned and N, K are multiples of 8.
+//
+// FAST kernels whose pending state is small (at most 6 registers per 4-element
+// segment: bf16 W with bf16 / 8-bit moments or one fp32 moment, fp32 W with one
+// compact moment) run three workgroups per CU: a 3-stage ring, G staged in
+// two 64-row halves, 2 passes of state in flight, <= 168 VGPRs without spills.
+// The rest (two fp32 moments, exact accumulation) keep two workgroups per CU
+// with a 4-stage ring and 4 passes in flight: there the state stream is the
+// bound and the extra registers carry it.
+constexpr int raw_words(int fmt) {
+  return fmt == FMT_F32 ? 4 : fmt == FMT_BF16 ? 2 : fmt == FMT_NONE ? 0 : 2;
+}
+template <int OPT, int WF, int MF, int VF, bool FAST, bool ACC>
+constexpr bool three_per_cu() {
+  using S = Step<OPT, WF, MF, VF, FAST>;
+  return FAST && !ACC && raw_words(S::WFMT) + raw_words(S::MFMT) + raw_words(S::VFMT) <= 6;
+}
+
 template <int IN, bool FAST, int OPT, int WF, int MF, int VF, bool ACC = false>
-__global__ void __launch_bounds__(NT, 2) k_fused(const KArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+__global__ void __launch_bounds__(NT, (three_per_cu<OPT, WF, MF, VF, FAST, ACC>() ? 3 : 2)) k_fused(const KArgs a) {
+  constexpr bool OCC3 = three_per_cu<OPT, WF, MF, VF, FAST, ACC>();
+  __shared__ __attribute__((aligned(16))) char lds[OCC3 ? LDS_HALF : LDS_BYTES];
   int ti, tj;
   tile_coords(blockIdx.x, a.tiles_n, a.tiles_k, ti, tj);
   const int row0 = ti * TILE, col0 = tj * TILE;
@@ -1312,16 +1380,24 @@ __global__ void __launch_bounds__(NT, 2) k_fused(const KArgs a) {
   // These loads are older than every mainloop load, so the mainloop's
   // in-order vmcnt waits still count exactly its own chunks.  (The
   // register-staged mainloop has no registers to spare for it.)
-  Epilogue<Step<OPT, WF, MF, VF, FAST>, FMT_NONE, FAST, 4, NT, ACC> epi;
+  Epilogue<Step<OPT, WF, MF, VF, FAST>, FMT_NONE, FAST, OCC3 ? 2 : 4, NT, ACC> epi;
   epi.tid = threadIdx.x;
-  if constexpr (FAST) {
+  if constexpr (OCC3) {
+    epi.prefetch(a, row0, col0);
+    f32x16 acc[2][2];
+    WorkgroupSync sync;
+    dma_accumulate<MainBF16Dma3>(a, lds, row0, col0, threadIdx.x, acc, sync);
+    bar();   // every wave is done reading the stages before G overwrites them
+    epi.run_halves(a, reinterpret_cast<float*>(lds), acc, row0, col0);
+  } else if constexpr (FAST) {
     epi.prefetch(a, row0, col0);
     tile_gradient_dma(a, lds, row0, col0);
+    epi.run_prefetched(a, reinterpret_cast<const float*>(lds), row0, col0);
   } else {
     tile_gradient<IN>(a, lds, row0, col0);
     epi.prefetch(a, row0, col0);
+    epi.run_prefetched(a, reinterpret_cast<const float*>(lds), row0, col0);
   }
-  epi.run_prefetched(a, reinterpret_cast<const float*>(lds), row0, col0);
 }
 
 // Several independent layers in one launch: the workgroups cover the
@@ -1330,8 +1406,10 @@ __global__ void __launch_bounds__(NT, 2) k_fused(const KArgs a) {
 // counts (uniform scalar work) and then runs exactly the k_fused code on it,
 // so every element is computed as a separate call would compute it.
 template <int OPT, int WF, int MF, int VF>
-__global__ void __launch_bounds__(NT, 2) k_fused_group(const GroupArgs g) {
-  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+__global__ void __launch_bounds__(NT, (three_per_cu<OPT, WF, MF, VF, true, false>() ? 3 : 2))
+    k_fused_group(const GroupArgs g) {
+  constexpr bool OCC3 = three_per_cu<OPT, WF, MF, VF, true, false>();
+  __shared__ __attribute__((aligned(16))) char lds[OCC3 ? LDS_HALF : LDS_BYTES];
   const int bid = (int)blockIdx.x;
   int li = 0;
 #pragma unroll
@@ -1340,11 +1418,19 @@ __global__ void __launch_bounds__(NT, 2) k_fused_group(const GroupArgs g) {
   int ti, tj;
   tile_coords(bid - g.first_tile[li], a.tiles_n, a.tiles_k, ti, tj);
   const int row0 = ti * TILE, col0 = tj * TILE;
-  Epilogue<Step<OPT, WF, MF, VF, true>, FMT_NONE, true, 4> epi;
+  Epilogue<Step<OPT, WF, MF, VF, true>, FMT_NONE, true, OCC3 ? 2 : 4> epi;
   epi.tid = threadIdx.x;
   epi.prefetch(a, row0, col0);                      // as in k_fused
-  tile_gradient_dma(a, lds, row0, col0);
-  epi.run_prefetched(a, reinterpret_cast<const float*>(lds), row0, col0);
+  if constexpr (OCC3) {
+    f32x16 acc[2][2];
+    WorkgroupSync sync;
+    dma_accumulate<MainBF16Dma3>(a, lds, row0, col0, threadIdx.x, acc, sync);
+    bar();
+    epi.run_halves(a, reinterpret_cast<float*>(lds), acc, row0, col0);
+  } else {
+    tile_gradient_dma(a, lds, row0, col0);
+    epi.run_prefetched(a, reinterpret_cast<const float*>(lds), row0, col0);
+  }
 }
 
 constexpr int LDS_WIDE = MainWide::S * MainWide::STAGE;   // 128 KiB
