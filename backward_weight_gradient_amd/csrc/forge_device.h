@@ -1352,25 +1352,37 @@ struct Epilogue {
 // direct-to-LDS mainloop and the vector-only epilogue; the host selects it
 // when X, dY and the state rows are aligned and N, K are multiples of 8.
 //
-// FAST kernels whose pending state is small (at most 6 registers per 4-element
-// segment: bf16 W with bf16 / 8-bit moments or one fp32 moment, fp32 W with one
-// compact moment) run three workgroups per CU: a 3-stage ring, G staged in
-// two 64-row halves, 2 passes of state in flight, <= 168 VGPRs without spills.
-// The rest (two fp32 moments, exact accumulation) keep two workgroups per CU
-// with a 4-stage ring and 4 passes in flight: there the state stream is the
-// bound and the extra registers carry it.
+// Occupancy.  FAST kernels whose pending state is small (at most 6 registers
+// per 4-element segment: bf16 W with bf16 / 8-bit moments or one fp32 moment,
+// fp32 W with one compact moment, SGD) run three workgroups per CU: a 3-stage
+// ring, G staged in two 64-row halves, 2 passes of state in flight, <= 168
+// VGPRs without spills.  With a larger state (two fp32 moments) the grouped
+// kernel does the same with 1 pass in flight (measured faster on the
+// Llama decoder layer), while the single-layer kernel keeps two workgroups
+// per CU, a 4-stage ring and 4 passes in flight (measured faster per layer,
+// most on the short q / k / v / o launches).  Exact accumulation keeps two.
 constexpr int raw_words(int fmt) {
   return fmt == FMT_F32 ? 4 : fmt == FMT_BF16 ? 2 : fmt == FMT_NONE ? 0 : 2;
 }
-template <int OPT, int WF, int MF, int VF, bool FAST, bool ACC>
-constexpr bool three_per_cu() {
+template <int OPT, int WF, int MF, int VF, bool FAST>
+constexpr bool small_state() {
   using S = Step<OPT, WF, MF, VF, FAST>;
-  return FAST && !ACC && raw_words(S::WFMT) + raw_words(S::MFMT) + raw_words(S::VFMT) <= 6;
+  return raw_words(S::WFMT) + raw_words(S::MFMT) + raw_words(S::VFMT) <= 6;
+}
+template <int OPT, int WF, int MF, int VF, bool FAST, bool ACC, bool GROUP>
+constexpr bool three_per_cu() {
+  return FAST && !ACC && (GROUP || small_state<OPT, WF, MF, VF, FAST>());
+}
+// passes of state in flight
+template <int OPT, int WF, int MF, int VF, bool FAST, bool ACC, bool GROUP>
+constexpr int epi_depth() {
+  return !three_per_cu<OPT, WF, MF, VF, FAST, ACC, GROUP>() ? 4 : small_state<OPT, WF, MF, VF, FAST>() ? 2 : 1;
 }
 
 template <int IN, bool FAST, int OPT, int WF, int MF, int VF, bool ACC = false>
-__global__ void __launch_bounds__(NT, (three_per_cu<OPT, WF, MF, VF, FAST, ACC>() ? 3 : 2)) k_fused(const KArgs a) {
-  constexpr bool OCC3 = three_per_cu<OPT, WF, MF, VF, FAST, ACC>();
+__global__ void __launch_bounds__(NT, (three_per_cu<OPT, WF, MF, VF, FAST, ACC, false>() ? 3 : 2))
+    k_fused(const KArgs a) {
+  constexpr bool OCC3 = three_per_cu<OPT, WF, MF, VF, FAST, ACC, false>();
   __shared__ __attribute__((aligned(16))) char lds[OCC3 ? LDS_HALF : LDS_BYTES];
   int ti, tj;
   tile_coords(blockIdx.x, a.tiles_n, a.tiles_k, ti, tj);
@@ -1380,7 +1392,7 @@ __global__ void __launch_bounds__(NT, (three_per_cu<OPT, WF, MF, VF, FAST, ACC>(
   // These loads are older than every mainloop load, so the mainloop's
   // in-order vmcnt waits still count exactly its own chunks.  (The
   // register-staged mainloop has no registers to spare for it.)
-  Epilogue<Step<OPT, WF, MF, VF, FAST>, FMT_NONE, FAST, OCC3 ? 2 : 4, NT, ACC> epi;
+  Epilogue<Step<OPT, WF, MF, VF, FAST>, FMT_NONE, FAST, epi_depth<OPT, WF, MF, VF, FAST, ACC, false>(), NT, ACC> epi;
   epi.tid = threadIdx.x;
   if constexpr (OCC3) {
     epi.prefetch(a, row0, col0);
@@ -1406,9 +1418,9 @@ __global__ void __launch_bounds__(NT, (three_per_cu<OPT, WF, MF, VF, FAST, ACC>(
 // counts (uniform scalar work) and then runs exactly the k_fused code on it,
 // so every element is computed as a separate call would compute it.
 template <int OPT, int WF, int MF, int VF>
-__global__ void __launch_bounds__(NT, (three_per_cu<OPT, WF, MF, VF, true, false>() ? 3 : 2))
+__global__ void __launch_bounds__(NT, (three_per_cu<OPT, WF, MF, VF, true, false, true>() ? 3 : 2))
     k_fused_group(const GroupArgs g) {
-  constexpr bool OCC3 = three_per_cu<OPT, WF, MF, VF, true, false>();
+  constexpr bool OCC3 = three_per_cu<OPT, WF, MF, VF, true, false, true>();
   __shared__ __attribute__((aligned(16))) char lds[OCC3 ? LDS_HALF : LDS_BYTES];
   const int bid = (int)blockIdx.x;
   int li = 0;
@@ -1418,7 +1430,7 @@ __global__ void __launch_bounds__(NT, (three_per_cu<OPT, WF, MF, VF, true, false
   int ti, tj;
   tile_coords(bid - g.first_tile[li], a.tiles_n, a.tiles_k, ti, tj);
   const int row0 = ti * TILE, col0 = tj * TILE;
-  Epilogue<Step<OPT, WF, MF, VF, true>, FMT_NONE, true, OCC3 ? 2 : 4> epi;
+  Epilogue<Step<OPT, WF, MF, VF, true>, FMT_NONE, true, epi_depth<OPT, WF, MF, VF, true, false, true>()> epi;
   epi.tid = threadIdx.x;
   epi.prefetch(a, row0, col0);                      // as in k_fused
   if constexpr (OCC3) {
