@@ -292,6 +292,10 @@ struct MainBF16DmaT {
 
 using MainBF16Dma = MainBF16DmaT<4>;    // 64 KiB ring: two workgroups per CU
 using MainBF16Dma3 = MainBF16DmaT<3>;   // 48 KiB ring: three workgroups per CU
+static_assert(MainBF16Dma3::S * MainBF16Dma3::STAGE <= LDS_HALF && 64 * GP * 4 <= LDS_HALF &&
+                  3 * LDS_HALF <= 160 * 1024,
+              "three workgroups per CU: the ring and a 64-row half of G each fit, three fit in 160 KiB");
+static_assert(2 * LDS_BYTES <= 160 * 1024, "two workgroups per CU");
 
 // Transposing LDS read issued as inline assembly: the compiler cannot tell
 // which stage an in-flight LDS DMA writes, and would otherwise wait for all
