@@ -1296,10 +1296,18 @@ struct Epilogue {
   // One tile with a rolling window of DEPTH passes in flight: prefetch()
   // requests the first DEPTH passes (state only, no G needed), and
   // run_prefetched() the rest of the tile.
+  template <int NPRE = DEPTH>
   __device__ __forceinline__ void prefetch(const KArgs& a, int row0, int col0) {
     rows(a, row0, col0);
 #pragma unroll
-    for (int s = 0; s < DEPTH && s < PASSES; ++s) issue(a, row0, col0, s, s);
+    for (int s = 0; s < NPRE && s < PASSES; ++s) issue(a, row0, col0, s, s);
+  }
+
+  // The passes NPRE .. DEPTH - 1 that prefetch<NPRE>() left out.
+  template <int NPRE>
+  __device__ __forceinline__ void prefetch_rest(const KArgs& a, int row0, int col0) {
+#pragma unroll
+    for (int s = NPRE; s < DEPTH && s < PASSES; ++s) issue(a, row0, col0, s, s);
   }
 
   __device__ __forceinline__ void run_tile(const KArgs& a, const float* sG, int row0, int col0) {
@@ -1377,10 +1385,19 @@ template <int OPT, int WF, int MF, int VF, bool FAST, bool ACC, bool GROUP>
 constexpr bool three_per_cu() {
   return FAST && !ACC && (GROUP || small_state<OPT, WF, MF, VF, FAST>());
 }
-// passes of state in flight
+// passes of state in flight, and how many of them are requested before the mainloop
+constexpr int SMALL_DEPTH = 2, SMALL_PRE = 2, GROUP_LARGE_DEPTH = 2, GROUP_LARGE_PRE = 0;
 template <int OPT, int WF, int MF, int VF, bool FAST, bool ACC, bool GROUP>
 constexpr int epi_depth() {
-  return !three_per_cu<OPT, WF, MF, VF, FAST, ACC, GROUP>() ? 4 : small_state<OPT, WF, MF, VF, FAST>() ? 2 : 1;
+  return !three_per_cu<OPT, WF, MF, VF, FAST, ACC, GROUP>() ? 4
+         : small_state<OPT, WF, MF, VF, FAST>()              ? SMALL_DEPTH
+                                                              : GROUP_LARGE_DEPTH;
+}
+template <int OPT, int WF, int MF, int VF, bool FAST, bool ACC, bool GROUP>
+constexpr int epi_pre() {
+  return !three_per_cu<OPT, WF, MF, VF, FAST, ACC, GROUP>() ? 4
+         : small_state<OPT, WF, MF, VF, FAST>()              ? SMALL_PRE
+                                                              : GROUP_LARGE_PRE;
 }
 
 template <int IN, bool FAST, int OPT, int WF, int MF, int VF, bool ACC = false>
@@ -1399,11 +1416,13 @@ __global__ void __launch_bounds__(NT, (three_per_cu<OPT, WF, MF, VF, FAST, ACC, 
   Epilogue<Step<OPT, WF, MF, VF, FAST>, FMT_NONE, FAST, epi_depth<OPT, WF, MF, VF, FAST, ACC, false>(), NT, ACC> epi;
   epi.tid = threadIdx.x;
   if constexpr (OCC3) {
-    epi.prefetch(a, row0, col0);
+    constexpr int PRE = epi_pre<OPT, WF, MF, VF, FAST, ACC, false>();
+    epi.template prefetch<PRE>(a, row0, col0);
     f32x16 acc[2][2];
     WorkgroupSync sync;
     dma_accumulate<MainBF16Dma3>(a, lds, row0, col0, threadIdx.x, acc, sync);
     bar();   // every wave is done reading the stages before G overwrites them
+    epi.template prefetch_rest<PRE>(a, row0, col0);
     epi.run_halves(a, reinterpret_cast<float*>(lds), acc, row0, col0);
   } else if constexpr (FAST) {
     epi.prefetch(a, row0, col0);
@@ -1435,13 +1454,15 @@ __global__ void __launch_bounds__(NT, (three_per_cu<OPT, WF, MF, VF, true, false
   tile_coords(bid - g.first_tile[li], a.tiles_n, a.tiles_k, ti, tj);
   const int row0 = ti * TILE, col0 = tj * TILE;
   Epilogue<Step<OPT, WF, MF, VF, true>, FMT_NONE, true, epi_depth<OPT, WF, MF, VF, true, false, true>()> epi;
+  constexpr int PRE = epi_pre<OPT, WF, MF, VF, true, false, true>();
   epi.tid = threadIdx.x;
-  epi.prefetch(a, row0, col0);                      // as in k_fused
+  epi.template prefetch<PRE>(a, row0, col0);        // as in k_fused
   if constexpr (OCC3) {
     f32x16 acc[2][2];
     WorkgroupSync sync;
     dma_accumulate<MainBF16Dma3>(a, lds, row0, col0, threadIdx.x, acc, sync);
     bar();
+    epi.template prefetch_rest<PRE>(a, row0, col0);
     epi.run_halves(a, reinterpret_cast<float*>(lds), acc, row0, col0);
   } else {
     tile_gradient_dma(a, lds, row0, col0);
