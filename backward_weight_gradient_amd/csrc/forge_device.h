@@ -21,12 +21,14 @@
 // LDS read (ds_read_b64_tr_b16).  Rows are XOR-swizzled in 64-byte units so
 // that the four token rows one transposing read touches fall in distinct
 // banks.  v_mfma_f32_32x32x16_bf16: 128 x 128 tiles with 4 waves in a 2 x 2
-// arrangement of 64 x 64 (a 4-stage LDS-DMA ring for aligned shapes,
-// double-buffered register staging otherwise); for long token axes 256 x 256
+// arrangement of 64 x 64 (a 3- or 4-stage LDS-DMA ring for aligned shapes,
+// for three or two workgroups per CU; double-buffered register staging
+// otherwise); for long token axes 256 x 256
 // tiles with 8 waves of 128 x 64.  fp32 inputs use v_mfma_f32_32x32x2_f32
 // straight from a row-major LDS copy.
 //
-// Epilogue: the fp32 accumulators are staged through LDS so that each
+// Epilogue: the fp32 accumulators are staged through LDS (the whole tile, or
+// in two 64-row halves where three workgroups share a CU) so that each
 // thread owns two 4-element segments of a row; the 16 lanes of a row read
 // and write W / m / v in contiguous 64-element runs, and an 8-bit state
 // block (<= 128 elements of one row) is owned by <= 16 adjacent lanes,
@@ -1369,10 +1371,12 @@ struct Epilogue {
 // fp32 W with one compact moment, SGD) run three workgroups per CU: a 3-stage
 // ring, G staged in two 64-row halves, 2 passes of state in flight, <= 168
 // VGPRs without spills.  With a larger state (two fp32 moments) the grouped
-// kernel does the same with 1 pass in flight (measured faster on the
-// Llama decoder layer), while the single-layer kernel keeps two workgroups
-// per CU, a 4-stage ring and 4 passes in flight (measured faster per layer,
-// most on the short q / k / v / o launches).  Exact accumulation keeps two.
+// kernel does the same with 2 passes in flight, none of them requested before
+// the mainloop (so that they hold no registers during it; measured faster on
+// the Llama decoder layer), while the single-layer kernel keeps two
+// workgroups per CU, a 4-stage ring and 4 passes in flight (measured faster
+// per layer, most on the short q / k / v / o launches).  Exact accumulation
+// keeps two.
 constexpr int raw_words(int fmt) {
   return fmt == FMT_F32 ? 4 : fmt == FMT_BF16 ? 2 : fmt == FMT_NONE ? 0 : 2;
 }
