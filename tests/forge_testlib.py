@@ -293,6 +293,22 @@ def assert_ok(rep: Report, label: str = ""):
         raise AssertionError(f"{label}: " + "\n".join(rep.failures[:10]))
 
 
+def assert_rejected(L: Layer, call, extra=(), code=None):
+    """`call()` (a binding call with check=False) must return `code`
+    (FORGE_E_SHAPE by default) and leave every tensor of the layer, and the
+    tensors in `extra`, unchanged: validation happens before anything is
+    enqueued."""
+    code = F.FORGE_E_SHAPE if code is None else code
+    ts = [t for t in (L.W, L.m, L.v, L.ms, L.vs, *extra) if t is not None]
+    before = [_codes(t).clone() for t in ts]
+    torch.cuda.synchronize()
+    rc = call()
+    torch.cuda.synchronize()
+    assert rc == code, f"expected {F.forge_status_str(code)}, got {F.forge_status_str(rc)}"
+    for a, b in zip(ts, before):
+        assert torch.equal(_codes(a), b), "a rejected call modified its arguments"
+
+
 def sample_rows(N: int, n: int, seed: int) -> np.ndarray:
     """First, last and tile-boundary rows plus random ones, sorted."""
     rng = np.random.default_rng(seed)

@@ -20,7 +20,7 @@ import torch
 import backward_weight_gradient_amd as F
 import oracle as O
 import synth
-from forge_testlib import assert_ok, check_against_oracle, make_layer, snapshot
+from forge_testlib import assert_ok, assert_rejected, check_against_oracle, make_layer, snapshot
 
 pytestmark = pytest.mark.gpu
 SEED = 1337
@@ -100,8 +100,6 @@ CASES = [("adamw", "f32"), ("adamw", "bf16"), ("adamw", "int8"), ("adamw", "e4m3
                                                (130, 136, (65, 33, 100), "bf16"),    # unaligned: accumulate, then step
                                                (128, 256, (50, 70), "f32")])         # fp32 inputs: accumulate, then step
 def test_step_accumulated_matches_oracle(opt, state, N, K, bts, in_dtype):
-    if state in ("int8", "e4m3") and K % 128:
-        pytest.skip("8-bit block-scaled state needs K % 128 == 0")
     _say(f"case: accumulated step {opt} {state} {N}x{K} {bts} {in_dtype}")
     spec = _spec(opt, state or "f32", in_dtype)
     L = make_layer(22, N, K, 1, 8, spec, outlier_p=0.0)
@@ -109,12 +107,19 @@ def test_step_accumulated_matches_oracle(opt, state, N, K, bts, in_dtype):
     acc = torch.empty((N, K), device="cuda")
     for i, (X, dY) in enumerate(mb[:-1]):
         F.forge_wgrad_accumulate(X, dY, acc, first=(i == 0))
+    h = F.hyper(opt, lr=1e-4 if opt == "lion" else 1e-3, beta2=0.99 if opt == "lion" else None)
+    if state in ("int8", "e4m3") and K % 128:
+        # block-scaled states need K % block == 0: the final step is rejected
+        # before any launch, and the accumulator is left as it was
+        Xl, dYl = mb[-1]
+        assert_rejected(L, lambda: F.forge_wgrad_step_accumulated(Xl, dYl, acc, L.W, L.forge_m(), L.forge_v(), h, 8,
+                                                                  SEED, check=False), extra=(acc,))
+        return
     # the oracle's batch: all micro-batches' tokens
     L.X = torch.cat([X for X, _ in mb])
     L.dY = torch.cat([dY for _, dY in mb])
     snap = snapshot(L)
     snap.extra_terms = len(bts)
-    h = F.hyper(opt, lr=1e-4 if opt == "lion" else 1e-3, beta2=0.99 if opt == "lion" else None)
     Xl, dYl = mb[-1]
     F.forge_wgrad_step_accumulated(Xl, dYl, acc, L.W, L.forge_m(), L.forge_v(), h, 8, SEED)
     torch.cuda.synchronize()

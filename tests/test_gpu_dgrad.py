@@ -20,7 +20,7 @@ import torch
 import backward_weight_gradient_amd as F
 import oracle as O
 import synth
-from forge_testlib import make_layer
+from forge_testlib import assert_rejected, make_layer
 
 pytestmark = pytest.mark.gpu
 SEED = 1337
@@ -129,14 +129,19 @@ def test_dgrad_full_size_llama_bt512(name):
 @pytest.mark.parametrize("N,K,BT", [(512, 1024, 300), (130, 136, 65)])
 def test_backward_step_orders_dgrad_before_the_update(opt, spec, N, K, BT):
     """dX comes from the weight before the step; the step is forge_wgrad_step's, bit for bit."""
-    if spec.m_fmt in ("s8", "e4m3") and K % spec.block:
-        pytest.skip("8-bit block-scaled state needs K % block == 0")
     _say(f"case: backward step {opt} {N}x{K} BT{BT}")
     L = make_layer(31, N, K, BT, 6, spec)
     R = L.clone()
     W_before = L.W.clone()
     dX = torch.empty((BT, K), device="cuda", dtype=torch.bfloat16)
     h = F.hyper(opt)
+    if spec.m_fmt in ("s8", "e4m3") and K % spec.block:
+        # block-scaled states need K % block == 0: rejected before anything
+        # (the dX GEMM included) is enqueued
+        dX.fill_(3.0)
+        assert_rejected(L, lambda: F.forge_backward_step(L.X, L.dY, L.W, L.forge_m(), L.forge_v(), h, 6, SEED, dX,
+                                                         check=False), extra=(dX,))
+        return
     F.forge_backward_step(L.X, L.dY, L.W, L.forge_m(), L.forge_v(), h, 6, SEED, dX)
     dX_ref = torch.empty_like(dX)
     F.forge_dgrad(R.dY, W_before, dX_ref)
