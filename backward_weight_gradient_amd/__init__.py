@@ -103,6 +103,11 @@ def _load() -> ctypes.CDLL:
     lib.forge_wgrad_step_accumulated.restype = st
     lib.forge_dgrad.argtypes = [P(forge_mat), P(forge_mat), P(forge_mat), ctypes.c_void_p]
     lib.forge_dgrad.restype = st
+    lib.forge_dgrad_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
+    lib.forge_dgrad_workspace_bytes.restype = ctypes.c_int64
+    lib.forge_dgrad_split.argtypes = [P(forge_mat), P(forge_mat), P(forge_mat), ctypes.c_void_p, ctypes.c_int64,
+                                      ctypes.c_void_p]
+    lib.forge_dgrad_split.restype = st
     lib.forge_backward_step.argtypes = [P(forge_mat), P(forge_mat), P(forge_mat), P(forge_state), P(forge_state),
                                         P(forge_hyper), ctypes.c_int64, ctypes.c_uint64, P(forge_mat),
                                         ctypes.c_void_p]
@@ -275,6 +280,27 @@ def forge_dgrad(dY, W, dX, stream=None, check: bool = True) -> int:
     rc = lib.forge_dgrad(_ref(dY), _ref(W), _ref(dX), _stream(stream))
     if check and rc != FORGE_OK:
         raise ForgeError(rc, "forge_dgrad")
+    return rc
+
+
+def forge_dgrad_workspace_bytes(BT: int, N: int, K: int) -> int:
+    """Bytes of workspace forge_dgrad_split uses for these shapes (0: none)."""
+    return int(lib.forge_dgrad_workspace_bytes(BT, N, K))
+
+
+def forge_dgrad_split(dY, W, dX, workspace=None, stream=None, check: bool = True) -> int:
+    """forge_dgrad with the reduction split across workgroups into `workspace`
+    (a device tensor of at least forge_dgrad_workspace_bytes bytes, or None)."""
+    dY = mat(dY) if not isinstance(dY, forge_mat) else dY
+    W = mat(W) if not isinstance(W, forge_mat) else W
+    dX = mat(dX) if not isinstance(dX, forge_mat) else dX
+    if workspace is None:
+        ptr, nbytes = None, 0
+    else:
+        ptr, nbytes = workspace.data_ptr() or None, workspace.numel() * workspace.element_size()
+    rc = lib.forge_dgrad_split(_ref(dY), _ref(W), _ref(dX), ptr, nbytes, _stream(stream))
+    if check and rc != FORGE_OK:
+        raise ForgeError(rc, "forge_dgrad_split")
     return rc
 
 

@@ -253,6 +253,8 @@ forge_status check_dgrad(const forge_mat* dY, const forge_mat* W, const forge_ma
   g.tiles_k = (int32_t)((K + 127) / 128);
   g.in_fmt = dY->dtype; g.w_fmt = W->dtype; g.dx_fmt = dX->dtype;
   g.vec_out = vec_ok(dX->data, dX->ld, 4, elem_size(dX->dtype)) ? 1 : 0;
+  g.splits = 1;
+  g.ws = nullptr;
   fast = dY->dtype == FORGE_BF16 && W->dtype == FORGE_BF16 && N % 8 == 0 && K % 8 == 0 &&
          vec_ok(dY->data, dY->ld, 8, 2) && vec_ok(W->data, W->ld, 8, 2) &&
          (uint64_t)BT * (uint64_t)dY->ld * 2 < (1ull << 31) && (uint64_t)N * (uint64_t)W->ld * 2 < (1ull << 31);
@@ -514,6 +516,33 @@ forge_status forge_dgrad(const forge_mat* dY, const forge_mat* W, forge_mat* dX,
   bool fast = false;
   const forge_status st = check_dgrad(dY, W, dX, g, fast);
   if (st != FORGE_OK) return st;
+  return hip_status(launch_dgrad(g, fast, (hipStream_t)stream));
+}
+
+int64_t forge_dgrad_workspace_bytes(int64_t BT, int64_t N, int64_t K) {
+  if (BT <= 0 || N <= 0 || K <= 0 || BT >= (1ll << 31) || N >= (1ll << 31) || K >= (1ll << 31)) return 0;
+  const int s = dgrad_splits(BT, N, K);
+  return s > 1 ? (int64_t)s * BT * K * 4 : 0;
+}
+
+forge_status forge_dgrad_split(const forge_mat* dY, const forge_mat* W, forge_mat* dX, void* workspace,
+                               int64_t workspace_bytes, void* stream) {
+  DgArgs g;
+  bool fast = false;
+  const forge_status st = check_dgrad(dY, W, dX, g, fast);
+  if (st != FORGE_OK) return st;
+  if (workspace_bytes < 0) return FORGE_E_SHAPE;
+  const int64_t need = forge_dgrad_workspace_bytes(g.BT, g.N, g.K);
+  if (fast && need > 0) {
+    if (!workspace) return FORGE_E_NULL;
+    if (workspace_bytes < need) return FORGE_E_SHAPE;
+    if (!aligned(workspace, 16)) return FORGE_E_ALIGN;
+    const Range rw = raw_range(workspace, (uint64_t)need);
+    if (overlap(rw, mat_range(*dY)) || overlap(rw, mat_range(*W)) || overlap(rw, mat_range(*dX)))
+      return FORGE_E_ALIAS;
+    g.splits = dgrad_splits(g.BT, g.N, g.K);
+    g.ws = static_cast<float*>(workspace);
+  }
   return hip_status(launch_dgrad(g, fast, (hipStream_t)stream));
 }
 

@@ -119,9 +119,27 @@ struct DgArgs {
   int32_t tiles_m, tiles_k;       // ceil(BT/128), ceil(K/128) (MFMA kernel)
   int32_t in_fmt, w_fmt, dx_fmt;  // dtypes of dY, W, dX
   int32_t vec_out;                // dX rows allow 4-element vector stores
+  int32_t splits;                 // > 1: the reduction split across workgroups (fast path only)
+  float* ws;                      // splits x [BT, K] fp32 partials (splits > 1)
 };
 // forge_k_dgrad.hip: fast = bf16 dY and W with 16-byte aligned rows, N and K multiples of 8.
 hipError_t launch_dgrad(const DgArgs& g, bool fast, hipStream_t stream);
+
+// Reduction splits of the MFMA dX kernel for dY [BT, N], W [N, K]: 1 (no
+// split) when 128-token tiles already give every CU a workgroup, else up to
+// 4, so that 128-token tiles x splits fill the chip twice (two workgroups
+// per CU), each split covering at least 32 chunks (1024 reduction elements;
+// measured: 8-chunk splits of k / v_proj at BT 512 run 50% slower than the
+// unsplit 64-token kernel).
+inline int dgrad_splits(int64_t BT, int64_t N, int64_t K) {
+  const int64_t t128 = ((BT + 127) / 128) * ((K + 127) / 128);
+  if (t128 == 0 || t128 >= 256) return 1;
+  const int64_t nk = (N + 31) / 32;
+  int64_t s = (512 + t128 - 1) / t128;
+  if (s > 4) s = 4;
+  while (s > 1 && nk / s < 32) --s;
+  return (int)s;
+}
 
 inline bool combo_supported(int in_fmt, int w_fmt, int opt, int m_fmt, int v_fmt) {
   if (in_fmt != FMT_F32 && in_fmt != FMT_BF16) return false;

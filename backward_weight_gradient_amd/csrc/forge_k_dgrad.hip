@@ -16,6 +16,13 @@
 // lane, its 64-byte rows XOR-swizzled in 16-byte units so that 16 lanes
 // reading 16 consecutive rows cover all 64 banks.
 //
+// Split reduction (128-token tiles only): blockIdx.y = split s takes the
+// chunks [s c, min(nk, (s + 1) c)), c = ceil(nk / splits), and writes its
+// fp32 partial tile to the workspace; k_dgrad_reduce then adds the splits'
+// partials in split order (deterministic) and stores dX.  For the short-token,
+// long-reduction layers this moves each W panel through L2 -> LDS once per
+// 128 tokens instead of once per 64 on the same number of workgroups.
+//
 // k_dgrad_generic (any dtype combination, any alignment): 64 x 64 tiles, fp32
 // FMA from an LDS-staged fp32 copy of both operands.
 
@@ -162,16 +169,20 @@ __global__ void __launch_bounds__(NT * KG, KG == 1 ? 2 : 1) k_dgrad_bf16(const D
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[bi][bj][e] = 0.f;
   const int nk = (g.N + DG_TN - 1) / DG_TN;
-  const int nj = (nk + KG - 1) / KG;                 // iterations of every group
+  // this workgroup's chunks: c0 + kg + KG j, j < nj (a split range only with KG = 1)
+  const int sp = (int)blockIdx.y;
+  const int cps = (nk + g.splits - 1) / g.splits;
+  const int c0 = KG == 1 ? sp * cps : 0;
+  const int nj = KG == 1 ? max(0, min(cps, nk - c0)) : (nk + KG - 1) / KG;
   DgradLoader<TM, S> ld;
   ld.init(g, tok0, col0, gtid);
 #pragma unroll
   for (int k = 0; k < S - 1; ++k)
-    if (k < nj) ld.issue(g, kg + KG * k, ring + k * SH::STAGE);
+    if (k < nj) ld.issue(g, c0 + kg + KG * k, ring + k * SH::STAGE);
   for (int j = 0; j < nj; ++j) {
     dg_wait_ahead<SH::LOADS, S - 2>(min(S - 2, nj - 1 - j));   // chunk j of this group landed
     bar();
-    if (j + S - 1 < nj) ld.issue(g, kg + KG * (j + S - 1), ring + ((j + S - 1) % S) * SH::STAGE);
+    if (j + S - 1 < nj) ld.issue(g, c0 + kg + KG * (j + S - 1), ring + ((j + S - 1) % S) * SH::STAGE);
     const uint32_t cur = lds0 + (uint32_t)((j % S) * SH::STAGE);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -236,15 +247,19 @@ __global__ void __launch_bounds__(NT * KG, KG == 1 ? 2 : 1) k_dgrad_bf16(const D
   }
   __syncthreads();
   if (kg != 0) return;
-  // write out: pass s, thread t -> row s*16 + t/16, two 4-column segments 64 apart
+  // write out: pass s, thread t -> row s*16 + t/16, two 4-column segments 64
+  // apart; a split writes its fp32 partial to its [BT, K] slice of ws
   const int cl = 4 * (gtid & 15);
-  const bool vec = g.vec_out != 0;
+  const bool part = g.splits > 1;
+  const bool vec = part || g.vec_out != 0;
+  const int ofmt = part ? FMT_F32 : g.dx_fmt;
 #pragma unroll
   for (int s = 0; s < TM / 16; ++s) {
     const int rl = s * 16 + (gtid >> 4);
     const int p = tok0 + rl;
     if (p >= g.BT) continue;
-    char* rowp = static_cast<char*>(g.dX) + (int64_t)p * g.ldx * (g.dx_fmt == FMT_F32 ? 4 : 2);
+    char* rowp = part ? reinterpret_cast<char*>(g.ws + ((int64_t)sp * g.BT + p) * g.K)
+                      : static_cast<char*>(g.dX) + (int64_t)p * g.ldx * (g.dx_fmt == FMT_F32 ? 4 : 2);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       Seg sg;
@@ -255,10 +270,36 @@ __global__ void __launch_bounds__(NT * KG, KG == 1 ? 2 : 1) k_dgrad_bf16(const D
       float x[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) x[i] = sG[rl * SH::GP_ + 64 * h + cl + i];
-      if (g.dx_fmt == FMT_F32) st4<FMT_F32, false>(rowp, sg, vec, x, 0, 0, 0);
+      if (ofmt == FMT_F32) st4<FMT_F32, false>(rowp, sg, vec, x, 0, 0, 0);
       else st4<FMT_BF16, false>(rowp, sg, vec, x, 0, 0, 0);
     }
   }
+}
+
+// dX = sum over s = 0 .. splits - 1 of ws[s] (in that order), 4 elements per
+// thread (K % 8 == 0 on the split path: a 4-element group never crosses a row).
+__global__ void __launch_bounds__(NT) k_dgrad_reduce(const DgArgs g) {
+  const int64_t n4 = (int64_t)g.BT * g.K / 4;
+  const int64_t q = (int64_t)blockIdx.x * NT + threadIdx.x;
+  if (q >= n4) return;
+  const f32x4* ws = reinterpret_cast<const f32x4*>(g.ws);
+  f32x4 acc = ws[q];
+  for (int s = 1; s < g.splits; ++s) {
+    const f32x4 t = ws[(int64_t)s * n4 + q];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = acc[i] + t[i];
+  }
+  const int64_t e = 4 * q;
+  const int p = (int)(e / g.K);
+  Seg sg;
+  sg.q = (int)(e - (int64_t)p * g.K);
+  sg.nv = 4;
+  sg.ok = true;
+  float x[4] = {acc[0], acc[1], acc[2], acc[3]};
+  const bool vec = g.vec_out != 0;
+  char* rowp = static_cast<char*>(g.dX) + (int64_t)p * g.ldx * (g.dx_fmt == FMT_F32 ? 4 : 2);
+  if (g.dx_fmt == FMT_F32) st4<FMT_F32, false>(rowp, sg, vec, x, 0, 0, 0);
+  else st4<FMT_BF16, false>(rowp, sg, vec, x, 0, 0, 0);
 }
 
 namespace {
@@ -331,7 +372,11 @@ hipError_t launch_dgrad(const DgArgs& g, bool fast, hipStream_t st) {
     // with 4 MFMAs per wave and chunk the per-chunk overhead dominates)
     const int64_t t128 = (int64_t)((g.BT + 127) / 128) * g.tiles_k;
     const int64_t t64 = (int64_t)((g.BT + 63) / 64) * g.tiles_k;
-    if (t128 >= 256) {
+    if (g.splits > 1) {
+      hipLaunchKernelGGL((k_dgrad_bf16<128, 4, 1>), dim3((unsigned)t128, (unsigned)g.splits), dim3(NT), 0, st, g);
+      const int64_t n4 = (int64_t)g.BT * g.K / 4;
+      hipLaunchKernelGGL(k_dgrad_reduce, dim3((unsigned)((n4 + NT - 1) / NT)), dim3(NT), 0, st, g);
+    } else if (t128 >= 256) {
       hipLaunchKernelGGL((k_dgrad_bf16<128, 4, 1>), dim3((unsigned)t128), dim3(NT), 0, st, g);
     } else if (t64 < 512 && g.N >= 8 * DG_TN) {
       hipLaunchKernelGGL((k_dgrad_bf16<64, 4, 2>), dim3((unsigned)t64), dim3(2 * NT), 0, st, g);

@@ -283,29 +283,39 @@ def accumulation_sweep(F, synth, h, micro=4, reps=5):
 
 def dgrad_sweep(F, L, layers, reps=5):
     """dX = dY W (bf16, fp32 accumulation, bf16 dX) for each layer of the step
-    at BT = 512, from the step's own dY and W (median of `reps` launches)."""
+    at BT = 512, from the step's own dY and W (median of `reps` launches):
+    forge_dgrad_split with its workspace (the reduction split across
+    workgroups where that applies) and forge_dgrad (never split)."""
     import torch
     stream = torch.cuda.current_stream()
     out = {}
-    for name, (N, K) in layers.items():
-        d = L[name]
-        dX = torch.empty((BT, K), device="cuda", dtype=torch.bfloat16)
-        dXm = F.mat(dX)
-        F.forge_dgrad(d["dYm"], d["Wm"], dXm, stream=stream.cuda_stream)
+
+    def timed(fn):
+        fn()
         torch.cuda.synchronize()
         times = []
         for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            F.forge_dgrad(d["dYm"], d["Wm"], dXm, stream=stream.cuda_stream)
+            fn()
             e1.record(stream)
             torch.cuda.synchronize()
             times.append(e0.elapsed_time(e1))
-        ms = sorted(times)[len(times) // 2]
+        return sorted(times)[len(times) // 2]
+
+    for name, (N, K) in layers.items():
+        d = L[name]
+        dX = torch.empty((BT, K), device="cuda", dtype=torch.bfloat16)
+        dXm = F.mat(dX)
+        need = F.forge_dgrad_workspace_bytes(BT, N, K)
+        ws = torch.empty((need // 4,), device="cuda") if need else None
+        ms = timed(lambda: F.forge_dgrad_split(d["dYm"], d["Wm"], dXm, ws, stream=stream.cuda_stream))
+        ms_plain = timed(lambda: F.forge_dgrad(d["dYm"], d["Wm"], dXm, stream=stream.cuda_stream))
         tflops = 2.0 * BT * N * K / (ms * 1e-3) / 1e12
         out[name] = {"us": round(1e3 * ms, 1), "tflops": round(tflops, 1),
-                     "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4)}
-        del dX
+                     "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4), "workspace_bytes": need,
+                     "us_unsplit": round(1e3 * ms_plain, 1)}
+        del dX, ws
     return out
 
 

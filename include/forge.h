@@ -244,6 +244,35 @@ forge_status forge_wgrad_step_accumulated(const forge_mat* X, const forge_mat* d
 forge_status forge_dgrad(const forge_mat* dY, const forge_mat* W, forge_mat* dX, void* stream);
 
 /*
+ * forge_dgrad_workspace_bytes -- bytes of device workspace forge_dgrad_split
+ * uses for dY [BT, N] and W [N, K] on the MFMA path: splits x BT x K x 4 when
+ * the reduction over N is split across workgroups (short token axis, few
+ * 128 x 128 output tiles, long reduction), else 0.  Non-positive or
+ * too-large sizes give 0.  Host-only, no device call.
+ */
+int64_t forge_dgrad_workspace_bytes(int64_t BT, int64_t N, int64_t K);
+
+/*
+ * forge_dgrad_split -- forge_dgrad (same dX, paper, Appendix A, Remark 1)
+ * with the reduction over N split across workgroups where
+ * forge_dgrad_workspace_bytes is non-zero and the MFMA path applies: each
+ * split writes an fp32 partial [BT, K] into `workspace`, and a second kernel
+ * adds the partials in split order (a fixed order: the result is the same
+ * from call to call, and within the fp32 summation bound of the exact
+ * product like forge_dgrad's) and stores dX.  Elsewhere it is forge_dgrad
+ * and the workspace is not touched.
+ * workspace : caller-owned device memory of `workspace_bytes` bytes,
+ *             16-byte aligned, not overlapping dY, W or dX; its contents
+ *             are scratch (overwritten, not read before written).  May be
+ *             NULL when no workspace is needed.
+ * Errors: those of forge_dgrad; E_NULL (workspace needed but NULL), E_SHAPE
+ * (workspace_bytes negative or smaller than needed), E_ALIGN, E_ALIAS
+ * (nothing enqueued), or E_HIP.
+ */
+forge_status forge_dgrad_split(const forge_mat* dY, const forge_mat* W, forge_mat* dX, void* workspace,
+                               int64_t workspace_bytes, void* stream);
+
+/*
  * forge_backward_step -- a linear layer's whole weight-side backward in the
  * order Remark 1 requires: dX = dY W from the current W (forge_dgrad), then
  * forge_wgrad_step, enqueued in that order on `stream`.  Arguments as for

@@ -413,6 +413,32 @@ def test_dgrad_validation():
     assert dg(F.mat_raw(addr(1), F.FORGE_BF16, 0, 256), W, F.mat_raw(addr(7), F.FORGE_BF16, 0, 256)) == F.FORGE_OK
 
 
+def test_dgrad_split_workspace_and_validation():
+    # workspace sizes: splits x BT x K x 4 bytes where the reduction is split, else 0
+    wb = F.forge_dgrad_workspace_bytes
+    assert wb(512, 14336, 4096) == 4 * 512 * 4096 * 4      # gate / up at BT 512: 128 tiles, 4 splits
+    assert wb(512, 4096, 4096) == 4 * 512 * 4096 * 4       # q / o: 128 chunks, 32 per split
+    assert wb(512, 2048, 4096) == 2 * 512 * 4096 * 4       # 64 chunks: 2 splits of 32
+    assert wb(512, 1024, 4096) == 0                        # k / v: 32 chunks, too short to split
+    assert wb(2048, 4096, 4096) == 0                       # 256 tiles of 128 tokens: no split
+    assert wb(0, 4096, 4096) == 0 and wb(512, 0, 4096) == 0 and wb(-1, 8, 8) == 0
+    # validation (nothing reaches the device): dY [512, 2048], W [2048, 1024], dX [512, 1024]
+    dY = F.mat_raw(addr(1), F.FORGE_BF16, 512, 2048)
+    W = F.mat_raw(addr(2), F.FORGE_BF16, 2048, 1024)
+    dX = F.mat_raw(addr(7), F.FORGE_BF16, 512, 1024)
+    need = wb(512, 2048, 1024)
+    assert need > 0
+    sp = lambda ws, nbytes, out=dX: F.lib.forge_dgrad_split(F._ref(dY), F._ref(W), F._ref(out), ws, nbytes, None)
+    assert sp(None, need) == F.FORGE_E_NULL
+    assert sp(addr(8), need - 16) == F.FORGE_E_SHAPE
+    assert sp(addr(8), -1) == F.FORGE_E_SHAPE
+    assert sp(addr(8) + 4, need) == F.FORGE_E_ALIGN
+    assert sp(addr(7), need) == F.FORGE_E_ALIAS                          # on top of dX
+    assert sp(addr(2) + 1024, need) == F.FORGE_E_ALIAS                   # inside W
+    assert sp(addr(8), need, F.mat_raw(addr(7), F.FORGE_BF16, 511, 1024)) == F.FORGE_E_SHAPE
+    assert F.lib.forge_dgrad_split(F._ref(dY), F._ref(W), None, addr(8), need, None) == F.FORGE_E_NULL
+
+
 def test_backward_step_validation():
     X, dY, W, m, v = layer()
     bs = lambda dX, **k: F.forge_backward_step(X, dY, W, m, v, F.hyper(), k.get("step", 10), 1, dX, stream=0,

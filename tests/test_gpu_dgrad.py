@@ -153,3 +153,65 @@ def test_backward_step_orders_dgrad_before_the_update(opt, spec, N, K, BT):
         if a is not None:
             assert torch.equal(a.view(torch.uint8) if a.dtype != torch.uint8 else a,
                                b.view(torch.uint8) if b.dtype != torch.uint8 else b), f"{name} differs"
+
+
+# ---------------------------------------------------------------------------
+# forge_dgrad_split: the reduction split across workgroups into a workspace
+# ---------------------------------------------------------------------------
+# (130, 2056, 520): ragged token and column tiles, two splits of 33 and 32 chunks, the last one partial
+@pytest.mark.parametrize("BT,N,K", [(300, 2048, 1024), (130, 2056, 520), (64, 4096, 128), (512, 8192, 2048)])
+@pytest.mark.parametrize("dx_dtype", ["bf16", "f32"])
+def test_dgrad_split_matches_oracle(BT, N, K, dx_dtype):
+    _say(f"case: dgrad split {BT}x{N}x{K} dX {dx_dtype}")
+    need = F.forge_dgrad_workspace_bytes(BT, N, K)
+    assert need > 0, "these shapes take the split"
+    dY, W = _operands(BT, N, K, "bf16", "bf16")
+    ws = torch.full((need // 4,), float("nan"), device="cuda")
+    dX = torch.full((BT, K), float("nan"), device="cuda", dtype=DT[dx_dtype])
+    F.forge_dgrad_split(dY, W, dX, ws)
+    torch.cuda.synchronize()
+    _check(dX, dY, W, what=f"split {BT}x{N}x{K}")
+    again = torch.full_like(dX, float("nan"))
+    F.forge_dgrad_split(dY, W, again, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(dX.view(torch.uint8), again.view(torch.uint8)), "split result differs between calls"
+
+
+@pytest.mark.parametrize("name", ["q_proj", "gate_proj"])
+def test_dgrad_split_full_size_llama_bt512(name):
+    N, K = synth.LLAMA8B_LAYERS[name]
+    _say(f"case: dgrad split {name} {N}x{K} BT512")
+    need = F.forge_dgrad_workspace_bytes(512, N, K)
+    assert need > 0
+    dY, W = _operands(512, N, K, "bf16", "bf16")
+    ws = torch.empty((need // 4,), device="cuda")
+    dX = torch.empty((512, K), device="cuda", dtype=torch.bfloat16)
+    F.forge_dgrad_split(dY, W, dX, ws)
+    torch.cuda.synchronize()
+    rows = np.array(sorted({0, 1, 127, 128, 255, 256, 511} | set(np.random.default_rng(5).choice(512, 20).tolist())))
+    _check(dX, dY, W, rows, what=f"split {name}")
+
+
+def test_dgrad_split_where_it_does_not_apply_is_dgrad():
+    _say("case: dgrad split not applicable")
+    # enough 128-token tiles: no split, no workspace, bit-equal to forge_dgrad
+    BT, N, K = 2048, 256, 2048
+    assert F.forge_dgrad_workspace_bytes(BT, N, K) == 0
+    dY, W = _operands(BT, N, K, "bf16", "bf16")
+    a = torch.empty((BT, K), device="cuda", dtype=torch.bfloat16)
+    b = torch.empty_like(a)
+    F.forge_dgrad(dY, W, a)
+    F.forge_dgrad_split(dY, W, b, None)
+    # fp32 operands take the plain kernel: the workspace is not touched
+    BT, N, K = 300, 2048, 1024
+    need = F.forge_dgrad_workspace_bytes(BT, N, K)
+    dY32, W32 = _operands(BT, N, K, "f32", "f32")
+    ws = torch.full((need // 4,), float("nan"), device="cuda")
+    c = torch.empty((BT, K), device="cuda")
+    d = torch.empty_like(c)
+    F.forge_dgrad(dY32, W32, c)
+    F.forge_dgrad_split(dY32, W32, d, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(c, d)
+    assert torch.isnan(ws).all(), "the workspace was written on the plain path"
