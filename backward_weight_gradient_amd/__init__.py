@@ -112,6 +112,10 @@ def _load() -> ctypes.CDLL:
                                         P(forge_hyper), ctypes.c_int64, ctypes.c_uint64, P(forge_mat),
                                         ctypes.c_void_p]
     lib.forge_backward_step.restype = st
+    lib.forge_backward_step_split.argtypes = [P(forge_mat), P(forge_mat), P(forge_mat), P(forge_state),
+                                              P(forge_state), P(forge_hyper), ctypes.c_int64, ctypes.c_uint64,
+                                              P(forge_mat), ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.forge_backward_step_split.restype = st
     lib.forge_debug_e4m3.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
     lib.forge_debug_e4m3.restype = st
     lib.forge_debug_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
@@ -315,6 +319,25 @@ def forge_backward_step(X, dY, W, m, v, h: forge_hyper, step: int, seed: int, dX
                                  _stream(stream))
     if check and rc != FORGE_OK:
         raise ForgeError(rc, "forge_backward_step")
+    return rc
+
+
+def forge_backward_step_split(X, dY, W, m, v, h: forge_hyper, step: int, seed: int, dX, workspace=None,
+                              stream=None, check: bool = True) -> int:
+    """forge_backward_step with dX from the split kernel (workspace: a device tensor
+    of at least forge_dgrad_workspace_bytes bytes, or None)."""
+    X = mat(X) if not isinstance(X, forge_mat) else X
+    dY = mat(dY) if not isinstance(dY, forge_mat) else dY
+    W = mat(W) if not isinstance(W, forge_mat) else W
+    dX = mat(dX) if not isinstance(dX, forge_mat) else dX
+    if workspace is None:
+        ptr, nbytes = None, 0
+    else:
+        ptr, nbytes = workspace.data_ptr() or None, workspace.numel() * workspace.element_size()
+    rc = lib.forge_backward_step_split(_ref(X), _ref(dY), _ref(W), _ref(m), _ref(v), _ref(h), step, seed, _ref(dX),
+                                       ptr, nbytes, _stream(stream))
+    if check and rc != FORGE_OK:
+        raise ForgeError(rc, "forge_backward_step_split")
     return rc
 
 

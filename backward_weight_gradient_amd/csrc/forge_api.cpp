@@ -525,29 +525,38 @@ int64_t forge_dgrad_workspace_bytes(int64_t BT, int64_t N, int64_t K) {
   return s > 1 ? (int64_t)s * BT * K * 4 : 0;
 }
 
+// The workspace of the split dX kernel, checked against every buffer of the
+// call (`others`), and the split recorded in g; no-op where no split applies.
+static forge_status attach_dgrad_workspace(DgArgs& g, bool fast, void* workspace, int64_t workspace_bytes,
+                                           const Range* others, int n_others) {
+  if (workspace_bytes < 0) return FORGE_E_SHAPE;
+  const int64_t need = forge_dgrad_workspace_bytes(g.BT, g.N, g.K);
+  if (!fast || need == 0) return FORGE_OK;
+  if (!workspace) return FORGE_E_NULL;
+  if (workspace_bytes < need) return FORGE_E_SHAPE;
+  if (!aligned(workspace, 16)) return FORGE_E_ALIGN;
+  const Range rw = raw_range(workspace, (uint64_t)need);
+  for (int i = 0; i < n_others; ++i)
+    if (overlap(rw, others[i])) return FORGE_E_ALIAS;
+  g.splits = dgrad_splits(g.BT, g.N, g.K);
+  g.ws = static_cast<float*>(workspace);
+  return FORGE_OK;
+}
+
 forge_status forge_dgrad_split(const forge_mat* dY, const forge_mat* W, forge_mat* dX, void* workspace,
                                int64_t workspace_bytes, void* stream) {
   DgArgs g;
   bool fast = false;
-  const forge_status st = check_dgrad(dY, W, dX, g, fast);
+  forge_status st = check_dgrad(dY, W, dX, g, fast);
   if (st != FORGE_OK) return st;
-  if (workspace_bytes < 0) return FORGE_E_SHAPE;
-  const int64_t need = forge_dgrad_workspace_bytes(g.BT, g.N, g.K);
-  if (fast && need > 0) {
-    if (!workspace) return FORGE_E_NULL;
-    if (workspace_bytes < need) return FORGE_E_SHAPE;
-    if (!aligned(workspace, 16)) return FORGE_E_ALIGN;
-    const Range rw = raw_range(workspace, (uint64_t)need);
-    if (overlap(rw, mat_range(*dY)) || overlap(rw, mat_range(*W)) || overlap(rw, mat_range(*dX)))
-      return FORGE_E_ALIAS;
-    g.splits = dgrad_splits(g.BT, g.N, g.K);
-    g.ws = static_cast<float*>(workspace);
-  }
+  const Range others[3] = {mat_range(*dY), mat_range(*W), mat_range(*dX)};
+  if ((st = attach_dgrad_workspace(g, fast, workspace, workspace_bytes, others, 3)) != FORGE_OK) return st;
   return hip_status(launch_dgrad(g, fast, (hipStream_t)stream));
 }
 
-forge_status forge_backward_step(const forge_mat* X, const forge_mat* dY, forge_mat* W, forge_state* m, forge_state* v,
-                                 const forge_hyper* h, int64_t step, uint64_t seed, forge_mat* dX, void* stream) {
+static forge_status backward_step(const forge_mat* X, const forge_mat* dY, forge_mat* W, forge_state* m,
+                                  forge_state* v, const forge_hyper* h, int64_t step, uint64_t seed, forge_mat* dX,
+                                  bool split, void* workspace, int64_t workspace_bytes, void* stream) {
   Plan pl;
   forge_status st = validate(X, dY, W, m, v, h, step, pl);
   if (st != FORGE_OK) return st;
@@ -561,12 +570,27 @@ forge_status forge_backward_step(const forge_mat* X, const forge_mat* dY, forge_
     if (overlap(rx, r)) return FORGE_E_ALIAS;
   for (const Range& r : ins)
     if (overlap(rx, r)) return FORGE_E_ALIAS;
+  if (split) {
+    const Range others[8] = {outs[0], outs[1], outs[2], outs[3], outs[4], ins[0], ins[1], rx};
+    if ((st = attach_dgrad_workspace(g, fast, workspace, workspace_bytes, others, 8)) != FORGE_OK) return st;
+  }
   // stream order is the contract: dX reads W before the fused step rewrites it
   hipError_t e = launch_dgrad(g, fast, (hipStream_t)stream);
   if (e != hipSuccess) return hip_status(e);
   if (pl.empty) return FORGE_OK;
   const KArgs a = make_args(X, dY, W, m, v, h, step, seed, pl);
   return hip_status(launch_fused(a, pl.in_fmt, pl.w_fmt, h->opt, pl.m_fmt, pl.v_fmt, (hipStream_t)stream));
+}
+
+forge_status forge_backward_step(const forge_mat* X, const forge_mat* dY, forge_mat* W, forge_state* m, forge_state* v,
+                                 const forge_hyper* h, int64_t step, uint64_t seed, forge_mat* dX, void* stream) {
+  return backward_step(X, dY, W, m, v, h, step, seed, dX, false, nullptr, 0, stream);
+}
+
+forge_status forge_backward_step_split(const forge_mat* X, const forge_mat* dY, forge_mat* W, forge_state* m,
+                                       forge_state* v, const forge_hyper* h, int64_t step, uint64_t seed,
+                                       forge_mat* dX, void* workspace, int64_t workspace_bytes, void* stream) {
+  return backward_step(X, dY, W, m, v, h, step, seed, dX, true, workspace, workspace_bytes, stream);
 }
 
 forge_status forge_debug_sr_bf16(const float* in, uint16_t* out, int64_t n, uint64_t seed, int64_t step,

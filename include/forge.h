@@ -284,6 +284,18 @@ forge_status forge_backward_step(const forge_mat* X, const forge_mat* dY, forge_
                                  forge_mat* dX, void* stream);
 
 /*
+ * forge_backward_step_split -- forge_backward_step with dX computed as
+ * forge_dgrad_split does (the same order: dX from the current W, then the
+ * fused step).  workspace / workspace_bytes as for forge_dgrad_split
+ * (forge_dgrad_workspace_bytes(BT, N, K) bytes); the workspace must not
+ * overlap any other buffer either.  Errors: those of forge_backward_step and
+ * of forge_dgrad_split, all checked before anything is enqueued, or E_HIP.
+ */
+forge_status forge_backward_step_split(const forge_mat* X, const forge_mat* dY, forge_mat* W, forge_state* m,
+                                       forge_state* v, const forge_hyper* h, int64_t step, uint64_t seed,
+                                       forge_mat* dX, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
  * forge_wgrad_check -- the validation of forge_wgrad_step alone: same
  * arguments, same return codes, no device call at all (usable on a host
  * without a GPU).

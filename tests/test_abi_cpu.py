@@ -439,6 +439,24 @@ def test_dgrad_split_workspace_and_validation():
     assert F.lib.forge_dgrad_split(F._ref(dY), F._ref(W), None, addr(8), need, None) == F.FORGE_E_NULL
 
 
+def test_backward_step_split_validation():
+    # X [300, 1024], dY [300, 2048], W [2048, 1024]: the dX reduction (N = 2048) is split in two
+    X, dY, W, m, v = layer(N=2048, K=1024, BT=300)
+    need = F.forge_dgrad_workspace_bytes(300, 2048, 1024)
+    assert need == 2 * 300 * 1024 * 4
+    dX = F.mat_raw(addr(7), F.FORGE_BF16, 300, 1024)
+    bs = lambda ws, nbytes, step=10: F.lib.forge_backward_step_split(
+        F._ref(X), F._ref(dY), F._ref(W), F._ref(m), F._ref(v), F._ref(F.hyper()), step, 1, F._ref(dX), ws, nbytes,
+        None)
+    assert bs(None, need) == F.FORGE_E_NULL
+    assert bs(addr(8), need - 4) == F.FORGE_E_SHAPE
+    assert bs(addr(8) + 8, need) == F.FORGE_E_ALIGN
+    assert bs(m.q.data, need) == F.FORGE_E_ALIAS                          # on top of m
+    assert bs(X.data, need) == F.FORGE_E_ALIAS                            # on top of X
+    assert bs(addr(7), need) == F.FORGE_E_ALIAS                           # on top of dX
+    assert bs(addr(8), need, step=0) == F.FORGE_E_STEP
+
+
 def test_backward_step_validation():
     X, dY, W, m, v = layer()
     bs = lambda dX, **k: F.forge_backward_step(X, dY, W, m, v, F.hyper(), k.get("step", 10), 1, dX, stream=0,

@@ -215,3 +215,28 @@ def test_dgrad_split_where_it_does_not_apply_is_dgrad():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     assert torch.equal(c, d)
     assert torch.isnan(ws).all(), "the workspace was written on the plain path"
+
+
+def test_backward_step_split_orders_split_dgrad_before_the_update():
+    """forge_backward_step_split = forge_dgrad_split on the weight before the step, then forge_wgrad_step."""
+    BT, N, K = 300, 2048, 1024
+    _say(f"case: backward step split {N}x{K} BT{BT}")
+    spec = synth.LayerSpec("bf16", "bf16", "f32", "f32")
+    need = F.forge_dgrad_workspace_bytes(BT, N, K)
+    assert need > 0
+    L = make_layer(32, N, K, BT, 6, spec)
+    R = L.clone()
+    W_before = L.W.clone()
+    ws = torch.empty((need // 4,), device="cuda")
+    dX = torch.empty((BT, K), device="cuda", dtype=torch.bfloat16)
+    h = F.hyper("adamw")
+    F.forge_backward_step_split(L.X, L.dY, L.W, L.forge_m(), L.forge_v(), h, 6, SEED, dX, ws)
+    dX_ref = torch.empty_like(dX)
+    F.forge_dgrad_split(R.dY, W_before, dX_ref, ws)
+    F.forge_wgrad_step(R.X, R.dY, R.W, R.forge_m(), R.forge_v(), h, 6, SEED)
+    torch.cuda.synchronize()
+    assert torch.equal(dX.view(torch.int16), dX_ref.view(torch.int16)), "dX did not use the pre-update weight"
+    for name in ("W", "m", "v"):
+        a, b = getattr(L, name), getattr(R, name)
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"{name} differs"
+    _check(dX, L.dY, W_before, what="backward step split")
