@@ -131,21 +131,24 @@ def test_group_repeated_steps_bit_equal():
 
 
 # The seven layers of a Llama-3.1-8B decoder layer at BT = 512 in one call, in
-# the order the throughput figure launches them: bf16 X, dY and W, fp32 m and
-# v, AdamW with SR on W at t = 10.  Every element of every layer is compared
+# the order the throughput figure launches them: bf16 X, dY and W, AdamW with
+# SR on W at t = 10; fp32 m and v (the timed configuration), bf16 m and v, and
+# int8 m and v with 1% gradient outliers.  Every element of every layer is compared
 # with separate single-layer calls (bit for bit), and sampled rows and column
 # blocks of each layer with the oracle.
 DECODER_LAYER = ("gate_proj", "up_proj", "down_proj", "q_proj", "k_proj", "v_proj", "o_proj")
 
 
-def test_llama_decoder_layer_group_full_size():
-    _say("case: group, Llama-3.1-8B decoder layer, BT 512, full size")
+@pytest.mark.parametrize("cfg,spec", [(1, SPEC_CFG1), (2, SPEC_CFG2), (3, SPEC_CFG3)])
+def test_llama_decoder_layer_group_full_size(cfg, spec):
+    _say(f"case: group, Llama-3.1-8B decoder layer, BT 512, full size, {spec}")
     step, BT = 10, 512
     h = F.hyper("adamw", lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, round="sr")
     layers, snaps, cols = [], [], []
     for i, name in enumerate(DECODER_LAYER):
         N, K = synth.LLAMA8B_LAYERS[name]
-        L = make_layer(1, N, K, BT, step, SPEC_CFG1, gen_device="cuda", extra=i)
+        L = make_layer(cfg, N, K, BT, step, spec, gen_device="cuda", extra=i,
+                       outlier_p=0.01 if spec.m_fmt == "s8" else 0.0)
         rows = sample_rows(N, 24, seed=N + K + i)
         nb = K // 128
         rng = np.random.default_rng(K + i)
