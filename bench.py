@@ -63,6 +63,8 @@ def parse():
                         "[gate, up] [o] [q, k, v]; layer: one forge_wgrad_step launch per layer")
     p.add_argument("--no-family-sweep", action="store_true",
                    help="skip the per-optimizer timing (gate_proj, BT 512, all eight families)")
+    p.add_argument("--no-state-formats", action="store_true",
+                   help="skip the grouped decoder-layer step with bf16, int8 and E4M3 moments")
     p.add_argument("--no-accumulation", action="store_true",
                    help="skip the gradient-accumulation timing (gate_proj, 4 micro-batches of 128 tokens)")
     p.add_argument("--no-dgrad", action="store_true",
@@ -224,6 +226,57 @@ def family_sweep(F, synth, reps=5):
         del st, args, m, v
     del X, dY
     torch.cuda.empty_cache()
+    return out
+
+
+def state_format_sweep(F, synth, h, reps=10):
+    """The step's grouped launch (the seven Llama-3.1-8B layers at BT = 512,
+    AdamW t = 10, SR) with compact moments: bf16 W, m, v (all three rounded
+    stochastically), int8 m / v with fp32 scales per 128 elements (1% x50
+    gradient outliers) and E4M3 m / v with fp32 scales per 128 elements;
+    median of `reps` launches after one untimed.  Algorithmic bytes: W read
+    and written (4 B), each bf16 moment 4 B, each 8-bit moment 2 + 8/128 B,
+    X and dY read once."""
+    import torch
+    order = ("gate_proj", "up_proj", "down_proj", "q_proj", "k_proj", "v_proj", "o_proj")
+    specs = {"bf16": synth.LayerSpec(in_dtype="bf16", w_fmt="bf16", m_fmt="bf16", v_fmt="bf16"),
+             "int8": synth.LayerSpec(in_dtype="bf16", w_fmt="bf16", m_fmt="s8", v_fmt="u8", block=128),
+             "e4m3": synth.LayerSpec(in_dtype="bf16", w_fmt="bf16", m_fmt="e4m3", v_fmt="e4m3", block=128)}
+    cfg_of = {"bf16": 2, "int8": 3, "e4m3": 3}
+    stream = torch.cuda.current_stream()
+    out = {}
+    for fmt, spec in specs.items():
+        keep, layers_arg, P_total, nbytes = [], [], 0, 0
+        bpp = 4 + (8.0 if fmt == "bf16" else 2 * (2 + 8 / 128))
+        for i, name in enumerate(order):
+            N, K = synth.LLAMA8B_LAYERS[name]
+            X, dY = synth.activations(cfg_of[fmt], BT, N, K, STEP_T, device="cuda", extra=i,
+                                      outlier_p=0.01 if fmt == "int8" else 0.0)
+            st = synth.state(cfg_of[fmt], N, K, spec, device="cuda", extra=i)
+            blocked = fmt != "bf16"
+            m = F.state(st["m"], st["m_scale"], 128) if blocked else F.state(st["m"])
+            v = F.state(st["v"], st["v_scale"], 128) if blocked else F.state(st["v"])
+            keep.append((X, dY, st))
+            layers_arg.append((F.mat(X), F.mat(dY), F.mat(st["W"]), m, v, SEED))
+            P_total += N * K
+            nbytes += bpp * N * K + 2 * BT * (N + K) * 2
+        launch = lambda: F.forge_wgrad_step_group(layers_arg, h, STEP_T, stream=stream.cuda_stream)
+        launch()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            launch()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        ms = sorted(times)[len(times) // 2]
+        out[fmt] = {"us": round(1e3 * ms, 1), "params_per_s": round(P_total / (ms * 1e-3), 1),
+                    "state_bytes_per_param": bpp, "hbm_gbs_alg": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                    "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del keep, layers_arg
+        torch.cuda.empty_cache()
     return out
 
 
@@ -545,6 +598,8 @@ def main():
 
     if not args.no_family_sweep:
         extras["optimizer_families_gate_proj_bt512"] = family_sweep(F, synth)
+    if not args.no_state_formats:
+        extras["state_formats_llama8b_bt512_grouped"] = state_format_sweep(F, synth, h)
     if not args.no_dgrad:
         extras["dgrad_bt512"] = dgrad_sweep(F, L, layers)
     if not args.no_accumulation:
