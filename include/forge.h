@@ -17,8 +17,9 @@
  *
  * Conventions shared by every entry point
  *   - All matrix data pointers are DEVICE pointers owned by the caller.  The
- *     library never allocates, frees or retains them (forge_wgrad_unfused
- *     writes into a caller-provided workspace).
+ *     library never allocates, frees or retains them (forge_wgrad_unfused,
+ *     forge_dgrad_split and forge_backward_step_split write into a
+ *     caller-provided workspace).
  *   - Matrices are row-major; `ld` is the leading dimension in elements
  *     (ld >= cols).  Flat indices used by stochastic rounding are the logical
  *     row-major index p*K + q, independent of ld.
