@@ -1522,11 +1522,40 @@ __global__ void __launch_bounds__(NT, 2) k_gemm(const KArgs a) {
   int ti, tj;
   tile_coords(blockIdx.x, a.tiles_n, a.tiles_k, ti, tj);
   const int row0 = ti * TILE, col0 = tj * TILE;
-  if constexpr (DMA) tile_gradient_dma(a, lds, row0, col0);
-  else tile_gradient<IN>(a, lds, row0, col0);
-  const float* sG = reinterpret_cast<const float*>(lds);
   const int cl = 4 * (threadIdx.x & 15);
   const bool vec = a.vec_dw != 0;
+  // Gradient accumulation (dw_add, fp32 dW): the old values of all 8 passes
+  // are requested at once, before any store -- issued per pass, each load
+  // would wait behind the previous pass's stores to the same buffer.  On the
+  // DMA path they are requested before the mainloop (older than every chunk
+  // load, so its in-order vmcnt waits stay exact), as the fused kernels do
+  // with the optimizer state.
+  Raw4<FMT_F32> old[8][2];
+  const auto request_old = [&]() {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int p = row0 + s * 16 + (threadIdx.x >> 4);
+      const char* rowp = static_cast<const char*>(a.dW) + (int64_t)p * a.lddw * 4;
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        Seg sg;
+        sg.q = col0 + 64 * g + cl;
+        sg.nv = max(0, min(4, a.K - sg.q));
+        sg.ok = sg.nv > 0 && p < a.N;
+        if (sg.ok) ld4<FMT_F32, false>(old[s][g], rowp, sg, vec);
+        else zero4(old[s][g]);
+      }
+    }
+  };
+  const bool add = a.dw_add != 0 && a.dw_fmt == FMT_F32;
+  if constexpr (DMA) {
+    if (add) request_old();
+    tile_gradient_dma(a, lds, row0, col0);
+  } else {
+    tile_gradient<IN>(a, lds, row0, col0);
+    if (add) request_old();
+  }
+  const float* sG = reinterpret_cast<const float*>(lds);
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     const int rl = s * 16 + (threadIdx.x >> 4);
@@ -1543,13 +1572,11 @@ __global__ void __launch_bounds__(NT, 2) k_gemm(const KArgs a) {
       float x[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) x[i] = sG[rl * GP + 64 * g + cl + i];
-      if (a.dw_add) {                       // gradient accumulation: old + G, one fp32 addition
-        Raw4<FMT_F32> r;
-        ld4<FMT_F32, false>(r, rowp, sg, vec);
-        float old[4];
-        dec4<FMT_F32>(r, old);
+      if (add) {                            // gradient accumulation: old + G, one fp32 addition
+        float o[4];
+        dec4<FMT_F32>(old[s][g], o);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = old[i] + x[i];
+        for (int i = 0; i < 4; ++i) x[i] = o[i] + x[i];
       }
       if (a.dw_fmt == FMT_F32) st4<FMT_F32, false>(rowp, sg, vec, x, 0, 0, 0);
       else st4<FMT_BF16, false>(rowp, sg, vec, x, 0, 0, 0);
