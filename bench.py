@@ -459,7 +459,7 @@ def cpu_baseline(layers, seconds):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1"}), flush=True)
+        print(json.dumps({"error": "bench.py measures one GPU only; --gpus must be 1"}), flush=True)
         sys.exit(2)
 
     if args.copy_calibration:

@@ -58,7 +58,7 @@ typedef enum {
   FORGE_E_STEP = 5,        /* step < 1                                              */
   FORGE_E_HYPER = 6,       /* a hyper-parameter is non-finite or out of range       */
   FORGE_E_ALIAS = 7,       /* an output buffer overlaps an input or another output  */
-  FORGE_E_UNSUPPORTED = 8, /* a valid combination this build does not implement     */
+  FORGE_E_UNSUPPORTED = 8, /* a valid combination the library does not implement  */
   FORGE_E_HIP = 9          /* the HIP runtime reported an error at launch           */
 } forge_status;
 
