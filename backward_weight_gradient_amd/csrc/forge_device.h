@@ -1442,13 +1442,13 @@ __global__ void __launch_bounds__(NT, (three_per_cu<OPT, WF, MF, VF, FAST, ACC, 
 // Several independent layers in one launch: the workgroups cover the
 // concatenation of the layers' tile spaces (layer order, row-major tiles
 // within a layer).  Each workgroup finds its layer from the prefix tile
-// counts (uniform scalar work) and then runs exactly the k_fused code on it,
-// so every element is computed as a separate call would compute it.
+// counts (uniform scalar work) and then runs the k_fused code path of three
+// workgroups per CU on it (for every state size, see above), so every
+// element is computed as a separate call would compute it.
 template <int OPT, int WF, int MF, int VF>
-__global__ void __launch_bounds__(NT, (three_per_cu<OPT, WF, MF, VF, true, false, true>() ? 3 : 2))
-    k_fused_group(const GroupArgs g) {
-  constexpr bool OCC3 = three_per_cu<OPT, WF, MF, VF, true, false, true>();
-  __shared__ __attribute__((aligned(16))) char lds[OCC3 ? LDS_HALF : LDS_BYTES];
+__global__ void __launch_bounds__(NT, 3) k_fused_group(const GroupArgs g) {
+  static_assert(three_per_cu<OPT, WF, MF, VF, true, false, true>(), "the grouped kernel runs three per CU");
+  __shared__ __attribute__((aligned(16))) char lds[LDS_HALF];
   const int bid = (int)blockIdx.x;
   int li = 0;
 #pragma unroll
@@ -1461,17 +1461,12 @@ __global__ void __launch_bounds__(NT, (three_per_cu<OPT, WF, MF, VF, true, false
   constexpr int PRE = epi_pre<OPT, WF, MF, VF, true, false, true>();
   epi.tid = threadIdx.x;
   epi.template prefetch<PRE>(a, row0, col0);        // as in k_fused
-  if constexpr (OCC3) {
-    f32x16 acc[2][2];
-    WorkgroupSync sync;
-    dma_accumulate<MainBF16Dma3>(a, lds, row0, col0, threadIdx.x, acc, sync);
-    bar();
-    epi.template prefetch_rest<PRE>(a, row0, col0);
-    epi.run_halves(a, reinterpret_cast<float*>(lds), acc, row0, col0);
-  } else {
-    tile_gradient_dma(a, lds, row0, col0);
-    epi.run_prefetched(a, reinterpret_cast<const float*>(lds), row0, col0);
-  }
+  f32x16 acc[2][2];
+  WorkgroupSync sync;
+  dma_accumulate<MainBF16Dma3>(a, lds, row0, col0, threadIdx.x, acc, sync);
+  bar();   // every wave is done reading the stages before G overwrites them
+  epi.template prefetch_rest<PRE>(a, row0, col0);
+  epi.run_halves(a, reinterpret_cast<float*>(lds), acc, row0, col0);
 }
 
 constexpr int LDS_WIDE = MainWide::S * MainWide::STAGE;   // 128 KiB
