@@ -240,3 +240,20 @@ def test_backward_step_split_orders_split_dgrad_before_the_update():
         a, b = getattr(L, name), getattr(R, name)
         assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"{name} differs"
     _check(dX, L.dY, W_before, what="backward step split")
+
+
+def test_dgrad_split_strided_buffers():
+    """Leading dimensions larger than the row length on dY, W and dX; dX columns past K stay untouched."""
+    _say("case: dgrad split strided")
+    BT, N, K = 200, 2048, 1024
+    need = F.forge_dgrad_workspace_bytes(BT, N, K)
+    assert need > 0
+    dYb, Wb = _operands(BT, N + 8, K + 16, "bf16", "bf16")
+    dY, W = dYb[:, :N], Wb[:N, :K]                     # 16-byte aligned rows, ld > cols
+    big = torch.full((BT, K + 24), float("nan"), device="cuda", dtype=torch.bfloat16)
+    dX = big[:, :K]
+    ws = torch.full((need // 4,), float("nan"), device="cuda")
+    F.forge_dgrad_split(dY, W, dX, ws)
+    torch.cuda.synchronize()
+    _check(dX, dY.contiguous(), W.contiguous(), what="split strided")
+    assert torch.isnan(big[:, K:].float()).all(), "dX columns past K were written"
