@@ -1381,27 +1381,43 @@ constexpr int raw_words(int fmt) {
   return fmt == FMT_F32 ? 4 : fmt == FMT_BF16 ? 2 : fmt == FMT_NONE ? 0 : 2;
 }
 template <int OPT, int WF, int MF, int VF, bool FAST>
-constexpr bool small_state() {
+constexpr int pending_words() {
   using S = Step<OPT, WF, MF, VF, FAST>;
-  return raw_words(S::WFMT) + raw_words(S::MFMT) + raw_words(S::VFMT) <= 6;
+  return raw_words(S::WFMT) + raw_words(S::MFMT) + raw_words(S::VFMT);
+}
+template <int OPT, int WF, int MF, int VF, bool FAST>
+constexpr bool small_state() {
+  return pending_words<OPT, WF, MF, VF, FAST>() <= 6;
 }
 template <int OPT, int WF, int MF, int VF, bool FAST, bool ACC, bool GROUP>
 constexpr bool three_per_cu() {
   return FAST && !ACC && (GROUP || small_state<OPT, WF, MF, VF, FAST>());
 }
-// passes of state in flight, and how many of them are requested before the mainloop
+template <int OPT, int WF, int MF, int VF, bool FAST>
+constexpr bool scaled_state() {
+  using S = Step<OPT, WF, MF, VF, FAST>;
+  return fmt_blocked(S::MFMT) || fmt_blocked(S::VFMT);
+}
+// Passes of state in flight, and how many of them are requested before the
+// mainloop.  In the grouped kernel (a few more registers for the layer
+// lookup) states with block scales request none early: AdamW with int8 or
+// E4M3 moments otherwise spills, and measured 9-10% slower on the Llama
+// decoder layer (Lion with int8 m 2%), while bf16 moments and one fp32
+// moment are 2-3% faster with both requested early.
 constexpr int SMALL_DEPTH = 2, SMALL_PRE = 2, GROUP_LARGE_DEPTH = 2, GROUP_LARGE_PRE = 0;
 template <int OPT, int WF, int MF, int VF, bool FAST, bool ACC, bool GROUP>
 constexpr int epi_depth() {
   return !three_per_cu<OPT, WF, MF, VF, FAST, ACC, GROUP>() ? 4
          : small_state<OPT, WF, MF, VF, FAST>()              ? SMALL_DEPTH
-                                                              : GROUP_LARGE_DEPTH;
+         : pending_words<OPT, WF, MF, VF, FAST>() <= 10      ? GROUP_LARGE_DEPTH
+                                                              : 1;   // fp32 W and two fp32 moments
 }
 template <int OPT, int WF, int MF, int VF, bool FAST, bool ACC, bool GROUP>
 constexpr int epi_pre() {
   return !three_per_cu<OPT, WF, MF, VF, FAST, ACC, GROUP>() ? 4
-         : small_state<OPT, WF, MF, VF, FAST>()              ? SMALL_PRE
-                                                              : GROUP_LARGE_PRE;
+         : !small_state<OPT, WF, MF, VF, FAST>()             ? GROUP_LARGE_PRE
+         : GROUP && scaled_state<OPT, WF, MF, VF, FAST>()    ? 0
+                                                              : SMALL_PRE;
 }
 
 template <int IN, bool FAST, int OPT, int WF, int MF, int VF, bool ACC = false>
