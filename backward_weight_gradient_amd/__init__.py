@@ -118,6 +118,9 @@ def _load() -> ctypes.CDLL:
     lib.forge_backward_step_split.restype = st
     lib.forge_debug_e4m3.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
     lib.forge_debug_e4m3.restype = st
+    lib.forge_debug_quant.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                      ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    lib.forge_debug_quant.restype = st
     lib.forge_debug_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
     lib.forge_debug_copy.restype = st
     lib.forge_debug_mfma_peak.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
@@ -162,9 +165,21 @@ def mat(t) -> forge_mat:
 
 
 def state(t, scale=None, block: int = 0) -> forge_state:
-    """A forge_state: values (f32 / bf16) or int8 codes plus fp32 block scales."""
-    return forge_state(mat(t), (scale.data_ptr() or None) if scale is not None else None,
-                       block if scale is not None else 0)
+    """A forge_state: values (f32 / bf16), or 8-bit codes (int8 / uint8 / E4M3)
+    plus fp32 block scales.  The scale tensor must be float32, contiguous, on
+    t's device, with rows * cols / block elements, block in {32, 64, 128}:
+    the kernels read and write exactly that many scales through its pointer."""
+    if scale is None:
+        return forge_state(mat(t), None, 0)
+    if block not in (32, 64, 128):
+        raise ValueError(f"state: block must be 32, 64 or 128, got {block}")
+    if t.dim() != 2 or t.shape[1] % block:
+        raise ValueError("state: the code tensor must be 2-D with cols a multiple of the block")
+    if scale.dtype != torch.float32 or not scale.is_contiguous() or scale.device != t.device:
+        raise ValueError("state: the scale tensor must be contiguous float32 on the codes' device")
+    if scale.numel() != t.shape[0] * (t.shape[1] // block):
+        raise ValueError(f"state: {scale.numel()} scales given, {t.shape[0] * (t.shape[1] // block)} needed")
+    return forge_state(mat(t), scale.data_ptr() or None, block)
 
 
 def hyper(opt: str = "adamw", lr: float = 1e-3, beta1: float = 0.9, beta2: Optional[float] = None,
@@ -230,7 +245,8 @@ def forge_wgrad_step_group(layers, h: forge_hyper, step: int, stream=None, check
     """forge_wgrad_step on several independent layers in as few launches as possible.
 
     layers: sequence of (X, dY, W, m, v, seed) with X, dY, W tensors or forge_mat,
-    m, v forge_state (v None unless AdamW).
+    m, v forge_state or None (m for AdamW, NAdam, RAdam, Lion, SGD-m; v for AdamW,
+    NAdam, RAdam, RMSprop, AdaGrad).
     """
     keep = []
     arr = (forge_layer * max(1, len(layers)))()
@@ -359,6 +375,26 @@ def forge_debug_e4m3(inp, out, stream=None, check: bool = True) -> int:
     rc = lib.forge_debug_e4m3(inp.data_ptr(), out.data_ptr(), inp.numel(), _stream(stream))
     if check and rc != FORGE_OK:
         raise ForgeError(rc, "forge_debug_e4m3")
+    return rc
+
+
+def forge_debug_quant(inp, codes, scales, dtype: int, second_moment: bool, block: int, stream=None,
+                      check: bool = True) -> int:
+    """The epilogue's 8-bit block quantiser on a 2-D float32 tensor (test hook):
+    codes (int8 / uint8 / float8_e4m3fn, same shape) and fp32 scales
+    [rows, cols / block] are written; dtype FORGE_S8, FORGE_U8 or FORGE_E4M3."""
+    if inp.dim() != 2 or not inp.is_contiguous() or inp.dtype != torch.float32:
+        raise ValueError("forge_debug_quant: inp must be a contiguous 2-D float32 tensor")
+    rows, cols = inp.shape
+    if codes.shape != inp.shape or not codes.is_contiguous() or codes.element_size() != 1:
+        raise ValueError("forge_debug_quant: codes must be a contiguous 1-byte tensor of inp's shape")
+    if scales.dtype != torch.float32 or not scales.is_contiguous() or \
+            (block > 0 and scales.numel() != rows * (cols // block)):
+        raise ValueError("forge_debug_quant: scales must be contiguous float32 with rows * cols / block elements")
+    rc = lib.forge_debug_quant(inp.data_ptr() or None, codes.data_ptr() or None, scales.data_ptr() or None,
+                               rows, cols, dtype, 1 if second_moment else 0, block, _stream(stream))
+    if check and rc != FORGE_OK:
+        raise ForgeError(rc, "forge_debug_quant")
     return rc
 
 

@@ -16,6 +16,7 @@ namespace {
 using namespace forge;
 
 constexpr uint32_t kGolden = 0x9E3779B9u;
+constexpr uint64_t kMaxExtent = 1ull << 48;   // largest byte extent of one matrix
 
 // MurmurHash3 32-bit finaliser (Appleby, public domain).
 uint32_t fmix32_host(uint32_t h) {
@@ -87,6 +88,13 @@ forge_status check_mat(const forge_mat& m, int64_t rows, int64_t cols) {
   const int es = elem_size(m.dtype);
   if (es == 0) return FORGE_E_DTYPE;
   if (m.rows > 0 && m.cols > 0) {
+    // byte extent ((rows - 1) ld + cols) es: no wrap-around, at most 2^48
+    // (so that every row offset the kernels form in 64 bits is exact)
+    uint64_t ext = 0;
+    if (__builtin_mul_overflow((uint64_t)(m.rows - 1), (uint64_t)m.ld, &ext) ||
+        __builtin_add_overflow(ext, (uint64_t)m.cols, &ext) || __builtin_mul_overflow(ext, (uint64_t)es, &ext) ||
+        ext > kMaxExtent)
+      return FORGE_E_SHAPE;
     if (m.data == nullptr) return FORGE_E_NULL;
     if (!aligned(m.data, es)) return FORGE_E_ALIGN;
   }
@@ -612,6 +620,25 @@ forge_status forge_debug_e4m3(const float* in, uint8_t* out, int64_t n, void* st
   if (!aligned(in, 4)) return FORGE_E_ALIGN;
   if (overlap(raw_range(in, (uint64_t)n * 4), raw_range(out, (uint64_t)n))) return FORGE_E_ALIAS;
   return hip_status(launch_debug_e4m3(in, out, (uint32_t)n, (hipStream_t)stream));
+}
+
+forge_status forge_debug_quant(const float* in, uint8_t* codes, float* scales, int64_t rows, int64_t cols,
+                               int32_t dtype, int32_t second_moment, int32_t block, void* stream) {
+  if (dtype != FORGE_S8 && dtype != FORGE_U8 && dtype != FORGE_E4M3) return FORGE_E_DTYPE;
+  if (second_moment != 0 && second_moment != 1) return FORGE_E_DTYPE;
+  if ((dtype == FORGE_S8 && second_moment) || (dtype == FORGE_U8 && !second_moment)) return FORGE_E_DTYPE;
+  if (!(block == 32 || block == 64 || block == 128)) return FORGE_E_SHAPE;
+  if (rows < 0 || cols < 0 || cols % block != 0) return FORGE_E_SHAPE;
+  if ((uint64_t)rows * (uint64_t)cols >= (1ull << 32) || rows >= (1ll << 31) || cols >= (1ll << 31))
+    return FORGE_E_SHAPE;
+  if (rows == 0 || cols == 0) return FORGE_OK;
+  if (!in || !codes || !scales) return FORGE_E_NULL;
+  if (!aligned(in, 4) || !aligned(codes, 4) || !aligned(scales, 4)) return FORGE_E_ALIGN;
+  const uint64_t n = (uint64_t)rows * (uint64_t)cols;
+  const Range ri = raw_range(in, n * 4), rc = raw_range(codes, n), rs = raw_range(scales, n / (uint64_t)block * 4);
+  if (overlap(ri, rc) || overlap(ri, rs) || overlap(rc, rs)) return FORGE_E_ALIAS;
+  return hip_status(launch_debug_quant(in, codes, scales, (int)rows, (int)cols, dtype, second_moment != 0, block,
+                                       (hipStream_t)stream));
 }
 
 forge_status forge_debug_copy(const void* src, void* dst, int64_t bytes, void* stream) {

@@ -968,10 +968,17 @@ __device__ __forceinline__ void st4(void* row, const Seg& g, bool vec, const flo
 //           never becomes code 0 but the smallest subnormal 2^-9, which is
 //           what rounding max(y, 2^-9) gives for every positive y.
 // a is the block absmax; the scale and the reciprocal are correctly rounded
-// fp32 divisions.
+// fp32 divisions.  A block whose absmax is below 2^-64 (a long-decayed
+// moment) would overflow QMAX / a; there the values and the reciprocal are
+// taken 2^64 times larger and smaller (exact scalings), which gives the
+// product x * (QMAX / a) as if the exponent range were unbounded -- the same
+// bits as the plain product wherever that one is finite.
 template <int FMT, bool POSITIVE>
-__device__ __forceinline__ void quantize_chunk(const float (&x)[8], int block, const Seg (&sg)[2], void* row_codes,
-                                               bool vec, float* row_scales) {
+__device__ __forceinline__ void quantize_chunk(const float (&x_in)[8], int block, const Seg (&sg)[2],
+                                               void* row_codes, bool vec, float* row_scales) {
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = x_in[i];
   constexpr float QMAX = FMT == FMT_S8 ? 127.f : FMT == FMT_U8 ? 255.f : 448.f;
   // absmax as the unsigned max of |x| bit patterns (the second moment is
   // never negative, so for U8 this is max x)
@@ -1002,6 +1009,17 @@ __device__ __forceinline__ void quantize_chunk(const float (&x)[8], int block, c
   } else {
     sc[1] = a[1] > 0.f ? a[1] / QMAX : 0.f;
     inv[1] = a[1] > 0.f ? QMAX / a[1] : 0.f;
+  }
+  const bool tiny0 = a[0] > 0.f && a[0] < 0x1p-64f, tiny1 = a[1] > 0.f && a[1] < 0x1p-64f;
+  if (tiny0 || tiny1) {   // rare; skipped by the whole wave when no lane needs it
+    const bool tiny[2] = {tiny0, tiny1};
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      if (!tiny[g]) continue;
+      inv[g] = QMAX / (a[g] * 0x1p64f);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[4 * g + i] *= 0x1p64f;
+    }
   }
   const int lpb = block == 32 ? 8 : 16;
   const bool writer = (threadIdx.x & (lpb - 1)) == 0;

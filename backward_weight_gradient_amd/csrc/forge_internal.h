@@ -187,6 +187,10 @@ hipError_t launch_debug_sr(const float* in, uint16_t* out, uint32_t n, uint32_t 
                            hipStream_t stream);
 // E4M3 rounding (nearest even, saturating) of n floats.
 hipError_t launch_debug_e4m3(const float* in, uint8_t* out, uint32_t n, hipStream_t stream);
+// The 8-bit block quantiser of the epilogue (S8 / U8 / E4M3 codes and fp32
+// scales) on a dense [rows, cols] fp32 array; positive: the second-moment rule.
+hipError_t launch_debug_quant(const float* in, uint8_t* codes, float* scales, int rows, int cols, int fmt,
+                              bool positive, int block, hipStream_t stream);
 hipError_t launch_debug_copy(const void* src, void* dst, uint64_t bytes, hipStream_t stream);
 hipError_t launch_debug_mfma(float* out, int blocks, int iters, hipStream_t stream);
 

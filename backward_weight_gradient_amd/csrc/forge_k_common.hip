@@ -27,6 +27,50 @@ __global__ void k_debug_e4m3(const float* __restrict__ in, uint8_t* __restrict__
     if (i0 + k < n) out[i0 + k] = (uint8_t)((w >> (8 * k)) & 0xFFu);
 }
 
+// The fused epilogue's 8-bit block quantiser on its own: quantize_chunk with
+// the epilogue's thread mapping (thread t of a 256-thread workgroup owns row
+// t / 16 of a 16-row slab and the two 4-element segments at columns
+// 4 (t % 16) and 64 + 4 (t % 16) of a 128-column tile).  in, codes: dense
+// [rows, cols]; scales: dense [rows, cols / block].  cols % block == 0, so a
+// segment is entirely inside or outside; rows past the end take no part.
+template <int FMT, bool POSITIVE>
+__global__ void __launch_bounds__(256) k_debug_quant(const float* __restrict__ in, uint8_t* __restrict__ codes,
+                                                    float* __restrict__ scales, int rows, int cols, int block) {
+  const int tiles_c = (cols + 127) / 128;
+  const int rg = (int)blockIdx.x / tiles_c, ct = (int)blockIdx.x - rg * tiles_c;
+  const int tid = threadIdx.x;
+  const int p = rg * 16 + (tid >> 4);
+  Seg sg[2];
+  float x[8];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    sg[g].q = ct * 128 + 64 * g + 4 * (tid & 15);
+    sg[g].nv = max(0, min(4, cols - sg[g].q));
+    sg[g].ok = sg[g].nv > 0 && p < rows;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[4 * g + i] = sg[g].ok ? in[(int64_t)p * cols + sg[g].q + i] : 0.f;
+  }
+  const int64_t prow = p < rows ? p : 0;   // a valid row base for lanes that store nothing
+  quantize_chunk<FMT, POSITIVE>(x, block, sg, codes + prow * cols, true, scales + prow * (cols / block));
+}
+
+hipError_t launch_debug_quant(const float* in, uint8_t* codes, float* scales, int rows, int cols, int fmt,
+                              bool positive, int block, hipStream_t st) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  const dim3 grid((unsigned)(((rows + 15) / 16) * ((cols + 127) / 128))), b(256);
+  if (fmt == FMT_S8 && !positive)
+    hipLaunchKernelGGL((k_debug_quant<FMT_S8, false>), grid, b, 0, st, in, codes, scales, rows, cols, block);
+  else if (fmt == FMT_U8 && positive)
+    hipLaunchKernelGGL((k_debug_quant<FMT_U8, true>), grid, b, 0, st, in, codes, scales, rows, cols, block);
+  else if (fmt == FMT_E4M3 && !positive)
+    hipLaunchKernelGGL((k_debug_quant<FMT_E4M3, false>), grid, b, 0, st, in, codes, scales, rows, cols, block);
+  else if (fmt == FMT_E4M3 && positive)
+    hipLaunchKernelGGL((k_debug_quant<FMT_E4M3, true>), grid, b, 0, st, in, codes, scales, rows, cols, block);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 hipError_t launch_debug_e4m3(const float* in, uint8_t* out, uint32_t n, hipStream_t st) {
   if (n == 0) return hipSuccess;
   const uint64_t threads = (n + 3ull) / 4ull;

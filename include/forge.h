@@ -21,8 +21,10 @@
  *     forge_dgrad_split and forge_backward_step_split write into a
  *     caller-provided workspace).
  *   - Matrices are row-major; `ld` is the leading dimension in elements
- *     (ld >= cols).  Flat indices used by stochastic rounding are the logical
- *     row-major index p*K + q, independent of ld.
+ *     (ld >= cols); a matrix spans ((rows - 1) * ld + cols) elements, whose
+ *     bytes must not exceed 2^48 (else FORGE_E_SHAPE).  Flat indices used by
+ *     stochastic rounding are the logical row-major index p*K + q,
+ *     independent of ld.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *     stream) and return after the kernels are enqueued.  W, m, v and the
  *     block scales (int8 / E4M3 states) are updated in place.
@@ -33,8 +35,9 @@
  *     buffers.
  *   - Precondition the library cannot check (paper, Appendix A, Remark 1):
  *     the caller has already computed the input gradient dX = dY W from the
- *     pre-update W; a weight with more than one gradient consumer in a step
- *     (tied embeddings, expert-parallel experts) must not be stepped here.
+ *     pre-update W; a weight whose gradient comes from several consumers in
+ *     one step (tied embeddings, expert-parallel experts) must not be stepped
+ *     here.
  *   - Precondition of the fused schedule: no global gradient-norm clip, and
  *     forge_wgrad_step sees the whole gradient of the step; to accumulate
  *     micro-batches use forge_wgrad_accumulate and
@@ -193,7 +196,7 @@ typedef struct {
   const forge_mat* dY;
   forge_mat* W;
   forge_state* m;
-  forge_state* v;  /* NULL unless AdamW */
+  forge_state* v;  /* as forge_wgrad_step: NULL unless the optimizer keeps a second state */
   uint64_t seed;
 } forge_layer;
 
@@ -341,6 +344,24 @@ forge_status forge_debug_sr_bf16(const float* in, uint16_t* out, int64_t n, uint
  * E_SHAPE (n < 0 or n >= 2^32), E_ALIGN, E_ALIAS, E_HIP.
  */
 forge_status forge_debug_e4m3(const float* in, uint8_t* out, int64_t n, void* stream);
+
+/*
+ * forge_debug_quant -- test hook: the fused step's 8-bit block quantiser
+ * (the store of an S8, U8 or E4M3 state: paper, section 2.3 and Appendix B
+ * for int8, section 3.6 for FP8; the rules are those of forge_state above)
+ * on its own, through the same device function and thread mapping as the
+ * epilogue.  in: dense [rows, cols] fp32 device array; codes: dense
+ * [rows, cols] bytes (int8 / uint8 / E4M3), 4-byte aligned; scales: dense
+ * [rows, cols / block] fp32, written.
+ * dtype FORGE_S8 takes the first-moment rule (second_moment = 0), FORGE_U8
+ * the second-moment rule (second_moment = 1), FORGE_E4M3 either.
+ * block: 32, 64 or 128 with cols % block == 0; rows * cols < 2^32.
+ * A block whose absmax is below 2^-64 is quantised as if the exponent range
+ * were unbounded (x * (QMAX / absmax) with no overflow).
+ * Errors: E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_ALIAS, E_HIP.
+ */
+forge_status forge_debug_quant(const float* in, uint8_t* codes, float* scales, int64_t rows, int64_t cols,
+                               int32_t dtype, int32_t second_moment, int32_t block, void* stream);
 
 /*
  * forge_debug_copy -- measurement hook for the HBM roofline (the pages

@@ -30,8 +30,8 @@ design notes):
 * Lion follows its textbook form (Chen et al. 2023): interpolate
   ``c = b1*m + (1-b1)*G``, update ``W <- (1-lr*wd)*W - lr*sign(c)`` with
   sign(0) = 0, then ``m <- b2*m + (1-b2)*G``.
-* SGD with momentum follows PyTorch SGD semantics (the paper's per-family
-  check is against "a reference PyTorch implementation", Appendix N):
+* SGD with momentum follows PyTorch SGD semantics (the paper checks each
+  fused family against PyTorch's own implementation, Appendix N):
   coupled L2 decay ``g = G + wd*W``, ``b <- mu*b + g`` (dampening 0, no
   Nesterov), ``W <- W - lr*b``; ``mu`` is passed as ``beta1``.
 * NAdam, RAdam, RMSprop, AdaGrad and plain SGD: the pages name each family
@@ -43,14 +43,14 @@ design notes):
   takes the adaptive step only once ``rho_t > 5``; both take AdamW's
   decoupled decay (the pages call them AdamW variants).  RMSprop ("second
   moment only") keeps ``v <- a v + (1-a) g^2`` with ``a = beta2``, no
-  momentum, not centred; AdaGrad ("cumulative squared gradient") keeps
+  momentum, not centred; AdaGrad (a running sum of squared gradients) keeps
   ``v <- v + g^2`` with no learning-rate decay; RMSprop, AdaGrad and SGD take
   coupled L2 decay like SGD with momentum.
 * The step index t is 1-based and is used directly in the bias correction.
 * The SR random bits come from a counter-based hash of (seed, step, tensor,
-  flat index).  The pages ask only for "a six-operation splitmix-style
-  integer hash of (seed, offset)" (Appendix C, Implementation); the hash used
-  here is the MurmurHash3 32-bit finaliser ``fmix32`` (Appleby, public
+  flat index).  The pages name only a cheap integer hash of the seed and an
+  offset, of the splitmix kind, in place of Philox (Appendix C,
+  Implementation; Table 3); the hash used here is the MurmurHash3 32-bit finaliser ``fmix32`` (Appleby, public
   domain), composed as documented in :func:`sr_key` and :func:`sr_bits`.
 * Stochastic rounding adds 16 random bits below the bf16 cut and truncates
   (rounds |x| up with probability f = (x - x_lo)/ULP, quantised to 2^-16);
@@ -332,8 +332,8 @@ def adamw(W, G, m, v, t, lr, beta1, beta2, eps, weight_decay):
 
 
 def lion(W, G, m, lr, beta1, beta2, weight_decay):
-    """Lion (Appendix N: sign-of-momentum update with a single moment buffer;
-    textbook form of Chen et al. 2023), fp64."""
+    """Lion (Appendix N: the step is the sign of an interpolated momentum,
+    and one moment buffer is kept; textbook form of Chen et al. 2023), fp64."""
     c = beta1 * m + (1.0 - beta1) * G
     W1 = (1.0 - lr * weight_decay) * W - lr * np.sign(c)
     m1 = beta2 * m + (1.0 - beta2) * G
@@ -412,7 +412,7 @@ def rmsprop(W, G, v, lr, alpha, eps, weight_decay):
 
 
 def adagrad(W, G, v, lr, eps, weight_decay):
-    """AdaGrad (Appendix N: cumulative squared gradient, no decay), coupled
+    """AdaGrad (Appendix N: the squared gradients are summed, never decayed), coupled
     decay, no learning-rate decay, fp64:
     g = G + wd W;  v' = v + g^2;  W' = W - lr g / (sqrt(v') + eps)."""
     g = G + weight_decay * W
@@ -437,17 +437,35 @@ def _blocks(x32: np.ndarray, block: int) -> np.ndarray:
     return x32.reshape(r, c // block, block)
 
 
+_TINY = np.float32(2.0 ** -64)
+_BIG = np.float32(2.0 ** 64)
+
+
+def _scaled_codes(xb: np.ndarray, a: np.ndarray, qmax: float):
+    """fp32(x * fp32(qmax / a)) for every element of every block, and the
+    scale fp32(a / qmax).  The reciprocal is the correctly rounded fp32
+    quotient; for a block absmax below 2^-64 the quotient would overflow, so
+    there x and a are first multiplied by 2^64 (exact in fp32), which yields
+    the product as if the exponent range were unbounded and equals the plain
+    formula wherever that one is finite.  a = 0 gives inv = s = 0."""
+    q32 = np.float32(qmax)
+    tiny = (a > 0) & (a < _TINY)
+    a_eff = np.where(tiny, a * _BIG, a).astype(np.float32)
+    x_eff = np.where(tiny[:, :, None], xb * _BIG, xb).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        s = np.where(a > 0, a / q32, np.float32(0)).astype(np.float32)
+        inv = np.where(a > 0, q32 / a_eff, np.float32(0)).astype(np.float32)
+    return (x_eff * inv[:, :, None]).astype(np.float32), s
+
+
 def quantize_signed(x32: np.ndarray, block: int):
     """Signed block-absmax int8: a = max|x| over the block, s = fp32(a/127),
     code = clamp(rint(fp32(x * fp32(127/a))), -127, 127); a = 0 gives s = 0
     and all codes 0.  Returns (int8 codes, float32 scales)."""
     xb = _blocks(np.asarray(x32, dtype=np.float32), block)
     a = np.max(np.abs(xb), axis=2)
-    with np.errstate(divide="ignore", invalid="ignore"):
-        s = np.where(a > 0, a / np.float32(127), np.float32(0)).astype(np.float32)
-        inv = np.where(a > 0, np.float32(127) / a, np.float32(0)).astype(np.float32)
-    q = np.rint((xb * inv[:, :, None]).astype(np.float32))
-    q = np.clip(q, -127, 127).astype(np.int8)
+    y, s = _scaled_codes(xb, a, 127.0)
+    q = np.clip(np.rint(y), -127, 127).astype(np.int8)
     return q.reshape(x32.shape), s
 
 
@@ -458,11 +476,8 @@ def quantize_unsigned(x32: np.ndarray, block: int):
     Returns (uint8 codes, float32 scales)."""
     xb = _blocks(np.asarray(x32, dtype=np.float32), block)
     a = np.max(xb, axis=2)
-    with np.errstate(divide="ignore", invalid="ignore"):
-        s = np.where(a > 0, a / np.float32(255), np.float32(0)).astype(np.float32)
-        inv = np.where(a > 0, np.float32(255) / a, np.float32(0)).astype(np.float32)
-    q = np.rint((xb * inv[:, :, None]).astype(np.float32))
-    q = np.where(xb == 0, 0, np.clip(q, 1, 255)).astype(np.uint8)
+    y, s = _scaled_codes(xb, a, 255.0)
+    q = np.where(xb == 0, 0, np.clip(np.rint(y), 1, 255)).astype(np.uint8)
     return q.reshape(x32.shape), s
 
 
@@ -507,10 +522,8 @@ def quantize_e4m3(x32: np.ndarray, block: int, positive: bool):
     a = 0 gives s = 0 and all codes +-0.  Returns (uint8 codes, float32 scales)."""
     xb = _blocks(np.asarray(x32, dtype=np.float32), block)
     a = np.max(np.abs(xb), axis=2)
-    with np.errstate(divide="ignore", invalid="ignore"):
-        s = np.where(a > 0, a / np.float32(E4M3_MAX), np.float32(0)).astype(np.float32)
-        inv = np.where(a > 0, np.float32(E4M3_MAX) / a, np.float32(0)).astype(np.float32)
-    q = f32_to_e4m3_rne((xb * inv[:, :, None]).astype(np.float32))
+    y, s = _scaled_codes(xb, a, E4M3_MAX)
+    q = f32_to_e4m3_rne(y)
     if positive:
         q = np.where((xb > 0) & (q == 0), np.uint8(1), q).astype(np.uint8)
     return q.reshape(x32.shape), s

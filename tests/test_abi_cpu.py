@@ -485,3 +485,61 @@ def test_e4m3_state_rules():
     assert check(X, dY, W, m, v) == F.FORGE_E_NULL                                 # scales required
     m.scale, m.block = addr(5), 48
     assert check(X, dY, W, m, v) == F.FORGE_E_SHAPE                                # block 32 / 64 / 128
+
+
+def test_matrix_extent_is_bounded():
+    """A leading dimension whose byte extent wraps around 64 bits, or exceeds
+    2^48 bytes, is a shape error (not a spurious alias, not accepted)."""
+    X, dY, W, m, v = layer(N=8, K=256)
+    for ld in ((1 << 63) - 1, 1 << 62, 1 << 47):
+        Wbad = F.mat_raw(addr(2), F.FORGE_BF16, 8, 256, ld=ld)
+        assert check(X, dY, Wbad, m, v) == F.FORGE_E_SHAPE, ld
+    # just inside: the extent of W is exactly 2^48 bytes (the inputs and states
+    # are placed above it)
+    ld_ok = ((1 << 47) - 256) // 7
+    Wok = F.mat_raw(addr(2), F.FORGE_BF16, 8, 256, ld=ld_ok)
+    assert (7 * ld_ok + 256) * 2 <= 1 << 48
+    far = addr(2) + (1 << 48) + (1 << 36)
+    m2 = F.forge_state(F.mat_raw(far, F.FORGE_F32, 8, 256), None, 0)
+    v2 = F.forge_state(F.mat_raw(far + (1 << 36), F.FORGE_F32, 8, 256), None, 0)
+    assert check(X, dY, Wok, m2, v2) == F.FORGE_OK
+    # the same bound for the dX GEMM's operands
+    dYg = F.mat_raw(addr(0), F.FORGE_BF16, 4, 256)
+    Wg = F.mat_raw(addr(1), F.FORGE_BF16, 256, 256, ld=1 << 62)
+    dX = F.mat_raw(addr(2), F.FORGE_BF16, 4, 256)
+    assert F.lib.forge_dgrad(ctypes.byref(dYg), ctypes.byref(Wg), ctypes.byref(dX), None) == F.FORGE_E_SHAPE
+
+
+def test_debug_quant_argument_errors():
+    q = F.lib.forge_debug_quant
+    a, c, s = addr(0), addr(1), addr(2)
+    assert q(a, c, s, 4, 128, F.FORGE_F32, 0, 128, None) == F.FORGE_E_DTYPE
+    assert q(a, c, s, 4, 128, F.FORGE_S8, 1, 128, None) == F.FORGE_E_DTYPE   # signed codes: first-moment rule
+    assert q(a, c, s, 4, 128, F.FORGE_U8, 0, 128, None) == F.FORGE_E_DTYPE   # unsigned: second-moment rule
+    assert q(a, c, s, 4, 128, F.FORGE_E4M3, 2, 128, None) == F.FORGE_E_DTYPE
+    assert q(a, c, s, 4, 128, F.FORGE_S8, 0, 96, None) == F.FORGE_E_SHAPE
+    assert q(a, c, s, 4, 96, F.FORGE_S8, 0, 64, None) == F.FORGE_E_SHAPE      # cols % block
+    assert q(a, c, s, 1 << 17, 1 << 15, F.FORGE_S8, 0, 128, None) == F.FORGE_E_SHAPE   # 2^32 elements
+    assert q(None, c, s, 4, 128, F.FORGE_S8, 0, 128, None) == F.FORGE_E_NULL
+    assert q(a, c + 2, s, 4, 128, F.FORGE_S8, 0, 128, None) == F.FORGE_E_ALIGN
+    assert q(a, a + 256, s, 4, 128, F.FORGE_S8, 0, 128, None) == F.FORGE_E_ALIAS
+    assert q(a, c, c + 128, 4, 128, F.FORGE_E4M3, 1, 32, None) == F.FORGE_E_ALIAS
+    assert q(None, None, None, 0, 128, F.FORGE_U8, 1, 128, None) == F.FORGE_OK
+
+
+def test_binding_state_checks_the_scale_tensor():
+    """The binding forwards a scale pointer only for a float32, contiguous
+    tensor of exactly rows * cols / block elements on the codes' device."""
+    import torch
+    codes = torch.zeros((4, 256), dtype=torch.int8)
+    good = torch.zeros((4, 2), dtype=torch.float32)
+    assert F.state(codes, good, 128).block == 128
+    for bad, block in ((torch.zeros(1, dtype=torch.float32), 128),           # too few
+                       (torch.zeros((4, 2), dtype=torch.bfloat16), 128),     # wrong dtype
+                       (torch.zeros((2, 4), dtype=torch.float32).t(), 128),  # not contiguous
+                       (torch.zeros((4, 2), dtype=torch.float32), 96),       # block not allowed
+                       (torch.zeros((4, 4), dtype=torch.float32), 128)):     # too many
+        with pytest.raises(ValueError):
+            F.state(codes, bad, block)
+    with pytest.raises(ValueError):
+        F.state(torch.zeros((4, 200), dtype=torch.int8), torch.zeros((4, 1)), 128)

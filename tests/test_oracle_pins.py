@@ -241,6 +241,29 @@ def test_sr_bits_uniform_and_independent():
     assert len({O.sr_key(7, 3, t) for t in range(3)}) == 3
 
 
+def test_sr_key_and_bits_hand_worked():
+    """The key derivation and the per-element bits against values worked by
+    hand from the written specification (tests/golden/sr_key_worked.json:
+    every fmix32 call with its intermediate words).  A swapped hi/lo fold, an
+    addition in place of an xor, a wrong tensor offset or a different index
+    multiplier changes these words."""
+    with open(os.path.join(GOLDEN, "sr_key_worked.json")) as f:
+        doc = json.load(f)
+    n_calls = 0
+    for case in doc["cases"]:
+        seed, step, tid = int(case["seed"], 16), int(case["step"], 16), case["tensor_id"]
+        for w in case["key_working"]:
+            assert O.fmix32(int(w["in"], 16)) == int(w["out"], 16)
+            n_calls += 1
+        assert O.sr_key(seed, step, tid) == int(case["key"], 16), case
+        key = int(case["key"], 16)
+        for b in case["sr_bits"]:
+            assert O.fmix32(int(b["fmix32"]["in"], 16)) == int(b["fmix32"]["out"], 16)
+            got = O.sr_bits(key, np.array([b["flat_index"]], dtype=np.uint64))
+            assert int(got[0]) == int(b["r16"], 16), (case["seed"], b["flat_index"])
+    assert n_calls == 4 * len(doc["cases"]) and len(doc["cases"]) >= 5
+
+
 # ---------------------------------------------------------------------------
 # bf16 rounding (Appendix C)
 # ---------------------------------------------------------------------------
@@ -307,6 +330,38 @@ def test_sr_quarter_ulp_microbenchmark():
     assert abs(np.mean(w_sr.astype(np.float64) - 0.75) - (-0.100)) < 5e-4
 
 
+@pytest.mark.parametrize("BT", [512, 4100])
+@pytest.mark.parametrize("opt", ["adamw", "nadam"])
+def test_bf16_flip_fraction_is_under_the_parity_floor(BT, opt):
+    """The GPU parity tests require the stored bf16 patterns to equal the
+    oracle's for a fraction >= 1 - (1e-3 + 2 sqrt(BT) 2^-16) of the elements.
+    Derivation: with the same SR bits on both sides a pattern differs only
+    where the fp32 gradient's summation error (about sqrt(BT) 2^-24 relative
+    for a BT-term fp32 sum) moves the value across its rounding decision,
+    which happens with probability of that size in units of a bf16 ULP
+    (2^-8): about sqrt(BT) 2^-16, doubled, plus 1e-3 for the elements whose
+    gradient nearly cancels.  Checked here on the oracle itself: the step
+    stochastically rounded from an fp32 gradient summed in one fixed order
+    (tokens ascending, a pessimistic order for fp32) against the step from
+    the exact gradient, with the bf16 W, m and v and the inputs of the
+    bf16-everywhere workload."""
+    import synth
+    N, K, step, seed = 256, 256, 10, 1337
+    spec = synth.LayerSpec(in_dtype="bf16", w_fmt="bf16", m_fmt="bf16", v_fmt="bf16")
+    X, dY = synth.activations(2, BT, N, K, step, in_dtype="bf16")
+    st = synth.state(2, N, K, spec)
+    Xh, dYh = synth.host(X), synth.host(dY)
+    W, m, v = (O.Stored("bf16", synth.host(st[k])) for k in ("W", "m", "v"))
+    hyp = O.Hyper(opt=opt, round="sr")
+    exact = O.apply_step(O.weight_grad(Xh, dYh), W, m, v, hyp, step, seed)
+    fp32 = O.apply_step(O.weight_grad(Xh, dYh, order="seq32"), W, m, v, hyp, step, seed)
+    floor = 1e-3 + 2.0 * math.sqrt(BT) * 2.0 ** -16
+    for name in ("W", "m", "v"):
+        flips = float(np.mean(exact[name].data != fp32[name].data))
+        print(f"{opt} BT {BT} {name}: {flips:.6f} of the patterns differ (floor {floor:.6f})")
+        assert flips <= floor, (name, flips, floor)
+
+
 # ---------------------------------------------------------------------------
 # int8 moments (section 2.3, Appendix B)
 # ---------------------------------------------------------------------------
@@ -345,6 +400,52 @@ def test_int8_exact_grid_values():
     q, sc = O.quantize_signed(x, 256)
     assert sc[0, 0] == np.float32(127 * 0.5 / 127)
     np.testing.assert_array_equal(q[0, :255], codes)
+
+
+def test_quantisers_round_ties_to_even():
+    """Round to nearest with ties to even (reading of Appendix B, Prop. 4):
+    with absmax 127 (255) the reciprocal is exactly 1, so x = k + 1/2 is a
+    tie; codes worked by hand.  A kernel that rounded ties away from zero
+    (roundf) would give 1, 3, -1, -3, 127 here."""
+    x = np.zeros((1, 32), dtype=np.float32)
+    x[0, :8] = [127.0, 0.5, 2.5, -0.5, -2.5, 126.5, -126.5, 1.5]
+    q, s = O.quantize_signed(x, 32)
+    assert s[0, 0] == np.float32(1.0)
+    assert list(q[0, :8]) == [127, 0, 2, 0, -2, 126, -126, 2]
+    u = np.zeros((1, 32), dtype=np.float32)
+    u[0, :6] = [255.0, 0.5, 2.5, 3.5, 254.5, 0.25]
+    qu, su = O.quantize_unsigned(u, 32)
+    assert su[0, 0] == np.float32(1.0)
+    # 0.5 -> 0 by the tie rule, floored to 1 (a positive value never takes code 0)
+    assert list(qu[0, :6]) == [255, 1, 2, 4, 254, 1]
+    # the same ties with a non-trivial exact reciprocal: absmax 127/8, inv = 8
+    x2 = x / np.float32(8)
+    q2, s2 = O.quantize_signed(x2, 32)
+    assert s2[0, 0] == np.float32(0.125)
+    np.testing.assert_array_equal(q2, q)
+
+
+@pytest.mark.parametrize("shift", [-100, -70, -40, 40])
+def test_quantisers_commute_with_power_of_two_scaling(shift):
+    """Scaling a block by 2^k leaves every 8-bit code unchanged and scales its
+    scale by 2^k (every step of the quantiser is exact under such scaling
+    while no value leaves the normal range).  Shifts of -70 and -100 take the
+    block absmax below 2^-64, where the reciprocal is formed on values scaled
+    by 2^64; -100 also takes it below 127 / FLT_MAX, where the plain
+    reciprocal would overflow."""
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal((8, 256)) * 1e-3).astype(np.float32)
+    x[0, :64] = 0.0                                   # an all-zero 64-block
+    x[1, 3] = 0.25                                    # an outlier
+    f = np.float32(2.0 ** shift)
+    for block in (32, 64, 128):
+        for quant, arr in ((O.quantize_signed, x), (O.quantize_unsigned, np.abs(x)),
+                           (lambda a, b: O.quantize_e4m3(a, b, False), x),
+                           (lambda a, b: O.quantize_e4m3(a, b, True), np.abs(x))):
+            q0, s0 = quant(arr, block)
+            q1, s1 = quant((arr * f).astype(np.float32), block)
+            np.testing.assert_array_equal(q1, q0)
+            np.testing.assert_array_equal(s1, (s0 * f).astype(np.float32))
 
 
 def test_uint8_reserved_zero():
