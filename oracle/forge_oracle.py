@@ -450,8 +450,9 @@ def _scaled_codes(xb: np.ndarray, a: np.ndarray, qmax: float):
     formula wherever that one is finite.  a = 0 gives inv = s = 0."""
     q32 = np.float32(qmax)
     tiny = (a > 0) & (a < _TINY)
-    a_eff = np.where(tiny, a * _BIG, a).astype(np.float32)
-    x_eff = np.where(tiny[:, :, None], xb * _BIG, xb).astype(np.float32)
+    with np.errstate(over="ignore"):       # the scaled copies are used only where the block is tiny
+        a_eff = np.where(tiny, a * _BIG, a).astype(np.float32)
+        x_eff = np.where(tiny[:, :, None], xb * _BIG, xb).astype(np.float32)
     with np.errstate(divide="ignore", invalid="ignore"):
         s = np.where(a > 0, a / q32, np.float32(0)).astype(np.float32)
         inv = np.where(a > 0, q32 / a_eff, np.float32(0)).astype(np.float32)

@@ -69,15 +69,22 @@ class Layer:
     ms: Optional[torch.Tensor] = None
     vs: Optional[torch.Tensor] = None
 
-    def forge_m(self):
-        if self.m is None:
+    def _state(self, t, scale):
+        if t is None:
             return None
-        return F.state(self.m, self.ms, self.spec.block) if self.ms is not None else F.state(self.m)
+        if scale is None:
+            return F.state(t)
+        if self.K % self.spec.block:
+            # a shape the library must reject: built without the binding's own
+            # checks, so that the C ABI's validation is what is exercised
+            return F.forge_state(F.mat(t), scale.data_ptr(), self.spec.block)
+        return F.state(t, scale, self.spec.block)
+
+    def forge_m(self):
+        return self._state(self.m, self.ms)
 
     def forge_v(self):
-        if self.v is None:
-            return None
-        return F.state(self.v, self.vs, self.spec.block) if self.vs is not None else F.state(self.v)
+        return self._state(self.v, self.vs)
 
     def clone(self) -> "Layer":
         c = lambda t: None if t is None else t.clone()
@@ -97,7 +104,9 @@ def make_layer(cfg: int, N: int, K: int, BT: int, step: int, spec: synth.LayerSp
     X, dY = synth.activations(cfg, BT, N, K, step, in_dtype=spec.in_dtype, x_std=x_std, dy_std=dy_std,
                               outlier_p=outlier_p, device=gen_device, extra=extra)
     st = synth.state(cfg, N, K, spec, w_std=w_std, v_zero=v_zero, device=gen_device, extra=extra)
-    if spec.v_fmt in ("u8", "e4m3") and v_init == "quantized" and not v_zero:
+    # (a K that is not a multiple of the block keeps the stand-in codes: such a
+    # state is only used to check that the call is rejected)
+    if spec.v_fmt in ("u8", "e4m3") and v_init == "quantized" and not v_zero and K % spec.block == 0:
         v32 = synth.normal((N, K), 1e-6, "cpu", cfg, 0, synth.T_V, extra).abs().numpy()
         if spec.v_fmt == "u8":
             q, s = O.quantize_unsigned(v32, spec.block)
@@ -367,6 +376,7 @@ def _determined_codes(fmt: str, second: bool, xlo: np.ndarray, xhi: np.ndarray, 
 
 
 def assert_ok(rep: Report, label: str = ""):
+    print(f"  {label}: {rep.summary()}", flush=True)
     if not rep.ok():
         raise AssertionError(f"{label}: " + "\n".join(rep.failures[:10]))
 
