@@ -27,9 +27,11 @@ LIB_PATH = os.path.join(_HERE, "libforge.so")
 
 FORGE_OK = 0
 STATUS_NAMES = ["FORGE_OK", "FORGE_E_NULL", "FORGE_E_SHAPE", "FORGE_E_DTYPE", "FORGE_E_ALIGN",
-                "FORGE_E_STEP", "FORGE_E_HYPER", "FORGE_E_ALIAS", "FORGE_E_UNSUPPORTED", "FORGE_E_HIP"]
+                "FORGE_E_STEP", "FORGE_E_HYPER", "FORGE_E_ALIAS", "FORGE_E_UNSUPPORTED", "FORGE_E_HIP",
+                "FORGE_E_SCRATCH"]
 (FORGE_E_NULL, FORGE_E_SHAPE, FORGE_E_DTYPE, FORGE_E_ALIGN, FORGE_E_STEP, FORGE_E_HYPER,
- FORGE_E_ALIAS, FORGE_E_UNSUPPORTED, FORGE_E_HIP) = range(1, 10)
+ FORGE_E_ALIAS, FORGE_E_UNSUPPORTED, FORGE_E_HIP, FORGE_E_SCRATCH) = range(1, 11)
+FORGE_DGRAD_SCRATCH_BYTES = 32 << 20   # the static scratch of forge_dgrad_split_noalloc
 
 FORGE_F32, FORGE_BF16, FORGE_S8, FORGE_U8, FORGE_E4M3 = 0, 1, 2, 3, 4
 FORGE_ADAMW, FORGE_LION, FORGE_SGDM, FORGE_NADAM, FORGE_RADAM, FORGE_RMSPROP, FORGE_ADAGRAD, FORGE_SGD = range(8)
@@ -108,6 +110,8 @@ def _load() -> ctypes.CDLL:
     lib.forge_dgrad_split.argtypes = [P(forge_mat), P(forge_mat), P(forge_mat), ctypes.c_void_p, ctypes.c_int64,
                                       ctypes.c_void_p]
     lib.forge_dgrad_split.restype = st
+    lib.forge_dgrad_split_noalloc.argtypes = [P(forge_mat), P(forge_mat), P(forge_mat), ctypes.c_void_p]
+    lib.forge_dgrad_split_noalloc.restype = st
     lib.forge_backward_step.argtypes = [P(forge_mat), P(forge_mat), P(forge_mat), P(forge_state), P(forge_state),
                                         P(forge_hyper), ctypes.c_int64, ctypes.c_uint64, P(forge_mat),
                                         ctypes.c_void_p]
@@ -321,6 +325,18 @@ def forge_dgrad_split(dY, W, dX, workspace=None, stream=None, check: bool = True
     rc = lib.forge_dgrad_split(_ref(dY), _ref(W), _ref(dX), ptr, nbytes, _stream(stream))
     if check and rc != FORGE_OK:
         raise ForgeError(rc, "forge_dgrad_split")
+    return rc
+
+
+def forge_dgrad_split_noalloc(dY, W, dX, stream=None, check: bool = True) -> int:
+    """forge_dgrad_split with its partial sums in the library's static per-device
+    scratch array (no workspace, no allocation; overlapping calls on one GPU race)."""
+    dY = mat(dY) if not isinstance(dY, forge_mat) else dY
+    W = mat(W) if not isinstance(W, forge_mat) else W
+    dX = mat(dX) if not isinstance(dX, forge_mat) else dX
+    rc = lib.forge_dgrad_split_noalloc(_ref(dY), _ref(W), _ref(dX), _stream(stream))
+    if check and rc != FORGE_OK:
+        raise ForgeError(rc, "forge_dgrad_split_noalloc")
     return rc
 
 

@@ -10,6 +10,7 @@
 #include "forge_internal.h"
 
 static_assert(FORGE_GROUP_MAX == forge::GROUP_MAX, "group size of the ABI and the kernels");
+static_assert(FORGE_DGRAD_SCRATCH_BYTES == forge::DGRAD_SCRATCH_BYTES, "scratch size of the ABI and the kernels");
 
 namespace {
 
@@ -562,6 +563,17 @@ forge_status forge_dgrad_split(const forge_mat* dY, const forge_mat* W, forge_ma
   return hip_status(launch_dgrad(g, fast, (hipStream_t)stream));
 }
 
+forge_status forge_dgrad_split_noalloc(const forge_mat* dY, const forge_mat* W, forge_mat* dX, void* stream) {
+  DgArgs g;
+  bool fast = false;
+  const forge_status st = check_dgrad(dY, W, dX, g, fast);
+  if (st != FORGE_OK) return st;
+  const int64_t need = fast ? forge_dgrad_workspace_bytes(g.BT, g.N, g.K) : 0;
+  if (need > FORGE_DGRAD_SCRATCH_BYTES) return FORGE_E_SCRATCH;
+  if (need > 0) g.splits = dgrad_splits(g.BT, g.N, g.K);
+  return hip_status(launch_dgrad_scratch(g, fast, (hipStream_t)stream));
+}
+
 static forge_status backward_step(const forge_mat* X, const forge_mat* dY, forge_mat* W, forge_state* m,
                                   forge_state* v, const forge_hyper* h, int64_t step, uint64_t seed, forge_mat* dX,
                                   bool split, void* workspace, int64_t workspace_bytes, void* stream) {
@@ -671,6 +683,7 @@ const char* forge_status_str(forge_status s) {
     case FORGE_E_ALIAS: return "FORGE_E_ALIAS: an output overlaps another buffer";
     case FORGE_E_UNSUPPORTED: return "FORGE_E_UNSUPPORTED: combination not implemented";
     case FORGE_E_HIP: return "FORGE_E_HIP: HIP launch error";
+    case FORGE_E_SCRATCH: return "FORGE_E_SCRATCH: the call needs more than the static scratch array holds";
   }
   return "unknown forge_status";
 }

@@ -124,6 +124,11 @@ struct DgArgs {
 };
 // forge_k_dgrad.hip: fast = bf16 dY and W with 16-byte aligned rows, N and K multiples of 8.
 hipError_t launch_dgrad(const DgArgs& g, bool fast, hipStream_t stream);
+// The split path with the partials in the library's own per-device scratch
+// array (no caller workspace, no allocation); g.splits * BT * K * 4 must not
+// exceed DGRAD_SCRATCH_BYTES.
+constexpr int64_t DGRAD_SCRATCH_BYTES = 32ll << 20;
+hipError_t launch_dgrad_scratch(DgArgs g, bool fast, hipStream_t stream);
 
 // Reduction splits of the MFMA dX kernel for dY [BT, N], W [N, K]: 1 (no
 // split) when 128-token tiles already give every CU a workgroup, else up to

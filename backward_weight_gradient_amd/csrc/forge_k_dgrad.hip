@@ -28,6 +28,8 @@
 
 #include "forge_device.h"
 
+#include <mutex>
+
 namespace forge {
 
 namespace {
@@ -388,6 +390,64 @@ hipError_t launch_dgrad(const DgArgs& g, bool fast, hipStream_t st) {
     hipLaunchKernelGGL(k_dgrad_generic, dim3(tiles), dim3(NT), 0, st, g);
   }
   return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------
+// Allocation-free split dX (for callers that cannot allocate device memory):
+// the fp32 partials go to this file-scope device array instead of a caller
+// workspace.  Every GPU the library runs on holds its own copy from the
+// first use on that device until the process ends; its contents are left
+// from the last call, which is harmless here because every split writes its
+// whole [BT, K] slice before the reduction reads it.  Calls that overlap on
+// one GPU share the array and race.
+//
+// In host code `scratch` names a host-side stand-in, not device memory: the
+// device address is resolved once per device with hipGetSymbolAddress (with
+// that device current) and only that address is passed to the kernels.
+// ------------------------------------------------------------------------
+static __device__ __align__(256) float scratch[DGRAD_SCRATCH_BYTES / 4];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices];   // device address of `scratch` by device ordinal, once resolved
+
+// The device address of this device's `scratch`, `dev` being the device the
+// stream belongs to (the current device for the null stream).
+hipError_t scratch_address(hipStream_t st, void** out) {
+  int dev = 0;
+  hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    int cur = 0;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_dgrad_scratch(DgArgs g, bool fast, hipStream_t st) {
+  if (fast && g.splits > 1) {
+    if ((int64_t)g.splits * g.BT * g.K * 4 > (int64_t)DGRAD_SCRATCH_BYTES) return hipErrorInvalidValue;
+    void* p = nullptr;
+    const hipError_t e = scratch_address(st, &p);
+    if (e != hipSuccess) return e;
+    g.ws = static_cast<float*>(p);
+  }
+  return launch_dgrad(g, fast, st);
 }
 
 }  // namespace forge

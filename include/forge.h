@@ -31,8 +31,8 @@
  *   - Argument validation is synchronous and host-only.  On any error code
  *     other than FORGE_E_HIP nothing has been enqueued and nothing modified.
  *   - No exception crosses the ABI.  The library keeps no mutable global
- *     state; calls on distinct streams may run concurrently on disjoint
- *     buffers.
+ *     state apart from forge_dgrad_split_noalloc's per-device scratch array;
+ *     calls on distinct streams may run concurrently on disjoint buffers.
  *   - Precondition the library cannot check (paper, Appendix A, Remark 1):
  *     the caller has already computed the input gradient dX = dY W from the
  *     pre-update W; a weight whose gradient comes from several consumers in
@@ -62,7 +62,9 @@ typedef enum {
   FORGE_E_HYPER = 6,       /* a hyper-parameter is non-finite or out of range       */
   FORGE_E_ALIAS = 7,       /* an output buffer overlaps an input or another output  */
   FORGE_E_UNSUPPORTED = 8, /* a valid combination the library does not implement  */
-  FORGE_E_HIP = 9          /* the HIP runtime reported an error at launch           */
+  FORGE_E_HIP = 9,         /* the HIP runtime reported an error at launch           */
+  FORGE_E_SCRATCH = 10     /* forge_dgrad_split_noalloc: the call needs more than
+                              FORGE_DGRAD_SCRATCH_BYTES of scratch                   */
 } forge_status;
 
 typedef enum { FORGE_F32 = 0, FORGE_BF16 = 1, FORGE_S8 = 2, FORGE_U8 = 3, FORGE_E4M3 = 4 } forge_dtype;
@@ -275,6 +277,24 @@ int64_t forge_dgrad_workspace_bytes(int64_t BT, int64_t N, int64_t K);
  */
 forge_status forge_dgrad_split(const forge_mat* dY, const forge_mat* W, forge_mat* dX, void* workspace,
                                int64_t workspace_bytes, void* stream);
+
+/*
+ * forge_dgrad_split_noalloc -- forge_dgrad_split for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same kernels, splits and reduction
+ * order, so the same dX bit for bit, with the split partials in a
+ * file-scope device array of FORGE_DGRAD_SCRATCH_BYTES (32 MiB) that the
+ * library holds on each GPU it runs on until the process ends, instead of a
+ * caller workspace.  The call allocates nothing.  Every call on a GPU shares
+ * that GPU's array, so calls that may overlap on one GPU (several streams,
+ * several host threads) race and must be serialised by the caller.
+ * Shapes whose split needs more (forge_dgrad_workspace_bytes(BT, N, K) >
+ * FORGE_DGRAD_SCRATCH_BYTES) are rejected with FORGE_E_SCRATCH before
+ * anything is enqueued; every Llama-3.1-8B layer at BT <= 512 fits.
+ * Arguments and other errors as forge_dgrad.
+ */
+#define FORGE_DGRAD_SCRATCH_BYTES (32ll << 20)
+forge_status forge_dgrad_split_noalloc(const forge_mat* dY, const forge_mat* W, forge_mat* dX, void* stream);
 
 /*
  * forge_backward_step -- a linear layer's whole weight-side backward in the

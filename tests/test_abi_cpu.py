@@ -51,7 +51,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     assert "gfx950" in F.forge_version()
-    for code in range(10):
+    for code in range(11):
         assert F.forge_status_str(code).startswith(F.STATUS_NAMES[code])
 
 
@@ -543,3 +543,24 @@ def test_binding_state_checks_the_scale_tensor():
             F.state(codes, bad, block)
     with pytest.raises(ValueError):
         F.state(torch.zeros((4, 200), dtype=torch.int8), torch.zeros((4, 1)), 128)
+
+
+def test_dgrad_noalloc_validation():
+    """The allocation-free dX call validates like forge_dgrad and rejects, on
+    the host, a split that needs more than its static scratch array."""
+    nd = F.lib.forge_dgrad_split_noalloc
+    dY = F.mat_raw(addr(0), F.FORGE_BF16, 512, 4096)
+    W = F.mat_raw(addr(1), F.FORGE_BF16, 4096, 8064)
+    dX = F.mat_raw(addr(2), F.FORGE_BF16, 512, 8064)
+    assert F.forge_dgrad_workspace_bytes(512, 4096, 8064) > F.FORGE_DGRAD_SCRATCH_BYTES
+    assert nd(ctypes.byref(dY), ctypes.byref(W), ctypes.byref(dX), None) == F.FORGE_E_SCRATCH
+    # the Llama-3.1-8B shapes at BT 512 fit (32 MiB exactly for q / o / gate / up)
+    for N, K in ((4096, 4096), (14336, 4096), (1024, 4096), (4096, 14336)):
+        assert F.forge_dgrad_workspace_bytes(512, N, K) <= F.FORGE_DGRAD_SCRATCH_BYTES
+    assert F.forge_dgrad_workspace_bytes(512, 4096, 4096) == F.FORGE_DGRAD_SCRATCH_BYTES
+    # errors of forge_dgrad come first
+    bad = F.mat_raw(addr(2), F.FORGE_BF16, 511, 8064)
+    assert nd(ctypes.byref(dY), ctypes.byref(W), ctypes.byref(bad), None) == F.FORGE_E_SHAPE
+    assert nd(None, ctypes.byref(W), ctypes.byref(dX), None) == F.FORGE_E_NULL
+    alias = F.mat_raw(addr(1), F.FORGE_BF16, 512, 8064)
+    assert nd(ctypes.byref(dY), ctypes.byref(W), ctypes.byref(alias), None) == F.FORGE_E_ALIAS
