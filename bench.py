@@ -56,7 +56,6 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     p.add_argument("--no-unfused", action="store_true", help="skip the unfused comparison")
     p.add_argument("--no-ceilings", action="store_true", help="skip the measured HBM and MFMA ceilings")
-    p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle work in seconds")
     p.add_argument("--grouping", choices=["block", "subblock", "ready", "layer"], default="block",
                    help="block: one launch for the decoder layer's seven; subblock: one launch per sub-block, "
                         "[gate, up, down] and [q, k, v, o]; ready: as the gradients become available, [down] "
@@ -173,6 +172,20 @@ def mfma_sweep(F, synth, h, reps=3):
     return out
 
 
+def quantized_v(F, synth, st, cfg, N, K, fmt, extra, block=128):
+    """Replace the stand-in codes of a block-scaled second moment with the
+    int8 workload's init: |N(0, 1e-6^2)| quantised on the device by the
+    library's own block quantiser (forge_debug_quant, the epilogue's code)."""
+    import torch
+    v32 = synth.normal((N, K), 1e-6, "cuda", cfg, 0, synth.T_V, extra).abs()
+    codes = torch.empty((N, K), device="cuda", dtype=torch.uint8)
+    scales = torch.empty((N, K // block), device="cuda", dtype=torch.float32)
+    F.forge_debug_quant(v32, codes, scales, F.FORGE_U8 if fmt == "u8" else F.FORGE_E4M3, True, block)
+    st["v"] = codes if fmt == "u8" else codes.view(torch.float8_e4m3fn)
+    st["v_scale"] = scales
+    del v32
+
+
 def family_sweep(F, synth, reps=5):
     """Each of the eight optimizer families on gate_proj [14336, 4096] at
     BT = 512 (bf16 X / dY / W with SR, fp32 states where the family keeps
@@ -198,6 +211,8 @@ def family_sweep(F, synth, reps=5):
             spec = synth.LayerSpec(in_dtype="bf16", w_fmt="bf16", m_fmt="e4m3", v_fmt="e4m3", block=128)
         st = synth.state(1, N, K, spec, device="cuda", extra=40)
         blocked = state in ("int8", "e4m3")
+        if blocked:
+            quantized_v(F, synth, st, 1, N, K, spec.v_fmt, 40)
         m = (F.state(st["m"], st["m_scale"], 128) if blocked else F.state(st["m"])) if st["m"] is not None else None
         v = (F.state(st["v"], st["v_scale"], 128) if blocked else F.state(st["v"])) if st["v"] is not None else None
         args = (F.mat(X), F.mat(dY), F.mat(st["W"]), m, v)
@@ -218,7 +233,7 @@ def family_sweep(F, synth, reps=5):
         else:          # each fp32 state read and written: 8 B; each bf16 state: 4 B
             per = 8 if state == "f32" else 4
             bpp = 4 + per * (opt in F.KEEPS_M) + per * (opt in F.KEEPS_V)
-        nbytes = bpp * N * K + 2 * BT * (N + K) * 2
+        nbytes = bpp * N * K + 2 * BT * (N + K)          # X and dY (bf16) read once
         name = opt if state == "f32" else f"{opt}_{state}"
         out[name] = {"us": round(1e3 * ms, 1), "state_bytes_per_param": bpp,
                      "hbm_gbs_alg": round(nbytes / (ms * 1e-3) / 1e9, 1),
@@ -254,12 +269,14 @@ def state_format_sweep(F, synth, h, reps=10):
                                       outlier_p=0.01 if fmt == "int8" else 0.0)
             st = synth.state(cfg_of[fmt], N, K, spec, device="cuda", extra=i)
             blocked = fmt != "bf16"
+            if blocked:
+                quantized_v(F, synth, st, cfg_of[fmt], N, K, spec.v_fmt, i)
             m = F.state(st["m"], st["m_scale"], 128) if blocked else F.state(st["m"])
             v = F.state(st["v"], st["v_scale"], 128) if blocked else F.state(st["v"])
             keep.append((X, dY, st))
             layers_arg.append((F.mat(X), F.mat(dY), F.mat(st["W"]), m, v, SEED))
             P_total += N * K
-            nbytes += bpp * N * K + 2 * BT * (N + K) * 2
+            nbytes += bpp * N * K + 2 * BT * (N + K)     # X and dY (bf16) read once
         launch = lambda: F.forge_wgrad_step_group(layers_arg, h, STEP_T, stream=stream.cuda_stream)
         launch()
         torch.cuda.synchronize()
@@ -321,7 +338,7 @@ def accumulation_sweep(F, synth, h, micro=4, reps=5):
         for i in range(micro):
             per[i].append(ev[i][0].elapsed_time(ev[i][1]))
     med = [sorted(t)[len(t) // 2] for t in per]
-    act = 2 * bt * (N + K) * 2
+    act = 2 * bt * (N + K)                                  # X and dY (bf16) read once
     nbytes = [(4 if i == 0 else 8) * N * K + act for i in range(micro - 1)] + [24 * N * K + act]
     out = {"micro_batches": micro, "tokens_per_micro_batch": bt,
            "accumulate_first_us": round(1e3 * med[0], 1),
@@ -334,20 +351,24 @@ def accumulation_sweep(F, synth, h, micro=4, reps=5):
     return out
 
 
-def dgrad_sweep(F, L, layers, reps=5):
+def dgrad_sweep(F, L, layers, reps=6, sets=3):
     """dX = dY W (bf16, fp32 accumulation, bf16 dX) for each layer of the step
-    at BT = 512, from the step's own dY and W (median of `reps` launches):
-    forge_dgrad_split with its workspace (the reduction split across
-    workgroups where that applies) and forge_dgrad (never split)."""
+    at BT = 512 (median of `reps` launches): forge_dgrad_split with its
+    workspace (the reduction split across workgroups where that applies) and
+    forge_dgrad (never split).  The launches rotate over `sets` copies of dY
+    and W (the step's own, then clones), so consecutive launches do not find
+    their operands in the 256 MiB MALL (q / o W is 32 MiB, k / v W 8 MiB)."""
     import torch
     stream = torch.cuda.current_stream()
     out = {}
 
-    def timed(fn):
-        fn()
+    def timed(fns):
+        for fn in fns:
+            fn()
         torch.cuda.synchronize()
         times = []
-        for _ in range(reps):
+        for r in range(reps):
+            fn = fns[r % len(fns)]
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             fn()
@@ -358,17 +379,21 @@ def dgrad_sweep(F, L, layers, reps=5):
 
     for name, (N, K) in layers.items():
         d = L[name]
+        ops = [(d["dY"], d["W"])] + [(d["dY"].clone(), d["W"].clone()) for _ in range(sets - 1)]
+        mats = [(F.mat(a), F.mat(b)) for a, b in ops]
         dX = torch.empty((BT, K), device="cuda", dtype=torch.bfloat16)
         dXm = F.mat(dX)
         need = F.forge_dgrad_workspace_bytes(BT, N, K)
         ws = torch.empty((need // 4,), device="cuda") if need else None
-        ms = timed(lambda: F.forge_dgrad_split(d["dYm"], d["Wm"], dXm, ws, stream=stream.cuda_stream))
-        ms_plain = timed(lambda: F.forge_dgrad(d["dYm"], d["Wm"], dXm, stream=stream.cuda_stream))
+        sp = stream.cuda_stream
+        ms = timed([lambda a=a, b=b: F.forge_dgrad_split(a, b, dXm, ws, stream=sp) for a, b in mats])
+        ms_plain = timed([lambda a=a, b=b: F.forge_dgrad(a, b, dXm, stream=sp) for a, b in mats])
         tflops = 2.0 * BT * N * K / (ms * 1e-3) / 1e12
         out[name] = {"us": round(1e3 * ms, 1), "tflops": round(tflops, 1),
                      "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4), "workspace_bytes": need,
-                     "us_unsplit": round(1e3 * ms_plain, 1)}
-        del dX, ws
+                     "us_unsplit": round(1e3 * ms_plain, 1), "buffer_sets": sets}
+        del dX, ws, ops, mats
+    out["seven_layers_us"] = round(sum(v["us"] for v in out.values()), 1)
     return out
 
 
@@ -421,39 +446,151 @@ def cpu_model():
     return None
 
 
-def cpu_baseline(layers, seconds):
-    """The oracle on whole layers (k_proj first, then the others in turn)
-    until about `seconds` of CPU time are spent; params/s over them."""
+def host_cpu():
+    """The host's processor: model name, logical CPUs, and the CPUs this process may use."""
+    info = {"model": cpu_model(), "logical_cpus": os.cpu_count()}
+    try:
+        info["usable_cpus"] = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        info["usable_cpus"] = os.cpu_count()
+    return info
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def _oracle_layer(O, synth, cfg, N, K, bt, hyp, spec, outlier_p, threads):
+    """One whole-layer oracle step (G by fp64 matmul, then the step and its
+    stores).  Returns (matmul seconds on 1 BLAS thread, matmul seconds on
+    `threads` threads, step seconds); the step runs once."""
+    from threadpoolctl import threadpool_limits
+    X, dY = synth.activations(cfg, bt, N, K, STEP_T, outlier_p=outlier_p, extra=90)
+    st = synth.state(cfg, N, K, spec, extra=90)
+    Xh, dYh = synth.host(X), synth.host(dY)
+    del X, dY
+
+    def stored(fmt, t, sc):
+        if t is None:
+            return None
+        return O.Stored(fmt, synth.host(t), None if sc is None else sc.numpy(), spec.block)
+
+    W = stored(spec.w_fmt, st["W"], None)
+    m = stored(spec.m_fmt, st["m"], st["m_scale"])
+    v = stored(spec.v_fmt, st["v"], st["v_scale"])
+    mm = []
+    for n in ((1, threads) if threads > 1 else (1,)):
+        with threadpool_limits(n):
+            t0 = time.perf_counter()
+            G = O.weight_grad(Xh, dYh)
+            mm.append(time.perf_counter() - t0)
+    t1 = time.perf_counter()
+    O.apply_step(G, W, m, v, hyp, STEP_T, SEED)
+    return mm[0], mm[-1], time.perf_counter() - t1
+
+
+def oracle_cpu_times(layers):
+    """The oracle (oracle/) on the host cores, per layer, for the BT = 512
+    workloads: fp32 layer (config 0 shape, 256 x 256, BT 64), bf16 W with
+    fp32 m / v (config 1), bf16 W / m / v (config 2) and int8 m / v with 1%
+    x50 outliers (config 3), every layer in full.  The fp64 matmul is timed
+    on 1 thread and on all BLAS threads; the element-wise step is plain
+    single-threaded NumPy either way, so the all-core time of a layer is the
+    all-thread matmul plus the step.  Config 4 (BT 2048 / 8192): down_proj
+    in full (all threads) and lm_head on a seeded sample -- 4 corner and 12
+    random 128 x 128 tiles plus 4,096 random elements -- timed per checked
+    element with an extrapolated full-layer time, labelled as such."""
     import numpy as np
     import oracle as O
     import synth
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = 1
-    order = ["k_proj", "v_proj", "q_proj", "o_proj", "gate_proj", "up_proj", "down_proj"]
-    done, params, t_total = [], 0, 0.0
-    spec = synth.LayerSpec(in_dtype="bf16", w_fmt="bf16", m_fmt="f32", v_fmt="f32")
+    threads = _blas_threads()
+    specs = {1: synth.LayerSpec(in_dtype="bf16", w_fmt="bf16", m_fmt="f32", v_fmt="f32"),
+             2: synth.LayerSpec(in_dtype="bf16", w_fmt="bf16", m_fmt="bf16", v_fmt="bf16"),
+             3: synth.LayerSpec(in_dtype="bf16", w_fmt="bf16", m_fmt="s8", v_fmt="u8", block=128)}
     hyp = O.Hyper(opt="adamw", round="sr")
-    for name in order:
-        N, K = layers[name]
-        X, dY = synth.activations(1, BT, N, K, STEP_T, extra=order.index(name))
-        st = synth.state(1, N, K, spec, extra=order.index(name))
-        Xh, dYh = synth.host(X), synth.host(dY)
-        W = O.Stored("bf16", synth.host(st["W"]))
-        m = O.Stored("f32", synth.host(st["m"]))
-        v = O.Stored("f32", synth.host(st["v"]))
+    out = {"blas_threads": threads, "host": host_cpu()}
+    t_start = time.perf_counter()
+    # config 0: fp32 256 x 256, BT 64, one step
+    spec0 = synth.LayerSpec(in_dtype="f32", w_fmt="f32", m_fmt="f32", v_fmt="f32")
+    mm1, _, st1 = _oracle_layer(O, synth, 0, 256, 256, 64, hyp, spec0, 0.0, 1)
+    out["cfg0_fp32_256x256_bt64"] = {"matmul_1t_s": round(mm1, 5), "step_s": round(st1, 5)}
+    for cfg, spec in specs.items():
+        rows, tot1, totn, params = {}, 0.0, 0.0, 0
+        for name, (N, K) in layers.items():
+            mm1, mmn, step = _oracle_layer(O, synth, cfg, N, K, BT, hyp, spec, 0.01 if cfg == 3 else 0.0, threads)
+            rows[name] = {"matmul_1t_s": round(mm1, 3), f"matmul_{threads}t_s": round(mmn, 3),
+                          "step_s": round(step, 3), "single_thread_s": round(mm1 + step, 3),
+                          "all_core_s": round(mmn + step, 3)}
+            tot1 += mm1 + step
+            totn += mmn + step
+            params += N * K
+        out[f"cfg{cfg}_bt512"] = {"layers": rows, "single_thread_s": round(tot1, 2), "all_core_s": round(totn, 2),
+                                  "params": params, "params_per_s_all_core": round(params / totn, 1)}
+    # config 4: down_proj in full (all threads)
+    spec4 = synth.LayerSpec(in_dtype="bf16", w_fmt="bf16", m_fmt="f32", v_fmt="f32")
+    N, K = layers["down_proj"]
+    for bt in (2048, 8192):
+        _, mm, step = _oracle_layer(O, synth, 4, N, K, bt, hyp, spec4, 0.0, threads)
+        out[f"cfg4_down_proj_bt{bt}"] = {f"matmul_{threads}t_s": round(mm, 3), "step_s": round(step, 3),
+                                         "all_core_s": round(mm + step, 3)}
+    # config 4: lm_head at BT 8192 on a seeded sample of tiles and elements
+    NL, KL = synth.LM_HEAD
+    bt = 8192
+    rng = np.random.default_rng(4)
+    ti = [(0, 0), (0, KL // 128 - 1), (NL // 128 - 1, 0), (NL // 128 - 1, KL // 128 - 1)]
+    ti += [(int(a), int(b)) for a, b in zip(rng.integers(0, NL // 128, 12), rng.integers(0, KL // 128, 12))]
+    X = synth.host(synth.normal((bt, KL), 1.0, "cpu", 4, STEP_T, synth.T_X, 91).to(torch_bf16()))
+    t_tiles = 0.0
+    for (a, b) in ti:
+        dYs = synth.host(synth.normal((bt, 128), 1e-3, "cpu", 4, STEP_T, synth.T_DY, 1000 + a).to(torch_bf16()))
+        Wt = O.Stored("bf16", synth.host(synth.normal((128, 128), 0.02, "cpu", 4, 0, synth.T_W, a).to(torch_bf16())))
+        z = O.Stored("f32", np.zeros((128, 128), np.float32))
         t0 = time.perf_counter()
-        O.wgrad_step(Xh, dYh, W, m, v, hyp, STEP_T, SEED)
-        t_total += time.perf_counter() - t0
-        params += N * K
-        done.append(name)
-        if t_total >= seconds:
-            break
-    return {"value": params / t_total, "unit": "params/s", "cores": cores, "kind": "oracle",
-            "sample": f"whole layers {','.join(done)} at BT={BT} ({params} params, {t_total:.1f} s); "
-                      f"fp64 BLAS matmul on {cores} threads, element-wise step single-threaded NumPy"}
+        G = O.weight_grad(X[:, b * 128:(b + 1) * 128], dYs)
+        O.apply_step(G, Wt, z, z.copy(), hyp, STEP_T, SEED)
+        t_tiles += time.perf_counter() - t0
+    rows = rng.integers(0, NL, 4096)
+    cols = rng.integers(0, KL, 4096)
+    dYe = synth.host(synth.normal((bt, 4096), 1e-3, "cpu", 4, STEP_T, synth.T_DY, 2000).to(torch_bf16()))
+    t0 = time.perf_counter()
+    for j in range(4096):
+        O.weight_grad(X[:, cols[j]:cols[j] + 1], dYe[:, j:j + 1])
+    t_el = time.perf_counter() - t0
+    n_tiles = len(ti) * 128 * 128
+    out["cfg4_lm_head_bt8192_sample"] = {
+        "sample": "4 corner + 12 random 128x128 tiles (G by fp64 matmul over 8192 tokens, then the AdamW step) "
+                  "and 4096 random single elements (G by one fp64 dot product each)",
+        "tile_elements": n_tiles, "tile_seconds": round(t_tiles, 3),
+        "tile_us_per_element": round(1e6 * t_tiles / n_tiles, 4),
+        "single_elements": 4096, "single_seconds": round(t_el, 3),
+        "single_us_per_element": round(1e6 * t_el / 4096, 3),
+        "extrapolated_full_layer_s_from_tiles": round(t_tiles / n_tiles * NL * KL, 1),
+        "extrapolated": True}
+    out["total_s"] = round(time.perf_counter() - t_start, 1)
+    return out
+
+
+def torch_bf16():
+    import torch
+    return torch.bfloat16
+
+
+def cpu_baseline_from(detail):
+    """cpu_baseline: the oracle's params/s on the BT = 512 step's workload
+    (config 1, all seven layers in full), all-core wall time (BLAS matmul on
+    every thread, the element-wise step single-threaded)."""
+    c1 = detail["cfg1_bt512"]
+    h = detail["host"]
+    return {"value": c1["params_per_s_all_core"], "unit": "params/s", "cores": detail["blas_threads"],
+            "kind": "oracle",
+            "sample": f"the seven Llama-3.1-8B layers at BT={BT} in full ({c1['params']} params, "
+                      f"{c1['all_core_s']} s all-core, {c1['single_thread_s']} s single-thread); fp64 BLAS matmul "
+                      f"on {detail['blas_threads']} threads, element-wise step single-threaded NumPy; host "
+                      f"{h['model']}, {h['logical_cpus']} logical CPUs ({h['usable_cpus']} usable)"}
 
 
 def main():
@@ -616,8 +753,10 @@ def main():
             v["mfma_frac_of_measured"] = round(v["tflops"] / c["mfma_bf16_tflops"], 4)
 
     if not args.no_cpu_baseline:
-        extras["cpu_model"] = cpu_model()
-        cpu = cpu_baseline(layers, args.cpu_seconds)
+        detail = oracle_cpu_times(layers)
+        extras["oracle_cpu_times"] = detail
+        extras["host_cpu"] = detail["host"]
+        cpu = cpu_baseline_from(detail)
 
     out = {
         "metric": "fused wgrad+AdamW params/s & HBM GB/s (% roofline), Llama-8B shapes, BT=512",
