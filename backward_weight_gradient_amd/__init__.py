@@ -110,6 +110,15 @@ def _load() -> ctypes.CDLL:
     lib.forge_dgrad_split.argtypes = [P(forge_mat), P(forge_mat), P(forge_mat), ctypes.c_void_p, ctypes.c_int64,
                                       ctypes.c_void_p]
     lib.forge_dgrad_split.restype = st
+    lib.forge_wgrad_step_fp8w.argtypes = [P(forge_mat), P(forge_mat), P(forge_state), P(forge_state),
+                                          P(forge_state), P(forge_hyper), ctypes.c_int64, ctypes.c_uint64,
+                                          ctypes.c_void_p]
+    lib.forge_wgrad_step_fp8w.restype = st
+    lib.forge_wgrad_check_fp8w.argtypes = [P(forge_mat), P(forge_mat), P(forge_state), P(forge_state),
+                                           P(forge_state), P(forge_hyper), ctypes.c_int64]
+    lib.forge_wgrad_check_fp8w.restype = st
+    lib.forge_dgrad_fp8w.argtypes = [P(forge_mat), P(forge_state), P(forge_mat), ctypes.c_void_p]
+    lib.forge_dgrad_fp8w.restype = st
     lib.forge_dgrad_split_noalloc.argtypes = [P(forge_mat), P(forge_mat), P(forge_mat), ctypes.c_void_p]
     lib.forge_dgrad_split_noalloc.restype = st
     lib.forge_backward_step.argtypes = [P(forge_mat), P(forge_mat), P(forge_mat), P(forge_state), P(forge_state),
@@ -325,6 +334,33 @@ def forge_dgrad_split(dY, W, dX, workspace=None, stream=None, check: bool = True
     rc = lib.forge_dgrad_split(_ref(dY), _ref(W), _ref(dX), ptr, nbytes, _stream(stream))
     if check and rc != FORGE_OK:
         raise ForgeError(rc, "forge_dgrad_split")
+    return rc
+
+
+def forge_wgrad_step_fp8w(X, dY, W: forge_state, m, v, h: forge_hyper, step: int, seed: int, stream=None,
+                          check: bool = True) -> int:
+    """forge_wgrad_step with an E4M3 weight (W: forge_state of E4M3 codes and
+    block scales, updated in place)."""
+    X = mat(X) if not isinstance(X, forge_mat) else X
+    dY = mat(dY) if not isinstance(dY, forge_mat) else dY
+    rc = lib.forge_wgrad_step_fp8w(_ref(X), _ref(dY), _ref(W), _ref(m), _ref(v), _ref(h), step, seed,
+                                   _stream(stream))
+    if check and rc != FORGE_OK:
+        raise ForgeError(rc, "forge_wgrad_step_fp8w")
+    return rc
+
+
+def forge_wgrad_check_fp8w(X: forge_mat, dY: forge_mat, W: forge_state, m, v, h: forge_hyper, step: int) -> int:
+    return lib.forge_wgrad_check_fp8w(_ref(X), _ref(dY), _ref(W), _ref(m), _ref(v), _ref(h), step)
+
+
+def forge_dgrad_fp8w(dY, W: forge_state, dX, stream=None, check: bool = True) -> int:
+    """dX = dY W from an E4M3 weight with block scales (decoded exactly)."""
+    dY = mat(dY) if not isinstance(dY, forge_mat) else dY
+    dX = mat(dX) if not isinstance(dX, forge_mat) else dX
+    rc = lib.forge_dgrad_fp8w(_ref(dY), _ref(W), _ref(dX), _stream(stream))
+    if check and rc != FORGE_OK:
+        raise ForgeError(rc, "forge_dgrad_fp8w")
     return rc
 
 

@@ -145,8 +145,11 @@ void layer_ranges(const forge_mat* X, const forge_mat* dY, const forge_mat* W, c
   ins[1] = mat_range(*dY);
 }
 
+// wq: the weight as an E4M3 state (codes + block scales; W == &wq->q), or
+// NULL for a bf16 / fp32 weight.
 forge_status validate(const forge_mat* X, const forge_mat* dY, const forge_mat* W, const forge_state* m,
-                      const forge_state* v, const forge_hyper* h, int64_t step, Plan& pl) {
+                      const forge_state* v, const forge_hyper* h, int64_t step, Plan& pl,
+                      const forge_state* wq = nullptr) {
   if (!X || !dY || !W || !h) return FORGE_E_NULL;
   // optimizer and which states it keeps
   const int o = h->opt;
@@ -179,7 +182,18 @@ forge_status validate(const forge_mat* X, const forge_mat* dY, const forge_mat* 
   if ((st = check_mat(*W, pl.N, pl.K)) != FORGE_OK) return st;
   if (X->dtype != dY->dtype) return FORGE_E_DTYPE;
   if (X->dtype != FORGE_F32 && X->dtype != FORGE_BF16) return FORGE_E_DTYPE;
-  if (W->dtype != FORGE_F32 && W->dtype != FORGE_BF16) return FORGE_E_DTYPE;
+  if (wq) {
+    if (W->dtype != FORGE_E4M3) return FORGE_E_DTYPE;
+    if (!(wq->block == 32 || wq->block == 64 || wq->block == 128)) return FORGE_E_SHAPE;
+    if (pl.K % wq->block != 0) return FORGE_E_SHAPE;
+    if (pl.N > 0 && pl.K > 0) {
+      if (wq->scale == nullptr) return FORGE_E_NULL;
+      if (!aligned(wq->scale, 4)) return FORGE_E_ALIGN;
+    }
+    pl.block = wq->block;
+  } else if (W->dtype != FORGE_F32 && W->dtype != FORGE_BF16) {
+    return FORGE_E_DTYPE;
+  }
   if (m && (st = check_state(*m, pl.N, pl.K, true, pl)) != FORGE_OK) return st;
   if (v && (st = check_state(*v, pl.N, pl.K, false, pl)) != FORGE_OK) return st;
   // size limits: 32-bit flat SR index and 32-bit tile / token counters
@@ -195,6 +209,13 @@ forge_status validate(const forge_mat* X, const forge_mat* dY, const forge_mat* 
       if (overlap(outs[i], ins[j])) return FORGE_E_ALIAS;
     for (int j = i + 1; j < 5; ++j)
       if (overlap(outs[i], outs[j])) return FORGE_E_ALIAS;
+  }
+  if (wq && wq->scale) {   // the weight's block scales are written too
+    const Range rs = raw_range(wq->scale, (uint64_t)pl.N * (uint64_t)(pl.K / wq->block) * 4);
+    for (const Range& r : outs)
+      if (overlap(rs, r)) return FORGE_E_ALIAS;
+    for (const Range& r : ins)
+      if (overlap(rs, r)) return FORGE_E_ALIAS;
   }
   pl.in_fmt = X->dtype;
   pl.w_fmt = W->dtype;
@@ -239,7 +260,9 @@ bool vec_ok(const void* p, int64_t ld, int elems, int es) {
 }
 
 // dX = dY W: shapes, dtypes, limits, aliasing; fills the launch arguments.
-forge_status check_dgrad(const forge_mat* dY, const forge_mat* W, const forge_mat* dX, DgArgs& g, bool& fast) {
+// wq: the weight as an E4M3 state (W == &wq->q), or NULL.
+forge_status check_dgrad(const forge_mat* dY, const forge_mat* W, const forge_mat* dX, DgArgs& g, bool& fast,
+                         const forge_state* wq = nullptr) {
   if (!dY || !W || !dX) return FORGE_E_NULL;
   const int64_t BT = dY->rows, N = dY->cols, K = W->cols;
   if (BT < 0 || N < 0 || K < 0) return FORGE_E_SHAPE;
@@ -247,12 +270,26 @@ forge_status check_dgrad(const forge_mat* dY, const forge_mat* W, const forge_ma
   if ((st = check_mat(*dY, BT, N)) != FORGE_OK) return st;
   if ((st = check_mat(*W, N, K)) != FORGE_OK) return st;
   if ((st = check_mat(*dX, BT, K)) != FORGE_OK) return st;
-  for (const forge_mat* t : {dY, W, dX})
-    if (t->dtype != FORGE_F32 && t->dtype != FORGE_BF16) return FORGE_E_DTYPE;
+  for (const forge_mat* t : {dY, W, dX}) {
+    if (t == W && wq) {
+      if (t->dtype != FORGE_E4M3) return FORGE_E_DTYPE;
+    } else if (t->dtype != FORGE_F32 && t->dtype != FORGE_BF16) {
+      return FORGE_E_DTYPE;
+    }
+  }
   if (BT >= (1ll << 31) || N >= (1ll << 31) || K >= (1ll << 31)) return FORGE_E_SHAPE;
   if (((BT + 127) / 128) * ((K + 127) / 128) >= (1ll << 31)) return FORGE_E_SHAPE;
+  Range rws;
+  if (wq) {
+    if (!(wq->block == 32 || wq->block == 64 || wq->block == 128) || K % wq->block != 0) return FORGE_E_SHAPE;
+    if (N > 0 && K > 0) {
+      if (wq->scale == nullptr) return FORGE_E_NULL;
+      if (!aligned(wq->scale, 4)) return FORGE_E_ALIGN;
+    }
+    rws = raw_range(wq->scale, (uint64_t)N * (uint64_t)(K / wq->block) * 4);
+  }
   const Range out = mat_range(*dX);
-  if (overlap(out, mat_range(*dY)) || overlap(out, mat_range(*W))) return FORGE_E_ALIAS;
+  if (overlap(out, mat_range(*dY)) || overlap(out, mat_range(*W)) || overlap(out, rws)) return FORGE_E_ALIAS;
   std::memset(&g, 0, sizeof(g));
   g.dY = dY->data; g.lddy = dY->ld;
   g.W = W->data; g.ldw = W->ld;
@@ -264,6 +301,8 @@ forge_status check_dgrad(const forge_mat* dY, const forge_mat* W, const forge_ma
   g.vec_out = vec_ok(dX->data, dX->ld, 4, elem_size(dX->dtype)) ? 1 : 0;
   g.splits = 1;
   g.ws = nullptr;
+  g.wsc = wq ? wq->scale : nullptr;
+  g.wblock = wq ? wq->block : 0;
   fast = dY->dtype == FORGE_BF16 && W->dtype == FORGE_BF16 && N % 8 == 0 && K % 8 == 0 &&
          vec_ok(dY->data, dY->ld, 8, 2) && vec_ok(W->data, W->ld, 8, 2) &&
          (uint64_t)BT * (uint64_t)dY->ld * 2 < (1ull << 31) && (uint64_t)N * (uint64_t)W->ld * 2 < (1ull << 31);
@@ -385,6 +424,33 @@ forge_status forge_wgrad_step(const forge_mat* X, const forge_mat* dY, forge_mat
   if (st != FORGE_OK || pl.empty) return st;
   const KArgs a = make_args(X, dY, W, m, v, h, step, seed, pl);
   return hip_status(launch_fused(a, pl.in_fmt, pl.w_fmt, h->opt, pl.m_fmt, pl.v_fmt, (hipStream_t)stream));
+}
+
+forge_status forge_wgrad_step_fp8w(const forge_mat* X, const forge_mat* dY, forge_state* W, forge_state* m,
+                                   forge_state* v, const forge_hyper* h, int64_t step, uint64_t seed, void* stream) {
+  if (!W) return FORGE_E_NULL;
+  Plan pl;
+  forge_status st = validate(X, dY, &W->q, m, v, h, step, pl, W);
+  if (st != FORGE_OK || pl.empty) return st;
+  KArgs a = make_args(X, dY, &W->q, m, v, h, step, seed, pl);
+  a.wsc = W->scale;
+  return hip_status(launch_fused_fp8w(a, h->opt, pl.m_fmt, pl.v_fmt, (hipStream_t)stream));
+}
+
+forge_status forge_wgrad_check_fp8w(const forge_mat* X, const forge_mat* dY, const forge_state* W,
+                                    const forge_state* m, const forge_state* v, const forge_hyper* h, int64_t step) {
+  if (!W) return FORGE_E_NULL;
+  Plan pl;
+  return validate(X, dY, &W->q, m, v, h, step, pl, W);
+}
+
+forge_status forge_dgrad_fp8w(const forge_mat* dY, const forge_state* W, forge_mat* dX, void* stream) {
+  if (!W) return FORGE_E_NULL;
+  DgArgs g;
+  bool fast = false;
+  const forge_status st = check_dgrad(dY, &W->q, dX, g, fast, W);
+  if (st != FORGE_OK) return st;
+  return hip_status(launch_dgrad(g, false, (hipStream_t)stream));
 }
 
 forge_status forge_wgrad_step_group(const forge_layer* layers, int32_t n, const forge_hyper* h, int64_t step,

@@ -802,6 +802,25 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float y0, float y1, float y2, flo
   return (uint32_t)w;
 }
 
+// Stochastic rounding of y onto the E4M3 grid (the FP8 weight store): |y|
+// goes to one of its two neighbouring grid values, away from zero with
+// probability equal to its fractional position between them (quantised to
+// 2^-16), saturating at 448, keeping the sign.  Normal range (|y| >= 2^-6,
+// 3 fraction bits): r * 2^4 is added to the 20 fp32 fraction bits E4M3 drops
+// and they are cleared.  Subnormal range (spacing 2^-9): z = floor(|y| 2^25)
+// (exact) and the value is ((z + r) >> 16) 2^-9.  The result lies on the
+// grid, so e4m3_pack4 encodes it exactly.
+__device__ __forceinline__ float e4m3_sr_value(float y, uint32_t r16) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t au = u & 0x7FFFFFFFu;
+  const float ay = __uint_as_float(au);
+  const float normal = fminf(__uint_as_float((au + (r16 << 4)) & 0xFFF00000u), 448.f);
+  const uint32_t z = (uint32_t)(fminf(ay, 0x1p-6f) * 0x1p25f);          // < 2^19 where used
+  const float sub = (float)((z + r16) >> 16) * 0x1p-9f;
+  const float mag = ay >= 0x1p-6f ? normal : sub;
+  return __uint_as_float(__float_as_uint(mag) | (u & 0x80000000u));
+}
+
 __device__ __forceinline__ void e4m3_unpack4(uint32_t w, float* x) {
   const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);        // bytes 0, 1
   const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);         // bytes 2, 3
@@ -973,9 +992,13 @@ __device__ __forceinline__ void st4(void* row, const Seg& g, bool vec, const flo
 // taken 2^64 times larger and smaller (exact scalings), which gives the
 // product x * (QMAX / a) as if the exponent range were unbounded -- the same
 // bits as the plain product wherever that one is finite.
-template <int FMT, bool POSITIVE>
+// SRW (the E4M3 weight store): when sr != 0 the codes are drawn by
+// e4m3_sr_value with the SR bits of flat indices idx_mul[g] / GOLDEN + i
+// (key `key`), else they are the nearest ones.
+template <int FMT, bool POSITIVE, bool SRW = false>
 __device__ __forceinline__ void quantize_chunk(const float (&x_in)[8], int block, const Seg (&sg)[2],
-                                               void* row_codes, bool vec, float* row_scales) {
+                                               void* row_codes, bool vec, float* row_scales, int sr = 0,
+                                               uint32_t key = 0, const uint32_t* idx_mul = nullptr) {
   float x[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) x[i] = x_in[i];
@@ -1034,6 +1057,13 @@ __device__ __forceinline__ void quantize_chunk(const float (&x_in)[8], int block
         y[i] = xv * inv[g];
         if (POSITIVE) y[i] = xv > 0.f ? fmaxf(y[i], 0x1p-9f) : y[i];
       }
+      if constexpr (SRW) {
+        if (sr) {   // wave-uniform
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            y[i] = e4m3_sr_value(y[i], fmix32(key ^ (idx_mul[g] + (uint32_t)i * GOLDEN)) >> 16);
+        }
+      }
       word = e4m3_pack4(y[0], y[1], y[2], y[3]);
     } else {
 #pragma unroll
@@ -1076,6 +1106,7 @@ struct TileRows {
   const char* g;
   float* ms;               // block scales of row p0
   float* vs;
+  float* ws;               // the weight's block scales (E4M3 weight)
   int64_t dw, dm, dv, dg;  // bytes from one pass's row to the next
   int64_t ds;              // scale elements from one pass's row to the next
   uint32_t idx;            // p0 K GOLDEN (mod 2^32)
@@ -1111,6 +1142,7 @@ struct Step {
         continue;
       }
       ld4<WF, FAST>(r.w[g], rw, sg[g], vec);
+      if constexpr (fmt_blocked(WF)) r.w[g].s = (tr.ws + s * tr.ds)[sg[g].q >> bsh];
       if constexpr (HAS_M) {
         const char* rm = tr.m + s * tr.dm;
         ld4<MF, FAST>(r.m[g], rm, sg[g], vec);
@@ -1194,9 +1226,13 @@ struct Step {
     for (int s = 0; s < 2; ++s) {
       if (!sg[s].ok) continue;
       const uint32_t idx_mul = rowbase + tr.qg[s];
-      st4<WF, FAST>(rw, sg[s], vec, w + 4 * s, a.c.sr, a.c.keyW, idx_mul);
+      if constexpr (!fmt_blocked(WF)) st4<WF, FAST>(rw, sg[s], vec, w + 4 * s, a.c.sr, a.c.keyW, idx_mul);
       if constexpr (HAS_M && !fmt_blocked(MF)) st4<MF, FAST>(rm, sg[s], vec, m + 4 * s, a.c.sr, a.c.keyM, idx_mul);
       if constexpr (HAS_V && !fmt_blocked(VF)) st4<VF, FAST>(rv, sg[s], vec, v + 4 * s, a.c.sr, a.c.keyV, idx_mul);
+    }
+    if constexpr (fmt_blocked(WF)) {
+      const uint32_t im[2] = {rowbase + tr.qg[0], rowbase + tr.qg[1]};
+      quantize_chunk<WF, false, true>(w, a.block, sg, rw, vec, tr.ws + ps * tr.ds, a.c.sr, a.c.keyW, im);
     }
     if constexpr (HAS_M && fmt_blocked(MF)) quantize_chunk<MF, false>(m, a.block, sg, rm, vec, tr.ms + ps * tr.ds);
     if constexpr (HAS_V && fmt_blocked(VF)) quantize_chunk<VF, true>(v, a.block, sg, rv, vec, tr.vs + ps * tr.ds);
@@ -1244,10 +1280,11 @@ struct Epilogue {
       tr.g = static_cast<const char*>(a.dW) + p0 * a.lddw * esz(GR);
       tr.dg = (int64_t)RPP * a.lddw * esz(GR);
     }
-    if constexpr (fmt_blocked(S::MFMT) || fmt_blocked(S::VFMT)) {
+    if constexpr (fmt_blocked(S::MFMT) || fmt_blocked(S::VFMT) || fmt_blocked(S::WFMT)) {
       const int64_t spr = a.K >> __builtin_ctz((unsigned)a.block);   // scales per row
       if constexpr (fmt_blocked(S::MFMT)) tr.ms = a.ms + p0 * spr;
       if constexpr (fmt_blocked(S::VFMT)) tr.vs = a.vs + p0 * spr;
+      if constexpr (fmt_blocked(S::WFMT)) tr.ws = a.wsc + p0 * spr;
       tr.ds = (int64_t)RPP * spr;
     }
     tr.idx = ((uint32_t)p0 * (uint32_t)a.K) * GOLDEN;
@@ -1405,7 +1442,9 @@ constexpr int pending_words() {
 }
 template <int OPT, int WF, int MF, int VF, bool FAST>
 constexpr bool small_state() {
-  return pending_words<OPT, WF, MF, VF, FAST>() <= 6;
+  // an E4M3 weight beside two moments re-encodes three blocks per chunk:
+  // that epilogue spills within the register budget of three per CU
+  return pending_words<OPT, WF, MF, VF, FAST>() <= 6 && !(fmt_blocked(WF) && opt_has_m(OPT) && opt_has_v(OPT));
 }
 template <int OPT, int WF, int MF, int VF, bool FAST, bool ACC, bool GROUP>
 constexpr bool three_per_cu() {
@@ -1414,7 +1453,7 @@ constexpr bool three_per_cu() {
 template <int OPT, int WF, int MF, int VF, bool FAST>
 constexpr bool scaled_state() {
   using S = Step<OPT, WF, MF, VF, FAST>;
-  return fmt_blocked(S::MFMT) || fmt_blocked(S::VFMT);
+  return fmt_blocked(S::MFMT) || fmt_blocked(S::VFMT) || fmt_blocked(S::WFMT);
 }
 // Passes of state in flight, and how many of them are requested before the
 // mainloop.  In the grouped kernel (a few more registers for the layer
@@ -1688,6 +1727,25 @@ hipError_t combo_fused_acc(const KArgs& a, int w_fmt, hipStream_t st) {
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
+
+// An E4M3 weight with block scales (bf16 inputs): the same kernels as a bf16
+// or fp32 weight, instantiated only for the combinations of the FP8-weight
+// list.
+template <int O, int M, int V>
+hipError_t combo_fused_fp8w(const KArgs& a, hipStream_t st) {
+  const bool fast = a.dma_ok && a.vec_state && (a.K % 4) == 0;
+  if (fast && a.BT >= WIDE_MIN_BT) {
+    const dim3 g((unsigned)(((a.N + 255) / 256) * ((a.K + 255) / 256)));
+    hipLaunchKernelGGL((k_fused_wide<O, FMT_E4M3, M, V>), g, dim3(2 * NT), 0, st, a);
+  } else if (fast) {
+    hipLaunchKernelGGL((k_fused<FMT_BF16, true, O, FMT_E4M3, M, V>), tile_grid(a), dim3(NT), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((k_fused<FMT_BF16, false, O, FMT_E4M3, M, V>), tile_grid(a), dim3(NT), 0, st, a);
+  }
+  return hipGetLastError();
+}
+#define FORGE_INSTANTIATE_FP8W(O, M, V) \
+  template hipError_t combo_fused_fp8w<O, M, V>(const KArgs&, hipStream_t);
 
 // Explicit instantiation of the launchers of one combination.
 #define FORGE_INSTANTIATE(O, M, V)                                                  \

@@ -29,6 +29,14 @@ hipError_t launch_fused_acc(const KArgs& a, int w_fmt, int opt, int m_fmt, int v
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_fused_fp8w(const KArgs& a, int opt, int m_fmt, int v_fmt, hipStream_t st) {
+#define X(O, M, V) \
+  if (opt == O && m_fmt == M && v_fmt == V) return combo_fused_fp8w<O, M, V>(a, st);
+  FORGE_FP8W_LIST(X)
+#undef X
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_step(const KArgs& a, int w_fmt, int opt, int m_fmt, int v_fmt, hipStream_t st) {
 #define X(O, M, V) \
   if (opt == O && m_fmt == M && v_fmt == V) return combo_step<O, M, V>(a, w_fmt, st);

@@ -52,6 +52,7 @@ struct KArgs {
   const void* X;  int64_t ldx;    // [BT, K]
   const void* dY; int64_t lddy;   // [BT, N]
   void* W;  int64_t ldw;          // [N, K]
+  float* wsc;                     // block scales of an E4M3 weight [N, K/block] (else null)
   void* m;  int64_t ldm; float* ms;   // state 1 (+ int8 scales [N, K/block])
   void* v;  int64_t ldv; float* vs;   // state 2 (+ int8 scales)
   void* dW; int64_t lddw;         // G buffer [N, K]: unfused workspace (ld = K) or fp32 accumulator
@@ -107,6 +108,19 @@ constexpr int WIDE_MIN_BT = 2048;  // token count from which the 256 x 256 kerne
   X(OPT_ADAGRAD, FMT_NONE, FMT_F32)    \
   X(OPT_ADAGRAD, FMT_NONE, FMT_BF16)   \
   X(OPT_SGD, FMT_NONE, FMT_NONE)
+// Combinations that also take an E4M3 weight with block scales (bf16 inputs):
+// AdamW, Lion and SGD-momentum with every state format they support.
+#define FORGE_FP8W_LIST(X)         \
+  X(OPT_ADAMW, FMT_F32, FMT_F32)   \
+  X(OPT_ADAMW, FMT_BF16, FMT_BF16) \
+  X(OPT_ADAMW, FMT_S8, FMT_U8)     \
+  X(OPT_ADAMW, FMT_E4M3, FMT_E4M3) \
+  X(OPT_LION, FMT_F32, FMT_NONE)   \
+  X(OPT_LION, FMT_BF16, FMT_NONE)  \
+  X(OPT_LION, FMT_E4M3, FMT_NONE)  \
+  X(OPT_SGDM, FMT_F32, FMT_NONE)   \
+  X(OPT_SGDM, FMT_BF16, FMT_NONE)  \
+  X(OPT_SGDM, FMT_E4M3, FMT_NONE)
 #define FORGE_STATE_LIST(X) \
   FORGE_ADAMW_LIST(X) FORGE_LION_LIST(X) FORGE_SGDM_LIST(X) FORGE_ADAM_VARIANT_LIST(X) FORGE_SECOND_MOMENT_LIST(X)
 
@@ -117,7 +131,9 @@ struct DgArgs {
   void* dX; int64_t ldx;
   int32_t BT, N, K;
   int32_t tiles_m, tiles_k;       // ceil(BT/128), ceil(K/128) (MFMA kernel)
-  int32_t in_fmt, w_fmt, dx_fmt;  // dtypes of dY, W, dX
+  int32_t in_fmt, w_fmt, dx_fmt;  // dtypes of dY, W, dX (W may be E4M3 with block scales wsc)
+  const float* wsc;               // E4M3 W: fp32 scales [N, K / wblock]
+  int32_t wblock;
   int32_t vec_out;                // dX rows allow 4-element vector stores
   int32_t splits;                 // > 1: the reduction split across workgroups (fast path only)
   float* ws;                      // splits x [BT, K] fp32 partials (splits > 1)
@@ -148,6 +164,14 @@ inline int dgrad_splits(int64_t BT, int64_t N, int64_t K) {
 
 inline bool combo_supported(int in_fmt, int w_fmt, int opt, int m_fmt, int v_fmt) {
   if (in_fmt != FMT_F32 && in_fmt != FMT_BF16) return false;
+  if (w_fmt == FMT_E4M3) {
+    if (in_fmt != FMT_BF16) return false;
+#define X(O, M, V) \
+  if (opt == O && m_fmt == M && v_fmt == V) return true;
+    FORGE_FP8W_LIST(X)
+#undef X
+    return false;
+  }
   if (w_fmt != FMT_F32 && w_fmt != FMT_BF16) return false;
 #define X(O, M, V) \
   if (opt == O && m_fmt == M && v_fmt == V) return true;
@@ -177,6 +201,10 @@ hipError_t combo_fused_acc(const KArgs& a, int w_fmt, hipStream_t st);
 // Fused weight-gradient + step: one workgroup per 128 x 128 tile of W.
 hipError_t launch_fused(const KArgs& a, int in_fmt, int w_fmt, int opt, int m_fmt, int v_fmt,
                         hipStream_t stream);
+template <int O, int M, int V>
+hipError_t combo_fused_fp8w(const KArgs& a, hipStream_t st);
+// Fused step with an E4M3 weight (a.wsc its block scales; bf16 inputs).
+hipError_t launch_fused_fp8w(const KArgs& a, int opt, int m_fmt, int v_fmt, hipStream_t stream);
 // Fused step of g.n group-eligible layers in one launch (bf16 inputs).
 hipError_t launch_fused_group(const GroupArgs& g, int w_fmt, int opt, int m_fmt, int v_fmt, hipStream_t stream);
 // Fused step from an fp32 accumulator plus this call's gradient.

@@ -23,8 +23,9 @@
 // long-reduction layers this moves each W panel through L2 -> LDS once per
 // 128 tokens instead of once per 64 on the same number of workgroups.
 //
-// k_dgrad_generic (any dtype combination, any alignment): 64 x 64 tiles, fp32
-// FMA from an LDS-staged fp32 copy of both operands.
+// k_dgrad_generic (any dtype combination, any alignment, and the E4M3 weight
+// with block scales, decoded exactly): 64 x 64 tiles, fp32 FMA from an
+// LDS-staged fp32 copy of both operands.
 
 #include "forge_device.h"
 
@@ -312,6 +313,20 @@ __device__ __forceinline__ float ld_elem(const void* base, int fmt, int64_t i) {
   if (fmt == FMT_F32) return static_cast<const float*>(base)[i];
   return __uint_as_float((uint32_t)static_cast<const uint16_t*>(base)[i] << 16);
 }
+
+// W[n][col] as the step stores it: an E4M3 weight decodes to
+// fp32(E4M3 value of the code * its block's scale), exactly the value the
+// fused step reads back.
+__device__ __forceinline__ float ld_w(const DgArgs& g, int n, int col) {
+  const int64_t i = (int64_t)n * g.ldw + col;
+  if (g.w_fmt == FMT_E4M3) {
+    const int code = (int)static_cast<const uint8_t*>(g.W)[i];
+    const float v = __builtin_amdgcn_cvt_pk_f32_fp8(code, false)[0];
+    const int bsh = __builtin_ctz((unsigned)g.wblock);
+    return v * g.wsc[(int64_t)n * (g.K >> bsh) + (col >> bsh)];
+  }
+  return ld_elem(g.W, g.w_fmt, i);
+}
 }  // namespace
 
 __global__ void __launch_bounds__(NT) k_dgrad_generic(const DgArgs g) {
@@ -332,7 +347,7 @@ __global__ void __launch_bounds__(NT) k_dgrad_generic(const DgArgs g) {
       const int n = n0 + r;
       const int tok = tok0 + c, col = col0 + c;
       sa[r][c] = (n < g.N && tok < g.BT) ? ld_elem(g.dY, g.in_fmt, (int64_t)tok * g.lddy + n) : 0.f;
-      sb[r][c] = (n < g.N && col < g.K) ? ld_elem(g.W, g.w_fmt, (int64_t)n * g.ldw + col) : 0.f;
+      sb[r][c] = (n < g.N && col < g.K) ? ld_w(g, n, col) : 0.f;
     }
     __syncthreads();
 #pragma unroll

@@ -56,6 +56,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     p.add_argument("--no-unfused", action="store_true", help="skip the unfused comparison")
     p.add_argument("--no-ceilings", action="store_true", help="skip the measured HBM and MFMA ceilings")
+    p.add_argument("--cpu-quick", action="store_true",
+                   help="time the oracle on k_proj of the fp32-moment workload only (a short check of the output)")
     p.add_argument("--grouping", choices=["block", "subblock", "ready", "layer"], default="block",
                    help="block: one launch for the decoder layer's seven; subblock: one launch per sub-block, "
                         "[gate, up, down] and [q, k, v, o]; ready: as the gradients become available, [down] "
@@ -240,6 +242,65 @@ def family_sweep(F, synth, reps=5):
                      "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         del st, args, m, v
     del X, dY
+    torch.cuda.empty_cache()
+    return out
+
+
+def fp8_weight_sweep(F, synth, h, reps=5):
+    """E4M3 weight with fp32 block scales (forge_wgrad_step_fp8w) on gate_proj
+    [14336, 4096] at BT = 512, AdamW t = 10 with stochastic rounding of the
+    weight, moments fp32, bf16 or E4M3; and dX from the E4M3 weight
+    (forge_dgrad_fp8w, the plain fp32 kernel).  The weight starts as the
+    device-quantised N(0, 0.02^2) (forge_debug_quant, nearest code).
+    Algorithmic bytes: W codes read and written (2 B) plus its scales
+    (8 B per 128 elements), the moments' bytes, X and dY read once."""
+    import torch
+    N, K = synth.LLAMA8B_LAYERS["gate_proj"]
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    X, dY = synth.activations(1, BT, N, K, STEP_T, device="cuda", extra=60)
+    w32 = synth.normal((N, K), 0.02, "cuda", 1, 0, synth.T_W, 60)
+    wq = torch.empty((N, K), device="cuda", dtype=torch.uint8)
+    ws = torch.empty((N, K // 128), device="cuda", dtype=torch.float32)
+    F.forge_debug_quant(w32, wq, ws, F.FORGE_E4M3, False, 128)
+    del w32
+    W = F.state(wq.view(torch.float8_e4m3fn), ws, 128)
+    out = {}
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return sorted(ts)[len(ts) // 2]
+
+    for fmt, mbytes in (("f32", 16.0), ("bf16", 8.0), ("e4m3", 2 * (2 + 8 / 128))):
+        spec = synth.LayerSpec(in_dtype="bf16", w_fmt="bf16", m_fmt=fmt, v_fmt=fmt, block=128)
+        st = synth.state(1, N, K, spec, device="cuda", extra=60)
+        if fmt == "e4m3":
+            quantized_v(F, synth, st, 1, N, K, "e4m3", 60)
+            m, v = F.state(st["m"], st["m_scale"], 128), F.state(st["v"], st["v_scale"], 128)
+        else:
+            m, v = F.state(st["m"]), F.state(st["v"])
+        Xm, dYm = F.mat(X), F.mat(dY)
+        ms = timed(lambda: F.forge_wgrad_step_fp8w(Xm, dYm, W, m, v, h, STEP_T, SEED, stream=sp))
+        bpp = 2 + 8 / 128 + mbytes
+        nbytes = bpp * N * K + 2 * BT * (N + K)
+        out[f"adamw_{fmt}_moments"] = {"us": round(1e3 * ms, 1), "state_bytes_per_param": bpp,
+                                       "hbm_gbs_alg": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                                       "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del st, m, v
+    dX = torch.empty((BT, K), device="cuda", dtype=torch.bfloat16)
+    ms = timed(lambda: F.forge_dgrad_fp8w(dY, W, dX, stream=sp))
+    out["dgrad_fp8w_gate_proj_us"] = round(1e3 * ms, 1)
+    out["dgrad_fp8w_tflops"] = round(2.0 * BT * N * K / (ms * 1e-3) / 1e12, 1)
+    del X, dY, wq, ws, dX
     torch.cuda.empty_cache()
     return out
 
@@ -493,7 +554,7 @@ def _oracle_layer(O, synth, cfg, N, K, bt, hyp, spec, outlier_p, threads):
     return mm[0], mm[-1], time.perf_counter() - t1
 
 
-def oracle_cpu_times(layers):
+def oracle_cpu_times(layers, quick=False):
     """The oracle (oracle/) on the host cores, per layer, for the BT = 512
     workloads: fp32 layer (config 0 shape, 256 x 256, BT 64), bf16 W with
     fp32 m / v (config 1), bf16 W / m / v (config 2) and int8 m / v with 1%
@@ -514,6 +575,9 @@ def oracle_cpu_times(layers):
     hyp = O.Hyper(opt="adamw", round="sr")
     out = {"blas_threads": threads, "host": host_cpu()}
     t_start = time.perf_counter()
+    if quick:
+        specs = {1: specs[1]}
+        layers = {"k_proj": layers["k_proj"]}
     # config 0: fp32 256 x 256, BT 64, one step
     spec0 = synth.LayerSpec(in_dtype="f32", w_fmt="f32", m_fmt="f32", v_fmt="f32")
     mm1, _, st1 = _oracle_layer(O, synth, 0, 256, 256, 64, hyp, spec0, 0.0, 1)
@@ -530,6 +594,9 @@ def oracle_cpu_times(layers):
             params += N * K
         out[f"cfg{cfg}_bt512"] = {"layers": rows, "single_thread_s": round(tot1, 2), "all_core_s": round(totn, 2),
                                   "params": params, "params_per_s_all_core": round(params / totn, 1)}
+    if quick:
+        out["total_s"] = round(time.perf_counter() - t_start, 1)
+        return out
     # config 4: down_proj in full (all threads)
     spec4 = synth.LayerSpec(in_dtype="bf16", w_fmt="bf16", m_fmt="f32", v_fmt="f32")
     N, K = layers["down_proj"]
@@ -587,7 +654,8 @@ def cpu_baseline_from(detail):
     h = detail["host"]
     return {"value": c1["params_per_s_all_core"], "unit": "params/s", "cores": detail["blas_threads"],
             "kind": "oracle",
-            "sample": f"the seven Llama-3.1-8B layers at BT={BT} in full ({c1['params']} params, "
+            "sample": f"{','.join(c1['layers'])} of the Llama-3.1-8B decoder layer at BT={BT} in full "
+                      f"({c1['params']} params, "
                       f"{c1['all_core_s']} s all-core, {c1['single_thread_s']} s single-thread); fp64 BLAS matmul "
                       f"on {detail['blas_threads']} threads, element-wise step single-threaded NumPy; host "
                       f"{h['model']}, {h['logical_cpus']} logical CPUs ({h['usable_cpus']} usable)"}
@@ -737,6 +805,7 @@ def main():
         extras["optimizer_families_gate_proj_bt512"] = family_sweep(F, synth)
     if not args.no_state_formats:
         extras["state_formats_llama8b_bt512_grouped"] = state_format_sweep(F, synth, h)
+        extras["fp8_weight_gate_proj_bt512"] = fp8_weight_sweep(F, synth, h)
     if not args.no_dgrad:
         extras["dgrad_bt512"] = dgrad_sweep(F, L, layers)
     if not args.no_accumulation:
@@ -753,7 +822,7 @@ def main():
             v["mfma_frac_of_measured"] = round(v["tflops"] / c["mfma_bf16_tflops"], 4)
 
     if not args.no_cpu_baseline:
-        detail = oracle_cpu_times(layers)
+        detail = oracle_cpu_times(layers, quick=args.cpu_quick)
         extras["oracle_cpu_times"] = detail
         extras["host_cpu"] = detail["host"]
         cpu = cpu_baseline_from(detail)

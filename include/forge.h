@@ -170,6 +170,58 @@ forge_status forge_wgrad_step(const forge_mat* X, const forge_mat* dY, forge_mat
                               int64_t step, uint64_t seed, void* stream);
 
 /*
+ * FP8 weight storage (paper, section 3.6 and Figure 7, "FP8 w": FP8 weight
+ * quantization folded into the per-tile kernel; the pages give no format,
+ * scale or rounding rule, so this is the library's reading).  The weight is
+ * a forge_state of OCP E4M3 codes with one fp32 scale per `block`
+ * (32 / 64 / 128) consecutive elements of a row, the moments' block scheme:
+ * stored value = fp32(E4M3 value of the code * scale), scale =
+ * fp32(absmax / 448), and the new weight of a block is encoded from
+ * y = fp32(w * fp32(448 / absmax)):
+ *   h->round == FORGE_ROUND_RNE: the E4M3 value nearest to y (ties to even,
+ *     saturating at 448), as for E4M3 moments;
+ *   h->round == FORGE_ROUND_SR: stochastic rounding with the weight's SR
+ *     bits r (16 bits, the bf16 weight's key and flat index): for
+ *     |y| >= 2^-6, r * 2^4 is added to the 20 low fraction bits of |y|'s
+ *     fp32 pattern, which are then cleared; for |y| < 2^-6 (the subnormal
+ *     range, spacing 2^-9) the value is ((floor(|y| 2^25) + r) >> 16) 2^-9;
+ *     the magnitude saturates at 448 and the sign is kept.  |y| rounds away
+ *     from zero with probability equal to its position between its two
+ *     grid neighbours (quantised to 2^-16), so the store is unbiased.
+ * Non-finite weights are outside the contract.  A block-scaled m / v must
+ * use the weight's block size.
+ *
+ * forge_wgrad_step_fp8w -- forge_wgrad_step with such a weight: the fused
+ * kernel decodes W, applies the step in fp32 and re-encodes W (codes and
+ * scales, in place).  X and dY must be BF16.  Supported: AdamW with (m, v)
+ * in {(F32, F32), (BF16, BF16), (S8, U8), (E4M3, E4M3)}; Lion and SGD-m
+ * with m in {F32, BF16, E4M3}.  W->q.dtype must be FORGE_E4M3 (else E_DTYPE),
+ * K % W->block == 0 (else E_SHAPE), W->scale non-NULL (else E_NULL) and
+ * not overlapping any other buffer (else E_ALIAS).  Other arguments and
+ * errors as forge_wgrad_step (E_UNSUPPORTED for fp32 inputs or another
+ * optimizer / state combination).
+ */
+forge_status forge_wgrad_step_fp8w(const forge_mat* X, const forge_mat* dY, forge_state* W, forge_state* m,
+                                   forge_state* v, const forge_hyper* h, int64_t step, uint64_t seed,
+                                   void* stream);
+
+/* The validation of forge_wgrad_step_fp8w alone (no device call). */
+forge_status forge_wgrad_check_fp8w(const forge_mat* X, const forge_mat* dY, const forge_state* W,
+                                    const forge_state* m, const forge_state* v, const forge_hyper* h,
+                                    int64_t step);
+
+/*
+ * forge_dgrad_fp8w -- forge_dgrad (dX = dY W, paper Appendix A, Remark 1)
+ * from an E4M3 weight with block scales, decoded exactly to the values the
+ * step stores (fp32 code value * scale), fp32 accumulation over N.
+ * dY: [BT, N] BF16 or F32; dX: [BT, K] BF16 (round to nearest even) or F32,
+ * not overlapping dY, W or its scales.  Runs the plain fp32 kernel.
+ * Errors: those of forge_dgrad, and E_DTYPE / E_SHAPE / E_NULL / E_ALIGN
+ * for the weight state as forge_wgrad_step_fp8w.
+ */
+forge_status forge_dgrad_fp8w(const forge_mat* dY, const forge_state* W, forge_mat* dX, void* stream);
+
+/*
  * forge_wgrad_step_group -- forge_wgrad_step on n independent layers that
  * share one optimizer, step and hyper-parameters, with as few launches as
  * possible.  Layers whose gradients become available together in a backward

@@ -87,7 +87,7 @@ __all__ = [
     "adamw", "lion", "sgdm", "nadam", "radam", "rmsprop", "adagrad", "sgd",
     "nadam_mu", "radam_rect",
     "quantize_signed", "quantize_unsigned", "dequantize",
-    "E4M3_MAX", "e4m3_to_f64", "f32_to_e4m3_rne", "quantize_e4m3",
+    "E4M3_MAX", "e4m3_to_f64", "f32_to_e4m3_rne", "f32_to_e4m3_sr", "quantize_e4m3",
     "decode", "encode", "wgrad_step", "apply_step", "step_tiled",
     "TENSOR_W", "TENSOR_M", "TENSOR_V",
 ]
@@ -514,17 +514,54 @@ def f32_to_e4m3_rne(y32: np.ndarray) -> np.ndarray:
     return (pick | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
 
 
-def quantize_e4m3(x32: np.ndarray, block: int, positive: bool):
+def f32_to_e4m3_sr(y32: np.ndarray, r16: np.ndarray) -> np.ndarray:
+    """Stochastic rounding of fp32 values onto the E4M3 grid (the FP8 weight
+    store with stochastic rounding; the pages give no rule, this is the
+    reading): |y| is rounded to one of its two neighbouring E4M3 values,
+    away from zero with probability equal to its fractional position between
+    them (quantised to 2^-16), saturating at 448; the sign is kept (a result
+    of zero keeps the input's sign).  With 16 random bits r:
+
+    * |y| >= 2^-6 (the normal range, 3 fraction bits): r * 2^4 is added to
+      the 20 fraction bits of |y|'s fp32 pattern that E4M3 does not keep and
+      those bits are cleared (a carry moves |y| to the next grid value);
+    * |y| < 2^-6 (the subnormal range, spacing 2^-9): z = floor(|y| 2^25)
+      (exact), and the result is ((z + r) >> 16) * 2^-9.
+
+    Returns uint8 codes."""
+    y = np.ascontiguousarray(y32, dtype=np.float32)
+    u = y.view(np.uint32)
+    sign = u & np.uint32(0x80000000)
+    au = u & np.uint32(0x7FFFFFFF)
+    ay = au.view(np.float32)
+    r = np.asarray(r16, dtype=np.uint32) & np.uint32(0xFFFF)
+    with np.errstate(invalid="ignore", over="ignore"):
+        normal = np.minimum(((au + (r << np.uint32(4))) & np.uint32(0xFFF00000)).view(np.float32), np.float32(448.0))
+        z = np.floor(ay.astype(np.float64) * 2.0 ** 25)
+        z = np.where(ay < np.float32(2.0 ** -6), z, 0.0).astype(np.uint64)
+    sub = (((z + r.astype(np.uint64)) >> np.uint64(16)).astype(np.float64) * 2.0 ** -9).astype(np.float32)
+    mag = np.where(ay >= np.float32(2.0 ** -6), normal, sub).astype(np.float32)
+    val = (mag.view(np.uint32) | sign).view(np.float32)
+    return f32_to_e4m3_rne(val)          # on the grid: the conversion is exact
+
+
+def quantize_e4m3(x32: np.ndarray, block: int, positive: bool, r16: Optional[np.ndarray] = None):
     """E4M3 block quantisation (the int8 scheme with E4M3 codes; the paper's
     FP8 moment quantization, section 3.6, gives no format, this is the
     reading): a = max|x| over the block, s = fp32(a/448), code =
     f32_to_e4m3_rne(fp32(x * fp32(448/a))); with ``positive`` (the second
     moment) a positive x never takes code 0 but the smallest subnormal.
-    a = 0 gives s = 0 and all codes +-0.  Returns (uint8 codes, float32 scales)."""
+    a = 0 gives s = 0 and all codes +-0.  With ``r16`` (16 random bits per
+    element, the shape of x) the code is f32_to_e4m3_sr of the same scaled
+    value instead of the nearest one (the FP8 weight store with stochastic
+    rounding).  Returns (uint8 codes, float32 scales)."""
     xb = _blocks(np.asarray(x32, dtype=np.float32), block)
     a = np.max(np.abs(xb), axis=2)
     y, s = _scaled_codes(xb, a, E4M3_MAX)
-    q = f32_to_e4m3_rne(y)
+    if r16 is None:
+        q = f32_to_e4m3_rne(y)
+    else:
+        q = f32_to_e4m3_sr(y, np.asarray(r16).reshape(xb.shape))
     if positive:
         q = np.where((xb > 0) & (q == 0), np.uint8(1), q).astype(np.uint8)
     return q.reshape(x32.shape), s
@@ -562,14 +599,17 @@ def decode(st: Stored, rows=None, c0: int = 0, c1: Optional[int] = None) -> np.n
 
 
 def encode(x64: np.ndarray, fmt: str, *, round: str = "sr", key: int = 0,
-           flat_index: Optional[np.ndarray] = None, block: int = 128, positive: bool = False) -> Stored:
+           flat_index: Optional[np.ndarray] = None, block: int = 128, positive: bool = False,
+           fp8_round: str = "rne") -> Stored:
     """Round fp64 results once into the storage format (Algorithm 1 Phase 3).
 
     fp32: round to nearest even.  bf16: the value is first rounded to fp32,
     then to bf16 by round-to-nearest-even or by stochastic rounding with the
     counter-based bits of ``key`` and ``flat_index``.  s8 / u8 / e4m3: the
     fp32 value is block-quantised (e4m3 with ``positive`` for the second
-    moment).
+    moment); e4m3 codes are the nearest grid values, or, with
+    ``fp8_round="sr"`` (the FP8 weight with stochastic rounding), drawn with
+    the same counter-based bits as a bf16 store.
     """
     x32 = np.asarray(x64, dtype=np.float64).astype(np.float32)
     if fmt == "f32":
@@ -585,7 +625,8 @@ def encode(x64: np.ndarray, fmt: str, *, round: str = "sr", key: int = 0,
         q, s = quantize_unsigned(x32, block)
         return Stored("u8", q, s, block)
     if fmt == "e4m3":
-        q, s = quantize_e4m3(x32, block, positive)
+        r16 = sr_bits(key, flat_index) if fp8_round == "sr" else None
+        q, s = quantize_e4m3(x32, block, positive, r16)
         return Stored("e4m3", q, s, block)
     raise ValueError(f"unknown format {fmt!r}")
 
@@ -648,8 +689,11 @@ def apply_step(G: np.ndarray, W: Stored, m: Optional[Stored], v: Optional[Stored
     def store(x, st, tid):
         if st is None:
             return None
+        # an FP8 weight follows the rounding mode like a bf16 one; FP8
+        # moments always take the nearest code (the int8 scheme's rule)
         return encode(x, st.fmt, round=h.round, key=sr_key(seed, step, tid),
-                      flat_index=flat, block=st.block, positive=(tid == TENSOR_V))
+                      flat_index=flat, block=st.block, positive=(tid == TENSOR_V),
+                      fp8_round=h.round if tid == TENSOR_W else "rne")
 
     return {"W": store(W1, W, TENSOR_W), "m": store(m1, m, TENSOR_M),
             "v": store(v1, v, TENSOR_V), "pre": {"W": W1, "m": m1, "v": v1}}

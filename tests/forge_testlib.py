@@ -68,6 +68,7 @@ class Layer:
     v: Optional[torch.Tensor]
     ms: Optional[torch.Tensor] = None
     vs: Optional[torch.Tensor] = None
+    wsc: Optional[torch.Tensor] = None      # block scales of an E4M3 weight
 
     def _state(self, t, scale):
         if t is None:
@@ -83,13 +84,18 @@ class Layer:
     def forge_m(self):
         return self._state(self.m, self.ms)
 
+    def forge_w(self):
+        """The weight as the fused step takes it: a tensor, or for an E4M3
+        weight a forge_state with its block scales."""
+        return self._state(self.W, self.wsc) if self.wsc is not None else self.W
+
     def forge_v(self):
         return self._state(self.v, self.vs)
 
     def clone(self) -> "Layer":
         c = lambda t: None if t is None else t.clone()
         return Layer(self.N, self.K, self.BT, self.spec, self.X, self.dY, c(self.W), c(self.m), c(self.v),
-                     c(self.ms), c(self.vs))
+                     c(self.ms), c(self.vs), c(self.wsc))
 
 
 def make_layer(cfg: int, N: int, K: int, BT: int, step: int, spec: synth.LayerSpec, *, device="cuda",
@@ -116,13 +122,26 @@ def make_layer(cfg: int, N: int, K: int, BT: int, step: int, spec: synth.LayerSp
             st["v"] = torch.from_numpy(q).view(torch.float8_e4m3fn)
         st["v_scale"] = torch.from_numpy(s)
         del v32
+    w_scale = None
+    if spec.w_fmt == "e4m3":
+        # an E4M3 weight starts as the oracle's nearest-code quantisation of
+        # W ~ N(0, w_std^2) (the same codes and scales go to both sides)
+        w32 = st["W"].float().cpu().numpy()
+        if K % spec.block == 0:
+            q, sc = O.quantize_e4m3(w32, spec.block, False)
+        else:   # only used to check that the call is rejected
+            q, sc = np.zeros(w32.shape, np.uint8), np.zeros((N, max(1, K // spec.block)), np.float32)
+        st["W"], w_scale = torch.from_numpy(q).view(torch.float8_e4m3fn), torch.from_numpy(sc)
     mv = lambda t: None if t is None else t.to(device)
     return Layer(N, K, BT, spec, mv(X), mv(dY), mv(st["W"]), mv(st["m"]), mv(st["v"]), mv(st["m_scale"]),
-                 mv(st["v_scale"]))
+                 mv(st["v_scale"]), mv(w_scale))
 
 
 def run_fused(L: Layer, h, step: int, seed: int):
-    F.forge_wgrad_step(L.X, L.dY, L.W, L.forge_m(), L.forge_v(), h, step, seed)
+    if L.wsc is not None:
+        F.forge_wgrad_step_fp8w(L.X, L.dY, L.forge_w(), L.forge_m(), L.forge_v(), h, step, seed)
+    else:
+        F.forge_wgrad_step(L.X, L.dY, L.W, L.forge_m(), L.forge_v(), h, step, seed)
 
 
 def run_unfused(L: Layer, h, step: int, seed: int, dw_dtype=torch.float32):
@@ -168,7 +187,7 @@ def snapshot(L: Layer, rows=None) -> Snap:
     idx = torch.as_tensor(rows, device=L.dY.device, dtype=torch.long)
     s = L.spec
     return Snap(rows=rows, X=synth.host(L.X), dY=synth.host(L.dY.index_select(1, idx)),
-                W=_stored(L.W, s.w_fmt, None, s.block, rows),
+                W=_stored(L.W, s.w_fmt, L.wsc, s.block, rows),
                 m=_stored(L.m, s.m_fmt, L.ms, s.block, rows),
                 v=_stored(L.v, s.v_fmt, L.vs, s.block, rows))
 
@@ -259,7 +278,7 @@ def check_against_oracle(snap: Snap, L: Layer, h, step: int, seed: int, col_rang
         if c1 <= c0:
             continue
         ref, lo, hi, tscale = _hull(snap, hyp, step, seed, c0, c1, K)
-        got = {"W": (L.W, s.w_fmt, None), "m": (L.m, s.m_fmt, L.ms), "v": (L.v, s.v_fmt, L.vs)}
+        got = {"W": (L.W, s.w_fmt, L.wsc), "m": (L.m, s.m_fmt, L.ms), "v": (L.v, s.v_fmt, L.vs)}
         for name, (t, fmt, scale) in got.items():
             if t is None or fmt is None:
                 continue
@@ -306,7 +325,12 @@ def check_against_oracle(snap: Snap, L: Layer, h, step: int, seed: int, col_rang
                 exact = float(np.mean(d == 0)) if d.size else 1.0
                 rep.exact_frac[where] = exact
                 tol8 = 1e-5 * np.maximum(np.abs(r_pre), tscale[name])
-                det = _determined_codes(fmt, name == "v", lo[name] - tol8, hi[name] + tol8, s.block)
+                r16 = None
+                if name == "W" and hyp.round == "sr":   # the weight's own SR bits decide its code
+                    flat = snap.rows.astype(np.uint64)[:, None] * np.uint64(K) + \
+                        np.arange(c0, c1, dtype=np.uint64)[None, :]
+                    r16 = O.sr_bits(O.sr_key(seed, step, O.TENSOR_W), flat)
+                det = _determined_codes(fmt, name == "v", lo[name] - tol8, hi[name] + tol8, s.block, r16)
                 rep.determined[where] = float(np.mean(det)) if det.size else 1.0
                 if (det & (d != 0)).any():
                     i = np.argwhere(det & (d != 0))[0]
@@ -336,14 +360,17 @@ def check_against_oracle(snap: Snap, L: Layer, h, step: int, seed: int, col_rang
     return rep
 
 
-def _determined_codes(fmt: str, second: bool, xlo: np.ndarray, xhi: np.ndarray, block: int) -> np.ndarray:
+def _determined_codes(fmt: str, second: bool, xlo: np.ndarray, xhi: np.ndarray, block: int,
+                      r16: Optional[np.ndarray] = None) -> np.ndarray:
     """True where the 8-bit code is fixed by the inputs: every fp32
     pre-quantisation value in [xlo, xhi], multiplied by every reciprocal
     QMAX / a that the block absmax a can take (a over the same intervals),
     rounds to one code (the product's own fp32 rounding and the reciprocal's
     are covered by a relative widening of 2^-21).  Where this holds, the
     kernel's code and the oracle's must be identical: the quantiser is the
-    same definition on both sides."""
+    same definition on both sides.  With ``r16`` (an E4M3 weight stored with
+    stochastic rounding) the code is the SR code with those bits, which is
+    monotone in y too."""
     qmax = {"s8": 127.0, "u8": 255.0, "e4m3": O.E4M3_MAX}[fmt]
     R, C = xlo.shape
     alo = np.where((xlo <= 0) & (xhi >= 0), 0.0, np.minimum(np.abs(xlo), np.abs(xhi)))
@@ -364,7 +391,9 @@ def _determined_codes(fmt: str, second: bool, xlo: np.ndarray, xhi: np.ndarray, 
         if fmt == "u8":
             return np.clip(np.rint(y), 1, 255)
         yy = np.maximum(y, 2.0 ** -9) if second else y
-        cc = O.f32_to_e4m3_rne(np.clip(yy, -3e38, 3e38).astype(np.float32)).astype(np.int64)
+        yy = np.clip(yy, -3e38, 3e38).astype(np.float32)
+        # stochastic rounding with fixed bits is monotone in y, like the nearest code
+        cc = (O.f32_to_e4m3_rne(yy) if r16 is None else O.f32_to_e4m3_sr(yy, r16)).astype(np.int64)
         return np.where(cc & 0x80, -(cc & 0x7F), cc)
 
     det = ok & (code(ylo) == code(yhi))
@@ -387,7 +416,7 @@ def assert_rejected(L: Layer, call, extra=(), code=None):
     tensors in `extra`, unchanged: validation happens before anything is
     enqueued."""
     code = F.FORGE_E_SHAPE if code is None else code
-    ts = [t for t in (L.W, L.m, L.v, L.ms, L.vs, *extra) if t is not None]
+    ts = [t for t in (L.W, L.m, L.v, L.ms, L.vs, L.wsc, *extra) if t is not None]
     before = [_codes(t).clone() for t in ts]
     torch.cuda.synchronize()
     rc = call()

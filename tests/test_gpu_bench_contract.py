@@ -20,7 +20,7 @@ def _run(*args, timeout=240):
 
 def test_bench_json_contract():
     print("case: bench.py --steps 2 --warmup 1 (short sections)", flush=True)
-    r = _run("--steps", "2", "--warmup", "1", "--cpu-seconds", "1", "--no-unfused", "--no-family-sweep",
+    r = _run("--steps", "2", "--warmup", "1", "--cpu-quick", "--no-unfused", "--no-family-sweep",
              "--no-accumulation", "--no-dgrad", "--no-mfma-sweep", "--no-ceilings")
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [l for l in r.stdout.splitlines() if l.startswith("{")]

@@ -1,0 +1,153 @@
+"""GPU: FP8 (E4M3) weight storage (the paper's FP8 weight quantization
+folded into the per-tile kernel, section 3.6 and Figure 7; format, scale
+and rounding as documented in forge.h).
+
+forge_wgrad_step_fp8w against the oracle element by element: codes that the
+fp32 uncertainty of the new weight cannot change must be identical (for
+stochastic rounding: with the weight's own SR bits), the others within one
+grid step; scales within 1e-5 or the hull of the block absmax; moments as in
+the other parity tests.  AdamW with every moment format, Lion and SGD-m,
+both rounding modes, blocks of 128, 64 and 32, several steps, ragged shapes,
+the 256 x 256 kernel (BT >= 2048) and gate_proj at full size on sampled
+rows.  forge_dgrad_fp8w against the oracle's fp64 product with the decoded
+weight.  Unsupported combinations and shapes are refused before anything
+is enqueued.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import backward_weight_gradient_amd as F
+import oracle as O
+import synth
+from forge_testlib import assert_ok, assert_rejected, check_against_oracle, make_layer, run_fused, sample_rows, \
+    snapshot
+
+pytestmark = pytest.mark.gpu
+SEED = 1337
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _hyper(opt, round_):
+    if opt == "lion":
+        return F.hyper("lion", lr=1e-4, beta1=0.9, beta2=0.99, weight_decay=0.01, round=round_)
+    return F.hyper(opt, round=round_)
+
+
+def _spec(opt, state, block=128):
+    m = None if opt not in F.KEEPS_M else ("s8" if state == "int8" else state)
+    v = None if opt not in F.KEEPS_V else ("u8" if state == "int8" else state)
+    return synth.LayerSpec("bf16", "e4m3", m, v, block=block)
+
+
+CASES = [("adamw", "f32"), ("adamw", "bf16"), ("adamw", "int8"), ("adamw", "e4m3"), ("lion", "f32"),
+         ("lion", "e4m3"), ("sgdm", "bf16"), ("sgdm", "e4m3")]
+
+
+@pytest.mark.parametrize("opt,state", CASES)
+@pytest.mark.parametrize("round_", ["sr", "rne"])
+def test_fp8_weight_verification_shape(opt, state, round_):
+    _say(f"case: FP8 W {opt} {state} {round_} 512x512 BT256")
+    L = make_layer(70, 512, 512, 256, 1, _spec(opt, state), outlier_p=0.01 if state == "int8" else 0.0)
+    h = _hyper(opt, round_)
+    for t in (1, 2, 3):
+        X, dY = synth.activations(70, 256, 512, 512, t, outlier_p=0.01 if state == "int8" else 0.0)
+        L.X, L.dY = X.cuda(), dY.cuda()
+        snap = snapshot(L)
+        run_fused(L, h, t, SEED)
+        torch.cuda.synchronize()
+        assert_ok(check_against_oracle(snap, L, h, t, SEED), f"FP8 W {opt} {state} {round_} t={t}")
+
+
+@pytest.mark.parametrize("block", [64, 32])
+@pytest.mark.parametrize("N,K,BT", [(130, 256, 77), (264, 384, 129), (1, 128, 1), (200, 512, 0)])
+def test_fp8_weight_ragged(block, N, K, BT):
+    _say(f"case: FP8 W ragged {N}x{K} BT{BT} block {block}")
+    L = make_layer(71, N, K, BT, 5, _spec("adamw", "e4m3", block))
+    h = _hyper("adamw", "sr")
+    snap = snapshot(L)
+    run_fused(L, h, 5, SEED)
+    torch.cuda.synchronize()
+    assert_ok(check_against_oracle(snap, L, h, 5, SEED), f"FP8 W {N}x{K}x{BT}")
+
+
+@pytest.mark.parametrize("state", ["f32", "e4m3"])
+def test_fp8_weight_wide_kernel(state):
+    """BT >= 2048: the 256 x 256 macro-tile kernel with the E4M3 weight."""
+    _say(f"case: FP8 W wide kernel {state}")
+    L = make_layer(72, 520, 384, 2080, 4, _spec("adamw", state), gen_device="cuda")
+    h = _hyper("adamw", "sr")
+    snap = snapshot(L)
+    run_fused(L, h, 4, SEED)
+    torch.cuda.synchronize()
+    assert_ok(check_against_oracle(snap, L, h, 4, SEED), f"FP8 W wide {state}")
+
+
+@pytest.mark.parametrize("state", ["f32", "e4m3"])
+def test_fp8_weight_gate_proj_full_size(state):
+    """gate_proj [14336, 4096] at BT = 512 on sampled rows and column blocks."""
+    _say(f"case: FP8 W gate_proj BT512 {state}")
+    N, K = synth.LLAMA8B_LAYERS["gate_proj"]
+    L = make_layer(73, N, K, 512, 10, _spec("adamw", state), gen_device="cuda")
+    h = _hyper("adamw", "sr")
+    rows = sample_rows(N, 24, seed=73)
+    snap = snapshot(L, rows)
+    run_fused(L, h, 10, SEED)
+    torch.cuda.synchronize()
+    cols = [(0, 128), (1280, 1408), (K - 128, K)]
+    assert_ok(check_against_oracle(snap, L, h, 10, SEED, col_ranges=cols), f"FP8 W gate_proj {state}")
+    del L
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("N,K,BT,dx", [(512, 512, 256, torch.bfloat16), (130, 256, 77, torch.float32),
+                                       (14336, 4096, 512, torch.bfloat16)])
+def test_fp8_weight_dgrad(N, K, BT, dx):
+    _say(f"case: FP8 W dX {N}x{K} BT{BT} {dx}")
+    L = make_layer(75, N, K, BT, 2, _spec("adamw", "f32"), gen_device="cuda" if N > 4096 else "cpu")
+    dX = torch.full((BT, K), float("nan"), device="cuda", dtype=dx)
+    F.forge_dgrad_fp8w(L.dY, L.forge_w(), dX)
+    torch.cuda.synchronize()
+    rows = np.unique(np.array([0, 1, BT // 2, BT - 1] + list(np.random.default_rng(N).integers(0, BT, 12))))
+    Wst = O.Stored("e4m3", synth.host(L.W), L.wsc.cpu().numpy(), 128)
+    Wdec = O.decode(Wst).astype(np.float32)         # the stored weight, exactly (fp32)
+    dYh = synth.host(L.dY)
+    ref = O.input_grad(dYh, Wdec, rows)
+    bound = O.input_grad_error_bound(dYh, Wdec, rows)
+    got = synth.host(dX)[rows]
+    got = O.bf16_bits_to_f64(got) if dx == torch.bfloat16 else got.astype(np.float64)
+    if dx == torch.bfloat16:
+        bound = bound + np.abs(ref) * 2.0 ** -8
+    bad = np.abs(got - ref) > bound * (1 + 1e-6) + 1e-30
+    assert not bad.any(), f"{int(bad.sum())} dX elements outside the fp32 bound"
+    del L
+    torch.cuda.empty_cache()
+
+
+def test_fp8_weight_rejections_leave_everything_untouched():
+    _say("case: FP8 W rejected calls")
+    h = _hyper("adamw", "sr")
+    # K not a multiple of the block
+    L = make_layer(76, 64, 200, 32, 1, synth.LayerSpec("bf16", "e4m3", "f32", "f32", block=128))
+    assert_rejected(L, lambda: F.forge_wgrad_step_fp8w(L.X, L.dY, L.forge_w(), L.forge_m(), L.forge_v(), h, 1,
+                                                         SEED, check=False))
+    # a combination without an FP8-weight kernel (NAdam), and fp32 inputs
+    L = make_layer(76, 64, 256, 32, 1, synth.LayerSpec("bf16", "e4m3", "f32", "f32", block=128))
+    assert_rejected(L, lambda: F.forge_wgrad_step_fp8w(L.X, L.dY, L.forge_w(), L.forge_m(), L.forge_v(),
+                                                         F.hyper("nadam"), 1, SEED, check=False),
+                    code=F.FORGE_E_UNSUPPORTED)
+    X32, dY32 = L.X.float(), L.dY.float()
+    assert_rejected(L, lambda: F.forge_wgrad_step_fp8w(X32, dY32, L.forge_w(), L.forge_m(), L.forge_v(), h, 1,
+                                                         SEED, check=False), code=F.FORGE_E_UNSUPPORTED)
+    # a bf16 weight passed as the E4M3 state
+    Wb = torch.zeros((64, 256), device="cuda", dtype=torch.bfloat16)
+    bad = F.forge_state(F.mat(Wb), L.wsc.data_ptr(), 128)
+    assert_rejected(L, lambda: F.forge_wgrad_step_fp8w(L.X, L.dY, bad, L.forge_m(), L.forge_v(), h, 1, SEED,
+                                                         check=False), code=F.FORGE_E_DTYPE)

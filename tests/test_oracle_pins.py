@@ -791,3 +791,80 @@ def test_e4m3_block_quantisation():
     v[0, :3] = [1e-30, 0.0, 1e-12]
     qv, sv = O.quantize_e4m3(v, 128, positive=True)
     assert np.all(qv[v > 0] != 0) and np.all(qv[v == 0] == 0)
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) weight store with stochastic rounding (section 3.6; the pages
+# give no rule, the reading is in forge.h and the oracle)
+# ---------------------------------------------------------------------------
+def _e4m3_neighbours(y):
+    """The E4M3 grid values at or below |y| and at or above it (by search on
+    the grid itself), with |y| >= 448 saturating."""
+    grid = O.e4m3_to_f64(np.arange(0x7F))
+    ay = np.minimum(np.abs(y.astype(np.float64)), 448.0)
+    hi_i = np.searchsorted(grid, ay, side="left")
+    lo_i = np.where(grid[np.minimum(hi_i, 126)] == ay, hi_i, hi_i - 1)
+    return grid[np.clip(lo_i, 0, 126)], grid[np.clip(hi_i, 0, 126)]
+
+
+def test_e4m3_sr_takes_a_neighbour_and_truncates_with_zero_bits():
+    rng = np.random.default_rng(21)
+    y = np.concatenate([rng.uniform(-448, 448, 20000), 10.0 ** rng.uniform(-5, 2.6, 20000),
+                        -(10.0 ** rng.uniform(-5, 2.6, 20000)), [500.0, -1e9, 0.0, -0.0]]).astype(np.float32)
+    lo, hi = _e4m3_neighbours(y)
+    for r in (0, 1, 0x7FFF, 0x8000, 0xFFFF):
+        got = O.e4m3_to_f64(O.f32_to_e4m3_sr(y, np.full(y.shape, r)))
+        mag = np.abs(got)
+        assert np.all((mag == lo) | (mag == hi)), r
+        assert np.all(np.signbit(got) == np.signbit(y)), r
+        if r == 0:                                   # no random bits: toward zero
+            np.testing.assert_array_equal(mag, lo)
+    # grid values are kept for every r; beyond 448 saturates
+    grid = O.e4m3_to_f64(np.arange(0x7F)).astype(np.float32)
+    for r in (0, 0x1234, 0xFFFF):
+        np.testing.assert_array_equal(O.e4m3_to_f64(O.f32_to_e4m3_sr(grid, np.full(grid.shape, r))), grid)
+    assert O.e4m3_to_f64(O.f32_to_e4m3_sr(np.float32([479.0, 1e30]), np.full(2, 0xFFFF))).tolist() == [448.0, 448.0]
+
+
+@pytest.mark.parametrize("y", [1.0 + 2.0 ** -5, 0.3, 300.0, 5.1 * 2.0 ** -9, 2.0 ** -12, -0.0107])
+def test_e4m3_sr_unbiased(y):
+    """E[SR(y)] = y over 1e6 counter-based draws, in the normal range, the
+    subnormal range and across the sign; the probability of rounding up is
+    the fractional position (Appendix C's argument, applied to E4M3)."""
+    n = 1 << 20
+    ys = np.full(n, y, dtype=np.float32)
+    r = O.sr_bits(O.sr_key(1337, 3, 0), np.arange(n))
+    got = O.e4m3_to_f64(O.f32_to_e4m3_sr(ys, r))
+    lo, hi = _e4m3_neighbours(np.float32([y]))
+    f = (abs(np.float64(np.float32(y))) - lo[0]) / (hi[0] - lo[0])
+    sd = (hi[0] - lo[0]) * math.sqrt(f * (1 - f) / n)
+    assert abs(np.mean(got) - np.float64(np.float32(y))) < 5 * sd + 2.0 ** -16 * (hi[0] - lo[0])
+    up = np.mean(np.abs(got) == hi[0])
+    assert abs(up - f) < 5 * math.sqrt(f * (1 - f) / n) + 2.0 ** -16
+
+
+def test_fp8_weight_store_follows_the_rounding_mode():
+    """An E4M3 weight takes stochastic rounding when the step's mode is SR
+    (with the weight's own SR bits) and the nearest code when it is RNE;
+    E4M3 moments take the nearest code either way."""
+    rng = np.random.default_rng(5)
+    N, K = 8, 256
+    W0 = rng.standard_normal((N, K)).astype(np.float32) * 0.02
+    qw, sw = O.quantize_e4m3(W0, 128, False)
+    W = O.Stored("e4m3", qw, sw, 128)
+    m = O.Stored("e4m3", np.zeros((N, K), np.uint8), np.zeros((N, 2), np.float32), 128)
+    v = O.Stored("e4m3", np.zeros((N, K), np.uint8), np.zeros((N, 2), np.float32), 128)
+    G = rng.standard_normal((N, K)) * 1e-3
+    for mode in ("rne", "sr"):
+        hyp = O.Hyper(opt="adamw", round=mode)
+        out = O.apply_step(G, W, m, v, hyp, 10, 1337)
+        pre = out["pre"]
+        flat = np.arange(N * K, dtype=np.uint64).reshape(N, K)
+        r16 = O.sr_bits(O.sr_key(1337, 10, O.TENSOR_W), flat) if mode == "sr" else None
+        qW, sW = O.quantize_e4m3(pre["W"].astype(np.float32), 128, False, r16)
+        np.testing.assert_array_equal(out["W"].data, qW)
+        np.testing.assert_array_equal(out["W"].scale, sW)
+        qm, _ = O.quantize_e4m3(pre["m"].astype(np.float32), 128, False)
+        np.testing.assert_array_equal(out["m"].data, qm)
+    assert not np.array_equal(O.apply_step(G, W, m, v, O.Hyper(round="sr"), 10, 1337)["W"].data,
+                              O.apply_step(G, W, m, v, O.Hyper(round="rne"), 10, 1337)["W"].data)
