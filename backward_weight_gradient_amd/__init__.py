@@ -136,6 +136,9 @@ def _load() -> ctypes.CDLL:
     lib.forge_debug_quant.restype = st
     lib.forge_debug_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
     lib.forge_debug_copy.restype = st
+    lib.forge_debug_state_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                             ctypes.c_int64, ctypes.c_void_p]
+    lib.forge_debug_state_stream.restype = st
     lib.forge_debug_mfma_peak.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
     lib.forge_debug_mfma_peak.restype = st
     lib.forge_status_str.argtypes = [ctypes.c_int]
@@ -458,6 +461,19 @@ def forge_debug_copy(src, dst, stream=None, check: bool = True) -> int:
     rc = lib.forge_debug_copy(src.data_ptr(), dst.data_ptr(), nbytes, _stream(stream))
     if check and rc != FORGE_OK:
         raise ForgeError(rc, "forge_debug_copy")
+    return rc
+
+
+def forge_debug_state_stream(W, m, v, stream=None, check: bool = True) -> int:
+    """The epilogue-shaped W (bf16) / m / v (fp32) read-and-write stream (measurement hook)."""
+    N, K = W.shape
+    if W.dtype != torch.bfloat16 or m.dtype != torch.float32 or v.dtype != torch.float32 or \
+            m.shape != W.shape or v.shape != W.shape or not (W.is_contiguous() and m.is_contiguous()
+                                                              and v.is_contiguous()):
+        raise ValueError("forge_debug_state_stream: W bf16, m and v float32, contiguous, of one shape")
+    rc = lib.forge_debug_state_stream(W.data_ptr(), m.data_ptr(), v.data_ptr(), N, K, _stream(stream))
+    if check and rc != FORGE_OK:
+        raise ForgeError(rc, "forge_debug_state_stream")
     return rc
 
 

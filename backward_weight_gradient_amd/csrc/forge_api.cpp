@@ -728,6 +728,18 @@ forge_status forge_debug_copy(const void* src, void* dst, int64_t bytes, void* s
   return hip_status(launch_debug_copy(src, dst, (uint64_t)bytes, (hipStream_t)stream));
 }
 
+forge_status forge_debug_state_stream(uint16_t* W, float* m, float* v, int64_t N, int64_t K, void* stream) {
+  if (N < 0 || K < 0 || N % 128 != 0 || K % 128 != 0) return FORGE_E_SHAPE;
+  if ((uint64_t)N * (uint64_t)K >= (1ull << 32) || N >= (1ll << 31) || K >= (1ll << 31)) return FORGE_E_SHAPE;
+  if (N == 0 || K == 0) return FORGE_OK;
+  if (!W || !m || !v) return FORGE_E_NULL;
+  if (!aligned(W, 8) || !aligned(m, 16) || !aligned(v, 16)) return FORGE_E_ALIGN;
+  const uint64_t n = (uint64_t)N * (uint64_t)K;
+  const Range rw = raw_range(W, 2 * n), rm = raw_range(m, 4 * n), rv = raw_range(v, 4 * n);
+  if (overlap(rw, rm) || overlap(rw, rv) || overlap(rm, rv)) return FORGE_E_ALIAS;
+  return hip_status(launch_debug_state_stream(W, m, v, (int)N, (int)K, (hipStream_t)stream));
+}
+
 forge_status forge_debug_mfma_peak(float* out, int32_t blocks, int32_t iters, void* stream) {
   if (blocks < 1 || blocks > (1 << 20) || iters < 1 || iters > (1 << 20)) return FORGE_E_SHAPE;
   if (!out) return FORGE_E_NULL;

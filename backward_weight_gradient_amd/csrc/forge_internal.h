@@ -225,6 +225,7 @@ hipError_t launch_debug_e4m3(const float* in, uint8_t* out, uint32_t n, hipStrea
 hipError_t launch_debug_quant(const float* in, uint8_t* codes, float* scales, int rows, int cols, int fmt,
                               bool positive, int block, hipStream_t stream);
 hipError_t launch_debug_copy(const void* src, void* dst, uint64_t bytes, hipStream_t stream);
+hipError_t launch_debug_state_stream(uint16_t* W, float* m, float* v, int N, int K, hipStream_t stream);
 hipError_t launch_debug_mfma(float* out, int blocks, int iters, hipStream_t stream);
 
 }  // namespace forge

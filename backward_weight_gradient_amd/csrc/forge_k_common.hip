@@ -120,6 +120,63 @@ __global__ void __launch_bounds__(256) k_debug_mfma(float* __restrict__ out, int
   out[(uint64_t)blockIdx.x * 256u + threadIdx.x] = acc[0][0] + acc[1][0] + acc[2][0] + acc[3][0];
 }
 
+// Streaming ceiling of the fused step's own state traffic: W bf16, m and v
+// fp32 [N, K] read and written once (20 bytes per element) in 128 x 128
+// tiles, one 256-thread workgroup per tile, tiles in row-major order, each
+// thread one 4-element segment per row pass, 8 passes in flight, 16-byte
+// (8-byte for W) non-temporal accesses -- the access pattern of the
+// epilogue with no gradient and no arithmetic beyond a trivial update
+// (m' = m + 1, v' = v + 1, W' = W with its bit pattern incremented), so that
+// the kernel cannot be folded away.  Requires N % 128 == K % 128 == 0.
+__global__ void __launch_bounds__(256) k_debug_state_stream(uint16_t* __restrict__ W, float* __restrict__ m,
+                                                           float* __restrict__ v, int N, int K) {
+  constexpr int PASSES = 16, RPP = 8, DEPTH = 8;    // 128 rows, 8 per pass (32 segments of 4 per row)
+  const int tk = K / TILE;
+  const int ti = (int)blockIdx.x / tk, tj = (int)blockIdx.x - ti * tk;
+  const int t = threadIdx.x;
+  const int64_t q = (int64_t)tj * TILE + 4 * (t & 31);
+  const int64_t r0 = (int64_t)ti * TILE + (t >> 5);
+  u32x2 pw[DEPTH];
+  f32x4 pm[DEPTH], pv[DEPTH];
+#pragma unroll
+  for (int s = 0; s < DEPTH; ++s) {
+    const int64_t o = (r0 + s * RPP) * K + q;
+    pw[s] = ld_nt<u32x2>(W + o);
+    pm[s] = ld_nt<f32x4>(m + o);
+    pv[s] = ld_nt<f32x4>(v + o);
+  }
+#pragma unroll
+  for (int s = 0; s < PASSES; ++s) {
+    const int slot = s % DEPTH;
+    u32x2 w = pw[slot];
+    f32x4 mm = pm[slot], vv = pv[slot];
+    const int64_t o = (r0 + s * RPP) * K + q;
+    if (s + DEPTH < PASSES) {
+      const int64_t on = (r0 + (s + DEPTH) * RPP) * K + q;
+      pw[slot] = ld_nt<u32x2>(W + on);
+      pm[slot] = ld_nt<f32x4>(m + on);
+      pv[slot] = ld_nt<f32x4>(v + on);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      mm[i] = mm[i] + 1.f;
+      vv[i] = vv[i] + 1.f;
+    }
+    w[0] += 0x00010001u;
+    w[1] += 0x00010001u;
+    st_nt<u32x2>(W + o, w);
+    st_nt<f32x4>(m + o, mm);
+    st_nt<f32x4>(v + o, vv);
+  }
+}
+
+hipError_t launch_debug_state_stream(uint16_t* W, float* m, float* v, int N, int K, hipStream_t st) {
+  if (N == 0 || K == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_debug_state_stream, dim3((unsigned)((N / TILE) * (K / TILE))), dim3(256), 0, st, W, m, v, N,
+                     K);
+  return hipGetLastError();
+}
+
 hipError_t launch_debug_copy(const void* src, void* dst, uint64_t bytes, hipStream_t st) {
   if (bytes == 0) return hipSuccess;
   const uint64_t n16 = bytes / 16u;

@@ -104,13 +104,17 @@ def layer_bytes(N, K, bt):
     return 20 * P + 2 * bt * (N + K)
 
 
+# the sources the timed kernel (k_fused_group for AdamW) is built from
+HEADLINE_SOURCES = ("forge_device.h", "forge_internal.h", "forge_k_adamw.hip")
+
+
 def kernel_sha():
-    """sha256 over the device sources (the kernels and their launchers)."""
+    """sha256 over the sources of the timed kernel and its launcher (a change
+    to any of them voids counter readings taken before it)."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(KERNEL_DIR)):
-        if name.endswith((".h", ".hip")):
-            with open(os.path.join(KERNEL_DIR, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in HEADLINE_SOURCES:
+        with open(os.path.join(KERNEL_DIR, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
@@ -483,18 +487,78 @@ def measured_ceilings(F, reps=5):
 
     t_copy = timed(lambda: F.forge_debug_copy(src, dst))
     del src, dst
+    # the fused step's own state traffic (bf16 W, fp32 m and v, 20 B per element) through the
+    # epilogue's access pattern with nothing computed: gate_proj-sized, 1.17 GB moved
+    N, K = 14336, 4096
+    Ws = torch.zeros((N, K), device="cuda", dtype=torch.bfloat16)
+    ms_ = torch.zeros((N, K), device="cuda", dtype=torch.float32)
+    vs_ = torch.zeros((N, K), device="cuda", dtype=torch.float32)
+    t_state = timed(lambda: F.forge_debug_state_stream(Ws, ms_, vs_))
+    del Ws, ms_, vs_
     blocks, iters = 2048, 4000
     out = torch.empty(256 * blocks, device="cuda")
     t_mfma = timed(lambda: F.forge_debug_mfma_peak(out, blocks, iters))
     del out
     torch.cuda.empty_cache()
     gbs = 2 * n / t_copy / 1e9
+    gbs_state = 20.0 * N * K / t_state / 1e9
     tflops = blocks * 4 * iters * 131072 / t_mfma / 1e12
     return {"hbm_copy_gbs": round(gbs, 1), "hbm_copy_frac_of_spec": round(gbs / HBM_PEAK_GBS, 4),
+            "hbm_state_stream_gbs": round(gbs_state, 1),
+            "hbm_state_stream_frac_of_spec": round(gbs_state / HBM_PEAK_GBS, 4),
+            "state_stream": "forge_debug_state_stream: bf16 W, fp32 m, v [14336, 4096] read and written once "
+                            "(20 B per element) in the epilogue's 128 x 128 tile pattern, nothing computed",
             "mfma_bf16_tflops": round(tflops, 1), "mfma_frac_of_spec": round(tflops / BF16_PEAK_TFLOPS, 4),
             "copy": "1 GiB device copy, 16-byte non-temporal loads and stores, a contiguous chunk per workgroup "
                     "(2 GiB moved)",
             "mfma": f"{blocks} workgroups x 4 waves x {iters} rounds of 4 independent 32x32x16 bf16 MFMAs"}
+
+
+def library_gemm_reference(synth, L, layers, reps=5):
+    """The same GEMMs through hipBLASLt (torch.mm, bf16 in, bf16 out, fp32
+    accumulation), timed beside the library's kernels: dX = dY W for the
+    seven layers at BT = 512, and the weight gradient dY^T X alone (no
+    optimizer step, G stored) for down_proj and lm_head at BT = 8192.  Each
+    operand is made contiguous in the layout torch.mm reads best
+    (row-major A and B, no transposed views)."""
+    import torch
+    out = {}
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return sorted(ts)[len(ts) // 2]
+
+    dx = {}
+    for name in layers:
+        d = L[name]
+        dY, W = d["dY"], d["W"]
+        o = torch.empty((dY.shape[0], W.shape[1]), device="cuda", dtype=torch.bfloat16)
+        ms = timed(lambda: torch.mm(dY, W, out=o))
+        dx[name] = round(1e3 * ms, 1)
+        del o
+    out["dgrad_bt512_us"] = dx
+    out["dgrad_bt512_seven_layers_us"] = round(sum(dx.values()), 1)
+    for name, (N, K) in (("down_proj", (4096, 14336)), ("lm_head", (128256, 4096))):
+        bt = 8192
+        X, dY = synth.activations(4, bt, N, K, STEP_T, device="cuda")
+        dYt = dY.t().contiguous()                    # [N, BT]: G = dY^T X as a plain NN product
+        G = torch.empty((N, K), device="cuda", dtype=torch.bfloat16)
+        ms = timed(lambda: torch.mm(dYt, X, out=G))
+        tf = 2.0 * bt * N * K / (ms * 1e-3) / 1e12
+        out[f"wgrad_gemm_{name}_bt{bt}"] = {"us": round(1e3 * ms, 1), "tflops": round(tf, 1),
+                                           "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4)}
+        del X, dY, dYt, G
+        torch.cuda.empty_cache()
+    return out
 
 
 def cpu_model():
@@ -812,12 +876,15 @@ def main():
         extras["grad_accumulation_gate_proj"] = accumulation_sweep(F, synth, h)
     if not args.no_mfma_sweep:
         extras["compute_bound_sweep"] = mfma_sweep(F, synth, h)
+    if not args.no_dgrad and not args.no_mfma_sweep:
+        extras["hipblaslt_reference"] = library_gemm_reference(synth, L, layers)
 
     cpu = None
     if not args.no_ceilings:
         c = measured_ceilings(F)
         extras["measured_ceilings"] = c
         extras["roofline_frac_of_measured_hbm"] = round(achieved_gbs / c["hbm_copy_gbs"], 4)
+        extras["roofline_frac_of_state_stream"] = round(achieved_gbs / c["hbm_state_stream_gbs"], 4)
         for v in extras.get("compute_bound_sweep", {}).values():
             v["mfma_frac_of_measured"] = round(v["tflops"] / c["mfma_bf16_tflops"], 4)
 

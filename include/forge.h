@@ -446,6 +446,20 @@ forge_status forge_debug_quant(const float* in, uint8_t* codes, float* scales, i
 forge_status forge_debug_copy(const void* src, void* dst, int64_t bytes, void* stream);
 
 /*
+ * forge_debug_state_stream -- measurement hook for the HBM roofline of the
+ * fused step's own traffic: streams a bf16 W and fp32 m, v [N, K] (dense,
+ * row-major) through the epilogue's access pattern -- 128 x 128 tiles in
+ * row-major order, one 256-thread workgroup per tile, 16-byte non-temporal
+ * accesses (8-byte for W), 8 row passes in flight -- reading and writing
+ * every element once (20 bytes per element) with no gradient and a trivial
+ * update (m and v incremented by 1, W's bit pattern by 1).  Device
+ * pointers: W 8-byte aligned, m and v 16-byte aligned, pairwise disjoint.
+ * N and K multiples of 128, N * K < 2^32.  Errors: E_SHAPE, E_NULL,
+ * E_ALIGN, E_ALIAS, E_HIP.
+ */
+forge_status forge_debug_state_stream(uint16_t* W, float* m, float* v, int64_t N, int64_t K, void* stream);
+
+/*
  * forge_debug_mfma_peak -- measurement hook for the matrix-core roofline:
  * `blocks` workgroups of 4 waves; every wave runs `iters` rounds of four
  * independent v_mfma_f32_32x32x16_bf16 (32,768 flops each) on register

@@ -564,3 +564,13 @@ def test_dgrad_noalloc_validation():
     assert nd(None, ctypes.byref(W), ctypes.byref(dX), None) == F.FORGE_E_NULL
     alias = F.mat_raw(addr(1), F.FORGE_BF16, 512, 8064)
     assert nd(ctypes.byref(dY), ctypes.byref(W), ctypes.byref(alias), None) == F.FORGE_E_ALIAS
+
+
+def test_state_stream_hook_argument_errors():
+    f = F.lib.forge_debug_state_stream
+    assert f(addr(0), addr(1), addr(2), 128, 100, None) == F.FORGE_E_SHAPE        # K % 128
+    assert f(addr(0), addr(1), addr(2), 65536, 65536, None) == F.FORGE_E_SHAPE    # 2^32 elements
+    assert f(None, addr(1), addr(2), 128, 128, None) == F.FORGE_E_NULL
+    assert f(addr(0) + 4, addr(1), addr(2), 128, 128, None) == F.FORGE_E_ALIGN
+    assert f(addr(0), addr(0) + 1024, addr(2), 128, 128, None) == F.FORGE_E_ALIAS
+    assert f(None, None, None, 0, 128, None) == F.FORGE_OK
