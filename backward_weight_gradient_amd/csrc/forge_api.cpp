@@ -450,7 +450,7 @@ forge_status forge_dgrad_fp8w(const forge_mat* dY, const forge_state* W, forge_m
   bool fast = false;
   const forge_status st = check_dgrad(dY, &W->q, dX, g, fast, W);
   if (st != FORGE_OK) return st;
-  return hip_status(launch_dgrad(g, false, (hipStream_t)stream));
+  return hip_status(launch_dgrad_fp8w(g, (hipStream_t)stream));
 }
 
 forge_status forge_wgrad_step_group(const forge_layer* layers, int32_t n, const forge_hyper* h, int64_t step,

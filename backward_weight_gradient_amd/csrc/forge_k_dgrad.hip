@@ -380,6 +380,159 @@ __global__ void __launch_bounds__(NT) k_dgrad_generic(const DgArgs g) {
   }
 }
 
+// ------------------------------------------------------------------------
+// dX from an E4M3 weight with block scales on the matrix cores.  Each chunk
+// of 16 reduction elements is staged in LDS as fp32: dY widened from bf16
+// (exact), the weight decoded exactly to the value the step stores (E4M3
+// value of the code x its block's scale, one fp32 product); then
+// v_mfma_f32_32x32x2_f32 accumulates in fp32, a sum of fp32 products in a
+// fixed order per element (within the fp32 summation bound like the plain
+// kernel).  One TM x 128 dX tile per 256-thread workgroup (TM = 64: 4 waves
+// in a 2 x 2 arrangement of 32 x 64; TM = 32, when 64-token tiles would not
+// give every CU two workgroups: 1 x 4 of 32 x 32), register-staged double
+// buffering.  LDS rows are padded so that the two half-waves of a fragment
+// read (reduction rows k and k + 1) fall 32 banks apart.  bf16 dY, any
+// leading dimensions, ragged BT, N and K (K a multiple of the block, >= 32).
+// ------------------------------------------------------------------------
+namespace {
+constexpr int F8_TN = 128, F8_R = 16;
+constexpr int F8_BP = 160;                 // LDS row pitch of W's chunk in floats (rows k, k + 1: 32 banks apart)
+
+// TM-token tiles (64 or 32): waves in a (TM / 32) x (4 / (TM / 32)) arrangement of 32-token parts.
+template <int TM>
+struct Fp8wShape {
+  static constexpr int WR = TM / 32;                 // wave rows
+  static constexpr int WCN = 4 / WR;                 // wave columns
+  static constexpr int BJ = F8_TN / (32 * WCN);      // 32-column blocks per wave
+  static constexpr int AE = TM * F8_R / NT;          // dY elements staged per thread (4 or 2)
+  static constexpr int AP = TM % 64 == 32 ? TM : TM + 32;   // LDS row pitch of dY's chunk: 32 banks mod 64
+};
+
+template <int TM>
+struct Fp8wStage {
+  float a[Fp8wShape<TM>::AE];   // dY[tok][n .. n + AE - 1] of this thread, widened
+  float b[8];                   // W[n][col .. col + 7] of this thread, decoded
+};
+
+template <int TM>
+__device__ __forceinline__ void f8_load(const DgArgs& g, int tok0, int col0, int n0, Fp8wStage<TM>& st) {
+  using SH = Fp8wShape<TM>;
+  constexpr int PER = F8_R / SH::AE;                 // threads per token row
+  const int t = threadIdx.x;
+  {   // dY: token row t / PER, reduction elements AE (t % PER) ..
+    const int tok = tok0 + t / PER, n = n0 + SH::AE * (t % PER);
+    const uint16_t* p = static_cast<const uint16_t*>(g.dY) + (int64_t)tok * g.lddy + n;
+#pragma unroll
+    for (int i = 0; i < SH::AE; ++i)
+      st.a[i] = (tok < g.BT && n + i < g.N) ? __uint_as_float((uint32_t)p[i] << 16) : 0.f;
+  }
+  {   // W: reduction row t / 16, columns 8 (t % 16) .. + 7 (one block: the block is >= 32)
+    const int n = n0 + (t >> 4), col = col0 + 8 * (t & 15);
+    if (n < g.N && col < g.K) {
+      const uint8_t* p = static_cast<const uint8_t*>(g.W) + (int64_t)n * g.ldw + col;
+      uint32_t w0, w1;
+      if ((reinterpret_cast<uintptr_t>(p) & 7) == 0) {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+        w0 = w[0];
+        w1 = w[1];
+      } else {
+        w0 = p[0] | (p[1] << 8) | (p[2] << 16) | ((uint32_t)p[3] << 24);
+        w1 = p[4] | (p[5] << 8) | (p[6] << 16) | ((uint32_t)p[7] << 24);
+      }
+      const int bsh = __builtin_ctz((unsigned)g.wblock);
+      const float sc = g.wsc[(int64_t)n * (g.K >> bsh) + (col >> bsh)];
+      e4m3_unpack4(w0, st.b);
+      e4m3_unpack4(w1, st.b + 4);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) st.b[i] *= sc;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) st.b[i] = 0.f;
+    }
+  }
+}
+
+template <int TM>
+__device__ __forceinline__ void f8_store(const Fp8wStage<TM>& st, float* sA, float* sB) {
+  using SH = Fp8wShape<TM>;
+  constexpr int PER = F8_R / SH::AE;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < SH::AE; ++i) sA[(SH::AE * (t % PER) + i) * SH::AP + t / PER] = st.a[i];
+  float* b = sB + (t >> 4) * F8_BP + 8 * (t & 15);
+  *reinterpret_cast<f32x4*>(b) = f32x4{st.b[0], st.b[1], st.b[2], st.b[3]};
+  *reinterpret_cast<f32x4*>(b + 4) = f32x4{st.b[4], st.b[5], st.b[6], st.b[7]};
+}
+}  // namespace
+
+template <int TM>
+__global__ void __launch_bounds__(NT) k_dgrad_fp8w(const DgArgs g) {
+  using SH = Fp8wShape<TM>;
+  __shared__ __attribute__((aligned(16))) float sA[2][F8_R * SH::AP];
+  __shared__ __attribute__((aligned(16))) float sB[2][F8_R * F8_BP];
+  const int tiles_k = (g.K + F8_TN - 1) / F8_TN;
+  const int ti = (int)blockIdx.x / tiles_k, tj = (int)blockIdx.x - ti * tiles_k;
+  const int tok0 = ti * TM, col0 = tj * F8_TN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wr = wave / SH::WCN, wc = wave % SH::WCN;
+  f32x16 acc[SH::BJ];
+#pragma unroll
+  for (int bj = 0; bj < SH::BJ; ++bj)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[bj][e] = 0.f;
+  const int nk = (g.N + F8_R - 1) / F8_R;
+  Fp8wStage<TM> st;
+  if (nk > 0) {
+    f8_load<TM>(g, tok0, col0, 0, st);
+    f8_store<TM>(st, sA[0], sB[0]);
+  }
+  __syncthreads();
+  for (int kc = 0; kc < nk; ++kc) {
+    const int cur = kc & 1;
+    if (kc + 1 < nk) f8_load<TM>(g, tok0, col0, (kc + 1) * F8_R, st);
+    const float* A = sA[cur];
+    const float* B = sB[cur];
+#pragma unroll
+    for (int kk = 0; kk < F8_R / 2; ++kk) {
+      const int k = 2 * kk + (lane >> 5);
+      const float fa = A[k * SH::AP + wr * 32 + (lane & 31)];
+#pragma unroll
+      for (int bj = 0; bj < SH::BJ; ++bj) {
+        const float fb = B[k * F8_BP + wc * (32 * SH::BJ) + bj * 32 + (lane & 31)];
+        acc[bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa, fb, acc[bj], 0, 0, 0);
+      }
+    }
+    if (kc + 1 < nk) f8_store<TM>(st, sA[cur ^ 1], sB[cur ^ 1]);
+    __syncthreads();
+  }
+  // lane l, register 4j + i of a 32 x 32 block: row 8j + 4(l / 32) + i, column l % 32
+#pragma unroll
+  for (int bj = 0; bj < SH::BJ; ++bj)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int tok = tok0 + wr * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      const int col = col0 + wc * (32 * SH::BJ) + bj * 32 + (lane & 31);
+      if (tok >= g.BT || col >= g.K) continue;
+      const int64_t o = (int64_t)tok * g.ldx + col;
+      if (g.dx_fmt == FMT_F32) static_cast<float*>(g.dX)[o] = acc[bj][e];
+      else static_cast<uint16_t*>(g.dX)[o] = (uint16_t)bf16_rne_bits(acc[bj][e]);
+    }
+}
+
+// 32-token tiles when 64-token tiles would not give every CU two workgroups.
+hipError_t launch_dgrad_fp8w(const DgArgs& g, hipStream_t st) {
+  if (g.BT == 0 || g.K == 0) return hipSuccess;
+  if (g.in_fmt != FMT_BF16 || g.w_fmt != FMT_E4M3 || g.wblock < 32) return launch_dgrad(g, false, st);
+  const int64_t tk = (g.K + F8_TN - 1) / F8_TN;
+  const int64_t t64 = ((g.BT + 63) / 64) * tk;
+  if (t64 >= 512) {
+    hipLaunchKernelGGL(k_dgrad_fp8w<64>, dim3((unsigned)t64), dim3(NT), 0, st, g);
+  } else {
+    hipLaunchKernelGGL(k_dgrad_fp8w<32>, dim3((unsigned)(((g.BT + 31) / 32) * tk)), dim3(NT), 0, st, g);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_dgrad(const DgArgs& g, bool fast, hipStream_t st) {
   if (g.BT == 0 || g.K == 0) return hipSuccess;
   if (fast) {

@@ -107,11 +107,15 @@ def test_fp8_weight_gate_proj_full_size(state):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("N,K,BT,dx", [(512, 512, 256, torch.bfloat16), (130, 256, 77, torch.float32),
-                                       (14336, 4096, 512, torch.bfloat16)])
-def test_fp8_weight_dgrad(N, K, BT, dx):
-    _say(f"case: FP8 W dX {N}x{K} BT{BT} {dx}")
+@pytest.mark.parametrize("N,K,BT,dx,dy32", [(512, 512, 256, torch.bfloat16, False),
+                                            (130, 256, 77, torch.float32, False),   # ragged tokens, N, K
+                                            (97, 384, 130, torch.bfloat16, True),   # fp32 dY: the plain kernel
+                                            (14336, 4096, 512, torch.bfloat16, False)])
+def test_fp8_weight_dgrad(N, K, BT, dx, dy32):
+    _say(f"case: FP8 W dX {N}x{K} BT{BT} {dx} dY {'f32' if dy32 else 'bf16'}")
     L = make_layer(75, N, K, BT, 2, _spec("adamw", "f32"), gen_device="cuda" if N > 4096 else "cpu")
+    if dy32:
+        L.dY = L.dY.float()
     dX = torch.full((BT, K), float("nan"), device="cuda", dtype=dx)
     F.forge_dgrad_fp8w(L.dY, L.forge_w(), dX)
     torch.cuda.synchronize()
