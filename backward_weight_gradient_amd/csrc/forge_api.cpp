@@ -393,7 +393,7 @@ KArgs make_args(const forge_mat* X, const forge_mat* dY, forge_mat* W, forge_sta
   c.keyW = sr_key(seed, (uint64_t)step, 0);
   c.keyM = sr_key(seed, (uint64_t)step, 1);
   c.keyV = sr_key(seed, (uint64_t)step, 2);
-  c.sr = h->round == FORGE_ROUND_SR ? 1 : 0;
+  c.sr = h->round == FORGE_ROUND_SR ? 0xFFFFFFFFu : 0u;
   return a;
 }
 

@@ -65,53 +65,60 @@ constexpr uint32_t GOLDEN = 0x9E3779B9u;
 // ------------------------------------------------------------------------
 // Rounding helpers (paper, Appendix C)
 // ------------------------------------------------------------------------
-// MurmurHash3 32-bit finaliser (Appleby, public domain).
-__device__ __forceinline__ uint32_t fmix32(uint32_t h) {
+// The 32-bit word whose top 16 bits are the SR bits of an element, the top
+// half of fmix32(key ^ idx_mul), fmix32 being MurmurHash3's 32-bit
+// finaliser (Appleby, public domain): xor-shifts by 16, 13, 16 around
+// multiplies by 0x85EBCA6B and 0xC2B2AE35.  Its last xor-shift changes only
+// the low half, so it is left out.  Callers that round
+// consecutive indices pass idx * 0x9E3779B9 (mod 2^32) directly and step it
+// by adding the constant.
+__device__ __forceinline__ uint32_t sr_word(uint32_t key, uint32_t idx_mul) {
+  uint32_t h = key ^ idx_mul;
   h ^= h >> 16;
   h *= 0x85EBCA6Bu;
   h ^= h >> 13;
   h *= 0xC2B2AE35u;
-  h ^= h >> 16;
   return h;
 }
 
-// fp32 -> bf16 bit patterns, branch-free.  Round to nearest even adds
-// 0x7FFF plus the kept half's lowest bit and truncates.  Stochastic rounding
-// adds 16 random bits instead and truncates: the carry into the kept half
-// happens with probability (x - x_lo)/ULP.  Inf and NaN keep their pattern
-// (NaN made quiet) in both modes.
-// Written as masks and selects of constants: non-finite values add nothing
-// (infinity keeps its pattern, NaN gets the quiet bit), so no per-element
-// branch is needed.
-__device__ __forceinline__ uint32_t bf16_bits_add(float x, uint32_t add) {
-  const uint32_t u = __float_as_uint(x);
-  const uint32_t nonfinite = (u & 0x7F800000u) == 0x7F800000u ? 0xFFFFFFFFu : 0u;
-  const uint32_t quiet = (u & 0x7FFFFFFFu) > 0x7F800000u ? 0x40u : 0u;
-  return ((u + (add & ~nonfinite)) >> 16) | quiet;
-}
+// fp32 -> bf16 on the gfx950 converters.  v_cvt_pk_bf16_f32 rounds two
+// values to nearest even (a NaN becomes the quiet NaN with the same top
+// bits).  v_cvt_sr_bf16_f32 adds the top 16 bits of its second operand to
+// the 16 bits below the cut and truncates, which is the add-and-truncate
+// stochastic rounding: the carry into the kept half happens with
+// probability (x - x_lo)/ULP; infinities keep their pattern and NaN is made
+// quiet, as in round to nearest.  Both instructions agree bit for bit with
+// these definitions on every special pattern (zeros, subnormals, the
+// largest finite values, infinities, quiet and signalling NaNs) against
+// boundary random words and on 2 million random patterns.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
-  return bf16_bits_add(x, 0x7FFFu + ((__float_as_uint(x) >> 16) & 1u));
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x) { return bf16x2_rne(x, 0.f) & 0xFFFFu; }
 
-// The SR bits are the top half of fmix32(key ^ (idx * 0x9E3779B9)); callers
-// that round consecutive indices pass idx * 0x9E3779B9 (mod 2^32) directly
-// and step it by adding the constant.
-__device__ __forceinline__ uint32_t bf16_sr_bits_m(float x, uint32_t key, uint32_t idx_mul) {
-  return bf16_bits_add(x, fmix32(key ^ idx_mul) >> 16);
+// a -> low half, b -> high half, with random words ra, rb.
+__device__ __forceinline__ uint32_t bf16x2_sr(float a, float b, uint32_t ra, uint32_t rb) {
+  bf16x2_t s = {};
+  s = __builtin_amdgcn_cvt_sr_bf16_f32(s, a, ra, false);
+  s = __builtin_amdgcn_cvt_sr_bf16_f32(s, b, rb, true);
+  return __builtin_bit_cast(uint32_t, s);
 }
 __device__ __forceinline__ uint32_t bf16_sr_bits(float x, uint32_t key, uint32_t idx) {
-  return bf16_sr_bits_m(x, key, idx * GOLDEN);
+  return bf16x2_sr(x, 0.f, sr_word(key, idx * GOLDEN), 0u) & 0xFFFFu;
 }
 
-// sr != 0 (wave-uniform): stochastic rounding, else round to nearest even.
-// The empty asm keeps the increment in a register ahead of the finite test,
-// so the compiler selects instead of branching around the hash per element.
-__device__ __forceinline__ uint32_t bf16_store_bits(float x, int sr, uint32_t key, uint32_t idx_mul) {
-  const uint32_t rne_add = 0x7FFFu + ((__float_as_uint(x) >> 16) & 1u);
-  uint32_t add = sr ? fmix32(key ^ idx_mul) >> 16 : rne_add;
-  asm volatile("" : "+v"(add));
-  return bf16_bits_add(x, add);
+// Two stored bf16 patterns (a low, b high; flat indices idx_mul / GOLDEN and
+// the next one): stochastic rounding where srmask is all ones, round to
+// nearest even where it is zero.  Both are formed and the mask selects, so
+// the wave-uniform mode costs no branch.
+__device__ __forceinline__ uint32_t bf16x2_store(float a, float b, uint32_t srmask, uint32_t key,
+                                                 uint32_t idx_mul) {
+  const uint32_t s = bf16x2_sr(a, b, sr_word(key, idx_mul), sr_word(key, idx_mul + GOLDEN));
+  const uint32_t n = bf16x2_rne(a, b);
+  return (s & srmask) | (n & ~srmask);
 }
 
 __device__ __forceinline__ float bf16_val(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
@@ -944,10 +951,10 @@ __device__ __forceinline__ void dec4(const Raw4<FMT>& r, float* x) {
 }
 
 // Store 4 fp32 values as FMT (int8 formats go through quantize_chunk instead).
-// bf16: stochastic rounding when sr != 0 (idx_mul = flat index of the first
-// element times 0x9E3779B9), else round to nearest even.
+// bf16: stochastic rounding when sr is all ones (idx_mul = flat index of the
+// first element times 0x9E3779B9), round to nearest even when it is zero.
 template <int FMT, bool FAST>
-__device__ __forceinline__ void st4(void* row, const Seg& g, bool vec, const float* x, int sr, uint32_t key,
+__device__ __forceinline__ void st4(void* row, const Seg& g, bool vec, const float* x, uint32_t sr, uint32_t key,
                                     uint32_t idx_mul) {
   if constexpr (FMT == FMT_F32) {
     float* p = static_cast<float*>(row) + g.q;
@@ -959,13 +966,13 @@ __device__ __forceinline__ void st4(void* row, const Seg& g, bool vec, const flo
         if (i < g.nv) p[i] = x[i];
     }
   } else if constexpr (FMT == FMT_BF16) {
-    uint32_t b[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) b[i] = bf16_store_bits(x[i], sr, key, idx_mul + (uint32_t)i * GOLDEN);
+    const uint32_t lo = bf16x2_store(x[0], x[1], sr, key, idx_mul);
+    const uint32_t hi = bf16x2_store(x[2], x[3], sr, key, idx_mul + 2u * GOLDEN);
     uint16_t* p = static_cast<uint16_t*>(row) + g.q;
     if (FAST || (vec && g.nv == 4)) {
-      st_nt<u32x2>(p, u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)});
+      st_nt<u32x2>(p, u32x2{lo, hi});
     } else {
+      const uint32_t b[4] = {lo & 0xFFFFu, lo >> 16, hi & 0xFFFFu, hi >> 16};
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (i < g.nv) p[i] = (uint16_t)b[i];
@@ -997,7 +1004,7 @@ __device__ __forceinline__ void st4(void* row, const Seg& g, bool vec, const flo
 // (key `key`), else they are the nearest ones.
 template <int FMT, bool POSITIVE, bool SRW = false>
 __device__ __forceinline__ void quantize_chunk(const float (&x_in)[8], int block, const Seg (&sg)[2],
-                                               void* row_codes, bool vec, float* row_scales, int sr = 0,
+                                               void* row_codes, bool vec, float* row_scales, uint32_t sr = 0,
                                                uint32_t key = 0, const uint32_t* idx_mul = nullptr) {
   float x[8];
 #pragma unroll
@@ -1061,7 +1068,7 @@ __device__ __forceinline__ void quantize_chunk(const float (&x_in)[8], int block
         if (sr) {   // wave-uniform
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            y[i] = e4m3_sr_value(y[i], fmix32(key ^ (idx_mul[g] + (uint32_t)i * GOLDEN)) >> 16);
+            y[i] = e4m3_sr_value(y[i], sr_word(key, idx_mul[g] + (uint32_t)i * GOLDEN) >> 16);
         }
       }
       word = e4m3_pack4(y[0], y[1], y[2], y[3]);

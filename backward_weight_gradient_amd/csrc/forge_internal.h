@@ -43,7 +43,7 @@ struct EpiConst {
   float rc;        // RAdam, rectified: r_t sqrt(1 - beta2^t) / (1 - beta1^t)
   int32_t rect;    // RAdam: 1 once rho_t > 5 (adaptive step), else 0 (momentum step)
   uint32_t keyW, keyM, keyV;  // stochastic-rounding keys of the three tensors
-  int32_t sr;      // 1: stochastic rounding of bf16 stores, 0: round to nearest even
+  uint32_t sr;     // all ones: stochastic rounding of bf16 (and E4M3 weight) stores, 0: round to nearest even
 };
 
 // Everything a launch needs.  Pointers are device pointers; leading
