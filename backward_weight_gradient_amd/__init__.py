@@ -32,6 +32,7 @@ STATUS_NAMES = ["FORGE_OK", "FORGE_E_NULL", "FORGE_E_SHAPE", "FORGE_E_DTYPE", "F
 (FORGE_E_NULL, FORGE_E_SHAPE, FORGE_E_DTYPE, FORGE_E_ALIGN, FORGE_E_STEP, FORGE_E_HYPER,
  FORGE_E_ALIAS, FORGE_E_UNSUPPORTED, FORGE_E_HIP, FORGE_E_SCRATCH) = range(1, 11)
 FORGE_DGRAD_SCRATCH_BYTES = 32 << 20   # the static scratch of forge_dgrad_split_noalloc
+FORGE_QUOTIENT_COUNTS = 2048 * 8       # counters written by forge_debug_quotients
 
 FORGE_F32, FORGE_BF16, FORGE_S8, FORGE_U8, FORGE_E4M3 = 0, 1, 2, 3, 4
 FORGE_ADAMW, FORGE_LION, FORGE_SGDM, FORGE_NADAM, FORGE_RADAM, FORGE_RMSPROP, FORGE_ADAGRAD, FORGE_SGD = range(8)
@@ -131,6 +132,11 @@ def _load() -> ctypes.CDLL:
     lib.forge_backward_step_split.restype = st
     lib.forge_debug_e4m3.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
     lib.forge_debug_e4m3.restype = st
+    lib.forge_debug_e4m3_sr.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64,
+                                        ctypes.c_int64, ctypes.c_void_p]
+    lib.forge_debug_e4m3_sr.restype = st
+    lib.forge_debug_quotients.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    lib.forge_debug_quotients.restype = st
     lib.forge_debug_quant.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                       ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
     lib.forge_debug_quant.restype = st
@@ -430,6 +436,31 @@ def forge_debug_e4m3(inp, out, stream=None, check: bool = True) -> int:
     rc = lib.forge_debug_e4m3(inp.data_ptr(), out.data_ptr(), inp.numel(), _stream(stream))
     if check and rc != FORGE_OK:
         raise ForgeError(rc, "forge_debug_e4m3")
+    return rc
+
+
+def forge_debug_e4m3_sr(inp, out, seed: int, step: int, stream=None, check: bool = True) -> int:
+    """The FP8 weight store's stochastic rounding of a float32 tensor into a
+    uint8 code tensor, element i with the SR bits of flat index i (test hook)."""
+    if out.numel() != inp.numel() or out.element_size() != 1:
+        raise ValueError("forge_debug_e4m3_sr: out must be a 1-byte tensor with inp's element count")
+    rc = lib.forge_debug_e4m3_sr(inp.data_ptr(), out.data_ptr(), inp.numel(), seed & (2**64 - 1), step,
+                                 _stream(stream))
+    if check and rc != FORGE_OK:
+        raise ForgeError(rc, "forge_debug_e4m3_sr")
+    return rc
+
+
+def forge_debug_quotients(counts, stream=None, check: bool = True) -> int:
+    """Exhaustive check of the quantiser's fast scale / reciprocal quotients
+    against IEEE division (test hook); counts: int64 device tensor of
+    FORGE_QUOTIENT_COUNTS elements (see forge.h for the layout)."""
+    if counts.numel() != FORGE_QUOTIENT_COUNTS or counts.element_size() != 8 or not counts.is_contiguous():
+        raise ValueError("forge_debug_quotients: counts must be a contiguous 8-byte tensor of "
+                         "FORGE_QUOTIENT_COUNTS elements")
+    rc = lib.forge_debug_quotients(counts.data_ptr(), _stream(stream))
+    if check and rc != FORGE_OK:
+        raise ForgeError(rc, "forge_debug_quotients")
     return rc
 
 

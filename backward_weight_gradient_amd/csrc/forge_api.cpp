@@ -11,6 +11,7 @@
 
 static_assert(FORGE_GROUP_MAX == forge::GROUP_MAX, "group size of the ABI and the kernels");
 static_assert(FORGE_DGRAD_SCRATCH_BYTES == forge::DGRAD_SCRATCH_BYTES, "scratch size of the ABI and the kernels");
+static_assert(FORGE_QUOTIENT_COUNTS == forge::QUOTIENT_CHECK_BLOCKS * 8, "quotient check counters of the ABI and the kernel");
 
 namespace {
 
@@ -698,6 +699,23 @@ forge_status forge_debug_e4m3(const float* in, uint8_t* out, int64_t n, void* st
   if (!aligned(in, 4)) return FORGE_E_ALIGN;
   if (overlap(raw_range(in, (uint64_t)n * 4), raw_range(out, (uint64_t)n))) return FORGE_E_ALIAS;
   return hip_status(launch_debug_e4m3(in, out, (uint32_t)n, (hipStream_t)stream));
+}
+
+forge_status forge_debug_e4m3_sr(const float* in, uint8_t* out, int64_t n, uint64_t seed, int64_t step,
+                                 void* stream) {
+  if (n < 0 || (uint64_t)n >= (1ull << 32)) return FORGE_E_SHAPE;
+  if (step < 1) return FORGE_E_STEP;
+  if (n == 0) return FORGE_OK;
+  if (!in || !out) return FORGE_E_NULL;
+  if (!aligned(in, 4)) return FORGE_E_ALIGN;
+  if (overlap(raw_range(in, (uint64_t)n * 4), raw_range(out, (uint64_t)n))) return FORGE_E_ALIAS;
+  return hip_status(launch_debug_e4m3_sr(in, out, (uint32_t)n, sr_key(seed, (uint64_t)step, 0), (hipStream_t)stream));
+}
+
+forge_status forge_debug_quotients(uint64_t* counts, void* stream) {
+  if (!counts) return FORGE_E_NULL;
+  if (!aligned(counts, 8)) return FORGE_E_ALIGN;
+  return hip_status(launch_debug_quotients(reinterpret_cast<unsigned long long*>(counts), (hipStream_t)stream));
 }
 
 forge_status forge_debug_quant(const float* in, uint8_t* codes, float* scales, int64_t rows, int64_t cols,

@@ -316,6 +316,17 @@ __device__ __forceinline__ u32x2 tr_read(uint32_t lds_addr) {
   return v;
 }
 
+// The same read at a VGPR address plus an immediate byte offset (the
+// instruction's 16-bit offset field), so that reads at fixed distances share
+// one address register.
+template <int OFF>
+__device__ __forceinline__ u32x2 tr_read_at(uint32_t lds_addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  u32x2 v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(lds_addr), "i"(OFF));
+  return v;
+}
+
 // 32-bit LDS address of (token row t, feature f) in a region at `region`.
 __device__ __forceinline__ uint32_t tr_addr(uint32_t region, int t, int f) {
   return region + (uint32_t)MainBF16::off(t, f);
@@ -380,6 +391,18 @@ __device__ __forceinline__ void dma_accumulate(const KArgs& a, char* ring, int r
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[bi][bj][e] = 0.f;
   const int nk = (a.BT + M::TK - 1) / M::TK;
+  // byte offsets of this lane's fragment reads (token rows 0 and 4 of a
+  // k-step, frag_issue's mapping) within a stage, per 32-feature block b
+  uint32_t fofsA[2], fofsB[2];
+  {
+    const int t = 8 * (lane >> 5) + ((lane & 15) >> 2);
+    const int f = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      fofsA[b] = (uint32_t)MainBF16::off(t, wr * 64 + b * 32 + f);
+      fofsB[b] = (uint32_t)(M::OPB + MainBF16::off(t, wc * 64 + b * 32 + f));
+    }
+  }
   M ml;
   ml.init(a, row0, col0, gtid);
 #pragma unroll
@@ -392,16 +415,28 @@ __device__ __forceinline__ void dma_accumulate(const KArgs& a, char* ring, int r
     if (kc + M::S - 1 < nk) ml.issue(a, kc + M::S - 1, ring + ((kc + M::S - 1) % M::S) * M::STAGE);
     const uint32_t cur = lds0 + (uint32_t)((kc % M::S) * M::STAGE);
     // operand fragments of the chunk's two k-steps: [A0 lo, A0 hi, A1 lo, A1 hi, B0 lo, B0 hi, B1 lo, B1 hi]
+    // (frag_issue's addresses: the hi half is 4 token rows = 1024 bytes on,
+    // the second k-step 16 rows = 4096 bytes on, the swizzle unchanged)
     u32x2 f0[8], f1[8];
+    uint32_t pa[2], pb[2];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      frag_issue(cur, 0, wr * 64 + b * 32, lane, f0[2 * b], f0[2 * b + 1]);
-      frag_issue(cur + M::OPB, 0, wc * 64 + b * 32, lane, f0[4 + 2 * b], f0[4 + 2 * b + 1]);
+      pa[b] = cur + fofsA[b];
+      pb[b] = cur + fofsB[b];
     }
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      frag_issue(cur, 16, wr * 64 + b * 32, lane, f1[2 * b], f1[2 * b + 1]);
-      frag_issue(cur + M::OPB, 16, wc * 64 + b * 32, lane, f1[4 + 2 * b], f1[4 + 2 * b + 1]);
+      f0[2 * b] = tr_read_at<0>(pa[b]);
+      f0[2 * b + 1] = tr_read_at<1024>(pa[b]);
+      f0[4 + 2 * b] = tr_read_at<0>(pb[b]);
+      f0[4 + 2 * b + 1] = tr_read_at<1024>(pb[b]);
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      f1[2 * b] = tr_read_at<4096>(pa[b]);
+      f1[2 * b + 1] = tr_read_at<5120>(pa[b]);
+      f1[4 + 2 * b] = tr_read_at<4096>(pb[b]);
+      f1[4 + 2 * b + 1] = tr_read_at<5120>(pb[b]);
     }
     lds_wait<8>(f0);
 #pragma unroll
@@ -541,15 +576,6 @@ struct MainWideT {
     (issue_one<J>(a, kc, stage), ...);
   }
 };
-
-// Transposing LDS read at a VGPR address plus an immediate byte offset.
-template <int IMM>
-__device__ __forceinline__ u32x2 tr_read_at(uint32_t lds_addr) {
-  static_assert(IMM >= 0 && IMM < 65536, "ds offset field");
-  u32x2 v;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(lds_addr), "i"(IMM));
-  return v;
-}
 
 // ------------------------------------------------------------------------
 // The wide mainloop's waves: 8 in a 2 x 4 arrangement of 128 x 64 parts (8
@@ -809,24 +835,47 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float y0, float y1, float y2, flo
   return (uint32_t)w;
 }
 
-// Stochastic rounding of y onto the E4M3 grid (the FP8 weight store): |y|
-// goes to one of its two neighbouring grid values, away from zero with
+// Stochastic rounding onto the E4M3 grid (the FP8 weight store): |y| goes
+// to one of its two neighbouring grid values, away from zero with
 // probability equal to its fractional position between them (quantised to
-// 2^-16), saturating at 448, keeping the sign.  Normal range (|y| >= 2^-6,
-// 3 fraction bits): r * 2^4 is added to the 20 fp32 fraction bits E4M3 drops
-// and they are cleared.  Subnormal range (spacing 2^-9): z = floor(|y| 2^25)
-// (exact) and the value is ((z + r) >> 16) 2^-9.  The result lies on the
-// grid, so e4m3_pack4 encodes it exactly.
-__device__ __forceinline__ float e4m3_sr_value(float y, uint32_t r16) {
-  const uint32_t u = __float_as_uint(y);
-  const uint32_t au = u & 0x7FFFFFFFu;
-  const float ay = __uint_as_float(au);
-  const float normal = fminf(__uint_as_float((au + (r16 << 4)) & 0xFFF00000u), 448.f);
-  const uint32_t z = (uint32_t)(fminf(ay, 0x1p-6f) * 0x1p25f);          // < 2^19 where used
-  const float sub = (float)((z + r16) >> 16) * 0x1p-9f;
-  const float mag = ay >= 0x1p-6f ? normal : sub;
-  return __uint_as_float(__float_as_uint(mag) | (u & 0x80000000u));
+// 2^-16), saturating at 448 and keeping the sign.  In the normal range
+// (|y| >= 2^-6, 3 fraction bits) this adds r16 * 2^4 to the 20 fp32 fraction
+// bits E4M3 drops and clears them; in the subnormal range (spacing 2^-9) the
+// value is ((floor(|y| 2^25) + r16) >> 16) 2^-9.  gfx950's v_cvt_sr_fp8_f32
+// computes exactly this when its input is clamped to +-448 and its random
+// word carries r16 in the top half with the low half clear (it adds the top
+// 20 bits of the word); forge_debug_e4m3_sr exposes the function for a
+// bit-for-bit comparison with the definition.  r[i]: words whose top 16 bits
+// are the SR bits of element i.
+__device__ __forceinline__ uint32_t e4m3_sr_pack4(const float (&y)[4], const uint32_t (&r)[4]) {
+  const auto sat = [](float v) { return fminf(fmaxf(v, -448.f), 448.f); };
+  int w = 0;
+  w = __builtin_amdgcn_cvt_sr_fp8_f32(sat(y[0]), (int)(r[0] & 0xFFFF0000u), w, 0);
+  w = __builtin_amdgcn_cvt_sr_fp8_f32(sat(y[1]), (int)(r[1] & 0xFFFF0000u), w, 1);
+  w = __builtin_amdgcn_cvt_sr_fp8_f32(sat(y[2]), (int)(r[2] & 0xFFFF0000u), w, 2);
+  w = __builtin_amdgcn_cvt_sr_fp8_f32(sat(y[3]), (int)(r[3] & 0xFFFF0000u), w, 3);
+  return (uint32_t)w;
 }
+
+// Block scale a / QMAX and reciprocal QMAX / a, a > 0, as correctly rounded
+// fp32 quotients.  For 2^-64 <= a < 2^126 short fma sequences give them
+// (Markstein's residual correction): a / Q = q0 + fma(-Q, q0, a) / Q with
+// q0 = a * fp32(1/Q); Q / a from the hardware reciprocal refined by one
+// Newton step y, then q0 = Q * y and q0 + fma(-a, q0, Q) * y.  Both equal
+// IEEE division for every fp32 a in that range and each QMAX used (127,
+// 255, 448; checked exhaustively by forge_debug_quotients).  Outside it the
+// caller divides with IEEE division.
+__device__ __forceinline__ float quot_by_q(float a, float q, float rq) {
+  const float q0 = a * rq;
+  return fmaf(fmaf(-q, q0, a), rq, q0);
+}
+__device__ __forceinline__ float q_by_quot(float q, float a) {
+  float y = __builtin_amdgcn_rcpf(a);
+  y = fmaf(fmaf(-a, y, 1.f), y, y);
+  const float q0 = q * y;
+  return fmaf(fmaf(-a, q0, q), y, q0);
+}
+__device__ __forceinline__ bool quot_fast_range(float a) { return a >= 0x1p-64f && a < 0x1p126f; }
 
 __device__ __forceinline__ void e4m3_unpack4(uint32_t w, float* x) {
   const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);        // bytes 0, 1
@@ -994,13 +1043,18 @@ __device__ __forceinline__ void st4(void* row, const Seg& g, bool vec, const flo
 //           never becomes code 0 but the smallest subnormal 2^-9, which is
 //           what rounding max(y, 2^-9) gives for every positive y.
 // a is the block absmax; the scale and the reciprocal are correctly rounded
-// fp32 divisions.  A block whose absmax is below 2^-64 (a long-decayed
-// moment) would overflow QMAX / a; there the values and the reciprocal are
-// taken 2^64 times larger and smaller (exact scalings), which gives the
-// product x * (QMAX / a) as if the exponent range were unbounded -- the same
-// bits as the plain product wherever that one is finite.
-// SRW (the E4M3 weight store): when sr != 0 the codes are drawn by
-// e4m3_sr_value with the SR bits of flat indices idx_mul[g] / GOLDEN + i
+// fp32 quotients (quot_by_q / q_by_quot, IEEE division outside their
+// range).  A block whose absmax is below 2^-64 (a long-decayed moment)
+// would overflow QMAX / a; there the values and the reciprocal are taken
+// 2^64 times larger and smaller (exact scalings), which gives the product
+// x * (QMAX / a) as if the exponent range were unbounded -- the same bits as
+// the plain product wherever that one is finite.
+// With |x| <= a the scaled value y = x * (QMAX / a) stays below
+// QMAX (1 + 2^-23), so rint(y) never leaves -127..127 (S8) or 0..255 (U8):
+// S8 needs no clamp, and U8 codes come from v_cvt_pk_u8_f32, which rounds
+// to nearest even, clamps to 0..255 and inserts the byte.
+// SRW (the E4M3 weight store): when sr is nonzero the codes are drawn by
+// e4m3_sr_pack4 with the SR bits of flat indices idx_mul[g] / GOLDEN + i
 // (key `key`), else they are the nearest ones.
 template <int FMT, bool POSITIVE, bool SRW = false>
 __device__ __forceinline__ void quantize_chunk(const float (&x_in)[8], int block, const Seg (&sg)[2],
@@ -1010,14 +1064,16 @@ __device__ __forceinline__ void quantize_chunk(const float (&x_in)[8], int block
 #pragma unroll
   for (int i = 0; i < 8; ++i) x[i] = x_in[i];
   constexpr float QMAX = FMT == FMT_S8 ? 127.f : FMT == FMT_U8 ? 255.f : 448.f;
-  // absmax as the unsigned max of |x| bit patterns (the second moment is
-  // never negative, so for U8 this is max x)
+  constexpr float RQ = 1.f / QMAX;
+  // absmax as the unsigned max of |x| bit patterns (for non-negative floats
+  // the same order); the second moment is never negative, so with POSITIVE
+  // the patterns are compared as they are
   uint32_t ab[2];
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
     uint32_t m = 0u;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) m = max(m, __float_as_uint(x[4 * g + i]) & 0x7FFFFFFFu);
+    for (int i = 0; i < 4; ++i) m = max(m, POSITIVE ? __float_as_uint(x[4 * g + i]) : __float_as_uint(x[4 * g + i]) & 0x7FFFFFFFu);
     ab[g] = sg[g].ok ? m : 0u;
   }
   if (block == 128) {
@@ -1031,24 +1087,29 @@ __device__ __forceinline__ void quantize_chunk(const float (&x_in)[8], int block
   }
   const float a[2] = {__uint_as_float(ab[0]), __uint_as_float(ab[1])};
   float sc[2], inv[2];
-  sc[0] = a[0] > 0.f ? a[0] / QMAX : 0.f;
-  inv[0] = a[0] > 0.f ? QMAX / a[0] : 0.f;
+  sc[0] = quot_by_q(a[0], QMAX, RQ);                    // 0 for a = 0
+  inv[0] = a[0] > 0.f ? q_by_quot(QMAX, a[0]) : 0.f;
   if (block == 128) {
     sc[1] = sc[0];
     inv[1] = inv[0];
   } else {
-    sc[1] = a[1] > 0.f ? a[1] / QMAX : 0.f;
-    inv[1] = a[1] > 0.f ? QMAX / a[1] : 0.f;
+    sc[1] = quot_by_q(a[1], QMAX, RQ);
+    inv[1] = a[1] > 0.f ? q_by_quot(QMAX, a[1]) : 0.f;
   }
-  const bool tiny0 = a[0] > 0.f && a[0] < 0x1p-64f, tiny1 = a[1] > 0.f && a[1] < 0x1p-64f;
-  if (tiny0 || tiny1) {   // rare; skipped by the whole wave when no lane needs it
-    const bool tiny[2] = {tiny0, tiny1};
+  const bool rare0 = a[0] != 0.f && !quot_fast_range(a[0]), rare1 = a[1] != 0.f && !quot_fast_range(a[1]);
+  if (rare0 || rare1) {   // rare; skipped by the whole wave when no lane needs it
+    const bool rare[2] = {rare0, rare1};
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      if (!tiny[g]) continue;
-      inv[g] = QMAX / (a[g] * 0x1p64f);
+      if (!rare[g]) continue;
+      sc[g] = a[g] > 0.f ? a[g] / QMAX : 0.f;
+      if (a[g] > 0.f && a[g] < 0x1p-64f) {
+        inv[g] = QMAX / (a[g] * 0x1p64f);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x[4 * g + i] *= 0x1p64f;
+        for (int i = 0; i < 4; ++i) x[4 * g + i] *= 0x1p64f;
+      } else {
+        inv[g] = a[g] > 0.f ? QMAX / a[g] : 0.f;
+      }
     }
   }
   const int lpb = block == 32 ? 8 : 16;
@@ -1066,26 +1127,28 @@ __device__ __forceinline__ void quantize_chunk(const float (&x_in)[8], int block
       }
       if constexpr (SRW) {
         if (sr) {   // wave-uniform
+          uint32_t r[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            y[i] = e4m3_sr_value(y[i], sr_word(key, idx_mul[g] + (uint32_t)i * GOLDEN) >> 16);
+          for (int i = 0; i < 4; ++i) r[i] = sr_word(key, idx_mul[g] + (uint32_t)i * GOLDEN);
+          word = e4m3_sr_pack4(y, r);
+        } else {
+          word = e4m3_pack4(y[0], y[1], y[2], y[3]);
         }
+      } else {
+        word = e4m3_pack4(y[0], y[1], y[2], y[3]);
       }
-      word = e4m3_pack4(y[0], y[1], y[2], y[3]);
-    } else {
+    } else if constexpr (FMT == FMT_S8) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t c = (uint32_t)(int32_t)rintf(x[4 * g + i] * inv[g]) & 0xFFu;
+        word |= c << (8 * i);
+      }
+    } else {   // U8: code 0 only for an exact zero, a positive value at least 1
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float xv = x[4 * g + i];
-        float r = rintf(xv * inv[g]);
-        uint32_t c;
-        if (FMT == FMT_S8) {
-          r = fminf(fmaxf(r, -127.f), 127.f);
-          c = (uint32_t)(int32_t)r & 0xFFu;
-        } else {
-          r = fminf(fmaxf(r, 1.f), 255.f);
-          c = xv == 0.f ? 0u : (uint32_t)r;
-        }
-        word |= c << (8 * i);
+        const float y = xv != 0.f ? fmaxf(xv * inv[g], 1.f) : 0.f;
+        word = __builtin_amdgcn_cvt_pk_u8_f32(y, i, word);
       }
     }
     if (!sg[g].ok) continue;

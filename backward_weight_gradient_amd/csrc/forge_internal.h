@@ -222,6 +222,9 @@ hipError_t launch_debug_sr(const float* in, uint16_t* out, uint32_t n, uint32_t 
                            hipStream_t stream);
 // E4M3 rounding (nearest even, saturating) of n floats.
 hipError_t launch_debug_e4m3(const float* in, uint8_t* out, uint32_t n, hipStream_t stream);
+hipError_t launch_debug_e4m3_sr(const float* in, uint8_t* out, uint32_t n, uint32_t key, hipStream_t stream);
+constexpr int QUOTIENT_CHECK_BLOCKS = 2048;   // forge_debug_quotients: workgroups, 8 counters each
+hipError_t launch_debug_quotients(unsigned long long* counts, hipStream_t stream);
 // The 8-bit block quantiser of the epilogue (S8 / U8 / E4M3 codes and fp32
 // scales) on a dense [rows, cols] fp32 array; positive: the second-moment rule.
 hipError_t launch_debug_quant(const float* in, uint8_t* codes, float* scales, int rows, int cols, int fmt,

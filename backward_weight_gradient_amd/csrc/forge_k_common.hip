@@ -27,6 +27,58 @@ __global__ void k_debug_e4m3(const float* __restrict__ in, uint8_t* __restrict__
     if (i0 + k < n) out[i0 + k] = (uint8_t)((w >> (8 * k)) & 0xFFu);
 }
 
+// The FP8 weight store's stochastic rounding on its own, through the same
+// four-value packing: thread i rounds elements 4i .. 4i+3 with the SR bits
+// of flat indices 4i .. 4i+3 under `key` (zeros past the end, not stored).
+__global__ void k_debug_e4m3_sr(const float* __restrict__ in, uint8_t* __restrict__ out, uint32_t n, uint32_t key) {
+  const uint64_t i0 = 4ull * (blockIdx.x * (uint64_t)blockDim.x + threadIdx.x);
+  if (i0 >= n) return;
+  float y[4];
+  uint32_t r[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    y[k] = i0 + k < n ? in[i0 + k] : 0.f;
+    r[k] = sr_word(key, (uint32_t)(i0 + k) * GOLDEN);
+  }
+  const uint32_t w = e4m3_sr_pack4(y, r);
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (i0 + k < n) out[i0 + k] = (uint8_t)((w >> (8 * k)) & 0xFFu);
+}
+
+// Exhaustive check of the block quantiser's quotients: for every fp32 a in
+// [2^-64, 2^126) and QMAX in {127, 255, 448}, quot_by_q(a) against the IEEE
+// a / QMAX and q_by_quot(a) against the IEEE QMAX / a.  Workgroup b writes
+// its mismatch counts (a/127, 127/a, a/255, 255/a, a/448, 448/a) and the
+// number of a values it checked to counts[8 b .. 8 b + 6].
+__global__ void __launch_bounds__(256) k_debug_quotients(unsigned long long* __restrict__ counts) {
+  constexpr uint32_t LO = 0x1F800000u, HI = 0x7E800000u;   // 2^-64, 2^126
+  __shared__ unsigned long long part[7];
+  if (threadIdx.x < 7) part[threadIdx.x] = 0ull;
+  __syncthreads();
+  unsigned long long bad[6] = {0, 0, 0, 0, 0, 0}, seen = 0;
+  const uint32_t stride = gridDim.x * blockDim.x;   // HI + stride < 2^32: no wrap
+  for (uint32_t u = LO + blockIdx.x * blockDim.x + threadIdx.x; u < HI; u += stride) {
+    const float a = __uint_as_float(u);
+    ++seen;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const float q = k == 0 ? 127.f : k == 1 ? 255.f : 448.f;
+      const float rq = k == 0 ? 1.f / 127.f : k == 1 ? 1.f / 255.f : 1.f / 448.f;
+      float qv = q;
+      asm volatile("" : "+v"(qv));   // an opaque divisor: the division below is the IEEE one
+      bad[2 * k] += __float_as_uint(quot_by_q(a, q, rq)) != __float_as_uint(a / qv);
+      bad[2 * k + 1] += __float_as_uint(q_by_quot(q, a)) != __float_as_uint(qv / a);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 6; ++k)
+    if (bad[k]) atomicAdd(&part[k], bad[k]);
+  atomicAdd(&part[6], seen);
+  __syncthreads();
+  if (threadIdx.x < 7) counts[8ull * blockIdx.x + threadIdx.x] = part[threadIdx.x];
+}
+
 // The fused epilogue's 8-bit block quantiser on its own: quantize_chunk with
 // the epilogue's thread mapping (thread t of a 256-thread workgroup owns row
 // t / 16 of a 16-row slab and the two 4-element segments at columns
@@ -68,6 +120,18 @@ hipError_t launch_debug_quant(const float* in, uint8_t* codes, float* scales, in
     hipLaunchKernelGGL((k_debug_quant<FMT_E4M3, true>), grid, b, 0, st, in, codes, scales, rows, cols, block);
   else
     return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_e4m3_sr(const float* in, uint8_t* out, uint32_t n, uint32_t key, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const uint64_t threads = (n + 3ull) / 4ull;
+  hipLaunchKernelGGL(k_debug_e4m3_sr, dim3((unsigned)((threads + 255u) / 256u)), dim3(256), 0, st, in, out, n, key);
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_quotients(unsigned long long* counts, hipStream_t st) {
+  hipLaunchKernelGGL(k_debug_quotients, dim3(QUOTIENT_CHECK_BLOCKS), dim3(256), 0, st, counts);
   return hipGetLastError();
 }
 

@@ -420,6 +420,34 @@ forge_status forge_debug_sr_bf16(const float* in, uint16_t* out, int64_t n, uint
 forge_status forge_debug_e4m3(const float* in, uint8_t* out, int64_t n, void* stream);
 
 /*
+ * forge_debug_e4m3_sr -- test hook: the FP8 weight store's stochastic
+ * rounding onto the E4M3 grid (the reading of the paper's section 3.6 given
+ * with forge_wgrad_step_fp8w below) of n floats, out[i] = code of in[i] with
+ * the 16 SR bits of flat index i under the weight's key for (seed, step),
+ * through the same four-value packing the fused step uses.  Values beyond
+ * +-448 saturate.  Device pointers.  Errors: E_NULL, E_SHAPE (n < 0 or
+ * n >= 2^32), E_STEP (step < 1), E_ALIGN, E_ALIAS, E_HIP.
+ */
+forge_status forge_debug_e4m3_sr(const float* in, uint8_t* out, int64_t n, uint64_t seed, int64_t step,
+                                 void* stream);
+
+/*
+ * forge_debug_quotients -- test hook: an exhaustive check of the block
+ * quantiser's scale and reciprocal (correctly rounded fp32 a / QMAX and
+ * QMAX / a, paper section 2.3 and Appendix B) computed by short fma
+ * sequences: for every fp32 a in [2^-64, 2^126) and QMAX in {127, 255, 448}
+ * it compares them with IEEE division.  counts: device array of
+ * FORGE_QUOTIENT_COUNTS uint64, 8-byte aligned; group g (entries 8g .. 8g+7,
+ * g < FORGE_QUOTIENT_COUNTS / 8) receives the mismatch counts of a/127,
+ * 127/a, a/255, 255/a, a/448, 448/a and, in entry 8g+6, the number of a
+ * values it checked; entry 8g+7 is not written.  The sums over the groups
+ * give the totals (the checked counts add up to 2^126 - 2^-64 in fp32 bit
+ * patterns, 0x5F000000).  Errors: E_NULL, E_ALIGN, E_HIP.
+ */
+#define FORGE_QUOTIENT_COUNTS (2048 * 8)
+forge_status forge_debug_quotients(uint64_t* counts, void* stream);
+
+/*
  * forge_debug_quant -- test hook: the fused step's 8-bit block quantiser
  * (the store of an S8, U8 or E4M3 state: paper, section 2.3 and Appendix B
  * for int8, section 3.6 for FP8; the rules are those of forge_state above)

@@ -527,6 +527,25 @@ def test_debug_quant_argument_errors():
     assert q(None, None, None, 0, 128, F.FORGE_U8, 1, 128, None) == F.FORGE_OK
 
 
+def test_debug_e4m3_sr_and_quotient_hook_argument_errors():
+    f = F.lib.forge_debug_e4m3_sr
+    assert f(None, None, -1, 1, 1, None) == F.FORGE_E_SHAPE
+    assert f(None, None, 1 << 32, 1, 1, None) == F.FORGE_E_SHAPE
+    assert f(addr(0), addr(1), 10, 1, 0, None) == F.FORGE_E_STEP
+    assert f(None, addr(1), 10, 1, 1, None) == F.FORGE_E_NULL
+    assert f(addr(0) + 2, addr(1), 10, 1, 1, None) == F.FORGE_E_ALIGN
+    assert f(addr(0), addr(0) + 36, 10, 1, 1, None) == F.FORGE_E_ALIAS
+    assert f(None, None, 0, 1, 1, None) == F.FORGE_OK
+    q = F.lib.forge_debug_quotients
+    assert q(None, None) == F.FORGE_E_NULL
+    assert q(addr(0) + 4, None) == F.FORGE_E_ALIGN
+    import torch
+    with pytest.raises(ValueError):
+        F.forge_debug_quotients(torch.zeros(8, dtype=torch.int64))
+    with pytest.raises(ValueError):
+        F.forge_debug_e4m3_sr(torch.zeros(8), torch.zeros(7, dtype=torch.uint8), 1, 1)
+
+
 def test_binding_state_checks_the_scale_tensor():
     """The binding forwards a scale pointer only for a float32, contiguous
     tensor of exactly rows * cols / block elements on the codes' device."""

@@ -9,8 +9,9 @@ grid step; scales within 1e-5 or the hull of the block absmax; moments as in
 the other parity tests.  AdamW with every moment format, Lion and SGD-m,
 both rounding modes, blocks of 128, 64 and 32, several steps, ragged shapes,
 the 256 x 256 kernel (BT >= 2048) and gate_proj at full size on sampled
-rows.  forge_dgrad_fp8w against the oracle's fp64 product with the decoded
-weight.  Unsupported combinations and shapes are refused before anything
+rows.  The device's E4M3 stochastic rounding on its own, bit for bit
+(forge_debug_e4m3_sr).  forge_dgrad_fp8w against the oracle's fp64 product
+with the decoded weight.  Unsupported combinations and shapes are refused before anything
 is enqueued.
 """
 
@@ -45,6 +46,32 @@ def _spec(opt, state, block=128):
     m = None if opt not in F.KEEPS_M else ("s8" if state == "int8" else state)
     v = None if opt not in F.KEEPS_V else ("u8" if state == "int8" else state)
     return synth.LayerSpec("bf16", "e4m3", m, v, block=block)
+
+
+def test_e4m3_stochastic_rounding_hook_bit_exact():
+    """The device's E4M3 stochastic rounding (the FP8 weight store) against
+    the oracle's definition, bit for bit, element i with the SR bits of flat
+    index i under the weight's key: every grid point, midpoint and its
+    neighbours, the subnormal range densely, values just below and above the
+    normal/subnormal boundary 2^-6, saturation, signed zeros, random
+    magnitudes over the whole range."""
+    _say("case: E4M3 SR hook")
+    grid = O.e4m3_to_f64(np.arange(0x7F))
+    mids = (grid[:-1] + grid[1:]) / 2
+    rng = np.random.default_rng(21)
+    sub = rng.integers(0, 0x3C800000, 300000, dtype=np.int64).astype(np.uint32).view(np.float32)
+    x = np.concatenate([grid, mids, np.nextafter(mids, 0), np.nextafter(mids, 1e9),
+                        [448.0, 449.0, 464.0, 480.0, 1e30, 2.0 ** -6, np.nextafter(np.float32(2.0 ** -6), 0),
+                         2.0 ** -9, 2.0 ** -10, 2.0 ** -149],
+                        sub, rng.uniform(0, 448, 200000), 10.0 ** rng.uniform(-12, 3, 200000)]).astype(np.float32)
+    x = np.concatenate([x, -x, np.float32([0.0, -0.0])])
+    for seed, step in ((SEED, 1), (2**63 + 12345, 7)):
+        xin = torch.from_numpy(x).cuda()
+        out = torch.empty(x.size, device="cuda", dtype=torch.uint8)
+        F.forge_debug_e4m3_sr(xin, out, seed, step)
+        torch.cuda.synchronize()
+        r16 = O.sr_bits(O.sr_key(seed, step, 0), np.arange(x.size, dtype=np.uint64))
+        np.testing.assert_array_equal(out.cpu().numpy(), O.f32_to_e4m3_sr(x, r16))
 
 
 CASES = [("adamw", "f32"), ("adamw", "bf16"), ("adamw", "int8"), ("adamw", "e4m3"), ("lion", "f32"),

@@ -10,8 +10,10 @@ The inputs are built so that a plausible mistake fails: exact ties (the
 reciprocal exactly 1 or 8, values k + 1/2), all-zero blocks, positive values
 below half a step (the U8 floor to code 1), the absmax element, negative
 zero, a lone outlier, blocks whose absmax is below 2^-64, in the fp32
-subnormal range or near the fp32 maximum, and ragged row / column counts
-against the 16-row, 128-column work unit of the kernel.
+subnormal range, near or above 2^126 and up to the fp32 maximum, and
+ragged row / column counts against the 16-row, 128-column work unit of the
+kernel.  The fast scale / reciprocal quotients the quantiser uses are
+checked against IEEE division for every fp32 absmax in their range.
 """
 
 import sys
@@ -45,7 +47,7 @@ def _inputs(rows: int, cols: int, block: int, qmax: float, positive: bool, seed:
     nb = cols // block
     grid = O.e4m3_to_f64(np.arange(0x7F))
     for r in range(rows):
-        kind = r % 12
+        kind = r % 13
         for b in range(nb):
             blk = np.zeros(block, dtype=np.float64)
             if kind == 0:                                   # plain normal values
@@ -82,6 +84,9 @@ def _inputs(rows: int, cols: int, block: int, qmax: float, positive: bool, seed:
                 blk = rng.integers(-50, 50, block) * 2.0 ** -149
             elif kind == 10:                                # huge values
                 blk = rng.standard_normal(block) * 1e37
+            elif kind == 11:                                # absmax at or above 2^126
+                blk = rng.uniform(-3.4e38, 3.4e38, block)
+                blk[0] = 2.0 ** 126
             else:                                           # exactly on the code grid
                 blk = rng.integers(-int(qmax), int(qmax) + 1, block) * (0.37 / qmax)
             x[r, b * block:(b + 1) * block] = blk.astype(np.float32)
@@ -118,3 +123,19 @@ def test_quantiser_empty_and_rejected_calls_touch_nothing():
     assert F.forge_debug_quant(xin, codes, scales, F.FORGE_S8, True, 128, check=False) == F.FORGE_E_DTYPE
     torch.cuda.synchronize()
     assert int(codes.sum()) == 7 * 512 and float(scales.sum()) == 20.0
+
+
+def test_quantiser_quotients_equal_ieee_division_exhaustively():
+    """The block scale a / QMAX and reciprocal QMAX / a from short fma
+    sequences, compared with IEEE division for every fp32 a in [2^-64,
+    2^126) and QMAX in {127, 255, 448} (outside that range the quantiser
+    divides with IEEE division)."""
+    _say("case: quantiser quotients, exhaustive")
+    counts = torch.zeros(F.FORGE_QUOTIENT_COUNTS, dtype=torch.int64, device="cuda")
+    F.forge_debug_quotients(counts)
+    torch.cuda.synchronize()
+    c = counts.cpu().numpy().reshape(-1, 8)
+    assert int(c[:, 6].sum()) == 0x7E800000 - 0x1F800000          # every a in the range checked
+    names = ["a/127", "127/a", "a/255", "255/a", "a/448", "448/a"]
+    bad = {n: int(c[:, k].sum()) for k, n in enumerate(names)}
+    assert all(v == 0 for v in bad.values()), bad
