@@ -260,6 +260,10 @@ bool vec_ok(const void* p, int64_t ld, int elems, int es) {
   return p == nullptr || (aligned(p, elems * es) && (ld % elems) == 0);
 }
 
+// Row pitch small enough for the aligned epilogue's 32-bit per-thread
+// offsets (up to 32 rows of a pass, 2^26 bytes each, plus the columns).
+bool pitch_ok(int64_t ld, int es) { return (uint64_t)ld * (uint64_t)es <= (1ull << 26); }
+
 // dX = dY W: shapes, dtypes, limits, aliasing; fills the launch arguments.
 // wq: the weight as an E4M3 state (W == &wq->q), or NULL.
 forge_status check_dgrad(const forge_mat* dY, const forge_mat* W, const forge_mat* dX, DgArgs& g, bool& fast,
@@ -334,7 +338,7 @@ void acc_args(forge_mat* acc, KArgs& a) {
   a.dW = acc->data;
   a.lddw = acc->ld;
   a.dw_fmt = FMT_F32;
-  a.vec_dw = vec_ok(acc->data, acc->ld, 4, 4) ? 1 : 0;
+  a.vec_dw = (vec_ok(acc->data, acc->ld, 4, 4) && pitch_ok(acc->ld, 4)) ? 1 : 0;
 }
 
 KArgs make_args(const forge_mat* X, const forge_mat* dY, forge_mat* W, forge_state* m, forge_state* v,
@@ -347,9 +351,9 @@ KArgs make_args(const forge_mat* X, const forge_mat* dY, forge_mat* W, forge_sta
   if (v) { a.v = v->q.data; a.ldv = v->q.ld; a.vs = v->scale; }
   a.block = pl.block ? pl.block : 128;
   // 4-element state accesses (16 B fp32, 8 B bf16, 4 B int8)
-  bool vs = vec_ok(W->data, W->ld, 4, elem_size(pl.w_fmt));
-  if (m) vs = vs && vec_ok(m->q.data, m->q.ld, 4, elem_size(pl.m_fmt));
-  if (v) vs = vs && vec_ok(v->q.data, v->q.ld, 4, elem_size(pl.v_fmt));
+  bool vs = vec_ok(W->data, W->ld, 4, elem_size(pl.w_fmt)) && pitch_ok(W->ld, elem_size(pl.w_fmt));
+  if (m) vs = vs && vec_ok(m->q.data, m->q.ld, 4, elem_size(pl.m_fmt)) && pitch_ok(m->q.ld, elem_size(pl.m_fmt));
+  if (v) vs = vs && vec_ok(v->q.data, v->q.ld, 4, elem_size(pl.v_fmt)) && pitch_ok(v->q.ld, elem_size(pl.v_fmt));
   a.vec_state = vs ? 1 : 0;
   // scalars, in double, rounded once
   const double lr = h->lr, b1 = h->beta1, b2 = h->beta2, wd = h->weight_decay;
@@ -366,6 +370,7 @@ KArgs make_args(const forge_mat* X, const forge_mat* dY, forge_mat* W, forge_sta
   const int o = h->opt;
   const bool adam_like = o == FORGE_ADAMW || o == FORGE_NADAM || o == FORGE_RADAM;
   c.bc1 = adam_like ? (float)(1.0 / (1.0 - std::pow(b1, t))) : 1.0f;
+  c.lrbc1 = adam_like ? (float)(lr / (1.0 - std::pow(b1, t))) : 0.0f;
   c.bc2s = (o == FORGE_ADAMW || o == FORGE_NADAM) ? (float)(1.0 / std::sqrt(1.0 - std::pow(b2, t))) : 1.0f;
   if (o == FORGE_NADAM) {
     // momentum schedule mu_i = b1 (1 - 0.5 * 0.96^(psi i)), psi = 0.004, and
@@ -536,7 +541,7 @@ forge_status forge_wgrad_unfused(const forge_mat* X, const forge_mat* dY, forge_
   KArgs a = make_args(X, dY, W, m, v, h, step, seed, pl);
   a.dW = dW;
   a.dw_fmt = dW_dtype == FORGE_F32 ? FMT_F32 : FMT_BF16;
-  a.vec_dw = (pl.K % 4) == 0 ? 1 : 0;   // the workspace is 16-byte aligned with ld = K
+  a.vec_dw = ((pl.K % 4) == 0 && pitch_ok(pl.K, 4)) ? 1 : 0;   // the workspace is 16-byte aligned with ld = K
   hipError_t e = launch_gemm(a, pl.in_fmt, (hipStream_t)stream);
   if (e == hipSuccess) e = launch_step(a, pl.w_fmt, h->opt, pl.m_fmt, pl.v_fmt, (hipStream_t)stream);
   return hip_status(e);

@@ -42,6 +42,8 @@
 // root and reciprocal are the hardware instructions, the block-scale
 // divisions are correctly rounded.
 
+#include <type_traits>
+
 #include "forge_internal.h"
 
 namespace forge {
@@ -931,10 +933,11 @@ struct Seg {
   int q;        // first column
 };
 
+// seg: the segment's first element.
 template <int FMT, bool FAST>
-__device__ __forceinline__ void ld4(Raw4<FMT>& r, const void* row, const Seg& g, bool vec) {
+__device__ __forceinline__ void ld4(Raw4<FMT>& r, const void* seg, const Seg& g, bool vec) {
   if constexpr (FMT == FMT_F32) {
-    const float* p = static_cast<const float*>(row) + g.q;
+    const float* p = static_cast<const float*>(seg);
     if (FAST || (vec && g.nv == 4)) {
       r.v = ld_nt<f32x4>(p);
     } else {
@@ -942,7 +945,7 @@ __device__ __forceinline__ void ld4(Raw4<FMT>& r, const void* row, const Seg& g,
       for (int i = 0; i < 4; ++i) r.v[i] = i < g.nv ? p[i] : 0.f;
     }
   } else if constexpr (FMT == FMT_BF16) {
-    const uint16_t* p = static_cast<const uint16_t*>(row) + g.q;
+    const uint16_t* p = static_cast<const uint16_t*>(seg);
     if (FAST || (vec && g.nv == 4)) {
       r.v = ld_nt<u32x2>(p);
     } else {
@@ -952,7 +955,7 @@ __device__ __forceinline__ void ld4(Raw4<FMT>& r, const void* row, const Seg& g,
       r.v = u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
     }
   } else if constexpr (fmt_blocked(FMT)) {
-    const uint8_t* p = static_cast<const uint8_t*>(row) + g.q;
+    const uint8_t* p = static_cast<const uint8_t*>(seg);
     if (FAST || (vec && g.nv == 4)) {
       r.v = ld_nt<uint32_t>(p);
     } else {
@@ -999,14 +1002,32 @@ __device__ __forceinline__ void dec4(const Raw4<FMT>& r, float* x) {
   }
 }
 
-// Store 4 fp32 values as FMT (int8 formats go through quantize_chunk instead).
+// The codes of a block-scaled state as fp32 values, without the scale:
+// callers whose only use of the decoded state x is a product c * x fold the
+// scale into c (one multiply per segment instead of one per element).
+template <int FMT>
+__device__ __forceinline__ void dec4_codes(const Raw4<FMT>& r, float* x) {
+  static_assert(fmt_blocked(FMT), "block-scaled formats only");
+  if constexpr (FMT == FMT_S8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = (float)(int8_t)((r.v >> (8 * i)) & 0xFFu);
+  } else if constexpr (FMT == FMT_U8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = (float)((r.v >> (8 * i)) & 0xFFu);
+  } else {
+    e4m3_unpack4(r.v, x);
+  }
+}
+
+// Store 4 fp32 values as FMT at seg, the segment's first element (int8
+// formats go through quantize_chunk instead).
 // bf16: stochastic rounding when sr is all ones (idx_mul = flat index of the
 // first element times 0x9E3779B9), round to nearest even when it is zero.
 template <int FMT, bool FAST>
-__device__ __forceinline__ void st4(void* row, const Seg& g, bool vec, const float* x, uint32_t sr, uint32_t key,
+__device__ __forceinline__ void st4(void* seg, const Seg& g, bool vec, const float* x, uint32_t sr, uint32_t key,
                                     uint32_t idx_mul) {
   if constexpr (FMT == FMT_F32) {
-    float* p = static_cast<float*>(row) + g.q;
+    float* p = static_cast<float*>(seg);
     if (FAST || (vec && g.nv == 4)) {
       st_nt<f32x4>(p, f32x4{x[0], x[1], x[2], x[3]});
     } else {
@@ -1017,7 +1038,7 @@ __device__ __forceinline__ void st4(void* row, const Seg& g, bool vec, const flo
   } else if constexpr (FMT == FMT_BF16) {
     const uint32_t lo = bf16x2_store(x[0], x[1], sr, key, idx_mul);
     const uint32_t hi = bf16x2_store(x[2], x[3], sr, key, idx_mul + 2u * GOLDEN);
-    uint16_t* p = static_cast<uint16_t*>(row) + g.q;
+    uint16_t* p = static_cast<uint16_t*>(seg);
     if (FAST || (vec && g.nv == 4)) {
       st_nt<u32x2>(p, u32x2{lo, hi});
     } else {
@@ -1030,7 +1051,8 @@ __device__ __forceinline__ void st4(void* row, const Seg& g, bool vec, const flo
 }
 
 // Block-absmax quantisation of a chunk (two 4-element segments 64 columns
-// apart) to 8-bit codes with one fp32 scale per block.  block == 128: one
+// apart) to 8-bit codes with one fp32 scale per block.  codes[g]: segment
+// g's first code; scales[g]: the scale of the block segment g lies in.  block == 128: one
 // block spans both segments of the 16 lanes of a row; block 64 / 32: each
 // segment lies in its own block, shared by 16 / 8 adjacent lanes.  Every
 // lane of the wave must call this (DPP reductions).  8-bit states need
@@ -1058,8 +1080,9 @@ __device__ __forceinline__ void st4(void* row, const Seg& g, bool vec, const flo
 // (key `key`), else they are the nearest ones.
 template <int FMT, bool POSITIVE, bool SRW = false>
 __device__ __forceinline__ void quantize_chunk(const float (&x_in)[8], int block, const Seg (&sg)[2],
-                                               void* row_codes, bool vec, float* row_scales, uint32_t sr = 0,
-                                               uint32_t key = 0, const uint32_t* idx_mul = nullptr) {
+                                               uint8_t* const (&codes)[2], bool vec, float* const (&scales)[2],
+                                               uint32_t sr = 0, uint32_t key = 0,
+                                               const uint32_t* idx_mul = nullptr) {
   float x[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) x[i] = x_in[i];
@@ -1152,8 +1175,8 @@ __device__ __forceinline__ void quantize_chunk(const float (&x_in)[8], int block
       }
     }
     if (!sg[g].ok) continue;
-    if (writer && (block != 128 || g == 0)) row_scales[sg[g].q >> __builtin_ctz((unsigned)block)] = sc[g];
-    uint8_t* p = static_cast<uint8_t*>(row_codes) + sg[g].q;
+    if (writer && (block != 128 || g == 0)) *scales[g] = sc[g];
+    uint8_t* p = codes[g];
     if (vec) {
       st_nt<uint32_t>(p, word);
     } else {
@@ -1163,26 +1186,47 @@ __device__ __forceinline__ void quantize_chunk(const float (&x_in)[8], int block
   }
 }
 
-// Per-thread addressing of the rows a thread steps in one tile: pointers to
-// its row of pass 0 and the uniform distance of one pass (RPP rows), so
-// pass s addresses its row with s * stride folded on the scalar unit and one
-// 64-bit add, instead of a 64-bit multiply per stream and pass; likewise the
-// flat SR index (p K + q) times the golden constant advances by a uniform
-// step per pass.  The arithmetic on the values is unchanged.
+// Addressing of the elements a thread steps in one tile.  Every stream has
+// a tile base (its row row0, column col0) and a step per pass (RPP rows),
+// both uniform over the workgroup and so held in scalar registers, and the
+// thread one byte offset from the tile base (its row tid / 16, column
+// 4 (tid % 16)); the second segment sits 64 columns further, a constant
+// (scales: s1 bytes further).  A state access is then a scalar base plus the
+// pass step (added on the scalar unit) plus the thread's offset, which the
+// FAST kernels keep in 32 bits (the host routes rows of 2^26 bytes or more to
+// the other kernels) so that it is the load's vector offset operand: no
+// per-pass vector address arithmetic.  The flat SR index (p K + q) times the
+// golden constant likewise advances by a uniform step per pass.
+template <bool FAST>
 struct TileRows {
-  char* w;                 // W, m, v, and the G source (dW / accumulator), at row p0
+  using Off = std::conditional_t<FAST, uint32_t, uint64_t>;
+  char* w;                 // W, m, v, and the G source (dW / accumulator) at (row0, col0)
   char* m;
   char* v;
   const char* g;
-  float* ms;               // block scales of row p0
-  float* vs;
-  float* ws;               // the weight's block scales (E4M3 weight)
-  int64_t dw, dm, dv, dg;  // bytes from one pass's row to the next
-  int64_t ds;              // scale elements from one pass's row to the next
+  char* ms;                // block scales at (row0, col0 / block)
+  char* vs;
+  char* ws;                // the weight's block scales (E4M3 weight)
+  int64_t dw, dm, dv, dg;  // bytes from one pass's rows to the next
+  int64_t ds;              // scale bytes from one pass's rows to the next
+  int64_t s1;              // scale bytes from segment 0's block to segment 1's
+  Off ow, om, ov, og, os;  // this thread's byte offsets from the tile bases
   uint32_t idx;            // p0 K GOLDEN (mod 2^32)
   uint32_t didx;           // RPP K GOLDEN
   uint32_t qg[2];          // q GOLDEN of the thread's two segments
 };
+
+// base + pass + off + extra, with base + pass uniform and off the thread's
+// offset: the shape the loads and stores take as scalar base plus vector
+// offset (plus the immediate offset field for a constant extra).
+template <class O>
+__device__ __forceinline__ char* at(char* base, int64_t pass, O off, int64_t extra) {
+  return (base + pass) + (uint64_t)off + extra;
+}
+template <class O>
+__device__ __forceinline__ const char* at(const char* base, int64_t pass, O off, int64_t extra) {
+  return (base + pass) + (uint64_t)off + extra;
+}
 
 template <int OPT, int WF, int MF, int VF, bool FAST>
 struct Step {
@@ -1199,29 +1243,29 @@ struct Step {
     Raw4<VFMT> v[2];
   };
 
-  __device__ __forceinline__ static void load(const KArgs& a, const TileRows& tr, int s, const Seg (&sg)[2],
+  static constexpr int esz(int fmt) { return fmt == FMT_F32 ? 4 : fmt == FMT_BF16 ? 2 : 1; }
+
+  __device__ __forceinline__ static void load(const KArgs& a, const TileRows<FAST>& tr, int s, const Seg (&sg)[2],
                                               Pending& r) {
     const bool vec = a.vec_state != 0;
-    const char* rw = tr.w + s * tr.dw;
-    // block is 32, 64 or 128: the scale index is a shift (a runtime division costs ~18 VALU)
-    const int bsh = __builtin_ctz((unsigned)a.block);
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       if (!sg[g].ok) {
         zero4(r.w[g]); zero4(r.m[g]); zero4(r.v[g]);
         continue;
       }
-      ld4<WF, FAST>(r.w[g], rw, sg[g], vec);
-      if constexpr (fmt_blocked(WF)) r.w[g].s = (tr.ws + s * tr.ds)[sg[g].q >> bsh];
+      ld4<WF, FAST>(r.w[g], at(tr.w, s * tr.dw, tr.ow, 64 * g * esz(WF)), sg[g], vec);
+      if constexpr (fmt_blocked(WF))
+        r.w[g].s = *reinterpret_cast<const float*>(at(tr.ws, s * tr.ds, tr.os, g * tr.s1));
       if constexpr (HAS_M) {
-        const char* rm = tr.m + s * tr.dm;
-        ld4<MF, FAST>(r.m[g], rm, sg[g], vec);
-        if constexpr (fmt_blocked(MF)) r.m[g].s = (tr.ms + s * tr.ds)[sg[g].q >> bsh];
+        ld4<MF, FAST>(r.m[g], at(tr.m, s * tr.dm, tr.om, 64 * g * esz(MF)), sg[g], vec);
+        if constexpr (fmt_blocked(MF))
+          r.m[g].s = *reinterpret_cast<const float*>(at(tr.ms, s * tr.ds, tr.os, g * tr.s1));
       }
       if constexpr (HAS_V) {
-        const char* rv = tr.v + s * tr.dv;
-        ld4<VF, FAST>(r.v[g], rv, sg[g], vec);
-        if constexpr (fmt_blocked(VF)) r.v[g].s = (tr.vs + s * tr.ds)[sg[g].q >> bsh];
+        ld4<VF, FAST>(r.v[g], at(tr.v, s * tr.dv, tr.ov, 64 * g * esz(VF)), sg[g], vec);
+        if constexpr (fmt_blocked(VF))
+          r.v[g].s = *reinterpret_cast<const float*>(at(tr.vs, s * tr.ds, tr.os, g * tr.s1));
       }
     }
   }
@@ -1234,8 +1278,8 @@ struct Step {
       m = fmaf(k.b1, m, k.omb1 * g);                                     // m' = b1 m + (1-b1) G
       v = fmaf(k.b2, v, k.omb2 * (g * g));                               // v' = b2 v + (1-b2) G^2
       const float den = fmaf(__builtin_amdgcn_sqrtf(v), k.bc2s, k.eps);  // sqrt(v'/(1-b2^t)) + eps
-      const float upd = (m * k.bc1) * __builtin_amdgcn_rcpf(den);        // m_hat / den
-      w = fmaf(k.decay, w, -k.lr * upd);                                 // (1 - lr wd) W - lr upd
+      const float upd = (m * k.lrbc1) * __builtin_amdgcn_rcpf(den);      // lr m_hat / den
+      w = fmaf(k.decay, w, -upd);                                        // (1 - lr wd) W - lr m_hat / den
     } else if constexpr (OPT == OPT_NADAM) {
       m = fmaf(k.b1, m, k.omb1 * g);
       v = fmaf(k.b2, v, k.omb2 * (g * g));
@@ -1274,38 +1318,73 @@ struct Step {
 
   // Decode, apply phi and store one chunk of row p.  Must be called by every
   // lane of the wave when a state is int8 (lane shuffles).
-  __device__ __forceinline__ static void apply_store(const KArgs& a, const TileRows& tr, int ps, const Seg (&sg)[2],
+  __device__ __forceinline__ static void apply_store(const KArgs& a, const TileRows<FAST>& tr, int ps, const Seg (&sg)[2],
                                                      const float (&g)[8], const Pending& r) {
     float w[8], m[8], v[8];
+    // A block-scaled m or v enters phi only through b1 m, b2 m (Lion) or
+    // b2 v, so its scale s is folded into those factors: phi sees the codes
+    // and (b s) instead of b and the dequantised code * s.
+    constexpr bool FOLD_M = fmt_blocked(MFMT) && (OPT == OPT_ADAMW || OPT == OPT_LION || OPT == OPT_SGDM);
+    constexpr bool FOLD_V = fmt_blocked(VFMT) && OPT == OPT_ADAMW;
+    EpiConst kc[2] = {a.c, a.c};
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       dec4<WF>(r.w[s], w + 4 * s);
-      dec4<MFMT>(r.m[s], m + 4 * s);
-      dec4<VFMT>(r.v[s], v + 4 * s);
+      if constexpr (FOLD_M) {
+        dec4_codes<MFMT>(r.m[s], m + 4 * s);
+        kc[s].b1 = a.c.b1 * r.m[s].s;
+        if constexpr (OPT == OPT_LION) kc[s].b2 = a.c.b2 * r.m[s].s;
+      } else {
+        dec4<MFMT>(r.m[s], m + 4 * s);
+      }
+      if constexpr (FOLD_V) {
+        dec4_codes<VFMT>(r.v[s], v + 4 * s);
+        kc[s].b2 = a.c.b2 * r.v[s].s;
+      } else {
+        dec4<VFMT>(r.v[s], v + 4 * s);
+      }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) phi(a.c, g[i], w[i], m[i], v[i]);
+    for (int i = 0; i < 8; ++i) phi(FOLD_M || FOLD_V ? kc[i >> 2] : a.c, g[i], w[i], m[i], v[i]);
     const bool vec = a.vec_state != 0;
-    char* rw = tr.w + ps * tr.dw;
-    char* rm = nullptr;
-    char* rv = nullptr;
-    if constexpr (HAS_M) rm = tr.m + ps * tr.dm;
-    if constexpr (HAS_V) rv = tr.v + ps * tr.dv;
     const uint32_t rowbase = tr.idx + (uint32_t)ps * tr.didx;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       if (!sg[s].ok) continue;
       const uint32_t idx_mul = rowbase + tr.qg[s];
-      if constexpr (!fmt_blocked(WF)) st4<WF, FAST>(rw, sg[s], vec, w + 4 * s, a.c.sr, a.c.keyW, idx_mul);
-      if constexpr (HAS_M && !fmt_blocked(MF)) st4<MF, FAST>(rm, sg[s], vec, m + 4 * s, a.c.sr, a.c.keyM, idx_mul);
-      if constexpr (HAS_V && !fmt_blocked(VF)) st4<VF, FAST>(rv, sg[s], vec, v + 4 * s, a.c.sr, a.c.keyV, idx_mul);
+      if constexpr (!fmt_blocked(WF))
+        st4<WF, FAST>(at(tr.w, ps * tr.dw, tr.ow, 64 * s * esz(WF)), sg[s], vec, w + 4 * s, a.c.sr, a.c.keyW,
+                      idx_mul);
+      if constexpr (HAS_M && !fmt_blocked(MF))
+        st4<MF, FAST>(at(tr.m, ps * tr.dm, tr.om, 64 * s * esz(MF)), sg[s], vec, m + 4 * s, a.c.sr, a.c.keyM,
+                      idx_mul);
+      if constexpr (HAS_V && !fmt_blocked(VF))
+        st4<VF, FAST>(at(tr.v, ps * tr.dv, tr.ov, 64 * s * esz(VF)), sg[s], vec, v + 4 * s, a.c.sr, a.c.keyV,
+                      idx_mul);
     }
+    // a block-scaled stream: segment pointers of the codes (1 byte each) and of the scales
     if constexpr (fmt_blocked(WF)) {
       const uint32_t im[2] = {rowbase + tr.qg[0], rowbase + tr.qg[1]};
-      quantize_chunk<WF, false, true>(w, a.block, sg, rw, vec, tr.ws + ps * tr.ds, a.c.sr, a.c.keyW, im);
+      uint8_t* const cp[2] = {reinterpret_cast<uint8_t*>(at(tr.w, ps * tr.dw, tr.ow, 0)),
+                              reinterpret_cast<uint8_t*>(at(tr.w, ps * tr.dw, tr.ow, 64))};
+      float* const sp[2] = {reinterpret_cast<float*>(at(tr.ws, ps * tr.ds, tr.os, 0)),
+                            reinterpret_cast<float*>(at(tr.ws, ps * tr.ds, tr.os, tr.s1))};
+      quantize_chunk<WF, false, true>(w, a.block, sg, cp, vec, sp, a.c.sr, a.c.keyW, im);
     }
-    if constexpr (HAS_M && fmt_blocked(MF)) quantize_chunk<MF, false>(m, a.block, sg, rm, vec, tr.ms + ps * tr.ds);
-    if constexpr (HAS_V && fmt_blocked(VF)) quantize_chunk<VF, true>(v, a.block, sg, rv, vec, tr.vs + ps * tr.ds);
+    if constexpr (HAS_M && fmt_blocked(MF)) {
+      uint8_t* const cp[2] = {reinterpret_cast<uint8_t*>(at(tr.m, ps * tr.dm, tr.om, 0)),
+                              reinterpret_cast<uint8_t*>(at(tr.m, ps * tr.dm, tr.om, 64))};
+      float* const sp[2] = {reinterpret_cast<float*>(at(tr.ms, ps * tr.ds, tr.os, 0)),
+                            reinterpret_cast<float*>(at(tr.ms, ps * tr.ds, tr.os, tr.s1))};
+      quantize_chunk<MF, false>(m, a.block, sg, cp, vec, sp);
+    }
+    if constexpr (HAS_V && fmt_blocked(VF)) {
+      uint8_t* const cp[2] = {reinterpret_cast<uint8_t*>(at(tr.v, ps * tr.dv, tr.ov, 0)),
+                              reinterpret_cast<uint8_t*>(at(tr.v, ps * tr.dv, tr.ov, 64))};
+      float* const sp[2] = {reinterpret_cast<float*>(at(tr.vs, ps * tr.ds, tr.os, 0)),
+                            reinterpret_cast<float*>(at(tr.vs, ps * tr.ds, tr.os, tr.s1))};
+      quantize_chunk<VF, true>(v, a.block, sg, cp, vec, sp);
+    }
   }
 };
 
@@ -1328,40 +1407,56 @@ struct Epilogue {
   static constexpr int GR = ACC ? FMT_F32 : GF;           // format of the G words loaded per pass
   typename S::Pending pend[DEPTH];
   Raw4<GR> graw[DEPTH][2];
-  TileRows tr;
+  TileRows<FAST> tr;
   int tid;
 
   static constexpr int esz(int fmt) { return fmt == FMT_F32 ? 4 : fmt == FMT_BF16 ? 2 : 1; }
 
-  // This thread's row bases and per-pass strides for the tile at (row0, col0).
+  // Tile bases, per-pass steps and this thread's offsets for the tile at
+  // (row0, col0).
   __device__ __forceinline__ void rows(const KArgs& a, int row0, int col0) {
-    const int64_t p0 = row0 + (tid >> 4);
-    tr.w = static_cast<char*>(a.W) + p0 * a.ldw * esz(S::WFMT);
+    using Off = typename TileRows<FAST>::Off;
+    const int64_t rl = tid >> 4, cl = 4 * (tid & 15);
+    const int64_t p0 = row0 + rl;
+    const auto base = [&](void* ptr, int64_t ld, int es) {
+      return static_cast<char*>(ptr) + ((int64_t)row0 * ld + col0) * es;
+    };
+    tr.w = base(a.W, a.ldw, esz(S::WFMT));
     tr.dw = (int64_t)RPP * a.ldw * esz(S::WFMT);
+    tr.ow = (Off)((rl * a.ldw + cl) * esz(S::WFMT));
     if constexpr (S::HAS_M) {
-      tr.m = static_cast<char*>(a.m) + p0 * a.ldm * esz(S::MFMT);
+      tr.m = base(a.m, a.ldm, esz(S::MFMT));
       tr.dm = (int64_t)RPP * a.ldm * esz(S::MFMT);
+      tr.om = (Off)((rl * a.ldm + cl) * esz(S::MFMT));
     }
     if constexpr (S::HAS_V) {
-      tr.v = static_cast<char*>(a.v) + p0 * a.ldv * esz(S::VFMT);
+      tr.v = base(a.v, a.ldv, esz(S::VFMT));
       tr.dv = (int64_t)RPP * a.ldv * esz(S::VFMT);
+      tr.ov = (Off)((rl * a.ldv + cl) * esz(S::VFMT));
     }
     if constexpr (GR != FMT_NONE) {
-      tr.g = static_cast<const char*>(a.dW) + p0 * a.lddw * esz(GR);
+      tr.g = base(a.dW, a.lddw, esz(GR));
       tr.dg = (int64_t)RPP * a.lddw * esz(GR);
+      tr.og = (Off)((rl * a.lddw + cl) * esz(GR));
     }
     if constexpr (fmt_blocked(S::MFMT) || fmt_blocked(S::VFMT) || fmt_blocked(S::WFMT)) {
-      const int64_t spr = a.K >> __builtin_ctz((unsigned)a.block);   // scales per row
-      if constexpr (fmt_blocked(S::MFMT)) tr.ms = a.ms + p0 * spr;
-      if constexpr (fmt_blocked(S::VFMT)) tr.vs = a.vs + p0 * spr;
-      if constexpr (fmt_blocked(S::WFMT)) tr.ws = a.wsc + p0 * spr;
-      tr.ds = (int64_t)RPP * spr;
+      // block is 32, 64 or 128: block indices are shifts; col0 is a multiple of 128
+      const int bsh = __builtin_ctz((unsigned)a.block);
+      const int64_t spr = a.K >> bsh;                                  // scales per row
+      const auto sbase = [&](float* ptr) {
+        return reinterpret_cast<char*>(ptr + (int64_t)row0 * spr + (col0 >> bsh));
+      };
+      if constexpr (fmt_blocked(S::MFMT)) tr.ms = sbase(a.ms);
+      if constexpr (fmt_blocked(S::VFMT)) tr.vs = sbase(a.vs);
+      if constexpr (fmt_blocked(S::WFMT)) tr.ws = sbase(a.wsc);
+      tr.ds = (int64_t)RPP * spr * 4;
+      tr.os = (Off)((rl * spr + (cl >> bsh)) * 4);
+      tr.s1 = (int64_t)(64 >> bsh) * 4;
     }
     tr.idx = ((uint32_t)p0 * (uint32_t)a.K) * GOLDEN;
     tr.didx = ((uint32_t)RPP * (uint32_t)a.K) * GOLDEN;
-    const int cl = 4 * (tid & 15);
 #pragma unroll
-    for (int g = 0; g < 2; ++g) tr.qg[g] = (uint32_t)(col0 + 64 * g + cl) * GOLDEN;
+    for (int g = 0; g < 2; ++g) tr.qg[g] = (uint32_t)(col0 + 64 * g + (int)cl) * GOLDEN;
   }
 
   __device__ __forceinline__ void segs(const KArgs& a, int p, int col0, Seg (&sg)[2]) const {
@@ -1381,10 +1476,9 @@ struct Epilogue {
     S::load(a, tr, s, sg, pend[slot]);
     if constexpr (GR != FMT_NONE) {
       const bool gvec = a.vec_dw != 0;
-      const char* rg = tr.g + s * tr.dg;
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        if (sg[g].ok) ld4<GR, FAST>(graw[slot][g], rg, sg[g], gvec);
+        if (sg[g].ok) ld4<GR, FAST>(graw[slot][g], at(tr.g, s * tr.dg, tr.og, 64 * g * esz(GR)), sg[g], gvec);
         else zero4(graw[slot][g]);
       }
     }
@@ -1680,7 +1774,7 @@ __global__ void __launch_bounds__(NT, 2) k_gemm(const KArgs a) {
         sg.q = col0 + 64 * g + cl;
         sg.nv = max(0, min(4, a.K - sg.q));
         sg.ok = sg.nv > 0 && p < a.N;
-        if (sg.ok) ld4<FMT_F32, false>(old[s][g], rowp, sg, vec);
+        if (sg.ok) ld4<FMT_F32, false>(old[s][g], rowp + (int64_t)sg.q * 4, sg, vec);
         else zero4(old[s][g]);
       }
     }
@@ -1716,8 +1810,8 @@ __global__ void __launch_bounds__(NT, 2) k_gemm(const KArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[i] = o[i] + x[i];
       }
-      if (a.dw_fmt == FMT_F32) st4<FMT_F32, false>(rowp, sg, vec, x, 0, 0, 0);
-      else st4<FMT_BF16, false>(rowp, sg, vec, x, 0, 0, 0);
+      if (a.dw_fmt == FMT_F32) st4<FMT_F32, false>(rowp + (int64_t)sg.q * 4, sg, vec, x, 0, 0, 0);
+      else st4<FMT_BF16, false>(rowp + (int64_t)sg.q * 2, sg, vec, x, 0, 0, 0);
     }
   }
 }

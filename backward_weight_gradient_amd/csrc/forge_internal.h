@@ -37,6 +37,7 @@ struct EpiConst {
   float decay;     // 1 - eta * lambda   (decoupled decay: AdamW, Lion)
   float wd;        // lambda             (L2 decay: SGD-m)
   float bc1;       // 1 / (1 - beta1^t)
+  float lrbc1;     // eta / (1 - beta1^t)   (AdamW)
   float bc2s;      // 1 / sqrt(1 - beta2^t)
   float na1;       // NAdam: mu_{t+1} / (1 - prod_{i<=t+1} mu_i)   (weight of m')
   float na2;       // NAdam: (1 - mu_t) / (1 - prod_{i<=t} mu_i)   (weight of G)

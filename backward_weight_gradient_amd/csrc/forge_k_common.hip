@@ -102,8 +102,12 @@ __global__ void __launch_bounds__(256) k_debug_quant(const float* __restrict__ i
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[4 * g + i] = sg[g].ok ? in[(int64_t)p * cols + sg[g].q + i] : 0.f;
   }
-  const int64_t prow = p < rows ? p : 0;   // a valid row base for lanes that store nothing
-  quantize_chunk<FMT, POSITIVE>(x, block, sg, codes + prow * cols, true, scales + prow * (cols / block));
+  const int64_t prow = p < rows ? p : 0;   // a valid row for lanes that store nothing
+  const int bsh = __builtin_ctz((unsigned)block);
+  uint8_t* const cp[2] = {codes + prow * cols + sg[0].q, codes + prow * cols + sg[1].q};
+  float* const sp[2] = {scales + prow * (cols / block) + (sg[0].q >> bsh),
+                        scales + prow * (cols / block) + (sg[1].q >> bsh)};
+  quantize_chunk<FMT, POSITIVE>(x, block, sg, cp, true, sp);
 }
 
 hipError_t launch_debug_quant(const float* in, uint8_t* codes, float* scales, int rows, int cols, int fmt,

@@ -273,8 +273,8 @@ __global__ void __launch_bounds__(NT * KG, KG == 1 ? 2 : 1) k_dgrad_bf16(const D
       float x[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) x[i] = sG[rl * SH::GP_ + 64 * h + cl + i];
-      if (ofmt == FMT_F32) st4<FMT_F32, false>(rowp, sg, vec, x, 0, 0, 0);
-      else st4<FMT_BF16, false>(rowp, sg, vec, x, 0, 0, 0);
+      if (ofmt == FMT_F32) st4<FMT_F32, false>(rowp + (int64_t)sg.q * 4, sg, vec, x, 0, 0, 0);
+      else st4<FMT_BF16, false>(rowp + (int64_t)sg.q * 2, sg, vec, x, 0, 0, 0);
     }
   }
 }
@@ -301,8 +301,8 @@ __global__ void __launch_bounds__(NT) k_dgrad_reduce(const DgArgs g) {
   float x[4] = {acc[0], acc[1], acc[2], acc[3]};
   const bool vec = g.vec_out != 0;
   char* rowp = static_cast<char*>(g.dX) + (int64_t)p * g.ldx * (g.dx_fmt == FMT_F32 ? 4 : 2);
-  if (g.dx_fmt == FMT_F32) st4<FMT_F32, false>(rowp, sg, vec, x, 0, 0, 0);
-  else st4<FMT_BF16, false>(rowp, sg, vec, x, 0, 0, 0);
+  if (g.dx_fmt == FMT_F32) st4<FMT_F32, false>(rowp + (int64_t)sg.q * 4, sg, vec, x, 0, 0, 0);
+  else st4<FMT_BF16, false>(rowp + (int64_t)sg.q * 2, sg, vec, x, 0, 0, 0);
 }
 
 namespace {
