@@ -67,20 +67,27 @@ constexpr uint32_t GOLDEN = 0x9E3779B9u;
 // ------------------------------------------------------------------------
 // Rounding helpers (paper, Appendix C)
 // ------------------------------------------------------------------------
-// The 32-bit word whose top 16 bits are the SR bits of an element, the top
-// half of fmix32(key ^ idx_mul), fmix32 being MurmurHash3's 32-bit
-// finaliser (Appleby, public domain): xor-shifts by 16, 13, 16 around
-// multiplies by 0x85EBCA6B and 0xC2B2AE35.  Its last xor-shift changes only
-// the low half, so it is left out.  Callers that round
-// consecutive indices pass idx * 0x9E3779B9 (mod 2^32) directly and step it
-// by adding the constant.
-__device__ __forceinline__ uint32_t sr_word(uint32_t key, uint32_t idx_mul) {
-  uint32_t h = key ^ idx_mul;
+// SR bits, 16 per element, from a counter-based hash.  The elements with
+// flat indices (p K + q) 2j and 2j + 1 share the word
+// h_j = fmix32(key ^ (j * 0x9E3779B9 mod 2^32)), fmix32 being MurmurHash3's
+// 32-bit finaliser (Appleby, public domain: xor-shifts by 16, 13, 16 around
+// multiplies by 0x85EBCA6B and 0xC2B2AE35); the even element takes its top
+// half, the odd one its bottom half.  sr_pair(key, j * GOLDEN) is h_j.
+__device__ __forceinline__ uint32_t sr_pair(uint32_t key, uint32_t jmul) {
+  uint32_t h = key ^ jmul;
   h ^= h >> 16;
   h *= 0x85EBCA6Bu;
   h ^= h >> 13;
   h *= 0xC2B2AE35u;
+  h ^= h >> 16;
   return h;
+}
+
+// The SR bits of flat index idx in the top half of a word (the operand
+// layout of the v_cvt_sr_* converters).
+__device__ __forceinline__ uint32_t sr_elem_word(uint32_t key, uint32_t idx) {
+  const uint32_t h = sr_pair(key, (idx >> 1) * GOLDEN);
+  return (idx & 1u) ? h << 16 : h;
 }
 
 // fp32 -> bf16 on the gfx950 converters.  v_cvt_pk_bf16_f32 rounds two
@@ -109,18 +116,24 @@ __device__ __forceinline__ uint32_t bf16x2_sr(float a, float b, uint32_t ra, uin
   return __builtin_bit_cast(uint32_t, s);
 }
 __device__ __forceinline__ uint32_t bf16_sr_bits(float x, uint32_t key, uint32_t idx) {
-  return bf16x2_sr(x, 0.f, sr_word(key, idx * GOLDEN), 0u) & 0xFFFFu;
+  return bf16x2_sr(x, 0.f, sr_elem_word(key, idx), 0u) & 0xFFFFu;
 }
 
-// Two stored bf16 patterns (a low, b high; flat indices idx_mul / GOLDEN and
-// the next one): stochastic rounding where srmask is all ones, round to
-// nearest even where it is zero.  Both are formed and the mask selects, so
-// the wave-uniform mode costs no branch.
-__device__ __forceinline__ uint32_t bf16x2_store(float a, float b, uint32_t srmask, uint32_t key,
-                                                 uint32_t idx_mul) {
-  const uint32_t s = bf16x2_sr(a, b, sr_word(key, idx_mul), sr_word(key, idx_mul + GOLDEN));
+// Two stored bf16 patterns (a low, b high) with random words ra, rb:
+// stochastic rounding where srmask is all ones, round to nearest even where
+// it is zero.  Both are formed and the mask selects, so the wave-uniform
+// mode costs no branch.
+__device__ __forceinline__ uint32_t bf16x2_select(float a, float b, uint32_t ra, uint32_t rb, uint32_t srmask) {
+  const uint32_t s = bf16x2_sr(a, b, ra, rb);
   const uint32_t n = bf16x2_rne(a, b);
   return (s & srmask) | (n & ~srmask);
+}
+
+// The pair of elements 2j (a, low half) and 2j + 1 (b, high half) with one
+// hash: jmul = j * GOLDEN.
+__device__ __forceinline__ uint32_t bf16x2_store(float a, float b, uint32_t srmask, uint32_t key, uint32_t jmul) {
+  const uint32_t h = sr_pair(key, jmul);
+  return bf16x2_select(a, b, h, h << 16, srmask);
 }
 
 __device__ __forceinline__ float bf16_val(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
@@ -1021,11 +1034,12 @@ __device__ __forceinline__ void dec4_codes(const Raw4<FMT>& r, float* x) {
 
 // Store 4 fp32 values as FMT at seg, the segment's first element (int8
 // formats go through quantize_chunk instead).
-// bf16: stochastic rounding when sr is all ones (idx_mul = flat index of the
-// first element times 0x9E3779B9), round to nearest even when it is zero.
+// bf16: stochastic rounding when sr is all ones (idx = flat index of the
+// first element), round to nearest even when it is zero.  FAST segments
+// start at an even flat index (K % 4 == 0), so they are two hash pairs.
 template <int FMT, bool FAST>
 __device__ __forceinline__ void st4(void* seg, const Seg& g, bool vec, const float* x, uint32_t sr, uint32_t key,
-                                    uint32_t idx_mul) {
+                                    uint32_t idx) {
   if constexpr (FMT == FMT_F32) {
     float* p = static_cast<float*>(seg);
     if (FAST || (vec && g.nv == 4)) {
@@ -1036,8 +1050,15 @@ __device__ __forceinline__ void st4(void* seg, const Seg& g, bool vec, const flo
         if (i < g.nv) p[i] = x[i];
     }
   } else if constexpr (FMT == FMT_BF16) {
-    const uint32_t lo = bf16x2_store(x[0], x[1], sr, key, idx_mul);
-    const uint32_t hi = bf16x2_store(x[2], x[3], sr, key, idx_mul + 2u * GOLDEN);
+    uint32_t lo, hi;
+    if constexpr (FAST) {
+      const uint32_t jmul = (idx >> 1) * GOLDEN;
+      lo = bf16x2_store(x[0], x[1], sr, key, jmul);
+      hi = bf16x2_store(x[2], x[3], sr, key, jmul + GOLDEN);
+    } else {
+      lo = bf16x2_select(x[0], x[1], sr_elem_word(key, idx), sr_elem_word(key, idx + 1u), sr);
+      hi = bf16x2_select(x[2], x[3], sr_elem_word(key, idx + 2u), sr_elem_word(key, idx + 3u), sr);
+    }
     uint16_t* p = static_cast<uint16_t*>(seg);
     if (FAST || (vec && g.nv == 4)) {
       st_nt<u32x2>(p, u32x2{lo, hi});
@@ -1076,13 +1097,13 @@ __device__ __forceinline__ void st4(void* seg, const Seg& g, bool vec, const flo
 // S8 needs no clamp, and U8 codes come from v_cvt_pk_u8_f32, which rounds
 // to nearest even, clamps to 0..255 and inserts the byte.
 // SRW (the E4M3 weight store): when sr is nonzero the codes are drawn by
-// e4m3_sr_pack4 with the SR bits of flat indices idx_mul[g] / GOLDEN + i
-// (key `key`), else they are the nearest ones.
+// e4m3_sr_pack4 with the SR bits of flat indices idx[g] + i (key `key`),
+// else they are the nearest ones.
 template <int FMT, bool POSITIVE, bool SRW = false>
 __device__ __forceinline__ void quantize_chunk(const float (&x_in)[8], int block, const Seg (&sg)[2],
                                                uint8_t* const (&codes)[2], bool vec, float* const (&scales)[2],
                                                uint32_t sr = 0, uint32_t key = 0,
-                                               const uint32_t* idx_mul = nullptr) {
+                                               const uint32_t* idx = nullptr) {
   float x[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) x[i] = x_in[i];
@@ -1150,9 +1171,10 @@ __device__ __forceinline__ void quantize_chunk(const float (&x_in)[8], int block
       }
       if constexpr (SRW) {
         if (sr) {   // wave-uniform
-          uint32_t r[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) r[i] = sr_word(key, idx_mul[g] + (uint32_t)i * GOLDEN);
+          // idx[g] is even (K % block == 0): the segment is two hash pairs
+          const uint32_t jmul = (idx[g] >> 1) * GOLDEN;
+          const uint32_t h0 = sr_pair(key, jmul), h1 = sr_pair(key, jmul + GOLDEN);
+          const uint32_t r[4] = {h0, h0 << 16, h1, h1 << 16};
           word = e4m3_sr_pack4(y, r);
         } else {
           word = e4m3_pack4(y[0], y[1], y[2], y[3]);
@@ -1194,9 +1216,9 @@ __device__ __forceinline__ void quantize_chunk(const float (&x_in)[8], int block
 // (scales: s1 bytes further).  A state access is then a scalar base plus the
 // pass step (added on the scalar unit) plus the thread's offset, which the
 // FAST kernels keep in 32 bits (the host routes rows of 2^26 bytes or more to
-// the other kernels) so that it is the load's vector offset operand: no
-// per-pass vector address arithmetic.  The flat SR index (p K + q) times the
-// golden constant likewise advances by a uniform step per pass.
+// the other kernels): one 64-bit add of a scalar and a zero-extended vector
+// register per access, no per-pass vector multiplies.  The flat SR index
+// (p K + q) likewise advances by a uniform step per pass.
 template <bool FAST>
 struct TileRows {
   using Off = std::conditional_t<FAST, uint32_t, uint64_t>;
@@ -1211,9 +1233,9 @@ struct TileRows {
   int64_t ds;              // scale bytes from one pass's rows to the next
   int64_t s1;              // scale bytes from segment 0's block to segment 1's
   Off ow, om, ov, og, os;  // this thread's byte offsets from the tile bases
-  uint32_t idx;            // p0 K GOLDEN (mod 2^32)
-  uint32_t didx;           // RPP K GOLDEN
-  uint32_t qg[2];          // q GOLDEN of the thread's two segments
+  uint32_t idx;            // p0 K (mod 2^32): the flat index of the thread's row in pass 0
+  uint32_t didx;           // RPP K
+  uint32_t qg[2];          // q of the thread's two segments
 };
 
 // base + pass + off + extra, with base + pass uniform and off the thread's
@@ -1351,16 +1373,16 @@ struct Step {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       if (!sg[s].ok) continue;
-      const uint32_t idx_mul = rowbase + tr.qg[s];
+      const uint32_t idx = rowbase + tr.qg[s];
       if constexpr (!fmt_blocked(WF))
         st4<WF, FAST>(at(tr.w, ps * tr.dw, tr.ow, 64 * s * esz(WF)), sg[s], vec, w + 4 * s, a.c.sr, a.c.keyW,
-                      idx_mul);
+                      idx);
       if constexpr (HAS_M && !fmt_blocked(MF))
         st4<MF, FAST>(at(tr.m, ps * tr.dm, tr.om, 64 * s * esz(MF)), sg[s], vec, m + 4 * s, a.c.sr, a.c.keyM,
-                      idx_mul);
+                      idx);
       if constexpr (HAS_V && !fmt_blocked(VF))
         st4<VF, FAST>(at(tr.v, ps * tr.dv, tr.ov, 64 * s * esz(VF)), sg[s], vec, v + 4 * s, a.c.sr, a.c.keyV,
-                      idx_mul);
+                      idx);
     }
     // a block-scaled stream: segment pointers of the codes (1 byte each) and of the scales
     if constexpr (fmt_blocked(WF)) {
@@ -1453,10 +1475,10 @@ struct Epilogue {
       tr.os = (Off)((rl * spr + (cl >> bsh)) * 4);
       tr.s1 = (int64_t)(64 >> bsh) * 4;
     }
-    tr.idx = ((uint32_t)p0 * (uint32_t)a.K) * GOLDEN;
-    tr.didx = ((uint32_t)RPP * (uint32_t)a.K) * GOLDEN;
+    tr.idx = (uint32_t)p0 * (uint32_t)a.K;
+    tr.didx = (uint32_t)RPP * (uint32_t)a.K;
 #pragma unroll
-    for (int g = 0; g < 2; ++g) tr.qg[g] = (uint32_t)(col0 + 64 * g + (int)cl) * GOLDEN;
+    for (int g = 0; g < 2; ++g) tr.qg[g] = (uint32_t)(col0 + 64 * g + (int)cl);
   }
 
   __device__ __forceinline__ void segs(const KArgs& a, int p, int col0, Seg (&sg)[2]) const {

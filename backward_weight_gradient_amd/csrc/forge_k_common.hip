@@ -6,10 +6,18 @@
 
 namespace forge {
 
-// The device stochastic rounding on its own: element i uses flat index i.
+// The device stochastic rounding on its own, element i with flat index i:
+// thread t rounds the pair 2t, 2t + 1 through the fused epilogue's pair
+// function (its RNE half masked off); a last unpaired element uses the same
+// function with a zero partner that is not stored.
 __global__ void k_debug_sr(const float* __restrict__ in, uint16_t* __restrict__ out, uint32_t n, uint32_t key) {
-  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) out[i] = (uint16_t)bf16_sr_bits(in[i], key, i);
+  const uint32_t t = blockIdx.x * blockDim.x + threadIdx.x;
+  const uint64_t i0 = 2ull * t;
+  if (i0 >= n) return;
+  const bool two = i0 + 1 < n;
+  const uint32_t w = bf16x2_store(in[i0], two ? in[i0 + 1] : 0.f, 0xFFFFFFFFu, key, t * GOLDEN);
+  out[i0] = (uint16_t)(w & 0xFFFFu);
+  if (two) out[i0 + 1] = (uint16_t)(w >> 16);
 }
 
 // The device E4M3 rounding on its own, through the same four-value packing
@@ -34,12 +42,12 @@ __global__ void k_debug_e4m3_sr(const float* __restrict__ in, uint8_t* __restric
   const uint64_t i0 = 4ull * (blockIdx.x * (uint64_t)blockDim.x + threadIdx.x);
   if (i0 >= n) return;
   float y[4];
-  uint32_t r[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    y[k] = i0 + k < n ? in[i0 + k] : 0.f;
-    r[k] = sr_word(key, (uint32_t)(i0 + k) * GOLDEN);
-  }
+  for (int k = 0; k < 4; ++k) y[k] = i0 + k < n ? in[i0 + k] : 0.f;
+  // i0 is even: two hash pairs, as in the fused FP8 weight store
+  const uint32_t jmul = (uint32_t)(i0 >> 1) * GOLDEN;
+  const uint32_t h0 = sr_pair(key, jmul), h1 = sr_pair(key, jmul + GOLDEN);
+  const uint32_t r[4] = {h0, h0 << 16, h1, h1 << 16};
   const uint32_t w = e4m3_sr_pack4(y, r);
 #pragma unroll
   for (int k = 0; k < 4; ++k)
@@ -270,8 +278,8 @@ hipError_t launch_gemm(const KArgs& a, int in_fmt, hipStream_t st) {
 
 hipError_t launch_debug_sr(const float* in, uint16_t* out, uint32_t n, uint32_t key, hipStream_t st) {
   if (n == 0) return hipSuccess;
-  const unsigned blocks = (unsigned)((n + 255u) / 256u);
-  hipLaunchKernelGGL(k_debug_sr, dim3(blocks), dim3(256), 0, st, in, out, n, key);
+  const uint64_t threads = (n + 1ull) / 2ull;   // one pair per thread
+  hipLaunchKernelGGL(k_debug_sr, dim3((unsigned)((threads + 255u) / 256u)), dim3(256), 0, st, in, out, n, key);
   return hipGetLastError();
 }
 

@@ -216,12 +216,21 @@ def sr_key(seed: int, step: int, tensor_id: int) -> int:
 
 
 def sr_bits(key: int, flat_index: np.ndarray) -> np.ndarray:
-    """16 random bits for each element: the top half of
-    ``fmix32(key ^ (flat_index * 0x9E3779B9 mod 2^32))``, where flat_index is
-    the row-major index p*K + q of the element in the logical [N, K] matrix."""
+    """16 random bits for each element.  flat_index is the row-major index
+    p*K + q of the element in the logical [N, K] matrix; the elements
+    2j and 2j + 1 share one hash word
+
+        h_j = fmix32(key ^ (j * 0x9E3779B9 mod 2^32)),
+
+    element 2j taking its top half and element 2j + 1 its bottom half (the
+    two halves of a finaliser output are independent uniform 16-bit values,
+    so one hash serves two elements)."""
     idx = np.asarray(flat_index, dtype=np.uint64)
-    mixed = ((idx * np.uint64(_GOLDEN32)) & np.uint64(_M32)).astype(np.uint32)
-    return fmix32(np.uint32(key) ^ mixed) >> np.uint32(16)
+    pair = idx >> np.uint64(1)
+    mixed = ((pair * np.uint64(_GOLDEN32)) & np.uint64(_M32)).astype(np.uint32)
+    h = fmix32(np.uint32(key) ^ mixed)
+    odd = (idx & np.uint64(1)).astype(bool)
+    return np.where(odd, h & np.uint32(0xFFFF), h >> np.uint32(16)).astype(np.uint32)
 
 
 # --------------------------------------------------------------------------

@@ -232,6 +232,10 @@ def test_sr_bits_uniform_and_independent():
     hist = np.bincount(r >> 8, minlength=256)
     chi2 = ((hist - n / 256) ** 2 / (n / 256)).sum()
     assert chi2 < 400  # 255 dof: mean 255, sd 22.6
+    # the two halves of a pair's hash (even and odd elements), and
+    # neighbouring pairs, are uncorrelated
+    for a, b in ((r[0::2], r[1::2]), (r[1::2][:-1], r[2::2])):
+        assert abs(np.corrcoef(a, b)[0, 1]) < 5 / math.sqrt(n / 2)
     # different tensor / step / seed -> uncorrelated streams
     for key in (O.sr_key(1337, 10, 1), O.sr_key(1337, 11, 0), O.sr_key(1338, 10, 0)):
         r2 = O.sr_bits(key, idx).astype(np.int64)
@@ -259,6 +263,10 @@ def test_sr_key_and_bits_hand_worked():
         key = int(case["key"], 16)
         for b in case["sr_bits"]:
             assert O.fmix32(int(b["fmix32"]["in"], 16)) == int(b["fmix32"]["out"], 16)
+            # the worked word is the stated half of the pair's hash
+            out = int(b["fmix32"]["out"], 16)
+            assert b["pair_index"] == b["flat_index"] >> 1
+            assert int(b["r16"], 16) == ((out & 0xFFFF) if b["half"] == "bottom" else (out >> 16))
             got = O.sr_bits(key, np.array([b["flat_index"]], dtype=np.uint64))
             assert int(got[0]) == int(b["r16"], 16), (case["seed"], b["flat_index"])
     assert n_calls == 4 * len(doc["cases"]) and len(doc["cases"]) >= 5
