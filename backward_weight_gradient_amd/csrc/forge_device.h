@@ -342,19 +342,6 @@ __device__ __forceinline__ u32x2 tr_read_at(uint32_t lds_addr) {
   return v;
 }
 
-// 32-bit LDS address of (token row t, feature f) in a region at `region`.
-__device__ __forceinline__ uint32_t tr_addr(uint32_t region, int t, int f) {
-  return region + (uint32_t)MainBF16::off(t, f);
-}
-
-// The two transposing reads of an MFMA operand fragment (see MainBF16::frag).
-__device__ __forceinline__ void frag_issue(uint32_t region, int t0, int f0, int lane, u32x2& lo, u32x2& hi) {
-  const int t = t0 + 8 * (lane >> 5) + ((lane & 15) >> 2);
-  const int f = f0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  lo = tr_read(tr_addr(region, t, f));
-  hi = tr_read(tr_addr(region, t + 4, f));
-}
-
 __device__ __forceinline__ bf16x8 frag_join(u32x2 lo, u32x2 hi) {
   return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
@@ -406,8 +393,11 @@ __device__ __forceinline__ void dma_accumulate(const KArgs& a, char* ring, int r
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[bi][bj][e] = 0.f;
   const int nk = (a.BT + M::TK - 1) / M::TK;
-  // byte offsets of this lane's fragment reads (token rows 0 and 4 of a
-  // k-step, frag_issue's mapping) within a stage, per 32-feature block b
+  // MFMA operand fragment of a 16-token k-step and a 32-feature block by two
+  // transposing reads: lane l reads token rows t and t + 4 at features f ..
+  // f + 3, t = 8 (l / 32) + (l % 16) / 4, f = 16 ((l / 16) % 2) + 4 (l % 4)
+  // (8 consecutive tokens of one feature per lane after the transpose).
+  // Byte offsets of this lane's reads within a stage, per block b:
   uint32_t fofsA[2], fofsB[2];
   {
     const int t = 8 * (lane >> 5) + ((lane & 15) >> 2);
@@ -430,8 +420,8 @@ __device__ __forceinline__ void dma_accumulate(const KArgs& a, char* ring, int r
     if (kc + M::S - 1 < nk) ml.issue(a, kc + M::S - 1, ring + ((kc + M::S - 1) % M::S) * M::STAGE);
     const uint32_t cur = lds0 + (uint32_t)((kc % M::S) * M::STAGE);
     // operand fragments of the chunk's two k-steps: [A0 lo, A0 hi, A1 lo, A1 hi, B0 lo, B0 hi, B1 lo, B1 hi]
-    // (frag_issue's addresses: the hi half is 4 token rows = 1024 bytes on,
-    // the second k-step 16 rows = 4096 bytes on, the swizzle unchanged)
+    // (the hi half is 4 token rows = 1024 bytes on, the second k-step 16
+    // rows = 4096 bytes on, the swizzle unchanged)
     u32x2 f0[8], f1[8];
     uint32_t pa[2], pb[2];
 #pragma unroll
@@ -461,6 +451,7 @@ __device__ __forceinline__ void dma_accumulate(const KArgs& a, char* ring, int r
         acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_join(f0[2 * bi], f0[2 * bi + 1]),
                                                               frag_join(f0[4 + 2 * bj], f0[4 + 2 * bj + 1]),
                                                               acc[bi][bj], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);   // the wait below stays after these MFMAs
     lds_wait<0>(f1);
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi)

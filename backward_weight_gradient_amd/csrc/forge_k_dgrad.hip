@@ -130,12 +130,16 @@ __device__ __forceinline__ u32x4 ds_read_16(uint32_t addr) {
   return v;
 }
 
+// Wait until at most N LDS reads are outstanding; the k-step's fragments
+// are threaded through the statement so that their uses stay after it.
+template <int N>
 __device__ __forceinline__ void dg_wait(u32x4 (&a)[2], u32x2 (&b)[4]) {
-  asm volatile("s_waitcnt lgkmcnt(0)"
-               : "+v"(a[0]), "+v"(a[1]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]));
+  asm volatile("s_waitcnt lgkmcnt(%6)"
+               : "+v"(a[0]), "+v"(a[1]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]) : "i"(N));
 }
+template <int N>
 __device__ __forceinline__ void dg_wait(u32x4 (&a)[1], u32x2 (&b)[4]) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]));
+  asm volatile("s_waitcnt lgkmcnt(%5)" : "+v"(a[0]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]) : "i"(N));
 }
 
 
@@ -177,6 +181,22 @@ __global__ void __launch_bounds__(NT * KG, KG == 1 ? 2 : 1) k_dgrad_bf16(const D
   const int cps = (nk + g.splits - 1) / g.splits;
   const int c0 = KG == 1 ? sp * cps : 0;
   const int nj = KG == 1 ? max(0, min(cps, nk - c0)) : (nk + KG - 1) / KG;
+  // this lane's fragment offsets within a stage: dY rows m(bi), 16-byte
+  // segment 2 ks + lane / 32 (its swizzle differs between the two k-steps);
+  // W (the weight-gradient mainloop's transposing-read fragments) per
+  // 32-column block bj, the hi half 4 rows = 1024 bytes and the second
+  // k-step 16 rows = 4096 bytes on
+  uint32_t aofs[2][BI], bofs[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int bi = 0; bi < BI; ++bi) aofs[ks][bi] = dg_a_off(wr * (TM / 2) + bi * 32 + (lane & 31), 2 * ks + (lane >> 5));
+  {
+    const int t = 8 * (lane >> 5) + ((lane & 15) >> 2);
+    const int f = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj) bofs[bj] = (uint32_t)(SH::APB + MainBF16::off(t, wc * 64 + bj * 32 + f));
+  }
   DgradLoader<TM, S> ld;
   ld.init(g, tok0, col0, gtid);
 #pragma unroll
@@ -187,27 +207,44 @@ __global__ void __launch_bounds__(NT * KG, KG == 1 ? 2 : 1) k_dgrad_bf16(const D
     bar();
     if (j + S - 1 < nj) ld.issue(g, c0 + kg + KG * (j + S - 1), ring + ((j + S - 1) % S) * SH::STAGE);
     const uint32_t cur = lds0 + (uint32_t)((j % S) * SH::STAGE);
+    // both k-steps' fragments are requested first; the first k-step's MFMAs
+    // run while the second's reads land
+    u32x4 af[2][BI];
+    u32x2 bf[2][4];
+    uint32_t pb[2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      u32x4 af[BI];
-      u32x2 bf[4];
+    for (int bj = 0; bj < 2; ++bj) pb[bj] = cur + bofs[bj];
 #pragma unroll
-      for (int bi = 0; bi < BI; ++bi) {
-        const int m = wr * (TM / 2) + bi * 32 + (lane & 31);
-        af[bi] = ds_read_16(cur + dg_a_off(m, 2 * ks + (lane >> 5)));
-      }
+    for (int bi = 0; bi < BI; ++bi) af[0][bi] = ds_read_16(cur + aofs[0][bi]);
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj) {
+      bf[0][2 * bj] = tr_read_at<0>(pb[bj]);
+      bf[0][2 * bj + 1] = tr_read_at<1024>(pb[bj]);
+    }
+#pragma unroll
+    for (int bi = 0; bi < BI; ++bi) af[1][bi] = ds_read_16(cur + aofs[1][bi]);
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj) {
+      bf[1][2 * bj] = tr_read_at<4096>(pb[bj]);
+      bf[1][2 * bj + 1] = tr_read_at<5120>(pb[bj]);
+    }
+    dg_wait<BI + 4>(af[0], bf[0]);
+#pragma unroll
+    for (int bi = 0; bi < BI; ++bi)
 #pragma unroll
       for (int bj = 0; bj < 2; ++bj)
-        frag_issue(cur + SH::APB, 16 * ks, wc * 64 + bj * 32, lane, bf[2 * bj], bf[2 * bj + 1]);
-      dg_wait(af, bf);
+        acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[0][bi]),
+                                                              frag_join(bf[0][2 * bj], bf[0][2 * bj + 1]),
+                                                              acc[bi][bj], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);   // the wait below stays after these MFMAs
+    dg_wait<0>(af[1], bf[1]);
 #pragma unroll
-      for (int bi = 0; bi < BI; ++bi)
+    for (int bi = 0; bi < BI; ++bi)
 #pragma unroll
-        for (int bj = 0; bj < 2; ++bj)
-          acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[bi]),
-                                                                frag_join(bf[2 * bj], bf[2 * bj + 1]),
-                                                                acc[bi][bj], 0, 0, 0);
-    }
+      for (int bj = 0; bj < 2; ++bj)
+        acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[1][bi]),
+                                                              frag_join(bf[1][2 * bj], bf[1][2 * bj + 1]),
+                                                              acc[bi][bj], 0, 0, 0);
   }
   wait_vmcnt<0>();
   bar();
