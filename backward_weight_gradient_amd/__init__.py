@@ -31,7 +31,7 @@ STATUS_NAMES = ["FORGE_OK", "FORGE_E_NULL", "FORGE_E_SHAPE", "FORGE_E_DTYPE", "F
                 "FORGE_E_SCRATCH"]
 (FORGE_E_NULL, FORGE_E_SHAPE, FORGE_E_DTYPE, FORGE_E_ALIGN, FORGE_E_STEP, FORGE_E_HYPER,
  FORGE_E_ALIAS, FORGE_E_UNSUPPORTED, FORGE_E_HIP, FORGE_E_SCRATCH) = range(1, 11)
-FORGE_DGRAD_SCRATCH_BYTES = 32 << 20   # the static scratch of forge_dgrad_split_noalloc
+FORGE_DGRAD_SCRATCH_BYTES = 64 << 20   # the static scratch of forge_dgrad_split_noalloc
 FORGE_QUOTIENT_COUNTS = 2048 * 8       # counters written by forge_debug_quotients
 
 FORGE_F32, FORGE_BF16, FORGE_S8, FORGE_U8, FORGE_E4M3 = 0, 1, 2, 3, 4

@@ -146,24 +146,53 @@ hipError_t launch_dgrad_fp8w(const DgArgs& g, hipStream_t stream);
 // The split path with the partials in the library's own per-device scratch
 // array (no caller workspace, no allocation); g.splits * BT * K * 4 must not
 // exceed DGRAD_SCRATCH_BYTES.
-constexpr int64_t DGRAD_SCRATCH_BYTES = 32ll << 20;
+constexpr int64_t DGRAD_SCRATCH_BYTES = 64ll << 20;
 hipError_t launch_dgrad_scratch(DgArgs g, bool fast, hipStream_t stream);
 
-// Reduction splits of the MFMA dX kernel for dY [BT, N], W [N, K]: 1 (no
-// split) when 128-token tiles already give every CU a workgroup, else up to
-// 4, so that 128-token tiles x splits fill the chip twice (two workgroups
-// per CU), each split covering at least 32 chunks (1024 reduction elements;
-// measured: 8-chunk splits of k / v_proj at BT 512 run 50% slower than the
-// unsplit 64-token kernel).
-inline int dgrad_splits(int64_t BT, int64_t N, int64_t K) {
-  const int64_t t128 = ((BT + 127) / 128) * ((K + 127) / 128);
-  if (t128 == 0 || t128 >= 256) return 1;
+// Plan of the split dX for dY [BT, N], W [N, K].
+//  wide (k_dgrad_wide, 256 x 256 tiles, one workgroup per CU): for a long
+//    reduction (at least 64 chunks of 32), BT >= 256 and fewer 128-token
+//    tiles than two per CU (the 128-token kernel cannot fill the chip
+//    twice; larger shapes keep it, unsplit), the split count
+//    s <= 8 (each split at least 32 chunks) that minimises
+//    ceil(tiles s / 256) ceil(chunks / s) -- rounds of workgroups times
+//    chunks per split -- the smallest such s, taken when s > 1 and
+//    tiles x s gives at least 3/4 of the CUs a workgroup (measured at
+//    BT 512: q / o_proj, 16-chunk splits on 256 workgroups, are slower than
+//    the 128-token kernel, because each split's fp32 partial tile is
+//    written and read back);
+//  else 128-token tiles (k_dgrad_bf16<128>): 1 (no split) when those already
+//    give every CU a workgroup, else up to 4, so that tiles x splits fill the
+//    chip twice (two workgroups per CU), each split covering at least 32
+//    chunks (measured: 8-chunk splits of k / v_proj at BT 512 run 50% slower
+//    than the unsplit 64-token kernel).
+struct DgPlan {
+  bool wide;
+  int splits;
+};
+inline DgPlan dgrad_plan(int64_t BT, int64_t N, int64_t K) {
   const int64_t nk = (N + 31) / 32;
+  const int64_t t128 = ((BT + 127) / 128) * ((K + 127) / 128);
+  const int64_t t256 = ((BT + 255) / 256) * ((K + 255) / 256);
+  if (BT >= 256 && nk >= 64 && t128 < 512 && t256 > 0) {
+    int best = 1;
+    int64_t best_cost = -1;
+    for (int s = 1; s <= 8 && nk / s >= 32; ++s) {
+      const int64_t cost = ((t256 * s + 255) / 256) * ((nk + s - 1) / s);
+      if (best_cost < 0 || cost < best_cost) {
+        best_cost = cost;
+        best = s;
+      }
+    }
+    if (best > 1 && t256 * best >= 192) return {true, best};
+  }
+  if (t128 == 0 || t128 >= 256) return {false, 1};
   int64_t s = (512 + t128 - 1) / t128;
   if (s > 4) s = 4;
   while (s > 1 && nk / s < 32) --s;
-  return (int)s;
+  return {false, (int)s};
 }
+inline int dgrad_splits(int64_t BT, int64_t N, int64_t K) { return dgrad_plan(BT, N, K).splits; }
 
 inline bool combo_supported(int in_fmt, int w_fmt, int opt, int m_fmt, int v_fmt) {
   if (in_fmt != FMT_F32 && in_fmt != FMT_BF16) return false;

@@ -316,6 +316,183 @@ __global__ void __launch_bounds__(NT * KG, KG == 1 ? 2 : 1) k_dgrad_bf16(const D
   }
 }
 
+// ---------------------------------------------------------------------------
+// k_dgrad_wide (split path, long reduction): one 256 x 256 tile of dX per
+// workgroup of 8 waves in a 2 x 4 arrangement of 128 tokens x 64 features
+// (8 accumulator blocks per wave, two waves per SIMD, one workgroup per CU),
+// the shape of the weight-gradient wide kernel.  Per 32-element reduction
+// chunk a stage holds dY's 256 token rows x 64 B (swizzled in 16-byte units,
+// dg_a_off) and W's 32 rows x 256 columns (the weight-gradient layout, read
+// with the transposing LDS read): 32 KiB, 4 stages.  Per token and feature
+// the tile moves half the L2 -> LDS bytes of the 128 x 128 tile.  Splits of
+// the reduction write fp32 partials, which k_dgrad_reduce adds in split order.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int DW_W = 256;                  // tile edge: tokens x features
+constexpr int DW_S = 4;                    // ring stages (3 chunks in flight)
+constexpr int DW_NW = 8;                   // waves
+constexpr int DW_APB = DW_W * DG_TN * 2;   // dY's chunk: 256 token rows x 64 B = 16 KiB
+constexpr int DW_BROWB = DW_W * 2;         // a row of W's chunk: 256 features
+constexpr int DW_BPB = DG_TN * DW_BROWB;   // 16 KiB
+constexpr int DW_STAGE = DW_APB + DW_BPB;
+constexpr int DW_LOADS = 4;                // buffer loads per thread per chunk (2 dY, 2 W)
+static_assert(DW_S * DW_STAGE <= 160 * 1024, "one workgroup per CU");
+
+// byte offset of (row t, feature f) in W's chunk region, 64-byte XOR swizzle
+__device__ __forceinline__ uint32_t dw_b_off(int t, int f) {
+  return (uint32_t)(t * DW_BROWB + ((f * 2) ^ ((t & 3) << 6)));
+}
+
+template <int OFF>
+__device__ __forceinline__ u32x4 ds_read_16_at(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+  return v;
+}
+
+template <int N>
+__device__ __forceinline__ void dw_wait(u32x4 (&a)[4], u32x2 (&b)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(%8)"
+               : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3])
+               : "i"(N));
+}
+
+// The fragments of one k-step: dY blocks bi (16-byte reads at 32-row =
+// 2048-byte steps from pa), W blocks bj (transposing reads, hi half 4 rows =
+// 2048 bytes on, the second k-step 16 rows = 8192 bytes on).
+template <int KS>
+__device__ __forceinline__ void dw_reads(uint32_t pa, uint32_t pb0, uint32_t pb1, u32x4 (&a)[4], u32x2 (&b)[4]) {
+  a[0] = ds_read_16_at<0>(pa);
+  a[1] = ds_read_16_at<2048>(pa);
+  a[2] = ds_read_16_at<4096>(pa);
+  a[3] = ds_read_16_at<6144>(pa);
+  b[0] = tr_read_at<8192 * KS>(pb0);
+  b[1] = tr_read_at<8192 * KS + 2048>(pb0);
+  b[2] = tr_read_at<8192 * KS>(pb1);
+  b[3] = tr_read_at<8192 * KS + 2048>(pb1);
+}
+
+__device__ __forceinline__ void dw_mfma(f32x16 (&acc)[4][2], const u32x4 (&a)[4], const u32x2 (&b)[4]) {
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj)
+      acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[bi]),
+                                                            frag_join(b[2 * bj], b[2 * bj + 1]), acc[bi][bj], 0, 0,
+                                                            0);
+}
+}  // namespace
+
+__global__ void __launch_bounds__(DW_NW * 64, 1) k_dgrad_wide(const DgArgs g) {
+  __shared__ __attribute__((aligned(16))) char lds[DW_S * DW_STAGE];
+  const int tiles_m = (g.BT + DW_W - 1) / DW_W;
+  const int tj = (int)blockIdx.x / tiles_m, ti = (int)blockIdx.x - tj * tiles_m;
+  const int tok0 = ti * DW_W, col0 = tj * DW_W;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wr = wave >> 2, wc = wave & 3;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)lds;
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[bi][bj][e] = 0.f;
+  // this split's chunks: [c0, c0 + nj)
+  const int nk = (g.N + DG_TN - 1) / DG_TN;
+  const int sp = (int)blockIdx.y;
+  const int cps = (nk + g.splits - 1) / g.splits;
+  const int c0 = sp * cps;
+  const int nj = max(0, min(cps, nk - c0));
+  // loads: instruction (wave, r) fills KiB NW r + wave of each region;
+  // dY: 16 token rows x 4 segments per KiB, W: 2 rows x 32 chunks of 8 features
+  const uint32_t oobA = (uint32_t)((uint64_t)g.BT * g.lddy * 2);
+  const uint32_t oobB = (uint32_t)((uint64_t)g.N * g.ldw * 2);
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.dY, oobA), rB = make_rsrc(g.W, oobB);
+  uint32_t aTok[2], aSeg[2], bCol[2];
+  int bRow[2];
+  bool aOk[2], bOk[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int blk = DW_NW * r + wave;
+    const int m = blk * 16 + (lane >> 2);
+    const int sgl = (lane & 3) ^ ((m >> 2) & 3);        // logical 16-byte segment stored at this slot
+    aOk[r] = tok0 + m < g.BT;
+    aTok[r] = (uint32_t)((uint64_t)(tok0 + m) * g.lddy * 2);
+    aSeg[r] = (uint32_t)(sgl * 16);
+    const int t = blk * 2 + (lane >> 5);
+    const int c = (lane & 31) ^ ((t & 3) << 2);          // logical 8-feature chunk stored at this slot
+    bRow[r] = t;
+    bOk[r] = col0 + c * 8 < g.K;
+    bCol[r] = (uint32_t)(col0 + c * 8) * 2;
+  }
+  const auto issue = [&](int kc, char* stage) {
+    const int n0 = kc * DG_TN;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const uint32_t oa = (aOk[r] && n0 + (int)(aSeg[r] >> 1) < g.N) ? aTok[r] + (uint32_t)n0 * 2 + aSeg[r] : oobA;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void*)(stage + (DW_NW * r + wave) * 1024), 16, oa, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int n = n0 + bRow[r];
+      const uint32_t ob = (bOk[r] && n < g.N) ? (uint32_t)n * (uint32_t)(g.ldw * 2) + bCol[r] : oobB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void*)(stage + DW_APB + (DW_NW * r + wave) * 1024), 16, ob,
+                                               0, 0, 0);
+    }
+  };
+  // this lane's fragment offsets within a stage: dY rows wr 128 + lane % 32
+  // (+ 32 bi), 16-byte segment 2 ks + lane / 32 (its swizzle differs between
+  // the k-steps); W as in the weight-gradient mainloop, per 32-feature block bj
+  uint32_t aofs[2], bofs[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) aofs[ks] = dg_a_off(wr * 128 + (lane & 31), 2 * ks + (lane >> 5));
+  {
+    const int t = 8 * (lane >> 5) + ((lane & 15) >> 2);
+    const int f = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj) bofs[bj] = DW_APB + dw_b_off(t, wc * 64 + bj * 32 + f);
+  }
+#pragma unroll
+  for (int k = 0; k < DW_S - 1; ++k)
+    if (k < nj) issue(c0 + k, lds + k * DW_STAGE);
+  for (int j = 0; j < nj; ++j) {
+    dg_wait_ahead<DW_LOADS, DW_S - 2>(min(DW_S - 2, nj - 1 - j));   // chunk j landed
+    bar();                                                          // ... for all waves; stage j - 1 free
+    if (j + DW_S - 1 < nj) issue(c0 + j + DW_S - 1, lds + ((j + DW_S - 1) % DW_S) * DW_STAGE);
+    const uint32_t cur = lds0 + (uint32_t)((j % DW_S) * DW_STAGE);
+    u32x4 a0[4], a1[4];
+    u32x2 b0[4], b1[4];
+    const uint32_t pb0 = cur + bofs[0], pb1 = cur + bofs[1];
+    dw_reads<0>(cur + aofs[0], pb0, pb1, a0, b0);
+    dw_reads<1>(cur + aofs[1], pb0, pb1, a1, b1);
+    dw_wait<8>(a0, b0);
+    dw_mfma(acc, a0, b0);
+    __builtin_amdgcn_sched_barrier(0);   // the wait below stays after these MFMAs
+    dw_wait<0>(a1, b1);
+    dw_mfma(acc, a1, b1);
+  }
+  wait_vmcnt<0>();
+  // lane l, register 4j + i of a 32 x 32 block holds row 8j + 4 (l / 32) + i,
+  // column l % 32: 32 lanes store 32 consecutive columns of a row
+  const bool part = g.splits > 1;
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int tok = tok0 + wr * 128 + bi * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        const int col = col0 + wc * 64 + bj * 32 + (lane & 31);
+        if (tok >= g.BT || col >= g.K) continue;
+        const float x = acc[bi][bj][e];
+        if (part) g.ws[((int64_t)sp * g.BT + tok) * g.K + col] = x;
+        else if (g.dx_fmt == FMT_F32) static_cast<float*>(g.dX)[(int64_t)tok * g.ldx + col] = x;
+        else static_cast<uint16_t*>(g.dX)[(int64_t)tok * g.ldx + col] = (uint16_t)bf16_rne_bits(x);
+      }
+}
+
 // dX = sum over s = 0 .. splits - 1 of ws[s] (in that order), 4 elements per
 // thread (K % 8 == 0 on the split path: a 4-element group never crosses a row).
 __global__ void __launch_bounds__(NT) k_dgrad_reduce(const DgArgs g) {
@@ -579,7 +756,12 @@ hipError_t launch_dgrad(const DgArgs& g, bool fast, hipStream_t st) {
     // with 4 MFMAs per wave and chunk the per-chunk overhead dominates)
     const int64_t t128 = (int64_t)((g.BT + 127) / 128) * g.tiles_k;
     const int64_t t64 = (int64_t)((g.BT + 63) / 64) * g.tiles_k;
-    if (g.splits > 1) {
+    if (g.splits > 1 && dgrad_plan(g.BT, g.N, g.K).wide) {
+      const unsigned t256 = (unsigned)(((g.BT + DW_W - 1) / DW_W) * ((g.K + DW_W - 1) / DW_W));
+      hipLaunchKernelGGL(k_dgrad_wide, dim3(t256, (unsigned)g.splits), dim3(DW_NW * 64), 0, st, g);
+      const int64_t n4 = (int64_t)g.BT * g.K / 4;
+      hipLaunchKernelGGL(k_dgrad_reduce, dim3((unsigned)((n4 + NT - 1) / NT)), dim3(NT), 0, st, g);
+    } else if (g.splits > 1) {
       hipLaunchKernelGGL((k_dgrad_bf16<128, 4, 1>), dim3((unsigned)t128, (unsigned)g.splits), dim3(NT), 0, st, g);
       const int64_t n4 = (int64_t)g.BT * g.K / 4;
       hipLaunchKernelGGL(k_dgrad_reduce, dim3((unsigned)((n4 + NT - 1) / NT)), dim3(NT), 0, st, g);

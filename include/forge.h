@@ -306,9 +306,10 @@ forge_status forge_dgrad(const forge_mat* dY, const forge_mat* W, forge_mat* dX,
 /*
  * forge_dgrad_workspace_bytes -- bytes of device workspace forge_dgrad_split
  * uses for dY [BT, N] and W [N, K] on the MFMA path: splits x BT x K x 4 when
- * the reduction over N is split across workgroups (short token axis, few
- * 128 x 128 output tiles, long reduction), else 0.  Non-positive or
- * too-large sizes give 0.  Host-only, no device call.
+ * the reduction over N is split across workgroups (too few output tiles to
+ * fill the chip and a long reduction: up to 8 splits of 256 x 256 tiles, or
+ * up to 4 of 128-token tiles), else 0.  Non-positive or too-large sizes
+ * give 0.  Host-only, no device call.
  */
 int64_t forge_dgrad_workspace_bytes(int64_t BT, int64_t N, int64_t K);
 
@@ -337,7 +338,7 @@ forge_status forge_dgrad_split(const forge_mat* dY, const forge_mat* W, forge_ma
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc): the same kernels, splits and reduction
  * order, so the same dX bit for bit, with the split partials in a
- * file-scope device array of FORGE_DGRAD_SCRATCH_BYTES (32 MiB) that the
+ * file-scope device array of FORGE_DGRAD_SCRATCH_BYTES (64 MiB) that the
  * library holds on each GPU it runs on until the process ends, instead of a
  * caller workspace.  The call allocates nothing.  Every call on a GPU shares
  * that GPU's array, so calls that may overlap on one GPU (several streams,
@@ -347,7 +348,7 @@ forge_status forge_dgrad_split(const forge_mat* dY, const forge_mat* W, forge_ma
  * anything is enqueued; every Llama-3.1-8B layer at BT <= 512 fits.
  * Arguments and other errors as forge_dgrad.
  */
-#define FORGE_DGRAD_SCRATCH_BYTES (32ll << 20)
+#define FORGE_DGRAD_SCRATCH_BYTES (64ll << 20)
 forge_status forge_dgrad_split_noalloc(const forge_mat* dY, const forge_mat* W, forge_mat* dX, void* stream);
 
 /*

@@ -416,11 +416,16 @@ def test_dgrad_validation():
 def test_dgrad_split_workspace_and_validation():
     # workspace sizes: splits x BT x K x 4 bytes where the reduction is split, else 0
     wb = F.forge_dgrad_workspace_bytes
-    assert wb(512, 14336, 4096) == 4 * 512 * 4096 * 4      # gate / up at BT 512: 128 tiles, 4 splits
-    assert wb(512, 4096, 4096) == 4 * 512 * 4096 * 4       # q / o: 128 chunks, 32 per split
+    # 256 x 256 tiles: splits s <= 8 of >= 32 chunks minimising rounds x chunks per split
+    assert wb(512, 14336, 4096) == 8 * 512 * 4096 * 4      # gate / up at BT 512: 32 tiles, 8 splits of 56 chunks
+    assert wb(512, 4096, 14336) == 2 * 512 * 14336 * 4    # down: 112 tiles, 2 splits fill the chip once
+    assert wb(300, 8192, 4104) == 7 * 300 * 4104 * 4       # 34 tiles: 7 splits (238 workgroups) of <= 37 chunks
+    # 128-token tiles
+    assert wb(512, 4096, 4096) == 4 * 512 * 4096 * 4       # q / o: 4 splits of 32 chunks (too few 256-tile splits)
     assert wb(512, 2048, 4096) == 2 * 512 * 4096 * 4       # 64 chunks: 2 splits of 32
     assert wb(512, 1024, 4096) == 0                        # k / v: 32 chunks, too short to split
-    assert wb(2048, 4096, 4096) == 0                       # 256 tiles of 128 tokens: no split
+    assert wb(300, 2048, 1024) == 2 * 300 * 1024 * 4       # 24 tiles: 2 splits of 32 chunks
+    assert wb(2048, 4096, 4096) == 0                       # 512 tiles of 128 tokens: no split
     assert wb(0, 4096, 4096) == 0 and wb(512, 0, 4096) == 0 and wb(-1, 8, 8) == 0
     # validation (nothing reaches the device): dY [512, 2048], W [2048, 1024], dX [512, 1024]
     dY = F.mat_raw(addr(1), F.FORGE_BF16, 512, 2048)
@@ -568,20 +573,20 @@ def test_dgrad_noalloc_validation():
     """The allocation-free dX call validates like forge_dgrad and rejects, on
     the host, a split that needs more than its static scratch array."""
     nd = F.lib.forge_dgrad_split_noalloc
-    dY = F.mat_raw(addr(0), F.FORGE_BF16, 512, 4096)
-    W = F.mat_raw(addr(1), F.FORGE_BF16, 4096, 8064)
-    dX = F.mat_raw(addr(2), F.FORGE_BF16, 512, 8064)
-    assert F.forge_dgrad_workspace_bytes(512, 4096, 8064) > F.FORGE_DGRAD_SCRATCH_BYTES
+    dY = F.mat_raw(addr(0), F.FORGE_BF16, 512, 8192)
+    W = F.mat_raw(addr(1), F.FORGE_BF16, 8192, 12288)
+    dX = F.mat_raw(addr(2), F.FORGE_BF16, 512, 12288)
+    assert F.forge_dgrad_workspace_bytes(512, 8192, 12288) > F.FORGE_DGRAD_SCRATCH_BYTES
     assert nd(ctypes.byref(dY), ctypes.byref(W), ctypes.byref(dX), None) == F.FORGE_E_SCRATCH
-    # the Llama-3.1-8B shapes at BT 512 fit (32 MiB exactly for q / o / gate / up)
+    # the Llama-3.1-8B shapes at BT 512 fit (64 MiB exactly for gate / up: 8 splits)
     for N, K in ((4096, 4096), (14336, 4096), (1024, 4096), (4096, 14336)):
         assert F.forge_dgrad_workspace_bytes(512, N, K) <= F.FORGE_DGRAD_SCRATCH_BYTES
-    assert F.forge_dgrad_workspace_bytes(512, 4096, 4096) == F.FORGE_DGRAD_SCRATCH_BYTES
+    assert F.forge_dgrad_workspace_bytes(512, 14336, 4096) == F.FORGE_DGRAD_SCRATCH_BYTES
     # errors of forge_dgrad come first
-    bad = F.mat_raw(addr(2), F.FORGE_BF16, 511, 8064)
+    bad = F.mat_raw(addr(2), F.FORGE_BF16, 511, 12288)
     assert nd(ctypes.byref(dY), ctypes.byref(W), ctypes.byref(bad), None) == F.FORGE_E_SHAPE
     assert nd(None, ctypes.byref(W), ctypes.byref(dX), None) == F.FORGE_E_NULL
-    alias = F.mat_raw(addr(1), F.FORGE_BF16, 512, 8064)
+    alias = F.mat_raw(addr(1), F.FORGE_BF16, 512, 12288)
     assert nd(ctypes.byref(dY), ctypes.byref(W), ctypes.byref(alias), None) == F.FORGE_E_ALIAS
 
 

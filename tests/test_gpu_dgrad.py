@@ -159,7 +159,12 @@ def test_backward_step_orders_dgrad_before_the_update(opt, spec, N, K, BT):
 # forge_dgrad_split: the reduction split across workgroups into a workspace
 # ---------------------------------------------------------------------------
 # (130, 2056, 520): ragged token and column tiles, two splits of 33 and 32 chunks, the last one partial
-@pytest.mark.parametrize("BT,N,K", [(300, 2048, 1024), (130, 2056, 520), (64, 4096, 128), (512, 8192, 2048)])
+# (300, 2048, 1024), (130, 2056, 520), (64, 4096, 128), (512, 8192, 2048):
+# 128-token tiles; (512, 8192, 3072), (520, 8200, 2056), (300, 8192, 4104):
+# 256 x 256 tiles (k_dgrad_wide), the last two ragged in tokens, reduction
+# and columns
+@pytest.mark.parametrize("BT,N,K", [(300, 2048, 1024), (130, 2056, 520), (64, 4096, 128), (512, 8192, 2048),
+                                    (512, 8192, 3072), (520, 8200, 2056), (300, 8192, 4104)])
 @pytest.mark.parametrize("dx_dtype", ["bf16", "f32"])
 def test_dgrad_split_matches_oracle(BT, N, K, dx_dtype):
     _say(f"case: dgrad split {BT}x{N}x{K} dX {dx_dtype}")
@@ -177,7 +182,7 @@ def test_dgrad_split_matches_oracle(BT, N, K, dx_dtype):
     assert torch.equal(dX.view(torch.uint8), again.view(torch.uint8)), "split result differs between calls"
 
 
-@pytest.mark.parametrize("name", ["q_proj", "gate_proj"])
+@pytest.mark.parametrize("name", ["q_proj", "gate_proj", "down_proj"])
 def test_dgrad_split_full_size_llama_bt512(name):
     N, K = synth.LLAMA8B_LAYERS[name]
     _say(f"case: dgrad split {name} {N}x{K} BT512")
@@ -242,10 +247,11 @@ def test_backward_step_split_orders_split_dgrad_before_the_update():
     _check(dX, L.dY, W_before, what="backward step split")
 
 
-def test_dgrad_split_strided_buffers():
-    """Leading dimensions larger than the row length on dY, W and dX; dX columns past K stay untouched."""
-    _say("case: dgrad split strided")
-    BT, N, K = 200, 2048, 1024
+@pytest.mark.parametrize("BT,N,K", [(200, 2048, 1024), (512, 8192, 3072)])
+def test_dgrad_split_strided_buffers(BT, N, K):
+    """Leading dimensions larger than the row length on dY, W and dX; dX columns past K stay untouched
+    (128-token tiles, then 256 x 256 tiles)."""
+    _say(f"case: dgrad split strided {BT}x{N}x{K}")
     need = F.forge_dgrad_workspace_bytes(BT, N, K)
     assert need > 0
     dYb, Wb = _operands(BT, N + 8, K + 16, "bf16", "bf16")

@@ -51,8 +51,9 @@ def _check_oracle(dY, W, dX, rows):
 
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 def test_noalloc_dgrad_equals_workspace_variant(out_dtype):
-    # 32 MiB of partials (the maximum), then 8 MiB, then no split, then too much
-    for i, (BT, N, K) in enumerate(((512, 4096, 4096), (256, 4096, 2048), (512, 1024, 4096))):
+    # 64 MiB of partials (the maximum, 256 x 256 tiles), then 8 MiB (128-token
+    # tiles), then no split, then too much
+    for i, (BT, N, K) in enumerate(((512, 14336, 4096), (256, 4096, 2048), (512, 1024, 4096))):
         _say(f"case: noalloc dX {BT}x{N}x{K} {out_dtype}")
         need = F.forge_dgrad_workspace_bytes(BT, N, K)
         assert need <= F.FORGE_DGRAD_SCRATCH_BYTES
@@ -67,7 +68,7 @@ def test_noalloc_dgrad_equals_workspace_variant(out_dtype):
         _check_oracle(dY, W, got, np.array([0, 1, BT // 2, BT - 1]))
         del dY, W, ws, ref, got
     _say("case: noalloc dX beyond the scratch")
-    BT, N, K = 512, 4096, 8064
+    BT, N, K = 512, 8192, 12288
     assert F.forge_dgrad_workspace_bytes(BT, N, K) > F.FORGE_DGRAD_SCRATCH_BYTES
     dY, W = _operands(BT, N, K, 9)
     dX = torch.full((BT, K), 3.0, device="cuda", dtype=out_dtype)
