@@ -161,11 +161,13 @@ hipError_t launch_dgrad_scratch(DgArgs g, bool fast, hipStream_t stream);
 //    BT 512: q / o_proj, 16-chunk splits on 256 workgroups, are slower than
 //    the 128-token kernel, because each split's fp32 partial tile is
 //    written and read back);
-//  else 128-token tiles (k_dgrad_bf16<128>): 1 (no split) when those already
-//    give every CU a workgroup, else up to 4, so that tiles x splits fill the
-//    chip twice (two workgroups per CU), each split covering at least 32
-//    chunks (measured: 8-chunk splits of k / v_proj at BT 512 run 50% slower
-//    than the unsplit 64-token kernel).
+//  else 128-token tiles (k_dgrad_bf16<128>): 1 (no split) when those, or the
+//    unsplit kernel's 64-token tiles, already give every CU a workgroup
+//    (measured at BT 512: q / o_proj unsplit on 64-token tiles 34 us, in 4
+//    splits 39 us), else up to 4, so that tiles x splits fill the chip twice
+//    (two workgroups per CU), each split covering at least 32 chunks
+//    (measured: 8-chunk splits of k / v_proj at BT 512 run 50% slower than
+//    the unsplit 64-token kernel).
 struct DgPlan {
   bool wide;
   int splits;
@@ -186,7 +188,8 @@ inline DgPlan dgrad_plan(int64_t BT, int64_t N, int64_t K) {
     }
     if (best > 1 && t256 * best >= 192) return {true, best};
   }
-  if (t128 == 0 || t128 >= 256) return {false, 1};
+  const int64_t t64 = ((BT + 63) / 64) * ((K + 127) / 128);
+  if (t128 == 0 || t128 >= 256 || t64 >= 256) return {false, 1};
   int64_t s = (512 + t128 - 1) / t128;
   if (s > 4) s = 4;
   while (s > 1 && nk / s < 32) --s;

@@ -16,7 +16,8 @@
 // lane, its 64-byte rows XOR-swizzled in 16-byte units so that 16 lanes
 // reading 16 consecutive rows cover all 64 banks.
 //
-// Split reduction (128-token tiles only): blockIdx.y = split s takes the
+// Split reduction (128-token tiles only): split s (the work index over the
+// tiles, see xcd_work) takes the
 // chunks [s c, min(nk, (s + 1) c)), c = ceil(nk / splits), and writes its
 // fp32 partial tile to the workspace; k_dgrad_reduce then adds the splits'
 // partials in split order (deterministic) and stores dX.  For the short-token,
@@ -142,8 +143,17 @@ __device__ __forceinline__ void dg_wait(u32x4 (&a)[1], u32x2 (&b)[4]) {
   asm volatile("s_waitcnt lgkmcnt(%5)" : "+v"(a[0]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]) : "i"(N));
 }
 
-
 }  // namespace
+
+// Workgroup L of T goes to XCD L % 8 (round-robin dispatch).  Give XCD x the
+// x-th contiguous block of the work order (token tile fastest, then feature
+// tile, then split): with 8 splits each XCD's L2 then serves one split's
+// slice of the reduction, read from HBM once; with fewer, each XCD holds a
+// run of feature tiles for both token tiles.
+__device__ __forceinline__ int xcd_work(int L, int T) {
+  const int q = T >> 3, r = T & 7, x = L & 7, slot = L >> 3;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + slot;
+}
 
 // KG reduction groups of 4 waves per workgroup (at most 4: 1024 threads): group k takes the chunks
 // k, k + KG, k + 2 KG, ... through a ring of its own (chunks past the end
@@ -160,8 +170,10 @@ __global__ void __launch_bounds__(NT * KG, KG == 1 ? 2 : 1) k_dgrad_bf16(const D
   constexpr int RINGS = KG * S * SH::STAGE;
   __shared__ __attribute__((aligned(16))) char lds[RINGS > SH::LDS ? RINGS : SH::LDS];
   // W panels are shared by the token tiles of one column: those run together
-  const int tiles_m = (g.BT + TM - 1) / TM;
-  const int tj = (int)blockIdx.x / tiles_m, ti = (int)blockIdx.x - tj * tiles_m;
+  const int tiles_m = (g.BT + TM - 1) / TM, tiles = tiles_m * ((g.K + TILE - 1) / TILE);
+  const int w = xcd_work((int)blockIdx.x, (int)gridDim.x);
+  const int tile = w % tiles, sp = w / tiles;
+  const int tj = tile / tiles_m, ti = tile - tj * tiles_m;
   const int tok0 = ti * TM, col0 = tj * TILE;
   const int kg = (int)threadIdx.x / NT, gtid = (int)threadIdx.x - kg * NT;
   const int lane = gtid & 63, wave = gtid >> 6;
@@ -177,7 +189,6 @@ __global__ void __launch_bounds__(NT * KG, KG == 1 ? 2 : 1) k_dgrad_bf16(const D
       for (int e = 0; e < 16; ++e) acc[bi][bj][e] = 0.f;
   const int nk = (g.N + DG_TN - 1) / DG_TN;
   // this workgroup's chunks: c0 + kg + KG j, j < nj (a split range only with KG = 1)
-  const int sp = (int)blockIdx.y;
   const int cps = (nk + g.splits - 1) / g.splits;
   const int c0 = KG == 1 ? sp * cps : 0;
   const int nj = KG == 1 ? max(0, min(cps, nk - c0)) : (nk + KG - 1) / KG;
@@ -386,8 +397,10 @@ __device__ __forceinline__ void dw_mfma(f32x16 (&acc)[4][2], const u32x4 (&a)[4]
 
 __global__ void __launch_bounds__(DW_NW * 64, 1) k_dgrad_wide(const DgArgs g) {
   __shared__ __attribute__((aligned(16))) char lds[DW_S * DW_STAGE];
-  const int tiles_m = (g.BT + DW_W - 1) / DW_W;
-  const int tj = (int)blockIdx.x / tiles_m, ti = (int)blockIdx.x - tj * tiles_m;
+  const int tiles_m = (g.BT + DW_W - 1) / DW_W, tiles_n = (g.K + DW_W - 1) / DW_W;
+  const int w = xcd_work((int)blockIdx.x, (int)gridDim.x);
+  const int tile = w % (tiles_m * tiles_n), sp = w / (tiles_m * tiles_n);
+  const int tj = tile / tiles_m, ti = tile - tj * tiles_m;
   const int tok0 = ti * DW_W, col0 = tj * DW_W;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wr = wave >> 2, wc = wave & 3;
@@ -401,7 +414,6 @@ __global__ void __launch_bounds__(DW_NW * 64, 1) k_dgrad_wide(const DgArgs g) {
       for (int e = 0; e < 16; ++e) acc[bi][bj][e] = 0.f;
   // this split's chunks: [c0, c0 + nj)
   const int nk = (g.N + DG_TN - 1) / DG_TN;
-  const int sp = (int)blockIdx.y;
   const int cps = (nk + g.splits - 1) / g.splits;
   const int c0 = sp * cps;
   const int nj = max(0, min(cps, nk - c0));
@@ -758,11 +770,11 @@ hipError_t launch_dgrad(const DgArgs& g, bool fast, hipStream_t st) {
     const int64_t t64 = (int64_t)((g.BT + 63) / 64) * g.tiles_k;
     if (g.splits > 1 && dgrad_plan(g.BT, g.N, g.K).wide) {
       const unsigned t256 = (unsigned)(((g.BT + DW_W - 1) / DW_W) * ((g.K + DW_W - 1) / DW_W));
-      hipLaunchKernelGGL(k_dgrad_wide, dim3(t256, (unsigned)g.splits), dim3(DW_NW * 64), 0, st, g);
+      hipLaunchKernelGGL(k_dgrad_wide, dim3(t256 * (unsigned)g.splits), dim3(DW_NW * 64), 0, st, g);
       const int64_t n4 = (int64_t)g.BT * g.K / 4;
       hipLaunchKernelGGL(k_dgrad_reduce, dim3((unsigned)((n4 + NT - 1) / NT)), dim3(NT), 0, st, g);
     } else if (g.splits > 1) {
-      hipLaunchKernelGGL((k_dgrad_bf16<128, 4, 1>), dim3((unsigned)t128, (unsigned)g.splits), dim3(NT), 0, st, g);
+      hipLaunchKernelGGL((k_dgrad_bf16<128, 4, 1>), dim3((unsigned)t128 * (unsigned)g.splits), dim3(NT), 0, st, g);
       const int64_t n4 = (int64_t)g.BT * g.K / 4;
       hipLaunchKernelGGL(k_dgrad_reduce, dim3((unsigned)((n4 + NT - 1) / NT)), dim3(NT), 0, st, g);
     } else if (t128 >= 256) {

@@ -421,8 +421,9 @@ def test_dgrad_split_workspace_and_validation():
     assert wb(512, 4096, 14336) == 2 * 512 * 14336 * 4    # down: 112 tiles, 2 splits fill the chip once
     assert wb(300, 8192, 4104) == 7 * 300 * 4104 * 4       # 34 tiles: 7 splits (238 workgroups) of <= 37 chunks
     # 128-token tiles
-    assert wb(512, 4096, 4096) == 4 * 512 * 4096 * 4       # q / o: 4 splits of 32 chunks (too few 256-tile splits)
-    assert wb(512, 2048, 4096) == 2 * 512 * 4096 * 4       # 64 chunks: 2 splits of 32
+    assert wb(512, 4096, 4096) == 0                        # q / o: 256 tiles of 64 tokens fill the chip unsplit
+    assert wb(512, 2048, 4096) == 0
+    assert wb(256, 4096, 4096) == 4 * 256 * 4096 * 4       # 128 tiles of 64 tokens: 4 splits of 32 chunks
     assert wb(512, 1024, 4096) == 0                        # k / v: 32 chunks, too short to split
     assert wb(300, 2048, 1024) == 2 * 300 * 1024 * 4       # 24 tiles: 2 splits of 32 chunks
     assert wb(2048, 4096, 4096) == 0                       # 512 tiles of 128 tokens: no split
