@@ -78,6 +78,19 @@ def parse():
     return p.parse_args()
 
 
+LEAD_IN_CYCLES = 400_000   # about 0.2 ms of spinning at the engine clock
+
+
+def lead_in():
+    """Queue a short device-side spin on the current stream ahead of a
+    per-call timing: while it runs, the host records the start event and
+    enqueues the timed call, so the interval between the two events is
+    device time (the kernels and the gaps between them), not the binding's
+    argument marshalling on the host."""
+    import torch
+    torch.cuda._sleep(LEAD_IN_CYCLES)
+
+
 def copy_calibration(steps):
     """A plain device-to-device copy of known size, for calibrating the
     FETCH_SIZE / WRITE_SIZE counters against a kernel whose traffic is known."""
@@ -87,6 +100,7 @@ def copy_calibration(steps):
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    lead_in()
     e0.record()
     for _ in range(steps):
         dst.copy_(src)
@@ -159,6 +173,7 @@ def mfma_sweep(F, synth, h, reps=3):
                 times = []
                 for _ in range(reps):
                     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    lead_in()
                     e0.record(stream)
                     F.forge_wgrad_step(*args, hy, STEP_T, SEED, stream=stream.cuda_stream)
                     e1.record(stream)
@@ -228,6 +243,7 @@ def family_sweep(F, synth, reps=5):
         times = []
         for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            lead_in()
             e0.record(stream)
             F.forge_wgrad_step(*args, h, STEP_T, SEED, stream=stream.cuda_stream)
             e1.record(stream)
@@ -277,6 +293,7 @@ def fp8_weight_sweep(F, synth, h, reps=5):
         ts = []
         for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            lead_in()
             e0.record(stream)
             fn()
             e1.record(stream)
@@ -348,6 +365,7 @@ def state_format_sweep(F, synth, h, reps=10):
         times = []
         for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            lead_in()
             e0.record(stream)
             launch()
             e1.record(stream)
@@ -383,6 +401,8 @@ def accumulation_sweep(F, synth, h, micro=4, reps=5):
     accm = F.mat(acc)
 
     def run(ev=None):
+        if ev is not None:
+            lead_in()
         for i, (Xm, dYm) in enumerate(mats):
             if ev is not None:
                 ev[i][0].record(stream)
@@ -435,6 +455,7 @@ def dgrad_sweep(F, L, layers, reps=6, sets=3):
         for r in range(reps):
             fn = fns[r % len(fns)]
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            lead_in()
             e0.record(stream)
             fn()
             e1.record(stream)
@@ -478,6 +499,7 @@ def measured_ceilings(F, reps=5):
         ts = []
         for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            lead_in()
             e0.record()
             fn()
             e1.record()
@@ -530,6 +552,7 @@ def library_gemm_reference(synth, L, layers, reps=5):
         ts = []
         for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            lead_in()
             e0.record()
             fn()
             e1.record()
