@@ -505,7 +505,7 @@ __global__ void __launch_bounds__(DW_NW * 64, 1) k_dgrad_wide(const DgArgs g) {
       }
 }
 
-// dX = sum over s = 0 .. splits - 1 of ws[s] (in that order), 4 elements per
+// dX = sum over s = 0 .. splits - 1 (at most 8) of ws[s] (in that order), 4 elements per
 // thread (K % 8 == 0 on the split path: a 4-element group never crosses a row).
 __global__ void __launch_bounds__(NT) k_dgrad_reduce(const DgArgs g) {
   const int64_t n4 = (int64_t)g.BT * g.K / 4;
@@ -761,6 +761,7 @@ hipError_t launch_dgrad_fp8w(const DgArgs& g, hipStream_t st) {
 
 hipError_t launch_dgrad(const DgArgs& g, bool fast, hipStream_t st) {
   if (g.BT == 0 || g.K == 0) return hipSuccess;
+  if (g.splits < 1 || g.splits > 8) return hipErrorInvalidValue;   // k_dgrad_reduce holds at most 8 partials
   if (fast) {
     // 128-token tiles, two workgroups per CU; when those would not give every
     // CU a workgroup (short token axis, few columns), 64-token tiles, up to
