@@ -158,10 +158,9 @@ __device__ __forceinline__ int xcd_work(int L, int T) {
 // KG reduction groups of 4 waves per workgroup (at most 4: 1024 threads): group k takes the chunks
 // k, k + KG, k + 2 KG, ... through a ring of its own (chunks past the end
 // read zero, so every group runs the same iterations and barriers), and the
-// groups' partial tiles are added through LDS in a fixed order.  KG = 2
-// serves the short-token, long-reduction layers, whose few tiles would
-// otherwise leave one 4-wave workgroup per CU with every per-chunk latency
-// exposed.
+// groups' partial tiles are added through LDS in a fixed order.  KG = 2 and
+// 4 serve the short-token layers, whose few tiles would otherwise leave one
+// 4-wave workgroup per CU with every per-chunk latency exposed.
 template <int TM, int S, int KG>
 __global__ void __launch_bounds__(NT * KG, KG == 1 ? 2 : 1) k_dgrad_bf16(const DgArgs g) {
   static_assert(KG >= 1 && KG <= 4, "at most 1024 threads per workgroup");
@@ -781,7 +780,13 @@ hipError_t launch_dgrad(const DgArgs& g, bool fast, hipStream_t st) {
     } else if (t128 >= 256) {
       hipLaunchKernelGGL((k_dgrad_bf16<128, 4, 1>), dim3((unsigned)t128), dim3(NT), 0, st, g);
     } else if (t64 < 512 && g.N >= 8 * DG_TN) {
-      hipLaunchKernelGGL((k_dgrad_bf16<64, 4, 2>), dim3((unsigned)t64), dim3(2 * NT), 0, st, g);
+      // the reduction in 4 groups of 4 waves (3-stage rings, 144 KiB of LDS)
+      // up to 128 chunks, else in 2 (measured at BT 512: q / o_proj 33 -> 29
+      // us with 4 groups, gate_proj unsplit 106 -> 110 us)
+      if (g.N <= 128 * DG_TN)
+        hipLaunchKernelGGL((k_dgrad_bf16<64, 3, 4>), dim3((unsigned)t64), dim3(4 * NT), 0, st, g);
+      else
+        hipLaunchKernelGGL((k_dgrad_bf16<64, 4, 2>), dim3((unsigned)t64), dim3(2 * NT), 0, st, g);
     } else {
       hipLaunchKernelGGL((k_dgrad_bf16<64, 4, 1>), dim3((unsigned)t64), dim3(NT), 0, st, g);
     }

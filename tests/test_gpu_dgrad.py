@@ -64,10 +64,10 @@ def _operands(BT, N, K, dy_dtype, w_dtype, cfg=30):
 DT = {"bf16": torch.bfloat16, "f32": torch.float32}
 
 
-# (200, 520, 264): two reduction groups with an odd number of chunks (17: the second group's last
-# iteration reads a chunk past the end, which must contribute zero)
+# (200, 520, 264): four reduction groups over 17 chunks (the last iteration of groups 1-3 reads a
+# chunk past the end, which must contribute zero); (130, 4360, 264): two groups over 137 chunks
 @pytest.mark.parametrize("BT,N,K", [(300, 136, 264), (1, 8, 8), (130, 1000, 520), (512, 1024, 1024),
-                                    (64, 32, 128), (200, 520, 264)])
+                                    (64, 32, 128), (200, 520, 264), (130, 4360, 264)])
 @pytest.mark.parametrize("dx_dtype", ["bf16", "f32"])
 def test_dgrad_mfma_kernel(BT, N, K, dx_dtype):
     _say(f"case: dgrad MFMA {BT}x{N}x{K} dX {dx_dtype}")
