@@ -136,6 +136,12 @@ __device__ __forceinline__ uint32_t bf16x2_store(float a, float b, uint32_t srma
   return bf16x2_select(a, b, h, h << 16, srmask);
 }
 
+// How a bf16 store picks its rounding: RM_SEL from the wave-uniform mask at
+// run time (both roundings formed, one kept), RM_SR / RM_RNE fixed at
+// compile time (the fused kernels branch once per tile on the mask and run
+// an epilogue specialised to it; the stored bits are the same).
+constexpr int RM_SEL = 0, RM_SR = 1, RM_RNE = 2;
+
 __device__ __forceinline__ float bf16_val(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
 // ------------------------------------------------------------------------
@@ -1028,7 +1034,7 @@ __device__ __forceinline__ void dec4_codes(const Raw4<FMT>& r, float* x) {
 // bf16: stochastic rounding when sr is all ones (idx = flat index of the
 // first element), round to nearest even when it is zero.  FAST segments
 // start at an even flat index (K % 4 == 0), so they are two hash pairs.
-template <int FMT, bool FAST>
+template <int FMT, bool FAST, int RM = RM_SEL>
 __device__ __forceinline__ void st4(void* seg, const Seg& g, bool vec, const float* x, uint32_t sr, uint32_t key,
                                     uint32_t idx) {
   if constexpr (FMT == FMT_F32) {
@@ -1042,7 +1048,18 @@ __device__ __forceinline__ void st4(void* seg, const Seg& g, bool vec, const flo
     }
   } else if constexpr (FMT == FMT_BF16) {
     uint32_t lo, hi;
-    if constexpr (FAST) {
+    if constexpr (RM == RM_RNE) {
+      lo = bf16x2_rne(x[0], x[1]);
+      hi = bf16x2_rne(x[2], x[3]);
+    } else if constexpr (RM == RM_SR && FAST) {
+      const uint32_t jmul = (idx >> 1) * GOLDEN;
+      const uint32_t h0 = sr_pair(key, jmul), h1 = sr_pair(key, jmul + GOLDEN);
+      lo = bf16x2_sr(x[0], x[1], h0, h0 << 16);
+      hi = bf16x2_sr(x[2], x[3], h1, h1 << 16);
+    } else if constexpr (RM == RM_SR) {
+      lo = bf16x2_sr(x[0], x[1], sr_elem_word(key, idx), sr_elem_word(key, idx + 1u));
+      hi = bf16x2_sr(x[2], x[3], sr_elem_word(key, idx + 2u), sr_elem_word(key, idx + 3u));
+    } else if constexpr (FAST) {
       const uint32_t jmul = (idx >> 1) * GOLDEN;
       lo = bf16x2_store(x[0], x[1], sr, key, jmul);
       hi = bf16x2_store(x[2], x[3], sr, key, jmul + GOLDEN);
@@ -1248,6 +1265,9 @@ struct Step {
   static constexpr int WFMT = WF;
   static constexpr int MFMT = HAS_M ? MF : FMT_NONE;
   static constexpr int VFMT = HAS_V ? VF : FMT_NONE;
+  // bf16 weight and bf16 moments: the stores whose rounding is worth fixing
+  // per tile (elsewhere the second epilogue copy costs registers: spills)
+  static constexpr bool BF16_STORE = WFMT == FMT_BF16 && (MFMT == FMT_BF16 || VFMT == FMT_BF16);
 
   // Everything one chunk reads, still undecoded.
   struct Pending {
@@ -1331,6 +1351,7 @@ struct Step {
 
   // Decode, apply phi and store one chunk of row p.  Must be called by every
   // lane of the wave when a state is int8 (lane shuffles).
+  template <int RM = RM_SEL>
   __device__ __forceinline__ static void apply_store(const KArgs& a, const TileRows<FAST>& tr, int ps, const Seg (&sg)[2],
                                                      const float (&g)[8], const Pending& r) {
     float w[8], m[8], v[8];
@@ -1366,13 +1387,13 @@ struct Step {
       if (!sg[s].ok) continue;
       const uint32_t idx = rowbase + tr.qg[s];
       if constexpr (!fmt_blocked(WF))
-        st4<WF, FAST>(at(tr.w, ps * tr.dw, tr.ow, 64 * s * esz(WF)), sg[s], vec, w + 4 * s, a.c.sr, a.c.keyW,
+        st4<WF, FAST, RM>(at(tr.w, ps * tr.dw, tr.ow, 64 * s * esz(WF)), sg[s], vec, w + 4 * s, a.c.sr, a.c.keyW,
                       idx);
       if constexpr (HAS_M && !fmt_blocked(MF))
-        st4<MF, FAST>(at(tr.m, ps * tr.dm, tr.om, 64 * s * esz(MF)), sg[s], vec, m + 4 * s, a.c.sr, a.c.keyM,
+        st4<MF, FAST, RM>(at(tr.m, ps * tr.dm, tr.om, 64 * s * esz(MF)), sg[s], vec, m + 4 * s, a.c.sr, a.c.keyM,
                       idx);
       if constexpr (HAS_V && !fmt_blocked(VF))
-        st4<VF, FAST>(at(tr.v, ps * tr.dv, tr.ov, 64 * s * esz(VF)), sg[s], vec, v + 4 * s, a.c.sr, a.c.keyV,
+        st4<VF, FAST, RM>(at(tr.v, ps * tr.dv, tr.ov, 64 * s * esz(VF)), sg[s], vec, v + 4 * s, a.c.sr, a.c.keyV,
                       idx);
     }
     // a block-scaled stream: segment pointers of the codes (1 byte each) and of the scales
@@ -1519,12 +1540,13 @@ struct Epilogue {
     }
   }
 
+  template <int RM>
   __device__ __forceinline__ void consume(const KArgs& a, int row0, int col0, int s, const float (&g)[8],
                                           const typename S::Pending& cur) const {
     const int p = row0 + s * RPP + (tid >> 4);
     Seg sg[2];
     segs(a, p, col0, sg);
-    S::apply_store(a, tr, s, sg, g, cur);
+    S::template apply_store<RM>(a, tr, s, sg, g, cur);
   }
 
   // One tile with a rolling window of DEPTH passes in flight: prefetch()
@@ -1544,15 +1566,17 @@ struct Epilogue {
     for (int s = NPRE; s < DEPTH && s < PASSES; ++s) issue(a, row0, col0, s, s);
   }
 
+  template <int RM = RM_SEL>
   __device__ __forceinline__ void run_tile(const KArgs& a, const float* sG, int row0, int col0) {
     prefetch(a, row0, col0);
-    run_prefetched(a, sG, row0, col0);
+    run_prefetched<RM>(a, sG, row0, col0);
   }
 
   // The rest of the tile with G staged through LDS in two 64-row halves (sG
   // holds 64 rows): the waves that own a half (wr = h) write it, and all four
   // consume it in passes 4h .. 4h + 3.  Called right after the mainloop with
   // a barrier between: the stages are free.
+  template <int RM = RM_SEL>
   __device__ __forceinline__ void run_halves(const KArgs& a, float* sG, const f32x16 (&acc)[2][2], int row0,
                                              int col0) {
     static_assert(NTE == NT && PASSES == 8, "four passes per 64-row half");
@@ -1569,7 +1593,7 @@ struct Epilogue {
         grad(sG, s, slot, g, 64 * h);
         const typename S::Pending cur = pend[slot];
         if (s + DEPTH < PASSES) issue(a, row0, col0, s + DEPTH, slot);
-        consume(a, row0, col0, s, g, cur);
+        consume<RM>(a, row0, col0, s, g, cur);
       }
       if (h == 0) {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -1578,6 +1602,7 @@ struct Epilogue {
     }
   }
 
+  template <int RM = RM_SEL>
   __device__ __forceinline__ void run_prefetched(const KArgs& a, const float* sG, int row0, int col0) {
 #pragma unroll
     for (int s = 0; s < PASSES; ++s) {
@@ -1586,8 +1611,32 @@ struct Epilogue {
       grad(sG, s, slot, g);
       const typename S::Pending cur = pend[slot];
       if (s + DEPTH < PASSES) issue(a, row0, col0, s + DEPTH, slot);
-      consume(a, row0, col0, s, g, cur);
+      consume<RM>(a, row0, col0, s, g, cur);
     }
+  }
+
+  // The same with the rounding mode fixed per tile from the wave-uniform
+  // mask, where the step stores bf16.
+  __device__ __forceinline__ void run_halves_rm(const KArgs& a, float* sG, const f32x16 (&acc)[2][2], int row0,
+                                                int col0) {
+    if constexpr (S::BF16_STORE) {
+      if (a.c.sr) run_halves<RM_SR>(a, sG, acc, row0, col0);
+      else run_halves<RM_RNE>(a, sG, acc, row0, col0);
+    } else {
+      run_halves(a, sG, acc, row0, col0);
+    }
+  }
+  __device__ __forceinline__ void run_prefetched_rm(const KArgs& a, const float* sG, int row0, int col0) {
+    if constexpr (S::BF16_STORE) {
+      if (a.c.sr) run_prefetched<RM_SR>(a, sG, row0, col0);
+      else run_prefetched<RM_RNE>(a, sG, row0, col0);
+    } else {
+      run_prefetched(a, sG, row0, col0);
+    }
+  }
+  __device__ __forceinline__ void run_tile_rm(const KArgs& a, const float* sG, int row0, int col0) {
+    prefetch(a, row0, col0);
+    run_prefetched_rm(a, sG, row0, col0);
   }
 };
 
@@ -1602,7 +1651,8 @@ struct Epilogue {
 // per 4-element segment: bf16 W with bf16 / 8-bit moments or one fp32 moment,
 // fp32 W with one compact moment, SGD) run three workgroups per CU: a 3-stage
 // ring, G staged in two 64-row halves, 2 passes of state in flight, <= 168
-// VGPRs without spills.  With a larger state (two fp32 moments) the grouped
+// VGPRs (without spills, except 2 registers in Lion with an E4M3 weight and
+// E4M3 m).  With a larger state (two fp32 moments) the grouped
 // kernel does the same with 2 passes in flight, none of them requested before
 // the mainloop (so that they hold no registers during it; measured faster on
 // the Llama decoder layer), while the single-layer kernel keeps two
@@ -1677,11 +1727,11 @@ __global__ void __launch_bounds__(NT, (three_per_cu<OPT, WF, MF, VF, FAST, ACC, 
     dma_accumulate<MainBF16Dma3>(a, lds, row0, col0, threadIdx.x, acc, sync);
     bar();   // every wave is done reading the stages before G overwrites them
     epi.template prefetch_rest<PRE>(a, row0, col0);
-    epi.run_halves(a, reinterpret_cast<float*>(lds), acc, row0, col0);
+    epi.run_halves_rm(a, reinterpret_cast<float*>(lds), acc, row0, col0);
   } else if constexpr (FAST) {
     epi.prefetch(a, row0, col0);
     tile_gradient_dma(a, lds, row0, col0);
-    epi.run_prefetched(a, reinterpret_cast<const float*>(lds), row0, col0);
+    epi.run_prefetched_rm(a, reinterpret_cast<const float*>(lds), row0, col0);
   } else {
     tile_gradient<IN>(a, lds, row0, col0);
     epi.prefetch(a, row0, col0);
@@ -1716,7 +1766,7 @@ __global__ void __launch_bounds__(NT, 3) k_fused_group(const GroupArgs g) {
   dma_accumulate<MainBF16Dma3>(a, lds, row0, col0, threadIdx.x, acc, sync);
   bar();   // every wave is done reading the stages before G overwrites them
   epi.template prefetch_rest<PRE>(a, row0, col0);
-  epi.run_halves(a, reinterpret_cast<float*>(lds), acc, row0, col0);
+  epi.run_halves_rm(a, reinterpret_cast<float*>(lds), acc, row0, col0);
 }
 
 constexpr int LDS_WIDE = MainWide::S * MainWide::STAGE;   // 128 KiB
@@ -1757,7 +1807,7 @@ __global__ void __launch_bounds__(2 * NT, 1) k_fused_wide(const KArgs a) {
           }
     }
     __syncthreads();
-    if (srow0 < a.N && scol0 < a.K) epi.run_tile(a, sG, srow0, scol0);
+    if (srow0 < a.N && scol0 < a.K) epi.run_tile_rm(a, sG, srow0, scol0);
   }
 }
 
