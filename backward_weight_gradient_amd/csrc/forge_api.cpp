@@ -456,7 +456,14 @@ forge_status forge_dgrad_fp8w(const forge_mat* dY, const forge_state* W, forge_m
   bool fast = false;
   const forge_status st = check_dgrad(dY, &W->q, dX, g, fast, W);
   if (st != FORGE_OK) return st;
-  return hip_status(launch_dgrad_fp8w(g, (hipStream_t)stream));
+  // the bf16 matrix-core kernel: 16-byte rows of dY (8 bf16) and W (16
+  // codes), whole 16-byte segments, buffer offsets within 32 bits
+  const int64_t N = dY->cols, K = W->q.cols;
+  const bool fast8 = dY->dtype == FORGE_BF16 && N % 8 == 0 && K % 16 == 0 && vec_ok(dY->data, dY->ld, 8, 2) &&
+                     vec_ok(W->q.data, W->q.ld, 16, 1) && (uint64_t)dY->rows * (uint64_t)dY->ld * 2 < (1ull << 31) &&
+                     (uint64_t)N * (uint64_t)W->q.ld < (1ull << 31) &&
+                     (uint64_t)N * (uint64_t)(K / W->block) * 4 < (1ull << 31);
+  return hip_status(launch_dgrad_fp8w(g, fast8, (hipStream_t)stream));
 }
 
 forge_status forge_wgrad_step_group(const forge_layer* layers, int32_t n, const forge_hyper* h, int64_t step,

@@ -141,8 +141,9 @@ struct DgArgs {
 };
 // forge_k_dgrad.hip: fast = bf16 dY and W with 16-byte aligned rows, N and K multiples of 8.
 hipError_t launch_dgrad(const DgArgs& g, bool fast, hipStream_t stream);
-// dX from an E4M3 weight (g.wsc, g.wblock): the fp32 matrix-core kernel for bf16 dY, else the plain one.
-hipError_t launch_dgrad_fp8w(const DgArgs& g, hipStream_t stream);
+// dX from an E4M3 weight (g.wsc, g.wblock), bf16 dY: the bf16 matrix-core kernel when fast (aligned rows,
+// N % 8 == 0, K % 16 == 0, 32-bit buffer offsets), else the fp32 matrix-core kernel; other dY: the plain one.
+hipError_t launch_dgrad_fp8w(const DgArgs& g, bool fast, hipStream_t stream);
 // The split path with the partials in the library's own per-device scratch
 // array (no caller workspace, no allocation); g.splits * BT * K * 4 must not
 // exceed DGRAD_SCRATCH_BYTES.

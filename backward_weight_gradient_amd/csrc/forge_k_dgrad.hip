@@ -107,6 +107,17 @@ struct DgradLoader {
     }
   }
 
+  // dY's chunk kc alone (ABLK loads per wave)
+  __device__ __forceinline__ void issue_a(const DgArgs& g, int kc, char* stage) const {
+    const int n0 = kc * DG_TN;
+#pragma unroll
+    for (int r = 0; r < SH::ABLK; ++r) {
+      const uint32_t oa = (aOk[r] && n0 + (int)(aSeg[r] >> 1) < g.N) ? aTok[r] + (uint32_t)n0 * 2 + aSeg[r] : oobA;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void*)(stage + (SH::ABLK * wave + r) * 1024), 16, oa, 0, 0,
+                                               0);
+    }
+  }
+
   __device__ __forceinline__ void issue(const DgArgs& g, int kc, char* stage) const {
     const int n0 = kc * DG_TN;
 #pragma unroll
@@ -744,10 +755,242 @@ __global__ void __launch_bounds__(NT) k_dgrad_fp8w(const DgArgs g) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// k_dgrad_fp8w3<TM> (bf16 dY with 16-byte aligned rows and N % 8 == 0, E4M3
+// W with 16-byte aligned rows and K % 16 == 0, fp32 block scales): dX on the
+// bf16 matrix cores.  A weight element decodes to w = fp32(code * scale),
+// the value the fused step reads back, and w splits exactly into three bf16
+// terms: h = w with its low 16 bits cleared, m = (w - h) likewise, l =
+// w - h - m (8 significant bits each; every subtraction is exact).  So dX =
+// dY h + dY m + dY l with exact products and fp32 accumulation: three MFMAs
+// per fragment pair, the work of the fp32 kernel at the bf16 rate.  Tiles of
+// TM tokens x 128 columns, 4 waves in 2 x 2.  Per 32-row chunk a stage holds
+// dY's chunk (as k_dgrad_bf16), W's raw 32 x 128 bytes and their scales
+// (buffer_load ... lds), and the three bf16 terms in the weight-gradient
+// layout, which the threads write from the raw bytes one chunk ahead of
+// the MFMAs.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int F3_S = 4;                       // ring stages
+template <int TM>
+struct F3Shape {
+  static constexpr int APB = TM * DG_TN * 2;  // dY's chunk
+  static constexpr int RAW = APB;             // W's chunk, 32 rows x 128 bytes
+  static constexpr int SCL = RAW + 4096;      // its scales: slot r * (128 / block) + b, 256 slots
+  static constexpr int TRM = SCL + 1024;      // three bf16 terms, DG_OPB bytes each
+  static constexpr int STAGE = TRM + 3 * DG_OPB;
+  static constexpr int LOADS = TM / 64 + 2;   // buffer loads per wave per chunk
+};
+static_assert(F3_S * F3Shape<128>::STAGE <= 160 * 1024, "one workgroup per CU");
+
+// the high halves of two fp32 patterns as one bf16 pair (a low, b high)
+__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
+
+// LDS accesses of this kernel are written out (the buffer_load ... lds
+// writes are invisible to the compiler's own wait insertion); every read's
+// result is threaded through an explicit wait before its use.
+__device__ __forceinline__ uint32_t lds_rd32(uint32_t addr) {
+  uint32_t v;
+  asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr));
+  return v;
+}
+__device__ __forceinline__ void lds_wr128(uint32_t addr, u32x4 v) {
+  asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void f3_wait_b(u32x2 (&b)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]) : "i"(N));
+}
+
+// term K's fragments of k-step KS for the two 32-column blocks at pb0, pb1
+template <int K, int KS>
+__device__ __forceinline__ void f3_bfrag(uint32_t pb0, uint32_t pb1, u32x2 (&b)[4]) {
+  b[0] = tr_read_at<K * DG_OPB + KS * 4096>(pb0);
+  b[1] = tr_read_at<K * DG_OPB + KS * 4096 + 1024>(pb0);
+  b[2] = tr_read_at<K * DG_OPB + KS * 4096>(pb1);
+  b[3] = tr_read_at<K * DG_OPB + KS * 4096 + 1024>(pb1);
+}
+
+template <int BI>
+__device__ __forceinline__ void f3_mfma(f32x16 (&acc)[BI][2], const u32x4 (&af)[BI], const u32x2 (&b)[4]) {
+#pragma unroll
+  for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj)
+      acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[bi]),
+                                                            frag_join(b[2 * bj], b[2 * bj + 1]), acc[bi][bj], 0, 0, 0);
+}
+
+// One k-step: dY's fragments and all three terms' requested up front
+// (BI + 12 reads), the terms' MFMAs as their reads land.
+template <int KS, int BI>
+__device__ __forceinline__ void f3_kstep(f32x16 (&acc)[BI][2], uint32_t cur, const uint32_t (&aofs)[2][BI],
+                                         uint32_t pb0, uint32_t pb1) {
+  u32x4 af[BI];
+  u32x2 b0[4], b1[4], b2[4];
+#pragma unroll
+  for (int bi = 0; bi < BI; ++bi) af[bi] = ds_read_16(cur + aofs[KS][bi]);
+  f3_bfrag<0, KS>(pb0, pb1, b0);
+  f3_bfrag<1, KS>(pb0, pb1, b1);
+  f3_bfrag<2, KS>(pb0, pb1, b2);
+  dg_wait<8>(af, b0);
+  f3_mfma<BI>(acc, af, b0);
+  __builtin_amdgcn_sched_barrier(0);
+  f3_wait_b<4>(b1);
+  f3_mfma<BI>(acc, af, b1);
+  __builtin_amdgcn_sched_barrier(0);
+  f3_wait_b<0>(b2);
+  f3_mfma<BI>(acc, af, b2);
+  __builtin_amdgcn_sched_barrier(0);
+}
+}  // namespace
+
+template <int TM>
+__global__ void __launch_bounds__(NT, 1) k_dgrad_fp8w3(const DgArgs g) {
+  using SH = F3Shape<TM>;
+  constexpr int S = F3_S, BI = TM / 64;
+  __shared__ __attribute__((aligned(16))) char lds[S * SH::STAGE];
+  const int tiles_m = (g.BT + TM - 1) / TM;
+  const int w = xcd_work((int)blockIdx.x, (int)gridDim.x);
+  const int tj = w / tiles_m, ti = w - tj * tiles_m;
+  const int tok0 = ti * TM, col0 = tj * TILE;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)lds;
+  f32x16 acc[BI][2];
+#pragma unroll
+  for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[bi][bj][e] = 0.f;
+  const int nk = (g.N + DG_TN - 1) / DG_TN;
+  DgradLoader<TM, S> ld;
+  ld.init(g, tok0, col0, tid);
+  // raw W: wave v, lane l -> row 8 v + l / 8, bytes 16 (l % 8) .. + 15;
+  // scales: slot q = 64 v + l -> row q / bpt, block q % bpt of the tile
+  const int bsh = __builtin_ctz((unsigned)g.wblock);
+  const int bpt_sh = 7 - bsh;                               // log2 of the tile's blocks per row
+  const int64_t spr = g.K >> bsh;                           // scales per row of W
+  const uint32_t oobW = (uint32_t)((uint64_t)g.N * g.ldw);
+  const uint32_t oobS = (uint32_t)((uint64_t)g.N * spr * 4);
+  const __amdgpu_buffer_rsrc_t rW = make_rsrc(g.W, oobW), rS = make_rsrc(g.wsc, oobS);
+  const int wrow = 8 * wave + (lane >> 3), wcol = col0 + 16 * (lane & 7);
+  const bool wOk = wcol < g.K;
+  const int q = 64 * wave + lane, srow = q >> bpt_sh, sblk = (col0 >> bsh) + (q & ((1 << bpt_sh) - 1));
+  const bool sOk = srow < DG_TN && sblk < spr;
+  const auto issue = [&](int kc, char* stage) {
+    ld.issue_a(g, kc, stage);
+    const int n = kc * DG_TN + wrow;
+    const uint32_t ow = (wOk && n < g.N) ? (uint32_t)n * (uint32_t)g.ldw + (uint32_t)wcol : oobW;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_void*)(stage + SH::RAW + wave * 1024), 16, ow, 0, 0, 0);
+    const int ns = kc * DG_TN + srow;
+    const uint32_t os = (sOk && ns < g.N) ? (uint32_t)(((int64_t)ns * spr + sblk) * 4) : oobS;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_void*)(stage + SH::SCL + wave * 256), 4, os, 0, 0, 0);
+  };
+  // this thread's 16 weights of a chunk: row tid / 8, columns 16 (tid % 8) ..
+  const int crow = tid >> 3, ccol = 16 * (tid & 7);
+  const uint32_t cslot = (uint32_t)(((crow << bpt_sh) + (ccol >> bsh)) * 4);
+  uint32_t cwr[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) cwr[h] = (uint32_t)(SH::TRM + MainBF16::off(crow, ccol + 8 * h));
+  const auto convert = [&](uint32_t stage) {   // stage: LDS address
+    u32x4 raw = ds_read_16(stage + SH::RAW + tid * 16);
+    uint32_t scb = lds_rd32(stage + SH::SCL + cslot);
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(raw), "+v"(scb));
+    const float sc = __uint_as_float(scb);
+    uint32_t t[3][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float x[4];
+      e4m3_unpack4(raw[i], x);
+      uint32_t hb[4], mb[4], lb[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v = x[e] * sc;                              // fp32(code * scale)
+        hb[e] = __float_as_uint(v) & 0xFFFF0000u;
+        const float r1 = v - __uint_as_float(hb[e]);
+        mb[e] = __float_as_uint(r1) & 0xFFFF0000u;
+        lb[e] = __float_as_uint(r1 - __uint_as_float(mb[e]));  // low 16 bits zero
+      }
+      t[0][2 * i] = hi_pair(hb[0], hb[1]);
+      t[0][2 * i + 1] = hi_pair(hb[2], hb[3]);
+      t[1][2 * i] = hi_pair(mb[0], mb[1]);
+      t[1][2 * i + 1] = hi_pair(mb[2], mb[3]);
+      t[2][2 * i] = hi_pair(lb[0], lb[1]);
+      t[2][2 * i + 1] = hi_pair(lb[2], lb[3]);
+    }
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      lds_wr128(stage + k * DG_OPB + cwr[0], u32x4{t[k][0], t[k][1], t[k][2], t[k][3]});
+      lds_wr128(stage + k * DG_OPB + cwr[1], u32x4{t[k][4], t[k][5], t[k][6], t[k][7]});
+    }
+    // the writes done before the k-steps' 14 reads: at most 15 LDS
+    // operations outstanding
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  };
+  // fragment offsets within a stage (as k_dgrad_bf16)
+  uint32_t aofs[2][BI], bofs[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int bi = 0; bi < BI; ++bi) aofs[ks][bi] = dg_a_off(wr * (TM / 2) + bi * 32 + (lane & 31), 2 * ks + (lane >> 5));
+  {
+    const int t = 8 * (lane >> 5) + ((lane & 15) >> 2);
+    const int f = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj) bofs[bj] = (uint32_t)(SH::TRM + MainBF16::off(t, wc * 64 + bj * 32 + f));
+  }
+  // every chunk issues its loads (past the end they read zero), so the
+  // vector-memory counts are the same in every iteration
+#pragma unroll
+  for (int k = 0; k < S - 1; ++k) issue(k, lds + k * SH::STAGE);
+  wait_vmcnt<(S - 2) * SH::LOADS>();   // chunk 0 landed
+  bar();
+  convert(lds0);
+  for (int j = 0; j < nk; ++j) {
+    wait_vmcnt<(S - 3) * SH::LOADS>();   // chunk j + 1 landed
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this thread's term writes done
+    bar();                               // ... for every thread; stage j - 1 free
+    issue(j + S - 1, lds + ((j + S - 1) % S) * SH::STAGE);
+    if (j + 1 < nk) convert(lds0 + (uint32_t)(((j + 1) % S) * SH::STAGE));
+    const uint32_t cur = lds0 + (uint32_t)((j % S) * SH::STAGE);
+    const uint32_t pb0 = cur + bofs[0], pb1 = cur + bofs[1];
+    f3_kstep<0, BI>(acc, cur, aofs, pb0, pb1);
+    f3_kstep<1, BI>(acc, cur, aofs, pb0, pb1);
+  }
+  wait_vmcnt<0>();
+  // lane l, register 4j + i of a 32 x 32 block holds row 8j + 4 (l / 32) + i, column l % 32
+#pragma unroll
+  for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int tok = tok0 + wr * (TM / 2) + bi * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        const int col = col0 + wc * 64 + bj * 32 + (lane & 31);
+        if (tok >= g.BT || col >= g.K) continue;
+        const int64_t o = (int64_t)tok * g.ldx + col;
+        if (g.dx_fmt == FMT_F32) static_cast<float*>(g.dX)[o] = acc[bi][bj][e];
+        else static_cast<uint16_t*>(g.dX)[o] = (uint16_t)bf16_rne_bits(acc[bi][bj][e]);
+      }
+}
+
+// fast (aligned operands): the bf16 matrix-core kernel, 128-token tiles when
+// those give every CU a workgroup, else 64; otherwise the fp32 kernel, with
 // 32-token tiles when 64-token tiles would not give every CU two workgroups.
-hipError_t launch_dgrad_fp8w(const DgArgs& g, hipStream_t st) {
+hipError_t launch_dgrad_fp8w(const DgArgs& g, bool fast, hipStream_t st) {
   if (g.BT == 0 || g.K == 0) return hipSuccess;
   if (g.in_fmt != FMT_BF16 || g.w_fmt != FMT_E4M3 || g.wblock < 32) return launch_dgrad(g, false, st);
+  if (fast) {
+    const int64_t tk = (g.K + TILE - 1) / TILE;
+    const int64_t t128 = ((g.BT + 127) / 128) * tk;
+    if (t128 >= 256)
+      hipLaunchKernelGGL(k_dgrad_fp8w3<128>, dim3((unsigned)t128), dim3(NT), 0, st, g);
+    else
+      hipLaunchKernelGGL(k_dgrad_fp8w3<64>, dim3((unsigned)(((g.BT + 63) / 64) * tk)), dim3(NT), 0, st, g);
+    return hipGetLastError();
+  }
   const int64_t tk = (g.K + F8_TN - 1) / F8_TN;
   const int64_t t64 = ((g.BT + 63) / 64) * tk;
   if (t64 >= 512) {

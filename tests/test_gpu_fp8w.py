@@ -134,20 +134,29 @@ def test_fp8_weight_gate_proj_full_size(state):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("N,K,BT,dx,dy32", [(512, 512, 256, torch.bfloat16, False),
-                                            (130, 256, 77, torch.float32, False),   # ragged tokens, N, K
-                                            (97, 384, 130, torch.bfloat16, True),   # fp32 dY: the plain kernel
-                                            (14336, 4096, 512, torch.bfloat16, False)])
-def test_fp8_weight_dgrad(N, K, BT, dx, dy32):
-    _say(f"case: FP8 W dX {N}x{K} BT{BT} {dx} dY {'f32' if dy32 else 'bf16'}")
-    L = make_layer(75, N, K, BT, 2, _spec("adamw", "f32"), gen_device="cuda" if N > 4096 else "cpu")
+# bf16 dY with N % 8 == 0 and aligned rows takes the bf16 matrix-core kernel
+# (three bf16 terms per decoded weight): (512, 512, 256), (14336, 4096, 512),
+# (1000, 1056, 77) (64-token tiles, ragged tokens, reduction chunk and column
+# tile, blocks of 32), (520, 2048, 2048) (128-token tiles, blocks of 64),
+# (264, 384, 300); N % 8 != 0 takes the fp32 matrix-core kernel: (130, 256,
+# 77); fp32 dY the plain kernel: (97, 384, 130).
+@pytest.mark.parametrize("N,K,BT,dx,dy32,block", [(512, 512, 256, torch.bfloat16, False, 128),
+                                                  (130, 256, 77, torch.float32, False, 128),
+                                                  (97, 384, 130, torch.bfloat16, True, 128),
+                                                  (14336, 4096, 512, torch.bfloat16, False, 128),
+                                                  (1000, 1056, 77, torch.bfloat16, False, 32),
+                                                  (520, 2048, 2048, torch.float32, False, 64),
+                                                  (264, 384, 300, torch.float32, False, 128)])
+def test_fp8_weight_dgrad(N, K, BT, dx, dy32, block):
+    _say(f"case: FP8 W dX {N}x{K} BT{BT} {dx} dY {'f32' if dy32 else 'bf16'} block {block}")
+    L = make_layer(75, N, K, BT, 2, _spec("adamw", "f32", block), gen_device="cuda" if N > 4096 else "cpu")
     if dy32:
         L.dY = L.dY.float()
     dX = torch.full((BT, K), float("nan"), device="cuda", dtype=dx)
     F.forge_dgrad_fp8w(L.dY, L.forge_w(), dX)
     torch.cuda.synchronize()
     rows = np.unique(np.array([0, 1, BT // 2, BT - 1] + list(np.random.default_rng(N).integers(0, BT, 12))))
-    Wst = O.Stored("e4m3", synth.host(L.W), L.wsc.cpu().numpy(), 128)
+    Wst = O.Stored("e4m3", synth.host(L.W), L.wsc.cpu().numpy(), block)
     Wdec = O.decode(Wst).astype(np.float32)         # the stored weight, exactly (fp32)
     dYh = synth.host(L.dY)
     ref = O.input_grad(dYh, Wdec, rows)
