@@ -764,24 +764,28 @@ __global__ void __launch_bounds__(NT) k_dgrad_fp8w(const DgArgs g) {
 // w - h - m (8 significant bits each; every subtraction is exact).  So dX =
 // dY h + dY m + dY l with exact products and fp32 accumulation: three MFMAs
 // per fragment pair, the work of the fp32 kernel at the bf16 rate.  Tiles of
-// TM tokens x 128 columns, 4 waves in 2 x 2.  Per 32-row chunk a stage holds
-// dY's chunk (as k_dgrad_bf16), W's raw 32 x 128 bytes and their scales
-// (buffer_load ... lds), and the three bf16 terms in the weight-gradient
-// layout, which the threads write from the raw bytes one chunk ahead of
-// the MFMAs.
+// TM tokens x 128 columns, 4 waves in 2 x 2.  Per 32-row chunk a ring stage
+// holds dY's chunk (as k_dgrad_bf16), W's raw 32 x 128 bytes and their
+// scales (buffer_load ... lds); the threads write the three bf16 terms of
+// the next chunk from its raw bytes into one of two term buffers (weight-
+// gradient layout) while the MFMAs read the other.  64-token tiles: a
+// 3-stage ring, 75 KiB, two workgroups per CU; 128-token tiles: 4 stages,
+// one per CU.
 // ---------------------------------------------------------------------------
 namespace {
-constexpr int F3_S = 4;                       // ring stages
 template <int TM>
 struct F3Shape {
+  static constexpr int S = TM == 64 ? 3 : 4;  // ring stages
+  static constexpr int OCC = TM == 64 ? 2 : 1;  // workgroups per CU
   static constexpr int APB = TM * DG_TN * 2;  // dY's chunk
   static constexpr int RAW = APB;             // W's chunk, 32 rows x 128 bytes
   static constexpr int SCL = RAW + 4096;      // its scales: slot r * (128 / block) + b, 256 slots
-  static constexpr int TRM = SCL + 1024;      // three bf16 terms, DG_OPB bytes each
-  static constexpr int STAGE = TRM + 3 * DG_OPB;
+  static constexpr int STAGE = SCL + 1024;
+  static constexpr int TRM = S * STAGE;       // two buffers of three bf16 terms, DG_OPB bytes each
+  static constexpr int LDS = TRM + 6 * DG_OPB;
   static constexpr int LOADS = TM / 64 + 2;   // buffer loads per wave per chunk
 };
-static_assert(F3_S * F3Shape<128>::STAGE <= 160 * 1024, "one workgroup per CU");
+static_assert(F3Shape<64>::LDS * 2 <= 160 * 1024 && F3Shape<128>::LDS <= 160 * 1024, "LDS per CU");
 
 // the high halves of two fp32 patterns as one bf16 pair (a low, b high)
 __device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
@@ -821,35 +825,45 @@ __device__ __forceinline__ void f3_mfma(f32x16 (&acc)[BI][2], const u32x4 (&af)[
                                                             frag_join(b[2 * bj], b[2 * bj + 1]), acc[bi][bj], 0, 0, 0);
 }
 
-// One k-step: dY's fragments and all three terms' requested up front
-// (BI + 12 reads), the terms' MFMAs as their reads land.
+// Three bf16 terms of four decoded weights (the codes of one word, times
+// the scale): pairs 2 i, 2 i + 1 of t[k].
+__device__ __forceinline__ void f3_split4(uint32_t word, float sc, uint32_t (&t)[3][8], int i) {
+  float x[4];
+  e4m3_unpack4(word, x);
+  uint32_t hb[4], mb[4], lb[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float v = x[e] * sc;                              // fp32(code * scale)
+    hb[e] = __float_as_uint(v) & 0xFFFF0000u;
+    const float r1 = v - __uint_as_float(hb[e]);
+    mb[e] = __float_as_uint(r1) & 0xFFFF0000u;
+    lb[e] = __float_as_uint(r1 - __uint_as_float(mb[e]));  // low 16 bits zero
+  }
+  t[0][2 * i] = hi_pair(hb[0], hb[1]);
+  t[0][2 * i + 1] = hi_pair(hb[2], hb[3]);
+  t[1][2 * i] = hi_pair(mb[0], mb[1]);
+  t[1][2 * i + 1] = hi_pair(mb[2], mb[3]);
+  t[2][2 * i] = hi_pair(lb[0], lb[1]);
+  t[2][2 * i + 1] = hi_pair(lb[2], lb[3]);
+}
+
+// One k-step's reads: dY's fragments and all three terms' (BI + 12).
 template <int KS, int BI>
-__device__ __forceinline__ void f3_kstep(f32x16 (&acc)[BI][2], uint32_t cur, const uint32_t (&aofs)[2][BI],
-                                         uint32_t pb0, uint32_t pb1) {
-  u32x4 af[BI];
-  u32x2 b0[4], b1[4], b2[4];
+__device__ __forceinline__ void f3_reads(uint32_t cur, const uint32_t (&aofs)[2][BI], uint32_t pb0, uint32_t pb1,
+                                         u32x4 (&af)[BI], u32x2 (&b0)[4], u32x2 (&b1)[4], u32x2 (&b2)[4]) {
 #pragma unroll
   for (int bi = 0; bi < BI; ++bi) af[bi] = ds_read_16(cur + aofs[KS][bi]);
   f3_bfrag<0, KS>(pb0, pb1, b0);
   f3_bfrag<1, KS>(pb0, pb1, b1);
   f3_bfrag<2, KS>(pb0, pb1, b2);
-  dg_wait<8>(af, b0);
-  f3_mfma<BI>(acc, af, b0);
-  __builtin_amdgcn_sched_barrier(0);
-  f3_wait_b<4>(b1);
-  f3_mfma<BI>(acc, af, b1);
-  __builtin_amdgcn_sched_barrier(0);
-  f3_wait_b<0>(b2);
-  f3_mfma<BI>(acc, af, b2);
-  __builtin_amdgcn_sched_barrier(0);
 }
 }  // namespace
 
 template <int TM>
-__global__ void __launch_bounds__(NT, 1) k_dgrad_fp8w3(const DgArgs g) {
+__global__ void __launch_bounds__(NT, F3Shape<TM>::OCC) k_dgrad_fp8w3(const DgArgs g) {
   using SH = F3Shape<TM>;
-  constexpr int S = F3_S, BI = TM / 64;
-  __shared__ __attribute__((aligned(16))) char lds[S * SH::STAGE];
+  constexpr int S = SH::S, BI = TM / 64;
+  __shared__ __attribute__((aligned(16))) char lds[SH::LDS];
   const int tiles_m = (g.BT + TM - 1) / TM;
   const int w = xcd_work((int)blockIdx.x, (int)gridDim.x);
   const int tj = w / tiles_m, ti = w - tj * tiles_m;
@@ -867,8 +881,11 @@ __global__ void __launch_bounds__(NT, 1) k_dgrad_fp8w3(const DgArgs g) {
   const int nk = (g.N + DG_TN - 1) / DG_TN;
   DgradLoader<TM, S> ld;
   ld.init(g, tok0, col0, tid);
-  // raw W: wave v, lane l -> row 8 v + l / 8, bytes 16 (l % 8) .. + 15;
-  // scales: slot q = 64 v + l -> row q / bpt, block q % bpt of the tile
+  // Each wave brings in exactly what its own threads convert: raw W rows
+  // 8 v .. 8 v + 7 (lane l -> row 8 v + l / 8, bytes 16 (l % 8) .. + 15)
+  // and their scales (lane l < 8 bpt -> row 8 v + l / bpt, block l % bpt of
+  // the tile, slot 64 v + l), so a thread may convert a chunk as soon as its
+  // own wave's loads of it have landed.
   const int bsh = __builtin_ctz((unsigned)g.wblock);
   const int bpt_sh = 7 - bsh;                               // log2 of the tile's blocks per row
   const int64_t spr = g.K >> bsh;                           // scales per row of W
@@ -877,8 +894,8 @@ __global__ void __launch_bounds__(NT, 1) k_dgrad_fp8w3(const DgArgs g) {
   const __amdgpu_buffer_rsrc_t rW = make_rsrc(g.W, oobW), rS = make_rsrc(g.wsc, oobS);
   const int wrow = 8 * wave + (lane >> 3), wcol = col0 + 16 * (lane & 7);
   const bool wOk = wcol < g.K;
-  const int q = 64 * wave + lane, srow = q >> bpt_sh, sblk = (col0 >> bsh) + (q & ((1 << bpt_sh) - 1));
-  const bool sOk = srow < DG_TN && sblk < spr;
+  const int srow = 8 * wave + (lane >> bpt_sh), sblk = (col0 >> bsh) + (lane & ((1 << bpt_sh) - 1));
+  const bool sOk = lane < (8 << bpt_sh) && sblk < spr;
   const auto issue = [&](int kc, char* stage) {
     ld.issue_a(g, kc, stage);
     const int n = kc * DG_TN + wrow;
@@ -890,44 +907,17 @@ __global__ void __launch_bounds__(NT, 1) k_dgrad_fp8w3(const DgArgs g) {
   };
   // this thread's 16 weights of a chunk: row tid / 8, columns 16 (tid % 8) ..
   const int crow = tid >> 3, ccol = 16 * (tid & 7);
-  const uint32_t cslot = (uint32_t)(((crow << bpt_sh) + (ccol >> bsh)) * 4);
+  const uint32_t craw = (uint32_t)(SH::RAW + tid * 16);
+  const uint32_t cscl = (uint32_t)(SH::SCL + (64 * wave + (((lane >> 3) << bpt_sh) + (ccol >> bsh))) * 4);
   uint32_t cwr[2];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) cwr[h] = (uint32_t)(SH::TRM + MainBF16::off(crow, ccol + 8 * h));
-  const auto convert = [&](uint32_t stage) {   // stage: LDS address
-    u32x4 raw = ds_read_16(stage + SH::RAW + tid * 16);
-    uint32_t scb = lds_rd32(stage + SH::SCL + cslot);
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(raw), "+v"(scb));
-    const float sc = __uint_as_float(scb);
-    uint32_t t[3][8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float x[4];
-      e4m3_unpack4(raw[i], x);
-      uint32_t hb[4], mb[4], lb[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float v = x[e] * sc;                              // fp32(code * scale)
-        hb[e] = __float_as_uint(v) & 0xFFFF0000u;
-        const float r1 = v - __uint_as_float(hb[e]);
-        mb[e] = __float_as_uint(r1) & 0xFFFF0000u;
-        lb[e] = __float_as_uint(r1 - __uint_as_float(mb[e]));  // low 16 bits zero
-      }
-      t[0][2 * i] = hi_pair(hb[0], hb[1]);
-      t[0][2 * i + 1] = hi_pair(hb[2], hb[3]);
-      t[1][2 * i] = hi_pair(mb[0], mb[1]);
-      t[1][2 * i + 1] = hi_pair(mb[2], mb[3]);
-      t[2][2 * i] = hi_pair(lb[0], lb[1]);
-      t[2][2 * i + 1] = hi_pair(lb[2], lb[3]);
-    }
+  for (int h = 0; h < 2; ++h) cwr[h] = (uint32_t)MainBF16::off(crow, ccol + 8 * h);
+  const auto write_terms = [&](uint32_t terms, const uint32_t (&t)[3][8]) {
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
-      lds_wr128(stage + k * DG_OPB + cwr[0], u32x4{t[k][0], t[k][1], t[k][2], t[k][3]});
-      lds_wr128(stage + k * DG_OPB + cwr[1], u32x4{t[k][4], t[k][5], t[k][6], t[k][7]});
+      lds_wr128(terms + k * DG_OPB + cwr[0], u32x4{t[k][0], t[k][1], t[k][2], t[k][3]});
+      lds_wr128(terms + k * DG_OPB + cwr[1], u32x4{t[k][4], t[k][5], t[k][6], t[k][7]});
     }
-    // the writes done before the k-steps' 14 reads: at most 15 LDS
-    // operations outstanding
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   };
   // fragment offsets within a stage (as k_dgrad_bf16)
   uint32_t aofs[2][BI], bofs[2];
@@ -939,25 +929,70 @@ __global__ void __launch_bounds__(NT, 1) k_dgrad_fp8w3(const DgArgs g) {
     const int t = 8 * (lane >> 5) + ((lane & 15) >> 2);
     const int f = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
-    for (int bj = 0; bj < 2; ++bj) bofs[bj] = (uint32_t)(SH::TRM + MainBF16::off(t, wc * 64 + bj * 32 + f));
+    for (int bj = 0; bj < 2; ++bj) bofs[bj] = (uint32_t)MainBF16::off(t, wc * 64 + bj * 32 + f);
   }
+  const uint32_t terms0 = lds0 + (uint32_t)SH::TRM;   // term buffer of chunk c: terms0 + (c & 1) 3 DG_OPB
   // every chunk issues its loads (past the end they read zero), so the
   // vector-memory counts are the same in every iteration
 #pragma unroll
   for (int k = 0; k < S - 1; ++k) issue(k, lds + k * SH::STAGE);
-  wait_vmcnt<(S - 2) * SH::LOADS>();   // chunk 0 landed
-  bar();
-  convert(lds0);
+  wait_vmcnt<(S - 2) * SH::LOADS>();   // chunk 0 landed (this wave's loads)
+  {
+    u32x4 raw = ds_read_16(lds0 + craw);
+    uint32_t scb = lds_rd32(lds0 + cscl);
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(raw), "+v"(scb));
+    uint32_t t[3][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f3_split4(raw[i], __uint_as_float(scb), t, i);
+    write_terms(terms0, t);
+  }
   for (int j = 0; j < nk; ++j) {
-    wait_vmcnt<(S - 3) * SH::LOADS>();   // chunk j + 1 landed
+    wait_vmcnt<(S - 3) * SH::LOADS>();   // chunk j + 1 landed (this wave's loads)
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this thread's term writes done
-    bar();                               // ... for every thread; stage j - 1 free
+    bar();                               // chunk j's terms and dY in place; stage j - 1 free
     issue(j + S - 1, lds + ((j + S - 1) % S) * SH::STAGE);
-    if (j + 1 < nk) convert(lds0 + (uint32_t)(((j + 1) % S) * SH::STAGE));
     const uint32_t cur = lds0 + (uint32_t)((j % S) * SH::STAGE);
-    const uint32_t pb0 = cur + bofs[0], pb1 = cur + bofs[1];
-    f3_kstep<0, BI>(acc, cur, aofs, pb0, pb1);
-    f3_kstep<1, BI>(acc, cur, aofs, pb0, pb1);
+    const uint32_t nxt = lds0 + (uint32_t)(((j + 1) % S) * SH::STAGE);
+    const uint32_t tb = terms0 + (uint32_t)((j & 1) * 3 * DG_OPB);
+    const uint32_t pb0 = tb + bofs[0], pb1 = tb + bofs[1];
+    u32x4 af[BI];
+    u32x2 b0[4], b1[4], b2[4];
+    uint32_t t[3][8];
+    // k-step 0; chunk j + 1's raw words and scale requested behind its reads
+    f3_reads<0, BI>(cur, aofs, pb0, pb1, af, b0, b1, b2);
+    dg_wait<8>(af, b0);
+    f3_mfma<BI>(acc, af, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 raw = ds_read_16(nxt + craw);
+    uint32_t scb = lds_rd32(nxt + cscl);
+    f3_wait_b<6>(b1);
+    f3_mfma<BI>(acc, af, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    f3_wait_b<2>(b2);
+    f3_mfma<BI>(acc, af, b2);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(raw), "+v"(scb));
+    // half of chunk j + 1's conversion while k-step 0's MFMAs run
+    const float sc = __uint_as_float(scb);
+    f3_split4(raw[0], sc, t, 0);
+    f3_split4(raw[1], sc, t, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    // k-step 1
+    f3_reads<1, BI>(cur, aofs, pb0, pb1, af, b0, b1, b2);
+    dg_wait<8>(af, b0);
+    f3_mfma<BI>(acc, af, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    f3_wait_b<4>(b1);
+    f3_mfma<BI>(acc, af, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    f3_wait_b<0>(b2);
+    f3_mfma<BI>(acc, af, b2);
+    __builtin_amdgcn_sched_barrier(0);
+    // the other half while k-step 1's MFMAs run; chunk j + 1's terms into
+    // the other buffer (after the last chunk: the zeros past the end, never read)
+    f3_split4(raw[2], sc, t, 2);
+    f3_split4(raw[3], sc, t, 3);
+    write_terms(terms0 + (uint32_t)(((j + 1) & 1) * 3 * DG_OPB), t);
   }
   wait_vmcnt<0>();
   // lane l, register 4j + i of a 32 x 32 block holds row 8j + 4 (l / 32) + i, column l % 32
