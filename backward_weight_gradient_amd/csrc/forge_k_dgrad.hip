@@ -763,29 +763,26 @@ __global__ void __launch_bounds__(NT) k_dgrad_fp8w(const DgArgs g) {
 // terms: h = w with its low 16 bits cleared, m = (w - h) likewise, l =
 // w - h - m (8 significant bits each; every subtraction is exact).  So dX =
 // dY h + dY m + dY l with exact products and fp32 accumulation: three MFMAs
-// per fragment pair, the work of the fp32 kernel at the bf16 rate.  Tiles of
-// TM tokens x 128 columns, 4 waves in 2 x 2.  Per 32-row chunk a ring stage
-// holds dY's chunk (as k_dgrad_bf16), W's raw 32 x 128 bytes and their
-// scales (buffer_load ... lds); the threads write the three bf16 terms of
-// the next chunk from its raw bytes into one of two term buffers (weight-
-// gradient layout) while the MFMAs read the other.  64-token tiles: a
-// 3-stage ring, 75 KiB, two workgroups per CU; 128-token tiles: 4 stages,
-// one per CU.
+// per fragment pair, the fp32 kernel's work at the bf16 rate.  Tiles of TM
+// tokens x 128 columns; 4 waves side by side, each all TM tokens x 32
+// columns.  Per 32-row chunk a ring stage holds dY's chunk (as
+// k_dgrad_bf16), W's raw 32 x 128 bytes (16-byte segments XOR-swizzled by
+// row) and the chunk's scales (block-major), all by buffer_load ... lds.
+// Each lane takes its B fragment's 8 codes (8 rows of one column) with the
+// 8-bit transposing LDS read and its 8 rows' scales, and forms the three
+// bf16 fragments in registers.
 // ---------------------------------------------------------------------------
 namespace {
+constexpr int F3_S = 4;                       // ring stages
 template <int TM>
 struct F3Shape {
-  static constexpr int S = TM == 64 ? 3 : 4;  // ring stages
-  static constexpr int OCC = TM == 64 ? 2 : 1;  // workgroups per CU
   static constexpr int APB = TM * DG_TN * 2;  // dY's chunk
   static constexpr int RAW = APB;             // W's chunk, 32 rows x 128 bytes
-  static constexpr int SCL = RAW + 4096;      // its scales: slot r * (128 / block) + b, 256 slots
-  static constexpr int STAGE = SCL + 1024;
-  static constexpr int TRM = S * STAGE;       // two buffers of three bf16 terms, DG_OPB bytes each
-  static constexpr int LDS = TRM + 6 * DG_OPB;
+  static constexpr int SCL = RAW + 4096;      // its scales: slot b * 32 + r (block b of the tile, row r);
+  static constexpr int STAGE = SCL + 1024;    // 256 slots, 64 loaded by each wave (slots past 4 blocks read zero)
   static constexpr int LOADS = TM / 64 + 2;   // buffer loads per wave per chunk
 };
-static_assert(F3Shape<64>::LDS * 2 <= 160 * 1024 && F3Shape<128>::LDS <= 160 * 1024, "LDS per CU");
+static_assert(2 * F3_S * F3Shape<128>::STAGE <= 160 * 1024, "two workgroups per CU");
 
 // the high halves of two fp32 patterns as one bf16 pair (a low, b high)
 __device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
@@ -793,222 +790,176 @@ __device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) { return (a 
 // LDS accesses of this kernel are written out (the buffer_load ... lds
 // writes are invisible to the compiler's own wait insertion); every read's
 // result is threaded through an explicit wait before its use.
-__device__ __forceinline__ uint32_t lds_rd32(uint32_t addr) {
-  uint32_t v;
-  asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr));
+template <int OFF>
+__device__ __forceinline__ u32x2 tr8_read_at(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  u32x2 v;
+  asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
   return v;
 }
-__device__ __forceinline__ void lds_wr128(uint32_t addr, u32x4 v) {
-  asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(v) : "memory");
-}
-template <int N>
-__device__ __forceinline__ void f3_wait_b(u32x2 (&b)[4]) {
-  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]) : "i"(N));
-}
 
-// term K's fragments of k-step KS for the two 32-column blocks at pb0, pb1
-template <int K, int KS>
-__device__ __forceinline__ void f3_bfrag(uint32_t pb0, uint32_t pb1, u32x2 (&b)[4]) {
-  b[0] = tr_read_at<K * DG_OPB + KS * 4096>(pb0);
-  b[1] = tr_read_at<K * DG_OPB + KS * 4096 + 1024>(pb0);
-  b[2] = tr_read_at<K * DG_OPB + KS * 4096>(pb1);
-  b[3] = tr_read_at<K * DG_OPB + KS * 4096 + 1024>(pb1);
-}
-
-template <int BI>
-__device__ __forceinline__ void f3_mfma(f32x16 (&acc)[BI][2], const u32x4 (&af)[BI], const u32x2 (&b)[4]) {
+// The three bf16 fragments of 8 codes (rows k .. k + 7 of one column) with
+// the scales of those rows.
+__device__ __forceinline__ void f3_split8(u32x2 raw, const float (&sc)[8], bf16x8 (&t)[3]) {
+  float x[8];
+  e4m3_unpack4(raw[0], x);
+  e4m3_unpack4(raw[1], x + 4);
+  uint32_t hb[8], mb[8], lb[8];
 #pragma unroll
-  for (int bi = 0; bi < BI; ++bi)
-#pragma unroll
-    for (int bj = 0; bj < 2; ++bj)
-      acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[bi]),
-                                                            frag_join(b[2 * bj], b[2 * bj + 1]), acc[bi][bj], 0, 0, 0);
-}
-
-// Three bf16 terms of four decoded weights (the codes of one word, times
-// the scale): pairs 2 i, 2 i + 1 of t[k].
-__device__ __forceinline__ void f3_split4(uint32_t word, float sc, uint32_t (&t)[3][8], int i) {
-  float x[4];
-  e4m3_unpack4(word, x);
-  uint32_t hb[4], mb[4], lb[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float v = x[e] * sc;                              // fp32(code * scale)
+  for (int e = 0; e < 8; ++e) {
+    const float v = x[e] * sc[e];                           // fp32(code * scale)
     hb[e] = __float_as_uint(v) & 0xFFFF0000u;
     const float r1 = v - __uint_as_float(hb[e]);
     mb[e] = __float_as_uint(r1) & 0xFFFF0000u;
     lb[e] = __float_as_uint(r1 - __uint_as_float(mb[e]));  // low 16 bits zero
   }
-  t[0][2 * i] = hi_pair(hb[0], hb[1]);
-  t[0][2 * i + 1] = hi_pair(hb[2], hb[3]);
-  t[1][2 * i] = hi_pair(mb[0], mb[1]);
-  t[1][2 * i + 1] = hi_pair(mb[2], mb[3]);
-  t[2][2 * i] = hi_pair(lb[0], lb[1]);
-  t[2][2 * i + 1] = hi_pair(lb[2], lb[3]);
+  t[0] = __builtin_bit_cast(bf16x8, u32x4{hi_pair(hb[0], hb[1]), hi_pair(hb[2], hb[3]), hi_pair(hb[4], hb[5]),
+                                          hi_pair(hb[6], hb[7])});
+  t[1] = __builtin_bit_cast(bf16x8, u32x4{hi_pair(mb[0], mb[1]), hi_pair(mb[2], mb[3]), hi_pair(mb[4], mb[5]),
+                                          hi_pair(mb[6], mb[7])});
+  t[2] = __builtin_bit_cast(bf16x8, u32x4{hi_pair(lb[0], lb[1]), hi_pair(lb[2], lb[3]), hi_pair(lb[4], lb[5]),
+                                          hi_pair(lb[6], lb[7])});
 }
 
-// One k-step's reads: dY's fragments and all three terms' (BI + 12).
+// One k-step's operands: dY's BI fragments, the B codes, the 8 scales.
+template <int BI>
+struct F3Frag {
+  u32x4 a[BI];
+  u32x2 raw;
+  u32x4 s0, s1;
+};
 template <int KS, int BI>
-__device__ __forceinline__ void f3_reads(uint32_t cur, const uint32_t (&aofs)[2][BI], uint32_t pb0, uint32_t pb1,
-                                         u32x4 (&af)[BI], u32x2 (&b0)[4], u32x2 (&b1)[4], u32x2 (&b2)[4]) {
+__device__ __forceinline__ void f3_reads(uint32_t cur, const uint32_t (&aofs)[2][BI], uint32_t braw, uint32_t bscl,
+                                         F3Frag<BI>& f) {
 #pragma unroll
-  for (int bi = 0; bi < BI; ++bi) af[bi] = ds_read_16(cur + aofs[KS][bi]);
-  f3_bfrag<0, KS>(pb0, pb1, b0);
-  f3_bfrag<1, KS>(pb0, pb1, b1);
-  f3_bfrag<2, KS>(pb0, pb1, b2);
+  for (int bi = 0; bi < BI; ++bi) f.a[bi] = ds_read_16(cur + aofs[KS][bi]);
+  f.raw = tr8_read_at<KS * 2048>(cur + braw);
+  f.s0 = ds_read_16_at<KS * 64>(cur + bscl);
+  f.s1 = ds_read_16_at<KS * 64 + 16>(cur + bscl);
+}
+template <int N, int BI>
+__device__ __forceinline__ void f3_wait(F3Frag<BI>& f) {
+  if constexpr (BI == 2)
+    asm volatile("s_waitcnt lgkmcnt(%5)" : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.raw), "+v"(f.s0), "+v"(f.s1) : "i"(N));
+  else
+    asm volatile("s_waitcnt lgkmcnt(%7)"
+                 : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]), "+v"(f.raw), "+v"(f.s0), "+v"(f.s1)
+                 : "i"(N));
+}
+template <int BI>
+__device__ __forceinline__ void f3_mfma(f32x16 (&acc)[BI], const F3Frag<BI>& f) {
+  float sc[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sc[i] = __uint_as_float(f.s0[i]);
+    sc[4 + i] = __uint_as_float(f.s1[i]);
+  }
+  bf16x8 t[3];
+  f3_split8(f.raw, sc, t);
+#pragma unroll
+  for (int k = 0; k < 3; ++k)
+#pragma unroll
+    for (int bi = 0; bi < BI; ++bi)
+      acc[bi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f.a[bi]), t[k], acc[bi], 0, 0, 0);
 }
 }  // namespace
 
 template <int TM>
-__global__ void __launch_bounds__(NT, F3Shape<TM>::OCC) k_dgrad_fp8w3(const DgArgs g) {
+__global__ void __launch_bounds__(NT, 2) k_dgrad_fp8w3(const DgArgs g) {
   using SH = F3Shape<TM>;
-  constexpr int S = SH::S, BI = TM / 64;
-  __shared__ __attribute__((aligned(16))) char lds[SH::LDS];
+  constexpr int S = F3_S, BI = TM / 32;
+  static_assert(BI == 2 || BI == 4, "64- or 128-token tiles");
+  __shared__ __attribute__((aligned(16))) char lds[S * SH::STAGE];
   const int tiles_m = (g.BT + TM - 1) / TM;
   const int w = xcd_work((int)blockIdx.x, (int)gridDim.x);
   const int tj = w / tiles_m, ti = w - tj * tiles_m;
   const int tok0 = ti * TM, col0 = tj * TILE;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wr = wave >> 1, wc = wave & 1;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)lds;
-  f32x16 acc[BI][2];
+  f32x16 acc[BI];
 #pragma unroll
   for (int bi = 0; bi < BI; ++bi)
 #pragma unroll
-    for (int bj = 0; bj < 2; ++bj)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[bi][bj][e] = 0.f;
+    for (int e = 0; e < 16; ++e) acc[bi][e] = 0.f;
   const int nk = (g.N + DG_TN - 1) / DG_TN;
   DgradLoader<TM, S> ld;
   ld.init(g, tok0, col0, tid);
-  // Each wave brings in exactly what its own threads convert: raw W rows
-  // 8 v .. 8 v + 7 (lane l -> row 8 v + l / 8, bytes 16 (l % 8) .. + 15)
-  // and their scales (lane l < 8 bpt -> row 8 v + l / bpt, block l % bpt of
-  // the tile, slot 64 v + l), so a thread may convert a chunk as soon as its
-  // own wave's loads of it have landed.
+  // raw W: wave v, lane l -> row r = 8 v + l / 8 at 16-byte position
+  // l % 8, holding the row's segment (l % 8) ^ (r % 8)
   const int bsh = __builtin_ctz((unsigned)g.wblock);
-  const int bpt_sh = 7 - bsh;                               // log2 of the tile's blocks per row
+  const int bpt = TILE >> bsh;                              // blocks of the tile per row: 1, 2 or 4
   const int64_t spr = g.K >> bsh;                           // scales per row of W
   const uint32_t oobW = (uint32_t)((uint64_t)g.N * g.ldw);
   const uint32_t oobS = (uint32_t)((uint64_t)g.N * spr * 4);
   const __amdgpu_buffer_rsrc_t rW = make_rsrc(g.W, oobW), rS = make_rsrc(g.wsc, oobS);
-  const int wrow = 8 * wave + (lane >> 3), wcol = col0 + 16 * (lane & 7);
+  const int wrow = 8 * wave + (lane >> 3);
+  const int wcol = col0 + 16 * ((lane & 7) ^ (lane >> 3));
   const bool wOk = wcol < g.K;
-  const int srow = 8 * wave + (lane >> bpt_sh), sblk = (col0 >> bsh) + (lane & ((1 << bpt_sh) - 1));
-  const bool sOk = lane < (8 << bpt_sh) && sblk < spr;
+  // scales: slot q = 64 v + l -> block q / 32 of the tile, row q % 32
+  const int q = 64 * wave + lane, sblk = q >> 5, srow = q & 31;
+  const bool sOk = sblk < bpt && (col0 >> bsh) + sblk < spr;
   const auto issue = [&](int kc, char* stage) {
     ld.issue_a(g, kc, stage);
     const int n = kc * DG_TN + wrow;
     const uint32_t ow = (wOk && n < g.N) ? (uint32_t)n * (uint32_t)g.ldw + (uint32_t)wcol : oobW;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_void*)(stage + SH::RAW + wave * 1024), 16, ow, 0, 0, 0);
     const int ns = kc * DG_TN + srow;
-    const uint32_t os = (sOk && ns < g.N) ? (uint32_t)(((int64_t)ns * spr + sblk) * 4) : oobS;
+    const uint32_t os = (sOk && ns < g.N) ? (uint32_t)(((int64_t)ns * spr + (col0 >> bsh) + sblk) * 4) : oobS;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_void*)(stage + SH::SCL + wave * 256), 4, os, 0, 0, 0);
   };
-  // this thread's 16 weights of a chunk: row tid / 8, columns 16 (tid % 8) ..
-  const int crow = tid >> 3, ccol = 16 * (tid & 7);
-  const uint32_t craw = (uint32_t)(SH::RAW + tid * 16);
-  const uint32_t cscl = (uint32_t)(SH::SCL + (64 * wave + (((lane >> 3) << bpt_sh) + (ccol >> bsh))) * 4);
-  uint32_t cwr[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) cwr[h] = (uint32_t)MainBF16::off(crow, ccol + 8 * h);
-  const auto write_terms = [&](uint32_t terms, const uint32_t (&t)[3][8]) {
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      lds_wr128(terms + k * DG_OPB + cwr[0], u32x4{t[k][0], t[k][1], t[k][2], t[k][3]});
-      lds_wr128(terms + k * DG_OPB + cwr[1], u32x4{t[k][4], t[k][5], t[k][6], t[k][7]});
-    }
-  };
-  // fragment offsets within a stage (as k_dgrad_bf16)
-  uint32_t aofs[2][BI], bofs[2];
+  // fragment offsets within a stage.  dY: rows bi 32 + lane % 32, segment
+  // 2 ks + lane / 32 (as k_dgrad_bf16).  B: in 16-lane group G = lane / 16
+  // the 8-bit transposing read gives lane j byte b from byte j % 8 of the
+  // 8 bytes that lane 2 b + j / 8 of the group addresses; lane s of the
+  // group therefore addresses row 8 (lane / 32) + s / 2 (+ 16 in k-step 1),
+  // columns 32 wave + 16 (G % 2) + 8 (s % 2) .. + 7, so that lane l gets
+  // rows 8 (l / 32) .. + 7 of column 32 wave + l % 32: the MFMA's B layout.
+  uint32_t aofs[2][BI];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-    for (int bi = 0; bi < BI; ++bi) aofs[ks][bi] = dg_a_off(wr * (TM / 2) + bi * 32 + (lane & 31), 2 * ks + (lane >> 5));
+    for (int bi = 0; bi < BI; ++bi) aofs[ks][bi] = dg_a_off(bi * 32 + (lane & 31), 2 * ks + (lane >> 5));
+  uint32_t braw, bscl;
   {
-    const int t = 8 * (lane >> 5) + ((lane & 15) >> 2);
-    const int f = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-#pragma unroll
-    for (int bj = 0; bj < 2; ++bj) bofs[bj] = (uint32_t)MainBF16::off(t, wc * 64 + bj * 32 + f);
+    const int sl = lane & 15, grp = lane >> 4;
+    const int r = 8 * (lane >> 5) + (sl >> 1);
+    const int c = 32 * wave + 16 * (grp & 1) + 8 * (sl & 1);
+    braw = (uint32_t)(SH::RAW + r * 128 + ((((c >> 4) ^ (r & 7)) << 4) | (c & 15)));
+    const int tb = (32 * wave + (lane & 31)) >> bsh;         // this lane's block of the tile
+    bscl = (uint32_t)(SH::SCL + (tb * 32 + 8 * (lane >> 5)) * 4);
   }
-  const uint32_t terms0 = lds0 + (uint32_t)SH::TRM;   // term buffer of chunk c: terms0 + (c & 1) 3 DG_OPB
   // every chunk issues its loads (past the end they read zero), so the
   // vector-memory counts are the same in every iteration
 #pragma unroll
   for (int k = 0; k < S - 1; ++k) issue(k, lds + k * SH::STAGE);
-  wait_vmcnt<(S - 2) * SH::LOADS>();   // chunk 0 landed (this wave's loads)
-  {
-    u32x4 raw = ds_read_16(lds0 + craw);
-    uint32_t scb = lds_rd32(lds0 + cscl);
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(raw), "+v"(scb));
-    uint32_t t[3][8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) f3_split4(raw[i], __uint_as_float(scb), t, i);
-    write_terms(terms0, t);
-  }
   for (int j = 0; j < nk; ++j) {
-    wait_vmcnt<(S - 3) * SH::LOADS>();   // chunk j + 1 landed (this wave's loads)
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this thread's term writes done
-    bar();                               // chunk j's terms and dY in place; stage j - 1 free
+    wait_vmcnt<(S - 2) * SH::LOADS>();   // chunk j landed (this wave's loads)
+    bar();                               // ... every wave's; stage j - 1 free
     issue(j + S - 1, lds + ((j + S - 1) % S) * SH::STAGE);
     const uint32_t cur = lds0 + (uint32_t)((j % S) * SH::STAGE);
-    const uint32_t nxt = lds0 + (uint32_t)(((j + 1) % S) * SH::STAGE);
-    const uint32_t tb = terms0 + (uint32_t)((j & 1) * 3 * DG_OPB);
-    const uint32_t pb0 = tb + bofs[0], pb1 = tb + bofs[1];
-    u32x4 af[BI];
-    u32x2 b0[4], b1[4], b2[4];
-    uint32_t t[3][8];
-    // k-step 0; chunk j + 1's raw words and scale requested behind its reads
-    f3_reads<0, BI>(cur, aofs, pb0, pb1, af, b0, b1, b2);
-    dg_wait<8>(af, b0);
-    f3_mfma<BI>(acc, af, b0);
+    F3Frag<BI> f0, f1;
+    f3_reads<0, BI>(cur, aofs, braw, bscl, f0);
+    f3_reads<1, BI>(cur, aofs, braw, bscl, f1);
+    f3_wait<BI + 3, BI>(f0);
+    f3_mfma<BI>(acc, f0);
     __builtin_amdgcn_sched_barrier(0);
-    u32x4 raw = ds_read_16(nxt + craw);
-    uint32_t scb = lds_rd32(nxt + cscl);
-    f3_wait_b<6>(b1);
-    f3_mfma<BI>(acc, af, b1);
+    f3_wait<0, BI>(f1);
+    f3_mfma<BI>(acc, f1);
     __builtin_amdgcn_sched_barrier(0);
-    f3_wait_b<2>(b2);
-    f3_mfma<BI>(acc, af, b2);
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(raw), "+v"(scb));
-    // half of chunk j + 1's conversion while k-step 0's MFMAs run
-    const float sc = __uint_as_float(scb);
-    f3_split4(raw[0], sc, t, 0);
-    f3_split4(raw[1], sc, t, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    // k-step 1
-    f3_reads<1, BI>(cur, aofs, pb0, pb1, af, b0, b1, b2);
-    dg_wait<8>(af, b0);
-    f3_mfma<BI>(acc, af, b0);
-    __builtin_amdgcn_sched_barrier(0);
-    f3_wait_b<4>(b1);
-    f3_mfma<BI>(acc, af, b1);
-    __builtin_amdgcn_sched_barrier(0);
-    f3_wait_b<0>(b2);
-    f3_mfma<BI>(acc, af, b2);
-    __builtin_amdgcn_sched_barrier(0);
-    // the other half while k-step 1's MFMAs run; chunk j + 1's terms into
-    // the other buffer (after the last chunk: the zeros past the end, never read)
-    f3_split4(raw[2], sc, t, 2);
-    f3_split4(raw[3], sc, t, 3);
-    write_terms(terms0 + (uint32_t)(((j + 1) & 1) * 3 * DG_OPB), t);
   }
   wait_vmcnt<0>();
   // lane l, register 4j + i of a 32 x 32 block holds row 8j + 4 (l / 32) + i, column l % 32
 #pragma unroll
   for (int bi = 0; bi < BI; ++bi)
 #pragma unroll
-    for (int bj = 0; bj < 2; ++bj)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int tok = tok0 + wr * (TM / 2) + bi * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        const int col = col0 + wc * 64 + bj * 32 + (lane & 31);
-        if (tok >= g.BT || col >= g.K) continue;
-        const int64_t o = (int64_t)tok * g.ldx + col;
-        if (g.dx_fmt == FMT_F32) static_cast<float*>(g.dX)[o] = acc[bi][bj][e];
-        else static_cast<uint16_t*>(g.dX)[o] = (uint16_t)bf16_rne_bits(acc[bi][bj][e]);
-      }
+    for (int e = 0; e < 16; ++e) {
+      const int tok = tok0 + bi * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      const int col = col0 + 32 * wave + (lane & 31);
+      if (tok >= g.BT || col >= g.K) continue;
+      const int64_t o = (int64_t)tok * g.ldx + col;
+      if (g.dx_fmt == FMT_F32) static_cast<float*>(g.dX)[o] = acc[bi][e];
+      else static_cast<uint16_t*>(g.dX)[o] = (uint16_t)bf16_rne_bits(acc[bi][e]);
+    }
 }
 
 // fast (aligned operands): the bf16 matrix-core kernel, 128-token tiles when
