@@ -215,9 +215,13 @@ forge_status forge_wgrad_check_fp8w(const forge_mat* X, const forge_mat* dY, con
  * from an E4M3 weight with block scales, decoded exactly to the values the
  * step stores (fp32 code value * scale), fp32 accumulation over N.
  * dY: [BT, N] BF16 or F32; dX: [BT, K] BF16 (round to nearest even) or F32,
- * not overlapping dY, W or its scales.  bf16 dY runs on the fp32 matrix
- * cores (v_mfma_f32_32x32x2_f32 on the exactly decoded operands), fp32 dY
- * on the plain fp32 kernel.
+ * not overlapping dY, W or its scales.  bf16 dY with 16-byte aligned rows
+ * of dY and of the codes, N % 8 == 0 and K % 16 == 0 runs on the bf16
+ * matrix cores: each decoded weight is split exactly into three bf16 terms
+ * (8 significant bits each), so every product is exact and the sum is
+ * accumulated in fp32.  Other bf16 dY runs on the fp32 matrix cores
+ * (v_mfma_f32_32x32x2_f32 on the exactly decoded operands), fp32 dY on the
+ * plain fp32 kernel.
  * Errors: those of forge_dgrad, and E_DTYPE / E_SHAPE / E_NULL / E_ALIGN
  * for the weight state as forge_wgrad_step_fp8w.
  */
