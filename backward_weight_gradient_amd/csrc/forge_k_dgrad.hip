@@ -770,7 +770,10 @@ __global__ void __launch_bounds__(NT) k_dgrad_fp8w(const DgArgs g) {
 // row) and the chunk's scales (block-major), all by buffer_load ... lds.
 // Each lane takes its B fragment's 8 codes (8 rows of one column) with the
 // 8-bit transposing LDS read and its 8 rows' scales, and forms the three
-// bf16 fragments in registers.
+// bf16 fragments in registers.  KG reduction groups of 4 waves (each its
+// own ring, chunks g, g + KG, ...) are added through LDS in a fixed order at
+// the end: KG = 2 for 64-token tiles, whose few workgroups would otherwise
+// leave one 4-wave workgroup per CU.
 // ---------------------------------------------------------------------------
 namespace {
 constexpr int F3_S = 4;                       // ring stages
@@ -864,24 +867,27 @@ __device__ __forceinline__ void f3_mfma(f32x16 (&acc)[BI], const F3Frag<BI>& f) 
 }
 }  // namespace
 
-template <int TM>
-__global__ void __launch_bounds__(NT, 2) k_dgrad_fp8w3(const DgArgs g) {
+template <int TM, int KG>
+__global__ void __launch_bounds__(NT * KG, 2) k_dgrad_fp8w3(const DgArgs g) {
   using SH = F3Shape<TM>;
   constexpr int S = F3_S, BI = TM / 32;
   static_assert(BI == 2 || BI == 4, "64- or 128-token tiles");
-  __shared__ __attribute__((aligned(16))) char lds[S * SH::STAGE];
+  static_assert(KG == 1 || KG * S * SH::STAGE >= TM * TILE * 4, "the groups' partial tiles fit the rings");
+  __shared__ __attribute__((aligned(16))) char lds[KG * S * SH::STAGE];
   const int tiles_m = (g.BT + TM - 1) / TM;
   const int w = xcd_work((int)blockIdx.x, (int)gridDim.x);
   const int tj = w / tiles_m, ti = w - tj * tiles_m;
   const int tok0 = ti * TM, col0 = tj * TILE;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)lds;
+  const int kg = (int)threadIdx.x / NT, tid = (int)threadIdx.x - kg * NT, lane = tid & 63, wave = tid >> 6;
+  char* const ring = lds + kg * S * SH::STAGE;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)ring;
   f32x16 acc[BI];
 #pragma unroll
   for (int bi = 0; bi < BI; ++bi)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[bi][e] = 0.f;
   const int nk = (g.N + DG_TN - 1) / DG_TN;
+  const int nj = (nk + KG - 1) / KG;   // this group's chunks kg + KG jj, jj < nj (past the end: zeros)
   DgradLoader<TM, S> ld;
   ld.init(g, tok0, col0, tid);
   // raw W: wave v, lane l -> row r = 8 v + l / 8 at 16-byte position
@@ -931,11 +937,11 @@ __global__ void __launch_bounds__(NT, 2) k_dgrad_fp8w3(const DgArgs g) {
   // every chunk issues its loads (past the end they read zero), so the
   // vector-memory counts are the same in every iteration
 #pragma unroll
-  for (int k = 0; k < S - 1; ++k) issue(k, lds + k * SH::STAGE);
-  for (int j = 0; j < nk; ++j) {
+  for (int k = 0; k < S - 1; ++k) issue(kg + KG * k, ring + k * SH::STAGE);
+  for (int j = 0; j < nj; ++j) {
     wait_vmcnt<(S - 2) * SH::LOADS>();   // chunk j landed (this wave's loads)
     bar();                               // ... every wave's; stage j - 1 free
-    issue(j + S - 1, lds + ((j + S - 1) % S) * SH::STAGE);
+    issue(kg + KG * (j + S - 1), ring + ((j + S - 1) % S) * SH::STAGE);
     const uint32_t cur = lds0 + (uint32_t)((j % S) * SH::STAGE);
     F3Frag<BI> f0, f1;
     f3_reads<0, BI>(cur, aofs, braw, bscl, f0);
@@ -948,6 +954,32 @@ __global__ void __launch_bounds__(NT, 2) k_dgrad_fp8w3(const DgArgs g) {
     __builtin_amdgcn_sched_barrier(0);
   }
   wait_vmcnt<0>();
+  if constexpr (KG > 1) {
+    // group 0's partial + group 1's + ... in that order, through LDS
+    // (lane l, register 4j + i of a 32 x 32 block: row 8j + 4 (l / 32) + i, column l % 32)
+    float* sP = reinterpret_cast<float*>(lds);
+    const auto at = [&](int bi, int e) -> float& {
+      return sP[(bi * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * TILE + 32 * wave + (lane & 31)];
+    };
+    bar();   // every group's rings are idle
+    for (int k = 1; k < KG; ++k) {
+      if (kg == k) {
+#pragma unroll
+        for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) at(bi, e) = acc[bi][e];
+      }
+      __syncthreads();
+      if (kg == 0) {
+#pragma unroll
+        for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[bi][e] = acc[bi][e] + at(bi, e);
+      }
+      __syncthreads();
+    }
+    if (kg != 0) return;
+  }
   // lane l, register 4j + i of a 32 x 32 block holds row 8j + 4 (l / 32) + i, column l % 32
 #pragma unroll
   for (int bi = 0; bi < BI; ++bi)
@@ -972,9 +1004,9 @@ hipError_t launch_dgrad_fp8w(const DgArgs& g, bool fast, hipStream_t st) {
     const int64_t tk = (g.K + TILE - 1) / TILE;
     const int64_t t128 = ((g.BT + 127) / 128) * tk;
     if (t128 >= 256)
-      hipLaunchKernelGGL(k_dgrad_fp8w3<128>, dim3((unsigned)t128), dim3(NT), 0, st, g);
+      hipLaunchKernelGGL((k_dgrad_fp8w3<128, 1>), dim3((unsigned)t128), dim3(NT), 0, st, g);
     else
-      hipLaunchKernelGGL(k_dgrad_fp8w3<64>, dim3((unsigned)(((g.BT + 63) / 64) * tk)), dim3(NT), 0, st, g);
+      hipLaunchKernelGGL((k_dgrad_fp8w3<64, 2>), dim3((unsigned)(((g.BT + 63) / 64) * tk)), dim3(2 * NT), 0, st, g);
     return hipGetLastError();
   }
   const int64_t tk = (g.K + F8_TN - 1) / F8_TN;

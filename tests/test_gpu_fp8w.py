@@ -138,14 +138,16 @@ def test_fp8_weight_gate_proj_full_size(state):
 # (three bf16 terms per decoded weight): (512, 512, 256), (14336, 4096, 512),
 # (1000, 1056, 77) (64-token tiles, ragged tokens, reduction chunk and column
 # tile, blocks of 32), (520, 2048, 2048) (128-token tiles, blocks of 64),
-# (264, 384, 300); N % 8 != 0 takes the fp32 matrix-core kernel: (130, 256,
-# 77); fp32 dY the plain kernel: (97, 384, 130).
+# (136, 2016, 2048) (128-token tiles, a partial last column tile, blocks of
+# 32), (264, 384, 300); N % 8 != 0 takes the fp32 matrix-core kernel: (130,
+# 256, 77); fp32 dY the plain kernel: (97, 384, 130).
 @pytest.mark.parametrize("N,K,BT,dx,dy32,block", [(512, 512, 256, torch.bfloat16, False, 128),
                                                   (130, 256, 77, torch.float32, False, 128),
                                                   (97, 384, 130, torch.bfloat16, True, 128),
                                                   (14336, 4096, 512, torch.bfloat16, False, 128),
                                                   (1000, 1056, 77, torch.bfloat16, False, 32),
                                                   (520, 2048, 2048, torch.float32, False, 64),
+                                                  (136, 2016, 2048, torch.bfloat16, False, 32),
                                                   (264, 384, 300, torch.float32, False, 128)])
 def test_fp8_weight_dgrad(N, K, BT, dx, dy32, block):
     _say(f"case: FP8 W dX {N}x{K} BT{BT} {dx} dY {'f32' if dy32 else 'bf16'} block {block}")
