@@ -173,6 +173,38 @@ def test_fp8_weight_dgrad(N, K, BT, dx, dy32, block):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("wpad", [16, 8])
+def test_fp8_weight_dgrad_strided(wpad):
+    """Row pitches above the row length on dY, the codes and dX: a code pitch that is a multiple of 16
+    (K + 16) takes the bf16 matrix-core kernel, K + 8 the fp32 one; dX columns past K stay untouched."""
+    N, K, BT, block = 264, 256, 130, 64
+    _say(f"case: FP8 W dX strided, code pitch K + {wpad}")
+    L = make_layer(77, N, K, BT, 2, _spec("adamw", "f32", block))
+    codes = torch.zeros((N, K + wpad), dtype=torch.uint8)
+    codes[:, :K] = L.W.view(torch.uint8).cpu()
+    codes = codes.to("cuda")
+    Wv = codes[:, :K].view(torch.float8_e4m3fn)
+    dYb = torch.zeros((BT, N + 8), device="cuda", dtype=torch.bfloat16)
+    dYb[:, :N] = L.dY.to("cuda")
+    dY = dYb[:, :N]
+    big = torch.full((BT, K + 24), float("nan"), device="cuda", dtype=torch.bfloat16)
+    dX = big[:, :K]
+    wsc = L.wsc.to("cuda")
+    W = F.state(Wv, wsc, block)
+    F.forge_dgrad_fp8w(dY, W, dX)
+    torch.cuda.synchronize()
+    rows = np.arange(BT)
+    Wst = O.Stored("e4m3", synth.host(L.W), L.wsc.cpu().numpy(), block)
+    Wdec = O.decode(Wst).astype(np.float32)
+    dYh = synth.host(L.dY)
+    ref = O.input_grad(dYh, Wdec, rows)
+    bound = O.input_grad_error_bound(dYh, Wdec, rows) + np.abs(ref) * 2.0 ** -8
+    got = O.bf16_bits_to_f64(synth.host(dX.contiguous()))
+    bad = np.abs(got - ref) > bound * (1 + 1e-6) + 1e-30
+    assert not bad.any(), f"{int(bad.sum())} dX elements outside the fp32 bound"
+    assert torch.isnan(big[:, K:].float()).all(), "dX columns past K were written"
+
+
 def test_fp8_weight_rejections_leave_everything_untouched():
     _say("case: FP8 W rejected calls")
     h = _hyper("adamw", "sr")
