@@ -270,7 +270,8 @@ def fp8_weight_sweep(F, synth, h, reps=5):
     """E4M3 weight with fp32 block scales (forge_wgrad_step_fp8w) on gate_proj
     [14336, 4096] at BT = 512, AdamW t = 10 with stochastic rounding of the
     weight, moments fp32, bf16 or E4M3; and dX from the E4M3 weight
-    (forge_dgrad_fp8w, the plain fp32 kernel).  The weight starts as the
+    (forge_dgrad_fp8w: the bf16 matrix cores, three exact bf16 terms per
+    decoded weight).  The weight starts as the
     device-quantised N(0, 0.02^2) (forge_debug_quant, nearest code).
     Algorithmic bytes: W codes read and written (2 B) plus its scales
     (8 B per 128 elements), the moments' bytes, X and dY read once."""
