@@ -52,10 +52,10 @@ def parse():
     p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=30,
-                   help="untimed steps before the timed ones; from an idle GPU the launches some 5 to 25 into a "
-                        "burst run 5-12%% slower than later ones (the chip's clocks settling under the load), "
-                        "so the default covers that")
+    p.add_argument("--warmup", type=int, default=100,
+                   help="untimed steps before the timed ones; from an idle GPU the engine clock takes some 50 ms "
+                        "of continuous load to settle, and launches in that time run 5-12%% slower, so the "
+                        "default (about 80 ms of steps) covers that")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     p.add_argument("--no-unfused", action="store_true", help="skip the unfused comparison")
     p.add_argument("--no-ceilings", action="store_true", help="skip the measured HBM and MFMA ceilings")
