@@ -90,6 +90,26 @@ def test_group_qkv_pattern(spec, opt):
         assert_ok(check_against_oracle(snap, L, h, 4, s), f"group q/k/v layer {i}")
 
 
+# Block-scaled moments at each block size: 128 takes the grouped kernel with
+# the block fixed at compile time, 32 and 64 the one that reads it per layer.
+@pytest.mark.parametrize("block", [32, 64, 128])
+@pytest.mark.parametrize("m_fmt,v_fmt", [("s8", "u8"), ("e4m3", "e4m3")])
+def test_group_block_sizes(m_fmt, v_fmt, block):
+    _say(f"case: group q/k/v, {m_fmt}/{v_fmt} moments, block {block}")
+    spec = synth.LayerSpec("bf16", "bf16", m_fmt, v_fmt, block=block)
+    BT, K = 300, 1024
+    layers = [make_layer(10, N, K, BT, 5, spec, extra=i, outlier_p=0.01)
+              for i, N in enumerate((384, 128, 136))]
+    for L in layers[1:]:
+        L.X = layers[0].X
+    h = F.hyper("adamw")
+    seeds = [SEED + 5 * i for i in range(3)]
+    snaps = [snapshot(L) for L in layers]
+    _group_vs_separate(layers, h, 5, seeds)      # `layers` now hold the grouped result
+    for i, (L, snap, s) in enumerate(zip(layers, snaps, seeds)):
+        assert_ok(check_against_oracle(snap, L, h, 5, s), f"group block {block} layer {i}")
+
+
 @pytest.mark.parametrize("spec", [SPEC_CFG1, SPEC_CFG2])
 def test_group_eight_mixed_layers(spec):
     """Eight layers of different shapes and token counts in one call."""
