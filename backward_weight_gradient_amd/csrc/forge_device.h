@@ -1707,7 +1707,7 @@ constexpr int epi_pre() {
                                                               : SMALL_PRE;
 }
 
-template <int IN, bool FAST, int OPT, int WF, int MF, int VF, bool ACC = false>
+template <int IN, bool FAST, int OPT, int WF, int MF, int VF, bool ACC = false, int BLK = 0>
 __global__ void __launch_bounds__(NT, (three_per_cu<OPT, WF, MF, VF, FAST, ACC, false>() ? 3 : 2))
     k_fused(const KArgs a) {
   constexpr bool OCC3 = three_per_cu<OPT, WF, MF, VF, FAST, ACC, false>();
@@ -1720,7 +1720,7 @@ __global__ void __launch_bounds__(NT, (three_per_cu<OPT, WF, MF, VF, FAST, ACC, 
   // These loads are older than every mainloop load, so the mainloop's
   // in-order vmcnt waits still count exactly its own chunks.  (The
   // register-staged mainloop has no registers to spare for it.)
-  Epilogue<Step<OPT, WF, MF, VF, FAST>, FMT_NONE, FAST, epi_depth<OPT, WF, MF, VF, FAST, ACC, false>(), NT, ACC> epi;
+  Epilogue<Step<OPT, WF, MF, VF, FAST, BLK>, FMT_NONE, FAST, epi_depth<OPT, WF, MF, VF, FAST, ACC, false>(), NT, ACC> epi;
   epi.tid = threadIdx.x;
   if constexpr (OCC3) {
     constexpr int PRE = epi_pre<OPT, WF, MF, VF, FAST, ACC, false>();
@@ -1908,6 +1908,14 @@ hipError_t combo_fused(const KArgs& a, int in_fmt, int w_fmt, hipStream_t st) {
     if (wbf) hipLaunchKernelGGL((k_fused_wide<O, FMT_BF16, M, V>), g, dim3(2 * NT), 0, st, a);
     else hipLaunchKernelGGL((k_fused_wide<O, FMT_F32, M, V>), g, dim3(2 * NT), 0, st, a);
   } else if (in_fmt == FMT_BF16 && fast) {
+    // block-scaled moments in 128-element blocks: the block fixed at compile time (as in combo_group)
+    if constexpr (fmt_blocked(M) || fmt_blocked(V)) {
+      if (a.block == 128) {
+        if (wbf) hipLaunchKernelGGL((k_fused<FMT_BF16, true, O, FMT_BF16, M, V, false, 128>), tile_grid(a), b, 0, st, a);
+        else hipLaunchKernelGGL((k_fused<FMT_BF16, true, O, FMT_F32, M, V, false, 128>), tile_grid(a), b, 0, st, a);
+        return hipGetLastError();
+      }
+    }
     if (wbf) hipLaunchKernelGGL((k_fused<FMT_BF16, true, O, FMT_BF16, M, V>), tile_grid(a), b, 0, st, a);
     else hipLaunchKernelGGL((k_fused<FMT_BF16, true, O, FMT_F32, M, V>), tile_grid(a), b, 0, st, a);
   } else if (in_fmt == FMT_BF16) {
