@@ -1191,11 +1191,15 @@ __device__ __forceinline__ void quantize_chunk(const float (&x_in)[8], int block
         word = e4m3_pack4(y[0], y[1], y[2], y[3]);
       }
     } else if constexpr (FMT == FMT_S8) {
+      // rint(y) from one fp32 addition: with |y| < 2^22 the sum y + 1.5 * 2^23
+      // is y rounded to an integer k, to nearest with ties to even (a unit
+      // in the last place of the sum is 1, and the sum's last mantissa bit is
+      // k's), and the sum's low byte is k in two's complement.  Two byte
+      // permutes and an or pack the four codes.
+      uint32_t b[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t c = (uint32_t)(int32_t)rintf(x[4 * g + i] * inv[g]) & 0xFFu;
-        word |= c << (8 * i);
-      }
+      for (int i = 0; i < 4; ++i) b[i] = __float_as_uint(x[4 * g + i] * inv[g] + 0x1.8p23f);
+      word = __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u) | __builtin_amdgcn_perm(b[3], b[2], 0x04000C0Cu);
     } else {   // U8: code 0 only for an exact zero, a positive value at least 1
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
