@@ -94,6 +94,28 @@ def lead_in():
     torch.cuda._sleep(LEAD_IN_CYCLES)
 
 
+# Before a per-call timing each case runs back to back for about this long
+# (at least once, at most WARM_MAX_CALLS calls): from an idle or lightly
+# loaded GPU the engine clock takes some 50 ms of continuous load to settle.
+WARM_MS = 80.0
+WARM_MAX_CALLS = 2000
+
+
+def warm_up(fn):
+    """Run fn back to back for about WARM_MS of device time, then synchronize."""
+    import torch
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    n = min(WARM_MAX_CALLS, int(WARM_MS / max(e0.elapsed_time(e1), 1e-3)))
+    for _ in range(n):
+        fn()
+    torch.cuda.synchronize()
+
+
 def copy_calibration(steps):
     """A plain device-to-device copy of known size, for calibrating the
     FETCH_SIZE / WRITE_SIZE counters against a kernel whose traffic is known."""
@@ -171,8 +193,7 @@ def mfma_sweep(F, synth, h, reps=3):
                 st = synth.state(4, N, K, spec, device="cuda")
                 args = (F.mat(X), F.mat(dY), F.mat(st["W"]), F.state(st["m"]),
                         None if st["v"] is None else F.state(st["v"]))
-                F.forge_wgrad_step(*args, hy, STEP_T, SEED, stream=stream.cuda_stream)
-                torch.cuda.synchronize()
+                warm_up(lambda: F.forge_wgrad_step(*args, hy, STEP_T, SEED, stream=stream.cuda_stream))
                 times = []
                 for _ in range(reps):
                     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -241,8 +262,7 @@ def family_sweep(F, synth, reps=5):
         v = (F.state(st["v"], st["v_scale"], 128) if blocked else F.state(st["v"])) if st["v"] is not None else None
         args = (F.mat(X), F.mat(dY), F.mat(st["W"]), m, v)
         h = F.hyper(opt, lr=1e-4 if opt == "lion" else 1e-3, beta2=0.99 if opt == "lion" else None)
-        F.forge_wgrad_step(*args, h, STEP_T, SEED, stream=stream.cuda_stream)
-        torch.cuda.synchronize()
+        warm_up(lambda: F.forge_wgrad_step(*args, h, STEP_T, SEED, stream=stream.cuda_stream))
         times = []
         for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -292,8 +312,7 @@ def fp8_weight_sweep(F, synth, h, reps=5):
     out = {}
 
     def timed(fn):
-        fn()
-        torch.cuda.synchronize()
+        warm_up(fn)
         ts = []
         for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -335,7 +354,7 @@ def state_format_sweep(F, synth, h, reps=10):
     AdamW t = 10, SR) with compact moments: bf16 W, m, v (all three rounded
     stochastically), int8 m / v with fp32 scales per 128 elements (1% x50
     gradient outliers) and E4M3 m / v with fp32 scales per 128 elements;
-    median of `reps` launches after one untimed.  Algorithmic bytes: W read
+    median of `reps` launches after the warm-up.  Algorithmic bytes: W read
     and written (4 B), each bf16 moment 4 B, each 8-bit moment 2 + 8/128 B,
     X and dY read once."""
     import torch
@@ -364,8 +383,7 @@ def state_format_sweep(F, synth, h, reps=10):
             P_total += N * K
             nbytes += bpp * N * K + 2 * BT * (N + K)     # X and dY (bf16) read once
         launch = lambda: F.forge_wgrad_step_group(layers_arg, h, STEP_T, stream=stream.cuda_stream)
-        launch()
-        torch.cuda.synchronize()
+        warm_up(launch)
         times = []
         for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -417,8 +435,7 @@ def accumulation_sweep(F, synth, h, micro=4, reps=5):
             if ev is not None:
                 ev[i][1].record(stream)
 
-    run()
-    torch.cuda.synchronize()
+    warm_up(run)
     per = [[] for _ in range(micro)]
     for _ in range(reps):
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(micro)]
@@ -452,9 +469,7 @@ def dgrad_sweep(F, L, layers, reps=6, sets=3):
     out = {}
 
     def timed(fns):
-        for fn in fns:
-            fn()
-        torch.cuda.synchronize()
+        warm_up(lambda: [fn() for fn in fns])
         times = []
         for r in range(reps):
             fn = fns[r % len(fns)]
@@ -498,8 +513,7 @@ def measured_ceilings(F, reps=5):
     dst = torch.empty_like(src)
 
     def timed(fn):
-        fn()
-        torch.cuda.synchronize()
+        warm_up(fn)
         ts = []
         for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -551,8 +565,7 @@ def library_gemm_reference(synth, L, layers, reps=5):
     out = {}
 
     def timed(fn):
-        fn()
-        torch.cuda.synchronize()
+        warm_up(fn)
         ts = []
         for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
