@@ -102,9 +102,12 @@ WARM_MAX_CALLS = 2000
 
 
 def warm_up(fn):
-    """Run fn back to back for about WARM_MS of device time, then synchronize."""
+    """Run fn back to back for about WARM_MS of device time, then synchronize
+    (the second call sizes the loop: the first may include one-time loading)."""
     import torch
     stream = torch.cuda.current_stream()
+    fn()
+    torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     fn()
