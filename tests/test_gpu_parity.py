@@ -302,11 +302,14 @@ def test_compute_bound_sweep_full_size(BT, name, N, K, opt):
 # and BT, every optimizer and state layout; bit-equal to the unfused baseline
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("spec,opt", [(SPEC_CFG1, "adamw"), (SPEC_CFG2, "adamw"), (SPEC_CFG3, "adamw"),
+                                      (synth.LayerSpec("bf16", "bf16", "e4m3", "e4m3", block=128), "adamw"),
                                       (synth.LayerSpec("bf16", "bf16", "f32", None), "lion"),
                                       (synth.LayerSpec("bf16", "f32", "bf16", None), "sgdm")])
-# The last two shapes take the 256 x 256 macro-tile kernel used for long token
-# axes (ragged against 256 in both W dimensions and in the token chunks).
-@pytest.mark.parametrize("N,K,BT", [(2000, 4096, 300), (4104, 1024, 520), (600, 17152, 256),
+# 1024 x 2048 is whole tiles (the epilogue without per-segment bounds checks,
+# for every state but bf16 moments); the next three are ragged; the last two
+# take the 256 x 256 macro-tile kernel used for long token axes (ragged
+# against 256 in both W dimensions and in the token chunks).
+@pytest.mark.parametrize("N,K,BT", [(1024, 2048, 300), (2000, 4096, 300), (4104, 1024, 520), (600, 17152, 256),
                                     (1000, 1408, 4100), (2048, 1664, 4128)])
 def test_aligned_multi_tile(spec, opt, N, K, BT):
     _say(f"case: aligned multi-tile {spec} {opt} {N}x{K} BT{BT}")
