@@ -1797,7 +1797,7 @@ static_assert(LDS_WIDE >= LDS_G, "the staged G tile aliases the ring");
 // staged through LDS one at a time, each by its two owner waves (wr = sub / 2,
 // wc / 2 = sub % 2), and all 512 threads run the epilogue on it with 2 of its
 // 4 passes in flight.
-template <int OPT, int WF, int MF, int VF>
+template <int OPT, int WF, int MF, int VF, bool FULL = false>
 __global__ void __launch_bounds__(2 * NT, 1) k_fused_wide(const KArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[LDS_WIDE];
   const int tw = (a.K + MainWide::W - 1) / MainWide::W;
@@ -1808,7 +1808,7 @@ __global__ void __launch_bounds__(2 * NT, 1) k_fused_wide(const KArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wr = wave >> 2, wc = wave & 3;
   float* sG = reinterpret_cast<float*>(lds);
-  Epilogue<Step<OPT, WF, MF, VF, true>, FMT_NONE, true, 2, 2 * NT> epi;   // 2 of the 4 passes in flight
+  Epilogue<Step<OPT, WF, MF, VF, true>, FMT_NONE, true, 2, 2 * NT, false, FULL> epi;   // 2 of the 4 passes in flight
   epi.tid = threadIdx.x;
   for (int sub = 0; sub < 4; ++sub) {
     const int srow0 = row0 + (sub >> 1) * TILE, scol0 = col0 + (sub & 1) * TILE;
@@ -1931,6 +1931,20 @@ hipError_t combo_fused(const KArgs& a, int in_fmt, int w_fmt, hipStream_t st) {
   const bool wbf = w_fmt == FMT_BF16;
   if (in_fmt == FMT_BF16 && fast && a.BT >= WIDE_MIN_BT) {
     const dim3 g((unsigned)(((a.N + 255) / 256) * ((a.K + 255) / 256)));
+    // whole 128 x 128 sub-tiles: the epilogue without per-segment bounds checks
+    // (not with bf16 moments, nor an fp32 weight beside 8-bit moments: those spill)
+    if constexpr (full_pays(M, V)) {
+      if (whole_tiles(a)) {
+        if (wbf) {
+          hipLaunchKernelGGL((k_fused_wide<O, FMT_BF16, M, V, true>), g, dim3(2 * NT), 0, st, a);
+          return hipGetLastError();
+        }
+        if constexpr (!fmt_blocked(M) && !fmt_blocked(V)) {
+          hipLaunchKernelGGL((k_fused_wide<O, FMT_F32, M, V, true>), g, dim3(2 * NT), 0, st, a);
+          return hipGetLastError();
+        }
+      }
+    }
     if (wbf) hipLaunchKernelGGL((k_fused_wide<O, FMT_BF16, M, V>), g, dim3(2 * NT), 0, st, a);
     else hipLaunchKernelGGL((k_fused_wide<O, FMT_F32, M, V>), g, dim3(2 * NT), 0, st, a);
   } else if (in_fmt == FMT_BF16 && fast) {
