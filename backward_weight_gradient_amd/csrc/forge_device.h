@@ -2046,6 +2046,9 @@ hipError_t combo_fused_fp8w(const KArgs& a, hipStream_t st) {
   if (fast && a.BT >= WIDE_MIN_BT) {
     const dim3 g((unsigned)(((a.N + 255) / 256) * ((a.K + 255) / 256)));
     hipLaunchKernelGGL((k_fused_wide<O, FMT_E4M3, M, V>), g, dim3(2 * NT), 0, st, a);
+  } else if (fast && whole_tiles(a) && a.block == 128) {
+    // whole tiles in 128-element blocks: the unchecked epilogue, the block fixed at compile time
+    hipLaunchKernelGGL((k_fused<FMT_BF16, true, O, FMT_E4M3, M, V, false, 128, true>), tile_grid(a), dim3(NT), 0, st, a);
   } else if (fast) {
     hipLaunchKernelGGL((k_fused<FMT_BF16, true, O, FMT_E4M3, M, V>), tile_grid(a), dim3(NT), 0, st, a);
   } else {
