@@ -2031,6 +2031,12 @@ hipError_t combo_step(const KArgs& a, int w_fmt, hipStream_t st) {
 
 template <int O, int M, int V>
 hipError_t combo_fused_acc(const KArgs& a, int w_fmt, hipStream_t st) {
+  if constexpr (full_pays(M, V) && !fmt_blocked(M) && !fmt_blocked(V)) {
+    if (w_fmt == FMT_BF16 && whole_tiles(a)) {   // whole tiles: the unchecked epilogue
+      hipLaunchKernelGGL((k_fused<FMT_BF16, true, O, FMT_BF16, M, V, true, 0, true>), tile_grid(a), dim3(NT), 0, st, a);
+      return hipGetLastError();
+    }
+  }
   if (w_fmt == FMT_BF16) hipLaunchKernelGGL((k_fused<FMT_BF16, true, O, FMT_BF16, M, V, true>), tile_grid(a), dim3(NT), 0, st, a);
   else if (w_fmt == FMT_F32) hipLaunchKernelGGL((k_fused<FMT_BF16, true, O, FMT_F32, M, V, true>), tile_grid(a), dim3(NT), 0, st, a);
   else return hipErrorInvalidValue;
