@@ -119,6 +119,35 @@ def warm_up(fn):
     torch.cuda.synchronize()
 
 
+# The per-call extras time BURST calls queued back to back between one pair of
+# events, as a training step would launch them, and report the mean per call:
+# an event pair around a lone call also holds the call's dispatch latency
+# (a few microseconds).
+BURST = 6
+
+
+def timed_burst(fns, reps):
+    """Median over `reps` samples of the mean device time per call (ms), each
+    sample BURST calls back to back, cycling over `fns` (consecutive calls
+    use different buffers where the caller passes several), after a lead-in
+    spin; the case is warmed up first."""
+    import torch
+    fns = list(fns)
+    stream = torch.cuda.current_stream()
+    warm_up(lambda: [fn() for fn in fns])
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        lead_in()
+        e0.record(stream)
+        for i in range(BURST):
+            fns[i % len(fns)]()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) / BURST)
+    return sorted(ts)[len(ts) // 2]
+
+
 def copy_calibration(steps):
     """A plain device-to-device copy of known size, for calibrating the
     FETCH_SIZE / WRITE_SIZE counters against a kernel whose traffic is known."""
@@ -238,7 +267,7 @@ def family_sweep(F, synth, reps=5):
     """Each of the eight optimizer families on gate_proj [14336, 4096] at
     BT = 512 (bf16 X / dY / W with SR, fp32 states where the family keeps
     them), and AdamW with bf16 moments (stochastic rounding on W, m and v), with
-    int8 and with E4M3 block-scaled moments; median of `reps` launches.
+    int8 and with E4M3 block-scaled moments; timed_burst, `reps` samples.
     Algorithmic bytes: W read + written (4 B), each fp32 state read + written
     (8 B), each bf16 state (4 B) or each 8-bit state with its block scales
     (2 + 8/128 B), X and dY read once."""
@@ -265,17 +294,7 @@ def family_sweep(F, synth, reps=5):
         v = (F.state(st["v"], st["v_scale"], 128) if blocked else F.state(st["v"])) if st["v"] is not None else None
         args = (F.mat(X), F.mat(dY), F.mat(st["W"]), m, v)
         h = F.hyper(opt, lr=1e-4 if opt == "lion" else 1e-3, beta2=0.99 if opt == "lion" else None)
-        warm_up(lambda: F.forge_wgrad_step(*args, h, STEP_T, SEED, stream=stream.cuda_stream))
-        times = []
-        for _ in range(reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            lead_in()
-            e0.record(stream)
-            F.forge_wgrad_step(*args, h, STEP_T, SEED, stream=stream.cuda_stream)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            times.append(e0.elapsed_time(e1))
-        ms = sorted(times)[len(times) // 2]
+        ms = timed_burst([lambda: F.forge_wgrad_step(*args, h, STEP_T, SEED, stream=stream.cuda_stream)], reps)
         if blocked:    # 1-byte codes + one fp32 scale per 128 elements, read and written
             bpp = 4 + 2 * (2 + 8 / 128)
         else:          # each fp32 state read and written: 8 B; each bf16 state: 4 B
@@ -315,17 +334,7 @@ def fp8_weight_sweep(F, synth, h, reps=5):
     out = {}
 
     def timed(fn):
-        warm_up(fn)
-        ts = []
-        for _ in range(reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            lead_in()
-            e0.record(stream)
-            fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        return sorted(ts)[len(ts) // 2]
+        return timed_burst([fn], reps)
 
     for fmt, mbytes in (("f32", 16.0), ("bf16", 8.0), ("e4m3", 2 * (2 + 8 / 128))):
         spec = synth.LayerSpec(in_dtype="bf16", w_fmt="bf16", m_fmt=fmt, v_fmt=fmt, block=128)
@@ -357,7 +366,7 @@ def state_format_sweep(F, synth, h, reps=10):
     AdamW t = 10, SR) with compact moments: bf16 W, m, v (all three rounded
     stochastically), int8 m / v with fp32 scales per 128 elements (1% x50
     gradient outliers) and E4M3 m / v with fp32 scales per 128 elements;
-    median of `reps` launches after the warm-up.  Algorithmic bytes: W read
+    median of `reps` samples of back-to-back launches (timed_burst).  Algorithmic bytes: W read
     and written (4 B), each bf16 moment 4 B, each 8-bit moment 2 + 8/128 B,
     X and dY read once."""
     import torch
@@ -385,18 +394,7 @@ def state_format_sweep(F, synth, h, reps=10):
             layers_arg.append((F.mat(X), F.mat(dY), F.mat(st["W"]), m, v, SEED))
             P_total += N * K
             nbytes += bpp * N * K + 2 * BT * (N + K)     # X and dY (bf16) read once
-        launch = lambda: F.forge_wgrad_step_group(layers_arg, h, STEP_T, stream=stream.cuda_stream)
-        warm_up(launch)
-        times = []
-        for _ in range(reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            lead_in()
-            e0.record(stream)
-            launch()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            times.append(e0.elapsed_time(e1))
-        ms = sorted(times)[len(times) // 2]
+        ms = timed_burst([lambda: F.forge_wgrad_step_group(layers_arg, h, STEP_T, stream=stream.cuda_stream)], reps)
         out[fmt] = {"us": round(1e3 * ms, 1), "params_per_s": round(P_total / (ms * 1e-3), 1),
                     "state_bytes_per_param": bpp, "hbm_gbs_alg": round(nbytes / (ms * 1e-3) / 1e9, 1),
                     "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
@@ -425,28 +423,16 @@ def accumulation_sweep(F, synth, h, micro=4, reps=5):
     mats = [(F.mat(X), F.mat(dY)) for X, dY in mb]
     accm = F.mat(acc)
 
-    def run(ev=None):
-        if ev is not None:
-            lead_in()
-        for i, (Xm, dYm) in enumerate(mats):
-            if ev is not None:
-                ev[i][0].record(stream)
-            if i < micro - 1:
-                F.forge_wgrad_accumulate(Xm, dYm, accm, first=(i == 0), stream=sp)
-            else:
-                F.forge_wgrad_step_accumulated(Xm, dYm, accm, W, m, v, h, STEP_T, SEED, stream=sp)
-            if ev is not None:
-                ev[i][1].record(stream)
-
-    warm_up(run)
-    per = [[] for _ in range(micro)]
-    for _ in range(reps):
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(micro)]
-        run(ev)
-        torch.cuda.synchronize()
-        for i in range(micro):
-            per[i].append(ev[i][0].elapsed_time(ev[i][1]))
-    med = [sorted(t)[len(t) // 2] for t in per]
+    # each phase timed on its own, its calls back to back (timed_burst): the
+    # first micro-step (overwrites), an adding one, and the fused final step
+    first = lambda: F.forge_wgrad_accumulate(*mats[0], accm, first=True, stream=sp)
+    adds = [lambda Xm=Xm, dYm=dYm: F.forge_wgrad_accumulate(Xm, dYm, accm, first=False, stream=sp)
+            for Xm, dYm in mats[1:-1]]
+    final = lambda: F.forge_wgrad_step_accumulated(*mats[-1], accm, W, m, v, h, STEP_T, SEED, stream=sp)
+    t_first = timed_burst([first], reps)
+    t_add = timed_burst(adds, reps) if adds else 0.0
+    t_final = timed_burst([final], reps)
+    med = [t_first] + [t_add] * (micro - 2) + [t_final]
     act = 2 * bt * (N + K)                                  # X and dY (bf16) read once
     nbytes = [(4 if i == 0 else 8) * N * K + act for i in range(micro - 1)] + [24 * N * K + act]
     out = {"micro_batches": micro, "tokens_per_micro_batch": bt,
@@ -462,7 +448,7 @@ def accumulation_sweep(F, synth, h, micro=4, reps=5):
 
 def dgrad_sweep(F, L, layers, reps=6, sets=3):
     """dX = dY W (bf16, fp32 accumulation, bf16 dX) for each layer of the step
-    at BT = 512 (median of `reps` launches): forge_dgrad_split with its
+    at BT = 512 (timed_burst, `reps` samples): forge_dgrad_split with its
     workspace (the reduction split across workgroups where that applies) and
     forge_dgrad (never split).  The launches rotate over `sets` copies of dY
     and W (the step's own, then clones), so consecutive launches do not find
@@ -472,18 +458,7 @@ def dgrad_sweep(F, L, layers, reps=6, sets=3):
     out = {}
 
     def timed(fns):
-        warm_up(lambda: [fn() for fn in fns])
-        times = []
-        for r in range(reps):
-            fn = fns[r % len(fns)]
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            lead_in()
-            e0.record(stream)
-            fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            times.append(e0.elapsed_time(e1))
-        return sorted(times)[len(times) // 2]
+        return timed_burst(fns, reps)
 
     for name, (N, K) in layers.items():
         d = L[name]
@@ -508,25 +483,15 @@ def dgrad_sweep(F, L, layers, reps=6, sets=3):
 def measured_ceilings(F, reps=5):
     """The box's own ceilings through the library's measurement hooks: HBM read + write in the
     fused epilogue's access width (a 1 GiB copy, 2 GiB moved; forge_debug_copy) and the matrix
-    cores in a register-only v_mfma_f32_32x32x16_bf16 loop (forge_debug_mfma_peak).  Medians of
-    `reps` launches timed with HIP events."""
+    cores in a register-only v_mfma_f32_32x32x16_bf16 loop (forge_debug_mfma_peak).  timed_burst,
+    `reps` samples."""
     import torch
     n = 1 << 30
     src = torch.empty(n // 4, device="cuda", dtype=torch.int32).random_()
     dst = torch.empty_like(src)
 
     def timed(fn):
-        warm_up(fn)
-        ts = []
-        for _ in range(reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            lead_in()
-            e0.record()
-            fn()
-            e1.record()
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1) * 1e-3)
-        return sorted(ts)[len(ts) // 2]
+        return timed_burst([fn], reps) * 1e-3
 
     t_copy = timed(lambda: F.forge_debug_copy(src, dst))
     del src, dst
@@ -568,17 +533,7 @@ def library_gemm_reference(synth, L, layers, reps=5):
     out = {}
 
     def timed(fn):
-        warm_up(fn)
-        ts = []
-        for _ in range(reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            lead_in()
-            e0.record()
-            fn()
-            e1.record()
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        return sorted(ts)[len(ts) // 2]
+        return timed_burst([fn], reps)
 
     dx = {}
     for name in layers:
